@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Throughput of one routed MoE layer step on one MI355X, as one JSON line.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+A step is one pass of the whole layer (router, top-k, permutation, routed experts,
+shared expert, combine; LatentMoE projections where the workload has them) over one
+batch of seeded synthetic tokens, with all weights resident in HBM.  Steps rotate over
+several independently generated layer instances and token batches, so no step finds the
+previous step's weights in the 256 MB last-level cache.  Each step is captured once as a
+HIP graph; the timed region replays K graphs back to back between two events.
+
+Also reported:
+  roofline      the routed gate/up dequant-GEMV (the kernel that moves the most bytes):
+                algorithmic bytes per launch / its average duration, measured with events
+                on the launch stream in a second, instrumented pass of the same steps;
+  cpu_baseline  the float64 oracle on a bounded sample of the same workload, on the
+                host cores (a baseline only).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+PEAK_HBM_GBPS = 8000.0
+PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(cfg, D):
+    """Algorithmic bytes and flops of one step at D distinct routed experts touched, for the
+    layer and for the routed gate/up kernel (weights of touched experts, router, shared
+    expert and projections once, activations in and out once)."""
+    K, I, H, T, k = cfg.d_model, cfg.I, cfg.H, cfg.T, cfg.k
+    P = T * k
+    if cfg.wfmt == "mxfp4":
+        gu_w = 2 * I * K * 17 // 32
+    else:
+        gu_w = 2 * I * K + 2 * (I // 128) * (K // 128) * 4
+    shared_b = cfg.expert_bytes(cfg.shared_K, cfg.shared_I) if cfg.shared else 0
+    router_b = cfg.E * H * 2 + (H * 2 if cfg.shared == "gated" else 0)
+    router_b += cfg.E * 4 * ((1 if cfg.logit_bias else 0) + (1 if cfg.select_bias_std else 0))
+    proj_b = 2 * cfg.latent * H * 2 if cfg.latent else 0
+    layer_bytes = D * cfg.expert_bytes() + shared_b + router_b + proj_b + T * H * 2 + T * H * 4
+    flops = 2 * P * 3 * K * I + 2 * T * cfg.E * H
+    if cfg.shared:
+        flops += 2 * T * 3 * cfg.shared_K * cfg.shared_I
+    if cfg.latent:
+        flops += 2 * T * 2 * cfg.latent * H
+    if cfg.act == "mxfp4":
+        gu_in, gu_out = T * K * 17 // 32, P * I * 17 // 32
+    else:
+        gu_in, gu_out = T * K * (4 if cfg.latent else 2), P * I * 4
+    return dict(layer_bytes=layer_bytes, layer_flops=flops, gu_bytes=D * gu_w + gu_in + gu_out,
+                gu_flops=2 * P * 2 * K * I)
+
+
+def cpu_baseline(cfg, steps):
+    """The float64 oracle on `steps` layer steps (token batches 0..steps-1 of instance 0)."""
+    import synth
+    from oracle import layer as OL
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:
+        threadpool_info = threadpool_limits = None
+    cores = len(os.sched_getaffinity(0))
+    limiter = threadpool_limits(cores) if threadpool_limits else None
+    total = 0.0
+    cache = {}
+    for b in range(steps):
+        inp = synth.layer_inputs_np(cfg, 0, 0, b)
+        r = OL.route(inp.x, inp.w_router, cfg.k, cfg.score, cfg.renormalize, cfg.routed_scaling, inp.logit_bias,
+                     inp.select_bias, inp.w_shared_gate if cfg.shared == "gated" else None)
+        for e in set(int(v) for v in r.ids.reshape(-1)):        # generation is not timed
+            if e not in cache:
+                cache[e] = synth.expert_np(cfg, e)
+        if cfg.shared and "s" not in cache:
+            cache["s"] = synth.expert_np(cfg, synth.SHARED)
+        t0 = time.perf_counter()
+        OL.layer(cfg, inp, lambda e: cache[e], lambda: cache["s"])
+        total += time.perf_counter() - t0
+    # threads the oracle could use: the BLAS pools (NumPy's elementwise work is single-threaded)
+    used = max((i.get("num_threads", 1) for i in threadpool_info()), default=1) if threadpool_info else 1
+    if limiter is not None:
+        limiter.restore_original_limits()
+    return dict(value=steps * cfg.T / total, unit="tokens/s", cores=used, kind="oracle",
+                sample=f"{steps} step(s) of {cfg.name} ({steps * cfg.T} tokens), float64 NumPy, "
+                       f"{total:.1f} s; expert bytes generated outside the timed region")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="qwen38max_decode")
+    ap.add_argument("--instances", type=int, default=4, help="independent layer instances rotated over")
+    ap.add_argument("--batches", type=int, default=16, help="token batches rotated over")
+    ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps for the CPU baseline (0: skip)")
+    ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of graph replays")
+    ap.add_argument("--json-out", default=None)
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from synth import device as sdev
+    import mxfp4_routed_expert_amd as M
+
+    cfg = synth.get(args.config)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    R, NB = max(1, args.instances), max(1, args.batches)
+    log(f"[bench] {cfg.name}: building {R} layer instance(s)")
+    layers = []
+    for r in range(R):
+        t, _ = sdev.layer_tensors(cfg, dev, 0, r)
+        w = M.LayerWeights(score=cfg.score, k=cfg.k, renormalize=cfg.renormalize, routed_scaling=cfg.routed_scaling,
+                           act=cfg.act, w_router=t["w_router"], experts=M.ExpertWeights.from_arrays(t["experts"]),
+                           logit_bias=t["logit_bias"], select_bias=t["select_bias"],
+                           shared=M.ExpertWeights.from_arrays(t["shared"]) if t["shared"] is not None else None,
+                           w_shared_gate=t["w_shared_gate"] if cfg.shared == "gated" else None,
+                           p_down=t["p_down"], p_up=t["p_up"])
+        layers.append(M.MoELayer(w, cfg.T, dev))
+    xs = [sdev.token_batch(cfg, dev, 0, 0, b) for b in range(NB)]
+    S = max(R, NB)
+    slot = lambda j: (layers[j % R], xs[j % NB])
+    torch.cuda.synchronize()
+
+    # eager warm-up of every slot (also what the graphs capture)
+    for j in range(S):
+        L, x = slot(j)
+        L.forward(x)
+    torch.cuda.synchronize()
+    graphs = None
+    if not args.no_graph:
+        log("[bench] capturing one graph per step slot")
+        graphs = []
+        stream = torch.cuda.Stream()
+        stream.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(stream):
+            for j in range(S):
+                g = torch.cuda.CUDAGraph()
+                L, x = slot(j)
+                with torch.cuda.graph(g, stream=stream):
+                    L.forward(x)
+                graphs.append(g)
+        torch.cuda.current_stream().wait_stream(stream)
+        torch.cuda.synchronize()
+
+    def step(s):
+        if graphs is not None:
+            graphs[s % S].replay()
+        else:
+            L, x = slot(s)
+            L.forward(x)
+
+    for s in range(args.warmup):
+        step(s)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for s in range(args.steps):
+        step(args.warmup + s)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_per_step = ev0.elapsed_time(ev1) / args.steps
+    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step")
+
+    # distinct routed experts touched per slot (read back after a step of that slot)
+    D_slot = []
+    for j in range(S):
+        L, x = slot(j)
+        L.forward(x)
+        torch.cuda.synchronize()
+        offs = L.offs.cpu()
+        D_slot.append(int(((offs[1:] - offs[:-1]) > 0).sum()))
+    D_steps = [D_slot[(args.warmup + s) % S] for s in range(args.steps)]
+    D_mean = sum(D_steps) / len(D_steps)
+
+    # instrumented pass: events around the routed gate/up kernel on its stream.  A block of
+    # matrix products is queued first so every step of the pass is enqueued before the GPU
+    # reaches it (no host gaps inside the measured intervals).
+    a = torch.randn(8192, 8192, device=dev)
+    for _ in range(4):
+        a = a @ a * 1e-4
+    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    for s in range(args.steps):
+        L, x = slot(args.warmup + s)
+        pair = marks[s]
+        L.forward(x, mark=lambda name, pair=pair: pair[0 if name == "gateup_begin" else 1].record())
+    torch.cuda.synchronize()
+    gu_ms = [b.elapsed_time(c) for b, c in marks]
+    gu_us = 1e3 * sum(gu_ms) / len(gu_ms)
+    del a
+
+    alg = [algorithmic(cfg, D) for D in D_steps]
+    gu_bytes = sum(x["gu_bytes"] for x in alg) / len(alg)
+    gu_flops = sum(x["gu_flops"] for x in alg) / len(alg)
+    layer_bytes = sum(x["layer_bytes"] for x in alg) / len(alg)
+    layer_flops = sum(x["layer_flops"] for x in alg) / len(alg)
+    step_s = ms_per_step * 1e-3
+    peak_flops = PEAK_TFLOPS["fp4"] if cfg.act == "mxfp4" else (PEAK_TFLOPS["fp8"] if cfg.wfmt != "mxfp4" else
+                                                                  PEAK_TFLOPS["bf16"])
+    intensity = gu_flops / gu_bytes
+    if intensity * PEAK_HBM_GBPS * 1e9 > peak_flops * 1e12:
+        achieved = gu_flops / (gu_us * 1e-6) / 1e12
+        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=peak_flops, unit="TFLOP/s",
+                    frac=round(achieved / peak_flops, 4))
+    else:
+        achieved = gu_bytes / (gu_us * 1e-6) / 1e9
+        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
+                    frac=round(achieved / PEAK_HBM_GBPS, 4))
+    roof.update(traffic=None, kernel="moe::gemv_kernel (routed gate/up, fused SwiGLU)"
+                if cfg.act == "float" or cfg.T * cfg.k <= 64 else "routed gate/up grouped GEMM",
+                bytes_per_launch=int(gu_bytes), flops_per_launch=int(gu_flops), avg_launch_us=round(gu_us, 2),
+                launches=len(gu_ms))
+
+    cpu = None
+    if args.cpu_steps > 0:
+        log(f"[bench] CPU baseline: oracle on {args.cpu_steps} step(s)")
+        cpu = cpu_baseline(cfg, args.cpu_steps)
+
+    dtype = {("mxfp4", "float"): "mxfp4 weights x bf16 activations, f32 accumulate",
+             ("mxfp4", "mxfp4"): "mxfp4 x mxfp4, f32 accumulate",
+             ("fp8b128", "float"): "fp8 e4m3 weights x bf16 activations, f32 accumulate"}[(cfg.wfmt, cfg.act)]
+    res = {
+        "metric": "MoE layer tokens/s; decode HBM GB/s and prefill TFLOP/s as % roofline",
+        "value": round(cfg.T / step_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "d_model": cfg.d_model, "I": cfg.I, "E": cfg.E,
+                   "k": cfg.k, "score": cfg.score, "weights": cfg.wfmt, "activations": cfg.act,
+                   "shared": cfg.shared, "latent": cfg.latent, "instances": R, "token_batches": NB,
+                   "graphs": graphs is not None, "distinct_experts_per_step": round(D_mean, 2)},
+        "layer": {"bytes_per_step": int(layer_bytes), "flops_per_step": int(layer_flops),
+                  "GB/s": round(layer_bytes / step_s / 1e9, 1),
+                  "hbm_frac": round(layer_bytes / step_s / 1e9 / PEAK_HBM_GBPS, 4),
+                  "TFLOP/s": round(layer_flops / step_s / 1e12, 3)},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+    }
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

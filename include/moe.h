@@ -1,0 +1,229 @@
+/*
+ * moe.h -- C ABI of the routed Mixture-of-Experts FFN layer over block-quantised
+ * expert weights, for AMD Instinct MI355X (gfx950).
+ *
+ * The layer (rabbit README, design section and architecture table; Kimi K3 article,
+ * architecture section): for each token a router scores every expert (softmax, or
+ * noaux_tc sigmoid with a selection-only bias), keeps the top k and renormalises their
+ * weights; tokens are grouped by expert; each selected expert, stored as OCP MXFP4
+ * (32-element E2M1 blocks sharing one E8M0 scale) or FP8 E4M3 with 128x128 block
+ * scales, computes a SwiGLU FFN; a (gated) shared expert runs on every token; the
+ * outputs are summed with the routing weights.  LatentMoE layers run the routed
+ * experts at a narrower width between two bf16 projections.
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE pointers, row-major, densely packed, owned by the
+ *     caller.  Descriptor structs are host memory, read during the call only.
+ *   - Inputs are read-only and must not alias outputs.  Outputs are fully overwritten.
+ *   - The library allocates no device memory.  Calls that need scratch space take a
+ *     caller-owned workspace (query its size with the matching *_workspace call); its
+ *     contents are undefined after the call.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ *     returns without synchronising.  Calls are thread-safe.
+ *   - Arguments are validated on the host before anything is enqueued; on failure the
+ *     call returns a non-zero status, enqueues nothing and moe_last_error() describes
+ *     the problem.  A failed launch returns MOE_ERR_HIP.  Faults inside kernels
+ *     surface at the caller's next synchronisation.
+ *   - T == 0 (no tokens) is valid: the call returns MOE_OK and enqueues nothing.
+ *   - Device-side values that index memory (expert ids, offsets, pair indices) are
+ *     range-checked in the kernels; out-of-range entries are skipped, never followed.
+ */
+#ifndef MXFP4_ROUTED_EXPERT_MOE_H
+#define MXFP4_ROUTED_EXPERT_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1, /* NULL required pointer, bad size or enum value        */
+    MOE_ERR_UNSUPPORTED = 2, /* valid request this library does not implement        */
+    MOE_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than the *_workspace size   */
+    MOE_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed            */
+} moe_status;
+
+enum { MOE_SCORE_SOFTMAX = 0, MOE_SCORE_SIGMOID = 1 };
+enum { MOE_W_MXFP4 = 0, MOE_W_FP8_E4M3_B128 = 1 };
+/* MOE_ACT_FLOAT: activations are used as given (bf16 x, float32 h): weight-only quantisation.
+ * MOE_ACT_MXFP4: x and h are OCP-MX-quantised to MXFP4 per 32-block and the products run on
+ *                the block-scaled FP4 matrix cores (MXFP4 weights only). */
+enum { MOE_ACT_FLOAT = 0, MOE_ACT_MXFP4 = 1 };
+enum { MOE_DT_BF16 = 0, MOE_DT_F32 = 1 };
+
+typedef void *moe_stream; /* hipStream_t */
+
+/* Maximum sizes accepted: k <= 16, E <= 2048, every int32 product of sizes < 2^31. */
+#define MOE_MAX_TOPK 16
+#define MOE_MAX_EXPERTS 2048
+
+typedef struct {
+    int32_t T;              /* tokens                                             */
+    int32_t H;              /* hidden width, multiple of 32                       */
+    int32_t E;              /* routed experts, 1 <= E <= MOE_MAX_EXPERTS          */
+    int32_t k;              /* experts per token, 1 <= k <= min(E, 16)            */
+    int32_t score;          /* MOE_SCORE_*                                        */
+    int32_t renormalize;    /* 1: divide the selected weights by their sum        */
+    float routed_scaling;   /* multiplies the final routing weights               */
+} moe_route_desc;
+
+/*
+ * moe_route -- router logits, scoring, top-k and renormalisation.
+ * ("softmax top-10 of 512 + gated shared expert" and "noaux_tc sigmoid": rabbit README,
+ * architecture table, "MoE routing" row.)
+ *   l[t][e]  = float32 rounding of the exact dot product x[t] . w_router[e]
+ *              (+ logit_bias[e], added in float64 after rounding)
+ *   softmax: select the k largest l (descending, ties to the lower expert index);
+ *            w = softmax probability of each selected expert, divided by the sum over
+ *            the selected ones when renormalize != 0.
+ *   sigmoid: s = sigmoid(l); select the k largest s + select_bias (bias used for
+ *            selection only); w = s, divided by the selected sum when renormalize != 0.
+ *   w *= routed_scaling.  Post-logit arithmetic runs in float64.
+ *   shared_gate[t] = sigmoid(float32(x[t] . w_shared_gate)) when w_shared_gate != NULL.
+ * x: bf16 [T][H].  w_router: bf16 [E][H].  logit_bias, select_bias: float32 [E] or NULL
+ * (select_bias only with MOE_SCORE_SIGMOID).  w_shared_gate: bf16 [H] or NULL.
+ * topk_ids: int32 [T][k] out.  topk_w: float32 [T][k] out.  shared_gate: float32 [T] out,
+ * required iff w_shared_gate != NULL.
+ * ws: moe_route_workspace(desc) bytes.
+ */
+moe_status moe_route(const moe_route_desc *desc, const void *x, const void *w_router,
+                     const float *logit_bias, const float *select_bias,
+                     const void *w_shared_gate, int32_t *topk_ids, float *topk_w,
+                     float *shared_gate, void *ws, size_t ws_bytes, moe_stream stream);
+size_t moe_route_workspace(const moe_route_desc *desc);
+
+/*
+ * moe_permute -- group the P = T*k (token, slot) pairs by expert with a stable counting
+ * sort.  Pair p = t*k + j refers to topk_ids[t][j].
+ *   expert_offsets[e] = number of pairs routed to experts < e   (int32 [E+1])
+ *   sorted_pairs[r]   = the pairs, grouped by expert, ascending p within an expert (int32 [P])
+ *   pair_to_row[p]    = r such that sorted_pairs[r] == p                              (int32 [P])
+ * Deterministic: positions come from a stable rank, not from atomics.
+ * Ids outside [0, E) are dropped; their pair_to_row entry is -1 and the unused tail
+ * of sorted_pairs is -1.  With T == 0 the call still writes expert_offsets (all zero).
+ * (Tokens grouped per expert: rabbit README features list, per-expert early drain;
+ * one launch for a step's routed experts: Rulith Inference README, engine section.)
+ */
+moe_status moe_permute(int32_t T, int32_t k, int32_t E, const int32_t *topk_ids,
+                       int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_to_row,
+                       void *ws, size_t ws_bytes, moe_stream stream);
+size_t moe_permute_workspace(int32_t T, int32_t k, int32_t E);
+
+/*
+ * Expert weights for E experts (or one shared expert), stacked along the expert axis.
+ *   MOE_W_MXFP4:          gate, up: codes uint8 [E][d_ff][d_model/2], scales uint8 E8M0
+ *                         [E][d_ff][d_model/32]; down: codes [E][d_model][d_ff/2], scales
+ *                         [E][d_model][d_ff/32].  Element k of a row is the LOW nibble of
+ *                         byte k/2 when k is even, the high nibble when odd; E2M1 codes;
+ *                         scale byte b means 2^(b-127), b = 255 is NaN.  d_model and d_ff
+ *                         are multiples of 32.
+ *   MOE_W_FP8_E4M3_B128:  gate, up: codes uint8 E4M3 (OCP "FN") [E][d_ff][d_model], scales
+ *                         float32 [E][d_ff/128][d_model/128]; down: codes [E][d_model][d_ff],
+ *                         scales [E][d_model/128][d_ff/128].  d_model and d_ff are
+ *                         multiples of 128.
+ * ("native quantization read: OCP MXFP4 ... FP8 (E4M3, block-scale)": rabbit README,
+ * architecture table.)
+ */
+typedef struct {
+    int32_t format;       /* MOE_W_*                                  */
+    int32_t num_experts;  /* E                                        */
+    int32_t d_model;      /* input width of gate/up, output of down   */
+    int32_t d_ff;         /* intermediate width                       */
+    const uint8_t *gate, *up, *down;
+    const void *gate_s, *up_s, *down_s;
+} moe_expert_weights;
+
+/*
+ * moe_expert_ffn -- every expert's SwiGLU FFN on the rows routed to it.
+ *   h = silu(gate . a) * (up . a),  silu(g) = g / (1 + exp(-g)),  y = down . h,
+ *   float32 accumulation.  ("SituAndMul" activation of the Kimi K3 experts, rabbit README
+ *   source tree, read as SiLU-and-multiply.)
+ * Routed form (expert_offsets != NULL): rows r in [expert_offsets[e], expert_offsets[e+1])
+ *   belong to expert e and read token sorted_pairs[r] / k;  y_rows is [T*k][d_model].
+ * Identity form (expert_offsets == NULL, num_experts must be 1): row t reads token t;
+ *   y_rows is [T][d_model].  This is the shared expert.
+ * x: [T][d_model], x_dtype MOE_DT_BF16 or MOE_DT_F32.
+ * act == MOE_ACT_MXFP4: x and h are MX-quantised (OCP MX v1.0: scale 2^(floor(log2 amax)-2),
+ *   round to nearest even, saturate at 6) and the products use the block-scaled FP4
+ *   matrix instructions; MXFP4 weights only (else MOE_ERR_UNSUPPORTED).
+ * ws: moe_expert_ffn_workspace(w, act, T, k) bytes (k ignored in the identity form).
+ */
+moe_status moe_expert_ffn(const moe_expert_weights *w, int32_t act, int32_t T, int32_t k,
+                          const void *x, int32_t x_dtype, const int32_t *expert_offsets,
+                          const int32_t *sorted_pairs, float *y_rows, void *ws, size_t ws_bytes,
+                          moe_stream stream);
+size_t moe_expert_ffn_workspace(const moe_expert_weights *w, int32_t act, int32_t T, int32_t k);
+
+/*
+ * The two stages of moe_expert_ffn, exposed separately (R = T*k rows routed, T identity).
+ * moe_expert_gateup writes h = silu(gate . a) * (up . a):
+ *   MOE_ACT_FLOAT: h float32 [R][d_ff] required; h_codes / h_scales ignored.
+ *   MOE_ACT_MXFP4: h_codes uint8 [R][d_ff/2] and h_scales uint8 [R][d_ff/32] required (the
+ *                  MX-quantised h); h (float32, before quantisation) optional.
+ *   ws: moe_expert_gateup_workspace(w, act, T, k) bytes (k ignored in the identity form).
+ * moe_expert_down writes y_rows[r] = down_e . h[r] from h (FLOAT) or h_codes/h_scales (MXFP4).
+ */
+moe_status moe_expert_gateup(const moe_expert_weights *w, int32_t act, int32_t T, int32_t k,
+                             const void *x, int32_t x_dtype, const int32_t *expert_offsets,
+                             const int32_t *sorted_pairs, float *h, uint8_t *h_codes,
+                             uint8_t *h_scales, void *ws, size_t ws_bytes, moe_stream stream);
+size_t moe_expert_gateup_workspace(const moe_expert_weights *w, int32_t act, int32_t T, int32_t k);
+moe_status moe_expert_down(const moe_expert_weights *w, int32_t act, int32_t T, int32_t k,
+                           const float *h, const uint8_t *h_codes, const uint8_t *h_scales,
+                           const int32_t *expert_offsets, float *y_rows, moe_stream stream);
+
+/*
+ * moe_combine -- atomic-free weighted sum (rabbit README, design section: routed expert
+ * outputs summed with their weights, plus the shared expert):
+ *   out[t] = sum_{j=0..k-1} topk_w[t][j] * y_rows[pair_to_row[t*k+j]]
+ *            + (shared_gate ? shared_gate[t] : 1) * y_shared[t]      (if y_shared != NULL)
+ * in this order, float32.  y_rows: [*][d]; y_shared: [T][d] or NULL; out: [T][d].
+ */
+moe_status moe_combine(int32_t T, int32_t k, int32_t d, const float *y_rows,
+                       const int32_t *pair_to_row, const float *topk_w, const float *y_shared,
+                       const float *shared_gate, float *out, moe_stream stream);
+
+/*
+ * moe_dense_bf16 -- y[t] = W . x[t] (+ residual[t]) with a bf16 weight W [n][kdim],
+ * float32 accumulation.  The LatentMoE down/up projections (Kimi K3 article,
+ * architecture section: routed experts compute in a narrower latent width).
+ * x: [T][kdim] bf16 or float32; residual: float32 [T][n] or NULL; y: float32 [T][n].
+ * kdim multiple of 8.
+ */
+moe_status moe_dense_bf16(int32_t T, int32_t n, int32_t kdim, const void *x, int32_t x_dtype,
+                          const void *w, const float *residual, float *y, moe_stream stream);
+
+/*
+ * moe_dequant -- decode a weight matrix [n][kdim] to float32 with the same device
+ * decoding the FFN kernels use: MXFP4 value E2M1(code) * 2^(s-127) (NaN for s = 255),
+ * FP8 value E4M3(code) * scale[n/128][kdim/128].  codes/scales as in moe_expert_weights
+ * for one matrix.  out: float32 [n][kdim].
+ */
+moe_status moe_dequant(int32_t format, int32_t n, int32_t kdim, const uint8_t *codes,
+                       const void *scales, float *out, moe_stream stream);
+
+/*
+ * moe_mx_quantize -- OCP MX conversion of rows [rows][cols] (bf16 or float32, cols a
+ * multiple of 32) to MXFP4: per 32-block scale byte X+127 with X = floor(log2 amax) - 2
+ * clamped to [-127,127] (byte 0 for an all-zero block, 0xFF and zero codes for a block
+ * holding NaN or Inf); codes = nearest E2M1 of v/2^X, ties to even, saturating at 6, sign
+ * kept.  codes: uint8 [rows][cols/2] (even element in the low nibble); scales: uint8
+ * [rows][cols/32].  The activation quantiser of MOE_ACT_MXFP4.
+ */
+moe_status moe_mx_quantize(int32_t rows, int32_t cols, const void *x, int32_t x_dtype,
+                           uint8_t *codes, uint8_t *scales, moe_stream stream);
+
+/* Text of the last error on the calling thread; valid until the next call on it. */
+const char *moe_last_error(void);
+/* MOE_ABI_VERSION of the loaded library. */
+int32_t moe_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MXFP4_ROUTED_EXPERT_MOE_H */

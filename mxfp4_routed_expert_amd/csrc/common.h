@@ -1,0 +1,144 @@
+// Shared helpers of the HIP library: device-side number decoding, wave reductions,
+// host-side error reporting and argument checks.  gfx950 (CDNA4) only: 64-lane
+// wavefronts, the scaled FP4/FP8 conversion instructions and the block-scaled MFMA.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "moe.h"
+
+#define MOE_DEV __device__ __forceinline__
+
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ device decoding
+
+MOE_DEV float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
+
+// E8M0 scale byte -> float32 2^(b-127).  b = 0 is the float32 subnormal 2^-127;
+// b = 255 is NaN (OCP MX v1.0, E8M0).
+MOE_DEV float e8m0_to_f32(uint32_t b) {
+    uint32_t bits = b == 0 ? 0x00400000u : (b == 255 ? 0x7fc00000u : (b << 23));
+    return __uint_as_float(bits);
+}
+
+// Two E2M1 codes (byte `sel` of `w`: low nibble first) -> two bf16 values, unscaled.
+// E2M1 magnitudes (0 .. 6) are exact in bf16.
+template <int SEL>
+MOE_DEV bf16x2 fp4x2_to_bf16x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, SEL);
+}
+template <int SEL>
+MOE_DEV f32x2 fp4x2_to_f32x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, 1.0f, SEL);
+}
+// Two E4M3 codes (16-bit half `HI` of `w`, low byte first) -> two values, unscaled.
+template <bool HI>
+MOE_DEV bf16x2 fp8x2_to_bf16x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, HI);
+}
+template <bool HI>
+MOE_DEV f32x2 fp8x2_to_f32x2(uint32_t w) {
+    return __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, HI);
+}
+// bf16 pair (packed in a dword, low half first) -> two floats.
+MOE_DEV f32x2 bf16x2_to_f32x2(uint32_t w) {
+    f32x2 r;
+    r.x = __uint_as_float(w << 16);
+    r.y = __uint_as_float(w & 0xffff0000u);
+    return r;
+}
+MOE_DEV bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
+
+MOE_DEV float dot2_bf16(bf16x2 a, bf16x2 b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(a, b, c, false);
+}
+
+// silu(g) = g / (1 + exp(-g)); finite for every finite g (exp overflow gives -0).
+MOE_DEV float silu(float g) { return g / (1.0f + expf(-g)); }
+
+// ------------------------------------------------------------------ wave reductions
+// Butterfly sums over aligned groups of `width` lanes (power of two <= 64); every lane
+// of the group ends with the same value, summed in the same order on every run.
+MOE_DEV float group_sum(float v, int width) {
+    for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+MOE_DEV double group_sum_f64(double v, int width) {
+    for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    return v;
+}
+
+MOE_DEV int lane_id() { return threadIdx.x & (kWave - 1); }
+MOE_DEV int wave_id() { return threadIdx.x >> 6; }
+
+// Index of the `slot`-th expert (in expert order) that owns at least one row, or -1.
+// Every thread of the block must call it; uses `scratch` (>= blockDim/64 + 1 ints of LDS).
+MOE_DEV int nth_nonempty_expert(const int32_t *offsets, int E, int slot, int *scratch) {
+    const int nw = blockDim.x >> 6;
+    int found = -1;
+    int base = 0;
+    __shared__ int s_found;
+    if (threadIdx.x == 0) s_found = -1;
+    for (int c = 0; c < E; c += blockDim.x) {
+        const int e = c + (int)threadIdx.x;
+        bool ne = false;
+        if (e < E) ne = offsets[e + 1] > offsets[e];
+        const uint64_t b = __ballot(ne);
+        const int lane = lane_id();
+        const int before = __popcll(b & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+        if (lane == 0) scratch[wave_id()] = __popcll(b);
+        __syncthreads();
+        int wbase = 0, total = 0;
+        for (int w = 0; w < nw; ++w) {
+            const int cw = scratch[w];
+            if (w < wave_id()) wbase += cw;
+            total += cw;
+        }
+        if (ne && base + wbase + before == slot) s_found = e;
+        base += total;
+        __syncthreads();
+    }
+    found = s_found;
+    __syncthreads();
+    return found;
+}
+
+}  // namespace moe
+
+// ------------------------------------------------------------------ host side
+namespace moe {
+
+void set_error(const char *fmt, ...);
+void clear_error();
+moe_status hip_check(hipError_t e, const char *what);
+moe_status launch_check(const char *what);
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+}  // namespace moe
+
+#define MOE_REQUIRE(cond, ...)                                       \
+    do {                                                             \
+        if (!(cond)) {                                               \
+            ::moe::set_error(__VA_ARGS__);                           \
+            return MOE_ERR_INVALID_ARG;                              \
+        }                                                            \
+    } while (0)
+
+#define MOE_TRY(expr)                      \
+    do {                                   \
+        moe_status _st = (expr);           \
+        if (_st != MOE_OK) return _st;     \
+    } while (0)

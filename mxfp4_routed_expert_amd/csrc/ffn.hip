@@ -1,0 +1,248 @@
+// Expert FFN entry points: argument checks, workspace layout and kernel selection.
+//
+// Each expert computes a SwiGLU FFN, h = silu(gate a) * (up a), y = down h (the
+// "SituAndMul" activation of the rabbit README source tree, read as SiLU-and-multiply),
+// on the rows routed to it.  Small row counts per expert (decode) run on the
+// dequant-GEMV kernels; MX-quantised activations with many rows per expert (prefill)
+// run on the block-scaled FP4 matrix-core grouped GEMM.
+#include "gemv.h"
+
+namespace moe {
+
+bool mfma_path_wanted(const moe_expert_weights *w, int act, int T, int k, bool routed);
+moe_status mfma_gateup_launch(const moe_expert_weights *w, int T, int k, const uint8_t *xq, const uint8_t *xs,
+                              const int32_t *offsets, const int32_t *sorted_pairs, int R, float *h,
+                              uint8_t *hq, uint8_t *hs, hipStream_t stream);
+moe_status mfma_down_launch(const moe_expert_weights *w, const uint8_t *hq, const uint8_t *hs,
+                            const int32_t *offsets, int R, float *y, hipStream_t stream);
+
+namespace {
+
+moe_status validate_weights(const moe_expert_weights *w, int act, const char *fn) {
+    MOE_REQUIRE(w != nullptr, "%s: weights descriptor is NULL", fn);
+    MOE_REQUIRE(w->format == MOE_W_MXFP4 || w->format == MOE_W_FP8_E4M3_B128, "%s: unknown weight format %d", fn,
+                w->format);
+    MOE_REQUIRE(w->num_experts >= 1 && w->num_experts <= MOE_MAX_EXPERTS, "%s: num_experts = %d outside [1, %d]", fn,
+                w->num_experts, MOE_MAX_EXPERTS);
+    MOE_REQUIRE(w->d_model > 0 && w->d_ff > 0, "%s: d_model and d_ff must be positive", fn);
+    if (w->format == MOE_W_MXFP4)
+        MOE_REQUIRE(w->d_model % 32 == 0 && w->d_ff % 32 == 0,
+                    "%s: MXFP4 needs d_model (%d) and d_ff (%d) to be multiples of 32", fn, w->d_model, w->d_ff);
+    else
+        MOE_REQUIRE(w->d_model % 128 == 0 && w->d_ff % 128 == 0,
+                    "%s: FP8 block-128 needs d_model (%d) and d_ff (%d) to be multiples of 128", fn, w->d_model,
+                    w->d_ff);
+    MOE_REQUIRE(act == MOE_ACT_FLOAT || act == MOE_ACT_MXFP4, "%s: unknown activation mode %d", fn, act);
+    MOE_REQUIRE((int64_t)w->num_experts * w->d_ff * w->d_model < ((int64_t)1 << 40),
+                "%s: expert stack too large", fn);
+    MOE_REQUIRE(w->gate && w->up && w->down && w->gate_s && w->up_s && w->down_s, "%s: NULL weight pointer", fn);
+    if (act == MOE_ACT_MXFP4 && w->format != MOE_W_MXFP4) {
+        set_error("%s: MX-quantised activations need MXFP4 weights", fn);
+        return MOE_ERR_UNSUPPORTED;
+    }
+    return MOE_OK;
+}
+
+moe_status validate_rows(const moe_expert_weights *w, int T, int k, const int32_t *offsets,
+                         const int32_t *sorted_pairs, const char *fn) {
+    MOE_REQUIRE(T >= 0, "%s: T = %d < 0", fn, T);
+    if (offsets) {
+        MOE_REQUIRE(k >= 1 && k <= MOE_MAX_TOPK && k <= w->num_experts, "%s: k = %d outside [1, min(E, %d)]", fn, k,
+                    MOE_MAX_TOPK);
+        MOE_REQUIRE(sorted_pairs != nullptr || T == 0, "%s: sorted_pairs is NULL", fn);
+    } else {
+        MOE_REQUIRE(w->num_experts == 1, "%s: expert_offsets == NULL needs exactly one expert (got %d)", fn,
+                    w->num_experts);
+    }
+    const int64_t R = offsets ? (int64_t)T * k : T;
+    const int64_t wide = w->d_model > w->d_ff ? w->d_model : w->d_ff;
+    MOE_REQUIRE(R * wide < INT32_MAX, "%s: rows x width overflows int32", fn);
+    return MOE_OK;
+}
+
+inline int rows_of(int T, int k, const int32_t *offsets) { return offsets ? T * k : T; }
+
+struct FfnWs {
+    uint8_t *xq = nullptr, *xs = nullptr;   // MX x codes/scales [T][d_model/2], [T][d_model/32]
+    float *h = nullptr;                     // [R][d_ff]
+    uint8_t *hq = nullptr, *hs = nullptr;   // MX h codes/scales
+    size_t bytes = 0;
+};
+
+// Workspace layout; `with_h` adds the float32 h buffer, `with_hq` the MX h buffers.
+FfnWs ffn_ws_layout(const moe_expert_weights *w, int act, int T, int R, bool with_h, bool with_hq, void *base) {
+    FfnWs l;
+    size_t off = 0;
+    auto take = [&](size_t bytes) {
+        unsigned char *p = base ? (unsigned char *)base + off : nullptr;
+        off += align_up(bytes, 256);
+        return p;
+    };
+    if (act == MOE_ACT_MXFP4) {
+        l.xq = take((size_t)T * w->d_model / 2);
+        l.xs = take((size_t)T * w->d_model / 32);
+    }
+    if (with_h) l.h = (float *)take((size_t)R * w->d_ff * sizeof(float));
+    if (with_hq && act == MOE_ACT_MXFP4) {
+        l.hq = take((size_t)R * w->d_ff / 2);
+        l.hs = take((size_t)R * w->d_ff / 32);
+    }
+    l.bytes = off;
+    return l;
+}
+
+GemvParams base_params(const moe_expert_weights *w, int T, int k, const int32_t *offsets,
+                       const int32_t *sorted_pairs, int R) {
+    GemvParams p = {};
+    p.E = w->num_experts;
+    p.offsets = offsets;
+    p.sorted_pairs = sorted_pairs;
+    p.k = k > 0 ? k : 1;
+    p.T = T;
+    p.R = R;
+    return p;
+}
+
+moe_status gateup_impl(const moe_expert_weights *w, int act, int T, int k, const void *x, int x_dtype,
+                       const int32_t *offsets, const int32_t *sorted_pairs, float *h, uint8_t *hq, uint8_t *hs,
+                       const FfnWs &ws, hipStream_t s) {
+    const int R = rows_of(T, k, offsets);
+    const int fmt = w->format == MOE_W_MXFP4 ? kFmtMXFP4 : kFmtFP8;
+    const int slots = offsets ? (w->num_experts < R ? w->num_experts : R) : 1;
+    if (act == MOE_ACT_MXFP4) {
+        MOE_TRY(mx_quantize_launch(T, w->d_model, x, x_dtype == MOE_DT_F32, ws.xq, ws.xs, s));
+        if (mfma_path_wanted(w, act, T, k, offsets != nullptr))
+            return mfma_gateup_launch(w, T, k, ws.xq, ws.xs, offsets, sorted_pairs, R, h, hq, hs, s);
+    }
+    GemvParams p = base_params(w, T, k, offsets, sorted_pairs, R);
+    p.w[0] = w->gate;
+    p.w[1] = w->up;
+    p.s[0] = w->gate_s;
+    p.s[1] = w->up_s;
+    p.N = w->d_ff;
+    p.K = w->d_model;
+    p.gather = offsets ? 1 : 0;
+    p.n_act_rows = T;
+    float *hout = h;
+    int actk;
+    if (act == MOE_ACT_MXFP4) {
+        p.act = ws.xq;
+        p.act_s = ws.xs;
+        actk = kActMX;
+        if (!hout) hout = ws.h;
+    } else {
+        p.act = x;
+        actk = x_dtype == MOE_DT_F32 ? kActF32 : kActBF16;
+    }
+    p.out = hout;
+    MOE_TRY(gemv_launch(fmt, actk, true, p, slots, T, s, "moe_expert_gateup"));
+    if (act == MOE_ACT_MXFP4) MOE_TRY(mx_quantize_launch(R, w->d_ff, hout, true, hq, hs, s));
+    return MOE_OK;
+}
+
+moe_status down_impl(const moe_expert_weights *w, int act, int T, int k, const float *h, const uint8_t *hq,
+                     const uint8_t *hs, const int32_t *offsets, float *y, hipStream_t s) {
+    const int R = rows_of(T, k, offsets);
+    const int fmt = w->format == MOE_W_MXFP4 ? kFmtMXFP4 : kFmtFP8;
+    const int slots = offsets ? (w->num_experts < R ? w->num_experts : R) : 1;
+    if (act == MOE_ACT_MXFP4 && mfma_path_wanted(w, act, T, k, offsets != nullptr))
+        return mfma_down_launch(w, hq, hs, offsets, R, y, s);
+    GemvParams p = base_params(w, T, k, offsets, nullptr, R);
+    p.w[0] = w->down;
+    p.s[0] = w->down_s;
+    p.N = w->d_model;
+    p.K = w->d_ff;
+    p.gather = 0;
+    p.n_act_rows = R;
+    p.out = y;
+    int actk;
+    if (act == MOE_ACT_MXFP4) {
+        p.act = hq;
+        p.act_s = hs;
+        actk = kActMX;
+    } else {
+        p.act = h;
+        actk = kActF32;
+    }
+    return gemv_launch(fmt, actk, false, p, slots, T, s, "moe_expert_down");
+}
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+extern "C" size_t moe_expert_gateup_workspace(const moe_expert_weights *w, int32_t act, int32_t T, int32_t k) {
+    if (!w || T <= 0) return 0;
+    if (act != MOE_ACT_MXFP4) return 0;
+    const int R = T * (k > 0 ? k : 1);
+    return ffn_ws_layout(w, act, T, R, true, false, nullptr).bytes;
+}
+
+extern "C" size_t moe_expert_ffn_workspace(const moe_expert_weights *w, int32_t act, int32_t T, int32_t k) {
+    if (!w || T <= 0) return 0;
+    const int R = T * (k > 0 ? k : 1);
+    return ffn_ws_layout(w, act, T, R, true, true, nullptr).bytes;
+}
+
+extern "C" moe_status moe_expert_gateup(const moe_expert_weights *w, int32_t act, int32_t T, int32_t k,
+                                        const void *x, int32_t x_dtype, const int32_t *expert_offsets,
+                                        const int32_t *sorted_pairs, float *h, uint8_t *h_codes,
+                                        uint8_t *h_scales, void *ws, size_t ws_bytes, moe_stream stream) {
+    clear_error();
+    MOE_TRY(validate_weights(w, act, "moe_expert_gateup"));
+    MOE_TRY(validate_rows(w, T, k, expert_offsets, sorted_pairs, "moe_expert_gateup"));
+    MOE_REQUIRE(x_dtype == MOE_DT_BF16 || x_dtype == MOE_DT_F32, "moe_expert_gateup: unknown x_dtype %d", x_dtype);
+    if (T == 0) return MOE_OK;
+    MOE_REQUIRE(x != nullptr, "moe_expert_gateup: NULL x");
+    if (act == MOE_ACT_FLOAT)
+        MOE_REQUIRE(h != nullptr, "moe_expert_gateup: NULL h (required with MOE_ACT_FLOAT)");
+    else
+        MOE_REQUIRE(h_codes && h_scales, "moe_expert_gateup: NULL h_codes or h_scales (required with MOE_ACT_MXFP4)");
+    const int R = rows_of(T, k, expert_offsets);
+    const size_t need = moe_expert_gateup_workspace(w, act, T, expert_offsets ? k : 1);
+    if (need && (!ws || ws_bytes < need)) {
+        set_error("moe_expert_gateup: workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+        return MOE_ERR_WORKSPACE;
+    }
+    FfnWs l = ffn_ws_layout(w, act, T, R, true, false, ws);
+    return gateup_impl(w, act, T, k, x, x_dtype, expert_offsets, sorted_pairs, h, h_codes, h_scales, l,
+                       (hipStream_t)stream);
+}
+
+extern "C" moe_status moe_expert_down(const moe_expert_weights *w, int32_t act, int32_t T, int32_t k, const float *h,
+                                      const uint8_t *h_codes, const uint8_t *h_scales, const int32_t *expert_offsets,
+                                      float *y_rows, moe_stream stream) {
+    clear_error();
+    MOE_TRY(validate_weights(w, act, "moe_expert_down"));
+    MOE_TRY(validate_rows(w, T, k, expert_offsets, (const int32_t *)1, "moe_expert_down"));
+    if (T == 0) return MOE_OK;
+    MOE_REQUIRE(y_rows != nullptr, "moe_expert_down: NULL y_rows");
+    if (act == MOE_ACT_FLOAT)
+        MOE_REQUIRE(h != nullptr, "moe_expert_down: NULL h (required with MOE_ACT_FLOAT)");
+    else
+        MOE_REQUIRE(h_codes && h_scales, "moe_expert_down: NULL h_codes or h_scales (required with MOE_ACT_MXFP4)");
+    return down_impl(w, act, T, k, h, h_codes, h_scales, expert_offsets, y_rows, (hipStream_t)stream);
+}
+
+extern "C" moe_status moe_expert_ffn(const moe_expert_weights *w, int32_t act, int32_t T, int32_t k, const void *x,
+                                     int32_t x_dtype, const int32_t *expert_offsets, const int32_t *sorted_pairs,
+                                     float *y_rows, void *ws, size_t ws_bytes, moe_stream stream) {
+    clear_error();
+    MOE_TRY(validate_weights(w, act, "moe_expert_ffn"));
+    MOE_TRY(validate_rows(w, T, k, expert_offsets, sorted_pairs, "moe_expert_ffn"));
+    MOE_REQUIRE(x_dtype == MOE_DT_BF16 || x_dtype == MOE_DT_F32, "moe_expert_ffn: unknown x_dtype %d", x_dtype);
+    if (T == 0) return MOE_OK;
+    MOE_REQUIRE(x && y_rows, "moe_expert_ffn: NULL x or y_rows");
+    const int kk = expert_offsets ? k : 1;
+    const int R = rows_of(T, k, expert_offsets);
+    const size_t need = moe_expert_ffn_workspace(w, act, T, kk);
+    if (!ws || ws_bytes < need) {
+        set_error("moe_expert_ffn: workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+        return MOE_ERR_WORKSPACE;
+    }
+    FfnWs l = ffn_ws_layout(w, act, T, R, true, true, ws);
+    hipStream_t s = (hipStream_t)stream;
+    MOE_TRY(gateup_impl(w, act, T, k, x, x_dtype, expert_offsets, sorted_pairs, l.h, l.hq, l.hs, l, s));
+    return down_impl(w, act, T, k, l.h, l.hq, l.hs, expert_offsets, y_rows, s);
+}

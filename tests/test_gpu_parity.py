@@ -1,0 +1,388 @@
+"""GPU parity: the HIP library (through its C ABI) against the float64 oracle.
+
+Bit-exact: decoded weights, MX-quantised activations, expert ids, the permutation.
+Within tolerance (relative L2 <= 1e-4 and max error <= 2e-3 x RMS of the reference):
+routing weights, shared gate, expert rows, layer outputs.
+"""
+from __future__ import annotations
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from gpu_common import assert_close, build, host_expert_getter, layer_weights, say, to_np
+from synth.device import bf16_tensor, f32_tensor
+from oracle import formats as OF
+from oracle import layer as OL
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import mxfp4_routed_expert_amd  # noqa: F401  (fails loudly when libmoe.so is missing)
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def M():
+    import mxfp4_routed_expert_amd as m
+    return m
+
+
+def tiny(**kw):
+    return dataclasses.replace(synth.get("tiny"), **kw)
+
+
+# ------------------------------------------------------------------ formats
+
+def test_device_generator_matches_host(dev):
+    for cfg in (tiny(), tiny(name="tfp8", wtag=77, wfmt="fp8b128", score="sigmoid", I=256, shared="ungated",
+                             shared_K=256, shared_I=128)):
+        es = synth.experts_torch(cfg, dev)
+        for e in range(cfg.E):
+            h = synth.expert_np(cfg, e)
+            for n in ("gate", "gate_s", "up", "up_s", "down", "down_s"):
+                np.testing.assert_array_equal(to_np(getattr(es, n)[e]), getattr(h, n)[0], err_msg=f"{cfg.name} {n}")
+        if cfg.shared:
+            s = synth.experts_torch(cfg, dev, shared=True)
+            h = synth.expert_np(cfg, synth.SHARED)
+            np.testing.assert_array_equal(to_np(s.down), h.down)
+
+
+def _bits_equal(gpu_f32, ref_f64):
+    ref = ref_f64.astype(np.float32)
+    g = np.asarray(gpu_f32, np.float32)
+    nan = np.isnan(ref)
+    assert (np.isnan(g) == nan).all()
+    np.testing.assert_array_equal(g[~nan].view(np.uint32), ref[~nan].view(np.uint32))
+
+
+def test_dequant_mxfp4_every_code_and_scale_bitexact(dev, M):
+    # row b: scale byte b on each of its 16 blocks, code bytes 0..255 across the row
+    codes = np.tile(np.arange(256, dtype=np.uint8), (256, 1))
+    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 16, axis=1)
+    g = M.moe_dequant("mxfp4", torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev))
+    _bits_equal(to_np(g), OF.dequant_mxfp4(codes, scales))
+
+
+def test_dequant_fp8_every_code_bitexact(dev, M):
+    r = np.arange(256)
+    codes = ((r[:, None] + r[None, :]) % 256).astype(np.uint8)
+    scales = np.array([[2.0 ** -6, 0.7], [3.0, 2.0 ** -20]], np.float32)
+    g = M.moe_dequant("fp8b128", torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev))
+    _bits_equal(to_np(g), OF.dequant_fp8_b128(codes, scales))
+
+
+def _mx_rows():
+    rng = np.random.default_rng(7)
+    rows = [rng.normal(0, s, 256) for s in (1.0, 1e-3, 1e3, 1e-30, 1e30)]
+    rows.append(np.zeros(256))
+    r = rng.normal(size=256); r[5] = np.nan; rows.append(r)
+    r = rng.normal(size=256); r[100] = np.inf; rows.append(r)
+    # exact E2M1 midpoints at several scales
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0])
+    r = np.tile(np.concatenate([mids, -mids]), 16) * 2.0 ** -3
+    rows.append(r)
+    r = rng.normal(size=256); r[::32] = 1e-40; rows.append(r)     # float32 subnormals
+    rows.append(np.full(256, 3e38))
+    return np.stack(rows).astype(np.float32)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_mx_quantize_bitexact(dev, M, dtype):
+    v = _mx_rows()
+    if dtype == "bf16":
+        bits = synth.to_bf16_bits(v.astype(np.float64))
+        x = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(dev)
+        ref_in = OF.bf16_value(bits)
+    else:
+        x = torch.from_numpy(v).to(dev)
+        ref_in = v.astype(np.float64)
+    q, s = M.moe_mx_quantize(x)
+    rq, rs = OF.mx_quantize(ref_in)
+    np.testing.assert_array_equal(to_np(s), rs)
+    np.testing.assert_array_equal(to_np(q), rq)
+
+
+# ------------------------------------------------------------------ routing
+
+ROUTE_CASES = {
+    "tiny": (tiny(), 0),
+    "tiny_sigmoid": (tiny(score="sigmoid", select_bias_std=0.01, k=3), 0),
+    "decode_router": (synth.get("qwen38max_decode"), 0),
+    "decode_router_16tok": (dataclasses.replace(synth.get("qwen38max_decode"), T=16), 0),
+    "latent_router": (synth.get("kimik3_latent_decode"), 0),
+    "prefill_router_zipf": (synth.get("qwen38max_prefill"), 0),
+    "fp8_router_sigmoid": (synth.get("glm52_fp8"), 0),
+    "tiny_no_renorm": (tiny(renormalize=False, routed_scaling=2.5), 0),
+}
+
+
+@pytest.mark.parametrize("name", list(ROUTE_CASES))
+def test_route_matches_oracle(dev, M, name):
+    cfg, seed = ROUTE_CASES[name]
+    inp = synth.layer_inputs_np(cfg, seed)
+    wsg = inp.w_shared_gate if cfg.shared == "gated" else None
+    ids, w, sg = M.moe_route(bf16_tensor(inp.x, dev), bf16_tensor(inp.w_router, dev), cfg.k, cfg.score,
+                             cfg.renormalize, cfg.routed_scaling, f32_tensor(inp.logit_bias, dev),
+                             f32_tensor(inp.select_bias, dev),
+                             bf16_tensor(wsg, dev) if wsg is not None else None)
+    r = OL.route(inp.x, inp.w_router, cfg.k, cfg.score, cfg.renormalize, cfg.routed_scaling, inp.logit_bias,
+                 inp.select_bias, wsg)
+    np.testing.assert_array_equal(to_np(ids), r.ids)
+    assert_close(to_np(w), r.weights, f"{name} topk_w")
+    if cfg.renormalize:
+        np.testing.assert_allclose(to_np(w).astype(np.float64).sum(1), cfg.routed_scaling, rtol=cfg.k * 2.0 ** -23)
+    if wsg is not None:
+        assert_close(to_np(sg), r.shared_gate, f"{name} shared_gate")
+
+
+# ------------------------------------------------------------------ permutation
+
+@pytest.mark.parametrize("T,k,E", [(1, 1, 1), (1, 10, 512), (4, 2, 8), (64, 8, 256), (513, 10, 512),
+                                   (2000, 16, 2048), (4, 8, 896)])
+def test_permute_matches_oracle(dev, M, T, k, E):
+    rng = np.random.default_rng(T * 131 + k * 7 + E)
+    # skewed choice so some experts are empty and some are hot
+    p = rng.zipf(1.3, size=E * 4) % E
+    ids = np.stack([rng.choice(E, k, replace=False, p=np.bincount(p, minlength=E) / len(p)) if E > k * 2
+                    else rng.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    offs, sp, p2r = M.moe_permute(torch.from_numpy(ids).to(dev), E)
+    ref = OL.permute(ids, E)
+    np.testing.assert_array_equal(to_np(offs), ref.expert_offsets)
+    np.testing.assert_array_equal(to_np(sp), ref.sorted_pairs)
+    np.testing.assert_array_equal(to_np(p2r), ref.pair_to_row)
+
+
+def test_permute_drops_out_of_range_ids(dev, M):
+    ids = np.array([[0, 3], [-1, 1], [3, 7]], np.int32)        # -1 and 7 are outside [0, 4)
+    offs, sp, p2r = M.moe_permute(torch.from_numpy(ids).to(dev), 4)
+    assert to_np(offs).tolist() == [0, 1, 2, 2, 4]
+    assert to_np(sp).tolist() == [0, 3, 1, 4, -1, -1]
+    assert to_np(p2r).tolist() == [0, 2, -1, 1, 3, -1]
+
+
+# ------------------------------------------------------------------ expert FFN
+
+FFN_CASES = {
+    "mxfp4_tiny": tiny(T=37),
+    "mxfp4_ragged": tiny(name="rag", wtag=81, T=29, H=1024, I=416, E=6, k=3),
+    "mxfp4_wide": tiny(name="wide", wtag=82, T=5, H=2368, I=7168 // 4, E=4, k=2),
+    "fp8": tiny(name="f8", wtag=83, wfmt="fp8b128", T=19, H=384, I=256, E=5, k=2),
+}
+
+
+@pytest.mark.parametrize("name", list(FFN_CASES))
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+def test_expert_ffn_float_matches_oracle(dev, M, name, xdt):
+    cfg = FFN_CASES[name]
+    t, inp = build(cfg, dev)
+    r = OL.route(inp.x, inp.w_router, cfg.k)
+    perm = OL.permute(r.ids, cfg.E)
+    x = OF.bf16_value(inp.x)
+    if xdt == "f32":
+        # float32 activations that are not bf16 values
+        x = (x * (1.0 + 2.0 ** -12)).astype(np.float32).astype(np.float64)
+        xg = torch.from_numpy(x.astype(np.float32)).to(dev)
+    else:
+        xg = t["x"]
+    w = layer_weights(cfg, t)
+    y = M.moe_expert_ffn(w.experts, xg, "float", cfg.k, torch.from_numpy(perm.expert_offsets.astype(np.int32)).to(dev),
+                         torch.from_numpy(perm.sorted_pairs.astype(np.int32)).to(dev))
+    ge, _ = host_expert_getter(cfg)
+    ref = OL.expert_rows(ge, x, perm, cfg.k)
+    assert_close(to_np(y), ref, f"{name}/{xdt} y_rows")
+
+
+def test_dense_bf16_matches_oracle(dev, M):
+    rng = np.random.default_rng(11)
+    T, n, kd = 5, 200, 448
+    w = synth.to_bf16_bits(0.05 * rng.normal(size=(n, kd)))
+    xb = synth.to_bf16_bits(rng.normal(size=(T, kd)))
+    res = rng.normal(size=(T, n)).astype(np.float32)
+    y1 = M.moe_dense_bf16(bf16_tensor(xb, dev), bf16_tensor(w, dev))
+    assert_close(to_np(y1), OL.dense_bf16(OF.bf16_value(xb), w), "dense bf16 x")
+    xf = rng.normal(size=(T, kd)).astype(np.float32)
+    y2 = M.moe_dense_bf16(torch.from_numpy(xf).to(dev), bf16_tensor(w, dev), torch.from_numpy(res).to(dev))
+    assert_close(to_np(y2), OL.dense_bf16(xf.astype(np.float64), w) + res, "dense f32 x + residual")
+
+
+def test_combine_matches_oracle(dev, M):
+    rng = np.random.default_rng(12)
+    T, k, d = 7, 3, 260
+    y_rows = rng.normal(size=(T * k, d)).astype(np.float32)
+    p2r = rng.permutation(T * k).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    ys = rng.normal(size=(T, d)).astype(np.float32)
+    g = rng.random(T).astype(np.float32)
+    tt = lambda a: torch.from_numpy(a).to(dev)
+    out = M.moe_combine(tt(y_rows), tt(p2r), tt(w), tt(ys), tt(g))
+    ref = OL.combine(y_rows.astype(np.float64), p2r, w.astype(np.float64), k, ys.astype(np.float64),
+                     g.astype(np.float64))
+    assert_close(to_np(out), ref, "combine")
+
+
+# ------------------------------------------------------------------ whole layers, small
+
+LAYER_CASES = {
+    "tiny": tiny(),
+    "tiny_gated_shared": tiny(name="tg", wtag=84, shared="gated", shared_K=256, shared_I=96),
+    "tiny_sigmoid_fp8": tiny(name="tf", wtag=85, wfmt="fp8b128", score="sigmoid", select_bias_std=0.01,
+                             I=256, T=9, k=3, shared="ungated", shared_K=256, shared_I=128),
+    "tiny_latent": tiny(name="tl", wtag=86, latent=128, H=512, I=96, shared="ungated", shared_K=512,
+                        shared_I=64),
+}
+
+
+def _run_layer(M, cfg, dev, seed=0, inst=0):
+    t, inp = build(cfg, dev, seed, inst)
+    layer = M.MoELayer(layer_weights(cfg, t), cfg.T, dev)
+    out = layer.forward(t["x"])
+    torch.cuda.synchronize()
+    return layer, out, inp
+
+
+@pytest.mark.parametrize("name", list(LAYER_CASES))
+def test_layer_matches_oracle(dev, M, name):
+    cfg = LAYER_CASES[name]
+    layer, out, inp = _run_layer(M, cfg, dev)
+    ge, gs = host_expert_getter(cfg)
+    ref = OL.layer(cfg, inp, ge, gs)
+    np.testing.assert_array_equal(to_np(layer.ids), ref.routing.ids)
+    np.testing.assert_array_equal(to_np(layer.sp), ref.perm.sorted_pairs)
+    assert_close(to_np(layer.y_rows), ref.y_rows, f"{name} y_rows")
+    assert_close(to_np(out), ref.out, f"{name} out")
+
+
+# ------------------------------------------------------------------ MX activation mode, stage by stage
+
+def _stagewise_mx(M, cfg, dev, tokens=None):
+    """Stage-wise parity of the MX-activation FFN (codes of x exact; g/u within tolerance; oracle's
+    quantiser on the GPU's h gives the GPU's h codes; down within tolerance on the GPU's h codes)."""
+    t, inp = build(cfg, dev)
+    w = layer_weights(cfg, t)
+    r = OL.route(inp.x, inp.w_router, cfg.k, cfg.score, cfg.renormalize, cfg.routed_scaling, inp.logit_bias)
+    perm = OL.permute(r.ids, cfg.E)
+    offs = torch.from_numpy(perm.expert_offsets.astype(np.int32)).to(dev)
+    sp = torch.from_numpy(perm.sorted_pairs.astype(np.int32)).to(dev)
+    x = OF.bf16_value(inp.x)
+    xq, xs = M.moe_mx_quantize(t["x"])
+    rq, rs = OF.mx_quantize(x)
+    np.testing.assert_array_equal(to_np(xq), rq)
+    np.testing.assert_array_equal(to_np(xs), rs)
+    h, hq, hs = M.moe_expert_gateup(w.experts, t["x"], "mxfp4", cfg.k, offs, sp, want_h=True)
+    y = M.moe_expert_down(w.experts, cfg.T, "mxfp4", cfg.k, offs, h_codes=hq, h_scales=hs)
+    torch.cuda.synchronize()
+    h, hq, hs, y = to_np(h), to_np(hq), to_np(hs), to_np(y)
+    # oracle quantiser on the GPU's float32 h reproduces the GPU's codes exactly
+    oq, os_ = OF.mx_quantize(h.astype(np.float64))
+    np.testing.assert_array_equal(hq, oq)
+    np.testing.assert_array_equal(hs, os_)
+    aq = OF.mx_dequantize(rq, rs)
+    rows = np.arange(len(perm.sorted_pairs))
+    if tokens is not None:
+        rows = rows[np.isin(perm.sorted_pairs // cfg.k, tokens)]
+    hdeq = OF.mx_dequantize(hq, hs)
+    ge, _ = host_expert_getter(cfg)
+    h_ref = np.zeros((len(rows), cfg.I))
+    y_ref = np.zeros((len(rows), cfg.d_model))
+    for e in np.unique(np.searchsorted(perm.expert_offsets, rows, side="right") - 1):
+        sel = np.where((rows >= perm.expert_offsets[e]) & (rows < perm.expert_offsets[e + 1]))[0]
+        G, U, D = OL.dequant_expert(ge(int(e)))
+        a = aq[perm.sorted_pairs[rows[sel]] // cfg.k]
+        h_ref[sel] = OL.silu(a @ G.T) * (a @ U.T)
+        y_ref[sel] = hdeq[rows[sel]] @ D.T
+    assert_close(h[rows], h_ref, f"{cfg.name} mx h")
+    assert_close(y[rows], y_ref, f"{cfg.name} mx y_rows (on GPU h codes)")
+    # end to end against the oracle's own h codes: report code flips (near-ties only)
+    flips = int((OF.mx_quantize(h_ref)[0] != hq[rows]).sum())
+    say(f"  {cfg.name}: {flips} h code bytes differ from the oracle's own quantisation")
+    return flips
+
+
+def test_mx_activation_tiny_stagewise(dev, M):
+    _stagewise_mx(M, tiny(name="tmx", wtag=87, act="mxfp4", T=33, H=512, I=256), dev)
+
+
+def test_mx_activation_layer_tiny_end_to_end(dev, M):
+    cfg = tiny(name="tmx2", wtag=88, act="mxfp4", shared="gated", shared_K=256, shared_I=128)
+    layer, out, inp = _run_layer(M, cfg, dev)
+    ge, gs = host_expert_getter(cfg)
+    ref = OL.layer(cfg, inp, ge, gs)
+    np.testing.assert_array_equal(to_np(layer.ids), ref.routing.ids)
+    assert_close(to_np(out), ref.out, "tiny mx layer out")
+
+
+# ------------------------------------------------------------------ full-size workloads
+
+def test_decode_layer_full_size(dev, M):
+    cfg = synth.get("qwen38max_decode")
+    say("building qwen38max_decode (13.85 GB of experts)")
+    layer, out, inp = _run_layer(M, cfg, dev)
+    say("oracle over the 11 touched experts")
+    ge, gs = host_expert_getter(cfg)
+    ref = OL.layer(cfg, inp, ge, gs)
+    np.testing.assert_array_equal(to_np(layer.ids), ref.routing.ids)
+    assert_close(to_np(layer.topk_w), ref.routing.weights, "decode topk_w")
+    assert_close(to_np(layer.y_rows), ref.y_rows, "decode y_rows")
+    assert_close(to_np(layer.y_s), ref.y_shared, "decode shared")
+    assert_close(to_np(out), ref.out, "decode out")
+    # a second step on the same buffers is bitwise identical (no atomics in value paths)
+    first = to_np(out).copy()
+    out2 = to_np(layer.forward(bf16_tensor(inp.x, dev)))
+    np.testing.assert_array_equal(out2, first)
+
+
+def test_latent_layer_full_size(dev, M):
+    cfg = synth.get("kimik3_latent_decode")
+    say("building kimik3_latent_decode")
+    layer, out, inp = _run_layer(M, cfg, dev)
+    ge, gs = host_expert_getter(cfg)
+    ref = OL.layer(cfg, inp, ge, gs)
+    np.testing.assert_array_equal(to_np(layer.ids), ref.routing.ids)
+    assert_close(to_np(layer.x_lat), ref.x_expert, "latent x_lat")
+    assert_close(to_np(layer.y_rows), ref.y_rows, "latent y_rows")
+    assert_close(to_np(out), ref.out, "latent out")
+
+
+def test_fp8_layer_full_size_sampled_tokens(dev, M):
+    cfg = synth.get("glm52_fp8")
+    say("building glm52_fp8")
+    layer, out, inp = _run_layer(M, cfg, dev)
+    r = OL.route(inp.x, inp.w_router, cfg.k, cfg.score, cfg.renormalize, cfg.routed_scaling, None,
+                 inp.select_bias)
+    np.testing.assert_array_equal(to_np(layer.ids), r.ids)
+    assert_close(to_np(layer.topk_w), r.weights, "fp8 topk_w")
+    ge, gs = host_expert_getter(cfg)
+    x = OF.bf16_value(inp.x)
+    G, U, D = OL.dequant_expert(gs())
+    sample = [0, 17, 63]
+    ys = OL.ffn(x[sample], G, U, D)
+    ref = np.zeros((len(sample), cfg.H))
+    for i, tkn in enumerate(sample):
+        for j in range(cfg.k):
+            ref[i] += r.weights[tkn, j] * OL.ffn(x[tkn:tkn + 1], *OL.dequant_expert(ge(int(r.ids[tkn, j]))))[0]
+        ref[i] += ys[i]
+    assert_close(to_np(out)[sample], ref, "fp8 out (sampled tokens)")
+
+
+def test_prefill_mx_full_size_stagewise_sampled(dev, M):
+    cfg = synth.get("qwen38max_prefill")
+    say("prefill, MX activations, stage-wise on sampled tokens")
+    _stagewise_mx(M, cfg, dev, tokens=[3, 300])
+
+
+def test_zero_tokens_is_a_no_op(dev, M):
+    cfg = tiny()
+    t, _ = build(cfg, dev)
+    w = layer_weights(cfg, t)
+    x0 = t["x"][:0]
+    ids, tw, _ = M.moe_route(x0, w.w_router, cfg.k)
+    assert ids.shape == (0, cfg.k)
+    offs, sp, p2r = M.moe_permute(ids, cfg.E)
+    assert to_np(offs).tolist() == [0] * (cfg.E + 1)
