@@ -14,7 +14,8 @@ from dataclasses import dataclass
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmoe.so")
+# MXFP4_MOE_LIB selects another build of the same library (e.g. a tuning variant).
+LIB_PATH = os.environ.get("MXFP4_MOE_LIB") or os.path.join(_HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_HIP = 0, 1, 2, 3, 4
 SCORE = {"softmax": 0, "sigmoid": 1}

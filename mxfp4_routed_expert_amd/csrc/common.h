@@ -83,36 +83,38 @@ MOE_DEV double group_sum_f64(double v, int width) {
 MOE_DEV int lane_id() { return threadIdx.x & (kWave - 1); }
 MOE_DEV int wave_id() { return threadIdx.x >> 6; }
 
-// Index of the `slot`-th expert (in expert order) that owns at least one row, or -1.
-// Every thread of the block must call it; uses `scratch` (>= blockDim/64 + 1 ints of LDS).
-MOE_DEV int nth_nonempty_expert(const int32_t *offsets, int E, int slot, int *scratch) {
-    const int nw = blockDim.x >> 6;
-    int found = -1;
-    int base = 0;
-    __shared__ int s_found;
-    if (threadIdx.x == 0) s_found = -1;
-    for (int c = 0; c < E; c += blockDim.x) {
-        const int e = c + (int)threadIdx.x;
-        bool ne = false;
-        if (e < E) ne = offsets[e + 1] > offsets[e];
-        const uint64_t b = __ballot(ne);
-        const int lane = lane_id();
-        const int before = __popcll(b & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-        if (lane == 0) scratch[wave_id()] = __popcll(b);
-        __syncthreads();
-        int wbase = 0, total = 0;
-        for (int w = 0; w < nw; ++w) {
-            const int cw = scratch[w];
-            if (w < wave_id()) wbase += cw;
-            total += cw;
-        }
-        if (ne && base + wbase + before == slot) s_found = e;
-        base += total;
-        __syncthreads();
+constexpr int kMaxOffsetChunks = MOE_MAX_EXPERTS / 64 + 1;
+
+// Index of the slot-th expert that owns rows (same value in every lane), -1 if none.
+// All offsets are loaded in one batch of independent loads, so the lookup costs one
+// memory round trip; no LDS and no barrier.
+MOE_DEV int wave_nth_nonempty(const int32_t *offsets, int E, int slot) {
+    const int lane = lane_id();
+    int o[kMaxOffsetChunks];
+#pragma unroll
+    for (int c = 0; c < kMaxOffsetChunks; ++c) {
+        const int i = c * 64 + lane;
+        o[c] = i <= E ? offsets[i] : 0;
     }
-    found = s_found;
-    __syncthreads();
-    return found;
+    int base = 0;
+#pragma unroll
+    for (int c = 0; c < kMaxOffsetChunks; ++c) {
+        if (c * 64 >= E) break;
+        const int next = c + 1 < kMaxOffsetChunks ? __shfl(o[c + 1], 0, kWave) : 0;
+        int o1 = __shfl_down(o[c], 1, kWave);
+        if (lane == 63) o1 = next;
+        const int e = c * 64 + lane;
+        const bool ne = e < E && o1 > o[c];
+        const uint64_t m = __ballot(ne);
+        const int cnt = __popcll(m);
+        if (slot < base + cnt) {
+            const int before = __popcll(m & ((1ull << lane) - 1ull));
+            const uint64_t hit = __ballot(ne && before == slot - base);
+            return c * 64 + __ffsll((long long)hit) - 1;
+        }
+        base += cnt;
+    }
+    return -1;
 }
 
 }  // namespace moe

@@ -7,6 +7,10 @@
 // run on the block-scaled FP4 matrix-core grouped GEMM.
 #include "gemv.h"
 
+#ifndef MOE_USE_MFMA_GEMV
+#define MOE_USE_MFMA_GEMV 0   // 1: decode GEMV on the matrix cores where the shape allows it
+#endif
+
 namespace moe {
 
 bool mfma_path_wanted(const moe_expert_weights *w, int act, int T, int k, bool routed);
@@ -135,7 +139,10 @@ moe_status gateup_impl(const moe_expert_weights *w, int act, int T, int k, const
         actk = x_dtype == MOE_DT_F32 ? kActF32 : kActBF16;
     }
     p.out = hout;
-    MOE_TRY(gemv_launch(fmt, actk, true, p, slots, T, s, "moe_expert_gateup"));
+    if (MOE_USE_MFMA_GEMV && gemv_mfma_supported(fmt, p))
+        MOE_TRY(gemv_mfma_launch(actk, true, p, slots, s, "moe_expert_gateup"));
+    else
+        MOE_TRY(gemv_launch(fmt, actk, true, p, slots, T, s, "moe_expert_gateup"));
     if (act == MOE_ACT_MXFP4) MOE_TRY(mx_quantize_launch(R, w->d_ff, hout, true, hq, hs, s));
     return MOE_OK;
 }
@@ -164,6 +171,8 @@ moe_status down_impl(const moe_expert_weights *w, int act, int T, int k, const f
         p.act = h;
         actk = kActF32;
     }
+    if (MOE_USE_MFMA_GEMV && gemv_mfma_supported(fmt, p))
+        return gemv_mfma_launch(actk, false, p, slots, s, "moe_expert_down");
     return gemv_launch(fmt, actk, false, p, slots, T, s, "moe_expert_down");
 }
 

@@ -27,6 +27,7 @@ struct GemvParams {
     int nl;                    // 16-byte units per lane per row
     int rows_per_wg;           // matrix rows per workgroup
     int chunk;                 // tokens staged in LDS at once (<= MAXM)
+    int lds_ld;                // LDS row stride in elements (matrix-core GEMV)
 };
 
 // Enqueue one GEMV launch.  `slots` is the number of expert slots in the grid (experts
@@ -34,6 +35,10 @@ struct GemvParams {
 // picks the register tile of tokens.
 moe_status gemv_launch(int fmt, int act, bool pair, GemvParams p, int slots, int max_rows_per_expert,
                        hipStream_t stream, const char *what);
+
+// Matrix-core decode GEMV (MXFP4 weights, N % 16 == 0); see gemv_mfma.hip.
+bool gemv_mfma_supported(int fmt, const GemvParams &p);
+moe_status gemv_mfma_launch(int act, bool pair, GemvParams p, int slots, hipStream_t stream, const char *what);
 
 moe_status mx_quantize_launch(int rows, int cols, const void *x, bool f32, uint8_t *codes, uint8_t *scales,
                               hipStream_t stream);

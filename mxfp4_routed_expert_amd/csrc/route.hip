@@ -16,12 +16,13 @@ namespace moe {
 namespace {
 
 constexpr int kRouterTB = 8;      // tokens per wave
-constexpr int kRouterUnroll = 4;  // 16-byte loads in flight per lane per pass
+constexpr int kRouterUnroll = 8;  // 16-byte loads in flight per lane per pass
 
-// One wave computes the dot products of one weight row (expert e < E, or the shared
-// gate row e == E) with up to kRouterTB tokens.  Lanes stride over H in 8-element
-// (16-byte) vectors; the float64 partial sums are reduced across the wave in a fixed
-// butterfly order.
+// One wave computes the dot products of one weight row (expert e < E, or the shared gate
+// row e == E) with up to kRouterTB tokens.  Lanes stride over H in 8-element (16-byte)
+// vectors; loads are issued unconditionally from clamped indices (a load under a branch
+// would be waited for at the join) and out-of-range vectors are skipped when consumed.
+// The float64 partial sums are reduced across the wave in a fixed butterfly order.
 __global__ __launch_bounds__(64) void router_logits_kernel(const uint16_t *__restrict__ x,
                                                            const uint16_t *__restrict__ wr,
                                                            const uint16_t *__restrict__ wsg,
@@ -37,38 +38,32 @@ __global__ __launch_bounds__(64) void router_logits_kernel(const uint16_t *__res
     for (int t = 0; t < kRouterTB; ++t) acc[t] = 0.0;
 
     const int nvec = H >> 3;
-    for (int v0 = lane; v0 < nvec; v0 += kWave * kRouterUnroll) {
+    for (int v0 = lane; v0 < nvec + lane; v0 += kWave * kRouterUnroll) {
         u32x4 wv[kRouterUnroll];
 #pragma unroll
-        for (int u = 0; u < kRouterUnroll; ++u) {
-            const int v = v0 + u * kWave;
-            wv[u] = v < nvec ? __builtin_nontemporal_load((const u32x4 *)(w) + v) : u32x4{0, 0, 0, 0};
-        }
+        for (int u = 0; u < kRouterUnroll; ++u)
+            wv[u] = __builtin_nontemporal_load((const u32x4 *)(w) + min(v0 + u * kWave, nvec - 1));
 #pragma unroll
-        for (int u = 0; u < kRouterUnroll; ++u) {
-            const int v = v0 + u * kWave;
-            if (v >= nvec) break;
-            double wd[8];
+        for (int t = 0; t < kRouterTB; ++t) {
+            if (t >= nt) break;                      // uniform across the wave
+            const u32x4 *xr = (const u32x4 *)(x + (size_t)(t0 + t) * H);
+            u32x4 xv[kRouterUnroll];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const f32x2 f = bf16x2_to_f32x2(wv[u][q]);
-                wd[2 * q] = (double)f.x;
-                wd[2 * q + 1] = (double)f.y;
-            }
+            for (int u = 0; u < kRouterUnroll; ++u) xv[u] = xr[min(v0 + u * kWave, nvec - 1)];
+            double s = acc[t];
 #pragma unroll
-            for (int t = 0; t < kRouterTB; ++t) {
-                if (t < nt) {
-                    const u32x4 xv = ((const u32x4 *)(x + (size_t)(t0 + t) * H))[v];
-                    double s = acc[t];
+            for (int u = 0; u < kRouterUnroll; ++u) {
+                if (v0 + u * kWave < nvec) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
-                        const f32x2 f = bf16x2_to_f32x2(xv[q]);
-                        s = fma(wd[2 * q], (double)f.x, s);
-                        s = fma(wd[2 * q + 1], (double)f.y, s);
+                        const f32x2 fw = bf16x2_to_f32x2(wv[u][q]);
+                        const f32x2 fx = bf16x2_to_f32x2(xv[u][q]);
+                        s = fma((double)fw.x, (double)fx.x, s);
+                        s = fma((double)fw.y, (double)fx.y, s);
                     }
-                    acc[t] = s;
                 }
             }
+            acc[t] = s;
         }
     }
 #pragma unroll
@@ -80,48 +75,96 @@ __global__ __launch_bounds__(64) void router_logits_kernel(const uint16_t *__res
 
 MOE_DEV double sigmoid_f64(double v) { return 1.0 / (1.0 + exp(-v)); }
 
-// One wave per token: k rounds of a wave-wide argmax over the selection keys (ties to
-// the lower expert index), then the weights.  Keys live in LDS; a taken key is set to
-// NaN, which never compares greater.
+// (key, index) order for selection: larger key first, equal keys -> lower index.
+MOE_DEV bool better(double ka, int ia, double kb, int ib) { return ka > kb || (ka == kb && ia < ib); }
+
+template <int CTRL>
+MOE_DEV void argmax_dpp_step(double &k, int &i) {
+    const int lo = __double2loint(k), hi = __double2hiint(k);
+    const int olo = __builtin_amdgcn_mov_dpp(lo, CTRL, 0xF, 0xF, false);
+    const int ohi = __builtin_amdgcn_mov_dpp(hi, CTRL, 0xF, 0xF, false);
+    const int oi = __builtin_amdgcn_mov_dpp(i, CTRL, 0xF, 0xF, false);
+    const double ok = __hiloint2double(ohi, olo);
+    if (better(ok, oi, k, i)) {
+        k = ok;
+        i = oi;
+    }
+}
+
+// Wave-wide best (key, index): DPP butterfly inside each 16-lane row (quad xor 1, quad
+// xor 2, half-row mirror, row mirror), then the four row results through readlane.
+MOE_DEV void wave_argmax(double &k, int &i) {
+    argmax_dpp_step<0xB1>(k, i);    // quad_perm(1,0,3,2)
+    argmax_dpp_step<0x4E>(k, i);    // quad_perm(2,3,0,1)
+    argmax_dpp_step<0x141>(k, i);   // row_half_mirror
+    argmax_dpp_step<0x140>(k, i);   // row_mirror
+    double bk = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(k), 0),
+                                 __builtin_amdgcn_readlane(__double2loint(k), 0));
+    int bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+    for (int r = 1; r < 4; ++r) {
+        const double rk = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(k), 16 * r),
+                                           __builtin_amdgcn_readlane(__double2loint(k), 16 * r));
+        const int ri = __builtin_amdgcn_readlane(i, 16 * r);
+        if (better(rk, ri, bk, bi)) {
+            bk = rk;
+            bi = ri;
+        }
+    }
+    k = bk;
+    i = bi;
+}
+
+// One wave per token.  Lane l holds the selection keys of experts l, l+64, ... in
+// registers and tracks its own best untaken key; each of the k rounds takes the wave-wide
+// best (ties to the lower expert index) and only the winning lane rescans its keys.
+// A NaN key is never selected (ids -1 are emitted if fewer than k keys compare).
+template <int NK>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int rows,
                                                    int T, int E, int k, int score, int renorm,
                                                    float scaling, const float *__restrict__ lbias,
                                                    const float *__restrict__ sbias, int has_sg,
                                                    int32_t *__restrict__ ids, float *__restrict__ w,
                                                    float *__restrict__ sg) {
-    extern __shared__ double s_key[];
     const int t = blockIdx.x * 4 + wave_id();
     if (t >= T) return;
-    double *key = s_key + (size_t)wave_id() * E;
     const int lane = lane_id();
     const float *lt = logits + (size_t)t * rows;
 
-    for (int e = lane; e < E; e += kWave) {
+    double key[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+        const int e = min(lane + 64 * i, E - 1);
         double l = (double)lt[e] + (lbias ? (double)lbias[e] : 0.0);
         if (score == MOE_SCORE_SIGMOID) l = sigmoid_f64(l) + (sbias ? (double)sbias[e] : 0.0);
-        key[e] = l;
+        key[i] = lane + 64 * i < E ? l : NAN;
     }
+    uint32_t taken = 0;
+    auto local_best = [&](double &bk, int &bi) {
+        bk = -INFINITY;
+        bi = INT_MAX;
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int e = lane + 64 * i;
+            if (!((taken >> i) & 1u) && better(key[i], e, bk, bi)) {
+                bk = key[i];
+                bi = e;
+            }
+        }
+    };
+    double lk;
+    int li;
+    local_best(lk, li);
     int my_e = -1;
     for (int j = 0; j < k; ++j) {
-        double bk = -INFINITY;
-        int be = INT_MAX;
-        for (int e = lane; e < E; e += kWave) {
-            const double kv = key[e];
-            if (kv > bk || (kv == bk && e < be)) {
-                bk = kv;
-                be = e;
-            }
+        double wk = lk;
+        int wi = li;
+        wave_argmax(wk, wi);
+        if (lane == j) my_e = wi == INT_MAX ? -1 : wi;
+        if (wi != INT_MAX && (wi & 63) == lane) {     // the winner drops its key
+            taken |= 1u << (wi >> 6);
+            local_best(lk, li);
         }
-        for (int o = kWave / 2; o > 0; o >>= 1) {
-            const double ok = __shfl_xor(bk, o, kWave);
-            const int oe = __shfl_xor(be, o, kWave);
-            if (ok > bk || (ok == bk && oe < be)) {
-                bk = ok;
-                be = oe;
-            }
-        }
-        if (be != INT_MAX && (be & (kWave - 1)) == lane) key[be] = NAN;
-        if (lane == j) my_e = be == INT_MAX ? -1 : be;
     }
 
     const bool mine = lane < k && my_e >= 0;
@@ -142,8 +185,8 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
         }
         wv = p / denom;
     } else {
-        const double s = mine ? sigmoid_f64(l) : 0.0;
-        wv = renorm ? s / group_sum_f64(s, kWave) : s;
+        const double sv = mine ? sigmoid_f64(l) : 0.0;
+        wv = renorm ? sv / group_sum_f64(sv, kWave) : sv;
     }
     wv *= (double)scaling;
     if (lane < k) {
@@ -203,9 +246,11 @@ extern "C" moe_status moe_route(const moe_route_desc *d, const void *x, const vo
                        (const uint16_t *)w_router, (const uint16_t *)w_shared_gate, d->T, d->H, d->E,
                        rows, logits);
     MOE_TRY(launch_check("moe_route: router_logits_kernel"));
-    const size_t lds = (size_t)4 * d->E * sizeof(double);
-    hipLaunchKernelGGL(topk_kernel, dim3((d->T + 3) / 4), dim3(256), lds, s, logits, rows, d->T, d->E,
-                       d->k, d->score, d->renormalize, d->routed_scaling, logit_bias, select_bias,
-                       w_shared_gate ? 1 : 0, topk_ids, topk_w, shared_gate);
+    auto topk = d->E <= 256 ? topk_kernel<4> : d->E <= 512 ? topk_kernel<8> : d->E <= 1024 ? topk_kernel<16>
+                                                                                           : topk_kernel<32>;
+    const int tb = d->T < 4 ? 64 * d->T : 256;
+    hipLaunchKernelGGL(topk, dim3((d->T + 3) / 4), dim3(tb), 0, s, logits, rows, d->T, d->E, d->k, d->score,
+                       d->renormalize, d->routed_scaling, logit_bias, select_bias, w_shared_gate ? 1 : 0,
+                       topk_ids, topk_w, shared_gate);
     return launch_check("moe_route: topk_kernel");
 }

@@ -66,6 +66,9 @@ class MoELayer:
         self.hq = e(T * k, I // 2, dt=torch.uint8) if w.act == "mxfp4" else None
         self.hs = e(T * k, I // 32, dt=torch.uint8) if w.act == "mxfp4" else None
         self.ws_gu = B._workspace(B.moe_expert_gateup_workspace(w.experts, w.act, T, k), device)
+        # the shared expert does not depend on routing: it runs on a second stream, joined
+        # before the combine, so it overlaps router, permutation and routed experts
+        self.side = torch.cuda.Stream(device=device) if w.shared is not None else None
 
     def forward(self, x, mark=None):
         """One layer step on tokens x (bf16 [T][H]); returns the float32 output buffer.
@@ -74,6 +77,11 @@ class MoELayer:
         mark("gateup_begin") / mark("gateup_end") are called around the gate/up call, so a
         caller can record events on the stream around that kernel."""
         w = self.w
+        if w.shared is not None:
+            cur = torch.cuda.current_stream()
+            self.side.wait_stream(cur)
+            with torch.cuda.stream(self.side):
+                B.moe_expert_ffn(w.shared, x, w.act, 1, None, None, out=self.y_s, ws=self.ws_sh)
         B.moe_route(x, w.w_router, w.k, w.score, w.renormalize, w.routed_scaling, w.logit_bias, w.select_bias,
                     w.w_shared_gate, out=(self.ids, self.topk_w, self.sg), ws=self.ws_route)
         B.moe_permute(self.ids, w.E, out=(self.offs, self.sp, self.p2r))
@@ -90,7 +98,7 @@ class MoELayer:
             mark("gateup_end")
             B.moe_expert_down(w.experts, self.T, w.act, w.k, self.offs, self.h, self.hq, self.hs, out=self.y_rows)
         if w.shared is not None:
-            B.moe_expert_ffn(w.shared, x, w.act, 1, None, None, out=self.y_s, ws=self.ws_sh)
+            cur.wait_stream(self.side)
         if w.p_up is not None:
             B.moe_combine(self.y_rows, self.p2r, self.topk_w, out=self.z)
             B.moe_dense_bf16(self.z, w.p_up, residual=self.y_s, out=self.out)
