@@ -153,23 +153,25 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
 #pragma unroll
         for (int mi = 0; mi < NM; ++mi) brow[mi][i] = p.w[mi] + ((size_t)e * p.N + n) * Kh;
     }
-    // scale rows: threads 0..127 -> A row tid; threads 128..255 -> B row tid-128 (each matrix)
-    const uint8_t *srow_a = nullptr;
-    const uint8_t *srow_b[NM] = {};
-    if (tid < kGBM) {
-        const int rr = min(m0 + tid, M - 1);
+    // scale rows: threads 0..127 -> A row tid; threads 128..255 -> B row tid-128 (each matrix).
+    // Every thread gets valid pointers for both roles and picks with a select, so the scale
+    // loads below are unconditional (a load under a branch is waited for at the join).
+    const uint8_t *sp0, *sp1;
+    {
+        const int rr = min(m0 + (tid & (kGBM - 1)), M - 1);
         int src = row0 + rr;
         if (p.gather) src = p.sorted_pairs[src] / p.k;
         src = min(max(src, 0), p.n_arows - 1);
-        srow_a = p.as + (size_t)src * Kb;
-    } else {
-        const int n = min(n0 + tid - kGBM, p.N - 1);
-#pragma unroll
-        for (int mi = 0; mi < NM; ++mi) srow_b[mi] = p.ws[mi] + ((size_t)e * p.N + n) * Kb;
+        const uint8_t *sa = p.as + (size_t)src * Kb;
+        const int n = min(n0 + (tid & (kGBN - 1)), p.N - 1);
+        const uint8_t *sb0 = p.ws[0] + ((size_t)e * p.N + n) * Kb;
+        const uint8_t *sb1 = p.ws[NM - 1] + ((size_t)e * p.N + n) * Kb;
+        sp0 = tid < kGBM ? sa : sb0;
+        sp1 = tid < kGBM ? sa : sb1;
     }
 
     u32x4 ra[2], rb[NM][2];
-    uint32_t rsa = 0, rsb[NM];
+    uint32_t rs0 = 0, rs1 = 0;
     auto gload = [&](int s) {
         // unconditional loads from clamped positions; blocks past K are zeroed at the store
 #pragma unroll
@@ -184,26 +186,22 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
                 const int blk = min(4 * s + bchunk[i], Kb - 1);
                 rb[mi][i] = __builtin_nontemporal_load((const u32x4 *)(brow[mi][i] + (size_t)blk * 16));
             }
-        uint32_t sc4 = 0;
+        uint32_t v0[4], v1[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const int blk = min(4 * s + q, Kb - 1);
-            const uint32_t v = tid < kGBM ? srow_a[blk] : srow_b[0][blk];
-            sc4 |= (4 * s + q < Kb ? v : 127u) << (8 * q);
+            v0[q] = sp0[blk];
+            if constexpr (PAIR) v1[q] = sp1[blk];
         }
-        if (tid < kGBM) rsa = sc4;
-        else rsb[0] = sc4;
-        if constexpr (PAIR) {
-            uint32_t s1 = 0;
-            if (tid >= kGBM) {
+        uint32_t s0 = 0, s1 = 0;
 #pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int blk = min(4 * s + q, Kb - 1);
-                    s1 |= (4 * s + q < Kb ? (uint32_t)srow_b[1][blk] : 127u) << (8 * q);
-                }
-            }
-            rsb[1] = s1;
+        for (int q = 0; q < 4; ++q) {
+            const bool ok = 4 * s + q < Kb;
+            s0 |= (ok ? v0[q] : 127u) << (8 * q);
+            if constexpr (PAIR) s1 |= (ok ? v1[q] : 127u) << (8 * q);
         }
+        rs0 = s0;
+        rs1 = s1;
     };
     auto lstore = [&](int s) {
 #pragma unroll
@@ -218,10 +216,11 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
                 const bool ok = 4 * s + bchunk[i] < Kb;
                 *(u32x4 *)(sB[mi] + brow_i[i] * kGRowPad + bchunk[i] * 16) = ok ? rb[mi][i] : u32x4{0, 0, 0, 0};
             }
-        if (tid < kGBM) sSA[tid] = rsa;
-        else {
-#pragma unroll
-            for (int mi = 0; mi < NM; ++mi) sSB[mi][tid - kGBM] = rsb[mi];
+        if (tid < kGBM) {
+            sSA[tid] = rs0;
+        } else {
+            sSB[0][tid - kGBM] = rs0;
+            if constexpr (PAIR) sSB[NM - 1][tid - kGBM] = rs1;
         }
     };
 

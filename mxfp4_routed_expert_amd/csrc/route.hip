@@ -73,6 +73,88 @@ __global__ __launch_bounds__(64) void router_logits_kernel(const uint16_t *__res
     }
 }
 
+// Many tokens: a tiled float64 product.  A workgroup owns 128 tokens x 128 rows and one
+// of kRouterKS slices of H; bf16 tiles are converted once to float64 into LDS (k-major),
+// each thread accumulates an 8 x 8 block of exact products in float64.  The slices' partial
+// sums go to the workspace and router_reduce_kernel adds them in a fixed order and rounds
+// once to float32 -- the same logits as the one-wave form, up to float64 rounding.
+constexpr int kRouterKS = 16;   // K slices
+constexpr int kRtTile = 128;
+constexpr int kRtKC = 16;       // bf16 values per stage
+
+__global__ __launch_bounds__(256) void router_tiled_kernel(const uint16_t *__restrict__ x,
+                                                           const uint16_t *__restrict__ wr,
+                                                           const uint16_t *__restrict__ wsg, int T, int H,
+                                                           int E, int rows, double *__restrict__ partial) {
+    __shared__ __align__(16) double xs[kRtKC][kRtTile];
+    __shared__ __align__(16) double wsm[kRtKC][kRtTile];
+    const int tid = threadIdx.x;
+    const int t0 = blockIdx.y * kRtTile, r0 = blockIdx.x * kRtTile;
+    const int ks = blockIdx.z;
+    const int hs = H / kRouterKS;                      // H % (32 * kRouterKS) is checked on the host
+    const int h0 = ks * hs, h1 = h0 + hs;
+    const int ty = tid >> 4, tx = tid & 15;
+    // staging: thread -> (tile row tid/2, 8 values at (tid&1)*8)
+    const int lr = tid >> 1, lh = (tid & 1) * 8;
+    const int tt = min(t0 + lr, T - 1), rr = min(r0 + lr, rows - 1);
+    const bool tok_ok = t0 + lr < T, row_ok = r0 + lr < rows;
+    const uint16_t *xrow = x + (size_t)tt * H;
+    const uint16_t *wrow = rr < E ? wr + (size_t)rr * H : wsg;
+    double acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
+    for (int h = h0; h < h1; h += kRtKC) {
+        const u32x4 xv = *(const u32x4 *)(xrow + h + lh);
+        const u32x4 wv = __builtin_nontemporal_load((const u32x4 *)(wrow + h + lh));
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const f32x2 fx = bf16x2_to_f32x2(xv[q]), fw = bf16x2_to_f32x2(wv[q]);
+            xs[lh + 2 * q][lr] = tok_ok ? (double)fx.x : 0.0;
+            xs[lh + 2 * q + 1][lr] = tok_ok ? (double)fx.y : 0.0;
+            wsm[lh + 2 * q][lr] = row_ok ? (double)fw.x : 0.0;
+            wsm[lh + 2 * q + 1][lr] = row_ok ? (double)fw.y : 0.0;
+        }
+        __syncthreads();
+#pragma unroll 4
+        for (int kk = 0; kk < kRtKC; ++kk) {
+            double a[8], b[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) a[i] = xs[kk][ty * 8 + i];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) b[j] = wsm[kk][tx * 8 + j];
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int t = t0 + ty * 8 + i;
+        if (t >= T) break;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int r = r0 + tx * 8 + j;
+            if (r < rows) partial[((size_t)ks * T + t) * rows + r] = acc[i][j];
+        }
+    }
+}
+
+__global__ __launch_bounds__(256) void router_reduce_kernel(const double *__restrict__ partial, int n,
+                                                            float *__restrict__ logits) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= n) return;
+    double s = 0.0;
+#pragma unroll
+    for (int ks = 0; ks < kRouterKS; ++ks) s += partial[(size_t)ks * n + i];
+    logits[i] = (float)s;
+}
+
+bool router_tiled(const moe_route_desc *d) { return d->T >= 32 && d->H % (32 * kRouterKS) == 0; }
+
 MOE_DEV double sigmoid_f64(double v) { return 1.0 / (1.0 + exp(-v)); }
 
 // (key, index) order for selection: larger key first, equal keys -> lower index.
@@ -218,7 +300,9 @@ using namespace moe;
 
 extern "C" size_t moe_route_workspace(const moe_route_desc *d) {
     if (!d || d->T <= 0 || d->E <= 0) return 0;
-    return align_up((size_t)d->T * (d->E + 1) * sizeof(float), 256);
+    size_t b = align_up((size_t)d->T * (d->E + 1) * sizeof(float), 256);
+    if (d->H % 32 == 0 && router_tiled(d)) b += (size_t)kRouterKS * d->T * (d->E + 1) * sizeof(double);
+    return b;
 }
 
 extern "C" moe_status moe_route(const moe_route_desc *d, const void *x, const void *w_router,
@@ -241,11 +325,22 @@ extern "C" moe_status moe_route(const moe_route_desc *d, const void *x, const vo
     const int rows = d->E + (w_shared_gate ? 1 : 0);
     float *logits = (float *)ws;
     hipStream_t s = (hipStream_t)stream;
-    dim3 g1(rows, (d->T + kRouterTB - 1) / kRouterTB);
-    hipLaunchKernelGGL(router_logits_kernel, g1, dim3(64), 0, s, (const uint16_t *)x,
-                       (const uint16_t *)w_router, (const uint16_t *)w_shared_gate, d->T, d->H, d->E,
-                       rows, logits);
-    MOE_TRY(launch_check("moe_route: router_logits_kernel"));
+    if (router_tiled(d)) {
+        double *partial = (double *)((unsigned char *)ws + align_up((size_t)d->T * (d->E + 1) * sizeof(float), 256));
+        dim3 gt((rows + kRtTile - 1) / kRtTile, (d->T + kRtTile - 1) / kRtTile, kRouterKS);
+        hipLaunchKernelGGL(router_tiled_kernel, gt, dim3(256), 0, s, (const uint16_t *)x, (const uint16_t *)w_router,
+                           (const uint16_t *)w_shared_gate, d->T, d->H, d->E, rows, partial);
+        MOE_TRY(launch_check("moe_route: router_tiled_kernel"));
+        const int n = d->T * rows;
+        hipLaunchKernelGGL(router_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, partial, n, logits);
+        MOE_TRY(launch_check("moe_route: router_reduce_kernel"));
+    } else {
+        dim3 g1(rows, (d->T + kRouterTB - 1) / kRouterTB);
+        hipLaunchKernelGGL(router_logits_kernel, g1, dim3(64), 0, s, (const uint16_t *)x,
+                           (const uint16_t *)w_router, (const uint16_t *)w_shared_gate, d->T, d->H, d->E,
+                           rows, logits);
+        MOE_TRY(launch_check("moe_route: router_logits_kernel"));
+    }
     auto topk = d->E <= 256 ? topk_kernel<4> : d->E <= 512 ? topk_kernel<8> : d->E <= 1024 ? topk_kernel<16>
                                                                                            : topk_kernel<32>;
     const int tb = d->T < 4 ? 64 * d->T : 256;

@@ -120,6 +120,9 @@ ROUTE_CASES = {
     "prefill_router_zipf": (synth.get("qwen38max_prefill"), 0),
     "fp8_router_sigmoid": (synth.get("glm52_fp8"), 0),
     "tiny_no_renorm": (tiny(renormalize=False, routed_scaling=2.5), 0),
+    # tiled float64 router (T >= 32, H a multiple of 512): ragged token and row tiles
+    "tiled_ragged_gated": (tiny(name="rt", T=300, H=1024, E=200, k=6, shared="gated"), 3),
+    "tiled_min_tokens": (tiny(name="rt32", T=32, H=512, E=130, k=4), 4),
 }
 
 
@@ -145,7 +148,8 @@ def test_route_matches_oracle(dev, M, name):
 # ------------------------------------------------------------------ permutation
 
 @pytest.mark.parametrize("T,k,E", [(1, 1, 1), (1, 10, 512), (4, 2, 8), (64, 8, 256), (513, 10, 512),
-                                   (2000, 16, 2048), (4, 8, 896)])
+                                   (2000, 16, 2048), (4, 8, 896), (7, 10, 512),
+                                   (819, 10, 896), (820, 10, 64)])
 def test_permute_matches_oracle(dev, M, T, k, E):
     rng = np.random.default_rng(T * 131 + k * 7 + E)
     # skewed choice so some experts are empty and some are hot
