@@ -231,9 +231,13 @@ def main():
         log(f"[bench] CPU baseline: oracle on {args.cpu_steps} step(s)")
         cpu = cpu_baseline(cfg, args.cpu_steps)
 
-    dtype = {("mxfp4", "float"): "mxfp4 weights x bf16 activations, f32 accumulate",
-             ("mxfp4", "mxfp4"): "mxfp4 x mxfp4, f32 accumulate",
-             ("fp8b128", "float"): "fp8 e4m3 weights x bf16 activations, f32 accumulate"}[(cfg.wfmt, cfg.act)]
+    # arithmetic type of the dominant products: bf16 dot products on exactly decoded weights
+    # (FLOAT mode), or FP4 x FP4 on the block-scaled MFMA (MX mode); fp32 accumulation
+    dtype = "fp4" if cfg.act == "mxfp4" else "bf16"
+    arith = {("mxfp4", "float"): "mxfp4 weights decoded exactly to bf16 x bf16 activations, fp32 accumulate",
+             ("mxfp4", "mxfp4"): "mxfp4 weights x OCP-MX fp4 activations on the scaled MFMA, fp32 accumulate",
+             ("fp8b128", "float"): "fp8 e4m3 weights decoded exactly to bf16 x bf16 activations, fp32 accumulate"
+             }[(cfg.wfmt, cfg.act)]
     res = {
         "metric": "MoE layer tokens/s; decode HBM GB/s and prefill TFLOP/s as % roofline",
         "value": round(cfg.T / step_s, 2),
@@ -249,7 +253,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "d_model": cfg.d_model, "I": cfg.I, "E": cfg.E,
                    "k": cfg.k, "score": cfg.score, "weights": cfg.wfmt, "activations": cfg.act,
-                   "shared": cfg.shared, "latent": cfg.latent, "instances": R, "token_batches": NB,
+                   "shared": cfg.shared, "latent": cfg.latent, "arith": arith, "instances": R, "token_batches": NB,
                    "graphs": graphs is not None, "distinct_experts_per_step": round(D_mean, 2)},
         "layer": {"bytes_per_step": int(layer_bytes), "flops_per_step": int(layer_flops),
                   "GB/s": round(layer_bytes / step_s / 1e9, 1),
