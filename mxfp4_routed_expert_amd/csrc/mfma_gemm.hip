@@ -2,21 +2,19 @@
 //
 // With MX-quantised activations both operands of every expert product are MXFP4: 32-value
 // E2M1 blocks sharing one E8M0 scale (the format the pages name: rabbit README, opening
-// section and architecture table).  v_mfma_scale_f32_16x16x128_f8f6f4 takes exactly that:
-// lane l supplies 16 bytes (one 32-value block) of row l%16, K-block l/16, and the block's
+// section and architecture table).  v_mfma_scale_f32_32x32x64_f8f6f4 takes exactly that:
+// lane l supplies 16 bytes (one 32-value block) of row l%32, K-block l/32, and the block's
 // scale byte; it accumulates the scaled products in float32.
 //
 // Tile: a workgroup computes 128 rows of one expert (tokens routed to it, in sorted order)
 // by 128 output columns -- of gate AND up for the SwiGLU pair.  Its 4 waves each own a
-// 64 x 64 quarter as 4 x 4 MFMA tiles per matrix.  K advances in steps of 128 values.
-// A step's A rows (gathered token rows), B rows (weight rows) and scale bytes travel from
-// global memory straight into LDS (global_load_lds), laid out lane-major exactly as the
-// MFMA reads its operands; several steps are in flight at once, so the copies of later
-// steps overlap the matrix work of the current one.
-// Epilogue, gate/up: h = silu(g) * u in registers, then OCP-MX quantisation of h per 32
-// columns: the 16 lanes of a DPP row hold 16 consecutive columns of the same token row,
-// so the block maximum is a row reduction and each lane encodes its own two values.
-// Epilogue, down: float32 rows of y.
+// 64 x 64 quarter as 2 x 2 MFMA tiles per matrix.  K advances in steps of 256 values; a
+// step's A rows (gathered token rows), B rows (weight rows) and scale windows travel from
+// global memory straight into LDS (global_load_lds), a whole 128-byte line per row, while
+// the matrix cores work on the previous step.
+// Epilogue, gate/up: h = silu(g) * u, staged through LDS so that each lane owns a row's
+// 32-column block and OCP-MX quantises it alone (block maximum, 16 packed code bytes, one
+// scale byte).  Epilogue, down: float32 rows of y.
 // The grid is persistent (one wave of resident workgroups); each workgroup turns
 // expert_offsets into a prefix of row tiles per expert in LDS and walks its share of the
 // (row tile, column tile) items, so no workgroup is launched for tiles that do not exist.
@@ -51,20 +49,9 @@ struct GemmParams {
     uint8_t *os;                   // gate/up: h scales [R][N/32]
 };
 
-MOE_DEV float row16_max(float v) {
-    // max over the 16 lanes of a DPP row (quad xor 1, quad xor 2, half mirror, mirror)
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));
-    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));
-    return v;
-}
-MOE_DEV uint32_t row16_max_u32(uint32_t v) {
-    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));
-    return v;
+// silu(g) = g / (1 + e^-g) with the hardware exp2 and reciprocal (about 2 ulp).
+MOE_DEV float silu_fast(float g) {
+    return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504088896341f));
 }
 
 MOE_DEV uint32_t e2m1_code_of(float a) {   // same midpoint rule as the activation quantiser
@@ -72,23 +59,26 @@ MOE_DEV uint32_t e2m1_code_of(float a) {   // same midpoint rule as the activati
            (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
 }
 
-#ifndef MOE_GEMM_STAGES
-#define MOE_GEMM_STAGES 4   // K-steps resident in LDS for gate/up (one fewer for down)
-#endif
-constexpr int kFrag = 1024;                    // one MFMA operand fragment: 64 lanes x 16 B
 
-// Asynchronous global -> LDS copy (global_load_lds): lane l's bytes land at dst + 16 l
-// (dst is the same in every lane; the instruction takes it from M0).  Written as asm so
-// that the compiler does not add a wait for all copies in flight before every LDS read;
-// the pipeline below waits for exactly the copies it needs.  The instruction has no
-// register result, so nothing the compiler allocates is written when it completes.
-MOE_DEV void dma16(const void *src, const unsigned char *dst) {
+// Asynchronous global -> LDS copy (global_load_lds): lane l reads base + voff (+ OFF) and
+// its bytes land at dst + l * size (base and dst are the same in every lane; the
+// instruction takes dst from M0).  Written as asm so that the compiler does not add a
+// wait for all copies in flight before every LDS read; the pipeline below waits for
+// exactly the copies it needs.  The instruction has no register result, so nothing the
+// compiler allocates is written when it completes.
+template <int OFF>
+MOE_DEV void dma16(const uint8_t *base, uint32_t voff, const unsigned char *dst) {
     const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(l) : "memory");
+    asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2" ::"v"(voff), "s"(base), "i"(OFF), "{m0}"(l) : "memory");
 }
-MOE_DEV void dma4(const void *src, const unsigned char *dst) {
+MOE_DEV void dma4(const uint8_t *base, uint32_t voff, const unsigned char *dst) {
     const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-    asm volatile("global_load_lds_dword %0, off" ::"v"(src), "{m0}"(l) : "memory");
+    asm volatile("global_load_lds_dword %0, %1" ::"v"(voff), "s"(base), "{m0}"(l) : "memory");
+}
+MOE_DEV const uint8_t *uniform_ptr(const void *q) {
+    const uint64_t v = (uint64_t)(uintptr_t)q;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint8_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
 // Wait until at most N of this wave's memory operations are outstanding, finish its LDS
@@ -148,21 +138,27 @@ MOE_DEV int tile_expert(const int *tp, int E, int mt) {
     return c * 32 + __ffsll((long long)m2) - 1;
 }
 
+// K-step of 256 values: each operand row contributes one whole 128-byte line per step.
+constexpr int kGStep = 256;
+constexpr int kRowB = kGStep / 2;              // code bytes per row per step
+constexpr int kScB = 16;                       // LDS bytes per scale row per step (window)
+
 template <bool PAIR>
-constexpr int gemm_stages() { return PAIR ? MOE_GEMM_STAGES : MOE_GEMM_STAGES - 1; }
+constexpr int gemm_stages() { return PAIR ? 2 : 3; }   // steps resident in LDS
 
 template <bool PAIR, bool ROUTED>
 __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
     constexpr int NM = PAIR ? 2 : 1;
     constexpr int kStages = gemm_stages<PAIR>();
-    constexpr int kA = 8 * kFrag;                      // A: 8 fragments of 16 rows
-    constexpr int kB = NM * 8 * kFrag;                 // B: 8 fragments per matrix
+    constexpr int kA = kGBM * kRowB;                   // A codes of a step
+    constexpr int kB = NM * kGBN * kRowB;              // B codes of a step
     constexpr int kSRows = kGBM + NM * kGBN;           // scale rows: A, then each matrix's
-    constexpr int kStage = kA + kB + kSRows * 8;       // each scale row: two aligned dwords
-    constexpr int kSDma = kSRows * 2 / (64 * 4);       // scale dword copies per wave per stage
-    constexpr int kOps = 2 + 2 * NM + kSDma;           // memory operations per wave per stage
-    static_assert(kSRows * 2 == kSDma * 64 * 4, "scale rows must fill whole wave copies");
-    static_assert(kStages >= 2 && (kStages - 2) * kOps <= 63, "vmcnt limit");
+    constexpr int kStage = kA + kB + kSRows * kScB;
+    constexpr int kCodeCopies = (kGBM + NM * kGBN) / 8 / 4;   // 1-KB copies (8 rows) per wave
+    constexpr int kScCopies = kSRows / 16 / 4;         // scale copies (16 rows x 4 dwords) per wave
+    constexpr int kOps = kCodeCopies + kScCopies;      // memory operations per wave per stage
+    static_assert(kSRows % 64 == 0 && (kGBM + NM * kGBN) % 32 == 0, "copy split");
+    static_assert((kStages - 2) * kOps <= 63, "vmcnt limit");
     __shared__ __align__(16) unsigned char smem[kStages * kStage];
     __shared__ uint8_t s_off[kSRows];
     __shared__ int s_tp[ROUTED ? MOE_MAX_EXPERTS : 1];
@@ -171,22 +167,34 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
     const int NT = (p.N + kGBN - 1) / kGBN;
     const int total_mt = ROUTED ? build_tile_prefix(p.offsets, p.E, p.R, s_tp, s_wave) : (p.T + kGBM - 1) / kGBM;
     const int items = total_mt * NT;
-    for (int item = blockIdx.x; item < items; item += gridDim.x) {
-        const int mt = item / NT;
-        int e = 0, tile = mt, row0 = 0, M = p.T;
+    // Items are ordered expert by expert, then by column tile, then by row tile, and each
+    // round of G workgroups hands XCD x (workgroups x, x+8, ...) a contiguous run of G/8
+    // items: the row tiles of one expert that share a column tile of weights run at the
+    // same time on the same XCD, so those weight bytes come from that XCD's L2.
+    const int G = gridDim.x;
+    const int slot = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+    const int lane = lane_id(), wave = wave_id();
+    const int wm = wave >> 1, wn = wave & 1;           // output quarter of this wave
+    const int hr = lane & 31, hb = lane >> 5;          // MFMA operand row / K-block of this lane
+    const int Kh = p.K / 2, Kb = p.K / 32;
+    const int S = (Kb + 7) / 8;                        // K-steps of 256 values
+
+    for (int item = slot; item < items; item += G) {
+        int e = 0, tile = 0, nt = 0, row0 = 0, M = p.T;
         if constexpr (ROUTED) {
-            e = tile_expert(s_tp, p.E, mt);
-            tile = mt - (e > 0 ? s_tp[e - 1] : 0);
+            e = tile_expert(s_tp, p.E, item / NT);
+            const int tpx = e > 0 ? s_tp[e - 1] : 0, te = s_tp[e] - tpx;
+            const int r = item - NT * tpx;
+            nt = r / te;
+            tile = r - nt * te;
             row0 = p.offsets[e];
             M = p.offsets[e + 1] - row0;
+        } else {
+            nt = item / total_mt;
+            tile = item - nt * total_mt;
         }
         const int m0 = tile * kGBM;
-        const int n0 = (item - mt * NT) * kGBN;
-        const int lane = lane_id(), wave = wave_id();
-        const int wm = wave >> 1, wn = wave & 1;       // output quarter of this wave
-        const int fr = lane & 15, fg = lane >> 4;      // fragment row / K-block of this lane
-        const int Kh = p.K / 2, Kb = p.K / 32;
-        const int S = (Kb + 3) / 4;                    // K-steps of 128 values
+        const int n0 = nt * kGBN;
 
         // Source row of A row r of the tile (rows past the expert's end repeat a valid row).
         auto a_src_row = [&](int r) {
@@ -194,176 +202,243 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
             if (p.gather) src = p.sorted_pairs[src] / p.k;
             return min(max(src, 0), p.n_arows - 1);
         };
-        auto b_src_row = [&](int n) { return (size_t)e * p.N + min(n0 + n, p.N - 1); };
+        auto b_src_row = [&](int n) { return min(n0 + n, p.N - 1); };
 
-        // ---- copy assignment.  Wave w copies fragments 2w and 2w+1 of A and of each B matrix:
-        // lane l fetches row 16f + l%16, K-block l/16 of the step, so LDS holds every fragment
-        // in the order the MFMA reads it (lane l at byte 16 l).
-        const uint8_t *a_row[2], *b_row[NM][2];
-    #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int r = 16 * (2 * wave + u) + fr;
-            a_row[u] = p.a + (size_t)a_src_row(r) * Kh + fg * 16;
-    #pragma unroll
-            for (int mi = 0; mi < NM; ++mi) b_row[mi][u] = p.w[mi] + b_src_row(r) * Kh + fg * 16;
+        // ---- copies.  A step's codes sit row-major in LDS, 128 bytes per row, with the
+        // 16-byte chunk c of row r stored at chunk position c ^ ((r >> 1) & 7): one 1-KB copy
+        // moves 8 rows, 8 lanes per row fetching one 128-byte line, and an MFMA operand read
+        // (rows r .. r+15 at one chunk, served 16 lanes per LDS cycle) hits 16 distinct
+        // 16-byte bank groups.  Wave w copies rows 32w .. 32w+31 of A and of each B matrix.
+        const int eu = __builtin_amdgcn_readfirstlane(e);
+        const uint8_t *a_base = uniform_ptr(p.a);
+        const uint8_t *b_base[NM], *bs_base[NM];
+#pragma unroll
+        for (int mi = 0; mi < NM; ++mi) {
+            b_base[mi] = uniform_ptr(p.w[mi] + (size_t)eu * p.N * Kh);
+            bs_base[mi] = uniform_ptr(p.ws[mi] + (size_t)eu * p.N * Kb);
         }
-        // Scale row q's four bytes of a step start at a fixed misalignment o within an aligned
-        // dword; copying that dword and the next gives an 8-byte window holding them.  The
-        // second dword is fetched only when a byte of the step lies in it (otherwise the first
-        // is fetched again), so every fetched dword holds a byte of the array.
-        const uint8_t *sc_row[kSDma];
-        int sc_part[kSDma];
-    #pragma unroll
-        for (int i = 0; i < kSDma; ++i) {
-            const int d = (kSDma * wave + i) * 64 + lane;
-            const int q = d >> 1;
-            sc_part[i] = d & 1;
-            const uint8_t *row;
-            if (q < kGBM) row = p.as + (size_t)a_src_row(q) * Kb;
-            else if (q < kGBM + kGBN) row = p.ws[0] + b_src_row(q - kGBM) * Kb;
-            else row = p.ws[NM - 1] + b_src_row(q - kGBM - kGBN) * Kb;
-            sc_row[i] = row;
-            if (sc_part[i] == 0) s_off[q] = (uint8_t)((uintptr_t)row & 3u);
+        const int cr = lane >> 3;                          // copy lane: row within the 8
+        uint32_t a_off[4], b_off[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            a_off[t] = (uint32_t)a_src_row(32 * wave + 8 * t + cr) * Kh;
+            b_off[t] = (uint32_t)b_src_row(32 * wave + 8 * t + cr) * Kh;
+        }
+        // Scale rows: 4 lanes per row, dword d of the row's window starting at the aligned
+        // dword that holds the step's first byte.  A dword is fetched only when it holds a
+        // byte of the step (otherwise the window's first dword is fetched again), so every
+        // fetched dword lies inside the array.
+        const int sd = lane & 3;
+        const uint8_t *sc_base[kScCopies];
+        uint32_t sc_off[kScCopies];
+#pragma unroll
+        for (int i = 0; i < kScCopies; ++i) {
+            const int q0 = __builtin_amdgcn_readfirstlane(16 * (kScCopies * wave + i));   // first row of the copy
+            const int q = q0 + (lane >> 2);
+            sc_base[i] = q0 < kGBM ? uniform_ptr(p.as) : bs_base[q0 < kGBM + kGBN ? 0 : NM - 1];
+            sc_off[i] = q < kGBM ? (uint32_t)a_src_row(q) * Kb : (uint32_t)b_src_row((q - kGBM) & (kGBN - 1)) * Kb;
+            if (sd == 0) s_off[q] = (uint8_t)((uintptr_t)(sc_base[i] + sc_off[i]) & 3u);
         }
         __syncthreads();
-        // Consumer side: LDS byte of each scale this lane feeds to the MFMA (step-relative).
-        int sa_at[4], sb_at[NM][4];
-    #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int r = wm * 64 + 16 * i + fr;
-            sa_at[i] = kA + kB + r * 8 + s_off[r] + fg;
-    #pragma unroll
+        uint32_t sc_mis[kScCopies];
+#pragma unroll
+        for (int i = 0; i < kScCopies; ++i) sc_mis[i] = s_off[16 * (kScCopies * wave + i) + (lane >> 2)];
+        // Consumer side: LDS byte (step-relative) of block 0 of each scale row this lane feeds.
+        int sa_at[2], sb_at[NM][2];
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int r = 32 * (2 * wm + i) + hr;
+            sa_at[i] = kA + kB + r * kScB + s_off[r] + hb;
+#pragma unroll
             for (int mi = 0; mi < NM; ++mi) {
-                const int q = kGBM + mi * kGBN + wn * 64 + 16 * i + fr;
-                sb_at[mi][i] = kA + kB + q * 8 + s_off[q] + fg;
+                const int q = kGBM + mi * kGBN + 32 * (2 * wn + i) + hr;
+                sb_at[mi][i] = kA + kB + q * kScB + s_off[q] + hb;
             }
         }
 
-        // Issue the copies of step s into its stage buffer (steps past the end re-fetch the
-        // last step; that data is never read).
+        // Issue the copies of step s into its stage buffer.  Steps past the end re-fetch the
+        // last step (never read); K-blocks past the end of a row are clamped to its last one.
         auto issue = [&](int s) {
             const int sc = min(s, S - 1);
             unsigned char *st = smem + (s % kStages) * kStage;
-            const size_t boff = (size_t)min(4 * sc + fg, Kb - 1) * 16 - (size_t)fg * 16;
-    #pragma unroll
-            for (int u = 0; u < 2; ++u) dma16(a_row[u] + boff, st + (2 * wave + u) * kFrag);
-    #pragma unroll
-            for (int mi = 0; mi < NM; ++mi)
-    #pragma unroll
-                for (int u = 0; u < 2; ++u) dma16(b_row[mi][u] + boff, st + kA + (mi * 8 + 2 * wave + u) * kFrag);
-            const int nvalid = min(4, Kb - 4 * sc);
-    #pragma unroll
-            for (int i = 0; i < kSDma; ++i) {
-                const uintptr_t a = (uintptr_t)(sc_row[i] + 4 * sc);
-                const uintptr_t o = a & 3u;
-                const uintptr_t al = a - o + ((sc_part[i] && o + nvalid > 4) ? 4u : 0u);
-                dma4((const void *)al, st + kA + kB + (kSDma * wave + i) * 256);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int cc = (lane & 7) ^ ((4 * t + (cr >> 1)) & 7);   // chunk this lane fetches
+                const uint32_t ko = (uint32_t)min(8 * sc + cc, Kb - 1) * 16;
+                dma16<0>(a_base, a_off[t] + ko, st + (32 * wave + 8 * t) * kRowB);
+#pragma unroll
+                for (int mi = 0; mi < NM; ++mi)
+                    dma16<0>(b_base[mi], b_off[t] + ko, st + kA + (mi * kGBN + 32 * wave + 8 * t) * kRowB);
+            }
+            const int last = min(8, Kb - 8 * sc) - 1;      // last block of the step in the row
+#pragma unroll
+            for (int i = 0; i < kScCopies; ++i) {
+                const uint32_t o = sc_mis[i];
+                const uint32_t need = (o + (uint32_t)last) >> 2;   // dwords 0..need hold bytes of the step
+                const uint32_t v = sc_off[i] + 8u * sc - o + ((uint32_t)sd <= need ? 4u * sd : 0u);
+                dma4(sc_base[i], v, st + kA + kB + (16 * (kScCopies * wave + i)) * kScB);
             }
         };
 
-        f32x4 acc[NM][4][4];
-    #pragma unroll
+        // Operands of one 64-value K-quarter q of a step: chunk 2q + hb of each row.
+        struct Quarter {
+            u32x4 a[2], b[NM][2];
+            int sa[2], sb[NM][2];
+        };
+        auto read = [&](const unsigned char *st, int q, Quarter &f) {
+            const int c = 2 * q + hb;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const int r = 32 * (2 * wm + i) + hr;
+                f.a[i] = *(const u32x4 *)(st + r * kRowB + ((c ^ ((r >> 1) & 7)) << 4));
+                f.sa[i] = st[sa_at[i] + 2 * q];
+#pragma unroll
+                for (int mi = 0; mi < NM; ++mi) {
+                    const int n = mi * kGBN + 32 * (2 * wn + i) + hr;
+                    f.b[mi][i] = *(const u32x4 *)(st + kA + n * kRowB + ((c ^ ((n >> 1) & 7)) << 4));
+                    f.sb[mi][i] = st[sb_at[mi][i] + 2 * q];
+                }
+            }
+        };
+        // K-blocks past the end of K (last step only): zero A codes, unit scales.
+        auto kill = [&](int s, int q, Quarter &f) {
+            if (8 * s + 2 * q + hb < Kb) return;
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                f.a[i] = u32x4{0, 0, 0, 0};
+                f.sa[i] = 127;
+#pragma unroll
+                for (int mi = 0; mi < NM; ++mi) f.sb[mi][i] = 127;
+            }
+        };
+
+        f32x16 acc[NM][2][2];
+#pragma unroll
         for (int mi = 0; mi < NM; ++mi)
-    #pragma unroll
-            for (int i = 0; i < 4; ++i)
-    #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[mi][i][j] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-        // One K-step of matrix work from stage buffer st.  TAIL: the last step when K is not a
-        // multiple of 128 -- K-blocks past the end get zero A codes and unit scales.
-        auto compute = [&](const unsigned char *st, auto tail) {
-            constexpr bool TAIL = decltype(tail)::value;
-            const bool dead = TAIL && 4 * (S - 1) + fg >= Kb;
-            i32x8_t af[4];
-            int asc[4];
-    #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const u32x4 v = *(const u32x4 *)(st + (wm * 4 + i) * kFrag + lane * 16);
-                af[i] = i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-                asc[i] = (int)st[sa_at[i]];
-                if constexpr (TAIL) {
-                    af[i] = dead ? i32x8_t{0, 0, 0, 0, 0, 0, 0, 0} : af[i];
-                    asc[i] = dead ? 127 : asc[i];
-                }
-            }
-    #pragma unroll
-            for (int mi = 0; mi < NM; ++mi) {
-    #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const u32x4 v = *(const u32x4 *)(st + kA + (mi * 8 + wn * 4 + j) * kFrag + lane * 16);
-                    const i32x8_t bf = i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
-                    int bsc = (int)st[sb_at[mi][j]];
-                    if constexpr (TAIL) bsc = dead ? 127 : bsc;
-    #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        acc[mi][i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(af[i], bf, acc[mi][i][j], 4, 4, 0,
-                                                                                       asc[i], 0, bsc);
-                }
-            }
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) acc[mi][i][j][v] = 0.0f;
+        auto mma = [&](const Quarter &f) {
+#pragma unroll
+            for (int mi = 0; mi < NM; ++mi)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int i = 0; i < 2; ++i) {
+                        const u32x4 av = f.a[i], bv = f.b[mi][j];
+                        acc[mi][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            i32x8_t{(int)av[0], (int)av[1], (int)av[2], (int)av[3], 0, 0, 0, 0},
+                            i32x8_t{(int)bv[0], (int)bv[1], (int)bv[2], (int)bv[3], 0, 0, 0, 0}, acc[mi][i][j], 4, 4,
+                            0, f.sa[i], 0, f.sb[mi][j]);
+                    }
         };
 
-    #pragma unroll
-        for (int s = 0; s < kStages - 1; ++s) issue(s);
-        const int S_full = (Kb & 3) ? S - 1 : S;           // steps with four whole K-blocks
-        for (int s = 0; s < S; ++s) {
-            // this wave's copies of step s are done once at most the later stages' are pending
+        // Pipeline: kStages steps in LDS.  At step s, stage s must have landed (the later
+        // kStages-2 may still be in flight); the barrier also tells every wave that step s-1's
+        // buffer has been read, so step s+kStages-1 can refill it.  Within a step the next
+        // quarter's operands load while the current quarter's MFMAs run.
+        auto step = [&](int s, auto last) {
             wait_vm_and_barrier<(kStages - 2) * kOps>();
-            issue(s + kStages - 1);                        // into the buffer read at step s-1
+            issue(s + kStages - 1);
             const unsigned char *st = smem + (s % kStages) * kStage;
-            if (s < S_full) compute(st, std::false_type{});
-            else compute(st, std::true_type{});
-        }
-        wait_vm_and_barrier<0>();                          // no copy in flight at exit
+            Quarter f0, f1;
+            read(st, 0, f0);
+#pragma unroll
+            for (int q = 0; q < 4; q += 2) {
+                read(st, q + 1, f1);
+                if constexpr (decltype(last)::value) kill(s, q, f0);
+                mma(f0);
+                if (q + 2 < 4) read(st, q + 2, f0);
+                if constexpr (decltype(last)::value) kill(s, q + 1, f1);
+                mma(f1);
+            }
+        };
+#pragma unroll
+        for (int s = 0; s < kStages - 1; ++s) issue(s);
+        for (int s = 0; s < S - 1; ++s) step(s, std::false_type{});
+        step(S - 1, std::true_type{});
+        wait_vm_and_barrier<0>();                          // no copy in flight past this point
 
-        // ---- epilogue.  Lane holds C[4*fg + v][fr] of each 16x16 tile.
-    #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-    #pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                const int r = m0 + wm * 64 + 16 * i + 4 * fg + v;      // row within the expert
-                const bool row_ok = r < M;
-                const size_t orow = (size_t)(row0 + (row_ok ? r : 0));
-                float val[4];
-    #pragma unroll
-                for (int j = 0; j < 4; ++j) val[j] = PAIR ? silu(acc[0][i][j][v]) * acc[NM - 1][i][j][v] : acc[0][i][j][v];
-                // float32 output (y, or h when requested)
+        // ---- epilogue.  Lane l holds C[8(v/4) + 4(l/32) + v%4][l%32] of each 32x32 tile.
+        if constexpr (!PAIR) {
+            // y rows: each (tile, v) is 32 consecutive float32 columns of one row per half-wave
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) {
+                    const int r = m0 + 32 * (2 * wm + i) + 8 * (v >> 2) + 4 * hb + (v & 3);
+                    if (r >= M) continue;
+                    const size_t orow = (size_t)(row0 + r);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const int n = n0 + 32 * (2 * wn + j) + hr;
+                        if (n < p.N) p.out[orow * p.N + n] = acc[0][i][j][v];
+                    }
+                }
+        } else {
+            // h = silu(g) * u goes through LDS (the stage buffers are idle now): the wave writes
+            // its 64 x 64 quarter row-major (row stride 68 floats against bank conflicts), then
+            // lane L owns row L of the quarter and OCP-MX quantises its two 32-column blocks
+            // alone: block maximum, 32 codes packed into 16 bytes, one scale byte.
+            constexpr int kLd = 68;
+            float *hq_lds = (float *)smem + wave * (64 * kLd);
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v) {
+                        const int r = 32 * i + 8 * (v >> 2) + 4 * hb + (v & 3);
+                        hq_lds[r * kLd + 32 * j + hr] = silu_fast(acc[0][i][j][v]) * acc[1][i][j][v];
+                    }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");    // LDS is in order within a wave
+            const int r = m0 + 64 * wm + lane;                        // row within the expert
+            const bool row_ok = r < M;
+            const size_t orow = (size_t)(row0 + (row_ok ? r : 0));
+            const bool vec_ok = (((uintptr_t)p.oq) & 15u) == 0;
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                const int nb = n0 + 64 * wn + 32 * jb;                // first column of the block
+                f32x4 h[8];
+#pragma unroll
+                for (int q = 0; q < 8; ++q) h[q] = *(const f32x4 *)(hq_lds + lane * kLd + 32 * jb + 4 * q);
+                if (!row_ok || nb >= p.N) continue;
                 if (p.out) {
-    #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int n = n0 + wn * 64 + 16 * j + fr;
-                        if (row_ok && n < p.N) p.out[orow * p.N + n] = val[j];
-                    }
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) *(f32x4 *)(p.out + orow * p.N + nb + 4 * q) = h[q];
                 }
-                if constexpr (PAIR) {
-                    // MX quantisation per 32 columns: tiles (j, j+1) = columns [32q, 32q+32) of the quarter
-    #pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        const float x0 = val[2 * q], x1 = val[2 * q + 1];
-                        const uint32_t a0 = __float_as_uint(x0) & 0x7fffffffu, a1 = __float_as_uint(x1) & 0x7fffffffu;
-                        const uint32_t amax = row16_max_u32(max(a0, a1));
-                        uint32_t c0 = 0, c1 = 0, sbyte = 255;
-                        if (amax < 0x7f800000u) {
-                            const int ebits = (int)(amax >> 23);
-                            int X = ebits == 0 ? -127 : ebits - 127 - 2;
-                            X = X < -127 ? -127 : (X > 127 ? 127 : X);
-                            const float inv = __uint_as_float((uint32_t)(127 - X) << 23);
-                            c0 = e2m1_code_of(fabsf(x0) * inv) | ((__float_as_uint(x0) >> 31) << 3);
-                            c1 = e2m1_code_of(fabsf(x1) * inv) | ((__float_as_uint(x1) >> 31) << 3);
-                            sbyte = (uint32_t)(X + 127);
+                uint32_t amax = 0;
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) amax = max(amax, __float_as_uint(h[q][c]) & 0x7fffffffu);
+                uint32_t w[4] = {0, 0, 0, 0}, sbyte = 255;
+                if (amax < 0x7f800000u) {
+                    const int ebits = (int)(amax >> 23);
+                    int X = ebits == 0 ? -127 : ebits - 127 - 2;
+                    X = X < -127 ? -127 : (X > 127 ? 127 : X);
+                    const float inv = __uint_as_float((uint32_t)(127 - X) << 23);
+#pragma unroll
+                    for (int q = 0; q < 8; ++q)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            const float x = h[q][c];
+                            const uint32_t code = e2m1_code_of(fabsf(x) * inv) | ((__float_as_uint(x) >> 31) << 3);
+                            w[q >> 1] |= code << (4 * (4 * (q & 1) + c));
                         }
-                        // element n of the 32-block: tile 2q holds n = fr, tile 2q+1 holds n = 16 + fr;
-                        // byte b = (n/2) packs elements 2b (low nibble) and 2b+1 (high nibble)
-                        const uint32_t o0 = (uint32_t)__builtin_amdgcn_mov_dpp((int)c0, 0xB1, 0xF, 0xF, false);
-                        const uint32_t o1 = (uint32_t)__builtin_amdgcn_mov_dpp((int)c1, 0xB1, 0xF, 0xF, false);
-                        const int nb = n0 + wn * 64 + 32 * q;              // first column of the block
-                        if (row_ok && nb < p.N && (fr & 1) == 0) {
-                            uint8_t *dst = p.oq + orow * (size_t)(p.N / 2) + nb / 2;
-                            dst[fr / 2] = (uint8_t)(c0 | (o0 << 4));
-                            dst[8 + fr / 2] = (uint8_t)(c1 | (o1 << 4));
-                        }
-                        if (row_ok && nb < p.N && fr == 0) p.os[orow * (size_t)(p.N / 32) + nb / 32] = (uint8_t)sbyte;
-                    }
+                    sbyte = (uint32_t)(X + 127);
                 }
+                uint8_t *dst = p.oq + orow * (size_t)(p.N / 2) + nb / 2;
+                if (vec_ok) {
+                    *(u32x4 *)dst = u32x4{w[0], w[1], w[2], w[3]};
+                } else {
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) dst[q] = (uint8_t)(w[q >> 2] >> (8 * (q & 3)));
+                }
+                p.os[orow * (size_t)(p.N / 32) + nb / 32] = (uint8_t)sbyte;
             }
         }
     }
