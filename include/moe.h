@@ -115,6 +115,19 @@ moe_status moe_permute(int32_t T, int32_t k, int32_t E, const int32_t *topk_ids,
 size_t moe_permute_workspace(int32_t T, int32_t k, int32_t E);
 
 /*
+ * moe_route_permute -- moe_route followed by moe_permute of its topk_ids, in one call.
+ * Arguments and results are exactly those of the two calls (same layouts, same errors,
+ * same workspace: moe_route_workspace(desc) bytes).  With T <= 4 and T*k <= 64 (decode)
+ * the permutation is written by the top-k kernel itself, one launch fewer.
+ * (Routing and per-expert grouping as in moe_route and moe_permute above.)
+ */
+moe_status moe_route_permute(const moe_route_desc *desc, const void *x, const void *w_router,
+                             const float *logit_bias, const float *select_bias,
+                             const void *w_shared_gate, int32_t *topk_ids, float *topk_w,
+                             float *shared_gate, int32_t *expert_offsets, int32_t *sorted_pairs,
+                             int32_t *pair_to_row, void *ws, size_t ws_bytes, moe_stream stream);
+
+/*
  * Expert weights for E experts (or one shared expert), stacked along the expert axis.
  *   MOE_W_MXFP4:          gate, up: codes uint8 [E][d_ff][d_model/2], scales uint8 E8M0
  *                         [E][d_ff][d_model/32]; down: codes [E][d_model][d_ff/2], scales

@@ -33,7 +33,7 @@ class MoeError(RuntimeError):
 def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"HIP library not built: {LIB_PATH} is missing "
-                          "(run `python -m mxfp4_routed_expert_amd.build`)")
+                          "(run `python mxfp4_routed_expert_amd/build.py`)")
     return ctypes.CDLL(LIB_PATH)
 
 
@@ -64,6 +64,7 @@ _sig("moe_abi_version", _i32)
 _sig("moe_route", _i32, ctypes.POINTER(RouteDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p)
 _sig("moe_route_workspace", _sz, ctypes.POINTER(RouteDesc))
 _sig("moe_permute", _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p)
+_sig("moe_route_permute", _i32, ctypes.POINTER(RouteDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p)
 _sig("moe_permute_workspace", _sz, _i32, _i32, _i32)
 _sig("moe_expert_ffn", _i32, ctypes.POINTER(ExpertWeightsC), _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p, _sz, _p)
 _sig("moe_expert_ffn_workspace", _sz, ctypes.POINTER(ExpertWeightsC), _i32, _i32, _i32)
@@ -76,7 +77,8 @@ _sig("moe_dense_bf16", _i32, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p)
 _sig("moe_dequant", _i32, _i32, _i32, _i32, _p, _p, _p, _p)
 _sig("moe_mx_quantize", _i32, _i32, _i32, _p, _i32, _p, _p, _p)
 
-EXPORTS = ["moe_route", "moe_route_workspace", "moe_permute", "moe_permute_workspace", "moe_expert_ffn",
+EXPORTS = ["moe_route", "moe_route_workspace", "moe_permute", "moe_permute_workspace", "moe_route_permute",
+           "moe_expert_ffn",
            "moe_expert_ffn_workspace", "moe_expert_gateup", "moe_expert_gateup_workspace", "moe_expert_down",
            "moe_combine", "moe_dense_bf16", "moe_dequant", "moe_mx_quantize", "moe_last_error",
            "moe_abi_version"]
@@ -162,6 +164,36 @@ def moe_permute(topk_ids, E, out=None):
         offs, sp, p2r = out
     check(lib.moe_permute(T, k, E, _ptr(topk_ids), _ptr(offs), _ptr(sp), _ptr(p2r), None, 0, _stream()))
     return offs, sp, p2r
+
+
+def moe_route_permute(x, w_router, k, score="softmax", renormalize=True, routed_scaling=1.0, logit_bias=None,
+                      select_bias=None, w_shared_gate=None, out=None, ws=None):
+    """moe_route then moe_permute in one call.  Returns (topk_ids, topk_w, shared_gate or None,
+    expert_offsets, sorted_pairs, pair_to_row)."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    _need(x, torch.bfloat16, "x")
+    _need(w_router, torch.bfloat16, "w_router", (E, H))
+    _need(logit_bias, torch.float32, "logit_bias", (E,))
+    _need(select_bias, torch.float32, "select_bias", (E,))
+    _need(w_shared_gate, torch.bfloat16, "w_shared_gate", (H,))
+    d = RouteDesc(T, H, E, k, SCORE[score], 1 if renormalize else 0, routed_scaling)
+    dev = x.device
+    if out is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        sg = torch.empty((T,), dtype=torch.float32, device=dev) if w_shared_gate is not None else None
+        offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+        sp = torch.empty((T * k,), dtype=torch.int32, device=dev)
+        p2r = torch.empty((T * k,), dtype=torch.int32, device=dev)
+    else:
+        ids, w, sg, offs, sp, p2r = out
+    if ws is None:
+        ws = _workspace(lib.moe_route_workspace(ctypes.byref(d)), dev)
+    check(lib.moe_route_permute(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias),
+                                _ptr(w_shared_gate), _ptr(ids), _ptr(w), _ptr(sg), _ptr(offs), _ptr(sp), _ptr(p2r),
+                                _ptr(ws), ws.numel(), _stream()))
+    return ids, w, sg, offs, sp, p2r
 
 
 # ------------------------------------------------------------------ experts

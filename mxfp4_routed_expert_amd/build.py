@@ -1,6 +1,6 @@
 """Build the HIP library libmoe.so in-tree for gfx950 (MI355X).
 
-    python -m mxfp4_routed_expert_amd.build [-j N]
+    python mxfp4_routed_expert_amd/build.py [-j N]
 
 Each .hip source under csrc/ is compiled to an object with hipcc, then linked into a
 shared library next to this file.  Packed-FP32 instructions are disabled in all device

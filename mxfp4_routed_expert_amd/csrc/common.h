@@ -117,6 +117,40 @@ MOE_DEV int wave_nth_nonempty(const int32_t *offsets, int E, int slot) {
     return -1;
 }
 
+// Token -> expert permutation of few pairs (P <= 64) by one workgroup of nthreads threads;
+// sid[0..P) in LDS holds the pairs' expert ids, already set to -1 where outside [0, E).
+// The stable rank of pair p is the number of valid pairs q with (id_q, q) < (id_p, p);
+// expert e's first row is the number of valid ids below e.  Needs a barrier between the
+// writes of sid and the call; ends without one.
+MOE_DEV void small_permutation(const int *sid, int P, int E, int32_t *offsets, int32_t *sorted, int32_t *p2r,
+                               int tid, int nthreads) {
+    int nvalid = 0;
+    for (int q = 0; q < P; ++q) nvalid += sid[q] >= 0;
+    for (int pp = tid; pp < P; pp += nthreads) {
+        const int me = sid[pp];
+        if (me < 0) {
+            p2r[pp] = -1;
+        } else {
+            int r = 0;
+            for (int q = 0; q < P; ++q) {
+                const int o = sid[q];
+                r += o >= 0 && (o < me || (o == me && q < pp));
+            }
+            sorted[r] = pp;
+            p2r[pp] = r;
+        }
+    }
+    for (int e = tid; e <= E; e += nthreads) {
+        int c = 0;
+        for (int q = 0; q < P; ++q) {
+            const int o = sid[q];
+            c += o >= 0 && o < e;
+        }
+        offsets[e] = c;
+    }
+    for (int r = nvalid + tid; r < P; r += nthreads) sorted[r] = -1;
+}
+
 }  // namespace moe
 
 // ------------------------------------------------------------------ host side

@@ -77,9 +77,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__
     }
 }
 
-// Few pairs (decode): P <= 64.  The stable rank of pair p is the number of valid pairs q
-// with (id_q, q) < (id_p, p); expert e's first row is the number of valid ids below e.
-// Same results as the counting sort, one barrier, no scan.
+// Few pairs (decode): P <= 64, ranks by counting (small_permutation).  Same results as
+// the counting sort, one barrier, no scan.
 constexpr int kPermSmallP = 64;
 
 __global__ __launch_bounds__(256) void permute_small_kernel(const int32_t *__restrict__ ids, int P, int E,
@@ -87,42 +86,13 @@ __global__ __launch_bounds__(256) void permute_small_kernel(const int32_t *__res
                                                             int32_t *__restrict__ sorted,
                                                             int32_t *__restrict__ p2r) {
     __shared__ int sid[kPermSmallP];
-    __shared__ int s_nvalid;
     const int tid = threadIdx.x;
     if (tid < kPermSmallP) {
         int e = tid < P ? ids[tid] : -1;
         sid[tid] = (e >= 0 && e < E) ? e : -1;
     }
     __syncthreads();
-    if (tid == 0) {
-        int n = 0;
-        for (int q = 0; q < P; ++q) n += sid[q] >= 0;
-        s_nvalid = n;
-    }
-    if (tid < P) {
-        const int me = sid[tid];
-        if (me < 0) {
-            p2r[tid] = -1;
-        } else {
-            int r = 0;
-            for (int q = 0; q < P; ++q) {
-                const int o = sid[q];
-                r += o >= 0 && (o < me || (o == me && q < tid));
-            }
-            sorted[r] = tid;
-            p2r[tid] = r;
-        }
-    }
-    for (int e = tid; e <= E; e += blockDim.x) {
-        int c = 0;
-        for (int q = 0; q < P; ++q) {
-            const int o = sid[q];
-            c += o >= 0 && o < e;
-        }
-        offsets[e] = c;
-    }
-    __syncthreads();
-    for (int r = s_nvalid + tid; r < P; r += blockDim.x) sorted[r] = -1;
+    small_permutation(sid, P, E, offsets, sorted, p2r, tid, blockDim.x);
 }
 
 // Many pairs (prefill): a bitonic sort of the unique keys (expert << s) | p in LDS by one

@@ -16,44 +16,50 @@ namespace moe {
 namespace {
 
 constexpr int kRouterTB = 8;      // tokens per wave
-constexpr int kRouterUnroll = 8;  // 16-byte loads in flight per lane per pass
+constexpr int kRouterUnroll = 4;  // 16-byte loads in flight per lane per pass
 
-// One wave computes the dot products of one weight row (expert e < E, or the shared gate
-// row e == E) with up to kRouterTB tokens.  Lanes stride over H in 8-element (16-byte)
-// vectors; loads are issued unconditionally from clamped indices (a load under a branch
-// would be waited for at the join) and out-of-range vectors are skipped when consumed.
-// The float64 partial sums are reduced across the wave in a fixed butterfly order.
-__global__ __launch_bounds__(64) void router_logits_kernel(const uint16_t *__restrict__ x,
-                                                           const uint16_t *__restrict__ wr,
-                                                           const uint16_t *__restrict__ wsg,
-                                                           int T, int H, int E, int rows,
-                                                           float *__restrict__ logits) {
+// A workgroup computes the dot products of one weight row (expert e < E, or the shared
+// gate row e == E) with up to kRouterTB tokens; wave w covers the w-th quarter of H, so a
+// row is read with four waves' worth of loads in flight.  Lanes stride over the quarter in
+// 8-element (16-byte) vectors; loads are issued unconditionally from clamped indices (a
+// load under a branch would be waited for at the join) and out-of-range vectors are
+// skipped when consumed.  Float64 partial sums are reduced over the wave in a fixed
+// butterfly order, then over the four waves in order.
+constexpr int kRouterWaves = 4;
+
+__global__ __launch_bounds__(64 * kRouterWaves) void router_logits_kernel(const uint16_t *__restrict__ x,
+                                                                         const uint16_t *__restrict__ wr,
+                                                                         const uint16_t *__restrict__ wsg,
+                                                                         int T, int H, int E, int rows,
+                                                                         float *__restrict__ logits) {
+    __shared__ double part[kRouterWaves][kRouterTB];
     const int row = blockIdx.x;
     const uint16_t *w = row < E ? wr + (size_t)row * H : wsg;
     const int t0 = blockIdx.y * kRouterTB;
     const int nt = min(kRouterTB, T - t0);
-    const int lane = lane_id();
+    const int lane = lane_id(), wave = wave_id();
     double acc[kRouterTB];
 #pragma unroll
     for (int t = 0; t < kRouterTB; ++t) acc[t] = 0.0;
 
-    const int nvec = H >> 3;
-    for (int v0 = lane; v0 < nvec + lane; v0 += kWave * kRouterUnroll) {
+    const int nvec = H >> 3;                                   // H % 32 == 0: quarters are whole
+    const int q0 = wave * (nvec / kRouterWaves), q1 = q0 + nvec / kRouterWaves;
+    for (int v0 = q0 + lane; v0 < q1 + lane; v0 += kWave * kRouterUnroll) {
         u32x4 wv[kRouterUnroll];
 #pragma unroll
         for (int u = 0; u < kRouterUnroll; ++u)
-            wv[u] = __builtin_nontemporal_load((const u32x4 *)(w) + min(v0 + u * kWave, nvec - 1));
+            wv[u] = __builtin_nontemporal_load((const u32x4 *)(w) + min(v0 + u * kWave, q1 - 1));
 #pragma unroll
         for (int t = 0; t < kRouterTB; ++t) {
             if (t >= nt) break;                      // uniform across the wave
             const u32x4 *xr = (const u32x4 *)(x + (size_t)(t0 + t) * H);
             u32x4 xv[kRouterUnroll];
 #pragma unroll
-            for (int u = 0; u < kRouterUnroll; ++u) xv[u] = xr[min(v0 + u * kWave, nvec - 1)];
+            for (int u = 0; u < kRouterUnroll; ++u) xv[u] = xr[min(v0 + u * kWave, q1 - 1)];
             double s = acc[t];
 #pragma unroll
             for (int u = 0; u < kRouterUnroll; ++u) {
-                if (v0 + u * kWave < nvec) {
+                if (v0 + u * kWave < q1) {
 #pragma unroll
                     for (int q = 0; q < 4; ++q) {
                         const f32x2 fw = bf16x2_to_f32x2(wv[u][q]);
@@ -69,7 +75,14 @@ __global__ __launch_bounds__(64) void router_logits_kernel(const uint16_t *__res
 #pragma unroll
     for (int t = 0; t < kRouterTB; ++t) {
         const double s = group_sum_f64(acc[t], kWave);
-        if (lane == 0 && t < nt) logits[(size_t)(t0 + t) * rows + row] = (float)s;
+        if (lane == 0) part[wave][t] = s;
+    }
+    __syncthreads();
+    if (threadIdx.x < nt) {
+        double s = 0.0;
+#pragma unroll
+        for (int w4 = 0; w4 < kRouterWaves; ++w4) s += part[w4][threadIdx.x];
+        logits[(size_t)(t0 + threadIdx.x) * rows + row] = (float)s;
     }
 }
 
@@ -157,95 +170,98 @@ bool router_tiled(const moe_route_desc *d) { return d->T >= 32 && d->H % (32 * k
 
 MOE_DEV double sigmoid_f64(double v) { return 1.0 / (1.0 + exp(-v)); }
 
-// (key, index) order for selection: larger key first, equal keys -> lower index.
-MOE_DEV bool better(double ka, int ia, double kb, int ib) { return ka > kb || (ka == kb && ia < ib); }
-
-template <int CTRL>
-MOE_DEV void argmax_dpp_step(double &k, int &i) {
-    const int lo = __double2loint(k), hi = __double2hiint(k);
-    const int olo = __builtin_amdgcn_mov_dpp(lo, CTRL, 0xF, 0xF, false);
-    const int ohi = __builtin_amdgcn_mov_dpp(hi, CTRL, 0xF, 0xF, false);
-    const int oi = __builtin_amdgcn_mov_dpp(i, CTRL, 0xF, 0xF, false);
-    const double ok = __hiloint2double(ohi, olo);
-    if (better(ok, oi, k, i)) {
-        k = ok;
-        i = oi;
-    }
+// Selection order: larger key first, equal keys (-0 == +0) -> lower expert index.  A key
+// is mapped to an unsigned 64-bit integer with the same order (NaN -> 0, below every
+// number), so the wave-wide maximum runs on 32-bit integer halves.
+MOE_DEV uint64_t order_key(double k) {
+    if (k != k) return 0;
+    const uint64_t b = (uint64_t)__double_as_longlong(k + 0.0);          // -0 -> +0
+    return b ^ ((b >> 63) ? ~0ull : 0x8000000000000000ull);
 }
 
-// Wave-wide best (key, index): DPP butterfly inside each 16-lane row (quad xor 1, quad
-// xor 2, half-row mirror, row mirror), then the four row results through readlane.
-MOE_DEV void wave_argmax(double &k, int &i) {
-    argmax_dpp_step<0xB1>(k, i);    // quad_perm(1,0,3,2)
-    argmax_dpp_step<0x4E>(k, i);    // quad_perm(2,3,0,1)
-    argmax_dpp_step<0x141>(k, i);   // row_half_mirror
-    argmax_dpp_step<0x140>(k, i);   // row_mirror
-    double bk = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(k), 0),
-                                 __builtin_amdgcn_readlane(__double2loint(k), 0));
-    int bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-    for (int r = 1; r < 4; ++r) {
-        const double rk = __hiloint2double(__builtin_amdgcn_readlane(__double2hiint(k), 16 * r),
-                                           __builtin_amdgcn_readlane(__double2loint(k), 16 * r));
-        const int ri = __builtin_amdgcn_readlane(i, 16 * r);
-        if (better(rk, ri, bk, bi)) {
-            bk = rk;
-            bi = ri;
+// Maximum of v over the wave, in every lane: a DPP butterfly inside each 16-lane row
+// (quad xor 1, quad xor 2, half-row mirror, row mirror), then the four rows via readlane.
+MOE_DEV uint32_t wave_max_u32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));
+    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));
+    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+    return max(max(r0, r1), max(r2, r3));
+}
+
+// Lane of the wave-wide best (key, index) among the lanes' current heads: the largest high
+// key half, then (only on a tie) the largest low half, then the lowest index.
+MOE_DEV int wave_best_lane(uint64_t hk, int hi) {
+    const uint32_t kh = (uint32_t)(hk >> 32), kl = (uint32_t)hk;
+    const uint32_t mh = wave_max_u32(kh);
+    uint64_t cand = __ballot(kh == mh);
+    if (__popcll(cand) > 1) {
+        const bool c1 = kh == mh;
+        const uint32_t ml = wave_max_u32(c1 ? kl : 0u);
+        cand = __ballot(c1 && kl == ml);
+        if (__popcll(cand) > 1) {
+            const bool c2 = c1 && kl == ml;
+            const uint32_t mi = ~wave_max_u32(c2 ? ~(uint32_t)hi : 0u);   // lowest index
+            cand = __ballot(c2 && (uint32_t)hi == mi);
         }
     }
-    k = bk;
-    i = bi;
+    return __ffsll((long long)cand) - 1;
 }
 
 // One wave per token.  Lane l holds the selection keys of experts l, l+64, ... in
-// registers and tracks its own best untaken key; each of the k rounds takes the wave-wide
-// best (ties to the lower expert index) and only the winning lane rescans its keys.
-// A NaN key is never selected (ids -1 are emitted if fewer than k keys compare).
-template <int NK>
+// registers and tracks its own best untaken key (its head); each of the k rounds takes the
+// wave-wide best head and only the winning lane rescans its keys.  NaN keys are never
+// selected (ids -1 are emitted if fewer than k keys compare).
+// PERM: one workgroup holds every token (T <= 4, T*k <= 64) and also writes the token ->
+// expert permutation of the selected ids, as moe_permute would.
+template <int NK, bool PERM>
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int rows,
                                                    int T, int E, int k, int score, int renorm,
                                                    float scaling, const float *__restrict__ lbias,
                                                    const float *__restrict__ sbias, int has_sg,
                                                    int32_t *__restrict__ ids, float *__restrict__ w,
-                                                   float *__restrict__ sg) {
+                                                   float *__restrict__ sg, int32_t *__restrict__ offsets,
+                                                   int32_t *__restrict__ sorted, int32_t *__restrict__ p2r) {
+    __shared__ int sid[PERM ? 64 : 1];
     const int t = blockIdx.x * 4 + wave_id();
-    if (t >= T) return;
+    if (!PERM && t >= T) return;
     const int lane = lane_id();
+    if (t < T) {
     const float *lt = logits + (size_t)t * rows;
 
-    double key[NK];
+    uint64_t key[NK];
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
         const int e = min(lane + 64 * i, E - 1);
         double l = (double)lt[e] + (lbias ? (double)lbias[e] : 0.0);
         if (score == MOE_SCORE_SIGMOID) l = sigmoid_f64(l) + (sbias ? (double)sbias[e] : 0.0);
-        key[i] = lane + 64 * i < E ? l : NAN;
+        key[i] = lane + 64 * i < E ? order_key(l) : 0;
     }
     uint32_t taken = 0;
-    auto local_best = [&](double &bk, int &bi) {
-        bk = -INFINITY;
-        bi = INT_MAX;
+    uint64_t hk;
+    int hi;
+    auto head = [&]() {          // best untaken key of this lane (equal keys: lower i = lower expert)
+        hk = 0;
+        hi = INT_MAX;
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
-            const int e = lane + 64 * i;
-            if (!((taken >> i) & 1u) && better(key[i], e, bk, bi)) {
-                bk = key[i];
-                bi = e;
+            if (!((taken >> i) & 1u) && key[i] > hk) {
+                hk = key[i];
+                hi = lane + 64 * i;
             }
         }
     };
-    double lk;
-    int li;
-    local_best(lk, li);
+    head();
     int my_e = -1;
     for (int j = 0; j < k; ++j) {
-        double wk = lk;
-        int wi = li;
-        wave_argmax(wk, wi);
+        const int L = wave_best_lane(hk, hi);
+        const int wi = __builtin_amdgcn_readlane(hi, L);
         if (lane == j) my_e = wi == INT_MAX ? -1 : wi;
-        if (wi != INT_MAX && (wi & 63) == lane) {     // the winner drops its key
+        if (lane == L && wi != INT_MAX) {     // the winner drops its key
             taken |= 1u << (wi >> 6);
-            local_best(lk, li);
+            head();
         }
     }
 
@@ -274,8 +290,14 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     if (lane < k) {
         ids[(size_t)t * k + lane] = my_e;
         w[(size_t)t * k + lane] = mine ? (float)wv : NAN;
+        if constexpr (PERM) sid[t * k + lane] = my_e;        // -1 when fewer than k keys compare
     }
     if (has_sg && lane == 0) sg[t] = (float)sigmoid_f64((double)lt[E]);
+    }
+    if constexpr (PERM) {
+        __syncthreads();
+        small_permutation(sid, T * k, E, offsets, sorted, p2r, threadIdx.x, blockDim.x);
+    }
 }
 
 moe_status validate_route(const moe_route_desc *d) {
@@ -298,6 +320,29 @@ moe_status validate_route(const moe_route_desc *d) {
 
 using namespace moe;
 
+namespace {
+
+template <bool PERM>
+moe_status launch_topk_t(const moe_route_desc *d, const float *logits, int rows, const float *lb, const float *sb,
+                         bool has_sg, int32_t *ids, float *w, float *sg, int32_t *offs, int32_t *sorted,
+                         int32_t *p2r, hipStream_t s) {
+    auto topk = d->E <= 256 ? topk_kernel<4, PERM> : d->E <= 512 ? topk_kernel<8, PERM>
+              : d->E <= 1024 ? topk_kernel<16, PERM> : topk_kernel<32, PERM>;
+    const int tb = d->T < 4 ? 64 * d->T : 256;
+    hipLaunchKernelGGL(topk, dim3((d->T + 3) / 4), dim3(tb), 0, s, logits, rows, d->T, d->E, d->k, d->score,
+                       d->renormalize, d->routed_scaling, lb, sb, has_sg ? 1 : 0, ids, w, sg, offs, sorted, p2r);
+    return launch_check(PERM ? "moe_route_permute: topk_kernel" : "moe_route: topk_kernel");
+}
+
+moe_status launch_topk(const moe_route_desc *d, const float *logits, int rows, const float *lb, const float *sb,
+                       bool has_sg, int32_t *ids, float *w, float *sg, int32_t *offs, int32_t *sorted, int32_t *p2r,
+                       hipStream_t s) {
+    if (offs) return launch_topk_t<true>(d, logits, rows, lb, sb, has_sg, ids, w, sg, offs, sorted, p2r, s);
+    return launch_topk_t<false>(d, logits, rows, lb, sb, has_sg, ids, w, sg, nullptr, nullptr, nullptr, s);
+}
+
+}  // namespace
+
 extern "C" size_t moe_route_workspace(const moe_route_desc *d) {
     if (!d || d->T <= 0 || d->E <= 0) return 0;
     size_t b = align_up((size_t)d->T * (d->E + 1) * sizeof(float), 256);
@@ -305,13 +350,13 @@ extern "C" size_t moe_route_workspace(const moe_route_desc *d) {
     return b;
 }
 
-extern "C" moe_status moe_route(const moe_route_desc *d, const void *x, const void *w_router,
-                                const float *logit_bias, const float *select_bias,
-                                const void *w_shared_gate, int32_t *topk_ids, float *topk_w,
-                                float *shared_gate, void *ws, size_t ws_bytes, moe_stream stream) {
-    clear_error();
-    MOE_TRY(validate_route(d));
-    if (d->T == 0) return MOE_OK;
+namespace {
+
+// Checks the routing arguments and enqueues the logits (router_logits_kernel, or the tiled
+// product and its reduction) into the workspace.
+moe_status route_logits(const moe_route_desc *d, const void *x, const void *w_router, const float *logit_bias,
+                        const float *select_bias, const void *w_shared_gate, int32_t *topk_ids, float *topk_w,
+                        float *shared_gate, void *ws, size_t ws_bytes, hipStream_t s) {
     MOE_REQUIRE(x && w_router && topk_ids && topk_w, "moe_route: NULL x, w_router, topk_ids or topk_w");
     MOE_REQUIRE(!(select_bias && d->score != MOE_SCORE_SIGMOID),
                 "moe_route: select_bias is only defined for MOE_SCORE_SIGMOID");
@@ -324,7 +369,6 @@ extern "C" moe_status moe_route(const moe_route_desc *d, const void *x, const vo
     }
     const int rows = d->E + (w_shared_gate ? 1 : 0);
     float *logits = (float *)ws;
-    hipStream_t s = (hipStream_t)stream;
     if (router_tiled(d)) {
         double *partial = (double *)((unsigned char *)ws + align_up((size_t)d->T * (d->E + 1) * sizeof(float), 256));
         dim3 gt((rows + kRtTile - 1) / kRtTile, (d->T + kRtTile - 1) / kRtTile, kRouterKS);
@@ -336,16 +380,51 @@ extern "C" moe_status moe_route(const moe_route_desc *d, const void *x, const vo
         MOE_TRY(launch_check("moe_route: router_reduce_kernel"));
     } else {
         dim3 g1(rows, (d->T + kRouterTB - 1) / kRouterTB);
-        hipLaunchKernelGGL(router_logits_kernel, g1, dim3(64), 0, s, (const uint16_t *)x,
+        hipLaunchKernelGGL(router_logits_kernel, g1, dim3(64 * kRouterWaves), 0, s, (const uint16_t *)x,
                            (const uint16_t *)w_router, (const uint16_t *)w_shared_gate, d->T, d->H, d->E,
                            rows, logits);
         MOE_TRY(launch_check("moe_route: router_logits_kernel"));
     }
-    auto topk = d->E <= 256 ? topk_kernel<4> : d->E <= 512 ? topk_kernel<8> : d->E <= 1024 ? topk_kernel<16>
-                                                                                           : topk_kernel<32>;
-    const int tb = d->T < 4 ? 64 * d->T : 256;
-    hipLaunchKernelGGL(topk, dim3((d->T + 3) / 4), dim3(tb), 0, s, logits, rows, d->T, d->E, d->k, d->score,
-                       d->renormalize, d->routed_scaling, logit_bias, select_bias, w_shared_gate ? 1 : 0,
-                       topk_ids, topk_w, shared_gate);
-    return launch_check("moe_route: topk_kernel");
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" moe_status moe_route(const moe_route_desc *d, const void *x, const void *w_router,
+                                const float *logit_bias, const float *select_bias,
+                                const void *w_shared_gate, int32_t *topk_ids, float *topk_w,
+                                float *shared_gate, void *ws, size_t ws_bytes, moe_stream stream) {
+    clear_error();
+    MOE_TRY(validate_route(d));
+    if (d->T == 0) return MOE_OK;
+    hipStream_t s = (hipStream_t)stream;
+    MOE_TRY(route_logits(d, x, w_router, logit_bias, select_bias, w_shared_gate, topk_ids, topk_w, shared_gate, ws,
+                         ws_bytes, s));
+    const int rows = d->E + (w_shared_gate ? 1 : 0);
+    return launch_topk(d, (const float *)ws, rows, logit_bias, select_bias, w_shared_gate != nullptr, topk_ids,
+                       topk_w, shared_gate, nullptr, nullptr, nullptr, s);
+}
+
+extern "C" moe_status moe_route_permute(const moe_route_desc *d, const void *x, const void *w_router,
+                                        const float *logit_bias, const float *select_bias,
+                                        const void *w_shared_gate, int32_t *topk_ids, float *topk_w,
+                                        float *shared_gate, int32_t *expert_offsets, int32_t *sorted_pairs,
+                                        int32_t *pair_to_row, void *ws, size_t ws_bytes, moe_stream stream) {
+    clear_error();
+    MOE_TRY(validate_route(d));
+    MOE_REQUIRE(expert_offsets != nullptr, "moe_route_permute: NULL expert_offsets");
+    MOE_REQUIRE((int64_t)d->T * d->k < INT32_MAX, "moe_route_permute: T*k overflows int32");
+    if (d->T > 0) MOE_REQUIRE(sorted_pairs && pair_to_row, "moe_route_permute: NULL sorted_pairs or pair_to_row");
+    hipStream_t s = (hipStream_t)stream;
+    if (d->T == 0) return moe_permute(0, d->k, d->E, topk_ids, expert_offsets, sorted_pairs, pair_to_row, nullptr, 0,
+                                      stream);
+    MOE_TRY(route_logits(d, x, w_router, logit_bias, select_bias, w_shared_gate, topk_ids, topk_w, shared_gate, ws,
+                         ws_bytes, s));
+    const int rows = d->E + (w_shared_gate ? 1 : 0);
+    if (d->T <= 4 && d->T * d->k <= 64)      // one workgroup holds every token: fused permutation
+        return launch_topk(d, (const float *)ws, rows, logit_bias, select_bias, w_shared_gate != nullptr, topk_ids,
+                           topk_w, shared_gate, expert_offsets, sorted_pairs, pair_to_row, s);
+    MOE_TRY(launch_topk(d, (const float *)ws, rows, logit_bias, select_bias, w_shared_gate != nullptr, topk_ids,
+                        topk_w, shared_gate, nullptr, nullptr, nullptr, s));
+    return moe_permute(d->T, d->k, d->E, topk_ids, expert_offsets, sorted_pairs, pair_to_row, nullptr, 0, stream);
 }

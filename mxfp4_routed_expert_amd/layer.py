@@ -82,9 +82,9 @@ class MoELayer:
             self.side.wait_stream(cur)
             with torch.cuda.stream(self.side):
                 B.moe_expert_ffn(w.shared, x, w.act, 1, None, None, out=self.y_s, ws=self.ws_sh)
-        B.moe_route(x, w.w_router, w.k, w.score, w.renormalize, w.routed_scaling, w.logit_bias, w.select_bias,
-                    w.w_shared_gate, out=(self.ids, self.topk_w, self.sg), ws=self.ws_route)
-        B.moe_permute(self.ids, w.E, out=(self.offs, self.sp, self.p2r))
+        B.moe_route_permute(x, w.w_router, w.k, w.score, w.renormalize, w.routed_scaling, w.logit_bias,
+                            w.select_bias, w.w_shared_gate,
+                            out=(self.ids, self.topk_w, self.sg, self.offs, self.sp, self.p2r), ws=self.ws_route)
         xe = x
         if w.p_down is not None:
             xe = B.moe_dense_bf16(x, w.p_down, out=self.x_lat)

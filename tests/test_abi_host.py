@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe.h")
 
 B = pytest.importorskip("mxfp4_routed_expert_amd.binding",
-                        reason="libmoe.so not built (python -m mxfp4_routed_expert_amd.build)")
+                        reason="libmoe.so not built (python mxfp4_routed_expert_amd/build.py)")
 lib = B.lib
 DUMMY = ctypes.c_void_p(0x1000)      # never dereferenced: validation fails first
 
@@ -78,6 +78,21 @@ def test_route_null_pointers_and_workspace():
     # a selection bias only exists for the sigmoid score
     assert lib.moe_route(ctypes.byref(d), DUMMY, DUMMY, None, DUMMY, None, DUMMY, DUMMY, None, DUMMY, need,
                          None) == B.MOE_ERR_INVALID_ARG
+
+
+def test_route_permute_checks():
+    d = _desc()
+    need = lib.moe_route_workspace(ctypes.byref(d))
+    # expert_offsets is required
+    assert lib.moe_route_permute(ctypes.byref(d), DUMMY, DUMMY, None, None, None, DUMMY, DUMMY, None, None, DUMMY,
+                                 DUMMY, DUMMY, need, None) == B.MOE_ERR_INVALID_ARG
+    # the route workspace rule applies
+    assert lib.moe_route_permute(ctypes.byref(d), DUMMY, DUMMY, None, None, None, DUMMY, DUMMY, None, DUMMY, DUMMY,
+                                 DUMMY, DUMMY, need - 1, None) == B.MOE_ERR_WORKSPACE
+    # a bad descriptor is refused before anything else
+    bad = _desc(k=0)
+    assert lib.moe_route_permute(ctypes.byref(bad), DUMMY, DUMMY, None, None, None, DUMMY, DUMMY, None, DUMMY, DUMMY,
+                                 DUMMY, DUMMY, need, None) == B.MOE_ERR_INVALID_ARG
 
 
 def test_route_zero_tokens_is_a_no_op():

@@ -147,6 +147,31 @@ def test_route_matches_oracle(dev, M, name):
 
 # ------------------------------------------------------------------ permutation
 
+@pytest.mark.parametrize("name", list(ROUTE_CASES))
+def test_route_permute_equals_route_then_permute(dev, M, name):
+    """The fused entry point (one launch fewer for T <= 4, T*k <= 64) gives exactly what the
+    two calls give, and the oracle's permutation of the oracle's ids."""
+    cfg, seed = ROUTE_CASES[name]
+    inp = synth.layer_inputs_np(cfg, seed)
+    wsg = inp.w_shared_gate if cfg.shared == "gated" else None
+    args = (bf16_tensor(inp.x, dev), bf16_tensor(inp.w_router, dev), cfg.k, cfg.score, cfg.renormalize,
+            cfg.routed_scaling, f32_tensor(inp.logit_bias, dev), f32_tensor(inp.select_bias, dev),
+            bf16_tensor(wsg, dev) if wsg is not None else None)
+    ids, w, sg, offs, sp, p2r = M.moe_route_permute(*args)
+    ids2, w2, sg2 = M.moe_route(*args)
+    offs2, sp2, p2r2 = M.moe_permute(ids2, cfg.E)
+    for a, b in [(ids, ids2), (w, w2), (offs, offs2), (sp, sp2), (p2r, p2r2)]:
+        np.testing.assert_array_equal(to_np(a), to_np(b))
+    if sg is not None:
+        np.testing.assert_array_equal(to_np(sg), to_np(sg2))
+    r = OL.route(inp.x, inp.w_router, cfg.k, cfg.score, cfg.renormalize, cfg.routed_scaling, inp.logit_bias,
+                 inp.select_bias, wsg)
+    ref = OL.permute(r.ids, cfg.E)
+    np.testing.assert_array_equal(to_np(offs), ref.expert_offsets)
+    np.testing.assert_array_equal(to_np(sp), ref.sorted_pairs)
+    np.testing.assert_array_equal(to_np(p2r), ref.pair_to_row)
+
+
 @pytest.mark.parametrize("T,k,E", [(1, 1, 1), (1, 10, 512), (4, 2, 8), (64, 8, 256), (513, 10, 512),
                                    (2000, 16, 2048), (4, 8, 896), (7, 10, 512),
                                    (819, 10, 896), (820, 10, 64)])
