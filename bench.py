@@ -16,6 +16,13 @@ Also reported:
                 on the launch stream in a second, instrumented pass of the same steps;
   cpu_baseline  the float64 oracle on a bounded sample of the same workload, on the
                 host cores (a baseline only).
+  traffic       HBM bytes per launch of that kernel from the hardware counters (FETCH_SIZE,
+                WRITE_SIZE), each scaled by what the same counter reads for a 1 GiB copy, taken
+                from profiles/traffic_<workload>.json when its sources still match the library's;
+                otherwise null.  Collect with two counter passes over `--traffic-run`:
+                  rocprofv3 --pmc FETCH_SIZE -d D1 -o run --output-format csv -- python3 bench.py --traffic-run
+                  rocprofv3 --pmc WRITE_SIZE -d D2 -o run --output-format csv -- python3 bench.py --traffic-run
+                  python3 bench.py --traffic-parse D1 D2
 """
 from __future__ import annotations
 
@@ -25,6 +32,8 @@ import os
 import sys
 import time
 
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "mxfp4_routed_expert_amd", "csrc")
 PEAK_HBM_GBPS = 8000.0
 PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0}
 
@@ -94,6 +103,71 @@ def cpu_baseline(cfg, steps):
                        f"{total:.1f} s; expert bytes generated outside the timed region")
 
 
+def dominant_kernel(cfg):
+    """Name pattern (as rocprofv3 reports it) of the routed gate/up kernel of a workload."""
+    if cfg.act == "mxfp4" and cfg.T >= 64:
+        return r"mxgemm_kernel<true, true>"
+    return r"gemv_kernel<\d+, \d+, \d+, true, true>"
+
+
+def source_digest():
+    """sha256 over the library sources: counter figures are void once any of them changes."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(CSRC)):
+        if f.endswith((".hip", ".h")):
+            with open(os.path.join(CSRC, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()
+
+
+def traffic_file(cfg):
+    return os.path.join(HERE, "profiles", f"traffic_{cfg.name}.json")
+
+
+def load_traffic(cfg):
+    try:
+        with open(traffic_file(cfg)) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    return t["traffic_bytes_per_launch"] if t.get("source_sha256") == source_digest() else None
+
+
+def parse_traffic(cfg, fetch_dir, write_dir):
+    """Counter passes -> profiles/traffic_<workload>.json (bytes per launch of the kernel)."""
+    import csv
+    import glob
+    import re
+
+    def per_dispatch(d, counter):
+        rows = []
+        for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            rows += list(csv.DictReader(open(f)))
+        pat = re.compile(dominant_kernel(cfg))
+        kern = [float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == counter and pat.search(r["Kernel_Name"])]
+        cal = [float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == counter and "neg_kernel" in r["Kernel_Name"]]
+        if not kern or not cal:
+            raise SystemExit(f"no {counter} rows for the kernel or the calibration copy in {d}")
+        return sum(kern) / len(kern), len(kern), max(cal)
+    f_k, nf, f_c = per_dispatch(fetch_dir, "FETCH_SIZE")
+    w_k, nw, w_c = per_dispatch(write_dir, "WRITE_SIZE")
+    gib = float(1 << 30)
+    ff, fw = gib / (f_c * 1024.0), gib / (w_c * 1024.0)
+    res = {"workload": cfg.name, "kernel": dominant_kernel(cfg), "source_sha256": source_digest(),
+           "fetch_kib_per_dispatch": f_k, "write_kib_per_dispatch": w_k, "dispatches": [nf, nw],
+           "calibration": "torch.neg of a 1 GiB float64 tensor (1 GiB read, 1 GiB written)",
+           "calib_fetch_kib": f_c, "calib_write_kib": w_c, "fetch_factor": ff, "write_factor": fw,
+           "traffic_bytes_per_launch": int(f_k * 1024 * ff + w_k * 1024 * fw),
+           "commands": [f"rocprofv3 --pmc FETCH_SIZE -d D1 -o run --output-format csv -- python3 bench.py --config {cfg.name} --traffic-run",
+                        f"rocprofv3 --pmc WRITE_SIZE -d D2 -o run --output-format csv -- python3 bench.py --config {cfg.name} --traffic-run",
+                        f"python3 bench.py --config {cfg.name} --traffic-parse D1 D2"]}
+    os.makedirs(os.path.dirname(traffic_file(cfg)), exist_ok=True)
+    with open(traffic_file(cfg), "w") as f:
+        json.dump(res, f, indent=1)
+    print(json.dumps(res))
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -105,7 +179,15 @@ def main():
     ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps for the CPU baseline (0: skip)")
     ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of graph replays")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="run a few steps and a 1 GiB calibration copy, untimed (for counter passes)")
+    ap.add_argument("--traffic-parse", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two counter passes into profiles/traffic_<workload>.json")
     args = ap.parse_args()
+    if args.traffic_parse:
+        import synth
+        parse_traffic(synth.get(args.config), *args.traffic_parse)
+        return
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
@@ -168,6 +250,14 @@ def main():
     for s in range(args.warmup):
         step(s)
     torch.cuda.synchronize()
+    if args.traffic_run:
+        for s in range(args.steps):
+            step(args.warmup + s)
+        a = torch.empty(1 << 27, dtype=torch.float64, device=dev).fill_(1.0)
+        torch.neg(a)
+        torch.cuda.synchronize()
+        log("[bench] traffic run done")
+        return
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     for s in range(args.steps):
@@ -221,7 +311,7 @@ def main():
         achieved = gu_bytes / (gu_us * 1e-6) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBPS, 4))
-    roof.update(traffic=None, kernel="moe::gemv_kernel (routed gate/up, fused SwiGLU)"
+    roof.update(traffic=load_traffic(cfg), kernel="moe::gemv_kernel (routed gate/up, fused SwiGLU)"
                 if cfg.act == "float" or cfg.T * cfg.k <= 64 else "routed gate/up grouped GEMM",
                 bytes_per_launch=int(gu_bytes), flops_per_launch=int(gu_flops), avg_launch_us=round(gu_us, 2),
                 launches=len(gu_ms))

@@ -120,35 +120,45 @@ MOE_DEV int wave_nth_nonempty(const int32_t *offsets, int E, int slot) {
 // Token -> expert permutation of few pairs (P <= 64) by one workgroup of nthreads threads;
 // sid[0..P) in LDS holds the pairs' expert ids, already set to -1 where outside [0, E).
 // The stable rank of pair p is the number of valid pairs q with (id_q, q) < (id_p, p);
-// expert e's first row is the number of valid ids below e.  Needs a barrier between the
-// writes of sid and the call; ends without one.
-MOE_DEV void small_permutation(const int *sid, int P, int E, int32_t *offsets, int32_t *sorted, int32_t *p2r,
-                               int tid, int nthreads) {
+// expert e's first row is the number of valid ids below e.  Every thread first copies the
+// ids to registers (CAP >= P slots, independent LDS reads), so the counting loops run on
+// registers.  Needs a barrier between the writes of sid and the call; ends without one.
+constexpr int kSmallPermMax = 64;
+template <int CAP>
+MOE_DEV void small_permutation_t(const int *sid, int P, int E, int32_t *offsets, int32_t *sorted, int32_t *p2r,
+                                 int tid, int nthreads) {
+    int id[CAP];
+#pragma unroll
+    for (int q = 0; q < CAP; ++q) id[q] = q < P ? sid[q] : -1;
     int nvalid = 0;
-    for (int q = 0; q < P; ++q) nvalid += sid[q] >= 0;
+#pragma unroll
+    for (int q = 0; q < CAP; ++q) nvalid += id[q] >= 0;
     for (int pp = tid; pp < P; pp += nthreads) {
-        const int me = sid[pp];
+        int me = -1;
+#pragma unroll
+        for (int q = 0; q < CAP; ++q) me = q == pp ? id[q] : me;
         if (me < 0) {
             p2r[pp] = -1;
         } else {
             int r = 0;
-            for (int q = 0; q < P; ++q) {
-                const int o = sid[q];
-                r += o >= 0 && (o < me || (o == me && q < pp));
-            }
+#pragma unroll
+            for (int q = 0; q < CAP; ++q) r += id[q] >= 0 && (id[q] < me || (id[q] == me && q < pp));
             sorted[r] = pp;
             p2r[pp] = r;
         }
     }
     for (int e = tid; e <= E; e += nthreads) {
         int c = 0;
-        for (int q = 0; q < P; ++q) {
-            const int o = sid[q];
-            c += o >= 0 && o < e;
-        }
+#pragma unroll
+        for (int q = 0; q < CAP; ++q) c += id[q] >= 0 && id[q] < e;
         offsets[e] = c;
     }
     for (int r = nvalid + tid; r < P; r += nthreads) sorted[r] = -1;
+}
+MOE_DEV void small_permutation(const int *sid, int P, int E, int32_t *offsets, int32_t *sorted, int32_t *p2r,
+                               int tid, int nthreads) {
+    if (P <= 16) small_permutation_t<16>(sid, P, E, offsets, sorted, p2r, tid, nthreads);
+    else small_permutation_t<kSmallPermMax>(sid, P, E, offsets, sorted, p2r, tid, nthreads);
 }
 
 }  // namespace moe

@@ -252,6 +252,9 @@ extern "C" moe_status moe_expert_ffn(const moe_expert_weights *w, int32_t act, i
     }
     FfnWs l = ffn_ws_layout(w, act, T, R, true, true, ws);
     hipStream_t s = (hipStream_t)stream;
-    MOE_TRY(gateup_impl(w, act, T, k, x, x_dtype, expert_offsets, sorted_pairs, l.h, l.hq, l.hs, l, s));
+    // MX mode hands h to the down product as codes only; float32 h is an intermediate of
+    // the GEMV form alone (which takes it from the workspace itself).
+    float *h = act == MOE_ACT_MXFP4 ? nullptr : l.h;
+    MOE_TRY(gateup_impl(w, act, T, k, x, x_dtype, expert_offsets, sorted_pairs, h, l.hq, l.hs, l, s));
     return down_impl(w, act, T, k, l.h, l.hq, l.hs, expert_offsets, y_rows, s);
 }

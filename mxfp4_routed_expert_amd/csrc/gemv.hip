@@ -24,7 +24,11 @@ namespace moe {
 
 // Tuning constants (compile-time; -D overrides build variants for sweeps).
 #ifndef MOE_GEMV_UNROLL
-#define MOE_GEMV_UNROLL 4        // 16-byte weight loads issued per lane per batch (two batches in flight)
+#define MOE_GEMV_UNROLL 4        // 16-byte weight loads issued per lane per batch
+#endif
+#ifndef MOE_GEMV_DEPTH
+#define MOE_GEMV_DEPTH 2         // batches in flight per wave (deeper measured slower: more
+                                 // registers, and no faster streaming at this occupancy)
 #endif
 #ifndef MOE_GEMV_TARGET_WG
 #define MOE_GEMV_TARGET_WG 1024  // workgroups a launch aims for
@@ -37,6 +41,7 @@ namespace moe {
 #endif
 constexpr int kGemvThreads = 256;
 constexpr int kGemvUnroll = MOE_GEMV_UNROLL;
+constexpr int kGemvDepth = MOE_GEMV_DEPTH;
 #if MOE_GEMV_WAVES_PER_EU > 0
 #define MOE_GEMV_ATTR __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(MOE_GEMV_WAVES_PER_EU)))
 #else
@@ -316,25 +321,34 @@ __global__ MOE_GEMV_ATTR void gemv_kernel(const GemvParams p) {
     ws.nbatch = (wave < passes ? (passes - 1 - wave) / NW + 1 : 0) * ws.nb;
     ws.n_end = n_end;
 
-    u32x4 wa[kGemvUnroll], wb[kGemvUnroll];
-    uint32_t sa[kGemvUnroll], sb[kGemvUnroll];
+    // batches rotate through kGemvDepth register buffers: while batch q is consumed, the
+    // next kGemvDepth-1 are in flight
+    u32x4 wbuf[kGemvDepth][kGemvUnroll];
+    uint32_t sbuf[kGemvDepth][kGemvUnroll];
     float acc[MAXM];
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
 
     for (int c0 = 0; c0 < M; c0 += p.chunk) {
         const int mc = min(p.chunk, M - c0);
-        // the first weight batch is in flight while the activations are staged
-        if (ws.nbatch > 0) load_batch<FMT>(p, ws, 0, e, wbase, sbase, j, units, wa, sa);
+        // the first weight batches are in flight while the activations are staged
+#pragma unroll
+        for (int b = 0; b < kGemvDepth - 1; ++b)
+            if (b < ws.nbatch) load_batch<FMT>(p, ws, b, e, wbase, sbase, j, units, wbuf[b], sbuf[b]);
         __syncthreads();
         stage_activations<FMT, ACT>(p, smem, row0, c0, mc);
         __syncthreads();
-        for (int q = 0; q < ws.nbatch; q += 2) {
-            if (q + 1 < ws.nbatch) load_batch<FMT>(p, ws, q + 1, e, wbase, sbase, j, units, wb, sb);
-            compute_batch<FMT, ACT, MAXM, PAIR>(p, ws, q, mat, j, units, smem, row0 + c0, mc, wa, sa, acc);
-            if (q + 2 < ws.nbatch) load_batch<FMT>(p, ws, q + 2, e, wbase, sbase, j, units, wa, sa);
-            if (q + 1 < ws.nbatch)
-                compute_batch<FMT, ACT, MAXM, PAIR>(p, ws, q + 1, mat, j, units, smem, row0 + c0, mc, wb, sb, acc);
+        for (int q = 0; q < ws.nbatch; q += kGemvDepth) {
+#pragma unroll
+            for (int i = 0; i < kGemvDepth; ++i) {
+                const int qq = q + i;
+                if (qq + kGemvDepth - 1 < ws.nbatch)
+                    load_batch<FMT>(p, ws, qq + kGemvDepth - 1, e, wbase, sbase, j, units,
+                                    wbuf[(i + kGemvDepth - 1) % kGemvDepth], sbuf[(i + kGemvDepth - 1) % kGemvDepth]);
+                if (qq < ws.nbatch)
+                    compute_batch<FMT, ACT, MAXM, PAIR>(p, ws, qq, mat, j, units, smem, row0 + c0, mc, wbuf[i],
+                                                        sbuf[i], acc);
+            }
         }
     }
 }
