@@ -42,10 +42,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def algorithmic(cfg, D):
+def algorithmic(cfg, D, fused=False):
     """Algorithmic bytes and flops of one step at D distinct routed experts touched, for the
     layer and for the routed gate/up kernel (weights of touched experts, router, shared
-    expert and projections once, activations in and out once)."""
+    expert and projections once, activations in and out once).  `fused`: the gate/up launch
+    also computes the shared expert's gate/up (its weights and h rows count there too)."""
     K, I, H, T, k = cfg.d_model, cfg.I, cfg.H, cfg.T, cfg.k
     P = T * k
     if cfg.wfmt == "mxfp4":
@@ -66,8 +67,11 @@ def algorithmic(cfg, D):
         gu_in, gu_out = T * K * 17 // 32, P * I * 17 // 32
     else:
         gu_in, gu_out = T * K * (4 if cfg.latent else 2), P * I * 4
-    return dict(layer_bytes=layer_bytes, layer_flops=flops, gu_bytes=D * gu_w + gu_in + gu_out,
-                gu_flops=2 * P * 2 * K * I)
+    gu_bytes, gu_flops = D * gu_w + gu_in + gu_out, 2 * P * 2 * K * I
+    if fused and cfg.shared:
+        gu_bytes += cfg.expert_bytes(cfg.shared_K, cfg.shared_I) * 2 // 3 + T * cfg.shared_I * 4
+        gu_flops += 2 * T * 2 * cfg.shared_K * cfg.shared_I
+    return dict(layer_bytes=layer_bytes, layer_flops=flops, gu_bytes=gu_bytes, gu_flops=gu_flops)
 
 
 def cpu_baseline(cfg, steps):
@@ -294,7 +298,8 @@ def main():
     gu_us = 1e3 * sum(gu_ms) / len(gu_ms)
     del a
 
-    alg = [algorithmic(cfg, D) for D in D_steps]
+    fused = layers[0].fused
+    alg = [algorithmic(cfg, D, fused) for D in D_steps]
     gu_bytes = sum(x["gu_bytes"] for x in alg) / len(alg)
     gu_flops = sum(x["gu_flops"] for x in alg) / len(alg)
     layer_bytes = sum(x["layer_bytes"] for x in alg) / len(alg)
@@ -311,8 +316,11 @@ def main():
         achieved = gu_bytes / (gu_us * 1e-6) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBPS, 4))
-    roof.update(traffic=load_traffic(cfg), kernel="moe::gemv_kernel (routed gate/up, fused SwiGLU)"
-                if cfg.act == "float" or cfg.T * cfg.k <= 64 else "routed gate/up grouped GEMM",
+    kname = "routed gate/up grouped GEMM (mxgemm_kernel)"
+    if cfg.act == "float" or cfg.T * cfg.k <= 64:
+        kname = "moe::gemv_kernel (routed gate/up" + (" + shared gate/up" if fused and cfg.shared else "") + \
+                ", fused SwiGLU)"
+    roof.update(traffic=load_traffic(cfg), kernel=kname,
                 bytes_per_launch=int(gu_bytes), flops_per_launch=int(gu_flops), avg_launch_us=round(gu_us, 2),
                 launches=len(gu_ms))
 

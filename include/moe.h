@@ -191,6 +191,34 @@ moe_status moe_expert_down(const moe_expert_weights *w, int32_t act, int32_t T, 
                            const int32_t *expert_offsets, float *y_rows, moe_stream stream);
 
 /*
+ * Decode fusion (FLOAT activations; the shared expert fused into the routed launches).
+ * (Routed experts plus a shared expert, weighted and summed: rabbit README, design section
+ * and architecture table; a step's routed experts in one launch: Rulith Inference README,
+ * engine section.)
+ * moe_expert_gateup_shared: one launch computes
+ *   h[r]        = SwiGLU of the routed expert of row r on its token (as moe_expert_gateup,
+ *                 MOE_ACT_FLOAT, with expert_offsets / sorted_pairs), float32 [T*k][d_ff];
+ *   h_shared[t] = SwiGLU of `shared` on x[t], float32 [T][shared->d_ff]   (shared != NULL).
+ * moe_expert_down_combine: one launch computes the layer output directly
+ *   out[t] = sum_{j=0..k-1} topk_w[t][j] * (down_{topk_ids[t][j]} . h[pair_to_row[t*k+j]])
+ *            + (shared_gate ? shared_gate[t] : 1) * (shared_down . h_shared[t])
+ * in this order, float32 [T][d_model] -- moe_expert_down followed by moe_combine, without
+ * the y_rows buffer.  Pairs whose id is outside [0, E) or whose row is -1 contribute 0.
+ * shared: one-expert set of the same format and d_model (and, for the down product, d_ff)
+ * or NULL.  Needs (k + 1) * d_ff * 4 bytes of LDS per workgroup (<= 150 KiB), else
+ * MOE_ERR_UNSUPPORTED.  No workspace.
+ */
+moe_status moe_expert_gateup_shared(const moe_expert_weights *w, const moe_expert_weights *shared,
+                                    int32_t T, int32_t k, const void *x, int32_t x_dtype,
+                                    const int32_t *expert_offsets, const int32_t *sorted_pairs,
+                                    float *h, float *h_shared, moe_stream stream);
+moe_status moe_expert_down_combine(const moe_expert_weights *w, const moe_expert_weights *shared,
+                                   int32_t T, int32_t k, const float *h, const float *h_shared,
+                                   const int32_t *topk_ids, const float *topk_w,
+                                   const int32_t *pair_to_row, const float *shared_gate, float *out,
+                                   moe_stream stream);
+
+/*
  * moe_combine -- atomic-free weighted sum (rabbit README, design section: routed expert
  * outputs summed with their weights, plus the shared expert):
  *   out[t] = sum_{j=0..k-1} topk_w[t][j] * y_rows[pair_to_row[t*k+j]]

@@ -5,6 +5,6 @@ exposes each entry point with the same name, `layer` composes one layer step.
 """
 from . import binding  # noqa: F401  (raises ImportError when the library is not built)
 from .binding import (ExpertWeights, MoeError, moe_combine, moe_dense_bf16, moe_dequant,  # noqa: F401
-                      moe_expert_down, moe_expert_ffn, moe_expert_gateup, moe_mx_quantize, moe_permute,
-                      moe_route, moe_route_permute)
+                      moe_expert_down, moe_expert_down_combine, moe_expert_ffn, moe_expert_gateup,
+                      moe_expert_gateup_shared, moe_mx_quantize, moe_permute, moe_route, moe_route_permute)
 from .layer import LayerWeights, MoELayer  # noqa: F401

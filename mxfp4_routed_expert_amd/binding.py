@@ -72,13 +72,17 @@ _sig("moe_expert_gateup", _i32, ctypes.POINTER(ExpertWeightsC), _i32, _i32, _i32
      _p, _sz, _p)
 _sig("moe_expert_gateup_workspace", _sz, ctypes.POINTER(ExpertWeightsC), _i32, _i32, _i32)
 _sig("moe_expert_down", _i32, ctypes.POINTER(ExpertWeightsC), _i32, _i32, _i32, _p, _p, _p, _p, _p, _p)
+_sig("moe_expert_gateup_shared", _i32, ctypes.POINTER(ExpertWeightsC), ctypes.POINTER(ExpertWeightsC), _i32, _i32, _p,
+     _i32, _p, _p, _p, _p, _p)
+_sig("moe_expert_down_combine", _i32, ctypes.POINTER(ExpertWeightsC), ctypes.POINTER(ExpertWeightsC), _i32, _i32, _p,
+     _p, _p, _p, _p, _p, _p, _p)
 _sig("moe_combine", _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p)
 _sig("moe_dense_bf16", _i32, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p)
 _sig("moe_dequant", _i32, _i32, _i32, _i32, _p, _p, _p, _p)
 _sig("moe_mx_quantize", _i32, _i32, _i32, _p, _i32, _p, _p, _p)
 
 EXPORTS = ["moe_route", "moe_route_workspace", "moe_permute", "moe_permute_workspace", "moe_route_permute",
-           "moe_expert_ffn",
+           "moe_expert_ffn", "moe_expert_gateup_shared", "moe_expert_down_combine",
            "moe_expert_ffn_workspace", "moe_expert_gateup", "moe_expert_gateup_workspace", "moe_expert_down",
            "moe_combine", "moe_dense_bf16", "moe_dequant", "moe_mx_quantize", "moe_last_error",
            "moe_abi_version"]
@@ -300,6 +304,40 @@ def moe_expert_down(w: ExpertWeights, T, act="float", k=1, expert_offsets=None, 
     check(lib.moe_expert_down(ctypes.byref(c), ACT[act], T, kk, _ptr(h), _ptr(h_codes), _ptr(h_scales),
                               _ptr(expert_offsets), _ptr(y), _stream()))
     return y
+
+
+def moe_expert_gateup_shared(w: ExpertWeights, shared, x, k, expert_offsets, sorted_pairs, out=None):
+    """Routed gate/up (FLOAT activations) and, when `shared` is given, the shared expert's
+    gate/up over every token, in one launch.  Returns (h [T*k][d_ff], h_shared [T][d_ff_s] or None)."""
+    T = x.shape[0]
+    _need(x, None, "x", (T, w.d_model))
+    dev = x.device
+    if out is not None:
+        h, hsh = out
+    else:
+        h = torch.empty((T * k, w.d_ff), dtype=torch.float32, device=dev)
+        hsh = torch.empty((T, shared.d_ff), dtype=torch.float32, device=dev) if shared is not None else None
+    c = w.c_struct()
+    cs = shared.c_struct() if shared is not None else None
+    check(lib.moe_expert_gateup_shared(ctypes.byref(c), ctypes.byref(cs) if cs is not None else None, T, k, _ptr(x),
+                                       DT[x.dtype], _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(h), _ptr(hsh),
+                                       _stream()))
+    return h, hsh
+
+
+def moe_expert_down_combine(w: ExpertWeights, shared, h, h_shared, topk_ids, topk_w, pair_to_row, shared_gate=None,
+                            out=None):
+    """out[t] = sum_j topk_w[t][j] * down_{e_j}(h[pair_to_row[t*k+j]]) + g_t * shared_down(h_shared[t]),
+    float32 [T][d_model], in one launch."""
+    T, k = topk_w.shape
+    _need(topk_ids, torch.int32, "topk_ids", (T, k))
+    o = out if out is not None else torch.empty((T, w.d_model), dtype=torch.float32, device=topk_w.device)
+    c = w.c_struct()
+    cs = shared.c_struct() if shared is not None else None
+    check(lib.moe_expert_down_combine(ctypes.byref(c), ctypes.byref(cs) if cs is not None else None, T, k, _ptr(h),
+                                      _ptr(h_shared), _ptr(topk_ids), _ptr(topk_w), _ptr(pair_to_row),
+                                      _ptr(shared_gate), _ptr(o), _stream()))
+    return o
 
 
 # ------------------------------------------------------------------ combine, dense, formats

@@ -258,3 +258,106 @@ extern "C" moe_status moe_expert_ffn(const moe_expert_weights *w, int32_t act, i
     MOE_TRY(gateup_impl(w, act, T, k, x, x_dtype, expert_offsets, sorted_pairs, h, l.hq, l.hs, l, s));
     return down_impl(w, act, T, k, l.h, l.hq, l.hs, expert_offsets, y_rows, s);
 }
+
+// ------------------------------------------------------------------ decode fusion
+
+namespace moe {
+namespace {
+
+moe_status validate_shared(const moe_expert_weights *w, const moe_expert_weights *sh, const char *fn) {
+    if (!sh) return MOE_OK;
+    MOE_TRY(validate_weights(sh, MOE_ACT_FLOAT, fn));
+    MOE_REQUIRE(sh->num_experts == 1, "%s: the shared expert set must hold one expert (got %d)", fn, sh->num_experts);
+    MOE_REQUIRE(sh->format == w->format && sh->d_model == w->d_model,
+                "%s: the shared expert must have the routed experts' format and d_model", fn);
+    return MOE_OK;
+}
+
+}  // namespace
+}  // namespace moe
+
+extern "C" moe_status moe_expert_gateup_shared(const moe_expert_weights *w, const moe_expert_weights *shared,
+                                               int32_t T, int32_t k, const void *x, int32_t x_dtype,
+                                               const int32_t *expert_offsets, const int32_t *sorted_pairs,
+                                               float *h, float *h_shared, moe_stream stream) {
+    clear_error();
+    MOE_TRY(validate_weights(w, MOE_ACT_FLOAT, "moe_expert_gateup_shared"));
+    MOE_TRY(validate_shared(w, shared, "moe_expert_gateup_shared"));
+    MOE_REQUIRE(expert_offsets != nullptr, "moe_expert_gateup_shared: NULL expert_offsets");
+    MOE_TRY(validate_rows(w, T, k, expert_offsets, sorted_pairs, "moe_expert_gateup_shared"));
+    MOE_REQUIRE(x_dtype == MOE_DT_BF16 || x_dtype == MOE_DT_F32, "moe_expert_gateup_shared: unknown x_dtype %d",
+                x_dtype);
+    if (T == 0) return MOE_OK;
+    MOE_REQUIRE(x && h, "moe_expert_gateup_shared: NULL x or h");
+    MOE_REQUIRE(!shared || h_shared, "moe_expert_gateup_shared: NULL h_shared with a shared expert");
+    if (shared) MOE_REQUIRE((int64_t)T * shared->d_ff < INT32_MAX, "moe_expert_gateup_shared: sizes overflow int32");
+    const int R = T * k;
+    const int fmt = w->format == MOE_W_MXFP4 ? kFmtMXFP4 : kFmtFP8;
+    const int slots = w->num_experts < R ? w->num_experts : R;
+    GemvParams p = base_params(w, T, k, expert_offsets, sorted_pairs, R);
+    p.w[0] = w->gate;
+    p.w[1] = w->up;
+    p.s[0] = w->gate_s;
+    p.s[1] = w->up_s;
+    p.N = w->d_ff;
+    p.K = w->d_model;
+    p.gather = 1;
+    p.n_act_rows = T;
+    p.act = x;
+    p.out = h;
+    if (shared) {
+        p.shared_slot = slots;
+        p.sw[0] = shared->gate;
+        p.sw[1] = shared->up;
+        p.ss[0] = shared->gate_s;
+        p.ss[1] = shared->up_s;
+        p.sN = shared->d_ff;
+        p.sout = h_shared;
+    }
+    return gemv_launch(fmt, x_dtype == MOE_DT_F32 ? kActF32 : kActBF16, true, p, slots + (shared ? 1 : 0), T,
+                       (hipStream_t)stream, "moe_expert_gateup_shared");
+}
+
+extern "C" moe_status moe_expert_down_combine(const moe_expert_weights *w, const moe_expert_weights *shared,
+                                              int32_t T, int32_t k, const float *h, const float *h_shared,
+                                              const int32_t *topk_ids, const float *topk_w,
+                                              const int32_t *pair_to_row, const float *shared_gate, float *out,
+                                              moe_stream stream) {
+    clear_error();
+    MOE_TRY(validate_weights(w, MOE_ACT_FLOAT, "moe_expert_down_combine"));
+    MOE_TRY(validate_shared(w, shared, "moe_expert_down_combine"));
+    MOE_REQUIRE(T >= 0, "moe_expert_down_combine: T = %d < 0", T);
+    MOE_REQUIRE(k >= 1 && k <= MOE_MAX_TOPK && k <= w->num_experts,
+                "moe_expert_down_combine: k = %d outside [1, min(E, %d)]", k, MOE_MAX_TOPK);
+    MOE_REQUIRE((int64_t)T * k * w->d_ff < INT32_MAX && (int64_t)T * w->d_model < INT32_MAX,
+                "moe_expert_down_combine: sizes overflow int32");
+    if (shared)
+        MOE_REQUIRE(shared->d_ff == w->d_ff, "moe_expert_down_combine: the shared expert's d_ff (%d) must equal d_ff (%d)",
+                    shared->d_ff, w->d_ff);
+    if (down_combine_lds(k, shared != nullptr, w->d_ff) > 150 * 1024) {
+        set_error("moe_expert_down_combine: %d rows of d_ff = %d do not fit in LDS", k + (shared ? 1 : 0), w->d_ff);
+        return MOE_ERR_UNSUPPORTED;
+    }
+    if (T == 0) return MOE_OK;
+    MOE_REQUIRE(h && topk_ids && topk_w && pair_to_row && out, "moe_expert_down_combine: NULL pointer argument");
+    MOE_REQUIRE(!shared || h_shared, "moe_expert_down_combine: NULL h_shared with a shared expert");
+    DownCombineParams p = {};
+    p.w = w->down;
+    p.s = w->down_s;
+    p.sw = shared ? shared->down : nullptr;
+    p.ss = shared ? shared->down_s : nullptr;
+    p.E = w->num_experts;
+    p.N = w->d_model;
+    p.I = w->d_ff;
+    p.h = h;
+    p.hs = h_shared;
+    p.ids = topk_ids;
+    p.tw = topk_w;
+    p.p2r = pair_to_row;
+    p.sg = shared ? shared_gate : nullptr;
+    p.T = T;
+    p.k = k;
+    p.R = T * k;
+    p.out = out;
+    return down_combine_launch(w->format == MOE_W_MXFP4 ? kFmtMXFP4 : kFmtFP8, p, (hipStream_t)stream);
+}

@@ -28,7 +28,36 @@ struct GemvParams {
     int rows_per_wg;           // matrix rows per workgroup
     int chunk;                 // tokens staged in LDS at once (<= MAXM)
     int lds_ld;                // LDS row stride in elements (matrix-core GEMV)
+    // Optional extra grid slot (grid y == shared_slot) that runs a second weight set over
+    // the identity rows 0..T-1 -- the shared expert fused into the routed launch.
+    int shared_slot = -1;      // -1: none
+    const uint8_t *sw[2] = {nullptr, nullptr};
+    const void *ss[2] = {nullptr, nullptr};
+    int sN = 0;
+    float *sout = nullptr;     // [T][sN]
 };
+
+// Down product and weighted combine of decode-sized batches in one launch (gemv.hip):
+//   out[t][n] = sum_j tw[t][j] * (W_down[ids[t][j]][n] . h[p2r[t*k+j]])
+//               + g[t] * (W_shared_down[n] . hs[t])        (g = sg[t], or 1 when sg == NULL)
+struct DownCombineParams {
+    const uint8_t *w;          // routed down codes [E][N][I/2] (MXFP4) or [E][N][I] (FP8)
+    const void *s;             // routed down scales
+    const uint8_t *sw;         // shared down codes [N][I/..] or NULL
+    const void *ss;
+    int E, N, I;               // experts, output rows (d_model), reduction length (d_ff)
+    const float *h;            // routed h rows [R][I] (sorted-pair order)
+    const float *hs;           // shared h [T][I] or NULL
+    const int32_t *ids;        // [T][k]
+    const float *tw;           // [T][k]
+    const int32_t *p2r;        // [T*k]
+    const float *sg;           // [T] or NULL
+    int T, k, R;
+    float *out;                // [T][N]
+    int G, nl, rows_per_wg;
+};
+moe_status down_combine_launch(int fmt, DownCombineParams p, hipStream_t stream);
+size_t down_combine_lds(int k, bool shared, int I);
 
 // Enqueue one GEMV launch.  `slots` is the number of expert slots in the grid (experts
 // that may own rows; 1 for the identity form); `max_rows_per_expert` bounds M_e and

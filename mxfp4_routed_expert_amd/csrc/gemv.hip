@@ -26,12 +26,11 @@ namespace moe {
 #ifndef MOE_GEMV_UNROLL
 #define MOE_GEMV_UNROLL 4        // 16-byte weight loads issued per lane per batch
 #endif
-#ifndef MOE_GEMV_DEPTH
-#define MOE_GEMV_DEPTH 2         // batches in flight per wave (deeper measured slower: more
-                                 // registers, and no faster streaming at this occupancy)
+#ifndef MOE_GEMV_TARGET_WAVES
+#define MOE_GEMV_TARGET_WAVES 4096  // waves a launch aims for (all resident at once)
 #endif
-#ifndef MOE_GEMV_TARGET_WG
-#define MOE_GEMV_TARGET_WG 1024  // workgroups a launch aims for
+#ifndef MOE_GEMV_THREADS
+#define MOE_GEMV_THREADS 256        // threads per workgroup
 #endif
 #ifndef MOE_GEMV_NT
 #define MOE_GEMV_NT 1            // non-temporal weight loads
@@ -39,9 +38,8 @@ namespace moe {
 #ifndef MOE_GEMV_WAVES_PER_EU
 #define MOE_GEMV_WAVES_PER_EU 0  // occupancy hint (0: compiler's choice)
 #endif
-constexpr int kGemvThreads = 256;
+constexpr int kGemvThreads = MOE_GEMV_THREADS;
 constexpr int kGemvUnroll = MOE_GEMV_UNROLL;
-constexpr int kGemvDepth = MOE_GEMV_DEPTH;
 #if MOE_GEMV_WAVES_PER_EU > 0
 #define MOE_GEMV_ATTR __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(MOE_GEMV_WAVES_PER_EU)))
 #else
@@ -138,64 +136,89 @@ MOE_DEV float unit_dot(const u32x4 wv, const void *a_unit, int z) {
 
 // Activation staging: rows of the token chunk are copied to LDS unchanged (bf16, f32) or,
 // for MX-quantised activations, decoded block by block to bf16 (E2M1 * 2^X is exact in
-// bf16).  Rows whose index is out of range are staged as zeros.
+// bf16).  Rows whose index is out of range are staged as zeros.  The source rows of the
+// (at most 8) staged rows are resolved first, then each thread issues its loads in groups
+// of kStageU independent loads before storing any, so staging costs a few memory round
+// trips rather than one per element.
+constexpr int kStageU = 4;
+
 template <int FMT, int ACT>
 MOE_DEV void stage_activations(const GemvParams &p, unsigned char *smem, int row0, int c0, int mc) {
     constexpr int ASZ = ACT == kActF32 ? 4 : 2;
     const int K = p.K;
+    __shared__ int s_arow[8];
+    if (threadIdx.x < 8) {
+        const int m = threadIdx.x;
+        const int r = row0 + c0 + min(m, mc - 1);
+        int a = p.gather ? p.sorted_pairs[r] : r;
+        if (p.gather) a = a >= 0 ? a / p.k : -1;
+        s_arow[m] = (m < mc && a >= 0 && a < p.n_act_rows) ? a : -1;
+    }
+    __syncthreads();
+    auto row_of = [&](int m) { return s_arow[m]; };
     if constexpr (ACT == kActMX) {
         const int nb = K / 32;
-        for (int i = threadIdx.x; i < mc * nb; i += kGemvThreads) {
-            const int m = i / nb, blk = i - m * nb;
-            const int r = row0 + c0 + m;
-            int arow = p.gather ? p.sorted_pairs[r] : r;
-            if (p.gather) arow = arow >= 0 ? arow / p.k : -1;
-            u32x4 *dst = (u32x4 *)(smem + ((size_t)m * K + (size_t)blk * 32) * 2);
-            const int z = act_swizzle<kFmtMXFP4, false>(blk);
-            if (arow >= 0 && arow < p.n_act_rows) {
-                const u32x4 cv = ((const u32x4 *)((const uint8_t *)p.act + (size_t)arow * (K / 2)))[blk];
-                const float sc = e8m0_to_f32(p.act_s[(size_t)arow * nb + blk]);
+        const int total = mc * nb;
+        for (int i0 = threadIdx.x; i0 < total; i0 += kGemvThreads * kStageU) {
+            u32x4 cv[kStageU];
+            uint32_t sb[kStageU];
+            int src[kStageU];
+#pragma unroll
+            for (int u = 0; u < kStageU; ++u) {
+                const int i = min(i0 + u * kGemvThreads, total - 1);
+                const int m = i / nb, blk = i - m * nb;
+                src[u] = row_of(m);
+                const int a = max(src[u], 0);
+                cv[u] = ((const u32x4 *)((const uint8_t *)p.act + (size_t)a * (K / 2)))[blk];
+                sb[u] = p.act_s[(size_t)a * nb + blk];
+            }
+#pragma unroll
+            for (int u = 0; u < kStageU; ++u) {
+                const int i = i0 + u * kGemvThreads;
+                if (i >= total) break;
+                const int m = i / nb, blk = i - m * nb;
+                u32x4 *dst = (u32x4 *)(smem + ((size_t)m * K + (size_t)blk * 32) * 2);
+                const int z = act_swizzle<kFmtMXFP4, false>(blk);
+                const bool ok = src[u] >= 0;
+                const float sc = e8m0_to_f32(sb[u]);
 #pragma unroll
                 for (int d = 0; d < 4; ++d) {
-                    const bf16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cv[d], sc, 0);
-                    const bf16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cv[d], sc, 1);
-                    const bf16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cv[d], sc, 2);
-                    const bf16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cv[d], sc, 3);
-                    dst[d ^ z] = u32x4{__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
+                    const bf16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cv[u][d], sc, 0);
+                    const bf16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cv[u][d], sc, 1);
+                    const bf16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cv[u][d], sc, 2);
+                    const bf16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cv[u][d], sc, 3);
+                    const u32x4 val = {__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
                                        __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3)};
+                    dst[d ^ z] = ok ? val : u32x4{0, 0, 0, 0};
                 }
-            } else {
-#pragma unroll
-                for (int d = 0; d < 4; ++d) dst[d] = u32x4{0, 0, 0, 0};
             }
         }
     } else {
         const int act_vec = K * ASZ / 16;      // 16-byte vectors per activation row
-        for (int i = threadIdx.x; i < mc * act_vec; i += kGemvThreads) {
-            const int m = i / act_vec, v = i - m * act_vec;
-            const int r = row0 + c0 + m;
-            int arow = p.gather ? p.sorted_pairs[r] : r;
-            if (p.gather) arow = arow >= 0 ? arow / p.k : -1;
-            u32x4 val = {0, 0, 0, 0};
-            if (arow >= 0 && arow < p.n_act_rows)
-                val = ((const u32x4 *)((const unsigned char *)p.act + (size_t)arow * K * ASZ))[v];
-            constexpr int P = act_slots<FMT, ACT == kActF32>();
-            const int b = v / P, sl = v - b * P;
-            ((u32x4 *)smem)[(size_t)m * act_vec + b * P + (sl ^ act_swizzle<FMT, ACT == kActF32>(b))] = val;
+        const int total = mc * act_vec;
+        constexpr int P = act_slots<FMT, ACT == kActF32>();
+        for (int i0 = threadIdx.x; i0 < total; i0 += kGemvThreads * kStageU) {
+            u32x4 val[kStageU];
+            int src[kStageU];
+#pragma unroll
+            for (int u = 0; u < kStageU; ++u) {
+                const int i = min(i0 + u * kGemvThreads, total - 1);
+                const int m = i / act_vec, v = i - m * act_vec;
+                src[u] = row_of(m);
+                val[u] = ((const u32x4 *)((const unsigned char *)p.act + (size_t)max(src[u], 0) * K * ASZ))[v];
+            }
+#pragma unroll
+            for (int u = 0; u < kStageU; ++u) {
+                const int i = i0 + u * kGemvThreads;
+                if (i >= total) break;
+                const int m = i / act_vec, v = i - m * act_vec;
+                const int b = v / P, sl = v - b * P;
+                ((u32x4 *)smem)[(size_t)m * act_vec + b * P + (sl ^ act_swizzle<FMT, ACT == kActF32>(b))] =
+                    src[u] >= 0 ? val[u] : u32x4{0, 0, 0, 0};
+            }
         }
     }
 }
-
-// Geometry of one wave's share of a workgroup's rows.  A wave walks its passes (one pass =
-// the rows_per_pass rows its lane groups own at once) as a stream of batches of
-// kGemvUnroll 16-byte units per lane; batch q covers pass q / nb, units [i0, i0 + U).
-struct WaveStream {
-    int n_first;     // row of this lane group in the wave's first pass
-    int row_step;    // rows between consecutive passes of this wave
-    int nb;          // batches per pass
-    int nbatch;      // batches of this wave
-    int n_end;
-};
 
 // wbase / sbase: this lane's matrix (gate or up for the pair), chosen once per kernel with a
 // select -- indexing the parameter arrays by a lane-dependent value would load the pointer
@@ -203,12 +226,12 @@ struct WaveStream {
 // address: a load under a branch would make the compiler wait for it (and, loads retiring
 // in order, for every load before it) where the branch joins.  Slots past the row or the
 // row range are skipped when the batch is consumed.  Scale bytes stay raw until then.
+// Batch ib of a pass covers this lane's units i0 .. i0+U-1 of row n (n clamped to a valid row).
 template <int FMT>
-MOE_DEV void load_batch(const GemvParams &p, const WaveStream &ws, int q, int e, const uint8_t *wbase,
+MOE_DEV void load_batch(const GemvParams &p, int n_row, int n_end, int ib, int e, const uint8_t *wbase,
                         const void *sbase, int j, int units, u32x4 (&w)[kGemvUnroll], uint32_t (&sc)[kGemvUnroll]) {
-    const int pi = q / ws.nb;
-    const int i0 = (q - pi * ws.nb) * kGemvUnroll;
-    const int n = min(ws.n_first + pi * ws.row_step, ws.n_end - 1);
+    const int i0 = ib * kGemvUnroll;
+    const int n = min(n_row, n_end - 1);
     const size_t ridx = (size_t)e * p.N + n;
     const uint8_t *wrow = wbase + ridx * (size_t)units * 16;
 #pragma unroll
@@ -238,17 +261,14 @@ MOE_DEV float unit_scale_value(int fmt, uint32_t raw) {
 // apply SwiGLU for the gate/up pair, write the rows and clear acc.  Called by the whole
 // wave with the same q (the reductions are wave-wide shuffles).
 template <int FMT, int ACT, int MAXM, bool PAIR>
-MOE_DEV void compute_batch(const GemvParams &p, const WaveStream &ws, int q, int mat, int j, int units,
+MOE_DEV void compute_batch(const GemvParams &p, int n, int n_end, int ib, int nb, int mat, int j, int units,
                            const unsigned char *smem, int out_row0, int mc, const u32x4 (&w)[kGemvUnroll],
                            const uint32_t (&sc)[kGemvUnroll], float (&acc)[MAXM]) {
     constexpr bool ACT_F32 = ACT == kActF32;
     constexpr int ASZ = ACT_F32 ? 4 : 2;
     constexpr int EPU = FMT == kFmtMXFP4 ? 32 : (FMT == kFmtFP8 ? 16 : 8);
-    const int pi = q / ws.nb;
-    const int ib = q - pi * ws.nb;
     const int i0 = ib * kGemvUnroll;
-    const int n = ws.n_first + pi * ws.row_step;
-    const bool row_ok = n < ws.n_end;
+    const bool row_ok = n < n_end;
 #pragma unroll
     for (int u = 0; u < kGemvUnroll; ++u) {
         const int b = j + (i0 + u) * p.G;
@@ -263,7 +283,7 @@ MOE_DEV void compute_batch(const GemvParams &p, const WaveStream &ws, int q, int
             }
         }
     }
-    if (ib != ws.nb - 1) return;
+    if (ib != nb - 1) return;
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) acc[m] = group_sum(acc[m], p.G);
     if constexpr (PAIR) {
@@ -289,12 +309,26 @@ MOE_DEV void compute_batch(const GemvParams &p, const WaveStream &ws, int q, int
 }
 
 template <int FMT, int ACT, int MAXM, bool PAIR, bool ROUTED>
-__global__ MOE_GEMV_ATTR void gemv_kernel(const GemvParams p) {
+__global__ MOE_GEMV_ATTR void gemv_kernel(const GemvParams p0) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int NW = kGemvThreads / 64;
 
+    // the shared-expert slot reads its own weight set over the identity rows
+    const bool shared = ROUTED && p0.shared_slot >= 0 && (int)blockIdx.y == p0.shared_slot;
+    GemvParams p = p0;
+    if (shared) {
+        p.w[0] = p0.sw[0];
+        p.w[1] = p0.sw[1];
+        p.s[0] = p0.ss[0];
+        p.s[1] = p0.ss[1];
+        p.N = p0.sN;
+        p.E = 1;
+        p.out = p0.sout;
+        p.gather = 0;
+        p.residual = nullptr;
+    }
     int e = 0, row0 = 0, M = p.T;
-    if constexpr (ROUTED) {
+    if (ROUTED && !shared) {
         e = wave_nth_nonempty(p.offsets, p.E, blockIdx.y);
         if (e < 0) return;
         row0 = p.offsets[e];
@@ -314,43 +348,223 @@ __global__ MOE_GEMV_ATTR void gemv_kernel(const GemvParams p) {
     const int n_end = min(p.N, n_begin + p.rows_per_wg);
     if (n_begin >= n_end) return;
     const int passes = (n_end - n_begin + rows_per_pass - 1) / rows_per_pass;
-    WaveStream ws;
-    ws.n_first = n_begin + wave * rows_per_pass + grp;
-    ws.row_step = NW * rows_per_pass;
-    ws.nb = (p.nl + kGemvUnroll - 1) / kGemvUnroll;
-    ws.nbatch = (wave < passes ? (passes - 1 - wave) / NW + 1 : 0) * ws.nb;
-    ws.n_end = n_end;
+    const int nb = (p.nl + kGemvUnroll - 1) / kGemvUnroll;    // batches per pass
+    auto row_of = [&](int pass) { return n_begin + pass * rows_per_pass + grp; };
 
-    // batches rotate through kGemvDepth register buffers: while batch q is consumed, the
-    // next kGemvDepth-1 are in flight
-    u32x4 wbuf[kGemvDepth][kGemvUnroll];
-    uint32_t sbuf[kGemvDepth][kGemvUnroll];
+    // Passes (rows_per_pass rows each) are handed out to the waves of the workgroup one at a
+    // time from an LDS counter, so a wave whose loads are served late is not left with a
+    // fixed share of the work: the others take more passes.  Each wave starts with pass
+    // `wave`, asks for its next pass while loading the current one, and stops at the first
+    // pass past the end.  Batches alternate between two register buffers, one in flight
+    // while the other is consumed.
+    __shared__ int s_pass;
+    auto grab = [&](int after) {
+        int v = passes;
+        if (after < passes) {
+            int g = 0;
+            if (lane == 0) g = atomicAdd(&s_pass, 1);
+            v = min(__builtin_amdgcn_readfirstlane(g), passes);
+        }
+        return v;
+    };
+    u32x4 wa[kGemvUnroll], wb[kGemvUnroll];
+    uint32_t sa[kGemvUnroll], sb[kGemvUnroll];
     float acc[MAXM];
 #pragma unroll
     for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
 
     for (int c0 = 0; c0 < M; c0 += p.chunk) {
         const int mc = min(p.chunk, M - c0);
-        // the first weight batches are in flight while the activations are staged
-#pragma unroll
-        for (int b = 0; b < kGemvDepth - 1; ++b)
-            if (b < ws.nbatch) load_batch<FMT>(p, ws, b, e, wbase, sbase, j, units, wbuf[b], sbuf[b]);
-        __syncthreads();
+        __syncthreads();                       // the previous chunk is done with LDS and the counter
+        if (threadIdx.x == 0) s_pass = NW;
+        int P = min(wave, passes), ib = 0;     // batch being consumed: pass P, batch ib
+        // the first weight batch is in flight while the activations are staged
+        if (P < passes) load_batch<FMT>(p, row_of(P), n_end, 0, e, wbase, sbase, j, units, wa, sa);
         stage_activations<FMT, ACT>(p, smem, row0, c0, mc);
         __syncthreads();
-        for (int q = 0; q < ws.nbatch; q += kGemvDepth) {
-#pragma unroll
-            for (int i = 0; i < kGemvDepth; ++i) {
-                const int qq = q + i;
-                if (qq + kGemvDepth - 1 < ws.nbatch)
-                    load_batch<FMT>(p, ws, qq + kGemvDepth - 1, e, wbase, sbase, j, units,
-                                    wbuf[(i + kGemvDepth - 1) % kGemvDepth], sbuf[(i + kGemvDepth - 1) % kGemvDepth]);
-                if (qq < ws.nbatch)
-                    compute_batch<FMT, ACT, MAXM, PAIR>(p, ws, qq, mat, j, units, smem, row0 + c0, mc, wbuf[i],
-                                                        sbuf[i], acc);
+        int Pn = grab(P);                      // the wave's next pass
+        int Pnn = passes;
+        // one batch: load the following one into `nx`, consume `cu`; false when the wave is done
+        auto step = [&](u32x4 (&cu)[kGemvUnroll], uint32_t (&cs)[kGemvUnroll], u32x4 (&nx)[kGemvUnroll],
+                        uint32_t (&ns)[kGemvUnroll]) {
+            const bool last = ib + 1 == nb;
+            const int P2 = last ? Pn : P, ib2 = last ? 0 : ib + 1;
+            if (P2 < passes) load_batch<FMT>(p, row_of(P2), n_end, ib2, e, wbase, sbase, j, units, nx, ns);
+            if (last) Pnn = grab(Pn);          // needed one pass later
+            compute_batch<FMT, ACT, MAXM, PAIR>(p, row_of(P), n_end, ib, nb, mat, j, units, smem, row0 + c0, mc,
+                                                cu, cs, acc);
+            if (last) {
+                P = Pn;
+                Pn = Pnn;
+                ib = 0;
+            } else {
+                ++ib;
             }
+            return P < passes;
+        };
+        bool more = P < passes;
+        while (more) {
+            more = step(wa, sa, wb, sb);
+            if (!more) break;
+            more = step(wb, sb, wa, sa);
         }
     }
+}
+
+static void pick_layout(int units, bool pair, int *G, int *nl);
+
+// ------------------------------------------------------------------ down + combine
+// Decode-sized batches: one workgroup per (range of output rows, token) computes
+//   out[t][n] = sum_j tw[t][j] * (W_down[e_j][n] . h_j) + g_t * (W_shared_down[n] . hs_t)
+// directly, the k routed slots in order, then the shared expert -- the same sum in the same
+// order as the combine step, without writing and re-reading the expert rows.  The token's
+// k+1 float32 h rows are staged in LDS (unit-swizzled as for the GEMV); each wave walks
+// passes of rows_per_pass output rows and, per pass, streams the rows of every slot's
+// matrix with two batches of loads in flight.
+constexpr int kDcThreads = 512;
+constexpr int kDcU = 8;                       // 16-byte units per lane per batch
+
+template <int FMT>
+__global__ __launch_bounds__(kDcThreads) void down_combine_kernel(const DownCombineParams p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int s_e[MOE_MAX_TOPK + 1], s_r[MOE_MAX_TOPK + 1];
+    __shared__ float s_w[MOE_MAX_TOPK + 1];
+    constexpr int NW = kDcThreads / 64;
+    constexpr int EPU = FMT == kFmtMXFP4 ? 32 : 16;
+    constexpr int P = act_slots<FMT, true>();
+    const int t = blockIdx.y;
+    const int nslot = p.k + (p.sw ? 1 : 0);
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    if (tid < nslot) {
+        int e = 0, r = t;
+        float wt = p.sg ? p.sg[t] : 1.0f;
+        if (tid < p.k) {
+            const int pi = t * p.k + tid;
+            e = p.ids[pi];
+            r = p.p2r[pi];
+            wt = p.tw[pi];
+            if (e < 0 || e >= p.E || r < 0 || r >= p.R) e = r = -1;
+        }
+        s_e[tid] = e;
+        s_r[tid] = r;
+        s_w[tid] = wt;
+    }
+    __syncthreads();
+    // stage the slots' h rows (invalid slots as zeros), loads issued in groups
+    const int act_vec = p.I / 4;                 // 16-byte vectors per float32 row
+    const int total = nslot * act_vec;
+    for (int i0 = tid; i0 < total; i0 += kDcThreads * kStageU) {
+        u32x4 val[kStageU];
+        int ok[kStageU];
+#pragma unroll
+        for (int u = 0; u < kStageU; ++u) {
+            const int i = min(i0 + u * kDcThreads, total - 1);
+            const int j = i / act_vec, v = i - j * act_vec;
+            const int r = s_r[j];
+            ok[u] = r >= 0;
+            const float *src = j < p.k ? p.h + (size_t)max(r, 0) * p.I : p.hs + (size_t)t * p.I;
+            val[u] = ((const u32x4 *)src)[v];
+        }
+#pragma unroll
+        for (int u = 0; u < kStageU; ++u) {
+            const int i = i0 + u * kDcThreads;
+            if (i >= total) break;
+            const int j = i / act_vec, v = i - j * act_vec;
+            const int b = v / P, sl = v - b * P;
+            ((u32x4 *)smem)[(size_t)j * act_vec + b * P + (sl ^ act_swizzle<FMT, true>(b))] =
+                ok[u] ? val[u] : u32x4{0, 0, 0, 0};
+        }
+    }
+    __syncthreads();
+
+    const int units = units_per_row<FMT>(p.I);
+    const int G = p.G, rows_per_pass = 64 / G, grp = lane / G, jl = lane & (G - 1);
+    const int nb = (p.nl + kDcU - 1) / kDcU;
+    const int n_begin = blockIdx.x * p.rows_per_wg;
+    const int n_end = min(p.N, n_begin + p.rows_per_wg);
+    if (n_begin >= n_end) return;
+    const int passes = (n_end - n_begin + rows_per_pass - 1) / rows_per_pass;
+    const int my_passes = wave < passes ? (passes - 1 - wave) / NW + 1 : 0;
+    const int per_pass = nslot * nb;
+    const int nbatch = my_passes * per_pass;
+    const size_t row_bytes = FMT == kFmtMXFP4 ? (size_t)p.I / 2 : (size_t)p.I;
+
+    auto load = [&](int q, u32x4 (&w)[kDcU], uint32_t (&sc)[kDcU]) {
+        const int pi = q / per_pass, rem = q - pi * per_pass;
+        const int j = rem / nb, ib = rem - j * nb;
+        const int n = min(n_begin + (wave + pi * NW) * rows_per_pass + grp, n_end - 1);
+        const bool sh = j >= p.k;
+        const int e = sh ? 0 : max(s_e[j], 0);
+        const uint8_t *wb = sh ? p.sw : p.w;
+        const void *sb = sh ? p.ss : p.s;
+        const size_t ridx = (size_t)e * p.N + n;
+        const uint8_t *wrow = wb + ridx * row_bytes;
+#pragma unroll
+        for (int u = 0; u < kDcU; ++u) {
+            const int b = min(jl + (ib * kDcU + u) * G, units - 1);
+            w[u] = __builtin_nontemporal_load((const u32x4 *)(wrow + (size_t)b * 16));
+            if constexpr (FMT == kFmtMXFP4) {
+                sc[u] = ((const uint8_t *)sb)[ridx * units + b];
+            } else {
+                const size_t srow = (size_t)e * (p.N / 128) + n / 128;
+                sc[u] = __float_as_uint(((const float *)sb)[srow * (p.I / 128) + (b * 16) / 128]);
+            }
+        }
+    };
+    float dot = 0.0f, acc = 0.0f;
+    auto compute = [&](int q, const u32x4 (&w)[kDcU], const uint32_t (&sc)[kDcU]) {
+        const int pi = q / per_pass, rem = q - pi * per_pass;
+        const int j = rem / nb, ib = rem - j * nb;
+        const int n = n_begin + (wave + pi * NW) * rows_per_pass + grp;
+        const float *hrow = (const float *)smem + (size_t)j * p.I;
+        if (s_e[j] >= 0) {
+#pragma unroll
+            for (int u = 0; u < kDcU; ++u) {
+                const int b = jl + (ib * kDcU + u) * G;
+                if ((ib * kDcU + u) < p.nl && b < units)
+                    dot = fmaf(unit_dot<FMT, true>(w[u], hrow + (size_t)b * EPU, act_swizzle<FMT, true>(b)),
+                               unit_scale_value(FMT, sc[u]), dot);
+            }
+        }
+        if (ib != nb - 1) return;
+        acc = fmaf(s_w[j], group_sum(dot, G), acc);     // slot order j = 0..k-1, then shared
+        dot = 0.0f;
+        if (j != nslot - 1) return;
+        if (jl == 0 && n < n_end) p.out[(size_t)t * p.N + n] = acc;
+        acc = 0.0f;
+    };
+    u32x4 wa[kDcU], wb[kDcU];
+    uint32_t sa[kDcU], sb[kDcU];
+    if (nbatch > 0) load(0, wa, sa);
+    for (int q = 0; q < nbatch; q += 2) {
+        if (q + 1 < nbatch) load(q + 1, wb, sb);
+        compute(q, wa, sa);
+        if (q + 2 < nbatch) load(q + 2, wa, sa);
+        if (q + 1 < nbatch) compute(q + 1, wb, sb);
+    }
+}
+
+size_t down_combine_lds(int k, bool shared, int I) { return (size_t)(k + (shared ? 1 : 0)) * I * 4; }
+
+moe_status down_combine_launch(int fmt, DownCombineParams p, hipStream_t stream) {
+    const int units = fmt == kFmtMXFP4 ? p.I / 32 : p.I / 16;
+    // 16 lanes per row (4 rows per wave pass) while a lane still gets >= 4 units, so a
+    // workgroup's few dozen rows spread over all 8 waves; short rows use the GEMV layout
+    p.G = 16;
+    p.nl = (units + 15) / 16;
+    if (p.nl < 4) pick_layout(units, false, &p.G, &p.nl);
+    const int rows_per_pass = 64 / p.G;
+    // about one workgroup per CU in total (LDS holds k+1 rows of h)
+    const long long rows_total = (long long)p.N * p.T;
+    int rpw = (int)((rows_total + 255) / 256);
+    rpw = max(rpw, rows_per_pass);
+    rpw = (rpw + rows_per_pass - 1) / rows_per_pass * rows_per_pass;
+    p.rows_per_wg = rpw;
+    const size_t lds = down_combine_lds(p.k, p.sw != nullptr, p.I);
+    dim3 grid((p.N + rpw - 1) / rpw, p.T);
+    auto fn = fmt == kFmtMXFP4 ? down_combine_kernel<kFmtMXFP4> : down_combine_kernel<kFmtFP8>;
+    hipLaunchKernelGGL(fn, grid, dim3(kDcThreads), lds, stream, p);
+    return launch_check("moe_expert_down_combine");
 }
 
 // Lanes per row and units per lane for a row of `units` 16-byte units: the widest group
@@ -432,14 +646,15 @@ moe_status gemv_launch(int fmt, int act, bool pair, GemvParams p, int slots, int
     while (maxm < want) maxm *= 2;
     p.chunk = want;
     const int rows_per_pass = pair ? 32 / p.G : 64 / p.G;
-    // aim for MOE_GEMV_TARGET_WG workgroups over the whole launch, at least one pass per wave
-    long long rows_total = (long long)p.N * slots;
-    int rpw = (int)(rows_total / MOE_GEMV_TARGET_WG);
+    // aim for MOE_GEMV_TARGET_WAVES waves over the whole launch, at least one pass per wave
+    const int n_grid = p.shared_slot >= 0 ? max(p.N, p.sN) : p.N;
+    long long rows_total = (long long)n_grid * slots;
+    int rpw = (int)(rows_total / (MOE_GEMV_TARGET_WAVES / (kGemvThreads / 64)));
     const int min_rpw = rows_per_pass * (kGemvThreads / 64);
     if (rpw < min_rpw) rpw = min_rpw;
     rpw = (rpw + rows_per_pass - 1) / rows_per_pass * rows_per_pass;
     p.rows_per_wg = rpw;
-    dim3 grid((p.N + rpw - 1) / rpw, slots);
+    dim3 grid((n_grid + rpw - 1) / rpw, slots);
     const size_t lds = (size_t)p.chunk * row_lds;
     GemvFn fn = pick_kernel(fmt, act, pair, maxm, p.offsets != nullptr);
     hipLaunchKernelGGL(fn, grid, dim3(kGemvThreads), lds, stream, p);

@@ -2,7 +2,9 @@
 
 route -> permute -> routed experts (moe_expert_ffn) -> shared expert (moe_expert_ffn,
 identity form) -> combine; LatentMoE layers add moe_dense_bf16 before the routed experts
-and after the combine (Kimi K3 article, architecture section).  Every step runs in the
+and after the combine (Kimi K3 article, architecture section).  Decode-sized batches use
+the fused calls instead: route+permute, routed and shared gate/up in one launch, down and
+combine in one launch.  Every step runs in the
 HIP library; this module only wires buffers.  All buffers for a token count are
 allocated once, so a step enqueues kernels and allocates nothing.
 """
@@ -41,42 +43,73 @@ class LayerWeights:
         return self.w_router.shape[0]
 
 
+# LDS a down-combine workgroup may hold: k + 1 float32 rows of d_ff
+FUSED_LDS_LIMIT = 150 * 1024
+
+
+def fuses(w: LayerWeights, T: int) -> bool:
+    """Whether a step of T tokens takes the fused decode calls: decode-sized batches
+    (T <= 4) with FLOAT activations and no latent projections, a shared expert (if any)
+    of the routed format and widths, and k + 1 rows of d_ff within the LDS limit."""
+    ex, sh = w.experts, w.shared
+    return (w.act == "float" and w.p_down is None and w.p_up is None and 1 <= T <= 4
+            and (sh is None or (sh.fmt == ex.fmt and sh.d_model == ex.d_model and sh.d_ff == ex.d_ff))
+            and (w.k + (sh is not None)) * ex.d_ff * 4 <= FUSED_LDS_LIMIT)
+
+
 class MoELayer:
     def __init__(self, w: LayerWeights, T: int, device):
         self.w, self.T, self.dev = w, T, device
         E, H, k = w.E, w.H, w.k
-        L = w.experts.d_model
+        L, I = w.experts.d_model, w.experts.d_ff
         f32, i32 = torch.float32, torch.int32
         e = lambda *s, dt=f32: torch.empty(s, dtype=dt, device=device)
+        # Decode-sized batches: the shared expert joins the routed gate/up launch and the
+        # down product writes the combined output directly (moe_expert_gateup_shared,
+        # moe_expert_down_combine), so y_rows and y_shared never exist.
+        self.fused = fuses(w, T)
+        sh = w.shared
         self.ids, self.topk_w = e(T, k, dt=i32), e(T, k)
         self.sg = e(T) if w.w_shared_gate is not None else None
         self.offs, self.sp, self.p2r = e(E + 1, dt=i32), e(T * k, dt=i32), e(T * k, dt=i32)
         self.x_lat = e(T, L) if w.p_down is not None else None
-        self.y_rows = e(T * k, L)
-        self.y_s = e(T, H) if w.shared is not None else None
+        self.y_rows = None if self.fused else e(T * k, L)
+        self.y_s = e(T, H) if (sh is not None and not self.fused) else None
         self.z = e(T, L) if w.p_up is not None else None
         self.out = e(T, H)
         self.ws_route = B._workspace(B.moe_route_workspace(T, H, E, k, w.score), device)
         self.ws_ffn = B._workspace(B.moe_expert_ffn_workspace(w.experts, w.act, T, k), device)
-        self.ws_sh = (B._workspace(B.moe_expert_ffn_workspace(w.shared, w.act, T, 1), device)
-                      if w.shared is not None else None)
-        # buffers of the staged form (gate/up and down as separate calls)
-        I = w.experts.d_ff
+        self.ws_sh = (B._workspace(B.moe_expert_ffn_workspace(sh, w.act, T, 1), device)
+                      if (sh is not None and not self.fused) else None)
+        # h rows of the staged form (gate/up and down as separate calls) and the fused form
         self.h = e(T * k, I)
         self.hq = e(T * k, I // 2, dt=torch.uint8) if w.act == "mxfp4" else None
         self.hs = e(T * k, I // 32, dt=torch.uint8) if w.act == "mxfp4" else None
         self.ws_gu = B._workspace(B.moe_expert_gateup_workspace(w.experts, w.act, T, k), device)
-        # the shared expert does not depend on routing: it runs on a second stream, joined
-        # before the combine, so it overlaps router, permutation and routed experts
-        self.side = torch.cuda.Stream(device=device) if w.shared is not None else None
+        self.h_sh = e(T, I) if (self.fused and sh is not None) else None
+        # otherwise the shared expert does not depend on routing: it runs on a second stream,
+        # joined before the combine, so it overlaps router, permutation and routed experts
+        self.side = torch.cuda.Stream(device=device) if (w.shared is not None and not self.fused) else None
 
     def forward(self, x, mark=None):
         """One layer step on tokens x (bf16 [T][H]); returns the float32 output buffer.
 
-        With `mark`, the routed experts run as two calls (gate/up, then down) and
-        mark("gateup_begin") / mark("gateup_end") are called around the gate/up call, so a
-        caller can record events on the stream around that kernel."""
+        With `mark`, the routed experts run as two calls (gate/up, then down; the fused
+        form always does) and mark("gateup_begin") / mark("gateup_end") are called around
+        the gate/up call, so a caller can record events on the stream around that kernel."""
         w = self.w
+        if self.fused:
+            B.moe_route_permute(x, w.w_router, w.k, w.score, w.renormalize, w.routed_scaling, w.logit_bias,
+                                w.select_bias, w.w_shared_gate,
+                                out=(self.ids, self.topk_w, self.sg, self.offs, self.sp, self.p2r), ws=self.ws_route)
+            if mark is not None:
+                mark("gateup_begin")
+            B.moe_expert_gateup_shared(w.experts, w.shared, x, w.k, self.offs, self.sp, out=(self.h, self.h_sh))
+            if mark is not None:
+                mark("gateup_end")
+            B.moe_expert_down_combine(w.experts, w.shared, self.h, self.h_sh, self.ids, self.topk_w, self.p2r,
+                                      self.sg, out=self.out)
+            return self.out
         if w.shared is not None:
             cur = torch.cuda.current_stream()
             self.side.wait_stream(cur)

@@ -162,6 +162,34 @@ def test_gateup_and_down_require_their_outputs():
                                None) == B.MOE_ERR_INVALID_ARG
 
 
+def test_fused_decode_calls_validation():
+    w, sh = _weights(), _weights(E=1)
+    gu, dc = lib.moe_expert_gateup_shared, lib.moe_expert_down_combine
+    ok_args = (4, 2, DUMMY, 0, DUMMY, DUMMY, DUMMY, DUMMY, None)
+    # the shared set holds one expert of the routed format and d_model
+    assert gu(ctypes.byref(w), ctypes.byref(_weights(E=2)), *ok_args) == B.MOE_ERR_INVALID_ARG
+    assert gu(ctypes.byref(w), ctypes.byref(_weights(fmt=1, E=1)), *ok_args) == B.MOE_ERR_INVALID_ARG
+    assert gu(ctypes.byref(w), ctypes.byref(_weights(E=1, K=512)), *ok_args) == B.MOE_ERR_INVALID_ARG
+    # routed rows need expert_offsets and sorted_pairs; h_shared is required with a shared set
+    assert gu(ctypes.byref(w), None, 4, 2, DUMMY, 0, None, DUMMY, DUMMY, None, None) == B.MOE_ERR_INVALID_ARG
+    assert gu(ctypes.byref(w), ctypes.byref(sh), 4, 2, DUMMY, 0, DUMMY, DUMMY, DUMMY, None,
+              None) == B.MOE_ERR_INVALID_ARG
+    assert gu(ctypes.byref(w), ctypes.byref(sh), 4, 2, DUMMY, 7, DUMMY, DUMMY, DUMMY, DUMMY,
+              None) == B.MOE_ERR_INVALID_ARG
+    assert gu(ctypes.byref(w), ctypes.byref(sh), 0, 2, None, 0, DUMMY, None, None, None, None) == B.MOE_OK
+    dc_args = (DUMMY, DUMMY, DUMMY, DUMMY, DUMMY, None, DUMMY, None)
+    # down-combine: the shared d_ff must equal d_ff; k + 1 rows of d_ff must fit in LDS
+    assert dc(ctypes.byref(w), ctypes.byref(_weights(E=1, I=256)), 4, 2, *dc_args) == B.MOE_ERR_INVALID_ARG
+    big = _weights(E=16, I=4096)
+    assert dc(ctypes.byref(big), None, 4, 10, *dc_args) == B.MOE_ERR_UNSUPPORTED
+    assert dc(ctypes.byref(w), None, 4, 9, *dc_args) == B.MOE_ERR_INVALID_ARG          # k > E
+    assert dc(ctypes.byref(w), ctypes.byref(sh), 4, 2, DUMMY, None, DUMMY, DUMMY, DUMMY, None, DUMMY,
+              None) == B.MOE_ERR_INVALID_ARG                                           # h_shared missing
+    assert dc(ctypes.byref(w), None, 4, 2, DUMMY, None, DUMMY, DUMMY, None, None, DUMMY,
+              None) == B.MOE_ERR_INVALID_ARG                                           # pair_to_row missing
+    assert dc(ctypes.byref(w), None, 0, 2, None, None, None, None, None, None, None, None) == B.MOE_OK
+
+
 def test_combine_dense_dequant_quantize_validation():
     assert lib.moe_combine(4, 17, 64, DUMMY, DUMMY, DUMMY, None, None, DUMMY, None) == B.MOE_ERR_INVALID_ARG
     assert lib.moe_combine(4, 2, 0, DUMMY, DUMMY, DUMMY, None, None, DUMMY, None) == B.MOE_ERR_INVALID_ARG
@@ -186,3 +214,18 @@ def test_product_path_has_no_oracle_dependency():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 src = open(os.path.join(dirpath, f)).read()
                 assert not pat.search(src), os.path.join(dirpath, f)
+
+
+def test_layer_fusion_rule():
+    from types import SimpleNamespace as NS
+    from mxfp4_routed_expert_amd.layer import fuses
+    ex = NS(fmt="mxfp4", d_model=7168, d_ff=2368)
+    base = dict(act="float", p_down=None, p_up=None, k=10, experts=ex, shared=NS(fmt="mxfp4", d_model=7168, d_ff=2368))
+    w = lambda **kw: NS(**{**base, **kw})
+    assert fuses(w(), 1) and fuses(w(), 4) and fuses(w(shared=None), 2)
+    assert not fuses(w(), 5)                                            # prefill-sized batch
+    assert not fuses(w(act="mxfp4"), 1)                                  # MX activations
+    assert not fuses(w(p_down=object(), p_up=object()), 1)               # LatentMoE
+    assert not fuses(w(shared=NS(fmt="mxfp4", d_model=7168, d_ff=1024)), 1)
+    assert not fuses(w(shared=NS(fmt="fp8b128", d_model=7168, d_ff=2368)), 1)
+    assert not fuses(w(k=16, experts=NS(fmt="mxfp4", d_model=7168, d_ff=4096), shared=None), 1)  # LDS

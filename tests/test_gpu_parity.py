@@ -265,6 +265,10 @@ LAYER_CASES = {
                              I=256, T=9, k=3, shared="ungated", shared_K=256, shared_I=128),
     "tiny_latent": tiny(name="tl", wtag=86, latent=128, H=512, I=96, shared="ungated", shared_K=512,
                         shared_I=64),
+    # decode fusion (T <= 4, shared d_ff == d_ff): fused gate/up + down-combine calls
+    "tiny_fused_gated": tiny(name="tfg", wtag=87, T=3, k=3, shared="gated", shared_K=256, shared_I=128),
+    "tiny_fused_fp8_ungated": tiny(name="tff", wtag=88, wfmt="fp8b128", score="sigmoid", select_bias_std=0.01,
+                                   I=256, T=2, k=4, shared="ungated", shared_K=256, shared_I=256),
 }
 
 
@@ -284,8 +288,50 @@ def test_layer_matches_oracle(dev, M, name):
     ref = OL.layer(cfg, inp, ge, gs)
     np.testing.assert_array_equal(to_np(layer.ids), ref.routing.ids)
     np.testing.assert_array_equal(to_np(layer.sp), ref.perm.sorted_pairs)
-    assert_close(to_np(layer.y_rows), ref.y_rows, f"{name} y_rows")
+    if not layer.fused:          # the fused calls never write y_rows
+        assert_close(to_np(layer.y_rows), ref.y_rows, f"{name} y_rows")
     assert_close(to_np(out), ref.out, f"{name} out")
+
+
+FUSED_CASES = ["tiny", "tiny_fused_gated", "tiny_fused_fp8_ungated"]
+
+
+@pytest.mark.parametrize("name", FUSED_CASES)
+def test_fused_decode_calls_match_unfused(dev, M, name):
+    """moe_expert_gateup_shared + moe_expert_down_combine against moe_expert_ffn (routed and
+    shared) + moe_combine on the same routing: h rows equal, output within tolerance."""
+    cfg = LAYER_CASES[name]
+    layer, out, inp = _run_layer(M, cfg, dev)
+    assert layer.fused
+    w = layer.w
+    t, _ = build(cfg, dev)
+    x = t["x"]
+    h, _, _ = M.moe_expert_gateup(w.experts, x, "float", w.k, layer.offs, layer.sp)
+    assert_close(to_np(layer.h), to_np(h), f"{name} h")
+    y = M.moe_expert_ffn(w.experts, x, "float", w.k, layer.offs, layer.sp)
+    ys = M.moe_expert_ffn(w.shared, x, "float", 1, None, None) if w.shared is not None else None
+    if w.shared is not None:
+        hs, _, _ = M.moe_expert_gateup(w.shared, x, "float", 1, None, None)
+        assert_close(to_np(layer.h_sh), to_np(hs), f"{name} shared h")
+    ref = M.moe_combine(y, layer.p2r, layer.topk_w, ys, layer.sg)
+    assert_close(to_np(out), to_np(ref), f"{name} out")
+
+
+def test_down_combine_drops_invalid_pairs(dev, M):
+    """A pair with id -1 or row -1 adds nothing; the rest is the weighted sum."""
+    cfg = LAYER_CASES["tiny_fused_gated"]
+    layer, out, inp = _run_layer(M, cfg, dev)
+    w = layer.w
+    ids = layer.ids.clone()
+    p2r = layer.p2r.clone()
+    ids[0, 1] = -1                       # slot 1 of token 0 dropped by id
+    p2r[1 * w.k + 2] = -1                # slot 2 of token 1 dropped by row
+    o = M.moe_expert_down_combine(w.experts, w.shared, layer.h, layer.h_sh, ids, layer.topk_w, p2r, layer.sg)
+    tw = layer.topk_w.clone()
+    tw[0, 1] = 0.0
+    tw[1, 2] = 0.0
+    ref = M.moe_expert_down_combine(w.experts, w.shared, layer.h, layer.h_sh, layer.ids, tw, layer.p2r, layer.sg)
+    assert_close(to_np(o), to_np(ref), "dropped pairs")
 
 
 # ------------------------------------------------------------------ MX activation mode, stage by stage
@@ -387,8 +433,9 @@ def test_decode_layer_full_size(dev, M):
     ref = OL.layer(cfg, inp, ge, gs)
     np.testing.assert_array_equal(to_np(layer.ids), ref.routing.ids)
     assert_close(to_np(layer.topk_w), ref.routing.weights, "decode topk_w")
-    assert_close(to_np(layer.y_rows), ref.y_rows, "decode y_rows")
-    assert_close(to_np(layer.y_s), ref.y_shared, "decode shared")
+    if not layer.fused:
+        assert_close(to_np(layer.y_rows), ref.y_rows, "decode y_rows")
+        assert_close(to_np(layer.y_s), ref.y_shared, "decode shared")
     assert_close(to_np(out), ref.out, "decode out")
     # a second step on the same buffers is bitwise identical (no atomics in value paths)
     first = to_np(out).copy()
