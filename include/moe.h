@@ -205,7 +205,9 @@ moe_status moe_expert_down(const moe_expert_weights *w, int32_t act, int32_t T, 
  * in this order, float32 [T][d_model] -- moe_expert_down followed by moe_combine, without
  * the y_rows buffer.  Pairs whose id is outside [0, E) or whose row is -1 contribute 0.
  * shared: one-expert set of the same format and d_model (and, for the down product, d_ff)
- * or NULL.  Needs (k + 1) * d_ff * 4 bytes of LDS per workgroup (<= 150 KiB), else
+ * or NULL.  h and h_shared 16-byte aligned.  A workgroup holds the slots' h rows and a
+ * table of 128 partial sums per slot in LDS: with S = k (+1 with a shared expert),
+ * S * (4 * roundup(d_ff, 256) + 512) bytes must be <= 150 KiB, else
  * MOE_ERR_UNSUPPORTED.  No workspace.
  */
 moe_status moe_expert_gateup_shared(const moe_expert_weights *w, const moe_expert_weights *shared,

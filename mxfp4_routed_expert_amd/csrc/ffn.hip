@@ -335,12 +335,15 @@ extern "C" moe_status moe_expert_down_combine(const moe_expert_weights *w, const
         MOE_REQUIRE(shared->d_ff == w->d_ff, "moe_expert_down_combine: the shared expert's d_ff (%d) must equal d_ff (%d)",
                     shared->d_ff, w->d_ff);
     if (down_combine_lds(k, shared != nullptr, w->d_ff) > 150 * 1024) {
-        set_error("moe_expert_down_combine: %d rows of d_ff = %d do not fit in LDS", k + (shared ? 1 : 0), w->d_ff);
+        set_error("moe_expert_down_combine: %d rows of d_ff = %d and the output table do not fit in LDS",
+                  k + (shared ? 1 : 0), w->d_ff);
         return MOE_ERR_UNSUPPORTED;
     }
     if (T == 0) return MOE_OK;
     MOE_REQUIRE(h && topk_ids && topk_w && pair_to_row && out, "moe_expert_down_combine: NULL pointer argument");
     MOE_REQUIRE(!shared || h_shared, "moe_expert_down_combine: NULL h_shared with a shared expert");
+    MOE_REQUIRE((((uintptr_t)h | (uintptr_t)h_shared) & 15) == 0, "moe_expert_down_combine: h and h_shared must be "
+                "16-byte aligned");
     DownCombineParams p = {};
     p.w = w->down;
     p.s = w->down_s;

@@ -55,9 +55,17 @@ struct DownCombineParams {
     int T, k, R;
     float *out;                // [T][N]
     int G, nl, rows_per_wg;
+    int h_lds_bytes;           // LDS bytes of the staged h rows (the table follows)
 };
 moe_status down_combine_launch(int fmt, DownCombineParams p, hipStream_t stream);
 size_t down_combine_lds(int k, bool shared, int I);
+// Down-combine launch shape: 512 threads; at most kDcMaxRows output rows per workgroup.
+// A slot's h occupies 4 * dc_plane_ld(I) bytes of LDS (a multiple of 1 KiB): the float32 row,
+// or bf16 hi + lo planes of dc_plane_ld(I) values.
+constexpr int kDcThreads = 512;
+constexpr int kDcMaxRows = 128;
+__host__ __device__ constexpr int dc_plane_ld(int I) { return (I + 255) / 256 * 256; }
+void down_combine_mfma_launch(const DownCombineParams &p, dim3 grid, size_t lds, hipStream_t stream);
 
 // Enqueue one GEMV launch.  `slots` is the number of expert slots in the grid (experts
 // that may own rows; 1 for the identity form); `max_rows_per_expert` bounds M_e and

@@ -417,24 +417,93 @@ static void pick_layout(int units, bool pair, int *G, int *nl);
 // Decode-sized batches: one workgroup per (range of output rows, token) computes
 //   out[t][n] = sum_j tw[t][j] * (W_down[e_j][n] . h_j) + g_t * (W_shared_down[n] . hs_t)
 // directly, the k routed slots in order, then the shared expert -- the same sum in the same
-// order as the combine step, without writing and re-reading the expert rows.  The token's
-// k+1 float32 h rows are staged in LDS (unit-swizzled as for the GEMV); each wave walks
-// passes of rows_per_pass output rows and, per pass, streams the rows of every slot's
-// matrix with two batches of loads in flight.
-constexpr int kDcThreads = 512;
-constexpr int kDcU = 8;                       // 16-byte units per lane per batch
+// order as the combine step, without writing and re-reading the expert rows.
+//   * The token's k+1 float32 h rows are copied into LDS by direct global->LDS loads
+//     (unit-swizzled as for the GEMV), after the first weight batches have been issued,
+//     so the copy's latency overlaps the first weight bytes.
+//   * A lane group of G lanes covers kDcRows rows of one slot: every h value read from LDS
+//     serves kDcRows weight rows (a float32 h costs 8x the LDS bytes of the FP4 weights it
+//     multiplies, so one row per read would make LDS, not HBM, the limit).
+//   * Work items are (pass of 64/G * kDcRows rows, slot); wave w takes items w, w+8, ...
+//     and keeps kDcDepth batches of loads in flight.  Each item's dot products go to an
+//     LDS table part[slot][row]; after a barrier every row's output is the slot-ordered
+//     sum of its table column.
+#ifndef MOE_DM_ROUND
+#define MOE_DM_ROUND 4           // MXFP4 (matrix-core) path: rows per workgroup rounded to this (tiles of 16 may end past them)
+#endif
+#ifndef MOE_DC_ROWS
+#define MOE_DC_ROWS 4            // weight rows per lane group
+#endif
+#ifndef MOE_DC_DEPTH
+#define MOE_DC_DEPTH 2           // batches in flight per wave
+#endif
+constexpr int kDcRows = MOE_DC_ROWS;
+constexpr int kDcDepth = MOE_DC_DEPTH;
+static_assert((64 / 4) * kDcRows <= kDcMaxRows, "a pass of the narrowest lane groups must fit the table");
 
-template <int FMT>
+MOE_DEV void dc_dma16(const void *src, uint32_t lds_wave_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+
+// s[r] = unscaled dot product of weight unit w[r] (row r) with the float32 activations of
+// the unit in LDS (slots swizzled with key z); each activation vector is read once.
+template <int FMT, int R>
+MOE_DEV void unit_dot_rows(const u32x4 (&w)[R], const float *a_unit, int z, float (&s)[R]) {
+    const f32x4 *a4s = (const f32x4 *)a_unit;
+#pragma unroll
+    for (int r = 0; r < R; ++r) s[r] = 0.0f;
+    if constexpr (FMT == kFmtMXFP4) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const f32x4 lo = a4s[(2 * d) ^ z], hi = a4s[(2 * d + 1) ^ z];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const f32x2 w0 = fp4x2_to_f32x2<0>(w[r][d]), w1 = fp4x2_to_f32x2<1>(w[r][d]);
+                const f32x2 w2 = fp4x2_to_f32x2<2>(w[r][d]), w3 = fp4x2_to_f32x2<3>(w[r][d]);
+                float v = s[r];
+                v = fmaf(w0.x, lo[0], v); v = fmaf(w0.y, lo[1], v);
+                v = fmaf(w1.x, lo[2], v); v = fmaf(w1.y, lo[3], v);
+                v = fmaf(w2.x, hi[0], v); v = fmaf(w2.y, hi[1], v);
+                v = fmaf(w3.x, hi[2], v); v = fmaf(w3.y, hi[3], v);
+                s[r] = v;
+            }
+        }
+    } else {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+            const f32x4 av = a4s[d ^ z];
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const f32x2 w0 = fp8x2_to_f32x2<false>(w[r][d]), w1 = fp8x2_to_f32x2<true>(w[r][d]);
+                float v = s[r];
+                v = fmaf(w0.x, av[0], v); v = fmaf(w0.y, av[1], v);
+                v = fmaf(w1.x, av[2], v); v = fmaf(w1.y, av[3], v);
+                s[r] = v;
+            }
+        }
+    }
+}
+
+// Position of a wave's batch: item (pass, slot j), sub-batch ib; every field wave-uniform.
+struct DcPos {
+    int q, j, ib, pass;
+};
+
+template <int FMT, int U>
 __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(const DownCombineParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_e[MOE_MAX_TOPK + 1], s_r[MOE_MAX_TOPK + 1];
     __shared__ float s_w[MOE_MAX_TOPK + 1];
     constexpr int NW = kDcThreads / 64;
+    constexpr int R = kDcRows;
     constexpr int EPU = FMT == kFmtMXFP4 ? 32 : 16;
     constexpr int P = act_slots<FMT, true>();
+    using ScT = typename std::conditional<FMT == kFmtMXFP4, uint8_t, uint32_t>::type;
     const int t = blockIdx.y;
     const int nslot = p.k + (p.sw ? 1 : 0);
-    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(wave_id());
     if (tid < nslot) {
         int e = 0, r = t;
         float wt = p.sg ? p.sg[t] : 1.0f;
@@ -443,127 +512,212 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(const DownComb
             e = p.ids[pi];
             r = p.p2r[pi];
             wt = p.tw[pi];
-            if (e < 0 || e >= p.E || r < 0 || r >= p.R) e = r = -1;
+            if (e < 0 || e >= p.E || r < 0 || r >= p.R) {      // dropped pair: contributes 0
+                e = r = -1;
+                wt = 0.0f;
+            }
         }
         s_e[tid] = e;
         s_r[tid] = r;
         s_w[tid] = wt;
     }
     __syncthreads();
-    // stage the slots' h rows (invalid slots as zeros), loads issued in groups
-    const int act_vec = p.I / 4;                 // 16-byte vectors per float32 row
-    const int total = nslot * act_vec;
-    for (int i0 = tid; i0 < total; i0 += kDcThreads * kStageU) {
-        u32x4 val[kStageU];
-        int ok[kStageU];
-#pragma unroll
-        for (int u = 0; u < kStageU; ++u) {
-            const int i = min(i0 + u * kDcThreads, total - 1);
-            const int j = i / act_vec, v = i - j * act_vec;
-            const int r = s_r[j];
-            ok[u] = r >= 0;
-            const float *src = j < p.k ? p.h + (size_t)max(r, 0) * p.I : p.hs + (size_t)t * p.I;
-            val[u] = ((const u32x4 *)src)[v];
+
+    const int units = units_per_row<FMT>(p.I);
+    const int G = p.G, grp = lane / G, jl = lane & (G - 1);
+    const int rpp = (64 / G) * R;                          // rows per pass
+    const int nb = (p.nl + U - 1) / U;
+    const int n_begin = blockIdx.x * p.rows_per_wg;
+    const int n_end = min(p.N, n_begin + p.rows_per_wg);
+    if (n_begin >= n_end) return;                          // the whole workgroup
+    const int npass = (n_end - n_begin + rpp - 1) / rpp;
+    const int nitems = npass * nslot;
+    const int my_items = wave < nitems ? (nitems - 1 - wave) / NW + 1 : 0;
+    const int nq = my_items * nb;
+    const size_t row_bytes = FMT == kFmtMXFP4 ? (size_t)p.I / 2 : (size_t)p.I;
+    const int act_vec = p.I / 4;                           // 16-byte vectors per float32 row
+    float *part = (float *)(smem + p.h_lds_bytes);          // [nslot][rows_per_wg]
+
+    auto advance = [&](DcPos &c) {
+        ++c.q;
+        if (++c.ib == nb) {
+            c.ib = 0;
+            c.j += NW;
+            while (c.j >= nslot) {
+                c.j -= nslot;
+                ++c.pass;
+            }
         }
+    };
+    // rows of the lane group in a pass: pass * rpp + grp * R + r
+    auto load = [&](const DcPos &c, u32x4 (&w)[U][R], ScT (&sc)[U][R]) {
+        const bool sh = c.j >= p.k;
+        const int e = sh ? 0 : max(__builtin_amdgcn_readfirstlane(s_e[c.j]), 0);
+        const uint8_t *wb = sh ? p.sw : p.w;
+        const void *sb = sh ? p.ss : p.s;
+        const int n0 = n_begin + c.pass * rpp + grp * R;
 #pragma unroll
-        for (int u = 0; u < kStageU; ++u) {
-            const int i = i0 + u * kDcThreads;
-            if (i >= total) break;
+        for (int r = 0; r < R; ++r) {
+            const int n = min(n0 + r, n_end - 1);
+            const size_t ridx = (size_t)e * p.N + n;
+            const uint8_t *wrow = wb + ridx * row_bytes;
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int b = min(jl + (c.ib * U + u) * G, units - 1);
+                w[u][r] = __builtin_nontemporal_load((const u32x4 *)(wrow + (size_t)b * 16));
+                if constexpr (FMT == kFmtMXFP4) {
+                    sc[u][r] = ((const uint8_t *)sb)[ridx * units + b];
+                } else {
+                    const size_t srow = (size_t)e * (p.N / 128) + n / 128;
+                    sc[u][r] = __float_as_uint(((const float *)sb)[srow * (p.I / 128) + (b * 16) / 128]);
+                }
+            }
+        }
+    };
+    float dot[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) dot[r] = 0.0f;
+    // Batch at c into dot (branch-free: out-of-row units are computed on a clamped unit and
+    // discarded by a select); the item's last sub-batch reduces over the lane group and
+    // stores the rows' dot products for slot j (0 for a dropped pair).  Positions past the
+    // wave's last batch compute on reloaded data and store nothing.
+    auto compute = [&](const DcPos &c, const u32x4 (&w)[U][R], const ScT (&sc)[U][R]) {
+        const float *hrow = (const float *)smem + (size_t)c.j * p.I;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int b = jl + (c.ib * U + u) * G;
+            const int bc = min(b, units - 1);
+            float s[R];
+            unit_dot_rows<FMT, R>(w[u], hrow + (size_t)bc * EPU, act_swizzle<FMT, true>(bc), s);
+            const bool ok = (c.ib * U + u) < p.nl && b < units;
+#pragma unroll
+            for (int r = 0; r < R; ++r) {
+                const float v = fmaf(s[r], unit_scale_value(FMT, (uint32_t)sc[u][r]), dot[r]);
+                dot[r] = ok ? v : dot[r];
+            }
+        }
+        if (c.ib != nb - 1) return;
+        const bool drop = __builtin_amdgcn_readfirstlane(s_e[c.j]) < 0;
+        const int l0 = c.pass * rpp + grp * R;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+            float v = group_sum(dot[r], G);
+            dot[r] = 0.0f;
+            if (drop) v = 0.0f;
+            if (jl == 0 && c.q < nq && n_begin + l0 + r < n_end) part[c.j * p.rows_per_wg + l0 + r] = v;
+        }
+    };
+
+    // first batches in flight before the h copy
+    u32x4 wv[kDcDepth][U][R];
+    ScT sv[kDcDepth][U][R];
+    DcPos lp{0, wave % nslot, 0, wave / nslot};
+    const DcPos first = lp;
+    if (nq > 0) {
+#pragma unroll
+        for (int d = 0; d < kDcDepth; ++d) {
+            load(lp, wv[d], sv[d]);
+            if (lp.q < nq - 1) advance(lp);
+        }
+    }
+    // h rows -> LDS: position i = (slot j, vector v) holds vector b*P + (s ^ swz(b)) of the
+    // slot's row, v = b*P + s; invalid slots copy row 0 (never used).  The copy covers whole
+    // 64-vector blocks; the tail of the last block reads a valid vector into the padding.
+    {
+        const int total = nslot * act_vec;
+        const int blocks = (total + 63) / 64;
+        for (int blk = wave; blk < blocks; blk += NW) {
+            const int i = min(blk * 64 + lane, total - 1);
             const int j = i / act_vec, v = i - j * act_vec;
             const int b = v / P, sl = v - b * P;
-            ((u32x4 *)smem)[(size_t)j * act_vec + b * P + (sl ^ act_swizzle<FMT, true>(b))] =
-                ok[u] ? val[u] : u32x4{0, 0, 0, 0};
+            const int vs = b * P + (sl ^ act_swizzle<FMT, true>(b));
+            const float *row = j < p.k ? p.h + (size_t)max(s_r[j], 0) * p.I : p.hs + (size_t)t * p.I;
+            dc_dma16(row + (size_t)vs * 4, (uint32_t)(uintptr_t)(smem + (size_t)blk * 1024));
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+
+    DcPos cp = first;
+    const int nqr = (nq + kDcDepth - 1) / kDcDepth * kDcDepth;
+    for (int q0 = 0; q0 < nqr; q0 += kDcDepth) {
+#pragma unroll
+        for (int d = 0; d < kDcDepth; ++d) {
+            compute(cp, wv[d], sv[d]);
+            advance(cp);
+            load(lp, wv[d], sv[d]);
+            if (lp.q < nq - 1) advance(lp);
         }
     }
     __syncthreads();
-
-    const int units = units_per_row<FMT>(p.I);
-    const int G = p.G, rows_per_pass = 64 / G, grp = lane / G, jl = lane & (G - 1);
-    const int nb = (p.nl + kDcU - 1) / kDcU;
-    const int n_begin = blockIdx.x * p.rows_per_wg;
-    const int n_end = min(p.N, n_begin + p.rows_per_wg);
-    if (n_begin >= n_end) return;
-    const int passes = (n_end - n_begin + rows_per_pass - 1) / rows_per_pass;
-    const int my_passes = wave < passes ? (passes - 1 - wave) / NW + 1 : 0;
-    const int per_pass = nslot * nb;
-    const int nbatch = my_passes * per_pass;
-    const size_t row_bytes = FMT == kFmtMXFP4 ? (size_t)p.I / 2 : (size_t)p.I;
-
-    auto load = [&](int q, u32x4 (&w)[kDcU], uint32_t (&sc)[kDcU]) {
-        const int pi = q / per_pass, rem = q - pi * per_pass;
-        const int j = rem / nb, ib = rem - j * nb;
-        const int n = min(n_begin + (wave + pi * NW) * rows_per_pass + grp, n_end - 1);
-        const bool sh = j >= p.k;
-        const int e = sh ? 0 : max(s_e[j], 0);
-        const uint8_t *wb = sh ? p.sw : p.w;
-        const void *sb = sh ? p.ss : p.s;
-        const size_t ridx = (size_t)e * p.N + n;
-        const uint8_t *wrow = wb + ridx * row_bytes;
-#pragma unroll
-        for (int u = 0; u < kDcU; ++u) {
-            const int b = min(jl + (ib * kDcU + u) * G, units - 1);
-            w[u] = __builtin_nontemporal_load((const u32x4 *)(wrow + (size_t)b * 16));
-            if constexpr (FMT == kFmtMXFP4) {
-                sc[u] = ((const uint8_t *)sb)[ridx * units + b];
-            } else {
-                const size_t srow = (size_t)e * (p.N / 128) + n / 128;
-                sc[u] = __float_as_uint(((const float *)sb)[srow * (p.I / 128) + (b * 16) / 128]);
-            }
-        }
-    };
-    float dot = 0.0f, acc = 0.0f;
-    auto compute = [&](int q, const u32x4 (&w)[kDcU], const uint32_t (&sc)[kDcU]) {
-        const int pi = q / per_pass, rem = q - pi * per_pass;
-        const int j = rem / nb, ib = rem - j * nb;
-        const int n = n_begin + (wave + pi * NW) * rows_per_pass + grp;
-        const float *hrow = (const float *)smem + (size_t)j * p.I;
-        if (s_e[j] >= 0) {
-#pragma unroll
-            for (int u = 0; u < kDcU; ++u) {
-                const int b = jl + (ib * kDcU + u) * G;
-                if ((ib * kDcU + u) < p.nl && b < units)
-                    dot = fmaf(unit_dot<FMT, true>(w[u], hrow + (size_t)b * EPU, act_swizzle<FMT, true>(b)),
-                               unit_scale_value(FMT, sc[u]), dot);
-            }
-        }
-        if (ib != nb - 1) return;
-        acc = fmaf(s_w[j], group_sum(dot, G), acc);     // slot order j = 0..k-1, then shared
-        dot = 0.0f;
-        if (j != nslot - 1) return;
-        if (jl == 0 && n < n_end) p.out[(size_t)t * p.N + n] = acc;
-        acc = 0.0f;
-    };
-    u32x4 wa[kDcU], wb[kDcU];
-    uint32_t sa[kDcU], sb[kDcU];
-    if (nbatch > 0) load(0, wa, sa);
-    for (int q = 0; q < nbatch; q += 2) {
-        if (q + 1 < nbatch) load(q + 1, wb, sb);
-        compute(q, wa, sa);
-        if (q + 2 < nbatch) load(q + 2, wa, sa);
-        if (q + 1 < nbatch) compute(q + 1, wb, sb);
+    for (int lr = tid; lr < n_end - n_begin; lr += kDcThreads) {
+        float acc = 0.0f;
+        for (int j = 0; j < nslot; ++j) acc = fmaf(s_w[j], part[j * p.rows_per_wg + lr], acc);   // slot order
+        p.out[(size_t)t * p.N + n_begin + lr] = acc;
     }
 }
 
-size_t down_combine_lds(int k, bool shared, int I) { return (size_t)(k + (shared ? 1 : 0)) * I * 4; }
+// LDS of a down-combine workgroup: the slots' h (4 * dc_plane_ld(I) bytes each), padded
+// to whole 1 KiB copy blocks, then the [slots][kDcMaxRows] float table.
+size_t down_combine_lds(int k, bool shared, int I) {
+    const size_t nslot = (size_t)k + (shared ? 1 : 0);
+    return align_up(nslot * 4 * dc_plane_ld(I), 1024) + nslot * kDcMaxRows * 4;
+}
+
+template <int FMT>
+static void (*down_combine_fn(int U))(const DownCombineParams) {
+    switch (U) {
+        case 1: return down_combine_kernel<FMT, 1>;
+        case 2: return down_combine_kernel<FMT, 2>;
+        case 3: return down_combine_kernel<FMT, 3>;
+        case 4: return down_combine_kernel<FMT, 4>;
+        default: return down_combine_kernel<FMT, 5>;
+    }
+}
+
+// Units per lane per batch for nl units per lane: the U <= 5 (larger batches of kDcRows
+// rows do not fit the registers) that wastes the fewest loads, the larger on a tie.
+static int down_combine_batch(int nl) {
+    int best = 1, waste = INT_MAX;
+    for (int u = 1; u <= 5; ++u) {
+        const int w = (nl + u - 1) / u * u - nl;
+        if (w <= waste) {
+            best = u;
+            waste = w;
+        }
+    }
+    return best;
+}
 
 moe_status down_combine_launch(int fmt, DownCombineParams p, hipStream_t stream) {
+    const bool mfma = fmt == kFmtMXFP4;
     const int units = fmt == kFmtMXFP4 ? p.I / 32 : p.I / 16;
-    // 16 lanes per row (4 rows per wave pass) while a lane still gets >= 4 units, so a
-    // workgroup's few dozen rows spread over all 8 waves; short rows use the GEMV layout
-    p.G = 16;
-    p.nl = (units + 15) / 16;
-    if (p.nl < 4) pick_layout(units, false, &p.G, &p.nl);
-    const int rows_per_pass = 64 / p.G;
-    // about one workgroup per CU in total (LDS holds k+1 rows of h)
+    int U = 1, rpp = MOE_DM_ROUND;                         // MFMA path: 16-row tiles, the last one clamped
+
+    if (!mfma) {
+        // 16 lanes per row segment while a lane still gets >= 4 units; short rows use the
+        // GEMV layout
+        p.G = 16;
+        p.nl = (units + 15) / 16;
+        if (p.nl < 4) pick_layout(units, false, &p.G, &p.nl);
+        U = down_combine_batch(p.nl);
+        rpp = (64 / p.G) * kDcRows;
+    }
+    // about one workgroup per CU in total (LDS holds k+1 rows of h; an HBM-bound launch
+    // does not need every CU), whole passes, at most kDcMaxRows rows
     const long long rows_total = (long long)p.N * p.T;
     int rpw = (int)((rows_total + 255) / 256);
-    rpw = max(rpw, rows_per_pass);
-    rpw = (rpw + rows_per_pass - 1) / rows_per_pass * rows_per_pass;
+    rpw = (max(rpw, rpp) + rpp - 1) / rpp * rpp;
+    rpw = min(rpw, max(rpp, kDcMaxRows / rpp * rpp));
     p.rows_per_wg = rpw;
+    const int nslot = p.k + (p.sw ? 1 : 0);
+    p.h_lds_bytes = (int)align_up((size_t)nslot * 4 * dc_plane_ld(p.I), 1024);
     const size_t lds = down_combine_lds(p.k, p.sw != nullptr, p.I);
     dim3 grid((p.N + rpw - 1) / rpw, p.T);
-    auto fn = fmt == kFmtMXFP4 ? down_combine_kernel<kFmtMXFP4> : down_combine_kernel<kFmtFP8>;
-    hipLaunchKernelGGL(fn, grid, dim3(kDcThreads), lds, stream, p);
+    if (mfma) {
+        down_combine_mfma_launch(p, grid, lds, stream);
+    } else {
+        hipLaunchKernelGGL(down_combine_fn<kFmtFP8>(U), grid, dim3(kDcThreads), lds, stream, p);
+    }
     return launch_check("moe_expert_down_combine");
 }
 

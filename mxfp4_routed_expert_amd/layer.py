@@ -43,8 +43,14 @@ class LayerWeights:
         return self.w_router.shape[0]
 
 
-# LDS a down-combine workgroup may hold: k + 1 float32 rows of d_ff
+# LDS a down-combine workgroup may hold: per slot (k, +1 with a shared expert) the h row
+# in 4 * roundup(d_ff, 256) bytes and a table of 128 floats (the library's own rule)
 FUSED_LDS_LIMIT = 150 * 1024
+
+
+def down_combine_lds(k: int, shared: bool, d_ff: int) -> int:
+    s = k + (1 if shared else 0)
+    return s * 4 * ((d_ff + 255) // 256 * 256) + s * 128 * 4
 
 
 def fuses(w: LayerWeights, T: int) -> bool:
@@ -54,7 +60,7 @@ def fuses(w: LayerWeights, T: int) -> bool:
     ex, sh = w.experts, w.shared
     return (w.act == "float" and w.p_down is None and w.p_up is None and 1 <= T <= 4
             and (sh is None or (sh.fmt == ex.fmt and sh.d_model == ex.d_model and sh.d_ff == ex.d_ff))
-            and (w.k + (sh is not None)) * ex.d_ff * 4 <= FUSED_LDS_LIMIT)
+            and down_combine_lds(w.k, sh is not None, ex.d_ff) <= FUSED_LDS_LIMIT)
 
 
 class MoELayer:
