@@ -2,78 +2,116 @@
 //
 // The pages group work per expert (rabbit README, features list: each expert's matmul
 // starts when its own bytes land) and run a step's routed experts in one launch
-// (Rulith Inference README, engine section).  Here: a histogram of expert ids (LDS
-// atomics -- counts do not depend on order), an exclusive prefix scan giving each
-// expert's first row, and a stable scatter in which every expert walks the pairs in
-// ascending order, so positions never depend on timing.
+// (Rulith Inference README, engine section).  Here: per-wave histograms of expert ids
+// (LDS atomics -- counts do not depend on order), exclusive prefix scans giving each
+// (wave, expert) its first row, and a scatter in which each wave places its pairs in
+// order, ranking equal ids within a 64-pair chunk by wave ballots -- so positions never
+// depend on timing.
 #include "common.h"
 
 namespace moe {
 namespace {
 
-constexpr int kPermThreads = 1024;
-constexpr int kPermIdCache = 12288;   // pair ids cached in LDS when P fits
+constexpr int kPermWaves = 16;
+constexpr int kPermThreads = 64 * kPermWaves;
 
+// Lanes of the wave whose expert id equals this lane's (ids < 2^11; invalid lanes are in no
+// set): the intersection, over the id's bits, of the lanes that agree on the bit.
+MOE_DEV uint64_t lanes_with_same_id(int e, bool valid) {
+    uint64_t m = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 11; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t ones = __ballot(valid && bit);
+        m &= bit ? ones : ~ones;
+    }
+    return m;
+}
+
+// One workgroup.  Wave w owns a contiguous range of 64-pair chunks.  (1) Each wave counts
+// its pairs per expert (LDS atomics: counts do not depend on order).  (2) A prefix over
+// experts, then over waves, gives every (wave, expert) its first row.  (3) Each wave walks
+// its chunks in order; a pair's row is its (wave, expert) base plus the number of lower
+// lanes of the chunk with the same expert, and the group's lowest lane advances the base.
+// Rows therefore follow the pair index within every expert, whatever the timing.
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__restrict__ ids, int P,
                                                                int E, int32_t *__restrict__ offsets,
                                                                int32_t *__restrict__ sorted,
                                                                int32_t *__restrict__ p2r) {
-    extern __shared__ int smem[];
-    int *cnt = smem;                       // [E + 1]
-    int *sid = smem + E + 1;               // [P] when cached
-    __shared__ int s_wave_tot[kPermThreads / 64];
-    const bool cached = P <= kPermIdCache;
-    const int tid = threadIdx.x;
-
-    for (int i = tid; i <= E; i += kPermThreads) cnt[i] = 0;
+    extern __shared__ int wc[];            // [kPermWaves][E]: counts, then bases
+    __shared__ int s_wave_tot[kPermWaves];
+    const int tid = threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(wave_id());
+    for (int i = tid; i < kPermWaves * E; i += kPermThreads) wc[i] = 0;
     __syncthreads();
-    for (int p = tid; p < P; p += kPermThreads) {
-        const int e = ids[p];
-        if (cached) sid[p] = e;
-        if (e >= 0 && e < E) atomicAdd(&cnt[e], 1);
-        else p2r[p] = -1;
+    const int nch = (P + 63) / 64;
+    const int cpw = (nch + kPermWaves - 1) / kPermWaves;
+    const int c0 = min(nch, wave * cpw), c1 = min(nch, c0 + cpw);
+    int *mine = wc + wave * E;
+    for (int c = c0; c < c1; ++c) {
+        const int p = c * 64 + lane;
+        const int e = p < P ? ids[p] : -1;
+        if (e >= 0 && e < E) atomicAdd(&mine[e], 1);
     }
     __syncthreads();
 
-    // exclusive scan of cnt[0..E) -> cnt (E <= 2 * kPermThreads): each thread owns two
-    // consecutive counts; wave-level inclusive scan of pair sums, then wave totals.
-    const int a0 = 2 * tid < E ? cnt[2 * tid] : 0;
-    const int a1 = 2 * tid + 1 < E ? cnt[2 * tid + 1] : 0;
-    int incl = a0 + a1;
-    const int lane = lane_id();
+    // (2) totals per expert, exclusive scan over experts (E <= 2 * kPermThreads: two per
+    // thread), then bases per wave
+    const int ea = 2 * tid, eb = 2 * tid + 1;
+    int ta = 0, tb = 0;
+    if (ea < E)
+        for (int w = 0; w < kPermWaves; ++w) ta += wc[w * E + ea];
+    if (eb < E)
+        for (int w = 0; w < kPermWaves; ++w) tb += wc[w * E + eb];
+    int incl = ta + tb;
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
         const int v = __shfl_up(incl, o, 64);
         if (lane >= o) incl += v;
     }
-    if (lane == 63) s_wave_tot[wave_id()] = incl;
+    if (lane == 63) s_wave_tot[wave] = incl;
     __syncthreads();
     int base = 0, total = 0;
-    for (int w = 0; w < kPermThreads / 64; ++w) {
-        if (w < wave_id()) base += s_wave_tot[w];
+    for (int w = 0; w < kPermWaves; ++w) {
+        if (w < wave) base += s_wave_tot[w];
         total += s_wave_tot[w];
     }
-    const int excl = base + incl - (a0 + a1);
-    if (2 * tid < E) cnt[2 * tid] = excl;
-    if (2 * tid + 1 < E) cnt[2 * tid + 1] = excl + a0;
-    if (tid == 0) cnt[E] = total;
-    __syncthreads();
-    for (int e = tid; e <= E; e += kPermThreads) offsets[e] = cnt[e];
-    for (int r = total + tid; r < P; r += kPermThreads) sorted[r] = -1;
-
-    // stable scatter: expert e visits the pairs in ascending order.
-    for (int e = tid; e < E; e += kPermThreads) {
-        int r = cnt[e];
-        const int end = cnt[e + 1];
-        if (r == end) continue;
-        for (int p = 0; p < P && r < end; ++p) {
-            const int id = cached ? sid[p] : ids[p];
-            if (id == e) {
-                sorted[r] = p;
-                p2r[p] = r;
-                ++r;
-            }
+    int oa = base + incl - (ta + tb), ob = oa + ta;
+    if (ea < E) offsets[ea] = oa;
+    if (eb < E) offsets[eb] = ob;
+    if (tid == 0) offsets[E] = total;
+    if (ea < E)
+        for (int w = 0; w < kPermWaves; ++w) {
+            const int c = wc[w * E + ea];
+            wc[w * E + ea] = oa;
+            oa += c;
         }
+    if (eb < E)
+        for (int w = 0; w < kPermWaves; ++w) {
+            const int c = wc[w * E + eb];
+            wc[w * E + eb] = ob;
+            ob += c;
+        }
+    for (int r = total + tid; r < P; r += kPermThreads) sorted[r] = -1;
+    __syncthreads();
+
+    // (3) stable scatter, chunk by chunk
+    const uint64_t below = (1ull << lane) - 1ull;
+    for (int c = c0; c < c1; ++c) {
+        const int p = c * 64 + lane;
+        const int e = p < P ? ids[p] : -1;
+        const bool valid = e >= 0 && e < E;
+        const uint64_t same = lanes_with_same_id(e, valid);
+        if (valid) {
+            const int r = mine[e] + __popcll(same & below);
+            sorted[r] = p;
+            p2r[p] = r;
+        } else if (p < P) {
+            p2r[p] = -1;
+        }
+        // the group's lowest lane moves the base past the group (after every lane read it:
+        // a wave's LDS accesses complete in order)
+        if (valid && (same & below) == 0) mine[e] += __popcll(same);
     }
 }
 
@@ -93,84 +131,6 @@ __global__ __launch_bounds__(256) void permute_small_kernel(const int32_t *__res
     }
     __syncthreads();
     small_permutation(sid, P, E, offsets, sorted, p2r, tid, blockDim.x);
-}
-
-// Many pairs (prefill): a bitonic sort of the unique keys (expert << s) | p in LDS by one
-// workgroup gives the stable order directly, whatever the routing skew; invalid ids sort
-// last.  Offsets come from the same histogram + scan as the counting sort.
-constexpr int kPermSortMax = 8192;
-
-__global__ __launch_bounds__(1024) void permute_sort_kernel(const int32_t *__restrict__ ids, int P, int E, int n2,
-                                                            int shift, int32_t *__restrict__ offsets,
-                                                            int32_t *__restrict__ sorted,
-                                                            int32_t *__restrict__ p2r) {
-    extern __shared__ uint32_t keys[];          // [n2]
-    __shared__ int cnt[MOE_MAX_EXPERTS + 1];
-    __shared__ int s_wave_tot[16];
-    const int tid = threadIdx.x;
-    for (int i = tid; i <= E; i += 1024) cnt[i] = 0;
-    __syncthreads();
-    for (int i = tid; i < n2; i += 1024) {
-        uint32_t key = 0xffffffffu;
-        if (i < P) {
-            const int e = ids[i];
-            if (e >= 0 && e < E) {
-                key = ((uint32_t)e << shift) | (uint32_t)i;
-                atomicAdd(&cnt[e], 1);
-            } else {
-                p2r[i] = -1;
-            }
-        }
-        keys[i] = key;
-    }
-    __syncthreads();
-    for (int k = 2; k <= n2; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < n2; i += 1024) {
-                const int l = i ^ j;
-                if (l > i) {
-                    const uint32_t a = keys[i], b = keys[l];
-                    const bool up = (i & k) == 0;
-                    if ((a > b) == up) {
-                        keys[i] = b;
-                        keys[l] = a;
-                    }
-                }
-            }
-            __syncthreads();
-        }
-    }
-    // exclusive scan of the counts (E <= 2048: two per thread)
-    const int a0 = 2 * tid < E ? cnt[2 * tid] : 0;
-    const int a1 = 2 * tid + 1 < E ? cnt[2 * tid + 1] : 0;
-    int incl = a0 + a1;
-    const int lane = lane_id();
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int v = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += v;
-    }
-    if (lane == 63) s_wave_tot[wave_id()] = incl;
-    __syncthreads();
-    int base = 0, total = 0;
-    for (int w = 0; w < 16; ++w) {
-        if (w < wave_id()) base += s_wave_tot[w];
-        total += s_wave_tot[w];
-    }
-    const int excl = base + incl - (a0 + a1);
-    if (2 * tid < E) offsets[2 * tid] = excl;
-    if (2 * tid + 1 < E) offsets[2 * tid + 1] = excl + a0;
-    if (tid == 0) offsets[E] = total;
-    const uint32_t pmask = (1u << shift) - 1u;
-    for (int r = tid; r < P; r += 1024) {
-        if (r < total) {
-            const int pp = (int)(keys[r] & pmask);
-            sorted[r] = pp;
-            p2r[pp] = r;
-        } else {
-            sorted[r] = -1;
-        }
-    }
 }
 
 }  // namespace
@@ -197,15 +157,7 @@ extern "C" moe_status moe_permute(int32_t T, int32_t k, int32_t E, const int32_t
                            expert_offsets, sorted_pairs, pair_to_row);
         return launch_check("moe_permute: permute_small_kernel");
     }
-    if (P <= kPermSortMax) {
-        int n2 = 1, shift = 0;
-        while (n2 < P) n2 <<= 1;
-        while ((1 << shift) < P) ++shift;
-        hipLaunchKernelGGL(permute_sort_kernel, dim3(1), dim3(1024), (size_t)n2 * sizeof(uint32_t), (hipStream_t)stream,
-                           topk_ids, P, E, n2, shift, expert_offsets, sorted_pairs, pair_to_row);
-        return launch_check("moe_permute: permute_sort_kernel");
-    }
-    const size_t lds = (size_t)(E + 1 + (P <= kPermIdCache ? P : 0)) * sizeof(int);
+    const size_t lds = (size_t)kPermWaves * E * sizeof(int);
     hipLaunchKernelGGL(permute_kernel, dim3(1), dim3(kPermThreads), lds, (hipStream_t)stream, topk_ids, P, E,
                        expert_offsets, sorted_pairs, pair_to_row);
     return launch_check("moe_permute: permute_kernel");
