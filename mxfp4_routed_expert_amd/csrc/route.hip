@@ -86,71 +86,111 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_logits_kernel(const 
     }
 }
 
-// Many tokens: a tiled float64 product.  A workgroup owns 128 tokens x 128 rows and one
-// of kRouterKS slices of H; bf16 tiles are converted once to float64 into LDS (k-major),
-// each thread accumulates an 8 x 8 block of exact products in float64.  The slices' partial
-// sums go to the workspace and router_reduce_kernel adds them in a fixed order and rounds
-// once to float32 -- the same logits as the one-wave form, up to float64 rounding.
+// Many tokens: a tiled float64 product.  A workgroup owns 128 tokens x 64 rows and one of
+// kRouterKS slices of H; bf16 tiles are converted once to float64 into LDS (k-major), and
+// each thread accumulates an 8 x 4 block of exact products in float64 (tokens ty + 16i,
+// rows tx + 16j: the 16 lanes of a row group read 16 consecutive doubles, so there are no
+// LDS bank conflicts; the small tile keeps two workgroups on a CU).  The next stage's
+// values are loaded while the current one is multiplied.  The slices' partial sums go to
+// the workspace and router_reduce_kernel adds them in a fixed order and rounds once to
+// float32 -- the same logits as the one-wave form, up to float64 rounding.
 constexpr int kRouterKS = 16;   // K slices
-constexpr int kRtTile = 128;
+constexpr int kRtTok = 128;     // tokens per tile
+constexpr int kRtRow = 64;      // rows per tile
 constexpr int kRtKC = 16;       // bf16 values per stage
+constexpr int kRtThin = 16;     // row tiles with at most this many rows use plain dot products
 
-__global__ __launch_bounds__(256) void router_tiled_kernel(const uint16_t *__restrict__ x,
-                                                           const uint16_t *__restrict__ wr,
-                                                           const uint16_t *__restrict__ wsg, int T, int H,
-                                                           int E, int rows, double *__restrict__ partial) {
-    __shared__ __align__(16) double xs[kRtKC][kRtTile];
-    __shared__ __align__(16) double wsm[kRtKC][kRtTile];
+__global__ __launch_bounds__(256, 2) void router_tiled_kernel(const uint16_t *__restrict__ x,
+                                                              const uint16_t *__restrict__ wr,
+                                                              const uint16_t *__restrict__ wsg, int T, int H,
+                                                              int E, int rows, double *__restrict__ partial) {
+    __shared__ __align__(16) double xs[kRtKC][kRtTok];
+    __shared__ __align__(16) double wsm[kRtKC][kRtRow];
     const int tid = threadIdx.x;
-    const int t0 = blockIdx.y * kRtTile, r0 = blockIdx.x * kRtTile;
+    const int t0 = blockIdx.y * kRtTok, r0 = blockIdx.x * kRtRow;
     const int ks = blockIdx.z;
     const int hs = H / kRouterKS;                      // H % (32 * kRouterKS) is checked on the host
     const int h0 = ks * hs, h1 = h0 + hs;
+    auto wrow_of = [&](int r) { return r < E ? wr + (size_t)r * H : wsg; };
+
+    // A tile with few rows (the shared-gate row after a whole number of row tiles, or a
+    // small E): each (token, row) pair of the tile is one thread's plain dot product over the
+    // slice, in the same order as the tiled form.
+    if (rows - r0 <= kRtThin) {
+        const int nr = rows - r0;
+        for (int i = tid; i < kRtTok * nr; i += 256) {
+            const int t = t0 + i / nr, r = r0 + i % nr;
+            if (t >= T) continue;
+            const uint16_t *xr = x + (size_t)t * H, *wrr = wrow_of(r);
+            double s = 0.0;
+            for (int h = h0; h < h1; h += 8) {
+                const u32x4 xv = *(const u32x4 *)(xr + h), wv = *(const u32x4 *)(wrr + h);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const f32x2 fx = bf16x2_to_f32x2(xv[q]), fw = bf16x2_to_f32x2(wv[q]);
+                    s = fma((double)fx.x, (double)fw.x, s);
+                    s = fma((double)fx.y, (double)fw.y, s);
+                }
+            }
+            partial[((size_t)ks * T + t) * rows + r] = s;
+        }
+        return;
+    }
+
     const int ty = tid >> 4, tx = tid & 15;
-    // staging: thread -> (tile row tid/2, 8 values at (tid&1)*8)
-    const int lr = tid >> 1, lh = (tid & 1) * 8;
-    const int tt = min(t0 + lr, T - 1), rr = min(r0 + lr, rows - 1);
-    const bool tok_ok = t0 + lr < T, row_ok = r0 + lr < rows;
+    // staging: x thread -> (token tid/2, 8 values at (tid&1)*8); w thread -> (row tid/4,
+    // 4 values at (tid&3)*4)
+    const int lt = tid >> 1, lh = (tid & 1) * 8;
+    const int lw = tid >> 2, lk = (tid & 3) * 4;
+    const int tt = min(t0 + lt, T - 1), rr = min(r0 + lw, rows - 1);
+    const bool tok_ok = t0 + lt < T, row_ok = r0 + lw < rows;
     const uint16_t *xrow = x + (size_t)tt * H;
-    const uint16_t *wrow = rr < E ? wr + (size_t)rr * H : wsg;
-    double acc[8][8];
+    const uint16_t *wrow = wrow_of(rr);
+    double acc[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0;
+        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+    u32x4 xv = *(const u32x4 *)(xrow + h0 + lh);
+    u32x2 wv = __builtin_nontemporal_load((const u32x2 *)(wrow + h0 + lk));
     for (int h = h0; h < h1; h += kRtKC) {
-        const u32x4 xv = *(const u32x4 *)(xrow + h + lh);
-        const u32x4 wv = __builtin_nontemporal_load((const u32x4 *)(wrow + h + lh));
-        __syncthreads();
+        __syncthreads();                               // the previous stage is consumed
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const f32x2 fx = bf16x2_to_f32x2(xv[q]), fw = bf16x2_to_f32x2(wv[q]);
-            xs[lh + 2 * q][lr] = tok_ok ? (double)fx.x : 0.0;
-            xs[lh + 2 * q + 1][lr] = tok_ok ? (double)fx.y : 0.0;
-            wsm[lh + 2 * q][lr] = row_ok ? (double)fw.x : 0.0;
-            wsm[lh + 2 * q + 1][lr] = row_ok ? (double)fw.y : 0.0;
+            const f32x2 fx = bf16x2_to_f32x2(xv[q]);
+            xs[lh + 2 * q][lt] = tok_ok ? (double)fx.x : 0.0;
+            xs[lh + 2 * q + 1][lt] = tok_ok ? (double)fx.y : 0.0;
         }
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const f32x2 fw = bf16x2_to_f32x2(wv[q]);
+            wsm[lk + 2 * q][lw] = row_ok ? (double)fw.x : 0.0;
+            wsm[lk + 2 * q + 1][lw] = row_ok ? (double)fw.y : 0.0;
+        }
+        const int hn = min(h + kRtKC, h1 - kRtKC);     // (the last stage reloads itself, unused)
+        xv = *(const u32x4 *)(xrow + hn + lh);
+        wv = __builtin_nontemporal_load((const u32x2 *)(wrow + hn + lk));
         __syncthreads();
 #pragma unroll 4
         for (int kk = 0; kk < kRtKC; ++kk) {
-            double a[8], b[8];
+            double a[8], b[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) a[i] = xs[kk][ty * 8 + i];
+            for (int i = 0; i < 8; ++i) a[i] = xs[kk][ty + 16 * i];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) b[j] = wsm[kk][tx * 8 + j];
+            for (int j = 0; j < 4; ++j) b[j] = wsm[kk][tx + 16 * j];
 #pragma unroll
             for (int i = 0; i < 8; ++i)
 #pragma unroll
-                for (int j = 0; j < 8; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+                for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
         }
     }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const int t = t0 + ty * 8 + i;
+        const int t = t0 + ty + 16 * i;
         if (t >= T) break;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int r = r0 + tx * 8 + j;
+        for (int j = 0; j < 4; ++j) {
+            const int r = r0 + tx + 16 * j;
             if (r < rows) partial[((size_t)ks * T + t) * rows + r] = acc[i][j];
         }
     }
@@ -371,7 +411,7 @@ moe_status route_logits(const moe_route_desc *d, const void *x, const void *w_ro
     float *logits = (float *)ws;
     if (router_tiled(d)) {
         double *partial = (double *)((unsigned char *)ws + align_up((size_t)d->T * (d->E + 1) * sizeof(float), 256));
-        dim3 gt((rows + kRtTile - 1) / kRtTile, (d->T + kRtTile - 1) / kRtTile, kRouterKS);
+        dim3 gt((rows + kRtRow - 1) / kRtRow, (d->T + kRtTok - 1) / kRtTok, kRouterKS);
         hipLaunchKernelGGL(router_tiled_kernel, gt, dim3(256), 0, s, (const uint16_t *)x, (const uint16_t *)w_router,
                            (const uint16_t *)w_shared_gate, d->T, d->H, d->E, rows, partial);
         MOE_TRY(launch_check("moe_route: router_tiled_kernel"));
