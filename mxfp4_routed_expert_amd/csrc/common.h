@@ -17,6 +17,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
 
 namespace moe {
@@ -89,7 +90,7 @@ constexpr int kMaxOffsetChunks = MOE_MAX_EXPERTS / 64 + 1;
 // Index of the slot-th expert that owns rows (same value in every lane), -1 if none.
 // All offsets are loaded in one batch of independent loads, so the lookup costs one
 // memory round trip; no LDS and no barrier.
-MOE_DEV int wave_nth_nonempty(const int32_t *offsets, int E, int slot) {
+MOE_DEV int wave_nth_nonempty(const int32_t *offsets, int E, int slot, int *row0 = nullptr, int *rows = nullptr) {
     const int lane = lane_id();
     int o[kMaxOffsetChunks];
 #pragma unroll
@@ -111,7 +112,12 @@ MOE_DEV int wave_nth_nonempty(const int32_t *offsets, int E, int slot) {
         if (slot < base + cnt) {
             const int before = __popcll(m & ((1ull << lane) - 1ull));
             const uint64_t hit = __ballot(ne && before == slot - base);
-            return c * 64 + __ffsll((long long)hit) - 1;
+            const int l = __ffsll((long long)hit) - 1;
+            // the expert's first row and row count come from the offsets already loaded
+            const int r0 = __builtin_amdgcn_readfirstlane(__shfl(o[c], l, kWave));
+            if (row0) *row0 = r0;
+            if (rows) *rows = __builtin_amdgcn_readfirstlane(__shfl(o1, l, kWave)) - r0;
+            return c * 64 + l;
         }
         base += cnt;
     }

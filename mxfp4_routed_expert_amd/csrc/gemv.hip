@@ -329,10 +329,8 @@ __global__ MOE_GEMV_ATTR void gemv_kernel(const GemvParams p0) {
     }
     int e = 0, row0 = 0, M = p.T;
     if (ROUTED && !shared) {
-        e = wave_nth_nonempty(p.offsets, p.E, blockIdx.y);
+        e = wave_nth_nonempty(p.offsets, p.E, blockIdx.y, &row0, &M);
         if (e < 0) return;
-        row0 = p.offsets[e];
-        M = p.offsets[e + 1] - row0;
         if (row0 < 0 || M <= 0 || row0 + M > p.R) return;
     }
     const int units = units_per_row<FMT>(p.K);

@@ -86,21 +86,22 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_logits_kernel(const 
     }
 }
 
-// Many tokens: a tiled float64 product.  A workgroup owns 128 tokens x 64 rows and one of
-// kRouterKS slices of H; bf16 tiles are converted once to float64 into LDS (k-major), and
-// each thread accumulates an 8 x 4 block of exact products in float64 (tokens ty + 16i,
-// rows tx + 16j: the 16 lanes of a row group read 16 consecutive doubles, so there are no
-// LDS bank conflicts; the small tile keeps two workgroups on a CU).  The next stage's
-// values are loaded while the current one is multiplied.  The slices' partial sums go to
-// the workspace and router_reduce_kernel adds them in a fixed order and rounds once to
-// float32 -- the same logits as the one-wave form, up to float64 rounding.
+// Many tokens: a tiled float64 product on the matrix cores.  A workgroup owns 128 tokens x
+// 64 rows and one of kRouterKS slices of H; bf16 tiles are converted once to float64 into
+// LDS (k-major).  Wave w multiplies tokens 32w .. 32w+31 by the 64 rows with
+// v_mfma_f64_16x16x4_f64 (lane l supplies A[l%16][l/16] and B[l/16][l%16]; it receives
+// C[l/16 + 4i][l%16]); the products of two bf16 values are exact in float64 and the sums
+// are float64.  The next stage's values are loaded while the current one is multiplied.
+// The slices' partial sums go to the workspace and router_reduce_kernel adds them in a
+// fixed order and rounds once to float32 -- the same logits as the one-wave form, up to
+// float64 rounding.
 constexpr int kRouterKS = 16;   // K slices
 constexpr int kRtTok = 128;     // tokens per tile
 constexpr int kRtRow = 64;      // rows per tile
 constexpr int kRtKC = 16;       // bf16 values per stage
 constexpr int kRtThin = 16;     // row tiles with at most this many rows use plain dot products
 
-__global__ __launch_bounds__(256, 2) void router_tiled_kernel(const uint16_t *__restrict__ x,
+__global__ __launch_bounds__(256) void router_tiled_kernel(const uint16_t *__restrict__ x,
                                                               const uint16_t *__restrict__ wr,
                                                               const uint16_t *__restrict__ wsg, int T, int H,
                                                               int E, int rows, double *__restrict__ partial) {
@@ -137,22 +138,23 @@ __global__ __launch_bounds__(256, 2) void router_tiled_kernel(const uint16_t *__
         return;
     }
 
-    const int ty = tid >> 4, tx = tid & 15;
+    const int lane = lane_id(), wave = wave_id();
+    const int lr = lane & 15, lk = lane >> 4;          // MFMA operand row/column, K index
     // staging: x thread -> (token tid/2, 8 values at (tid&1)*8); w thread -> (row tid/4,
     // 4 values at (tid&3)*4)
     const int lt = tid >> 1, lh = (tid & 1) * 8;
-    const int lw = tid >> 2, lk = (tid & 3) * 4;
+    const int lw = tid >> 2, lq = (tid & 3) * 4;
     const int tt = min(t0 + lt, T - 1), rr = min(r0 + lw, rows - 1);
     const bool tok_ok = t0 + lt < T, row_ok = r0 + lw < rows;
     const uint16_t *xrow = x + (size_t)tt * H;
     const uint16_t *wrow = wrow_of(rr);
-    double acc[8][4];
+    f64x4 acc[2][4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = 0.0;
+        for (int j = 0; j < 4; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
     u32x4 xv = *(const u32x4 *)(xrow + h0 + lh);
-    u32x2 wv = __builtin_nontemporal_load((const u32x2 *)(wrow + h0 + lk));
+    u32x2 wv = __builtin_nontemporal_load((const u32x2 *)(wrow + h0 + lq));
     for (int h = h0; h < h1; h += kRtKC) {
         __syncthreads();                               // the previous stage is consumed
 #pragma unroll
@@ -164,36 +166,38 @@ __global__ __launch_bounds__(256, 2) void router_tiled_kernel(const uint16_t *__
 #pragma unroll
         for (int q = 0; q < 2; ++q) {
             const f32x2 fw = bf16x2_to_f32x2(wv[q]);
-            wsm[lk + 2 * q][lw] = row_ok ? (double)fw.x : 0.0;
-            wsm[lk + 2 * q + 1][lw] = row_ok ? (double)fw.y : 0.0;
+            wsm[lq + 2 * q][lw] = row_ok ? (double)fw.x : 0.0;
+            wsm[lq + 2 * q + 1][lw] = row_ok ? (double)fw.y : 0.0;
         }
         const int hn = min(h + kRtKC, h1 - kRtKC);     // (the last stage reloads itself, unused)
         xv = *(const u32x4 *)(xrow + hn + lh);
-        wv = __builtin_nontemporal_load((const u32x2 *)(wrow + hn + lk));
+        wv = __builtin_nontemporal_load((const u32x2 *)(wrow + hn + lq));
         __syncthreads();
-#pragma unroll 4
-        for (int kk = 0; kk < kRtKC; ++kk) {
-            double a[8], b[4];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) a[i] = xs[kk][ty + 16 * i];
+        for (int k0 = 0; k0 < kRtKC; k0 += 4) {
+            double a[2], b[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) b[j] = wsm[kk][tx + 16 * j];
+            for (int i = 0; i < 2; ++i) a[i] = xs[k0 + lk][32 * wave + 16 * i + lr];
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
+            for (int j = 0; j < 4; ++j) b[j] = wsm[k0 + lk][16 * j + lr];
 #pragma unroll
-                for (int j = 0; j < 4; ++j) acc[i][j] = fma(a[i], b[j], acc[i][j]);
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f64_16x16x4f64(a[i], b[j], acc[i][j], 0, 0, 0);
         }
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int t = t0 + ty + 16 * i;
-        if (t >= T) break;
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = r0 + tx + 16 * j;
-            if (r < rows) partial[((size_t)ks * T + t) * rows + r] = acc[i][j];
+        for (int v = 0; v < 4; ++v) {
+            const int t = t0 + 32 * wave + 16 * i + lk + 4 * v;
+            if (t >= T) continue;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = r0 + 16 * j + lr;
+                if (r < rows) partial[((size_t)ks * T + t) * rows + r] = acc[i][j][v];
+            }
         }
-    }
 }
 
 __global__ __launch_bounds__(256) void router_reduce_kernel(const double *__restrict__ partial, int n,
