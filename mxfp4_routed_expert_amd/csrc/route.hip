@@ -98,7 +98,7 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_logits_kernel(const 
 constexpr int kRouterKS = 16;   // K slices
 constexpr int kRtTok = 128;     // tokens per tile
 constexpr int kRtRow = 64;      // rows per tile
-constexpr int kRtKC = 16;       // bf16 values per stage
+constexpr int kRtKC = 32;       // bf16 values per stage
 constexpr int kRtThin = 16;     // row tiles with at most this many rows use plain dot products
 
 __global__ __launch_bounds__(256) void router_tiled_kernel(const uint16_t *__restrict__ x,
@@ -140,10 +140,10 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const uint16_t *__res
 
     const int lane = lane_id(), wave = wave_id();
     const int lr = lane & 15, lk = lane >> 4;          // MFMA operand row/column, K index
-    // staging: x thread -> (token tid/2, 8 values at (tid&1)*8); w thread -> (row tid/4,
-    // 4 values at (tid&3)*4)
-    const int lt = tid >> 1, lh = (tid & 1) * 8;
-    const int lw = tid >> 2, lq = (tid & 3) * 4;
+    // staging (kRtKC = 32 values a stage): x thread -> (token tid/2, 16 values at (tid&1)*16);
+    // w thread -> (row tid/4, 8 values at (tid&3)*8)
+    const int lt = tid >> 1, lh = (tid & 1) * 16;
+    const int lw = tid >> 2, lq = (tid & 3) * 8;
     const int tt = min(t0 + lt, T - 1), rr = min(r0 + lw, rows - 1);
     const bool tok_ok = t0 + lt < T, row_ok = r0 + lw < rows;
     const uint16_t *xrow = x + (size_t)tt * H;
@@ -153,25 +153,25 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const uint16_t *__res
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f64x4{0.0, 0.0, 0.0, 0.0};
-    u32x4 xv = *(const u32x4 *)(xrow + h0 + lh);
-    u32x2 wv = __builtin_nontemporal_load((const u32x2 *)(wrow + h0 + lq));
+    u32x4 xv0 = *(const u32x4 *)(xrow + h0 + lh), xv1 = *(const u32x4 *)(xrow + h0 + lh + 8);
+    u32x4 wv = __builtin_nontemporal_load((const u32x4 *)(wrow + h0 + lq));
     for (int h = h0; h < h1; h += kRtKC) {
         __syncthreads();                               // the previous stage is consumed
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const f32x2 fx = bf16x2_to_f32x2(xv[q]);
-            xs[lh + 2 * q][lt] = tok_ok ? (double)fx.x : 0.0;
-            xs[lh + 2 * q + 1][lt] = tok_ok ? (double)fx.y : 0.0;
-        }
-#pragma unroll
-        for (int q = 0; q < 2; ++q) {
+            const f32x2 f0 = bf16x2_to_f32x2(xv0[q]), f1 = bf16x2_to_f32x2(xv1[q]);
+            xs[lh + 2 * q][lt] = tok_ok ? (double)f0.x : 0.0;
+            xs[lh + 2 * q + 1][lt] = tok_ok ? (double)f0.y : 0.0;
+            xs[lh + 8 + 2 * q][lt] = tok_ok ? (double)f1.x : 0.0;
+            xs[lh + 8 + 2 * q + 1][lt] = tok_ok ? (double)f1.y : 0.0;
             const f32x2 fw = bf16x2_to_f32x2(wv[q]);
             wsm[lq + 2 * q][lw] = row_ok ? (double)fw.x : 0.0;
             wsm[lq + 2 * q + 1][lw] = row_ok ? (double)fw.y : 0.0;
         }
         const int hn = min(h + kRtKC, h1 - kRtKC);     // (the last stage reloads itself, unused)
-        xv = *(const u32x4 *)(xrow + hn + lh);
-        wv = __builtin_nontemporal_load((const u32x2 *)(wrow + hn + lq));
+        xv0 = *(const u32x4 *)(xrow + hn + lh);
+        xv1 = *(const u32x4 *)(xrow + hn + lh + 8);
+        wv = __builtin_nontemporal_load((const u32x4 *)(wrow + hn + lq));
         __syncthreads();
 #pragma unroll
         for (int k0 = 0; k0 < kRtKC; k0 += 4) {
