@@ -372,7 +372,7 @@ moe_status launch_topk_t(const moe_route_desc *d, const float *logits, int rows,
                          int32_t *p2r, hipStream_t s) {
     auto topk = d->E <= 256 ? topk_kernel<4, PERM> : d->E <= 512 ? topk_kernel<8, PERM>
               : d->E <= 1024 ? topk_kernel<16, PERM> : topk_kernel<32, PERM>;
-    const int tb = d->T < 4 ? 64 * d->T : 256;
+    const int tb = (d->T < 4 && !PERM) ? 64 * d->T : 256;   // the permutation uses every thread
     hipLaunchKernelGGL(topk, dim3((d->T + 3) / 4), dim3(tb), 0, s, logits, rows, d->T, d->E, d->k, d->score,
                        d->renormalize, d->routed_scaling, lb, sb, has_sg ? 1 : 0, ids, w, sg, offs, sorted, p2r);
     return launch_check(PERM ? "moe_route_permute: topk_kernel" : "moe_route: topk_kernel");
