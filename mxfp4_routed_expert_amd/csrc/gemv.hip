@@ -150,8 +150,11 @@ MOE_DEV void stage_activations(const GemvParams &p, unsigned char *smem, int row
     if (threadIdx.x < 8) {
         const int m = threadIdx.x;
         const int r = row0 + c0 + min(m, mc - 1);
-        int a = p.gather ? p.sorted_pairs[r] : r;
-        if (p.gather) a = a >= 0 ? a / p.k : -1;
+        int a = 0;
+        if (p.n_act_rows > 1) {               // one activation row (a single token): no lookup
+            a = p.gather ? p.sorted_pairs[r] : r;
+            if (p.gather) a = a >= 0 ? a / p.k : -1;
+        }
         s_arow[m] = (m < mc && a >= 0 && a < p.n_act_rows) ? a : -1;
     }
     __syncthreads();

@@ -293,6 +293,7 @@ moe_status gemv_mfma_launch(int act, bool pair, GemvParams p, int slots, hipStre
 #define MOE_DM_NT 0              // non-temporal weight loads (off: the two half-lines of a row arrive in separate loads)
 #endif
 constexpr int kDmDepth = MOE_DM_DEPTH;
+constexpr int kDmLoadsPerStep = 4;       // vector memory operations of one step's load (2 units, 2 scales)
 
 MOE_DEV void dm_dma16(const void *src, uint32_t lds_wave_base) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
@@ -423,9 +424,11 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_mfma_kernel(const Dow
 
     // h rows -> LDS by direct copies: slot j's float32 row at byte 4*ld*j, in whole 1 KiB
     // blocks (the tail of a row's last block re-reads its last vector into the row's
-    // padding; 4*ld is a multiple of 1 KiB).  h is small and cache-resident; the copies
-    // complete before the first weight loads are issued, so the compiler's wait counts for
-    // those loads (it does not see the copies) stay exact.
+    // padding; 4*ld is a multiple of 1 KiB).  The copies are not loads the compiler
+    // tracks; they are issued first, the first kDmDepth steps of weight loads after them,
+    // and the wait below lets exactly those kDmLoadsPerStep * kDmDepth loads stay in
+    // flight (memory operations of a wave complete in order), so the copies' latency and
+    // the first weight bytes overlap and the compiler's wait counts stay exact.
     {
         const int act_vec = p.I / 4;
         const int bpr = (act_vec + 63) / 64;                 // copy blocks per row
@@ -436,8 +439,6 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_mfma_kernel(const Dow
             dm_dma16(row + (size_t)v * 4, (uint32_t)(uintptr_t)(smem + (size_t)j * 4 * ld + (size_t)b0 * 16));
         }
     }
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    // first steps in flight during the h conversion
     u32x4 wv[kDmDepth][2];
     uint8_t sv[kDmDepth][2];  // (bytes: a widened copy would be masked at the loop latch, forcing a wait)
     DmIt lp{0, wave % nslot, 0, wave / nslot, nullptr, nullptr, 0, 0};
@@ -448,6 +449,8 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_mfma_kernel(const Dow
         load(lp, wv[d], sv[d]);
         advance(lp);
     }
+    static_assert(kDmLoadsPerStep * kDmDepth <= 63, "vmcnt limit");
+    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(kDmLoadsPerStep * kDmDepth) : "memory");
     // float32 rows -> bf16 hi/lo planes in place (all reads before the barrier, all writes
     // after): plane hi at element 0 of the row's region, lo at element ld; zeros past d_ff
     // and for dropped pairs.  hi = RN_bf16(h), lo = RN_bf16(h - hi) by the packed
