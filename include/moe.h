@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
     MOE_OK = 0,
@@ -70,6 +70,8 @@ typedef struct {
     int32_t score;          /* MOE_SCORE_*                                        */
     int32_t renormalize;    /* 1: divide the selected weights by their sum        */
     float routed_scaling;   /* multiplies the final routing weights               */
+    int32_t n_group;        /* expert groups for group-limited selection (0 or 1: none) */
+    int32_t topk_group;     /* groups kept per token when n_group > 1              */
 } moe_route_desc;
 
 /*
@@ -84,6 +86,13 @@ typedef struct {
  *   sigmoid: s = sigmoid(l); select the k largest s + select_bias (bias used for
  *            selection only); w = s, divided by the selected sum when renormalize != 0.
  *   w *= routed_scaling.  Post-logit arithmetic runs in float64.
+ *   Group-limited selection ("grouped routing", Kimi Linear, and noaux_tc: rabbit README,
+ *   architecture table), when n_group > 1: experts e are in group e / (E / n_group); a
+ *   group's score is the sum of its two largest selection keys (sigmoid) or its largest
+ *   key (softmax), NaN keys counting as -inf; the topk_group best groups are kept (ties to
+ *   the lower group) and the k experts are selected among theirs only.  Needs
+ *   E % n_group == 0, n_group <= 64, E / n_group >= 2 for sigmoid, 1 <= topk_group <=
+ *   n_group and topk_group * (E / n_group) >= k.  The weights are computed as above.
  *   shared_gate[t] = sigmoid(float32(x[t] . w_shared_gate)) when w_shared_gate != NULL.
  * x: bf16 [T][H].  w_router: bf16 [E][H].  logit_bias, select_bias: float32 [E] or NULL
  * (select_bias only with MOE_SCORE_SIGMOID).  w_shared_gate: bf16 [H] or NULL.

@@ -44,7 +44,7 @@ _p, _i32, _sz, _f32 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t, ctypes.c
 
 class RouteDesc(ctypes.Structure):
     _fields_ = [("T", _i32), ("H", _i32), ("E", _i32), ("k", _i32), ("score", _i32),
-                ("renormalize", _i32), ("routed_scaling", _f32)]
+                ("renormalize", _i32), ("routed_scaling", _f32), ("n_group", _i32), ("topk_group", _i32)]
 
 
 class ExpertWeightsC(ctypes.Structure):
@@ -131,8 +131,9 @@ def _workspace(nbytes: int, device):
 # ------------------------------------------------------------------ router
 
 def moe_route(x, w_router, k, score="softmax", renormalize=True, routed_scaling=1.0, logit_bias=None,
-              select_bias=None, w_shared_gate=None, out=None, ws=None):
-    """Returns (topk_ids int32 [T][k], topk_w float32 [T][k], shared_gate float32 [T] or None)."""
+              select_bias=None, w_shared_gate=None, out=None, ws=None, n_group=1, topk_group=1):
+    """Returns (topk_ids int32 [T][k], topk_w float32 [T][k], shared_gate float32 [T] or None).
+    n_group > 1 selects among the topk_group best expert groups only (see moe.h)."""
     T, H = x.shape
     E = w_router.shape[0]
     _need(x, torch.bfloat16, "x")
@@ -140,7 +141,7 @@ def moe_route(x, w_router, k, score="softmax", renormalize=True, routed_scaling=
     _need(logit_bias, torch.float32, "logit_bias", (E,))
     _need(select_bias, torch.float32, "select_bias", (E,))
     _need(w_shared_gate, torch.bfloat16, "w_shared_gate", (H,))
-    d = RouteDesc(T, H, E, k, SCORE[score], 1 if renormalize else 0, routed_scaling)
+    d = RouteDesc(T, H, E, k, SCORE[score], 1 if renormalize else 0, routed_scaling, n_group, topk_group)
     dev = x.device
     if out is None:
         ids = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -171,7 +172,7 @@ def moe_permute(topk_ids, E, out=None):
 
 
 def moe_route_permute(x, w_router, k, score="softmax", renormalize=True, routed_scaling=1.0, logit_bias=None,
-                      select_bias=None, w_shared_gate=None, out=None, ws=None):
+                      select_bias=None, w_shared_gate=None, out=None, ws=None, n_group=1, topk_group=1):
     """moe_route then moe_permute in one call.  Returns (topk_ids, topk_w, shared_gate or None,
     expert_offsets, sorted_pairs, pair_to_row)."""
     T, H = x.shape
@@ -181,7 +182,7 @@ def moe_route_permute(x, w_router, k, score="softmax", renormalize=True, routed_
     _need(logit_bias, torch.float32, "logit_bias", (E,))
     _need(select_bias, torch.float32, "select_bias", (E,))
     _need(w_shared_gate, torch.bfloat16, "w_shared_gate", (H,))
-    d = RouteDesc(T, H, E, k, SCORE[score], 1 if renormalize else 0, routed_scaling)
+    d = RouteDesc(T, H, E, k, SCORE[score], 1 if renormalize else 0, routed_scaling, n_group, topk_group)
     dev = x.device
     if out is None:
         ids = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -343,7 +344,7 @@ def moe_expert_down_combine(w: ExpertWeights, shared, h, h_shared, topk_ids, top
 # ------------------------------------------------------------------ combine, dense, formats
 
 def moe_route_workspace(T, H, E, k, score="softmax"):
-    d = RouteDesc(T, H, E, k, SCORE[score], 1, 1.0)
+    d = RouteDesc(T, H, E, k, SCORE[score], 1, 1.0, 1, 1)
     return lib.moe_route_workspace(ctypes.byref(d))
 
 

@@ -267,8 +267,10 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
                                                    const float *__restrict__ sbias, int has_sg,
                                                    int32_t *__restrict__ ids, float *__restrict__ w,
                                                    float *__restrict__ sg, int32_t *__restrict__ offsets,
-                                                   int32_t *__restrict__ sorted, int32_t *__restrict__ p2r) {
+                                                   int32_t *__restrict__ sorted, int32_t *__restrict__ p2r,
+                                                   int n_group, int topk_group) {
     __shared__ int sid[PERM ? 64 : 1];
+    extern __shared__ double s_gkey[];      // [4 waves][E] selection keys, group-limited form only
     const int t = blockIdx.x * 4 + wave_id();
     if (!PERM && t >= T) return;
     const int lane = lane_id();
@@ -282,6 +284,39 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
         double l = (double)lt[e] + (lbias ? (double)lbias[e] : 0.0);
         if (score == MOE_SCORE_SIGMOID) l = sigmoid_f64(l) + (sbias ? (double)sbias[e] : 0.0);
         key[i] = lane + 64 * i < E ? order_key(l) : 0;
+        if (n_group > 1 && lane + 64 * i < E) s_gkey[wave_id() * E + lane + 64 * i] = l;
+    }
+    if (n_group > 1) {
+        // group-limited selection: lane g < n_group scores group g from the keys in LDS (a
+        // wave's LDS accesses complete in order), the topk_group best groups are taken by
+        // wave arg-max rounds, and keys outside them can no longer be selected
+        const int gs = E / n_group;
+        const double *kw = s_gkey + wave_id() * E;
+        double b1 = -INFINITY, b2 = -INFINITY;
+        if (lane < n_group) {
+            for (int q = 0; q < gs; ++q) {
+                double v = kw[lane * gs + q];
+                if (v != v) v = -INFINITY;
+                if (v > b1) {
+                    b2 = b1;
+                    b1 = v;
+                } else if (v > b2) {
+                    b2 = v;
+                }
+            }
+        }
+        uint64_t gk = lane < n_group ? order_key(score == MOE_SCORE_SIGMOID ? b1 + b2 : b1) : 0;
+        uint64_t keep = 0;
+        for (int r = 0; r < topk_group; ++r) {
+            const int L = wave_best_lane(gk, lane);
+            keep |= 1ull << L;
+            if (lane == L) gk = 0;
+        }
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int e = lane + 64 * i;
+            if (e < E && !((keep >> (e / gs)) & 1ull)) key[i] = 0;
+        }
     }
     uint32_t taken = 0;
     uint64_t hk;
@@ -356,6 +391,16 @@ moe_status validate_route(const moe_route_desc *d) {
                 "moe_route: unknown score %d", d->score);
     MOE_REQUIRE((int64_t)d->T * (d->E + 1) < INT32_MAX && (int64_t)d->T * d->H < INT32_MAX,
                 "moe_route: sizes overflow int32");
+    if (d->n_group > 1) {
+        const int ng = d->n_group, gs = d->E / ng;
+        MOE_REQUIRE(ng <= 64 && d->E % ng == 0, "moe_route: n_group = %d must divide E = %d and be <= 64", ng, d->E);
+        MOE_REQUIRE(d->score != MOE_SCORE_SIGMOID || gs >= 2,
+                    "moe_route: sigmoid group scores need at least 2 experts per group (E / n_group = %d)", gs);
+        MOE_REQUIRE(d->topk_group >= 1 && d->topk_group <= ng && (int64_t)d->topk_group * gs >= d->k,
+                    "moe_route: topk_group = %d must be in [1, n_group] and keep at least k experts", d->topk_group);
+    } else {
+        MOE_REQUIRE(d->n_group >= 0, "moe_route: n_group = %d < 0", d->n_group);
+    }
     return MOE_OK;
 }
 
@@ -373,8 +418,11 @@ moe_status launch_topk_t(const moe_route_desc *d, const float *logits, int rows,
     auto topk = d->E <= 256 ? topk_kernel<4, PERM> : d->E <= 512 ? topk_kernel<8, PERM>
               : d->E <= 1024 ? topk_kernel<16, PERM> : topk_kernel<32, PERM>;
     const int tb = (d->T < 4 && !PERM) ? 64 * d->T : 256;   // the permutation uses every thread
-    hipLaunchKernelGGL(topk, dim3((d->T + 3) / 4), dim3(tb), 0, s, logits, rows, d->T, d->E, d->k, d->score,
-                       d->renormalize, d->routed_scaling, lb, sb, has_sg ? 1 : 0, ids, w, sg, offs, sorted, p2r);
+    const int ng = d->n_group > 1 ? d->n_group : 1;
+    const size_t lds = ng > 1 ? (size_t)(tb / 64) * d->E * sizeof(double) : 0;
+    hipLaunchKernelGGL(topk, dim3((d->T + 3) / 4), dim3(tb), lds, s, logits, rows, d->T, d->E, d->k, d->score,
+                       d->renormalize, d->routed_scaling, lb, sb, has_sg ? 1 : 0, ids, w, sg, offs, sorted, p2r, ng,
+                       ng > 1 ? d->topk_group : 1);
     return launch_check(PERM ? "moe_route_permute: topk_kernel" : "moe_route: topk_kernel");
 }
 

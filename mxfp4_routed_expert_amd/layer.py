@@ -33,6 +33,8 @@ class LayerWeights:
     w_shared_gate: torch.Tensor | None = None  # bf16 [H]
     p_down: torch.Tensor | None = None     # bf16 [L][H]
     p_up: torch.Tensor | None = None       # bf16 [H][L]
+    n_group: int = 1                       # group-limited selection (1: none)
+    topk_group: int = 1
 
     @property
     def H(self):
@@ -107,7 +109,8 @@ class MoELayer:
         if self.fused:
             B.moe_route_permute(x, w.w_router, w.k, w.score, w.renormalize, w.routed_scaling, w.logit_bias,
                                 w.select_bias, w.w_shared_gate,
-                                out=(self.ids, self.topk_w, self.sg, self.offs, self.sp, self.p2r), ws=self.ws_route)
+                                out=(self.ids, self.topk_w, self.sg, self.offs, self.sp, self.p2r), ws=self.ws_route,
+                                n_group=w.n_group, topk_group=w.topk_group)
             if mark is not None:
                 mark("gateup_begin")
             B.moe_expert_gateup_shared(w.experts, w.shared, x, w.k, self.offs, self.sp, out=(self.h, self.h_sh))
@@ -123,7 +126,8 @@ class MoELayer:
                 B.moe_expert_ffn(w.shared, x, w.act, 1, None, None, out=self.y_s, ws=self.ws_sh)
         B.moe_route_permute(x, w.w_router, w.k, w.score, w.renormalize, w.routed_scaling, w.logit_bias,
                             w.select_bias, w.w_shared_gate,
-                            out=(self.ids, self.topk_w, self.sg, self.offs, self.sp, self.p2r), ws=self.ws_route)
+                            out=(self.ids, self.topk_w, self.sg, self.offs, self.sp, self.p2r), ws=self.ws_route,
+                            n_group=w.n_group, topk_group=w.topk_group)
         xe = x
         if w.p_down is not None:
             xe = B.moe_dense_bf16(x, w.p_down, out=self.x_lat)

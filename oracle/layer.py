@@ -80,8 +80,30 @@ class Routing:
     shared_gate: np.ndarray | None   # [T] float64
 
 
+def group_limit(key, n_group, topk_group, score):
+    """Group-limited selection ("grouped routing", Kimi Linear; noaux_tc: rabbit README,
+    architecture table; the pages give no rule, the reading is the published noaux_tc one).
+    Experts e are in group e // (E / n_group).  A group's score is the sum of its two
+    largest keys (sigmoid) or its largest key (softmax); NaN keys count as -inf.  The
+    topk_group best groups per token are kept, ties to the lower group; the keys of every
+    other expert become -inf so that they are never selected."""
+    key = np.array(key, dtype=np.float64)
+    T, E = key.shape
+    gs = E // n_group
+    for t in range(T):
+        kt = np.where(np.isnan(key[t]), -np.inf, key[t]).reshape(n_group, gs)
+        best = np.sort(kt, axis=1)[:, ::-1]
+        gscore = best[:, 0] + best[:, 1] if score == "sigmoid" else best[:, 0]
+        order = sorted(range(n_group), key=lambda g: (-gscore[g], g))
+        keep = set(order[:topk_group])
+        for g in range(n_group):
+            if g not in keep:
+                key[t, g * gs:(g + 1) * gs] = -np.inf
+    return key
+
+
 def route(x_bits, w_router_bits, k, score="softmax", renormalize=True, routed_scaling=1.0,
-          logit_bias=None, select_bias=None, w_shared_gate_bits=None):
+          logit_bias=None, select_bias=None, w_shared_gate_bits=None, n_group=1, topk_group=1):
     """Scoring, top-k and renormalisation.
 
     softmax ("softmax top-10 of 512", rabbit README architecture table): select the k
@@ -90,7 +112,8 @@ def route(x_bits, w_router_bits, k, score="softmax", renormalize=True, routed_sc
     sigmoid ("noaux_tc sigmoid", same table): s = sigmoid(l); select on s + beta with a
     per-expert bias beta used for selection only; weights s_j, divided by their sum when
     renormalising.  Weights are then multiplied by routed_scaling.  The gated shared
-    expert ("gated shared expert", same table) gets weight sigmoid(x . w_sg)."""
+    expert ("gated shared expert", same table) gets weight sigmoid(x . w_sg).  With
+    n_group > 1 the selection is group-limited first (group_limit)."""
     l = router_logits(x_bits, w_router_bits, logit_bias)
     T, E = l.shape
     if score == "softmax":
@@ -101,6 +124,8 @@ def route(x_bits, w_router_bits, k, score="softmax", renormalize=True, routed_sc
                    if select_bias is not None else 0.0)
     else:
         raise ValueError(score)
+    if n_group > 1:
+        key = group_limit(key, n_group, topk_group, score)
     ids = topk_ids(key, k)
     rows = np.arange(T)[:, None]
     if score == "softmax":

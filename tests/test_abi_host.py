@@ -63,6 +63,21 @@ def test_route_rejects_bad_descriptor(kw, msg):
     assert msg in B.last_error()
 
 
+@pytest.mark.parametrize("kw,msg", [
+    (dict(n_group=3), "n_group = 3"),                                   # does not divide E = 8
+    (dict(n_group=128, E=256), "n_group = 128"),                        # more than 64 groups
+    (dict(n_group=4, topk_group=0), "topk_group = 0"),
+    (dict(n_group=4, topk_group=5), "topk_group = 5"),
+    (dict(n_group=4, topk_group=1, k=3), "topk_group = 1"),             # 1 group of 2 < k
+    (dict(n_group=8, topk_group=4, score=1), "at least 2 experts"),     # sigmoid, groups of 1
+    (dict(n_group=-2), "n_group = -2"),
+])
+def test_route_rejects_bad_groups(kw, msg):
+    d = _desc(**kw)
+    st = lib.moe_route(ctypes.byref(d), DUMMY, DUMMY, None, None, None, DUMMY, DUMMY, None, DUMMY, 1 << 20, None)
+    assert st == B.MOE_ERR_INVALID_ARG and msg in B.last_error(), B.last_error()
+
+
 def test_route_null_pointers_and_workspace():
     d = _desc()
     assert lib.moe_route(ctypes.byref(d), None, DUMMY, None, None, None, DUMMY, DUMMY, None, DUMMY, 1 << 20,

@@ -145,6 +145,47 @@ def test_route_matches_oracle(dev, M, name):
         assert_close(to_np(sg), r.shared_gate, f"{name} shared_gate")
 
 
+GROUP_CASES = {
+    # noaux_tc-like: sigmoid + selection bias, 256 experts in 8 groups, 4 kept, top-8
+    "glm_groups_decode": (dataclasses.replace(synth.get("glm52_fp8"), T=3), 8, 4),
+    "glm_groups_64tok": (synth.get("glm52_fp8"), 8, 4),
+    # softmax with group maxima (grouped routing), 512 experts in 16 groups, 2 kept
+    "qwen_groups_decode": (synth.get("qwen38max_decode"), 16, 2),
+    "qwen_groups_tiled": (dataclasses.replace(synth.get("qwen38max_prefill"), T=40), 16, 3),
+    # the kept groups hold exactly k experts: topk_group * group size == k
+    "tiny_groups_exact": (tiny(score="sigmoid", select_bias_std=0.01, k=4), 4, 2),
+}
+
+
+@pytest.mark.parametrize("name", list(GROUP_CASES))
+def test_group_limited_route_matches_oracle(dev, M, name):
+    cfg, ng, tg = GROUP_CASES[name]
+    inp = synth.layer_inputs_np(cfg, 5)
+    wsg = inp.w_shared_gate if cfg.shared == "gated" else None
+    args = (bf16_tensor(inp.x, dev), bf16_tensor(inp.w_router, dev), cfg.k, cfg.score, cfg.renormalize,
+            cfg.routed_scaling, f32_tensor(inp.logit_bias, dev), f32_tensor(inp.select_bias, dev),
+            bf16_tensor(wsg, dev) if wsg is not None else None)
+    ids, w, sg = M.moe_route(*args, n_group=ng, topk_group=tg)
+    r = OL.route(inp.x, inp.w_router, cfg.k, cfg.score, cfg.renormalize, cfg.routed_scaling, inp.logit_bias,
+                 inp.select_bias, wsg, n_group=ng, topk_group=tg)
+    np.testing.assert_array_equal(to_np(ids), r.ids)
+    assert_close(to_np(w), r.weights, f"{name} topk_w")
+    gs = cfg.E // ng
+    assert max(len(set(row // gs)) for row in r.ids) <= tg
+    # the fused entry point selects the same experts and places them the same way
+    ids2, w2, _, offs, sp, p2r = M.moe_route_permute(*args, n_group=ng, topk_group=tg)
+    np.testing.assert_array_equal(to_np(ids2), r.ids)
+    np.testing.assert_array_equal(to_np(w2), to_np(w))
+    ref = OL.permute(r.ids, cfg.E)
+    np.testing.assert_array_equal(to_np(offs), ref.expert_offsets)
+    np.testing.assert_array_equal(to_np(sp), ref.sorted_pairs)
+    np.testing.assert_array_equal(to_np(p2r), ref.pair_to_row)
+    # without the limit the selection differs somewhere (the cases are chosen so)
+    r0 = OL.route(inp.x, inp.w_router, cfg.k, cfg.score, cfg.renormalize, cfg.routed_scaling, inp.logit_bias,
+                  inp.select_bias, wsg)
+    assert (r0.ids != r.ids).any()
+
+
 # ------------------------------------------------------------------ permutation
 
 @pytest.mark.parametrize("name", list(ROUTE_CASES))

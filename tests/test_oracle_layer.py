@@ -289,3 +289,68 @@ def test_sizes_agree_with_pages():
     assert abs(p["experts_total"] * mb / 1e6 - p["experts_tb"]) < 0.01
     # the synthetic intermediate width keeps the same parameter count within 1.5 %
     assert abs(3 * 7168 * 2368 - per_expert_params) / per_expert_params < 0.015
+
+
+# ------------------------------------------------------------------ group-limited selection
+
+def _brute_groups(key_row, n_group, topk_group, score):
+    """Kept groups by enumeration: a valid set's lowest score is at least the highest score
+    outside it; among valid sets, the lowest group indices."""
+    gs = len(key_row) // n_group
+    g = np.where(np.isnan(key_row), -np.inf, key_row).reshape(n_group, gs)
+    gscore = np.array([sorted(r)[-1] + (sorted(r)[-2] if score == "sigmoid" else 0.0) for r in g])
+    valid = []
+    for S in itertools.combinations(range(n_group), topk_group):
+        rest = [x for x in range(n_group) if x not in S]
+        if not rest or min(gscore[list(S)]) >= max(gscore[rest]):
+            valid.append(S)
+    return set(min(valid))
+
+
+def test_group_limit_hand_cases():
+    n = 0
+    for line in open(os.path.join(GOLDEN, "group_routing_cases.txt")):
+        line = line.split("#")[0].strip()
+        if not line:
+            continue
+        head, keys, want = (part.split() for part in line.split("|"))
+        score, ng, tg, k = head[0], int(head[1]), int(head[2]), int(head[3])
+        key = np.array([float(v) for v in keys])[None, :]
+        got = L.topk_ids(L.group_limit(key, ng, tg, score), k)[0]
+        assert list(got) == [int(v) for v in want], line
+        n += 1
+    assert n == 5
+
+
+def test_group_limit_bruteforce():
+    rng = np.random.default_rng(11)
+    for trial in range(300):
+        ng = [2, 4, 8][trial % 3]
+        gs = 2 + trial % 3
+        E = ng * gs
+        tg = 1 + trial % ng
+        k = 1 + trial % min(4, tg * gs)
+        score = "sigmoid" if trial % 2 else "softmax"
+        key = rng.integers(-3, 4, E).astype(np.float64) if trial % 4 < 2 else rng.normal(size=E)
+        kept = _brute_groups(key, ng, tg, score)
+        masked = np.array([key[e] if e // gs in kept else -np.inf for e in range(E)])
+        got = L.topk_ids(L.group_limit(key[None, :], ng, tg, score), k)[0]
+        assert list(got) == _brute_topk(masked, k), (key, ng, tg, k, score)
+        assert all(e // gs in kept for e in got)
+
+
+def test_group_limit_reduces_to_plain_selection():
+    rng = np.random.default_rng(12)
+    x, W = _rand_route_inputs(rng, 5, 64, 32)
+    for score in ("softmax", "sigmoid"):
+        r0 = L.route(x, W, 4, score=score)
+        for ng, tg in ((1, 1), (4, 4), (8, 8)):
+            r1 = L.route(x, W, 4, score=score, n_group=ng, topk_group=tg)
+            np.testing.assert_array_equal(r1.ids, r0.ids)
+            np.testing.assert_array_equal(r1.weights, r0.weights)
+        # a limit changes the selection only through the groups, never the weight formula
+        r2 = L.route(x, W, 4, score=score, n_group=8, topk_group=2)
+        if score == "sigmoid":
+            for t in range(5):
+                s = scipy.special.expit(r2.logits[t, r2.ids[t]])
+                np.testing.assert_allclose(r2.weights[t], s / s.sum(), rtol=1e-14)
