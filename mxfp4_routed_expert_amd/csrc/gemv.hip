@@ -223,6 +223,33 @@ MOE_DEV void stage_activations(const GemvParams &p, unsigned char *smem, int row
     }
 }
 
+MOE_DEV void gemv_dma16(const void *src, uint32_t lds_wave_base) {
+    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
+    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
+}
+
+MOE_DEV void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// A single activation row (one token) copied to LDS row 0 by direct global->LDS loads, in
+// the slot order stage_activations gives it: the swizzle is an XOR, so lane q of the copy
+// reads source vector b*P + (q%P ^ z(b)).  Lanes past the row read vector 0 into the padding
+// of the last 1 KiB block (the launch rounds the LDS size up to 1 KiB).  Issued before the
+// expert lookup, so the two memory round trips overlap; wait_vm_all() before LDS is read.
+template <int FMT, int ACT>
+MOE_DEV void stage_row_dma(const GemvParams &p, unsigned char *smem) {
+    constexpr bool F32 = ACT == kActF32;
+    constexpr int P = act_slots<FMT, F32>();
+    const int act_vec = p.K * (F32 ? 4 : 2) / 16;
+    const int nblk = (act_vec + 63) / 64;
+    const int lane = lane_id();
+    for (int c = __builtin_amdgcn_readfirstlane(wave_id()); c < nblk; c += kGemvThreads / 64) {
+        const int q = c * 64 + lane;
+        const int b = q / P, sl = q - b * P;
+        const int v = q < act_vec ? b * P + (sl ^ act_swizzle<FMT, F32>(b)) : 0;
+        gemv_dma16((const u32x4 *)p.act + v, (uint32_t)(uintptr_t)(smem + (size_t)c * 1024));
+    }
+}
+
 // wbase / sbase: this lane's matrix (gate or up for the pair), chosen once per kernel with a
 // select -- indexing the parameter arrays by a lane-dependent value would load the pointer
 // from memory on every use.  Every load is issued unconditionally from a clamped, valid
@@ -230,25 +257,30 @@ MOE_DEV void stage_activations(const GemvParams &p, unsigned char *smem, int row
 // in order, for every load before it) where the branch joins.  Slots past the row or the
 // row range are skipped when the batch is consumed.  Scale bytes stay raw until then.
 // Batch ib of a pass covers this lane's units i0 .. i0+U-1 of row n (n clamped to a valid row).
+// A batch that will not be consumed (live false: the wave has no further pass) is still
+// issued, from the first bytes of the arrays, so that the loads of the loop are
+// unconditional and the compiler can keep one batch in flight while the previous one is
+// consumed; those bytes stay in cache.
 template <int FMT>
 MOE_DEV void load_batch(const GemvParams &p, int n_row, int n_end, int ib, int e, const uint8_t *wbase,
-                        const void *sbase, int j, int units, u32x4 (&w)[kGemvUnroll], uint32_t (&sc)[kGemvUnroll]) {
+                        const void *sbase, int j, int units, bool live, u32x4 (&w)[kGemvUnroll],
+                        uint32_t (&sc)[kGemvUnroll]) {
     const int i0 = ib * kGemvUnroll;
     const int n = min(n_row, n_end - 1);
-    const size_t ridx = (size_t)e * p.N + n;
-    const uint8_t *wrow = wbase + ridx * (size_t)units * 16;
+    const size_t ridx = live ? (size_t)e * p.N + n : 0;
 #pragma unroll
     for (int u = 0; u < kGemvUnroll; ++u) {
-        const int b = min(j + (i0 + u) * p.G, units - 1);
+        const int b = live ? min(j + (i0 + u) * p.G, units - 1) : 0;
+        const size_t wo = (ridx * (size_t)units + b) * 16;
 #if MOE_GEMV_NT
-        w[u] = __builtin_nontemporal_load((const u32x4 *)(wrow + (size_t)b * 16));
+        w[u] = __builtin_nontemporal_load((const u32x4 *)(wbase + wo));
 #else
-        w[u] = *(const u32x4 *)(wrow + (size_t)b * 16);
+        w[u] = *(const u32x4 *)(wbase + wo);
 #endif
         if constexpr (FMT == kFmtMXFP4) {
             sc[u] = ((const uint8_t *)sbase)[ridx * units + b];
         } else if constexpr (FMT == kFmtFP8) {
-            const size_t srow = (size_t)e * (p.N / 128) + n / 128;
+            const size_t srow = live ? (size_t)e * (p.N / 128) + n / 128 : 0;
             sc[u] = __float_as_uint(((const float *)sbase)[srow * (p.K / 128) + (b * 16) / 128]);
         } else {
             sc[u] = 0;
@@ -330,11 +362,15 @@ __global__ MOE_GEMV_ATTR void gemv_kernel(const GemvParams p0) {
         p.gather = 0;
         p.residual = nullptr;
     }
+    const bool pre = ACT != kActMX && p.n_act_rows == 1;
+    if (pre) stage_row_dma<FMT, ACT>(p, smem);
     int e = 0, row0 = 0, M = p.T;
     if (ROUTED && !shared) {
         e = wave_nth_nonempty(p.offsets, p.E, blockIdx.y, &row0, &M);
-        if (e < 0) return;
-        if (row0 < 0 || M <= 0 || row0 + M > p.R) return;
+        if (e < 0 || row0 < 0 || M <= 0 || row0 + M > p.R) {
+            if (pre) wait_vm_all();          // no copy into LDS may be left in flight
+            return;
+        }
     }
     const int units = units_per_row<FMT>(p.K);
     const int lane = lane_id(), wave = wave_id();
@@ -347,7 +383,10 @@ __global__ MOE_GEMV_ATTR void gemv_kernel(const GemvParams p0) {
     const void *sbase = PAIR && mat ? p.s[1] : p.s[0];
     const int n_begin = blockIdx.x * p.rows_per_wg;
     const int n_end = min(p.N, n_begin + p.rows_per_wg);
-    if (n_begin >= n_end) return;
+    if (n_begin >= n_end) {
+        if (pre) wait_vm_all();
+        return;
+    }
     const int passes = (n_end - n_begin + rows_per_pass - 1) / rows_per_pass;
     const int nb = (p.nl + kGemvUnroll - 1) / kGemvUnroll;    // batches per pass
     auto row_of = [&](int pass) { return n_begin + pass * rows_per_pass + grp; };
@@ -380,8 +419,9 @@ __global__ MOE_GEMV_ATTR void gemv_kernel(const GemvParams p0) {
         if (threadIdx.x == 0) s_pass = NW;
         int P = min(wave, passes), ib = 0;     // batch being consumed: pass P, batch ib
         // the first weight batch is in flight while the activations are staged
-        if (P < passes) load_batch<FMT>(p, row_of(P), n_end, 0, e, wbase, sbase, j, units, wa, sa);
-        stage_activations<FMT, ACT>(p, smem, row0, c0, mc);
+        load_batch<FMT>(p, row_of(P), n_end, 0, e, wbase, sbase, j, units, P < passes, wa, sa);
+        if (pre && c0 == 0) wait_vm_all();     // the row copied at entry (and the first batch)
+        if (!(pre && mc == 1)) stage_activations<FMT, ACT>(p, smem, row0, c0, mc);
         __syncthreads();
         int Pn = grab(P);                      // the wave's next pass
         int Pnn = passes;
@@ -390,7 +430,7 @@ __global__ MOE_GEMV_ATTR void gemv_kernel(const GemvParams p0) {
                         uint32_t (&ns)[kGemvUnroll]) {
             const bool last = ib + 1 == nb;
             const int P2 = last ? Pn : P, ib2 = last ? 0 : ib + 1;
-            if (P2 < passes) load_batch<FMT>(p, row_of(P2), n_end, ib2, e, wbase, sbase, j, units, nx, ns);
+            load_batch<FMT>(p, row_of(P2), n_end, ib2, e, wbase, sbase, j, units, P2 < passes, nx, ns);
             if (last) Pnn = grab(Pn);          // needed one pass later
             compute_batch<FMT, ACT, MAXM, PAIR>(p, row_of(P), n_end, ib, nb, mat, j, units, smem, row0 + c0, mc,
                                                 cu, cs, acc);
@@ -801,16 +841,19 @@ moe_status gemv_launch(int fmt, int act, bool pair, GemvParams p, int slots, int
     while (maxm < want) maxm *= 2;
     p.chunk = want;
     const int rows_per_pass = pair ? 32 / p.G : 64 / p.G;
-    // aim for MOE_GEMV_TARGET_WAVES waves over the whole launch, at least one pass per wave
+    // aim for at most MOE_GEMV_TARGET_WAVES waves over the whole launch (rounding the rows
+    // per workgroup up: a workgroup more than the target puts a fifth one on some CUs, whose
+    // workgroups then finish last), at least one pass per wave
     const int n_grid = p.shared_slot >= 0 ? max(p.N, p.sN) : p.N;
-    long long rows_total = (long long)n_grid * slots;
-    int rpw = (int)(rows_total / (MOE_GEMV_TARGET_WAVES / (kGemvThreads / 64)));
+    const long long rows_total = (long long)n_grid * slots;
+    const int target_wgs = MOE_GEMV_TARGET_WAVES / (kGemvThreads / 64);
+    int rpw = (int)((rows_total + target_wgs - 1) / target_wgs);
     const int min_rpw = rows_per_pass * (kGemvThreads / 64);
     if (rpw < min_rpw) rpw = min_rpw;
     rpw = (rpw + rows_per_pass - 1) / rows_per_pass * rows_per_pass;
     p.rows_per_wg = rpw;
     dim3 grid((n_grid + rpw - 1) / rpw, slots);
-    const size_t lds = (size_t)p.chunk * row_lds;
+    const size_t lds = align_up((size_t)p.chunk * row_lds, 1024);   // whole 1 KiB blocks: stage_row_dma
     GemvFn fn = pick_kernel(fmt, act, pair, maxm, p.offsets != nullptr);
     hipLaunchKernelGGL(fn, grid, dim3(kGemvThreads), lds, stream, p);
     return launch_check(what);

@@ -214,6 +214,13 @@ bool router_tiled(const moe_route_desc *d) { return d->T >= 32 && d->H % (32 * k
 
 MOE_DEV double sigmoid_f64(double v) { return 1.0 / (1.0 + exp(-v)); }
 
+MOE_DEV double readlane_f64(double v, int l) {
+    const uint64_t b = (uint64_t)__double_as_longlong(v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
 // Selection order: larger key first, equal keys (-0 == +0) -> lower expert index.  A key
 // is mapped to an unsigned 64-bit integer with the same order (NaN -> 0, below every
 // number), so the wave-wide maximum runs on 32-bit integer halves.
@@ -277,14 +284,35 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     if (t < T) {
     const float *lt = logits + (size_t)t * rows;
 
-    uint64_t key[NK];
+    // All loads are issued before any is used (an absent bias array is read from the logits
+    // and the value dropped), so the keys cost one memory round trip.  base[i] is what a
+    // selected expert's weight is computed from -- its logit (softmax) or sigmoid (sigmoid)
+    // -- so nothing is read again after the selection.
+    const float *lbp = lbias ? lbias : lt, *sbp = sbias ? sbias : lt;
+    float lv[NK], lbv[NK], sbv[NK];
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
         const int e = min(lane + 64 * i, E - 1);
-        double l = (double)lt[e] + (lbias ? (double)lbias[e] : 0.0);
-        if (score == MOE_SCORE_SIGMOID) l = sigmoid_f64(l) + (sbias ? (double)sbias[e] : 0.0);
-        key[i] = lane + 64 * i < E ? order_key(l) : 0;
-        if (n_group > 1 && lane + 64 * i < E) s_gkey[wave_id() * E + lane + 64 * i] = l;
+        lv[i] = lt[e];
+        lbv[i] = lbp[e];
+        sbv[i] = sbp[e];
+    }
+    const float sg_logit = lt[has_sg ? E : 0];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) asm volatile("" : "+v"(lv[i]), "+v"(lbv[i]), "+v"(sbv[i]));   // loads stay here
+    uint64_t key[NK];
+    double base[NK];
+#pragma unroll
+    for (int i = 0; i < NK; ++i) {
+        double l = (double)lv[i] + (lbias ? (double)lbv[i] : 0.0);
+        double kv = l;
+        if (score == MOE_SCORE_SIGMOID) {
+            l = sigmoid_f64(l);
+            kv = l + (sbias ? (double)sbv[i] : 0.0);
+        }
+        base[i] = l;
+        key[i] = lane + 64 * i < E ? order_key(kv) : 0;
+        if (n_group > 1 && lane + 64 * i < E) s_gkey[wave_id() * E + lane + 64 * i] = kv;
     }
     if (n_group > 1) {
         // group-limited selection: lane g < n_group scores group g from the keys in LDS (a
@@ -321,23 +349,31 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     uint32_t taken = 0;
     uint64_t hk;
     int hi;
+    double hv;
     auto head = [&]() {          // best untaken key of this lane (equal keys: lower i = lower expert)
         hk = 0;
         hi = INT_MAX;
+        hv = 0.0;
 #pragma unroll
         for (int i = 0; i < NK; ++i) {
             if (!((taken >> i) & 1u) && key[i] > hk) {
                 hk = key[i];
                 hi = lane + 64 * i;
+                hv = base[i];
             }
         }
     };
     head();
     int my_e = -1;
+    double l = 0.0;              // lane j < k: base value of the j-th selected expert
     for (int j = 0; j < k; ++j) {
         const int L = wave_best_lane(hk, hi);
         const int wi = __builtin_amdgcn_readlane(hi, L);
-        if (lane == j) my_e = wi == INT_MAX ? -1 : wi;
+        const double wl = readlane_f64(hv, L);
+        if (lane == j && wi != INT_MAX) {
+            my_e = wi;
+            l = wl;
+        }
         if (lane == L && wi != INT_MAX) {     // the winner drops its key
             taken |= 1u << (wi >> 6);
             head();
@@ -345,8 +381,6 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     }
 
     const bool mine = lane < k && my_e >= 0;
-    double l = 0.0;
-    if (mine) l = (double)lt[my_e] + (lbias ? (double)lbias[my_e] : 0.0);
     double wv;
     if (score == MOE_SCORE_SOFTMAX) {
         const double lmax = __shfl(l, 0, kWave);   // first selected = largest logit
@@ -356,13 +390,14 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
             denom = group_sum_f64(p, kWave);
         } else {
             double s = 0.0;
-            for (int e = lane; e < E; e += kWave)
-                s += exp((double)lt[e] + (lbias ? (double)lbias[e] : 0.0) - lmax);
+#pragma unroll
+            for (int i = 0; i < NK; ++i)
+                if (lane + 64 * i < E) s += exp(base[i] - lmax);
             denom = group_sum_f64(s, kWave);
         }
         wv = p / denom;
     } else {
-        const double sv = mine ? sigmoid_f64(l) : 0.0;
+        const double sv = mine ? l : 0.0;
         wv = renorm ? sv / group_sum_f64(sv, kWave) : sv;
     }
     wv *= (double)scaling;
@@ -371,7 +406,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
         w[(size_t)t * k + lane] = mine ? (float)wv : NAN;
         if constexpr (PERM) sid[t * k + lane] = my_e;        // -1 when fewer than k keys compare
     }
-    if (has_sg && lane == 0) sg[t] = (float)sigmoid_f64((double)lt[E]);
+    if (has_sg && lane == 0) sg[t] = (float)sigmoid_f64((double)sg_logit);
     }
     if constexpr (PERM) {
         __syncthreads();
