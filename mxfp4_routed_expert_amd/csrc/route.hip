@@ -261,9 +261,37 @@ MOE_DEV int wave_best_lane(uint64_t hk, int hi) {
     return __ffsll((long long)cand) - 1;
 }
 
+// In-register bitonic sort of a lane's N (power of two) entries into descending order of
+// (key, then lower index first); base values move with their keys.
+template <int N>
+MOE_DEV void sort_desc(uint64_t (&key)[N], int (&idx)[N], double (&base)[N]) {
+#pragma unroll
+    for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+        for (int stride = size / 2; stride > 0; stride >>= 1) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int p = i ^ stride;
+                if (p <= i) continue;
+                // entries i < p: descending run when (i & size) == 0, ascending otherwise
+                const bool first_better = key[i] > key[p] || (key[i] == key[p] && idx[i] < idx[p]);
+                const bool swap = ((i & size) == 0) ? !first_better : first_better;
+                const uint64_t ka = key[i], kb = key[p];
+                const int ia = idx[i], ib = idx[p];
+                const double ba = base[i], bb = base[p];
+                key[i] = swap ? kb : ka;
+                key[p] = swap ? ka : kb;
+                idx[i] = swap ? ib : ia;
+                idx[p] = swap ? ia : ib;
+                base[i] = swap ? bb : ba;
+                base[p] = swap ? ba : bb;
+            }
+        }
+    }
+}
+
 // One wave per token.  Lane l holds the selection keys of experts l, l+64, ... in
-// registers and tracks its own best untaken key (its head); each of the k rounds takes the
-// wave-wide best head and only the winning lane rescans its keys.  NaN keys are never
+// registers, sorted; each of the k rounds takes the wave-wide best first entry.  NaN keys are never
 // selected (ids -1 are emitted if fewer than k keys compare).
 // PERM: one workgroup holds every token (T <= 4, T*k <= 64) and also writes the token ->
 // expert permutation of the selected ids, as moe_permute would.
@@ -346,37 +374,36 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
             if (e < E && !((keep >> (e / gs)) & 1ull)) key[i] = 0;
         }
     }
-    uint32_t taken = 0;
-    uint64_t hk;
-    int hi;
-    double hv;
-    auto head = [&]() {          // best untaken key of this lane (equal keys: lower i = lower expert)
-        hk = 0;
-        hi = INT_MAX;
-        hv = 0.0;
+    // The lane's keys sorted once, best first (larger key, then lower expert); each round
+    // takes the wave-wide best of the lanes' first entries and the winner shifts its list.
+    // Key 0 (NaN, masked or past E) is never selected.
+    int idx[NK];
+    double braw[NK];             // unsorted, for the full softmax denominator
 #pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            if (!((taken >> i) & 1u) && key[i] > hk) {
-                hk = key[i];
-                hi = lane + 64 * i;
-                hv = base[i];
-            }
-        }
-    };
-    head();
+    for (int i = 0; i < NK; ++i) {
+        idx[i] = lane + 64 * i;
+        braw[i] = base[i];
+    }
+    sort_desc<NK>(key, idx, base);
     int my_e = -1;
     double l = 0.0;              // lane j < k: base value of the j-th selected expert
     for (int j = 0; j < k; ++j) {
-        const int L = wave_best_lane(hk, hi);
-        const int wi = __builtin_amdgcn_readlane(hi, L);
-        const double wl = readlane_f64(hv, L);
-        if (lane == j && wi != INT_MAX) {
-            my_e = wi;
+        const int L = wave_best_lane(key[0], key[0] ? idx[0] : INT_MAX);
+        const int wi = key[0] ? idx[0] : INT_MAX;
+        const int win = __builtin_amdgcn_readlane(wi, L);
+        const double wl = readlane_f64(base[0], L);
+        if (lane == j && win != INT_MAX) {
+            my_e = win;
             l = wl;
         }
-        if (lane == L && wi != INT_MAX) {     // the winner drops its key
-            taken |= 1u << (wi >> 6);
-            head();
+        if (lane == L) {         // the winner drops its first entry
+#pragma unroll
+            for (int i = 0; i + 1 < NK; ++i) {
+                key[i] = key[i + 1];
+                idx[i] = idx[i + 1];
+                base[i] = base[i + 1];
+            }
+            key[NK - 1] = 0;
         }
     }
 
@@ -392,7 +419,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
             double s = 0.0;
 #pragma unroll
             for (int i = 0; i < NK; ++i)
-                if (lane + 64 * i < E) s += exp(base[i] - lmax);
+                if (lane + 64 * i < E) s += exp(braw[i] - lmax);
             denom = group_sum_f64(s, kWave);
         }
         wv = p / denom;
