@@ -83,6 +83,10 @@ MOE_DEV double group_sum_f64(double v, int width) {
 }
 
 MOE_DEV int lane_id() { return threadIdx.x & (kWave - 1); }
+
+// Workgroup barrier for LDS traffic only: this wave's LDS accesses are complete, then all
+// waves meet.  Unlike __syncthreads it does not wait for the wave's global loads in flight.
+MOE_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 MOE_DEV int wave_id() { return threadIdx.x >> 6; }
 
 constexpr int kMaxOffsetChunks = MOE_MAX_EXPERTS / 64 + 1;

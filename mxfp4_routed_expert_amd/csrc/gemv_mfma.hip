@@ -287,13 +287,12 @@ moe_status gemv_mfma_launch(int act, bool pair, GemvParams p, int slots, hipStre
 // keeps kDmDepth steps of loads in flight across item boundaries; results go through the
 // part[slot][row] LDS table and the slot-ordered final sum.
 #ifndef MOE_DM_DEPTH
-#define MOE_DM_DEPTH 8           // steps of loads in flight per wave
+#define MOE_DM_DEPTH 4           // steps of loads in flight per wave
 #endif
 #ifndef MOE_DM_NT
 #define MOE_DM_NT 0              // non-temporal weight loads (off: the two half-lines of a row arrive in separate loads)
 #endif
 constexpr int kDmDepth = MOE_DM_DEPTH;
-constexpr int kDmLoadsPerStep = 4;       // vector memory operations of one step's load (2 units, 2 scales)
 
 MOE_DEV void dm_dma16(const void *src, uint32_t lds_wave_base) {
     const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
@@ -310,11 +309,16 @@ struct DmIt {
     uint32_t wo, so;
 };
 
-__global__ __launch_bounds__(kDcThreads) void down_combine_mfma_kernel(const DownCombineParams p) {
+#ifndef MOE_DM_THREADS
+#define MOE_DM_THREADS 1024      // threads of a matrix-core down-combine workgroup (4 waves per SIMD)
+#endif
+constexpr int kDmThreads = MOE_DM_THREADS;
+
+__global__ __launch_bounds__(kDmThreads) void down_combine_mfma_kernel(const DownCombineParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_e[MOE_MAX_TOPK + 1], s_r[MOE_MAX_TOPK + 1];
     __shared__ float s_w[MOE_MAX_TOPK + 1];
-    constexpr int NW = kDcThreads / 64;
+    constexpr int NW = kDmThreads / 64;
     const int t = blockIdx.y;
     const int nslot = p.k + (p.sw ? 1 : 0);
     const int tid = threadIdx.x, lane = lane_id();
@@ -424,11 +428,11 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_mfma_kernel(const Dow
 
     // h rows -> LDS by direct copies: slot j's float32 row at byte 4*ld*j, in whole 1 KiB
     // blocks (the tail of a row's last block re-reads its last vector into the row's
-    // padding; 4*ld is a multiple of 1 KiB).  The copies are not loads the compiler
-    // tracks; they are issued first, the first kDmDepth steps of weight loads after them,
-    // and the wait below lets exactly those kDmLoadsPerStep * kDmDepth loads stay in
-    // flight (memory operations of a wave complete in order), so the copies' latency and
-    // the first weight bytes overlap and the compiler's wait counts stay exact.
+    // padding; 4*ld is a multiple of 1 KiB).  The copies are waited for before any weight
+    // load is issued: behind a full pipeline of weight loads they would land several times
+    // later.  The first kDmDepth steps of weight loads are then in flight during the
+    // conversion, whose barriers wait for LDS accesses only (a __syncthreads would also wait
+    // for every load in flight).
     {
         const int act_vec = p.I / 4;
         const int bpr = (act_vec + 63) / 64;                 // copy blocks per row
@@ -439,6 +443,7 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_mfma_kernel(const Dow
             dm_dma16(row + (size_t)v * 4, (uint32_t)(uintptr_t)(smem + (size_t)j * 4 * ld + (size_t)b0 * 16));
         }
     }
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     u32x4 wv[kDmDepth][2];
     uint8_t sv[kDmDepth][2];  // (bytes: a widened copy would be masked at the loop latch, forcing a wait)
     DmIt lp{0, wave % nslot, 0, wave / nslot, nullptr, nullptr, 0, 0};
@@ -449,31 +454,29 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_mfma_kernel(const Dow
         load(lp, wv[d], sv[d]);
         advance(lp);
     }
-    static_assert(kDmLoadsPerStep * kDmDepth <= 63, "vmcnt limit");
-    asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"i"(kDmLoadsPerStep * kDmDepth) : "memory");
     // float32 rows -> bf16 hi/lo planes in place (all reads before the barrier, all writes
     // after): plane hi at element 0 of the row's region, lo at element ld; zeros past d_ff
     // and for dropped pairs.  hi = RN_bf16(h), lo = RN_bf16(h - hi) by the packed
     // round-to-nearest-even conversion.
     {
-        // 8-value groups per thread: S * ld / 8 groups, S * 4 * ld <= 150 KiB -> <= 4800 groups
-        constexpr int kGroups = 10;
+        // 8-value groups: S * ld / 8 in all, S * 4 * ld <= 150 KiB -> <= 4800
+        constexpr int kGroups = (4800 + kDmThreads - 1) / kDmThreads;
         const int per = ld / 8;
         const int total = nslot * per;
         f32x4 va[kGroups], vb[kGroups];
 #pragma unroll
         for (int u = 0; u < kGroups; ++u) {
-            const int i = min(tid + u * kDcThreads, total - 1);
+            const int i = min(tid + u * kDmThreads, total - 1);
             const int j = i / per, v = i - j * per;
             const bool ok = v * 8 < p.I && (j >= p.k || s_r[j] >= 0);
             const f32x4 *src = (const f32x4 *)(smem + (size_t)j * 4 * ld) + 2 * v;
             va[u] = ok ? src[0] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             vb[u] = ok ? src[1] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
-        __syncthreads();
+        lds_barrier();
 #pragma unroll
         for (int u = 0; u < kGroups; ++u) {
-            const int i = tid + u * kDcThreads;
+            const int i = tid + u * kDmThreads;
             if (i >= total) break;
             const int j = i / per, v = i - j * per;
             const f32x2 f[4] = {{va[u][0], va[u][1]}, {va[u][2], va[u][3]}, {vb[u][0], vb[u][1]}, {vb[u][2], vb[u][3]}};
@@ -489,7 +492,7 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_mfma_kernel(const Dow
             *(u32x4 *)(planes + (size_t)(2 * j + 1) * ld + v * 8) = lv;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     DmIt cp = first;
     for (int q0 = 0; q0 < nq; q0 += kDmDepth) {
@@ -502,7 +505,7 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_mfma_kernel(const Dow
         }
     }
     __syncthreads();
-    for (int lr = tid; lr < n_end - n_begin; lr += kDcThreads) {
+    for (int lr = tid; lr < n_end - n_begin; lr += kDmThreads) {
         float o = 0.0f;
         for (int j = 0; j < nslot; ++j) o = fmaf(s_w[j], part[j * p.rows_per_wg + lr], o);   // slot order
         p.out[(size_t)t * p.N + n_begin + lr] = o;
@@ -510,7 +513,7 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_mfma_kernel(const Dow
 }
 
 void down_combine_mfma_launch(const DownCombineParams &p, dim3 grid, size_t lds, hipStream_t stream) {
-    hipLaunchKernelGGL(down_combine_mfma_kernel, grid, dim3(kDcThreads), lds, stream, p);
+    hipLaunchKernelGGL(down_combine_mfma_kernel, grid, dim3(kDmThreads), lds, stream, p);
 }
 
 }  // namespace moe
