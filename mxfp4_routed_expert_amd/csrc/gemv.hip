@@ -157,7 +157,7 @@ MOE_DEV void stage_activations(const GemvParams &p, unsigned char *smem, int row
         }
         s_arow[m] = (m < mc && a >= 0 && a < p.n_act_rows) ? a : -1;
     }
-    __syncthreads();
+    lds_barrier();                         // (weight loads issued before stay in flight)
     auto row_of = [&](int m) { return s_arow[m]; };
     if constexpr (ACT == kActMX) {
         const int nb = K / 32;
@@ -415,14 +415,14 @@ __global__ MOE_GEMV_ATTR void gemv_kernel(const GemvParams p0) {
 
     for (int c0 = 0; c0 < M; c0 += p.chunk) {
         const int mc = min(p.chunk, M - c0);
-        __syncthreads();                       // the previous chunk is done with LDS and the counter
+        lds_barrier();                         // the previous chunk is done with LDS and the counter
         if (threadIdx.x == 0) s_pass = NW;
         int P = min(wave, passes), ib = 0;     // batch being consumed: pass P, batch ib
         // the first weight batch is in flight while the activations are staged
         load_batch<FMT>(p, row_of(P), n_end, 0, e, wbase, sbase, j, units, P < passes, wa, sa);
         if (pre && c0 == 0) wait_vm_all();     // the row copied at entry (and the first batch)
         if (!(pre && mc == 1)) stage_activations<FMT, ACT>(p, smem, row0, c0, mc);
-        __syncthreads();
+        lds_barrier();
         int Pn = grab(P);                      // the wave's next pass
         int Pnn = passes;
         // one batch: load the following one into `nx`, consume `cu`; false when the wave is done
