@@ -138,13 +138,25 @@ MOE_DEV int tile_expert(const int *tp, int E, int mt) {
     return c * 32 + __ffsll((long long)m2) - 1;
 }
 
-// K-step of 256 values: each operand row contributes one whole 128-byte line per step.
-constexpr int kGStep = 256;
+// K-step of MOE_GEMM_KSTEP values (256: each operand row contributes one whole 128-byte
+// line per step; 128: half a line, so that more steps fit in LDS at once).
+#ifndef MOE_GEMM_KSTEP
+#define MOE_GEMM_KSTEP 256
+#endif
+constexpr int kGStep = MOE_GEMM_KSTEP;
 constexpr int kRowB = kGStep / 2;              // code bytes per row per step
+constexpr int kCh = kRowB / 16;                // 16-byte chunks (K-blocks) per row per step
+constexpr int kRpc = 1024 / kRowB;             // rows moved by one 1-KB copy
+constexpr int kCpo = 32 / kRpc;                // copies per operand per wave (32 rows)
 constexpr int kScB = 16;                       // LDS bytes per scale row per step (window)
+static_assert(kGStep == 256 || kGStep == 128, "K-step");
+
+// Chunk position of chunk c of row r in LDS: rows sharing a 256-byte bank period get
+// different chunk keys, so an operand read (16 rows at one chunk) hits 16 bank groups.
+MOE_DEV int chunk_swz(int r) { return (r / (256 / kRowB)) & (kCh - 1); }
 
 template <bool PAIR>
-constexpr int gemm_stages() { return PAIR ? 2 : 3; }   // steps resident in LDS
+constexpr int gemm_stages() { return kGStep == 256 ? (PAIR ? 2 : 3) : (PAIR ? 5 : 7); }   // steps resident in LDS
 
 template <bool PAIR, bool ROUTED>
 __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
@@ -154,7 +166,7 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
     constexpr int kB = NM * kGBN * kRowB;              // B codes of a step
     constexpr int kSRows = kGBM + NM * kGBN;           // scale rows: A, then each matrix's
     constexpr int kStage = kA + kB + kSRows * kScB;
-    constexpr int kCodeCopies = (kGBM + NM * kGBN) / 8 / 4;   // 1-KB copies (8 rows) per wave
+    constexpr int kCodeCopies = (kGBM + NM * kGBN) / kRpc / 4;   // 1-KB copies per wave
     constexpr int kScCopies = kSRows / 16 / 4;         // scale copies (16 rows x 4 dwords) per wave
     constexpr int kOps = kCodeCopies + kScCopies;      // memory operations per wave per stage
     static_assert(kSRows % 64 == 0 && (kGBM + NM * kGBN) % 32 == 0, "copy split");
@@ -177,7 +189,7 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
     const int wm = wave >> 1, wn = wave & 1;           // output quarter of this wave
     const int hr = lane & 31, hb = lane >> 5;          // MFMA operand row / K-block of this lane
     const int Kh = p.K / 2, Kb = p.K / 32;
-    const int S = (Kb + 7) / 8;                        // K-steps of 256 values
+    const int S = (Kb + kCh - 1) / kCh;                // K-steps
 
     for (int item = slot; item < items; item += G) {
         int e = 0, tile = 0, nt = 0, row0 = 0, M = p.T;
@@ -204,11 +216,11 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
         };
         auto b_src_row = [&](int n) { return min(n0 + n, p.N - 1); };
 
-        // ---- copies.  A step's codes sit row-major in LDS, 128 bytes per row, with the
-        // 16-byte chunk c of row r stored at chunk position c ^ ((r >> 1) & 7): one 1-KB copy
-        // moves 8 rows, 8 lanes per row fetching one 128-byte line, and an MFMA operand read
-        // (rows r .. r+15 at one chunk, served 16 lanes per LDS cycle) hits 16 distinct
-        // 16-byte bank groups.  Wave w copies rows 32w .. 32w+31 of A and of each B matrix.
+        // ---- copies.  A step's codes sit row-major in LDS, kRowB bytes per row, with the
+        // 16-byte chunk c of row r stored at chunk position c ^ chunk_swz(r): one 1-KB copy
+        // moves kRpc rows, kCh lanes per row, and an MFMA operand read (rows r .. r+15 at one
+        // chunk, served 16 lanes per LDS cycle) hits 16 distinct 16-byte bank groups.  Wave w
+        // copies rows 32w .. 32w+31 of A and of each B matrix.
         const int eu = __builtin_amdgcn_readfirstlane(e);
         const uint8_t *a_base = uniform_ptr(p.a);
         const uint8_t *b_base[NM], *bs_base[NM];
@@ -217,12 +229,12 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
             b_base[mi] = uniform_ptr(p.w[mi] + (size_t)eu * p.N * Kh);
             bs_base[mi] = uniform_ptr(p.ws[mi] + (size_t)eu * p.N * Kb);
         }
-        const int cr = lane >> 3;                          // copy lane: row within the 8
-        uint32_t a_off[4], b_off[4];
+        const int cr = lane / kCh;                         // copy lane: row within the copy
+        uint32_t a_off[kCpo], b_off[kCpo];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            a_off[t] = (uint32_t)a_src_row(32 * wave + 8 * t + cr) * Kh;
-            b_off[t] = (uint32_t)b_src_row(32 * wave + 8 * t + cr) * Kh;
+        for (int t = 0; t < kCpo; ++t) {
+            a_off[t] = (uint32_t)a_src_row(32 * wave + kRpc * t + cr) * Kh;
+            b_off[t] = (uint32_t)b_src_row(32 * wave + kRpc * t + cr) * Kh;
         }
         // Scale rows: 4 lanes per row, dword d of the row's window starting at the aligned
         // dword that holds the step's first byte.  A dword is fetched only when it holds a
@@ -262,20 +274,20 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
             const int sc = min(s, S - 1);
             unsigned char *st = smem + (s % kStages) * kStage;
 #pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int cc = (lane & 7) ^ ((4 * t + (cr >> 1)) & 7);   // chunk this lane fetches
-                const uint32_t ko = (uint32_t)min(8 * sc + cc, Kb - 1) * 16;
-                dma16<0>(a_base, a_off[t] + ko, st + (32 * wave + 8 * t) * kRowB);
+            for (int t = 0; t < kCpo; ++t) {
+                const int cc = (lane % kCh) ^ chunk_swz(32 * wave + kRpc * t + cr);   // chunk this lane fetches
+                const uint32_t ko = (uint32_t)min(kCh * sc + cc, Kb - 1) * 16;
+                dma16<0>(a_base, a_off[t] + ko, st + (32 * wave + kRpc * t) * kRowB);
 #pragma unroll
                 for (int mi = 0; mi < NM; ++mi)
-                    dma16<0>(b_base[mi], b_off[t] + ko, st + kA + (mi * kGBN + 32 * wave + 8 * t) * kRowB);
+                    dma16<0>(b_base[mi], b_off[t] + ko, st + kA + (mi * kGBN + 32 * wave + kRpc * t) * kRowB);
             }
-            const int last = min(8, Kb - 8 * sc) - 1;      // last block of the step in the row
+            const int last = min(kCh, Kb - kCh * sc) - 1;  // last block of the step in the row
 #pragma unroll
             for (int i = 0; i < kScCopies; ++i) {
                 const uint32_t o = sc_mis[i];
                 const uint32_t need = (o + (uint32_t)last) >> 2;   // dwords 0..need hold bytes of the step
-                const uint32_t v = sc_off[i] + 8u * sc - o + ((uint32_t)sd <= need ? 4u * sd : 0u);
+                const uint32_t v = sc_off[i] + (uint32_t)kCh * sc - o + ((uint32_t)sd <= need ? 4u * sd : 0u);
                 dma4(sc_base[i], v, st + kA + kB + (16 * (kScCopies * wave + i)) * kScB);
             }
         };
@@ -290,19 +302,19 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int r = 32 * (2 * wm + i) + hr;
-                f.a[i] = *(const u32x4 *)(st + r * kRowB + ((c ^ ((r >> 1) & 7)) << 4));
+                f.a[i] = *(const u32x4 *)(st + r * kRowB + ((c ^ chunk_swz(r)) << 4));
                 f.sa[i] = st[sa_at[i] + 2 * q];
 #pragma unroll
                 for (int mi = 0; mi < NM; ++mi) {
                     const int n = mi * kGBN + 32 * (2 * wn + i) + hr;
-                    f.b[mi][i] = *(const u32x4 *)(st + kA + n * kRowB + ((c ^ ((n >> 1) & 7)) << 4));
+                    f.b[mi][i] = *(const u32x4 *)(st + kA + n * kRowB + ((c ^ chunk_swz(n)) << 4));
                     f.sb[mi][i] = st[sb_at[mi][i] + 2 * q];
                 }
             }
         };
         // K-blocks past the end of K (last step only): zero A codes, unit scales.
         auto kill = [&](int s, int q, Quarter &f) {
-            if (8 * s + 2 * q + hb < Kb) return;
+            if (kCh * s + 2 * q + hb < Kb) return;
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 f.a[i] = u32x4{0, 0, 0, 0};
@@ -347,11 +359,11 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
             Quarter f0, f1;
             read(st, 0, f0);
 #pragma unroll
-            for (int q = 0; q < 4; q += 2) {
+            for (int q = 0; q < kCh / 2; q += 2) {
                 read(st, q + 1, f1);
                 if constexpr (decltype(last)::value) kill(s, q, f0);
                 mma(f0);
-                if (q + 2 < 4) read(st, q + 2, f0);
+                if (q + 2 < kCh / 2) read(st, q + 2, f0);
                 if constexpr (decltype(last)::value) kill(s, q + 1, f1);
                 mma(f1);
             }
