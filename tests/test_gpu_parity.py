@@ -313,6 +313,41 @@ LAYER_CASES = {
 }
 
 
+GRAPH_CASES = ["tiny_gated_shared", "tiny_fused_gated", "tiny_latent", "tiny_sigmoid_fp8"]
+
+
+@pytest.mark.parametrize("name", GRAPH_CASES)
+def test_graph_replays_match_eager(dev, M, name):
+    """One layer step captured as a HIP graph (with the shared expert's second stream where the
+    layer uses one) and replayed three times over three inputs, with eager copies and
+    synchronisations between the replays: every replay gives the eager output bit for bit."""
+    cfg = LAYER_CASES[name]
+    t, _ = build(cfg, dev)
+    layer = M.MoELayer(layer_weights(cfg, t), cfg.T, dev)
+    x0 = t["x"]
+    xs = [x0, (x0.float() * 0.5).to(torch.bfloat16), x0.roll(1, dims=1).contiguous()]
+    eager = [layer.forward(x).clone() for x in xs]
+    torch.cuda.synchronize()
+    x_static = x0.clone()
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        layer.forward(x_static)
+        st.synchronize()
+        with torch.cuda.graph(g, stream=st):
+            out = layer.forward(x_static)
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        for i, x in enumerate(xs):
+            x_static.copy_(x)
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, eager[i]), (name, rep, i)
+
+
 def _run_layer(M, cfg, dev, seed=0, inst=0):
     t, inp = build(cfg, dev, seed, inst)
     layer = M.MoELayer(layer_weights(cfg, t), cfg.T, dev)
