@@ -436,7 +436,7 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     if (has_sg && lane == 0) sg[t] = (float)sigmoid_f64((double)sg_logit);
     }
     if constexpr (PERM) {
-        __syncthreads();
+        lds_barrier();           // sid is in LDS; the id and weight stores need not land first
         small_permutation(sid, T * k, E, offsets, sorted, p2r, threadIdx.x, blockDim.x);
     }
 }
