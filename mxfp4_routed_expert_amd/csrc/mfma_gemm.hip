@@ -29,7 +29,16 @@ typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kGBM = 128;          // rows (tokens) per workgroup tile
 constexpr int kGBN = 128;          // output columns per workgroup tile
-constexpr int kGThreads = 256;
+#ifndef MOE_GEMM_WAVES
+#define MOE_GEMM_WAVES 8           // waves per workgroup: 4 (one per SIMD) or 8 (two per SIMD)
+#endif
+constexpr int kNW = MOE_GEMM_WAVES;
+constexpr int kGThreads = 64 * kNW;
+constexpr int kWN = 2;                         // waves along the output columns
+constexpr int kWM = kNW / kWN;                 // waves along the rows
+constexpr int kTM = kGBM / 32 / kWM;           // 32-row MFMA tiles per wave
+constexpr int kTN = kGBN / 32 / kWN;           // 32-column MFMA tiles per wave and matrix
+static_assert(kNW == 4 || kNW == 8, "waves per workgroup");
 
 struct GemmParams {
     const uint8_t *a;              // A codes: token rows [n_arows][K/2] (gather) or rows [R][K/2]
@@ -147,7 +156,8 @@ constexpr int kGStep = MOE_GEMM_KSTEP;
 constexpr int kRowB = kGStep / 2;              // code bytes per row per step
 constexpr int kCh = kRowB / 16;                // 16-byte chunks (K-blocks) per row per step
 constexpr int kRpc = 1024 / kRowB;             // rows moved by one 1-KB copy
-constexpr int kCpo = 32 / kRpc;                // copies per operand per wave (32 rows)
+constexpr int kRowsPW = kGBM / kNW;            // rows of each operand a wave copies
+constexpr int kCpo = kRowsPW / kRpc;           // copies per operand per wave
 constexpr int kScB = 16;                       // LDS bytes per scale row per step (window)
 static_assert(kGStep == 256 || kGStep == 128, "K-step");
 
@@ -166,10 +176,10 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
     constexpr int kB = NM * kGBN * kRowB;              // B codes of a step
     constexpr int kSRows = kGBM + NM * kGBN;           // scale rows: A, then each matrix's
     constexpr int kStage = kA + kB + kSRows * kScB;
-    constexpr int kCodeCopies = (kGBM + NM * kGBN) / kRpc / 4;   // 1-KB copies per wave
-    constexpr int kScCopies = kSRows / 16 / 4;         // scale copies (16 rows x 4 dwords) per wave
+    constexpr int kCodeCopies = (kGBM + NM * kGBN) / kRpc / kNW;   // 1-KB copies per wave
+    constexpr int kScCopies = kSRows / 16 / kNW;       // scale copies (16 rows x 4 dwords) per wave
     constexpr int kOps = kCodeCopies + kScCopies;      // memory operations per wave per stage
-    static_assert(kSRows % 64 == 0 && (kGBM + NM * kGBN) % 32 == 0, "copy split");
+    static_assert(kSRows % (16 * kNW) == 0 && kRowsPW % kRpc == 0, "copy split");
     static_assert((kStages - 2) * kOps <= 63, "vmcnt limit");
     __shared__ __align__(16) unsigned char smem[kStages * kStage];
     __shared__ uint8_t s_off[kSRows];
@@ -186,7 +196,7 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
     const int G = gridDim.x;
     const int slot = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
     const int lane = lane_id(), wave = wave_id();
-    const int wm = wave >> 1, wn = wave & 1;           // output quarter of this wave
+    const int wm = wave / kWN, wn = wave % kWN;        // output block of this wave
     const int hr = lane & 31, hb = lane >> 5;          // MFMA operand row / K-block of this lane
     const int Kh = p.K / 2, Kb = p.K / 32;
     const int S = (Kb + kCh - 1) / kCh;                // K-steps
@@ -220,7 +230,7 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
         // 16-byte chunk c of row r stored at chunk position c ^ chunk_swz(r): one 1-KB copy
         // moves kRpc rows, kCh lanes per row, and an MFMA operand read (rows r .. r+15 at one
         // chunk, served 16 lanes per LDS cycle) hits 16 distinct 16-byte bank groups.  Wave w
-        // copies rows 32w .. 32w+31 of A and of each B matrix.
+        // copies rows kRowsPW*w .. kRowsPW*(w+1)-1 of A and of each B matrix.
         const int eu = __builtin_amdgcn_readfirstlane(e);
         const uint8_t *a_base = uniform_ptr(p.a);
         const uint8_t *b_base[NM], *bs_base[NM];
@@ -233,8 +243,8 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
         uint32_t a_off[kCpo], b_off[kCpo];
 #pragma unroll
         for (int t = 0; t < kCpo; ++t) {
-            a_off[t] = (uint32_t)a_src_row(32 * wave + kRpc * t + cr) * Kh;
-            b_off[t] = (uint32_t)b_src_row(32 * wave + kRpc * t + cr) * Kh;
+            a_off[t] = (uint32_t)a_src_row(kRowsPW * wave + kRpc * t + cr) * Kh;
+            b_off[t] = (uint32_t)b_src_row(kRowsPW * wave + kRpc * t + cr) * Kh;
         }
         // Scale rows: 4 lanes per row, dword d of the row's window starting at the aligned
         // dword that holds the step's first byte.  A dword is fetched only when it holds a
@@ -256,17 +266,19 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
 #pragma unroll
         for (int i = 0; i < kScCopies; ++i) sc_mis[i] = s_off[16 * (kScCopies * wave + i) + (lane >> 2)];
         // Consumer side: LDS byte (step-relative) of block 0 of each scale row this lane feeds.
-        int sa_at[2], sb_at[NM][2];
+        int sa_at[kTM], sb_at[NM][kTN];
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int r = 32 * (2 * wm + i) + hr;
+        for (int i = 0; i < kTM; ++i) {
+            const int r = 32 * (kTM * wm + i) + hr;
             sa_at[i] = kA + kB + r * kScB + s_off[r] + hb;
+        }
+#pragma unroll
+        for (int j = 0; j < kTN; ++j)
 #pragma unroll
             for (int mi = 0; mi < NM; ++mi) {
-                const int q = kGBM + mi * kGBN + 32 * (2 * wn + i) + hr;
-                sb_at[mi][i] = kA + kB + q * kScB + s_off[q] + hb;
+                const int q = kGBM + mi * kGBN + 32 * (kTN * wn + j) + hr;
+                sb_at[mi][j] = kA + kB + q * kScB + s_off[q] + hb;
             }
-        }
 
         // Issue the copies of step s into its stage buffer.  Steps past the end re-fetch the
         // last step (never read); K-blocks past the end of a row are clamped to its last one.
@@ -275,12 +287,12 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
             unsigned char *st = smem + (s % kStages) * kStage;
 #pragma unroll
             for (int t = 0; t < kCpo; ++t) {
-                const int cc = (lane % kCh) ^ chunk_swz(32 * wave + kRpc * t + cr);   // chunk this lane fetches
+                const int cc = (lane % kCh) ^ chunk_swz(kRowsPW * wave + kRpc * t + cr);   // chunk this lane fetches
                 const uint32_t ko = (uint32_t)min(kCh * sc + cc, Kb - 1) * 16;
-                dma16<0>(a_base, a_off[t] + ko, st + (32 * wave + kRpc * t) * kRowB);
+                dma16<0>(a_base, a_off[t] + ko, st + (kRowsPW * wave + kRpc * t) * kRowB);
 #pragma unroll
                 for (int mi = 0; mi < NM; ++mi)
-                    dma16<0>(b_base[mi], b_off[t] + ko, st + kA + (mi * kGBN + 32 * wave + kRpc * t) * kRowB);
+                    dma16<0>(b_base[mi], b_off[t] + ko, st + kA + (mi * kGBN + kRowsPW * wave + kRpc * t) * kRowB);
             }
             const int last = min(kCh, Kb - kCh * sc) - 1;  // last block of the step in the row
 #pragma unroll
@@ -294,52 +306,56 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
 
         // Operands of one 64-value K-quarter q of a step: chunk 2q + hb of each row.
         struct Quarter {
-            u32x4 a[2], b[NM][2];
-            int sa[2], sb[NM][2];
+            u32x4 a[kTM], b[NM][kTN];
+            int sa[kTM], sb[NM][kTN];
         };
         auto read = [&](const unsigned char *st, int q, Quarter &f) {
             const int c = 2 * q + hb;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const int r = 32 * (2 * wm + i) + hr;
+            for (int i = 0; i < kTM; ++i) {
+                const int r = 32 * (kTM * wm + i) + hr;
                 f.a[i] = *(const u32x4 *)(st + r * kRowB + ((c ^ chunk_swz(r)) << 4));
                 f.sa[i] = st[sa_at[i] + 2 * q];
+            }
+#pragma unroll
+            for (int j = 0; j < kTN; ++j)
 #pragma unroll
                 for (int mi = 0; mi < NM; ++mi) {
-                    const int n = mi * kGBN + 32 * (2 * wn + i) + hr;
-                    f.b[mi][i] = *(const u32x4 *)(st + kA + n * kRowB + ((c ^ chunk_swz(n)) << 4));
-                    f.sb[mi][i] = st[sb_at[mi][i] + 2 * q];
+                    const int n = mi * kGBN + 32 * (kTN * wn + j) + hr;
+                    f.b[mi][j] = *(const u32x4 *)(st + kA + n * kRowB + ((c ^ chunk_swz(n)) << 4));
+                    f.sb[mi][j] = st[sb_at[mi][j] + 2 * q];
                 }
-            }
         };
         // K-blocks past the end of K (last step only): zero A codes, unit scales.
         auto kill = [&](int s, int q, Quarter &f) {
             if (kCh * s + 2 * q + hb < Kb) return;
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
+            for (int i = 0; i < kTM; ++i) {
                 f.a[i] = u32x4{0, 0, 0, 0};
                 f.sa[i] = 127;
-#pragma unroll
-                for (int mi = 0; mi < NM; ++mi) f.sb[mi][i] = 127;
             }
+#pragma unroll
+            for (int j = 0; j < kTN; ++j)
+#pragma unroll
+                for (int mi = 0; mi < NM; ++mi) f.sb[mi][j] = 127;
         };
 
-        f32x16 acc[NM][2][2];
+        f32x16 acc[NM][kTM][kTN];
 #pragma unroll
         for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < kTM; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < kTN; ++j)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) acc[mi][i][j][v] = 0.0f;
         auto mma = [&](const Quarter &f) {
 #pragma unroll
             for (int mi = 0; mi < NM; ++mi)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < kTN; ++j)
 #pragma unroll
-                    for (int i = 0; i < 2; ++i) {
+                    for (int i = 0; i < kTM; ++i) {
                         const u32x4 av = f.a[i], bv = f.b[mi][j];
                         acc[mi][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                             i32x8_t{(int)av[0], (int)av[1], (int)av[2], (int)av[3], 0, 0, 0, 0},
@@ -378,45 +394,47 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
         if constexpr (!PAIR) {
             // y rows: each (tile, v) is 32 consecutive float32 columns of one row per half-wave
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < kTM; ++i)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int r = m0 + 32 * (2 * wm + i) + 8 * (v >> 2) + 4 * hb + (v & 3);
+                    const int r = m0 + 32 * (kTM * wm + i) + 8 * (v >> 2) + 4 * hb + (v & 3);
                     if (r >= M) continue;
                     const size_t orow = (size_t)(row0 + r);
 #pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const int n = n0 + 32 * (2 * wn + j) + hr;
+                    for (int j = 0; j < kTN; ++j) {
+                        const int n = n0 + 32 * (kTN * wn + j) + hr;
                         if (n < p.N) p.out[orow * p.N + n] = acc[0][i][j][v];
                     }
                 }
         } else {
             // h = silu(g) * u goes through LDS (the stage buffers are idle now): the wave writes
-            // its 64 x 64 quarter row-major (row stride 68 floats against bank conflicts), then
-            // lane L owns row L of the quarter and OCP-MX quantises its two 32-column blocks
+            // its RW x 64 block row-major (row stride 68 floats against bank conflicts), then
+            // each lane owns one 32-column block of one row at a time and OCP-MX quantises it
             // alone: block maximum, 32 codes packed into 16 bytes, one scale byte.
             constexpr int kLd = 68;
-            float *hq_lds = (float *)smem + wave * (64 * kLd);
+            constexpr int RW = 32 * kTM;                              // rows of the wave's block
+            float *hq_lds = (float *)smem + wave * (RW * kLd);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < kTM; ++i)
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                for (int j = 0; j < kTN; ++j)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) {
                         const int r = 32 * i + 8 * (v >> 2) + 4 * hb + (v & 3);
                         hq_lds[r * kLd + 32 * j + hr] = silu_fast(acc[0][i][j][v]) * acc[1][i][j][v];
                     }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");    // LDS is in order within a wave
-            const int r = m0 + 64 * wm + lane;                        // row within the expert
-            const bool row_ok = r < M;
-            const size_t orow = (size_t)(row0 + (row_ok ? r : 0));
             const bool vec_ok = (((uintptr_t)p.oq) & 15u) == 0;
 #pragma unroll
-            for (int jb = 0; jb < 2; ++jb) {
-                const int nb = n0 + 64 * wn + 32 * jb;                // first column of the block
+            for (int it0 = 0; it0 < RW * kTN; it0 += 64) {
+                const int rr = (it0 + lane) % RW, jb = (it0 + lane) / RW;   // row in the block, column block
+                const int r = m0 + RW * wm + rr;                          // row within the expert
+                const bool row_ok = r < M;
+                const size_t orow = (size_t)(row0 + (row_ok ? r : 0));
+                const int nb = n0 + 32 * kTN * wn + 32 * jb;              // first column of the block
                 f32x4 h[8];
 #pragma unroll
-                for (int q = 0; q < 8; ++q) h[q] = *(const f32x4 *)(hq_lds + lane * kLd + 32 * jb + 4 * q);
+                for (int q = 0; q < 8; ++q) h[q] = *(const f32x4 *)(hq_lds + rr * kLd + 32 * jb + 4 * q);
                 if (!row_ok || nb >= p.N) continue;
                 if (p.out) {
 #pragma unroll
