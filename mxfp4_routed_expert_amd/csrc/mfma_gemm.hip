@@ -7,8 +7,9 @@
 // scale byte; it accumulates the scaled products in float32.
 //
 // Tile: a workgroup computes 128 rows of one expert (tokens routed to it, in sorted order)
-// by 128 output columns -- of gate AND up for the SwiGLU pair.  Its 4 waves each own a
-// 64 x 64 quarter as 2 x 2 MFMA tiles per matrix.  K advances in steps of 256 values; a
+// by 128 output columns -- of gate AND up for the SwiGLU pair.  Its 8 waves (two per SIMD,
+// so one wave's matrix work covers the other's barrier and LDS waits) each own 64 rows x 32
+// columns as 2 x 1 MFMA tiles per matrix.  K advances in steps of 256 values; a
 // step's A rows (gathered token rows), B rows (weight rows) and scale windows travel from
 // global memory straight into LDS (global_load_lds), a whole 128-byte line per row, while
 // the matrix cores work on the previous step.
@@ -34,11 +35,14 @@ constexpr int kGBN = 128;          // output columns per workgroup tile
 #endif
 constexpr int kNW = MOE_GEMM_WAVES;
 constexpr int kGThreads = 64 * kNW;
-constexpr int kWN = 2;                         // waves along the output columns
+#ifndef MOE_GEMM_WN
+#define MOE_GEMM_WN (MOE_GEMM_WAVES == 8 ? 4 : 2)   // waves along the output columns
+#endif
+constexpr int kWN = MOE_GEMM_WN;
 constexpr int kWM = kNW / kWN;                 // waves along the rows
 constexpr int kTM = kGBM / 32 / kWM;           // 32-row MFMA tiles per wave
 constexpr int kTN = kGBN / 32 / kWN;           // 32-column MFMA tiles per wave and matrix
-static_assert(kNW == 4 || kNW == 8, "waves per workgroup");
+static_assert((kNW == 4 || kNW == 8) && kTM >= 1 && kTN >= 1 && 32 * kTM * kTN % 64 == 0, "wave layout");
 
 struct GemmParams {
     const uint8_t *a;              // A codes: token rows [n_arows][K/2] (gather) or rows [R][K/2]
@@ -408,11 +412,13 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
                 }
         } else {
             // h = silu(g) * u goes through LDS (the stage buffers are idle now): the wave writes
-            // its RW x 64 block row-major (row stride 68 floats against bank conflicts), then
-            // each lane owns one 32-column block of one row at a time and OCP-MX quantises it
-            // alone: block maximum, 32 codes packed into 16 bytes, one scale byte.
-            constexpr int kLd = 68;
+            // its RW x 32*kTN block row-major (row stride skewed by 4 floats against bank
+            // conflicts), then each lane owns one 32-column block of one row at a time and
+            // OCP-MX quantises it alone: block maximum, 32 codes packed into 16 bytes, one
+            // scale byte.
+            constexpr int kLd = 32 * kTN + 4;                         // row stride (floats), skewed
             constexpr int RW = 32 * kTM;                              // rows of the wave's block
+            static_assert(kNW * RW * kLd * 4 <= kStages * kStage, "epilogue staging fits the stage buffers");
             float *hq_lds = (float *)smem + wave * (RW * kLd);
 #pragma unroll
             for (int i = 0; i < kTM; ++i)
