@@ -652,18 +652,11 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(const DownComb
     // first batches in flight before the h copy
     u32x4 wv[kDcDepth][U][R];
     ScT sv[kDcDepth][U][R];
-    DcPos lp{0, wave % nslot, 0, wave / nslot};
-    const DcPos first = lp;
-    if (nq > 0) {
-#pragma unroll
-        for (int d = 0; d < kDcDepth; ++d) {
-            load(lp, wv[d], sv[d]);
-            if (lp.q < nq - 1) advance(lp);
-        }
-    }
     // h rows -> LDS: position i = (slot j, vector v) holds vector b*P + (s ^ swz(b)) of the
     // slot's row, v = b*P + s; invalid slots copy row 0 (never used).  The copy covers whole
     // 64-vector blocks; the tail of the last block reads a valid vector into the padding.
+    // It is waited for before the first weight loads are issued, so it is not queued behind
+    // them.
     {
         const int total = nslot * act_vec;
         const int blocks = (total + 63) / 64;
@@ -677,6 +670,15 @@ __global__ __launch_bounds__(kDcThreads) void down_combine_kernel(const DownComb
         }
     }
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    DcPos lp{0, wave % nslot, 0, wave / nslot};
+    const DcPos first = lp;
+    if (nq > 0) {
+#pragma unroll
+        for (int d = 0; d < kDcDepth; ++d) {
+            load(lp, wv[d], sv[d]);
+            if (lp.q < nq - 1) advance(lp);
+        }
+    }
 
     DcPos cp = first;
     const int nqr = (nq + kDcDepth - 1) / kDcDepth * kDcDepth;

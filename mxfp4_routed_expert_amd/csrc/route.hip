@@ -156,7 +156,7 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const uint16_t *__res
     u32x4 xv0 = *(const u32x4 *)(xrow + h0 + lh), xv1 = *(const u32x4 *)(xrow + h0 + lh + 8);
     u32x4 wv = __builtin_nontemporal_load((const u32x4 *)(wrow + h0 + lq));
     for (int h = h0; h < h1; h += kRtKC) {
-        __syncthreads();                               // the previous stage is consumed
+        lds_barrier();                                 // the previous stage is consumed
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             const f32x2 f0 = bf16x2_to_f32x2(xv0[q]), f1 = bf16x2_to_f32x2(xv1[q]);
@@ -172,7 +172,7 @@ __global__ __launch_bounds__(256) void router_tiled_kernel(const uint16_t *__res
         xv0 = *(const u32x4 *)(xrow + hn + lh);
         xv1 = *(const u32x4 *)(xrow + hn + lh + 8);
         wv = __builtin_nontemporal_load((const u32x4 *)(wrow + hn + lq));
-        __syncthreads();
+        lds_barrier();                                 // (the next stage's loads stay in flight)
 #pragma unroll
         for (int k0 = 0; k0 < kRtKC; k0 += 4) {
             double a[2], b[4];
