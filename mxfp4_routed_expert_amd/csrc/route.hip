@@ -261,6 +261,11 @@ MOE_DEV int wave_best_lane(uint64_t hk, int hi) {
     return __ffsll((long long)cand) - 1;
 }
 
+#ifndef MOE_TOPK_SORT_NK
+#define MOE_TOPK_SORT_NK 8       // most keys per lane that are sorted (more: per-round rescans)
+#endif
+constexpr int kSortNK = MOE_TOPK_SORT_NK;
+
 // In-register bitonic sort of a lane's N (power of two) entries into descending order of
 // (key, then lower index first); base values move with their keys.
 template <int N>
@@ -374,36 +379,72 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
             if (e < E && !((keep >> (e / gs)) & 1ull)) key[i] = 0;
         }
     }
-    // The lane's keys sorted once, best first (larger key, then lower expert); each round
-    // takes the wave-wide best of the lanes' first entries and the winner shifts its list.
-    // Key 0 (NaN, masked or past E) is never selected.
-    int idx[NK];
+    // Up to kSortNK keys per lane: the lane's keys are sorted once, best first (larger key,
+    // then lower expert); each round takes the wave-wide best of the lanes' first entries
+    // and the winner shifts its list.  More keys per lane: each lane tracks its best
+    // untaken key (its head) and only the round's winner rescans -- the sorting network
+    // grows as n log^2 n while the rescans grow as k n.  Both select the same experts in
+    // the same order.  Key 0 (NaN, masked or past E) is never selected.
     double braw[NK];             // unsorted, for the full softmax denominator
 #pragma unroll
-    for (int i = 0; i < NK; ++i) {
-        idx[i] = lane + 64 * i;
-        braw[i] = base[i];
-    }
-    sort_desc<NK>(key, idx, base);
+    for (int i = 0; i < NK; ++i) braw[i] = base[i];
     int my_e = -1;
     double l = 0.0;              // lane j < k: base value of the j-th selected expert
-    for (int j = 0; j < k; ++j) {
-        const int L = wave_best_lane(key[0], key[0] ? idx[0] : INT_MAX);
-        const int wi = key[0] ? idx[0] : INT_MAX;
-        const int win = __builtin_amdgcn_readlane(wi, L);
-        const double wl = readlane_f64(base[0], L);
-        if (lane == j && win != INT_MAX) {
-            my_e = win;
-            l = wl;
-        }
-        if (lane == L) {         // the winner drops its first entry
+    if constexpr (NK <= kSortNK) {
+        int idx[NK];
 #pragma unroll
-            for (int i = 0; i + 1 < NK; ++i) {
-                key[i] = key[i + 1];
-                idx[i] = idx[i + 1];
-                base[i] = base[i + 1];
+        for (int i = 0; i < NK; ++i) idx[i] = lane + 64 * i;
+        sort_desc<NK>(key, idx, base);
+        for (int j = 0; j < k; ++j) {
+            const int L = wave_best_lane(key[0], key[0] ? idx[0] : INT_MAX);
+            const int wi = key[0] ? idx[0] : INT_MAX;
+            const int win = __builtin_amdgcn_readlane(wi, L);
+            const double wl = readlane_f64(base[0], L);
+            if (lane == j && win != INT_MAX) {
+                my_e = win;
+                l = wl;
             }
-            key[NK - 1] = 0;
+            if (lane == L) {     // the winner drops its first entry
+#pragma unroll
+                for (int i = 0; i + 1 < NK; ++i) {
+                    key[i] = key[i + 1];
+                    idx[i] = idx[i + 1];
+                    base[i] = base[i + 1];
+                }
+                key[NK - 1] = 0;
+            }
+        }
+    } else {
+        uint32_t taken = 0;
+        uint64_t hk;
+        int hi;
+        double hv;
+        auto head = [&]() {      // best untaken key of this lane (equal keys: lower i = lower expert)
+            hk = 0;
+            hi = INT_MAX;
+            hv = 0.0;
+#pragma unroll
+            for (int i = 0; i < NK; ++i) {
+                if (!((taken >> i) & 1u) && key[i] > hk) {
+                    hk = key[i];
+                    hi = lane + 64 * i;
+                    hv = base[i];
+                }
+            }
+        };
+        head();
+        for (int j = 0; j < k; ++j) {
+            const int L = wave_best_lane(hk, hi);
+            const int win = __builtin_amdgcn_readlane(hi, L);
+            const double wl = readlane_f64(hv, L);
+            if (lane == j && win != INT_MAX) {
+                my_e = win;
+                l = wl;
+            }
+            if (lane == L && win != INT_MAX) {   // the winner drops its key
+                taken |= 1u << (win >> 6);
+                head();
+            }
         }
     }
 
