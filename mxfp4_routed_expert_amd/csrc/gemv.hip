@@ -460,8 +460,8 @@ static void pick_layout(int units, bool pair, int *G, int *nl);
 // directly, the k routed slots in order, then the shared expert -- the same sum in the same
 // order as the combine step, without writing and re-reading the expert rows.
 //   * The token's k+1 float32 h rows are copied into LDS by direct global->LDS loads
-//     (unit-swizzled as for the GEMV), after the first weight batches have been issued,
-//     so the copy's latency overlaps the first weight bytes.
+//     (unit-swizzled as for the GEMV), waited for before the first weight batches are
+//     issued (behind them the copy would land much later).
 //   * A lane group of G lanes covers kDcRows rows of one slot: every h value read from LDS
 //     serves kDcRows weight rows (a float32 h costs 8x the LDS bytes of the FP4 weights it
 //     multiplies, so one row per read would make LDS, not HBM, the limit).

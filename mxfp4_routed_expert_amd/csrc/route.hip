@@ -296,8 +296,9 @@ MOE_DEV void sort_desc(uint64_t (&key)[N], int (&idx)[N], double (&base)[N]) {
 }
 
 // One wave per token.  Lane l holds the selection keys of experts l, l+64, ... in
-// registers, sorted; each of the k rounds takes the wave-wide best first entry.  NaN keys are never
-// selected (ids -1 are emitted if fewer than k keys compare).
+// registers; each of the k rounds takes the wave-wide best of the lanes' best untaken keys
+// (see the selection below).  NaN keys are never selected (ids -1 are emitted if fewer
+// than k keys compare).
 // PERM: one workgroup holds every token (T <= 4, T*k <= 64) and also writes the token ->
 // expert permutation of the selected ids, as moe_permute would.
 template <int NK, bool PERM>
