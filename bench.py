@@ -111,6 +111,8 @@ def dominant_kernel(cfg):
     """Name pattern (as rocprofv3 reports it) of the routed gate/up kernel of a workload."""
     if cfg.act == "mxfp4" and cfg.T >= 64:
         return r"mxgemm_kernel<true, true>"
+    if cfg.wfmt == "mxfp4" and cfg.T >= 64:
+        return r"fgemm_kernel<true, \w+, true>"
     return r"gemv_kernel<\d+, \d+, \d+, true, true>"
 
 
@@ -316,8 +318,11 @@ def main():
         achieved = gu_bytes / (gu_us * 1e-6) / 1e9
         roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
                     frac=round(achieved / PEAK_HBM_GBPS, 4))
-    kname = "routed gate/up grouped GEMM (mxgemm_kernel)"
-    if cfg.act == "float" or cfg.T * cfg.k <= 64:
+    if cfg.act == "mxfp4" and cfg.T >= 64:
+        kname = "routed gate/up grouped GEMM (mxgemm_kernel, FP4 x FP4)"
+    elif cfg.wfmt == "mxfp4" and cfg.T >= 64:
+        kname = "routed gate/up grouped GEMM (fgemm_kernel, MXFP4 weights decoded to bf16)"
+    else:
         kname = "moe::gemv_kernel (routed gate/up" + (" + shared gate/up" if fused and cfg.shared else "") + \
                 ", fused SwiGLU)"
     roof.update(traffic=load_traffic(cfg), kernel=kname,

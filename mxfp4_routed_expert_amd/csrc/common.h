@@ -16,6 +16,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
 typedef int32_t i32x8 __attribute__((ext_vector_type(8)));
@@ -28,11 +29,37 @@ constexpr int kWave = 64;
 
 MOE_DEV float bf16_to_f32(uint32_t bits16) { return __uint_as_float(bits16 << 16); }
 
+// float32 -> bf16 bits, rounded to nearest even; NaN stays NaN.
+MOE_DEV uint32_t bf16_rne_bits(float f) {
+    const uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;   // NaN stays NaN
+    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
 // E8M0 scale byte -> float32 2^(b-127).  b = 0 is the float32 subnormal 2^-127;
 // b = 255 is NaN (OCP MX v1.0, E8M0).
 MOE_DEV float e8m0_to_f32(uint32_t b) {
     uint32_t bits = b == 0 ? 0x00400000u : (b == 255 ? 0x7fc00000u : (b << 23));
     return __uint_as_float(bits);
+}
+
+// Four bf16 pairs -> one 8-value operand slice, in order.
+MOE_DEV bf16x8 pack8(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
+    bf16x8 r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+    return r;
+}
+
+// MFMA operand slices of one 32-code MXFP4 unit with its block scale: slice q = values 8q..8q+7.
+MOE_DEV void unit_to_bf16x8(const u32x4 w, float sc, bf16x8 (&a)[4]) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        a[q] = pack8(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 0),
+                     __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 1),
+                     __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 2),
+                     __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 3));
+    }
 }
 
 // Two E2M1 codes (byte `sel` of `w`: low nibble first) -> two bf16 values, unscaled.

@@ -3,8 +3,9 @@
 // Each expert computes a SwiGLU FFN, h = silu(gate a) * (up a), y = down h (the
 // "SituAndMul" activation of the rabbit README source tree, read as SiLU-and-multiply),
 // on the rows routed to it.  Small row counts per expert (decode) run on the
-// dequant-GEMV kernels; MX-quantised activations with many rows per expert (prefill)
-// run on the block-scaled FP4 matrix-core grouped GEMM.
+// dequant-GEMV kernels; with many rows per expert (prefill) MX-quantised activations run
+// on the block-scaled FP4 matrix-core grouped GEMM, and unquantised activations over MXFP4
+// weights on the bf16 matrix-core grouped GEMM.
 #include "gemv.h"
 
 #ifndef MOE_USE_MFMA_GEMV
@@ -19,6 +20,12 @@ moe_status mfma_gateup_launch(const moe_expert_weights *w, int T, int k, const u
                               uint8_t *hq, uint8_t *hs, hipStream_t stream);
 moe_status mfma_down_launch(const moe_expert_weights *w, const uint8_t *hq, const uint8_t *hs,
                             const int32_t *offsets, int R, float *y, hipStream_t stream);
+bool fgemm_wanted(const moe_expert_weights *w, int act, int T);
+moe_status fgemm_gateup_launch(const moe_expert_weights *w, int T, int k, const void *x, bool x_f32,
+                               const int32_t *offsets, const int32_t *sorted_pairs, int R, float *h,
+                               hipStream_t stream);
+moe_status fgemm_down_launch(const moe_expert_weights *w, const float *h, const int32_t *offsets, int R, float *y,
+                             hipStream_t stream);
 
 namespace {
 
@@ -117,6 +124,8 @@ moe_status gateup_impl(const moe_expert_weights *w, int act, int T, int k, const
         MOE_TRY(mx_quantize_launch(T, w->d_model, x, x_dtype == MOE_DT_F32, ws.xq, ws.xs, s));
         if (mfma_path_wanted(w, act, T, k, offsets != nullptr))
             return mfma_gateup_launch(w, T, k, ws.xq, ws.xs, offsets, sorted_pairs, R, h, hq, hs, s);
+    } else if (fgemm_wanted(w, act, T)) {
+        return fgemm_gateup_launch(w, T, k, x, x_dtype == MOE_DT_F32, offsets, sorted_pairs, R, h, s);
     }
     GemvParams p = base_params(w, T, k, offsets, sorted_pairs, R);
     p.w[0] = w->gate;
@@ -154,6 +163,7 @@ moe_status down_impl(const moe_expert_weights *w, int act, int T, int k, const f
     const int slots = offsets ? (w->num_experts < R ? w->num_experts : R) : 1;
     if (act == MOE_ACT_MXFP4 && mfma_path_wanted(w, act, T, k, offsets != nullptr))
         return mfma_down_launch(w, hq, hs, offsets, R, y, s);
+    if (act == MOE_ACT_FLOAT && fgemm_wanted(w, act, T)) return fgemm_down_launch(w, h, offsets, R, y, s);
     GemvParams p = base_params(w, T, k, offsets, nullptr, R);
     p.w[0] = w->down;
     p.s[0] = w->down_s;

@@ -20,8 +20,6 @@
 
 namespace moe {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-
 constexpr int kMfWaves = 4;
 constexpr int kMfThreads = kMfWaves * 64;
 #ifndef MOE_MFMA_KUNROLL
@@ -30,30 +28,6 @@ constexpr int kMfThreads = kMfWaves * 64;
 constexpr int kMfKU = MOE_MFMA_KUNROLL;   // K-steps loaded per lane before use
 constexpr int kMfMaxTok = 16;             // MFMA columns
 constexpr size_t kMfLdsBudget = 64 * 1024;
-
-MOE_DEV bf16x8 pack8(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
-    bf16x8 r;
-    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
-    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
-    return r;
-}
-
-// A-operand slices of one 32-code unit with its block scale: slice q = values 8q..8q+7.
-MOE_DEV void unit_to_bf16x8(const u32x4 w, float sc, bf16x8 (&a)[4]) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        a[q] = pack8(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 0),
-                     __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 1),
-                     __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 2),
-                     __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 3));
-    }
-}
-
-MOE_DEV uint32_t bf16_rne_bits(float f) {
-    const uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;   // NaN stays NaN
-    return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
 
 // Stage activation rows [c0, c0+mc) of the expert, K positions [k0, k1), into this wave's
 // LDS planes (bf16; f32 input also fills the lo plane).  Row stride `ld` elements.

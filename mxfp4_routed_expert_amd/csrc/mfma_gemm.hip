@@ -23,6 +23,7 @@
 #include <type_traits>
 
 #include "gemv.h"
+#include "tile_sched.h"
 
 namespace moe {
 
@@ -101,56 +102,6 @@ MOE_DEV void wait_vm_and_barrier() {
     asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N) : "memory");
 }
 
-// Row tiles per expert, as an inclusive prefix over experts in LDS: tp[e] = number of
-// 128-row tiles of experts 0..e.  Every workgroup builds it once from expert_offsets.
-MOE_DEV int build_tile_prefix(const int32_t *offsets, int E, int R, int *tp, int *s_wave) {
-    constexpr int kPer = (MOE_MAX_EXPERTS + kGThreads - 1) / kGThreads;   // experts per thread
-    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-    int t[kPer], sum = 0;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-        const int e = tid * kPer + u;
-        const int lo = offsets[min(e, E)], hi = offsets[min(e + 1, E)];
-        const int m = (e < E && lo >= 0 && hi <= R) ? max(hi - lo, 0) : 0;
-        t[u] = (m + kGBM - 1) / kGBM;
-        sum += t[u];
-    }
-    int incl = sum;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const int v = __shfl_up(incl, d, kWave);
-        if (lane >= d) incl += v;
-    }
-    if (lane == 63) s_wave[wave] = incl;
-    __syncthreads();
-    int base = 0, total = 0;
-#pragma unroll
-    for (int w = 0; w < kGThreads / 64; ++w) {
-        base += w < wave ? s_wave[w] : 0;
-        total += s_wave[w];
-    }
-    int run = base + incl - sum;
-#pragma unroll
-    for (int u = 0; u < kPer; ++u) {
-        run += t[u];
-        const int e = tid * kPer + u;
-        if (e < E) tp[e] = run;
-    }
-    __syncthreads();
-    return total;
-}
-
-// Expert owning row tile mt: the first e with tp[e] > mt (E <= 64 * 32: two probes).
-MOE_DEV int tile_expert(const int *tp, int E, int mt) {
-    const int lane = lane_id();
-    const int probe = min(lane * 32 + 31, E - 1);
-    const uint64_t m1 = __ballot(lane * 32 < E && tp[probe] > mt);
-    const int c = __ffsll((long long)m1) - 1;                  // chunk of 32 experts
-    const int e2 = c * 32 + (lane & 31);
-    const uint64_t m2 = __ballot(lane < 32 && e2 < E && tp[min(e2, E - 1)] > mt);
-    return c * 32 + __ffsll((long long)m2) - 1;
-}
-
 // K-step of MOE_GEMM_KSTEP values (256: each operand row contributes one whole 128-byte
 // line per step; 128: half a line, so that more steps fit in LDS at once).
 #ifndef MOE_GEMM_KSTEP
@@ -191,14 +142,14 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
     __shared__ int s_wave[kGThreads / 64];
 
     const int NT = (p.N + kGBN - 1) / kGBN;
-    const int total_mt = ROUTED ? build_tile_prefix(p.offsets, p.E, p.R, s_tp, s_wave) : (p.T + kGBM - 1) / kGBM;
+    const int total_mt = ROUTED ? build_tile_prefix<kGThreads, kGBM>(p.offsets, p.E, p.R, s_tp, s_wave) : (p.T + kGBM - 1) / kGBM;
     const int items = total_mt * NT;
     // Items are ordered expert by expert, then by column tile, then by row tile, and each
     // round of G workgroups hands XCD x (workgroups x, x+8, ...) a contiguous run of G/8
     // items: the row tiles of one expert that share a column tile of weights run at the
     // same time on the same XCD, so those weight bytes come from that XCD's L2.
     const int G = gridDim.x;
-    const int slot = (G & 7) == 0 ? (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3) : blockIdx.x;
+    const int slot = xcd_slot(blockIdx.x, G);
     const int lane = lane_id(), wave = wave_id();
     const int wm = wave / kWN, wn = wave % kWN;        // output block of this wave
     const int hr = lane & 31, hb = lane >> 5;          // MFMA operand row / K-block of this lane

@@ -244,6 +244,10 @@ FFN_CASES = {
     "mxfp4_ragged": tiny(name="rag", wtag=81, T=29, H=1024, I=416, E=6, k=3),
     "mxfp4_wide": tiny(name="wide", wtag=82, T=5, H=2368, I=7168 // 4, E=4, k=2),
     "fp8": tiny(name="f8", wtag=83, wfmt="fp8b128", T=19, H=384, I=256, E=5, k=2),
+    # >= 64 tokens over MXFP4 weights take the bf16 matrix-core GEMM: K tails of one MX block
+    # (544 = 8.5 x 64, 416 = 6.5 x 64), ragged 128-column tiles, experts over several row tiles
+    "mxfp4_prefill_ragged": tiny(name="fg1", wtag=95, T=150, H=544, I=416, E=6, k=3),
+    "mxfp4_prefill_multitile": tiny(name="fg2", wtag=96, T=300, H=256, I=160, E=2, k=1),
 }
 
 
@@ -310,10 +314,16 @@ LAYER_CASES = {
     "tiny_fused_gated": tiny(name="tfg", wtag=87, T=3, k=3, shared="gated", shared_K=256, shared_I=128),
     "tiny_fused_fp8_ungated": tiny(name="tff", wtag=88, wfmt="fp8b128", score="sigmoid", select_bias_std=0.01,
                                    I=256, T=2, k=4, shared="ungated", shared_K=256, shared_I=256),
+    # prefill sizes on the bf16 matrix-core GEMM: the shared expert in the identity form, and
+    # the latent form (float32 x_lat split into two bf16 terms)
+    "prefill_gated_shared": tiny(name="pgs", wtag=97, T=160, H=512, I=160, E=8, k=2, shared="gated",
+                                 shared_K=512, shared_I=192),
+    "prefill_latent": tiny(name="plt", wtag=98, latent=128, H=512, I=96, T=96, shared="ungated", shared_K=512,
+                           shared_I=64),
 }
 
 
-GRAPH_CASES = ["tiny_gated_shared", "tiny_fused_gated", "tiny_latent", "tiny_sigmoid_fp8"]
+GRAPH_CASES = ["tiny_gated_shared", "tiny_fused_gated", "tiny_latent", "tiny_sigmoid_fp8", "prefill_gated_shared"]
 
 
 @pytest.mark.parametrize("name", GRAPH_CASES)
@@ -556,6 +566,28 @@ def test_prefill_mx_full_size_stagewise_sampled(dev, M):
     cfg = synth.get("qwen38max_prefill")
     say("prefill, MX activations, stage-wise on sampled tokens")
     _stagewise_mx(M, cfg, dev, tokens=[3, 300])
+
+
+def test_prefill_float_full_size_sampled_tokens(dev, M):
+    cfg = synth.get("qwen38max_prefill_hot_float")
+    say("building qwen38max_prefill_hot_float")
+    layer, out, inp = _run_layer(M, cfg, dev)
+    r = OL.route(inp.x, inp.w_router, cfg.k, cfg.score, cfg.renormalize, cfg.routed_scaling, inp.logit_bias,
+                 None, inp.w_shared_gate)
+    np.testing.assert_array_equal(to_np(layer.ids), r.ids)
+    ge, gs = host_expert_getter(cfg)
+    x = OF.bf16_value(inp.x)
+    sample = [0, 129, 511]
+    ref = np.zeros((len(sample), cfg.H))
+    for e in np.unique(r.ids[sample]):
+        G, U, D = OL.dequant_expert(ge(int(e)))
+        for i, tkn in enumerate(sample):
+            for j in np.where(r.ids[tkn] == e)[0]:
+                ref[i] += r.weights[tkn, j] * OL.ffn(x[tkn:tkn + 1], G, U, D)[0]
+    G, U, D = OL.dequant_expert(gs())
+    ys = OL.ffn(x[sample], G, U, D)
+    ref += r.shared_gate[sample][:, None] * ys
+    assert_close(to_np(out)[sample], ref, "prefill float out (sampled tokens)")
 
 
 def test_zero_tokens_is_a_no_op(dev, M):
