@@ -112,7 +112,7 @@ def dominant_kernel(cfg):
     if cfg.act == "mxfp4" and cfg.T >= 64:
         return r"mxgemm_kernel<true, true>"
     if cfg.wfmt == "mxfp4" and cfg.T >= 64:
-        return r"fgemm_kernel<true, \w+, true>"
+        return r"fgemm_pair_kernel<\w+, true>"
     return r"gemv_kernel<\d+, \d+, \d+, true, true>"
 
 
@@ -321,7 +321,7 @@ def main():
     if cfg.act == "mxfp4" and cfg.T >= 64:
         kname = "routed gate/up grouped GEMM (mxgemm_kernel, FP4 x FP4)"
     elif cfg.wfmt == "mxfp4" and cfg.T >= 64:
-        kname = "routed gate/up grouped GEMM (fgemm_kernel, MXFP4 weights decoded to bf16)"
+        kname = "routed gate/up grouped GEMM (fgemm_pair_kernel, MXFP4 weights decoded to bf16)"
     else:
         kname = "moe::gemv_kernel (routed gate/up" + (" + shared gate/up" if fused and cfg.shared else "") + \
                 ", fused SwiGLU)"

@@ -7,18 +7,25 @@
 // the OCP MX element and scale formats).  float32 operands are split into
 // hi = RN_bf16(v) and lo = RN_bf16(v - hi), two products each, together within 2^-17 |v|.
 //
-// Tile: a workgroup computes 128 rows of one expert (tokens routed to it, in sorted order)
-// by 128 output columns -- of gate AND up for the SwiGLU pair, at the same columns, so
-// h = silu(g) * u is formed in registers.  Its 8 waves (two per SIMD) each own 64 rows x
-// 32 columns per matrix as 4 x 2 MFMA tiles of 16 x 16.  The weights are the MFMA's first
+// Both kernels: a workgroup computes 128 rows of one expert (tokens routed to it, in sorted
+// order) by a tile of output columns with 8 waves (two per SIMD), 2 along the rows x 4 along
+// the columns, each owning 64 rows as 16 x 16 MFMA tiles.  The weights are the MFMA's first
 // operand (rows = output columns n) and the activations its second, so a lane's four
-// accumulators are four consecutive columns of one row: one 16-byte store.
-// K advances in steps of 64 values.  A step's weight codes and scales and its activation
-// rows are loaded into registers MOE_FGEMM_PF steps ahead; when a step's turn comes its
-// codes are decoded to bf16 and written with the activation rows into one of two LDS
-// buffers while the matrix cores work on the other, one barrier per step.
-// The grid is persistent and walks (row tile, column tile) items expert by expert, with
-// the same XCD-aware order as the FP4 grouped GEMM.
+// accumulators are four consecutive columns of one row: one 16-byte store.  The activation
+// rows of a K-step, shared by all 8 waves, are staged in LDS, double-buffered: while the
+// matrix cores work on step s, step s+1 (loaded into registers earlier) is written to the
+// other buffer; one barrier per step.  The grid is persistent and walks (row tile, column
+// tile) items expert by expert, in the same XCD-aware order as the FP4 grouped GEMM.
+//
+// gate/up (fgemm_pair_kernel): 128 columns of gate AND up at the same columns, so
+// h = silu(g) * u is formed in registers.  K-steps of 64 values; each weight unit (32 codes
+// and a scale) of the step is decoded once, by one thread, into the LDS stage next to the
+// activations: the two row-waves that share a column then read it instead of decoding it twice.
+// down (fgemm_down_kernel): 256 columns of one matrix, K-steps of 128 values (4 MX blocks).
+// Weights never pass through LDS: for each of its four 16-column tiles a lane loads the
+// 16-byte unit of row l%16, block l/16 of the step, and decodes it right before its MFMAs
+// (MFMA q takes values 8q .. 8q+7 of every lane group's block); with float32 h each decoded
+// weight feeds twice as many products (hi and lo), which pays for decoding it per wave.
 #include <algorithm>
 
 #include "gemv.h"
@@ -26,19 +33,18 @@
 
 namespace moe {
 
-constexpr int kFBM = 128;                  // rows (tokens) per tile
-constexpr int kFBN = 128;                  // output columns per tile and matrix
-constexpr int kFBK = 64;                   // K values per step
-constexpr int kFThreads = 512;             // 8 waves: 2 along the rows x 4 along the columns
-constexpr int kFRow = kFBK * 2;            // LDS bytes per operand row per step (bf16)
 #ifndef MOE_USE_BF16_GEMM
 #define MOE_USE_BF16_GEMM 1                // 0: prefill with unquantised activations on the GEMV
 #endif
-#ifndef MOE_FGEMM_PF
-#define MOE_FGEMM_PF 3                     // steps whose loads are in flight
+#ifndef MOE_FGEMM_PAIR_PF
+#define MOE_FGEMM_PAIR_PF 2                // gate/up: steps whose loads are in flight
 #endif
-constexpr int kFPf = MOE_FGEMM_PF;
-static_assert(kFPf >= 1 && kFPf <= 4, "prefetch depth");
+#ifndef MOE_FGEMM_DOWN_PF
+#define MOE_FGEMM_DOWN_PF 1                // down: steps whose loads are in flight
+#endif
+
+constexpr int kFBM = 128;                  // rows (tokens) per tile
+constexpr int kFThreads = 512;             // 8 waves: 2 along the rows x 4 along the columns
 
 struct FGemmParams {
     const void *a;                 // activations: bf16 or float32 rows [n_arows][K]
@@ -55,128 +61,144 @@ struct FGemmParams {
     float *out;                    // [R][N] float32: h = silu(gate) * up, or y
 };
 
-// 16-byte chunk c (8 values) of LDS row r sits at chunk position c ^ fswz(r): an operand read
-// (16 rows at one chunk) then touches 16 distinct 16-byte bank groups.
-MOE_DEV int fswz(int r) { return (r >> 1) & 7; }
+// Item -> (expert, first row, rows of the expert, row tile, column tile).
+template <bool ROUTED>
+MOE_DEV void fgemm_item(const FGemmParams &p, const int *tp, int total_mt, int NT, int item, int &e, int &row0,
+                        int &M, int &tile, int &nt) {
+    if constexpr (ROUTED) {
+        e = tile_expert(tp, p.E, item / NT);
+        const int tpx = e > 0 ? tp[e - 1] : 0, te = tp[e] - tpx;
+        const int r = item - NT * tpx;
+        nt = r / te;
+        tile = r - nt * te;
+        row0 = p.offsets[e];
+        M = p.offsets[e + 1] - row0;
+    } else {
+        e = 0;
+        row0 = 0;
+        M = p.T;
+        nt = item / total_mt;
+        tile = item - nt * total_mt;
+    }
+}
+
+// Source of activation row r of a tile (rows past the expert's end repeat a valid row;
+// their results are not stored).
+template <bool SPLIT>
+MOE_DEV const unsigned char *fgemm_arow(const FGemmParams &p, int row0, int M, int m0, int r) {
+    int src = row0 + min(m0 + r, M - 1);
+    if (p.gather) src = p.sorted_pairs[src] / p.k;
+    src = min(max(src, 0), p.n_arows - 1);
+    return (const unsigned char *)p.a + (size_t)src * p.K * (SPLIT ? 4 : 2);
+}
+
+// 8 float32 values -> bf16 hi and lo terms, 16 bytes each.
+MOE_DEV void split8(const u32x4 a, const u32x4 b, u32x4 &h4, u32x4 &l4) {
+    uint32_t hb[8], lb[8];
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const float f = __uint_as_float(t < 4 ? a[t] : b[t - 4]);
+        hb[t] = bf16_rne_bits(f);
+        lb[t] = bf16_rne_bits(f - __uint_as_float(hb[t] << 16));
+    }
+    h4 = u32x4{hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, hb[4] | hb[5] << 16, hb[6] | hb[7] << 16};
+    l4 = u32x4{lb[0] | lb[1] << 16, lb[2] | lb[3] << 16, lb[4] | lb[5] << 16, lb[6] | lb[7] << 16};
+}
+
+// ------------------------------------------------------------------ gate/up
+
+constexpr int kPBK = 64;                   // K values per step (2 MX blocks)
+constexpr int kPRow = kPBK * 2;            // LDS bytes per operand row per step (bf16)
+constexpr int kPBN = 128;                  // output columns per tile and matrix
+
+// 16-byte chunk c (of 8) of LDS row r sits at position c ^ pswz(r): an operand read (16 rows
+// at one chunk) then touches 16 distinct 16-byte bank groups.
+MOE_DEV int pswz(int r) { return (r >> 1) & 7; }
 
 template <bool SPLIT>
-struct FStep {                     // one thread's loads for one K-step
+struct PStep {                     // one thread's loads for one K-step
     u32x4 wc;                      // 32 weight codes (one MX block)
     uint32_t wsc;                  // its scale byte
     u32x4 a[SPLIT ? 4 : 2];        // 16 activation values (bf16: 2 x 16 B; float32: 4 x 16 B)
 };
 
-template <bool PAIR, bool SPLIT, bool ROUTED>
-__global__ __launch_bounds__(kFThreads) void fgemm_kernel(const FGemmParams p) {
-    constexpr int NM = PAIR ? 2 : 1;
+template <bool SPLIT, bool ROUTED>
+__global__ __launch_bounds__(kFThreads) void fgemm_pair_kernel(const FGemmParams p) {
+    constexpr int PF = MOE_FGEMM_PAIR_PF;
     constexpr int NP = SPLIT ? 2 : 1;                  // activation planes: hi (and lo)
-    constexpr int kWPlane = kFBN * kFRow;              // one matrix's decoded step
-    constexpr int kAPlane = kFBM * kFRow;              // one activation plane's step
-    constexpr int kStage = NM * kWPlane + NP * kAPlane;
-    constexpr int kWTasks = NM * kFBN * 2;             // (matrix, row, MX block) per step
-    static_assert(kWTasks % 64 == 0 && kWTasks <= kFThreads && kFBM * 4 == kFThreads, "thread roles");
+    constexpr int kWPlane = kPBN * kPRow;              // one matrix's decoded step
+    constexpr int kAPlane = kFBM * kPRow;              // one activation plane's step
+    constexpr int kStage = 2 * kWPlane + NP * kAPlane;
+    static_assert(PF >= 1 && PF <= 4, "prefetch depth");
+    static_assert(2 * kPBN * 2 == kFThreads && kFBM * 4 == kFThreads, "thread roles");
     __shared__ __align__(16) unsigned char smem[2 * kStage];
     __shared__ int s_tp[ROUTED ? MOE_MAX_EXPERTS : 1];
     __shared__ int s_wave[kFThreads / 64];
 
-    const int NT = (p.N + kFBN - 1) / kFBN;
+    const int NT = (p.N + kPBN - 1) / kPBN;
     const int total_mt = ROUTED ? build_tile_prefix<kFThreads, kFBM>(p.offsets, p.E, p.R, s_tp, s_wave)
                                 : (p.T + kFBM - 1) / kFBM;
     const int items = total_mt * NT;
     const int G = gridDim.x;
     const int slot = xcd_slot(blockIdx.x, G);
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
-    const int wm = wave >> 2, wn = wave & 3;            // 64-row x 32-column block of this wave
+    const int wm = wave >> 2, wn = wave & 3;            // 64 rows x 32 columns (per matrix)
     const int lr = lane & 15, lg = lane >> 4;          // MFMA operand row / 8-value K slot
     const int Kh = p.K / 2, Kb = p.K / 32;
-    const int S = (p.K + kFBK - 1) / kFBK;             // K-steps (the last may hold one MX block)
-    // weight-decode role: matrix wm_, row wr, MX block wb of the step
-    const bool wrole = tid < kWTasks;
-    const int wm_ = tid / (2 * kFBN), wr = (tid >> 1) & (kFBN - 1), wb = tid & 1;
-    // activation role: row ar, values 16 * ac .. 16 * ac + 15 of the step
-    const int ar = tid >> 2, ac = tid & 3;
+    const int S = (p.K + kPBK - 1) / kPBK;             // K-steps (the last may hold one MX block)
+    const int wmat = tid >> 8, wr = (tid >> 1) & (kPBN - 1), wb = tid & 1;   // decode: matrix, row, block
+    const int ar = tid >> 2, ac = tid & 3;             // staging: row ar, values 16 ac .. 16 ac + 15
 
     for (int item = slot; item < items; item += G) {
-        int e = 0, tile = 0, nt = 0, row0 = 0, M = p.T;
-        if constexpr (ROUTED) {
-            e = tile_expert(s_tp, p.E, item / NT);
-            const int tpx = e > 0 ? s_tp[e - 1] : 0, te = s_tp[e] - tpx;
-            const int r = item - NT * tpx;
-            nt = r / te;
-            tile = r - nt * te;
-            row0 = p.offsets[e];
-            M = p.offsets[e + 1] - row0;
-        } else {
-            nt = item / total_mt;
-            tile = item - nt * total_mt;
-        }
-        const int m0 = tile * kFBM, n0 = nt * kFBN;
+        int e, row0, M, tile, nt;
+        fgemm_item<ROUTED>(p, s_tp, total_mt, NT, item, e, row0, M, tile, nt);
+        const int m0 = tile * kFBM, n0 = nt * kPBN;
+        const size_t wrow = (size_t)e * p.N + min(n0 + wr, p.N - 1);   // rows past N: not stored
+        const uint8_t *wsrc = p.w[wmat] + wrow * Kh;
+        const uint8_t *ssrc = p.ws[wmat] + wrow * Kb;
+        const unsigned char *asrc = fgemm_arow<SPLIT>(p, row0, M, m0, ar);
 
-        // this thread's source rows (rows past the expert's or the matrix's end repeat a
-        // valid row; their results are not stored)
-        const size_t wrow = ((size_t)e * p.N + min(n0 + wr, p.N - 1));
-        const uint8_t *wsrc = p.w[PAIR ? wm_ : 0] + wrow * Kh;
-        const uint8_t *ssrc = p.ws[PAIR ? wm_ : 0] + wrow * Kb;
-        int src = row0 + min(m0 + ar, M - 1);
-        if (p.gather) src = p.sorted_pairs[src] / p.k;
-        src = min(max(src, 0), p.n_arows - 1);
-        const unsigned char *asrc =
-            (const unsigned char *)p.a + (size_t)src * p.K * (SPLIT ? 4 : 2);
-
-        auto issue = [&](FStep<SPLIT> &L, int s) {
-            if (wrole) {
-                const int kb = min(2 * s + wb, Kb - 1);
-                L.wc = *(const u32x4 *)(wsrc + (size_t)kb * 16);
-                L.wsc = ssrc[kb];
-            }
-            const int kc = min(s * kFBK + 16 * ac, p.K - 16);   // K % 32 == 0
+        auto issue = [&](PStep<SPLIT> &L, int s) {
+            const int kb = min(2 * s + wb, Kb - 1);
+            L.wc = *(const u32x4 *)(wsrc + (size_t)kb * 16);
+            L.wsc = ssrc[kb];
+            const int kc = min(s * kPBK + 16 * ac, p.K - 16);   // K % 32 == 0
             const u32x4 *q = (const u32x4 *)(asrc + (size_t)kc * (SPLIT ? 4 : 2));
 #pragma unroll
             for (int i = 0; i < (SPLIT ? 4 : 2); ++i) L.a[i] = q[i];
         };
-        auto commit = [&](const FStep<SPLIT> &L, int s, int buf) {
+        auto commit = [&](const PStep<SPLIT> &L, int s, int buf) {
             unsigned char *st = smem + buf * kStage;
-            const int kv = p.K - s * kFBK;                     // valid values of the step
-            if (wrole) {
+            const int kv = p.K - s * kPBK;                     // valid values of the step
+            {
                 bf16x8 v[4];
                 unit_to_bf16x8(L.wc, e8m0_to_f32(L.wsc), v);
                 const bool live = wb * 32 < kv;
-                unsigned char *row = st + wm_ * kWPlane + wr * kFRow;
+                unsigned char *row = st + wmat * kWPlane + wr * kPRow;
 #pragma unroll
                 for (int q = 0; q < 4; ++q)
-                    *(u32x4 *)(row + (((4 * wb + q) ^ fswz(wr)) << 4)) =
+                    *(u32x4 *)(row + (((4 * wb + q) ^ pswz(wr)) << 4)) =
                         live ? __builtin_bit_cast(u32x4, v[q]) : u32x4{0, 0, 0, 0};
             }
             const bool live = 16 * ac < kv;
-            unsigned char *row = st + NM * kWPlane + ar * kFRow;
-            if constexpr (!SPLIT) {
+            unsigned char *row = st + 2 * kWPlane + ar * kPRow;
 #pragma unroll
-                for (int i = 0; i < 2; ++i)
-                    *(u32x4 *)(row + (((2 * ac + i) ^ fswz(ar)) << 4)) = live ? L.a[i] : u32x4{0, 0, 0, 0};
-            } else {
-#pragma unroll
-                for (int i = 0; i < 2; ++i) {
-                    uint32_t hb[8], lb[8];
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        const float f = __uint_as_float(L.a[2 * i + t / 4][t % 4]);
-                        hb[t] = bf16_rne_bits(f);
-                        lb[t] = bf16_rne_bits(f - __uint_as_float(hb[t] << 16));
-                    }
-                    const u32x4 h4 = {hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, hb[4] | hb[5] << 16,
-                                      hb[6] | hb[7] << 16};
-                    const u32x4 l4 = {lb[0] | lb[1] << 16, lb[2] | lb[3] << 16, lb[4] | lb[5] << 16,
-                                      lb[6] | lb[7] << 16};
-                    const int off = ((2 * ac + i) ^ fswz(ar)) << 4;
+            for (int i = 0; i < 2; ++i) {
+                const int off = ((2 * ac + i) ^ pswz(ar)) << 4;
+                if constexpr (!SPLIT) {
+                    *(u32x4 *)(row + off) = live ? L.a[i] : u32x4{0, 0, 0, 0};
+                } else {
+                    u32x4 h4, l4;
+                    split8(L.a[2 * i], L.a[2 * i + 1], h4, l4);
                     *(u32x4 *)(row + off) = live ? h4 : u32x4{0, 0, 0, 0};
                     *(u32x4 *)(row + kAPlane + off) = live ? l4 : u32x4{0, 0, 0, 0};
                 }
             }
         };
 
-        f32x4 acc[NM][2][4];
+        f32x4 acc[2][2][4];
 #pragma unroll
-        for (int m = 0; m < NM; ++m)
+        for (int m = 0; m < 2; ++m)
 #pragma unroll
             for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -185,26 +207,26 @@ __global__ __launch_bounds__(kFThreads) void fgemm_kernel(const FGemmParams p) {
         auto compute = [&](int buf) {
             const unsigned char *st = smem + buf * kStage;
 #pragma unroll
-            for (int ks = 0; ks < kFBK / 32; ++ks) {
+            for (int ks = 0; ks < kPBK / 32; ++ks) {
                 const int c = 4 * ks + lg;
-                bf16x8 bw[NM][2], xa[NP][4];
+                bf16x8 bw[2][2], xa[NP][4];
 #pragma unroll
-                for (int m = 0; m < NM; ++m)
+                for (int m = 0; m < 2; ++m)
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
                         const int r = 32 * wn + 16 * i + lr;
-                        bw[m][i] = *(const bf16x8 *)(st + m * kWPlane + r * kFRow + ((c ^ fswz(r)) << 4));
+                        bw[m][i] = *(const bf16x8 *)(st + m * kWPlane + r * kPRow + ((c ^ pswz(r)) << 4));
                     }
 #pragma unroll
                 for (int pl = 0; pl < NP; ++pl)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int r = 64 * wm + 16 * j + lr;
-                        xa[pl][j] = *(const bf16x8 *)(st + NM * kWPlane + pl * kAPlane + r * kFRow +
-                                                      ((c ^ fswz(r)) << 4));
+                        xa[pl][j] = *(const bf16x8 *)(st + 2 * kWPlane + pl * kAPlane + r * kPRow +
+                                                      ((c ^ pswz(r)) << 4));
                     }
 #pragma unroll
-                for (int m = 0; m < NM; ++m)
+                for (int m = 0; m < 2; ++m)
 #pragma unroll
                     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -216,29 +238,31 @@ __global__ __launch_bounds__(kFThreads) void fgemm_kernel(const FGemmParams p) {
             }
         };
 
-        // ---- pipeline: slot s % PF holds step s's loads from its issue until its commit
-        FStep<SPLIT> L[kFPf];
+        // ---- pipeline: slot s % PF holds step s's loads from their issue until commit(s),
+        // one step before compute(s).  Loads and commits are unconditional (past the last
+        // step they re-read clamped, valid addresses and write zeros to the buffer no wave
+        // reads): a load under a branch would make the compiler drain every load at the join.
+        // Only the last S % PF steps run under a guard, after the loop.
+        PStep<SPLIT> L[PF];
 #pragma unroll
-        for (int j = 0; j < kFPf; ++j)
-            if (j < S) issue(L[j], j);
+        for (int j = 0; j < PF; ++j) issue(L[j], j);
         commit(L[0], 0, 0);
-        if (kFPf < S) issue(L[0], kFPf);
+        issue(L[0], PF);
         lds_barrier();
-        for (int s0 = 0; s0 < S; s0 += kFPf) {
+        auto step = [&](PStep<SPLIT> &Ln, int s) {         // Ln: the slot of step s + 1
+            compute(s & 1);
+            commit(Ln, s + 1, (s + 1) & 1);
+            issue(Ln, s + 1 + PF);
+            lds_barrier();
+        };
+        const int Sf = S - S % PF;
+        for (int s0 = 0; s0 < Sf; s0 += PF) {
 #pragma unroll
-            for (int j = 0; j < kFPf; ++j) {
-                const int s = s0 + j;
-                if (s < S) {
-                    compute(s & 1);
-                    const int sn = s + 1;
-                    if (sn < S) {
-                        commit(L[(j + 1) % kFPf], sn, sn & 1);
-                        if (sn + kFPf < S) issue(L[(j + 1) % kFPf], sn + kFPf);
-                    }
-                    lds_barrier();
-                }
-            }
+            for (int j = 0; j < PF; ++j) step(L[(j + 1) % PF], s0 + j);
         }
+#pragma unroll
+        for (int j = 0; j < PF - 1; ++j)
+            if (Sf + j < S) step(L[(j + 1) % PF], Sf + j);
 
         // ---- epilogue: lane (lr, lg) of tile (i, j) holds columns 4 lg .. 4 lg + 3 of row lr
 #pragma unroll
@@ -249,18 +273,177 @@ __global__ __launch_bounds__(kFThreads) void fgemm_kernel(const FGemmParams p) {
                 const int r = m0 + 64 * wm + 16 * j + lr;
                 if (r < M && n < p.N) {
                     f32x4 v;
-                    if constexpr (PAIR) {
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) v[q] = silu(acc[0][i][j][q]) * acc[1][i][j][q];
-                    } else {
-                        v = acc[0][i][j];
-                    }
+                    for (int q = 0; q < 4; ++q) v[q] = silu(acc[0][i][j][q]) * acc[1][i][j][q];
                     *(f32x4 *)(p.out + (size_t)(row0 + r) * p.N + n) = v;
                 }
             }
         }
     }
 }
+
+// ------------------------------------------------------------------ down
+
+constexpr int kDBK = 128;                  // K values per step (4 MX blocks)
+constexpr int kDRow = kDBK * 2;            // LDS bytes per activation row per step (bf16)
+constexpr int kDNF = 4;                    // 16-column MFMA tiles per wave
+constexpr int kDBN = 4 * 16 * kDNF;        // output columns per tile (256)
+
+// 16-byte chunk c (of 16) of LDS row r sits at position c ^ (r & 15): an operand read (16
+// rows at one chunk) touches all 16 bank groups of a 256-byte row once.
+MOE_DEV int dswz(int r) { return r & 15; }
+
+struct DActs {                     // one thread's activation loads for one K-step
+    u32x4 v[8];                    // 32 float32 values
+};
+struct DWts {                      // one lane's weight units for one K-step
+    u32x4 c[kDNF];                 // 32 codes each (one MX block)
+    uint32_t s[kDNF];              // their scale bytes
+};
+
+template <bool ROUTED>
+__global__ __launch_bounds__(kFThreads) void fgemm_down_kernel(const FGemmParams p) {
+    constexpr int PF = MOE_FGEMM_DOWN_PF;
+    constexpr int kAPlane = kFBM * kDRow;              // one activation plane's step
+    constexpr int kStage = 2 * kAPlane;                // hi and lo planes
+    static_assert(PF >= 1 && PF <= 4, "prefetch depth");
+    static_assert(kFBM * 4 == kFThreads, "activation staging: four threads per row");
+    __shared__ __align__(16) unsigned char smem[2 * kStage];
+    __shared__ int s_tp[ROUTED ? MOE_MAX_EXPERTS : 1];
+    __shared__ int s_wave[kFThreads / 64];
+
+    const int NT = (p.N + kDBN - 1) / kDBN;
+    const int total_mt = ROUTED ? build_tile_prefix<kFThreads, kFBM>(p.offsets, p.E, p.R, s_tp, s_wave)
+                                : (p.T + kFBM - 1) / kFBM;
+    const int items = total_mt * NT;
+    const int G = gridDim.x;
+    const int slot = xcd_slot(blockIdx.x, G);
+    const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
+    const int wm = wave >> 2, wn = wave & 3;            // 64 rows x 64 columns of this wave
+    const int lr = lane & 15, lg = lane >> 4;          // MFMA operand row / MX block of the step
+    const int Kh = p.K / 2, Kb = p.K / 32;
+    const int S = (p.K + kDBK - 1) / kDBK;             // K-steps (the last may hold 1..4 blocks)
+    const int ar = tid >> 2, ac = tid & 3;             // staging: row ar, values 32 ac .. 32 ac + 31
+
+    for (int item = slot; item < items; item += G) {
+        int e, row0, M, tile, nt;
+        fgemm_item<ROUTED>(p, s_tp, total_mt, NT, item, e, row0, M, tile, nt);
+        const int m0 = tile * kFBM, n0 = nt * kDBN;
+        const uint8_t *wsrc[kDNF];
+        const uint8_t *ssrc[kDNF];
+#pragma unroll
+        for (int i = 0; i < kDNF; ++i) {
+            const size_t row = (size_t)e * p.N + min(n0 + 16 * (kDNF * wn + i) + lr, p.N - 1);  // past N: not stored
+            wsrc[i] = p.w[0] + row * Kh;
+            ssrc[i] = p.ws[0] + row * Kb;
+        }
+        const unsigned char *asrc = fgemm_arow<true>(p, row0, M, m0, ar);
+
+        auto issue_w = [&](DWts &W, int s) {
+            const int kb = min(4 * s + lg, Kb - 1);
+#pragma unroll
+            for (int i = 0; i < kDNF; ++i) {
+                W.c[i] = *(const u32x4 *)(wsrc[i] + (size_t)kb * 16);
+                W.s[i] = ssrc[i][kb];
+            }
+        };
+        auto issue_a = [&](DActs &A, int s) {
+            const int kc = min(s * kDBK + 32 * ac, p.K - 32);   // K % 32 == 0
+            const u32x4 *q = (const u32x4 *)(asrc + (size_t)kc * 4);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) A.v[i] = q[i];
+        };
+        auto commit = [&](const DActs &A, int s, int buf) {
+            unsigned char *row = smem + buf * kStage + ar * kDRow;
+            const bool live = 32 * ac < p.K - s * kDBK;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                u32x4 h4, l4;
+                split8(A.v[2 * i], A.v[2 * i + 1], h4, l4);
+                const int off = ((4 * ac + i) ^ dswz(ar)) << 4;
+                *(u32x4 *)(row + off) = live ? h4 : u32x4{0, 0, 0, 0};
+                *(u32x4 *)(row + kAPlane + off) = live ? l4 : u32x4{0, 0, 0, 0};
+            }
+        };
+
+        f32x4 acc[kDNF][4];
+#pragma unroll
+        for (int i = 0; i < kDNF; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+        auto compute = [&](const DWts &W, int s, int buf) {
+            const unsigned char *st = smem + buf * kStage;
+            const bool wlive = 4 * s + lg < Kb;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                bf16x8 xa[2][4];
+#pragma unroll
+                for (int pl = 0; pl < 2; ++pl)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int r = 64 * wm + 16 * j + lr;
+                        xa[pl][j] = *(const bf16x8 *)(st + pl * kAPlane + r * kDRow + (((4 * lg + q) ^ dswz(r)) << 4));
+                    }
+#pragma unroll
+                for (int i = 0; i < kDNF; ++i) {
+                    const uint32_t c = wlive ? W.c[i][q] : 0u;
+                    const float sc = e8m0_to_f32(wlive ? W.s[i] : 127u);
+                    const bf16x8 b = pack8(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 0),
+                                           __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 1),
+                                           __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 2),
+                                           __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 3));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+#pragma unroll
+                        for (int pl = 0; pl < 2; ++pl)
+                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, xa[pl][j], acc[i][j], 0, 0, 0);
+                }
+            }
+        };
+
+        // ---- pipeline: weight slot s % PF holds step s's units from their issue until
+        // compute(s); the activation slot holds step s + 1's rows until commit(s + 1).  Loads
+        // and commits are unconditional, as in the gate/up kernel; the last S % PF steps run
+        // under a guard after the loop.
+        DWts WL[PF];
+        DActs A;
+#pragma unroll
+        for (int j = 0; j < PF; ++j) issue_w(WL[j], j);
+        issue_a(A, 0);
+        commit(A, 0, 0);
+        issue_a(A, 1);
+        lds_barrier();
+        auto step = [&](DWts &W, int s) {
+            compute(W, s, s & 1);
+            issue_w(W, s + PF);
+            commit(A, s + 1, (s + 1) & 1);
+            issue_a(A, s + 2);
+            lds_barrier();
+        };
+        const int Sf = S - S % PF;
+        for (int s0 = 0; s0 < Sf; s0 += PF) {
+#pragma unroll
+            for (int j = 0; j < PF; ++j) step(WL[j], s0 + j);
+        }
+#pragma unroll
+        for (int j = 0; j < PF - 1; ++j)
+            if (Sf + j < S) step(WL[j], Sf + j);
+
+        // ---- epilogue: lane (lr, lg) of tile (i, j) holds columns 4 lg .. 4 lg + 3 of row lr
+#pragma unroll
+        for (int i = 0; i < kDNF; ++i) {
+            const int n = n0 + 16 * (kDNF * wn + i) + 4 * lg;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = m0 + 64 * wm + 16 * j + lr;
+                if (r < M && n < p.N) *(f32x4 *)(p.out + (size_t)(row0 + r) * p.N + n) = acc[i][j];
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------------ host
 
 // The bf16 matrix-core GEMM serves unquantised activations over MXFP4 weights when there
 // are enough tokens to fill 128-row tiles at least partly (prefill); decode sizes use the GEMV.
@@ -269,7 +452,8 @@ bool fgemm_wanted(const moe_expert_weights *w, int act, int T) {
            w->d_model % 32 == 0;
 }
 
-template <bool PAIR, bool SPLIT, bool ROUTED>
+// Workgroups of kernel KER resident at once on the current device (queried once per device).
+template <auto KER>
 static int fgemm_resident() {
     constexpr int kMaxDev = 64;
     static int cache[kMaxDev] = {};
@@ -278,24 +462,22 @@ static int fgemm_resident() {
     if (cache[dev] == 0) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fgemm_kernel<PAIR, SPLIT, ROUTED>, kFThreads, 0) !=
-                hipSuccess ||
-            per_cu <= 0)
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, KER, kFThreads, 0) != hipSuccess || per_cu <= 0)
             per_cu = 1;
         cache[dev] = cus * per_cu;
     }
     return cache[dev];
 }
 
-// Persistent launch: at most one wave of resident workgroups.  `mt_bound` bounds the row
-// tiles (sum over experts of ceil(M_e / 128) <= experts with rows + R / 128).
-template <bool PAIR, bool SPLIT, bool ROUTED>
-static moe_status fgemm_run(const FGemmParams &p, hipStream_t stream, const char *what) {
+// Persistent launch: at most one wave of resident workgroups.  The row tiles are bounded by
+// (experts with rows) + R / 128 >= sum over experts of ceil(M_e / 128).
+template <auto KER, bool ROUTED>
+static moe_status fgemm_run(const FGemmParams &p, int BN, hipStream_t stream, const char *what) {
     const int64_t mt_bound = ROUTED ? (int64_t)std::min(p.E, p.R) + p.R / kFBM : (p.T + kFBM - 1) / kFBM;
-    const int64_t items = mt_bound * ((p.N + kFBN - 1) / kFBN);
-    const int64_t g = std::min<int64_t>(items, fgemm_resident<PAIR, SPLIT, ROUTED>());
+    const int64_t items = mt_bound * ((p.N + BN - 1) / BN);
+    const int64_t g = std::min<int64_t>(items, fgemm_resident<KER>());
     if (g <= 0) return MOE_OK;
-    hipLaunchKernelGGL((fgemm_kernel<PAIR, SPLIT, ROUTED>), dim3((unsigned)g), dim3(kFThreads), 0, stream, p);
+    hipLaunchKernelGGL(KER, dim3((unsigned)g), dim3(kFThreads), 0, stream, p);
     return launch_check(what);
 }
 
@@ -321,8 +503,10 @@ moe_status fgemm_gateup_launch(const moe_expert_weights *w, int T, int k, const 
     p.out = h;
     const char *what = "moe_expert_gateup (bf16 GEMM)";
     if (offsets)
-        return x_f32 ? fgemm_run<true, true, true>(p, stream, what) : fgemm_run<true, false, true>(p, stream, what);
-    return x_f32 ? fgemm_run<true, true, false>(p, stream, what) : fgemm_run<true, false, false>(p, stream, what);
+        return x_f32 ? fgemm_run<fgemm_pair_kernel<true, true>, true>(p, kPBN, stream, what)
+                     : fgemm_run<fgemm_pair_kernel<false, true>, true>(p, kPBN, stream, what);
+    return x_f32 ? fgemm_run<fgemm_pair_kernel<true, false>, false>(p, kPBN, stream, what)
+                 : fgemm_run<fgemm_pair_kernel<false, false>, false>(p, kPBN, stream, what);
 }
 
 moe_status fgemm_down_launch(const moe_expert_weights *w, const float *h, const int32_t *offsets, int R, float *y,
@@ -342,7 +526,8 @@ moe_status fgemm_down_launch(const moe_expert_weights *w, const float *h, const 
     p.R = R;
     p.out = y;
     const char *what = "moe_expert_down (bf16 GEMM)";
-    return offsets ? fgemm_run<false, true, true>(p, stream, what) : fgemm_run<false, true, false>(p, stream, what);
+    return offsets ? fgemm_run<fgemm_down_kernel<true>, true>(p, kDBN, stream, what)
+                   : fgemm_run<fgemm_down_kernel<false>, false>(p, kDBN, stream, what);
 }
 
 }  // namespace moe
