@@ -92,17 +92,20 @@ MOE_DEV const unsigned char *fgemm_arow(const FGemmParams &p, int row0, int M, i
     return (const unsigned char *)p.a + (size_t)src * p.K * (SPLIT ? 4 : 2);
 }
 
-// 8 float32 values -> bf16 hi and lo terms, 16 bytes each.
+// 8 float32 values -> bf16 hi and lo terms, 16 bytes each.  The conversions are the
+// hardware's round-to-nearest-even (v_cvt_pk_bf16_f32, two values per instruction); v - hi
+// is exact in float32.
 MOE_DEV void split8(const u32x4 a, const u32x4 b, u32x4 &h4, u32x4 &l4) {
-    uint32_t hb[8], lb[8];
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const float f = __uint_as_float(t < 4 ? a[t] : b[t - 4]);
-        hb[t] = bf16_rne_bits(f);
-        lb[t] = bf16_rne_bits(f - __uint_as_float(hb[t] << 16));
+    for (int t = 0; t < 4; ++t) {
+        const float f0 = __uint_as_float(t < 2 ? a[2 * t] : b[2 * t - 4]);
+        const float f1 = __uint_as_float(t < 2 ? a[2 * t + 1] : b[2 * t - 3]);
+        const bf16x2 hv = {(__bf16)f0, (__bf16)f1};
+        const uint32_t hb = __builtin_bit_cast(uint32_t, hv);
+        const bf16x2 lv = {(__bf16)(f0 - __uint_as_float(hb << 16)), (__bf16)(f1 - __uint_as_float(hb & 0xffff0000u))};
+        h4[t] = hb;
+        l4[t] = __builtin_bit_cast(uint32_t, lv);
     }
-    h4 = u32x4{hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, hb[4] | hb[5] << 16, hb[6] | hb[7] << 16};
-    l4 = u32x4{lb[0] | lb[1] << 16, lb[2] | lb[3] << 16, lb[4] | lb[5] << 16, lb[6] | lb[7] << 16};
 }
 
 // ------------------------------------------------------------------ gate/up
