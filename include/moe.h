@@ -170,6 +170,11 @@ typedef struct {
  * Identity form (expert_offsets == NULL, num_experts must be 1): row t reads token t;
  *   y_rows is [T][d_model].  This is the shared expert.
  * x: [T][d_model], x_dtype MOE_DT_BF16 or MOE_DT_F32.
+ * act == MOE_ACT_FLOAT: weights are decoded exactly (an E2M1 code times its E8M0 scale is
+ *   a bf16 value); x and h are used as given.  With MXFP4 weights and T >= 64 the products
+ *   run on the bf16 matrix cores, a float32 operand (h, or float32 x) as the two bf16 terms
+ *   hi = RN(v), lo = RN(v - hi), together within 2^-17 |v|; otherwise, and for FP8 weights,
+ *   on the vector ALU in float32.
  * act == MOE_ACT_MXFP4: x and h are MX-quantised (OCP MX v1.0: scale 2^(floor(log2 amax)-2),
  *   round to nearest even, saturate at 6) and the products use the block-scaled FP4
  *   matrix instructions; MXFP4 weights only (else MOE_ERR_UNSUPPORTED).
