@@ -18,9 +18,10 @@
 // tile) items expert by expert, in the same XCD-aware order as the FP4 grouped GEMM.
 //
 // gate/up (fgemm_pair_kernel): 128 columns of gate AND up at the same columns, so
-// h = silu(g) * u is formed in registers.  K-steps of 64 values; each weight unit (32 codes
-// and a scale) of the step is decoded once, by one thread, into the LDS stage next to the
-// activations: the two row-waves that share a column then read it instead of decoding it twice.
+// h = silu(g) * u is formed in registers.  K-steps of 64 values; the step's weight units
+// (16 code bytes each) and their scales are staged in LDS next to the activations, and each
+// wave decodes the 8 codes of its lane slot right before the MFMAs: LDS carries the codes,
+// a quarter of the bytes of decoded bf16 weights.
 // down (fgemm_down_kernel): 256 columns of one matrix, K-steps of 128 values (4 MX blocks).
 // Weights never pass through LDS: for each of its four 16-column tiles a lane loads the
 // 16-byte unit of row l%16, block l/16 of the step, and decodes it right before its MFMAs
@@ -117,6 +118,9 @@ constexpr int kPBN = 128;                  // output columns per tile and matrix
 // 16-byte chunk c (of 8) of LDS row r sits at position c ^ pswz(r): an operand read (16 rows
 // at one chunk) then touches 16 distinct 16-byte bank groups.
 MOE_DEV int pswz(int r) { return (r >> 1) & 7; }
+// Weight codes: row R's 16-byte unit u (of 2) at position u ^ ((R >> 3) & 1), so that rows
+// R and R + 8 of an operand read (the same banks otherwise) use different halves.
+MOE_DEV int cswz(int R, int u) { return u ^ ((R >> 3) & 1); }
 
 template <bool SPLIT>
 struct PStep {                     // one thread's loads for one K-step
@@ -129,9 +133,11 @@ template <bool SPLIT, bool ROUTED>
 __global__ __launch_bounds__(kFThreads) void fgemm_pair_kernel(const FGemmParams p) {
     constexpr int PF = MOE_FGEMM_PAIR_PF;
     constexpr int NP = SPLIT ? 2 : 1;                  // activation planes: hi (and lo)
-    constexpr int kWPlane = kPBN * kPRow;              // one matrix's decoded step
+    constexpr int kCodes = 2 * kPBN * 32;              // codes of a step: 256 weight rows x 2 units
+    constexpr int kScales = 2 * kPBN * 2 * 4;          // their scales, as float32
     constexpr int kAPlane = kFBM * kPRow;              // one activation plane's step
-    constexpr int kStage = 2 * kWPlane + NP * kAPlane;
+    constexpr int kAOff = kCodes + kScales;            // activation planes after codes and scales
+    constexpr int kStage = kAOff + NP * kAPlane;
     static_assert(PF >= 1 && PF <= 4, "prefetch depth");
     static_assert(2 * kPBN * 2 == kFThreads && kFBM * 4 == kFThreads, "thread roles");
     __shared__ __align__(16) unsigned char smem[2 * kStage];
@@ -174,17 +180,14 @@ __global__ __launch_bounds__(kFThreads) void fgemm_pair_kernel(const FGemmParams
             unsigned char *st = smem + buf * kStage;
             const int kv = p.K - s * kPBK;                     // valid values of the step
             {
-                bf16x8 v[4];
-                unit_to_bf16x8(L.wc, e8m0_to_f32(L.wsc), v);
+                // a unit past K: zero codes under scale 1 (the scale byte may be any value)
                 const bool live = wb * 32 < kv;
-                unsigned char *row = st + wmat * kWPlane + wr * kPRow;
-#pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *(u32x4 *)(row + (((4 * wb + q) ^ pswz(wr)) << 4)) =
-                        live ? __builtin_bit_cast(u32x4, v[q]) : u32x4{0, 0, 0, 0};
+                const int R = wmat * kPBN + wr;
+                *(u32x4 *)(st + R * 32 + (cswz(R, wb) << 4)) = live ? L.wc : u32x4{0, 0, 0, 0};
+                *(float *)(st + kCodes + (R * 2 + wb) * 4) = live ? e8m0_to_f32(L.wsc) : 1.0f;
             }
             const bool live = 16 * ac < kv;
-            unsigned char *row = st + 2 * kWPlane + ar * kPRow;
+            unsigned char *row = st + kAOff + ar * kPRow;
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
                 const int off = ((2 * ac + i) ^ pswz(ar)) << 4;
@@ -217,15 +220,21 @@ __global__ __launch_bounds__(kFThreads) void fgemm_pair_kernel(const FGemmParams
                 for (int m = 0; m < 2; ++m)
 #pragma unroll
                     for (int i = 0; i < 2; ++i) {
-                        const int r = 32 * wn + 16 * i + lr;
-                        bw[m][i] = *(const bf16x8 *)(st + m * kWPlane + r * kPRow + ((c ^ pswz(r)) << 4));
+                        // codes 8 lg .. 8 lg + 7 of unit ks of weight row R, and its scale
+                        const int R = m * kPBN + 32 * wn + 16 * i + lr;
+                        const uint32_t cw = *(const uint32_t *)(st + R * 32 + (cswz(R, ks) << 4) + 4 * lg);
+                        const float sc = *(const float *)(st + kCodes + (R * 2 + ks) * 4);
+                        bw[m][i] = pack8(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 0),
+                                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 1),
+                                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 2),
+                                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 3));
                     }
 #pragma unroll
                 for (int pl = 0; pl < NP; ++pl)
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         const int r = 64 * wm + 16 * j + lr;
-                        xa[pl][j] = *(const bf16x8 *)(st + 2 * kWPlane + pl * kAPlane + r * kPRow +
+                        xa[pl][j] = *(const bf16x8 *)(st + kAOff + pl * kAPlane + r * kPRow +
                                                       ((c ^ pswz(r)) << 4));
                     }
 #pragma unroll

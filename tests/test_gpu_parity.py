@@ -273,6 +273,25 @@ def test_expert_ffn_float_matches_oracle(dev, M, name, xdt):
     assert_close(to_np(y), ref, f"{name}/{xdt} y_rows")
 
 
+@pytest.mark.parametrize("xdt", ["bf16", "f32"])
+def test_expert_ffn_identity_form_prefill_float(dev, M, xdt):
+    """The shared expert's form (NULL offsets, one expert) at a prefill size: the bf16
+    matrix-core GEMM without the permutation, with a ragged row tile and K tail."""
+    cfg = tiny(name="fid", wtag=99, T=130, H=544, I=416, E=4, k=2, shared="ungated", shared_K=544, shared_I=416)
+    t, inp = build(cfg, dev)
+    x = OF.bf16_value(inp.x)
+    if xdt == "f32":
+        x = (x * (1.0 + 2.0 ** -12)).astype(np.float32).astype(np.float64)
+        xg = torch.from_numpy(x.astype(np.float32)).to(dev)
+    else:
+        xg = t["x"]
+    w = layer_weights(cfg, t)
+    y = M.moe_expert_ffn(w.shared, xg, "float", 1, None, None)
+    _, gs = host_expert_getter(cfg)
+    ref = OL.ffn(x, *OL.dequant_expert(gs()))
+    assert_close(to_np(y), ref, f"identity form/{xdt} y")
+
+
 def test_dense_bf16_matches_oracle(dev, M):
     rng = np.random.default_rng(11)
     T, n, kd = 5, 200, 448
