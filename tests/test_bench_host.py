@@ -1,0 +1,60 @@
+"""Host-side checks of bench.py's accounting: the algorithmic bytes and flops that the
+roofline fractions divide by, and the kernel patterns that select the dominant kernel in
+rocprofv3 output.  The expected figures are worked by hand from the layer shapes."""
+import re
+
+import bench
+import synth
+
+
+def test_decode_gateup_bytes_and_flops():
+    cfg = synth.get("qwen38max_decode")              # T=1, K=H=7168, I=2368, k=10, gated shared
+    a = bench.algorithmic(cfg, 10, fused=True)
+    row = 7168 * 17 // 32                             # one MXFP4 weight row: codes + scales = 3808 B
+    assert row == 3808
+    routed = 10 * 2 * 2368 * row                      # ten experts' gate and up
+    shared = 2 * 2368 * row                           # the shared expert's gate and up (same launch)
+    x_in, h_out, hs_out = 7168 * 2, 10 * 2368 * 4, 2368 * 4
+    assert a["gu_bytes"] == routed + shared + x_in + h_out + hs_out == 198_500_096
+    assert a["gu_flops"] == 2 * 10 * 2 * 7168 * 2368 + 2 * 1 * 2 * 7168 * 2368
+
+
+def test_float_prefill_gateup_bytes_and_flops():
+    cfg = synth.get("qwen38max_prefill_hot_float")   # T=512, ten hot experts, bf16 x, float32 h
+    a = bench.algorithmic(cfg, 10, fused=False)
+    routed = 10 * 2 * 2368 * 3808
+    x_in, h_out = 512 * 7168 * 2, 512 * 10 * 2368 * 4
+    assert a["gu_bytes"] == routed + x_in + h_out == 236_183_552
+    assert a["gu_flops"] == 2 * 5120 * 2 * 7168 * 2368 == 347_623_915_520
+
+
+def test_mx_prefill_gateup_bytes():
+    cfg = synth.get("qwen38max_prefill_hot")         # MX activations: x and h as MXFP4 (17/32 B per value)
+    a = bench.algorithmic(cfg, 10, fused=False)
+    assert a["gu_bytes"] == 10 * 2 * 2368 * 3808 + 512 * 7168 * 17 // 32 + 5120 * 2368 * 17 // 32
+
+
+def test_dominant_kernel_patterns_select_one_instantiation():
+    names = {
+        "qwen38max_decode": ("void moe::gemv_kernel<0, 0, 1, true, true>(moe::GemvParams)",
+                             "void moe::gemv_kernel<0, 0, 1, true, false>(moe::GemvParams)"),
+        "qwen38max_prefill_hot": ("void moe::mxgemm_kernel<true, true>(moe::GemmParams)",
+                                  "void moe::mxgemm_kernel<true, false>(moe::GemmParams)"),
+        "qwen38max_prefill_hot_float": ("void moe::fgemm_pair_kernel<false, true>(moe::FGemmParams)",
+                                        "void moe::fgemm_pair_kernel<false, false>(moe::FGemmParams)"),
+    }
+    for wl, (routed, shared) in names.items():
+        pat = re.compile(bench.dominant_kernel(synth.get(wl)))
+        assert pat.search(routed), wl
+        assert not pat.search(shared), wl
+
+
+def test_more_than_one_gpu_is_refused_before_any_device_work():
+    import os
+    import subprocess
+    import sys
+    here = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(here, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=300, cwd=here)
+    assert r.returncode != 0
+    assert "one GPU only" in (r.stdout + r.stderr)
