@@ -304,6 +304,14 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
                 for (int j = 0; j < kTN; ++j)
 #pragma unroll
                     for (int v = 0; v < 16; ++v) acc[mi][i][j][v] = 0.0f;
+        // 32-row MFMA tiles of this wave that hold no row of the expert are skipped: their
+        // outputs are never stored.  An expert with at most 64 rows in a tile (most of them
+        // under skewed routing) then costs half the matrix work; the waves of rows 0-63 and
+        // 64-127 share each SIMD, so the remaining work stays spread over all four.
+        bool tlive[kTM];
+#pragma unroll
+        for (int i = 0; i < kTM; ++i)
+            tlive[i] = __builtin_amdgcn_readfirstlane(32 * (kTM * wm + i) < M - m0 ? 1 : 0) != 0;
         auto mma = [&](const Quarter &f) {
 #pragma unroll
             for (int mi = 0; mi < NM; ++mi)
@@ -311,6 +319,7 @@ __global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
                 for (int j = 0; j < kTN; ++j)
 #pragma unroll
                     for (int i = 0; i < kTM; ++i) {
+                        if (!tlive[i]) continue;
                         const u32x4 av = f.a[i], bv = f.b[mi][j];
                         acc[mi][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                             i32x8_t{(int)av[0], (int)av[1], (int)av[2], (int)av[3], 0, 0, 0, 0},
