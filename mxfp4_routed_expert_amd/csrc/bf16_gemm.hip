@@ -14,7 +14,8 @@
 // accumulators are four consecutive columns of one row: one 16-byte store.  The activation
 // rows of a K-step, shared by all 8 waves, are staged in LDS, double-buffered: while the
 // matrix cores work on step s, step s+1 (loaded into registers earlier) is written to the
-// other buffer; one barrier per step.  The grid is persistent and walks (row tile, column
+// other buffer; one barrier per step.  A wave skips the MFMAs of its 16-row tiles that start
+// past the expert's last row (their outputs are never stored).  The grid is persistent and walks (row tile, column
 // tile) items expert by expert, in the same XCD-aware order as the FP4 grouped GEMM.
 //
 // gate/up (fgemm_pair_kernel): 128 columns of gate AND up at the same columns, so
@@ -28,6 +29,7 @@
 // (MFMA q takes values 8q .. 8q+7 of every lane group's block); with float32 h each decoded
 // weight feeds twice as many products (hi and lo), which pays for decoding it per wave.
 #include <algorithm>
+#include <type_traits>
 
 #include "gemv.h"
 #include "tile_sched.h"
@@ -36,6 +38,9 @@ namespace moe {
 
 #ifndef MOE_USE_BF16_GEMM
 #define MOE_USE_BF16_GEMM 1                // 0: prefill with unquantised activations on the GEMV
+#endif
+#ifndef MOE_FGEMM_SKIP_DEAD
+#define MOE_FGEMM_SKIP_DEAD 1              // 0: compute 16-row tiles past an expert's last row too
 #endif
 #ifndef MOE_FGEMM_PAIR_PF
 #define MOE_FGEMM_PAIR_PF 2                // gate/up: steps whose loads are in flight
@@ -209,8 +214,13 @@ __global__ __launch_bounds__(kFThreads) void fgemm_pair_kernel(const FGemmParams
             for (int i = 0; i < 2; ++i)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[m][i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int live_rows = M - m0;
+        bool tlive[4];                                     // 16-row tiles holding a row of the expert
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tlive[j] = __builtin_amdgcn_readfirstlane(16 * (4 * wm + j) < live_rows) != 0;
 
-        auto compute = [&](int buf) {
+        // all: every 16-row tile of the wave holds rows (no per-tile test in the loop)
+        auto compute = [&](int buf, auto all) {
             const unsigned char *st = smem + buf * kStage;
 #pragma unroll
             for (int ks = 0; ks < kPBK / 32; ++ks) {
@@ -245,7 +255,8 @@ __global__ __launch_bounds__(kFThreads) void fgemm_pair_kernel(const FGemmParams
                         for (int j = 0; j < 4; ++j)
 #pragma unroll
                             for (int pl = 0; pl < NP; ++pl)
-                                acc[m][i][j] =
+                                if (decltype(all)::value || tlive[j])
+                                    acc[m][i][j] =
                                     __builtin_amdgcn_mfma_f32_16x16x32_bf16(bw[m][i], xa[pl][j], acc[m][i][j], 0, 0, 0);
             }
         };
@@ -261,20 +272,26 @@ __global__ __launch_bounds__(kFThreads) void fgemm_pair_kernel(const FGemmParams
         commit(L[0], 0, 0);
         issue(L[0], PF);
         lds_barrier();
-        auto step = [&](PStep<SPLIT> &Ln, int s) {         // Ln: the slot of step s + 1
-            compute(s & 1);
+        auto step = [&](PStep<SPLIT> &Ln, int s, auto all) {   // Ln: the slot of step s + 1
+            compute(s & 1, all);
             commit(Ln, s + 1, (s + 1) & 1);
             issue(Ln, s + 1 + PF);
             lds_barrier();
         };
         const int Sf = S - S % PF;
-        for (int s0 = 0; s0 < Sf; s0 += PF) {
+        auto run = [&](auto all) {
+            for (int s0 = 0; s0 < Sf; s0 += PF) {
 #pragma unroll
-            for (int j = 0; j < PF; ++j) step(L[(j + 1) % PF], s0 + j);
-        }
+                for (int j = 0; j < PF; ++j) step(L[(j + 1) % PF], s0 + j, all);
+            }
 #pragma unroll
-        for (int j = 0; j < PF - 1; ++j)
-            if (Sf + j < S) step(L[(j + 1) % PF], Sf + j);
+            for (int j = 0; j < PF - 1; ++j)
+                if (Sf + j < S) step(L[(j + 1) % PF], Sf + j, all);
+        };
+        // one test per item: full tiles run the loop without per-tile tests (float32 x always:
+        // a second copy of its loop does not fit in the registers)
+        if (SPLIT || !MOE_FGEMM_SKIP_DEAD || tlive[3]) run(std::true_type{});
+        else run(std::false_type{});
 
         // ---- epilogue: lane (lr, lg) of tile (i, j) holds columns 4 lg .. 4 lg + 3 of row lr
 #pragma unroll
@@ -383,8 +400,13 @@ __global__ __launch_bounds__(kFThreads) void fgemm_down_kernel(const FGemmParams
         for (int i = 0; i < kDNF; ++i)
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int live_rows = M - m0;
+        bool tlive[4];                                     // 16-row tiles holding a row of the expert
+#pragma unroll
+        for (int j = 0; j < 4; ++j) tlive[j] = __builtin_amdgcn_readfirstlane(16 * (4 * wm + j) < live_rows) != 0;
 
-        auto compute = [&](const DWts &W, int s, int buf) {
+        // all: every 16-row tile of the wave holds rows (no per-tile test in the loop)
+        auto compute = [&](const DWts &W, int s, int buf, auto all) {
             const unsigned char *st = smem + buf * kStage;
             const bool wlive = 4 * s + lg < Kb;
 #pragma unroll
@@ -409,7 +431,8 @@ __global__ __launch_bounds__(kFThreads) void fgemm_down_kernel(const FGemmParams
                     for (int j = 0; j < 4; ++j)
 #pragma unroll
                         for (int pl = 0; pl < 2; ++pl)
-                            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, xa[pl][j], acc[i][j], 0, 0, 0);
+                            if (decltype(all)::value || tlive[j])
+                                acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(b, xa[pl][j], acc[i][j], 0, 0, 0);
                 }
             }
         };
@@ -426,21 +449,26 @@ __global__ __launch_bounds__(kFThreads) void fgemm_down_kernel(const FGemmParams
         commit(A, 0, 0);
         issue_a(A, 1);
         lds_barrier();
-        auto step = [&](DWts &W, int s) {
-            compute(W, s, s & 1);
+        auto step = [&](DWts &W, int s, auto all) {
+            compute(W, s, s & 1, all);
             issue_w(W, s + PF);
             commit(A, s + 1, (s + 1) & 1);
             issue_a(A, s + 2);
             lds_barrier();
         };
         const int Sf = S - S % PF;
-        for (int s0 = 0; s0 < Sf; s0 += PF) {
+        auto run = [&](auto all) {
+            for (int s0 = 0; s0 < Sf; s0 += PF) {
 #pragma unroll
-            for (int j = 0; j < PF; ++j) step(WL[j], s0 + j);
-        }
+                for (int j = 0; j < PF; ++j) step(WL[j], s0 + j, all);
+            }
 #pragma unroll
-        for (int j = 0; j < PF - 1; ++j)
-            if (Sf + j < S) step(WL[j], Sf + j);
+            for (int j = 0; j < PF - 1; ++j)
+                if (Sf + j < S) step(WL[j], Sf + j, all);
+        };
+        // one test per item: full tiles run the loop without per-tile tests
+        if (!MOE_FGEMM_SKIP_DEAD || tlive[3]) run(std::true_type{});
+        else run(std::false_type{});
 
         // ---- epilogue: lane (lr, lg) of tile (i, j) holds columns 4 lg .. 4 lg + 3 of row lr
 #pragma unroll

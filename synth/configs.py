@@ -94,6 +94,11 @@ _add(LayerConfig(name="qwen38max_prefill_hot", tag=4, wtag=1, T=512, H=7168, I=2
                  act="mxfp4", shared="gated", shared_K=7168, shared_I=2368,
                  router_std=7168 ** -0.5, logit_bias="hot10",
                  notes="as the prefill, with a +100 logit bias on 10 fixed experts (512 tokens per expert)"))
+# The Zipf prefill with unquantised bf16 activations (weight-only quantisation).
+_add(LayerConfig(name="qwen38max_prefill_float", tag=3, wtag=1, T=512, H=7168, I=2368, E=512, k=10,
+                 act="float", shared="gated", shared_K=7168, shared_I=2368,
+                 router_std=7168 ** -0.5, logit_bias="zipf1.1",
+                 notes="as the prefill, with bf16 activations and float32 h (MXFP4 weights only)"))
 # The hot prefill with unquantised bf16 activations (weight-only quantisation): the same
 # tokens, routing and experts, the products on the bf16 matrix cores.
 _add(LayerConfig(name="qwen38max_prefill_hot_float", tag=4, wtag=1, T=512, H=7168, I=2368, E=512, k=10,

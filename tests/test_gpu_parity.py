@@ -587,16 +587,17 @@ def test_prefill_mx_full_size_stagewise_sampled(dev, M):
     _stagewise_mx(M, cfg, dev, tokens=[3, 300])
 
 
-def test_prefill_float_full_size_sampled_tokens(dev, M):
-    cfg = synth.get("qwen38max_prefill_hot_float")
-    say("building qwen38max_prefill_hot_float")
+@pytest.mark.parametrize("name,sample", [("qwen38max_prefill_hot_float", [0, 129, 511]),
+                                         ("qwen38max_prefill_float", [5, 300])])
+def test_prefill_float_full_size_sampled_tokens(dev, M, name, sample):
+    cfg = synth.get(name)
+    say(f"building {name}")
     layer, out, inp = _run_layer(M, cfg, dev)
     r = OL.route(inp.x, inp.w_router, cfg.k, cfg.score, cfg.renormalize, cfg.routed_scaling, inp.logit_bias,
                  None, inp.w_shared_gate)
     np.testing.assert_array_equal(to_np(layer.ids), r.ids)
     ge, gs = host_expert_getter(cfg)
     x = OF.bf16_value(inp.x)
-    sample = [0, 129, 511]
     ref = np.zeros((len(sample), cfg.H))
     for e in np.unique(r.ids[sample]):
         G, U, D = OL.dequant_expert(ge(int(e)))
