@@ -257,7 +257,8 @@ def layer(cfg, inp, get_expert, get_shared=None):
     synth.ExpertSet objects.  LatentMoE (Kimi K3 article, architecture section: routed
     experts compute in a narrower latent width): the router reads the full-width x,
     the routed experts read x_lat = P_d x, their weighted sum z is projected back with
-    P_u, and the full-width shared expert's output is added after that."""
+    P_u, and the full-width shared expert's output, times its gate when it has one, is
+    added after that."""
     x = bf16_value(inp.x)
     r = route(inp.x, inp.w_router, cfg.k, cfg.score, cfg.renormalize, cfg.routed_scaling,
               inp.logit_bias, inp.select_bias, inp.w_shared_gate if cfg.shared == "gated" else None)
@@ -270,7 +271,9 @@ def layer(cfg, inp, get_expert, get_shared=None):
         y_s = ffn(x, G, U, D, cfg.act)
     if cfg.latent:
         z = combine(y_rows, perm.pair_to_row, r.weights, cfg.k)
-        out = dense_bf16(z, inp.p_up) + (y_s if y_s is not None else 0.0)
+        out = dense_bf16(z, inp.p_up)
+        if y_s is not None:
+            out = out + (1.0 if r.shared_gate is None else r.shared_gate[:, None]) * y_s
     else:
         z = combine(y_rows, perm.pair_to_row, r.weights, cfg.k, y_s, r.shared_gate)
         out = z

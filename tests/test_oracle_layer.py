@@ -123,6 +123,37 @@ def test_sigmoid_bias_affects_selection_only():
     np.testing.assert_array_equal(r2.weights, r0.weights)
 
 
+def _golden_fields(name):
+    d = {}
+    for line in open(os.path.join(GOLDEN, name)):
+        line = line.split("#")[0].strip()
+        if line:
+            key, *vals = line.split()
+            d[key] = vals
+    return d
+
+
+def test_sigmoid_without_renorm_hand_case():
+    """Sigmoid scoring, selection bias, no renormalisation, routed_scaling 2.5: the hand-worked
+    case in tests/golden/sigmoid_no_renorm_case.txt.  Dividing by the selected sum, dropping
+    routed_scaling, selecting without the bias or adding the bias to the weights all fail it."""
+    g = _golden_fields("sigmoid_no_renorm_case.txt")
+    logits = [float(v) for v in g["logits"]]
+    E, H = len(logits), 32
+    x = _bf16([[1.0] + [0.0] * (H - 1)])
+    W = np.zeros((E, H))
+    W[:, 0] = logits
+    r = L.route(x, _bf16(W), int(g["k"][0]), score="sigmoid", renormalize=False,
+                routed_scaling=float(g["routed_scaling"][0]), select_bias=np.array(g["beta"], np.float32))
+    assert r.ids[0].tolist() == [int(v) for v in g["ids"]]
+    np.testing.assert_allclose(r.weights[0], [float(v) for v in g["weights"]], rtol=1e-15)
+    # with renormalisation the same selection gets the ratios (the two branches differ)
+    r2 = L.route(x, _bf16(W), 3, score="sigmoid", renormalize=True, routed_scaling=2.5,
+                 select_bias=np.array(g["beta"], np.float32))
+    assert r2.ids[0].tolist() == r.ids[0].tolist()
+    np.testing.assert_allclose(r2.weights[0], 2.5 * r.weights[0] / r.weights[0].sum(), rtol=1e-14)
+
+
 def test_shared_gate_is_sigmoid_of_rounded_logit():
     rng = np.random.default_rng(4)
     x, W = _rand_route_inputs(rng, 3, 64, 8)
@@ -233,8 +264,9 @@ def test_combine_hand_example():
     np.testing.assert_array_equal(out, [[0.25 * 3 + 0.75 * 1 + 5.0, 0.25 * 4 + 0.75 * 2 + 10.0]])
 
 
-def test_latent_identity_projection_equals_plain_layer():
-    plain = _tiny_cfg(k=2, shared="ungated", shared_K=64, shared_I=32)
+@pytest.mark.parametrize("shared", ["ungated", "gated"])
+def test_latent_identity_projection_equals_plain_layer(shared):
+    plain = _tiny_cfg(k=2, shared=shared, shared_K=64, shared_I=32)
     lat = dataclasses.replace(plain, latent=64)
     inp = synth.layer_inputs_np(plain)
     eye = _bf16(np.eye(64))
