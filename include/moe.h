@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
     MOE_OK = 0,
@@ -256,13 +256,29 @@ moe_status moe_dense_bf16(int32_t T, int32_t n, int32_t kdim, const void *x, int
                           const void *w, const float *residual, float *y, moe_stream stream);
 
 /*
- * moe_dequant -- decode a weight matrix [n][kdim] to float32 with the same device
- * decoding the FFN kernels use: MXFP4 value E2M1(code) * 2^(s-127) (NaN for s = 255),
- * FP8 value E4M3(code) * scale[n/128][kdim/128].  codes/scales as in moe_expert_weights
- * for one matrix.  out: float32 [n][kdim].
+ * moe_dequant -- decode a weight matrix [n][kdim] to float32 with the conversions of the
+ * decode GEMV: each code is decoded unscaled (E2M1 and E4M3 values are exact in bf16 and
+ * float32) and multiplied by its scale in float32 -- MXFP4 value E2M1(code) * 2^(s-127)
+ * (NaN for s = 255), FP8 value E4M3(code) * scale[n/128][kdim/128].  (The GEMV applies the
+ * same scale to each block's partial dot product instead of to each weight.)  codes/scales
+ * as in moe_expert_weights for one matrix.  out: float32 [n][kdim].
+ * (Formats: rabbit README, architecture table, "native quantization read" row.)
  */
 moe_status moe_dequant(int32_t format, int32_t n, int32_t kdim, const uint8_t *codes,
                        const void *scales, float *out, moe_stream stream);
+
+/*
+ * moe_dequant_bf16 -- decode an MXFP4 weight matrix [n][kdim] to bf16 with the decoding
+ * every matrix-core kernel multiplies (the down-combine of the fused decode, the bf16
+ * prefill GEMM, MX activation staging): the gfx950 scaled conversion of each 8-code dword
+ * with the block scale 2^(s-127) applied inside the instruction.  E2M1(code) * 2^(s-127) is
+ * a bf16 value for every code and scale byte except where it leaves bf16's range.
+ * codes: uint8 [n][kdim/2], scales: uint8 E8M0 [n][kdim/32], out: bf16 bits [n][kdim];
+ * codes and out 16-byte aligned, kdim a multiple of 32.
+ * (The format: rabbit README, opening section and architecture table, OCP MXFP4.)
+ */
+moe_status moe_dequant_bf16(int32_t n, int32_t kdim, const uint8_t *codes, const uint8_t *scales,
+                            uint16_t *out, moe_stream stream);
 
 /*
  * moe_mx_quantize -- OCP MX conversion of rows [rows][cols] (bf16 or float32, cols a

@@ -78,13 +78,14 @@ _sig("moe_expert_down_combine", _i32, ctypes.POINTER(ExpertWeightsC), ctypes.POI
      _p, _p, _p, _p, _p, _p, _p)
 _sig("moe_combine", _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p)
 _sig("moe_dense_bf16", _i32, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p)
+_sig("moe_dequant_bf16", _i32, _i32, _i32, _p, _p, _p, _p)
 _sig("moe_dequant", _i32, _i32, _i32, _i32, _p, _p, _p, _p)
 _sig("moe_mx_quantize", _i32, _i32, _i32, _p, _i32, _p, _p, _p)
 
 EXPORTS = ["moe_route", "moe_route_workspace", "moe_permute", "moe_permute_workspace", "moe_route_permute",
            "moe_expert_ffn", "moe_expert_gateup_shared", "moe_expert_down_combine",
            "moe_expert_ffn_workspace", "moe_expert_gateup", "moe_expert_gateup_workspace", "moe_expert_down",
-           "moe_combine", "moe_dense_bf16", "moe_dequant", "moe_mx_quantize", "moe_last_error",
+           "moe_combine", "moe_dense_bf16", "moe_dequant", "moe_dequant_bf16", "moe_mx_quantize", "moe_last_error",
            "moe_abi_version"]
 
 
@@ -380,6 +381,17 @@ def moe_dequant(fmt, codes, scales):
     kdim = codes.shape[1] * (2 if fmt == "mxfp4" else 1)
     out = torch.empty((n, kdim), dtype=torch.float32, device=codes.device)
     check(lib.moe_dequant(WFMT[fmt], n, kdim, _ptr(codes), _ptr(scales), _ptr(out), _stream()))
+    return out
+
+
+def moe_dequant_bf16(codes, scales):
+    """MXFP4 codes [n][kdim/2] + E8M0 scales [n][kdim/32] -> bf16 [n][kdim] (the matrix-core decode)."""
+    _need(codes, torch.uint8, "codes")
+    n = codes.shape[0]
+    kdim = codes.shape[1] * 2
+    _need(scales, torch.uint8, "scales", (n, kdim // 32))
+    out = torch.empty((n, kdim), dtype=torch.bfloat16, device=codes.device)
+    check(lib.moe_dequant_bf16(n, kdim, _ptr(codes), _ptr(scales), _ptr(out), _stream()))
     return out
 
 

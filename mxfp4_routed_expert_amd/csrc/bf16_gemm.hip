@@ -234,10 +234,7 @@ __global__ __launch_bounds__(kFThreads) void fgemm_pair_kernel(const FGemmParams
                         const int R = m * kPBN + 32 * wn + 16 * i + lr;
                         const uint32_t cw = *(const uint32_t *)(st + R * 32 + (cswz(R, ks) << 4) + 4 * lg);
                         const float sc = *(const float *)(st + kCodes + (R * 2 + ks) * 4);
-                        bw[m][i] = pack8(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 0),
-                                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 1),
-                                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 2),
-                                         __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cw, sc, 3));
+                        bw[m][i] = fp4x8_scaled_bf16(cw, sc);
                     }
 #pragma unroll
                 for (int pl = 0; pl < NP; ++pl)
@@ -423,10 +420,7 @@ __global__ __launch_bounds__(kFThreads) void fgemm_down_kernel(const FGemmParams
                 for (int i = 0; i < kDNF; ++i) {
                     const uint32_t c = wlive ? W.c[i][q] : 0u;
                     const float sc = e8m0_to_f32(wlive ? W.s[i] : 127u);
-                    const bf16x8 b = pack8(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 0),
-                                           __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 1),
-                                           __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 2),
-                                           __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(c, sc, 3));
+                    const bf16x8 b = fp4x8_scaled_bf16(c, sc);
 #pragma unroll
                     for (int j = 0; j < 4; ++j)
 #pragma unroll

@@ -51,15 +51,22 @@ MOE_DEV bf16x8 pack8(bf16x2 a, bf16x2 b, bf16x2 c, bf16x2 d) {
     return r;
 }
 
+// The scaled MXFP4 decode of every kernel that multiplies decoded weights (or MX-encoded
+// activations) in bf16: eight E2M1 codes of one dword (byte b holds elements 2b, 2b+1,
+// low nibble first) times the block scale `sc` (2^(s-127), e8m0_to_f32), by the gfx950
+// scaled conversion, which applies the scale inside the instruction.  An E2M1 value times
+// a power of two is a bf16 value unless it leaves bf16's range; moe_dequant_bf16 runs this
+// same function, so its output is what the kernels multiply.
+MOE_DEV bf16x8 fp4x8_scaled_bf16(uint32_t w, float sc) {
+    return pack8(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0), __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1),
+                 __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2), __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
+}
+MOE_DEV u32x4 fp4x8_scaled_bf16_bits(uint32_t w, float sc) { return __builtin_bit_cast(u32x4, fp4x8_scaled_bf16(w, sc)); }
+
 // MFMA operand slices of one 32-code MXFP4 unit with its block scale: slice q = values 8q..8q+7.
 MOE_DEV void unit_to_bf16x8(const u32x4 w, float sc, bf16x8 (&a)[4]) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        a[q] = pack8(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 0),
-                     __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 1),
-                     __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 2),
-                     __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[q], sc, 3));
-    }
+    for (int q = 0; q < 4; ++q) a[q] = fp4x8_scaled_bf16(w[q], sc);
 }
 
 // Two E2M1 codes (byte `sel` of `w`: low nibble first) -> two bf16 values, unscaled.

@@ -27,7 +27,6 @@ struct GemvParams {
     int nl;                    // 16-byte units per lane per row
     int rows_per_wg;           // matrix rows per workgroup
     int chunk;                 // tokens staged in LDS at once (<= MAXM)
-    int lds_ld;                // LDS row stride in elements (matrix-core GEMV)
     // Optional extra grid slot (grid y == shared_slot) that runs a second weight set over
     // the identity rows 0..T-1 -- the shared expert fused into the routed launch.
     int shared_slot = -1;      // -1: none
@@ -73,9 +72,6 @@ void down_combine_mfma_launch(const DownCombineParams &p, dim3 grid, size_t lds,
 moe_status gemv_launch(int fmt, int act, bool pair, GemvParams p, int slots, int max_rows_per_expert,
                        hipStream_t stream, const char *what);
 
-// Matrix-core decode GEMV (MXFP4 weights, N % 16 == 0); see gemv_mfma.hip.
-bool gemv_mfma_supported(int fmt, const GemvParams &p);
-moe_status gemv_mfma_launch(int act, bool pair, GemvParams p, int slots, hipStream_t stream, const char *what);
 
 moe_status mx_quantize_launch(int rows, int cols, const void *x, bool f32, uint8_t *codes, uint8_t *scales,
                               hipStream_t stream);

@@ -185,15 +185,7 @@ MOE_DEV void stage_activations(const GemvParams &p, unsigned char *smem, int row
                 const bool ok = src[u] >= 0;
                 const float sc = e8m0_to_f32(sb[u]);
 #pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    const bf16x2 v0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cv[u][d], sc, 0);
-                    const bf16x2 v1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cv[u][d], sc, 1);
-                    const bf16x2 v2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cv[u][d], sc, 2);
-                    const bf16x2 v3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cv[u][d], sc, 3);
-                    const u32x4 val = {__builtin_bit_cast(uint32_t, v0), __builtin_bit_cast(uint32_t, v1),
-                                       __builtin_bit_cast(uint32_t, v2), __builtin_bit_cast(uint32_t, v3)};
-                    dst[d ^ z] = ok ? val : u32x4{0, 0, 0, 0};
-                }
+                for (int d = 0; d < 4; ++d) dst[d ^ z] = ok ? fp4x8_scaled_bf16_bits(cv[u][d], sc) : u32x4{0, 0, 0, 0};
             }
         }
     } else {

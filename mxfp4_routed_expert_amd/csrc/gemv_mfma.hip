@@ -1,252 +1,7 @@
-// Decode-path GEMV on the matrix cores for MXFP4 expert weights.
-//
-// Same job as the VALU dequant-GEMV (gemv.hip) -- stream each routed expert's MXFP4 rows
-// once from HBM -- with the multiply-adds moved to v_mfma_f32_16x16x32_bf16, so the vector
-// ALU only converts codes (one scaled-conversion instruction per two weights, the E8M0
-// block scale applied inside it; E2M1 x 2^k is exact in bf16).
-//
-// Tile: one workgroup owns 16 rows of the matrix (of gate AND up for the SwiGLU pair) of one
-// expert.  Its 4 waves split K: wave w streams K-steps [w*S/4, (w+1)*S/4) of 128 values.
-// In a K-step every lane loads the 16-byte unit (32 codes) of row l%16, block 4s + l/16,
-// so one wave-wide load covers 16 rows x 64 contiguous bytes; the lane converts it to
-// 32 bf16 values, which form its A-operand slices for four MFMAs (K-slots of lane group
-// l/16 = the block's 8-value quarters).  The B operand holds the tokens as the 16 columns:
-// lane (n = l%16, g = l/16) supplies the same K positions of token n, read from the
-// wave's private LDS copy of its K-range of the activations.  float32 activations are
-// split into bf16 hi + lo (two MFMAs; |h - hi - lo| <= 2^-17 |h|).  At the end the four
-// waves' partial tiles are summed in a fixed order through LDS (no atomics), SwiGLU is
-// applied in registers and each lane stores 4 consecutive rows of one token.
+// Decode down product and weighted combine on the matrix cores, MXFP4 weights.
 #include "gemv.h"
 
 namespace moe {
-
-constexpr int kMfWaves = 4;
-constexpr int kMfThreads = kMfWaves * 64;
-#ifndef MOE_MFMA_KUNROLL
-#define MOE_MFMA_KUNROLL 2
-#endif
-constexpr int kMfKU = MOE_MFMA_KUNROLL;   // K-steps loaded per lane before use
-constexpr int kMfMaxTok = 16;             // MFMA columns
-constexpr size_t kMfLdsBudget = 64 * 1024;
-
-// Stage activation rows [c0, c0+mc) of the expert, K positions [k0, k1), into this wave's
-// LDS planes (bf16; f32 input also fills the lo plane).  Row stride `ld` elements.
-template <int ACT>
-MOE_DEV void stage_wave(const GemvParams &p, uint16_t *hi, uint16_t *lo, int ld, int row0, int c0, int mc, int k0,
-                        int k1) {
-    const int lane = lane_id();
-    const int kw = k1 - k0;
-    if constexpr (ACT == kActMX) {
-        const int nb = kw / 32;   // k0, k1 multiples of 32
-        for (int i = lane; i < mc * nb; i += 64) {
-            const int m = i / nb, blk = i - m * nb;
-            const int r = row0 + c0 + m;
-            int arow = p.gather ? p.sorted_pairs[r] : r;
-            if (p.gather) arow = arow >= 0 ? arow / p.k : -1;
-            u32x4 *dst = (u32x4 *)(hi + (size_t)m * ld + blk * 32);
-            if (arow >= 0 && arow < p.n_act_rows) {
-                const int gb = k0 / 32 + blk;
-                const u32x4 cv = ((const u32x4 *)((const uint8_t *)p.act + (size_t)arow * (p.K / 2)))[gb];
-                const float sc = e8m0_to_f32(p.act_s[(size_t)arow * (p.K / 32) + gb]);
-#pragma unroll
-                for (int d = 0; d < 4; ++d) {
-                    dst[d] = u32x4{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cv[d], sc, 0)),
-                                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cv[d], sc, 1)),
-                                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cv[d], sc, 2)),
-                                   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(cv[d], sc, 3))};
-                }
-            } else {
-#pragma unroll
-                for (int d = 0; d < 4; ++d) dst[d] = u32x4{0, 0, 0, 0};
-            }
-        }
-    } else {
-        // 8 elements per step: 16 bytes of bf16 or 32 bytes of f32
-        const int nv = kw / 8;
-        for (int i = lane; i < mc * nv; i += 64) {
-            const int m = i / nv, v = i - m * nv;
-            const int r = row0 + c0 + m;
-            int arow = p.gather ? p.sorted_pairs[r] : r;
-            if (p.gather) arow = arow >= 0 ? arow / p.k : -1;
-            const bool ok = arow >= 0 && arow < p.n_act_rows;
-            u32x4 *dh = (u32x4 *)(hi + (size_t)m * ld + v * 8);
-            if constexpr (ACT == kActBF16) {
-                *dh = ok ? ((const u32x4 *)((const uint16_t *)p.act + (size_t)arow * p.K + k0))[v] : u32x4{0, 0, 0, 0};
-            } else {
-                u32x4 h4 = {0, 0, 0, 0}, l4 = {0, 0, 0, 0};
-                if (ok) {
-                    const f32x4 *src = (const f32x4 *)((const float *)p.act + (size_t)arow * p.K + k0) + 2 * v;
-                    const f32x4 a = src[0], b = src[1];
-                    float f[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-                    uint32_t hb[8], lb[8];
-#pragma unroll
-                    for (int t = 0; t < 8; ++t) {
-                        hb[t] = bf16_rne_bits(f[t]);
-                        lb[t] = bf16_rne_bits(f[t] - __uint_as_float(hb[t] << 16));
-                    }
-                    h4 = u32x4{hb[0] | hb[1] << 16, hb[2] | hb[3] << 16, hb[4] | hb[5] << 16, hb[6] | hb[7] << 16};
-                    l4 = u32x4{lb[0] | lb[1] << 16, lb[2] | lb[3] << 16, lb[4] | lb[5] << 16, lb[6] | lb[7] << 16};
-                }
-                *dh = h4;
-                *(u32x4 *)(lo + (size_t)m * ld + v * 8) = l4;
-            }
-        }
-    }
-}
-
-template <int ACT, bool PAIR, bool ROUTED>
-__global__ __launch_bounds__(kMfThreads) void gemv_mfma_kernel(const GemvParams p) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    constexpr bool F32 = ACT == kActF32;
-    constexpr int NM = PAIR ? 2 : 1;
-
-    int e = 0, row0 = 0, M = p.T;
-    if constexpr (ROUTED) {
-        e = wave_nth_nonempty(p.offsets, p.E, blockIdx.y);
-        if (e < 0) return;
-        row0 = p.offsets[e];
-        M = p.offsets[e + 1] - row0;
-        if (row0 < 0 || M <= 0 || row0 + M > p.R) return;
-    }
-    const int lane = lane_id(), wave = wave_id();
-    const int col = lane & 15, g = lane >> 4;
-    const int n0 = blockIdx.x * 16;            // first row of the tile (N % 16 == 0)
-    const int Kb = p.K / 32;                   // MXFP4 blocks per row
-    const int S = (Kb + 3) / 4;                // K-steps of 128
-    const int s0 = wave * S / kMfWaves, s1 = (wave + 1) * S / kMfWaves;
-    const int k0 = s0 * 128, k1 = min(s1 * 128, p.K);
-    const int ld = p.lds_ld;                   // LDS row stride (elements) of a wave's plane
-    uint16_t *hi = (uint16_t *)smem + (size_t)wave * (F32 ? 2 : 1) * p.chunk * ld;
-    uint16_t *lo = hi + (size_t)p.chunk * ld;
-    float *red = (float *)(smem + (size_t)kMfWaves * (F32 ? 2 : 1) * p.chunk * ld * 2);   // [waves][NM][64][4]
-
-    const size_t row = (size_t)e * p.N + n0 + col;
-    const uint8_t *wrow[NM];
-    const uint8_t *srow[NM];
-#pragma unroll
-    for (int mi = 0; mi < NM; ++mi) {
-        wrow[mi] = p.w[mi] + row * (size_t)(p.K / 2);
-        srow[mi] = (const uint8_t *)p.s[mi] + row * (size_t)Kb;
-    }
-
-    for (int c0 = 0; c0 < M; c0 += p.chunk) {
-        const int mc = min(p.chunk, M - c0);
-        stage_wave<ACT>(p, hi, lo, ld, row0, c0, mc, k0, k1);
-        const int tok = min(col, mc - 1);
-        f32x4 acc[NM];
-#pragma unroll
-        for (int mi = 0; mi < NM; ++mi) acc[mi] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-
-        for (int s = s0; s < s1; s += kMfKU) {
-            u32x4 wv[kMfKU][NM];
-            uint32_t sb[kMfKU][NM];
-            // unconditional loads from clamped addresses (no wait at a branch join)
-#pragma unroll
-            for (int u = 0; u < kMfKU; ++u) {
-                const int blk = min((s + u) * 4 + g, Kb - 1);
-#pragma unroll
-                for (int mi = 0; mi < NM; ++mi) {
-                    wv[u][mi] = __builtin_nontemporal_load((const u32x4 *)(wrow[mi] + (size_t)blk * 16));
-                    sb[u][mi] = srow[mi][blk];
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < kMfKU; ++u) {
-                if (s + u >= s1) break;
-                const int kl = (s + u - s0) * 128 + g * 32;      // K offset inside the wave's slice
-                const bool kvalid = (s + u) * 4 + g < Kb;          // past K: zero B as well as A
-                bf16x8 bh[4], bl[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    u32x4 vh = {0, 0, 0, 0}, vl = {0, 0, 0, 0};
-                    if (kvalid) {
-                        vh = *(const u32x4 *)(hi + (size_t)tok * ld + kl + 8 * q);
-                        if constexpr (F32) vl = *(const u32x4 *)(lo + (size_t)tok * ld + kl + 8 * q);
-                    }
-                    bh[q] = __builtin_bit_cast(bf16x8, vh);
-                    bl[q] = __builtin_bit_cast(bf16x8, vl);
-                }
-#pragma unroll
-                for (int mi = 0; mi < NM; ++mi) {
-                    bf16x8 a[4];
-                    unit_to_bf16x8(wv[u][mi], kvalid ? e8m0_to_f32(sb[u][mi]) : 0.0f, a);
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q], bh[q], acc[mi], 0, 0, 0);
-                        if constexpr (F32) acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q], bl[q], acc[mi], 0, 0, 0);
-                    }
-                }
-            }
-        }
-        // split-K reduction in a fixed order: waves 0..3
-#pragma unroll
-        for (int mi = 0; mi < NM; ++mi) *(f32x4 *)(red + (((size_t)wave * NM + mi) * 64 + lane) * 4) = acc[mi];
-        __syncthreads();
-        if (wave == 0) {
-            f32x4 t[NM];
-#pragma unroll
-            for (int mi = 0; mi < NM; ++mi) {
-                t[mi] = *(const f32x4 *)(red + ((size_t)mi * 64 + lane) * 4);
-#pragma unroll
-                for (int w = 1; w < kMfWaves; ++w) {
-                    const f32x4 v = *(const f32x4 *)(red + (((size_t)w * NM + mi) * 64 + lane) * 4);
-                    t[mi][0] += v[0]; t[mi][1] += v[1]; t[mi][2] += v[2]; t[mi][3] += v[3];
-                }
-            }
-            if (col < mc) {
-                f32x4 r = t[0];
-                if constexpr (PAIR) {
-#pragma unroll
-                    for (int v = 0; v < 4; ++v) r[v] = silu(t[0][v]) * t[NM - 1][v];
-                }
-                const size_t o = (size_t)(row0 + c0 + col) * p.N + n0 + 4 * g;
-                if (p.residual) {
-                    const f32x4 rr = *(const f32x4 *)(p.residual + o);
-                    r[0] += rr[0]; r[1] += rr[1]; r[2] += rr[2]; r[3] += rr[3];
-                }
-                *(f32x4 *)(p.out + o) = r;
-            }
-        }
-        __syncthreads();
-    }
-}
-
-using MfFn = void (*)(const GemvParams);
-
-template <bool PAIR, bool ROUTED>
-static MfFn pick_mf(int act) {
-    if (act == kActF32) return gemv_mfma_kernel<kActF32, PAIR, ROUTED>;
-    if (act == kActMX) return gemv_mfma_kernel<kActMX, PAIR, ROUTED>;
-    return gemv_mfma_kernel<kActBF16, PAIR, ROUTED>;
-}
-
-bool gemv_mfma_supported(int fmt, const GemvParams &p) {
-    return fmt == kFmtMXFP4 && p.N % 16 == 0 && p.K % 32 == 0 && p.N >= 16;
-}
-
-moe_status gemv_mfma_launch(int act, bool pair, GemvParams p, int slots, hipStream_t stream, const char *what) {
-    const int Kb = p.K / 32;
-    const int S = (Kb + 3) / 4;
-    const int kw_max = ((S + kMfWaves - 1) / kMfWaves) * 128;   // widest wave slice
-    const int ld = kw_max + 8;                                  // 16-byte pad spreads LDS banks
-    const int planes = act == kActF32 ? 2 : 1;
-    const size_t red = (size_t)kMfWaves * (pair ? 2 : 1) * 64 * 16;
-    const size_t per_tok = (size_t)kMfWaves * planes * ld * 2;
-    int chunk = (int)((kMfLdsBudget - red) / per_tok);
-    if (chunk > kMfMaxTok) chunk = kMfMaxTok;
-    if (chunk < 1) {
-        set_error("%s: activation slice does not fit in LDS", what);
-        return MOE_ERR_UNSUPPORTED;
-    }
-    p.chunk = chunk;
-    p.lds_ld = ld;
-    const size_t lds = per_tok * chunk + red;
-    dim3 grid(p.N / 16, slots);
-    MfFn fn = pair ? (p.offsets ? pick_mf<true, true>(act) : pick_mf<true, false>(act))
-                   : (p.offsets ? pick_mf<false, true>(act) : pick_mf<false, false>(act));
-    hipLaunchKernelGGL(fn, grid, dim3(kMfThreads), lds, stream, p);
-    return launch_check(what);
-}
 
 // ------------------------------------------------------------------ down + combine
 // The decode down product with the weighted combine (as down_combine_kernel in gemv.hip),

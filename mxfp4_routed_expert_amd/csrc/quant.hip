@@ -87,7 +87,8 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const void *__restrict
     scales[blk] = (uint8_t)s;
 }
 
-// Decode one 16-byte unit per thread with the FFN kernels' conversions.
+// Decode one 16-byte unit per thread with the conversions of the decode GEMV: each code
+// unscaled to float32 (E2M1 and E4M3 values are exact), times the block scale in float32.
 template <int FMT>
 __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict__ codes,
                                                       const void *__restrict__ scales, int n, int kdim,
@@ -119,6 +120,20 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t *__restrict_
             o[4 * d + 2] = w1.x * sc; o[4 * d + 3] = w1.y * sc;
         }
     }
+}
+
+// MXFP4 unit -> 32 bf16 values with the scaled conversion of the matrix-core kernels
+// (fp4x8_scaled_bf16), one 16-byte unit per thread.
+__global__ __launch_bounds__(256) void dequant_bf16_kernel(const uint8_t *__restrict__ codes,
+                                                           const uint8_t *__restrict__ scales, long long units,
+                                                           uint16_t *__restrict__ out) {
+    const long long u = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    if (u >= units) return;
+    const u32x4 wv = ((const u32x4 *)codes)[u];
+    const float sc = e8m0_to_f32(scales[u]);
+    u32x4 *o = (u32x4 *)(out + (size_t)u * 32);
+#pragma unroll
+    for (int d = 0; d < 4; ++d) o[d] = fp4x8_scaled_bf16_bits(wv[d], sc);
 }
 
 }  // namespace
@@ -172,4 +187,19 @@ extern "C" moe_status moe_dequant(int32_t format, int32_t n, int32_t kdim, const
     else
         hipLaunchKernelGGL(dequant_kernel<1>, dim3(grid), dim3(256), 0, s, codes, scales, n, kdim, out);
     return launch_check("moe_dequant");
+}
+
+extern "C" moe_status moe_dequant_bf16(int32_t n, int32_t kdim, const uint8_t *codes, const uint8_t *scales,
+                                       uint16_t *out, moe_stream stream) {
+    clear_error();
+    MOE_REQUIRE(n >= 0 && kdim > 0 && kdim % 32 == 0,
+                "moe_dequant_bf16: need n >= 0 and kdim a positive multiple of 32 (n=%d kdim=%d)", n, kdim);
+    MOE_REQUIRE((int64_t)n * kdim < INT32_MAX, "moe_dequant_bf16: sizes overflow int32");
+    if (n == 0) return MOE_OK;
+    MOE_REQUIRE(codes && scales && out, "moe_dequant_bf16: NULL pointer argument");
+    MOE_REQUIRE((((uintptr_t)codes | (uintptr_t)out) & 15) == 0, "moe_dequant_bf16: codes and out must be 16-byte aligned");
+    const long long units = (long long)n * (kdim / 32);
+    hipLaunchKernelGGL(dequant_bf16_kernel, dim3((unsigned)((units + 255) / 256)), dim3(256), 0, (hipStream_t)stream,
+                       codes, scales, units, out);
+    return launch_check("moe_dequant_bf16");
 }
