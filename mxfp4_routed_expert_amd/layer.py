@@ -2,7 +2,8 @@
 
 route -> permute -> routed experts (moe_expert_ffn) -> shared expert (moe_expert_ffn,
 identity form) -> combine; LatentMoE layers add moe_dense_bf16 before the routed experts
-and after the combine (Kimi K3 article, architecture section).  Decode-sized batches use
+and after the combine (Kimi K3 article, architecture section); a gated shared expert's
+output is scaled by its gate before it is added after the up projection.  Decode-sized batches use
 the fused calls instead: route+permute, routed and shared gate/up in one launch, down and
 combine in one launch.  Every step runs in the
 HIP library; this module only wires buffers.  All buffers for a token count are
@@ -84,17 +85,27 @@ class MoELayer:
         self.y_rows = None if self.fused else e(T * k, L)
         self.y_s = e(T, H) if (sh is not None and not self.fused) else None
         self.z = e(T, L) if w.p_up is not None else None
+        # LatentMoE with a gated shared expert: g * y_s is formed by moe_combine with no
+        # routed slots (k = 0) before it becomes the residual of the up projection
+        self.latent_gate = w.p_up is not None and sh is not None and w.w_shared_gate is not None
+        self.y_sg = e(T, H) if self.latent_gate else None
+        self.no_rows = e(0, dt=i32)
+        self.no_w = e(T, 0)
         self.out = e(T, H)
         self.ws_route = B._workspace(B.moe_route_workspace(T, H, E, k, w.score), device)
-        self.ws_ffn = B._workspace(B.moe_expert_ffn_workspace(w.experts, w.act, T, k), device)
-        self.ws_sh = (B._workspace(B.moe_expert_ffn_workspace(sh, w.act, T, 1), device)
-                      if (sh is not None and not self.fused) else None)
-        # h rows of the staged form (gate/up and down as separate calls) and the fused form
+        # h rows: the staged form runs gate/up and down as separate calls on these buffers
+        # (float32 h in FLOAT mode, MX codes and scales in MXFP4 mode), as does the fused form
+        mx = w.act == "mxfp4"
         self.h = e(T * k, I)
-        self.hq = e(T * k, I // 2, dt=torch.uint8) if w.act == "mxfp4" else None
-        self.hs = e(T * k, I // 32, dt=torch.uint8) if w.act == "mxfp4" else None
+        self.hq = e(T * k, I // 2, dt=torch.uint8) if mx else None
+        self.hs = e(T * k, I // 32, dt=torch.uint8) if mx else None
         self.ws_gu = B._workspace(B.moe_expert_gateup_workspace(w.experts, w.act, T, k), device)
-        self.h_sh = e(T, I) if (self.fused and sh is not None) else None
+        staged_sh = sh is not None and not self.fused
+        Is = sh.d_ff if sh is not None else 0
+        self.h_sh = e(T, Is) if sh is not None else None
+        self.hq_sh = e(T, Is // 2, dt=torch.uint8) if (staged_sh and mx) else None
+        self.hs_sh = e(T, Is // 32, dt=torch.uint8) if (staged_sh and mx) else None
+        self.ws_gu_sh = B._workspace(B.moe_expert_gateup_workspace(sh, w.act, T, 1), device) if staged_sh else None
         # otherwise the shared expert does not depend on routing: it runs on a second stream,
         # joined before the combine, so it overlaps router, permutation and routed experts
         self.side = torch.cuda.Stream(device=device) if (w.shared is not None and not self.fused) else None
@@ -102,9 +113,8 @@ class MoELayer:
     def forward(self, x, mark=None):
         """One layer step on tokens x (bf16 [T][H]); returns the float32 output buffer.
 
-        With `mark`, the routed experts run as two calls (gate/up, then down; the fused
-        form always does) and mark("gateup_begin") / mark("gateup_end") are called around
-        the gate/up call, so a caller can record events on the stream around that kernel."""
+        With `mark`, mark("gateup_begin") / mark("gateup_end") are called around the routed
+        gate/up call, so a caller can record events on the stream around that kernel."""
         w = self.w
         if self.fused:
             B.moe_route_permute(x, w.w_router, w.k, w.score, w.renormalize, w.routed_scaling, w.logit_bias,
@@ -119,11 +129,15 @@ class MoELayer:
             B.moe_expert_down_combine(w.experts, w.shared, self.h, self.h_sh, self.ids, self.topk_w, self.p2r,
                                       self.sg, out=self.out)
             return self.out
+        mx = w.act == "mxfp4"
         if w.shared is not None:
             cur = torch.cuda.current_stream()
             self.side.wait_stream(cur)
             with torch.cuda.stream(self.side):
-                B.moe_expert_ffn(w.shared, x, w.act, 1, None, None, out=self.y_s, ws=self.ws_sh)
+                B.moe_expert_gateup(w.shared, x, w.act, 1, None, None,
+                                    out=(None if mx else self.h_sh, self.hq_sh, self.hs_sh), ws=self.ws_gu_sh)
+                B.moe_expert_down(w.shared, self.T, w.act, 1, None, self.h_sh, self.hq_sh, self.hs_sh,
+                                  out=self.y_s)
         B.moe_route_permute(x, w.w_router, w.k, w.score, w.renormalize, w.routed_scaling, w.logit_bias,
                             w.select_bias, w.w_shared_gate,
                             out=(self.ids, self.topk_w, self.sg, self.offs, self.sp, self.p2r), ws=self.ws_route,
@@ -131,20 +145,21 @@ class MoELayer:
         xe = x
         if w.p_down is not None:
             xe = B.moe_dense_bf16(x, w.p_down, out=self.x_lat)
-        if mark is None:
-            B.moe_expert_ffn(w.experts, xe, w.act, w.k, self.offs, self.sp, out=self.y_rows, ws=self.ws_ffn)
-        else:
+        if mark is not None:
             mark("gateup_begin")
-            h = self.h if w.act == "float" else None
-            B.moe_expert_gateup(w.experts, xe, w.act, w.k, self.offs, self.sp, out=(h, self.hq, self.hs),
-                                ws=self.ws_gu)
+        B.moe_expert_gateup(w.experts, xe, w.act, w.k, self.offs, self.sp,
+                            out=(None if mx else self.h, self.hq, self.hs), ws=self.ws_gu)
+        if mark is not None:
             mark("gateup_end")
-            B.moe_expert_down(w.experts, self.T, w.act, w.k, self.offs, self.h, self.hq, self.hs, out=self.y_rows)
+        B.moe_expert_down(w.experts, self.T, w.act, w.k, self.offs, self.h, self.hq, self.hs, out=self.y_rows)
         if w.shared is not None:
             cur.wait_stream(self.side)
         if w.p_up is not None:
             B.moe_combine(self.y_rows, self.p2r, self.topk_w, out=self.z)
-            B.moe_dense_bf16(self.z, w.p_up, residual=self.y_s, out=self.out)
+            res = self.y_s
+            if self.latent_gate:
+                res = B.moe_combine(None, self.no_rows, self.no_w, self.y_s, self.sg, out=self.y_sg)
+            B.moe_dense_bf16(self.z, w.p_up, residual=res, out=self.out)
         else:
             B.moe_combine(self.y_rows, self.p2r, self.topk_w, self.y_s, self.sg, out=self.out)
         return self.out
