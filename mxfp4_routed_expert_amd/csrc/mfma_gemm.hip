@@ -3,22 +3,30 @@
 // With MX-quantised activations both operands of every expert product are MXFP4: 32-value
 // E2M1 blocks sharing one E8M0 scale (the format the pages name: rabbit README, opening
 // section and architecture table).  v_mfma_scale_f32_32x32x64_f8f6f4 takes exactly that:
-// lane l supplies 16 bytes (one 32-value block) of row l%32, K-block l/32, and the block's
-// scale byte; it accumulates the scaled products in float32.
+// lane l supplies 16 bytes (one 32-value block) of row l%32 and K-group l/32, plus a 32-bit
+// register whose byte `opsel` is the block's scale; it accumulates the scaled products in
+// float32.  The K order inside a product is free as long as both operands use the same one,
+// so lane group g takes blocks 4g .. 4g+3 of each 256-value K-step, one per quarter q: the
+// four scale bytes a lane needs in a step are one dword, and quarter q selects byte q.
 //
-// Tile: a workgroup computes 128 rows of one expert (tokens routed to it, in sorted order)
-// by 128 output columns -- of gate AND up for the SwiGLU pair.  Its 8 waves (two per SIMD,
-// so one wave's matrix work covers the other's barrier and LDS waits) each own 64 rows x 32
-// columns as 2 x 1 MFMA tiles per matrix.  K advances in steps of 256 values; a
-// step's A rows (gathered token rows), B rows (weight rows) and scale windows travel from
-// global memory straight into LDS (global_load_lds), a whole 128-byte line per row, while
-// the matrix cores work on the previous step.
+// Item: 256 rows of one expert (tokens routed to it, in sorted order) by 256 weight rows
+// (128 columns of gate AND of up for the SwiGLU pair; 256 output columns for down).  One
+// workgroup of 4 waves per CU, one wave per SIMD; wave (wm, wn) owns 128 rows x 4 weight
+// tiles of 32, i.e. 16 accumulator tiles (256 registers), so each quarter it reads 8 KB
+// of operands from LDS for 16 matrix instructions -- half of what a 64 x 64 wave tile
+// reads -- which keeps LDS under its bandwidth at the matrix cores' rate.
+// K advances in steps of 256 values: every operand row contributes one whole 128-byte
+// line per step.  A step's A rows (gathered token rows), B rows (weight rows) and scale
+// windows go from global memory straight into LDS (global_load_lds), two steps resident
+// (2 x 72 KB), the next one in flight while the matrix cores work on the current one.
+// Small row counts: an item whose live rows fit 128 (or 64) runs with 2 (or 1) row tiles
+// per wave, so all four waves share the smaller tile; and when the last round of items
+// would leave CUs idle, its items are split into halves or quarters by rows.
 // Epilogue, gate/up: h = silu(g) * u, staged through LDS so that each lane owns a row's
 // 32-column block and OCP-MX quantises it alone (block maximum, 16 packed code bytes, one
 // scale byte).  Epilogue, down: float32 rows of y.
-// The grid is persistent (one wave of resident workgroups); each workgroup turns
-// expert_offsets into a prefix of row tiles per expert in LDS and walks its share of the
-// (row tile, column tile) items, so no workgroup is launched for tiles that do not exist.
+// The grid is persistent (one workgroup per CU); each workgroup turns expert_offsets into a
+// prefix of 256-row tiles per expert in LDS and walks its share of the work units.
 #include <algorithm>
 #include <type_traits>
 
@@ -29,21 +37,19 @@ namespace moe {
 
 typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 
-constexpr int kGBM = 128;          // rows (tokens) per workgroup tile
-constexpr int kGBN = 128;          // output columns per workgroup tile
-#ifndef MOE_GEMM_WAVES
-#define MOE_GEMM_WAVES 8           // waves per workgroup: 4 (one per SIMD) or 8 (two per SIMD)
-#endif
-constexpr int kNW = MOE_GEMM_WAVES;
-constexpr int kGThreads = 64 * kNW;
-#ifndef MOE_GEMM_WN
-#define MOE_GEMM_WN (MOE_GEMM_WAVES == 8 ? 4 : 2)   // waves along the output columns
-#endif
-constexpr int kWN = MOE_GEMM_WN;
-constexpr int kWM = kNW / kWN;                 // waves along the rows
-constexpr int kTM = kGBM / 32 / kWM;           // 32-row MFMA tiles per wave
-constexpr int kTN = kGBN / 32 / kWN;           // 32-column MFMA tiles per wave and matrix
-static_assert((kNW == 4 || kNW == 8) && kTM >= 1 && kTN >= 1 && 32 * kTM * kTN % 64 == 0, "wave layout");
+constexpr int kQBM = 256;              // rows per item
+constexpr int kQBR = 256;              // weight rows per item
+constexpr int kQThreads = 256;         // 4 waves, 2 along the rows x 2 along the weight rows
+constexpr int kQRowB = 128;            // code bytes per row per K-step (256 values)
+constexpr int kQSlot = 16;             // LDS bytes per scale row per step
+// LDS: A codes of both stages, then B codes of both stages, then scale windows of both.
+constexpr int kQA = kQBM * kQRowB;                   // 32 KB per stage
+constexpr int kQB = kQBR * kQRowB;                   // 32 KB per stage
+constexpr int kQS = (kQBM + kQBR) * kQSlot;          // 8 KB per stage
+constexpr int kQOffA = 0, kQOffB = 2 * kQA, kQOffS = 2 * kQA + 2 * kQB;
+constexpr int kQLds = kQOffS + 2 * kQS;              // 144 KB
+constexpr int kQLd = 64 + 4;                         // epilogue staging row stride (floats)
+static_assert(4 * 128 * kQLd * 4 <= kQLds, "epilogue staging fits the stage buffers");
 
 struct GemmParams {
     const uint8_t *a;              // A codes: token rows [n_arows][K/2] (gather) or rows [R][K/2]
@@ -73,17 +79,15 @@ MOE_DEV uint32_t e2m1_code_of(float a) {   // same midpoint rule as the activati
            (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) + (uint32_t)(a > 5.0f);
 }
 
-
-// Asynchronous global -> LDS copy (global_load_lds): lane l reads base + voff (+ OFF) and
-// its bytes land at dst + l * size (base and dst are the same in every lane; the
-// instruction takes dst from M0).  Written as asm so that the compiler does not add a
-// wait for all copies in flight before every LDS read; the pipeline below waits for
-// exactly the copies it needs.  The instruction has no register result, so nothing the
-// compiler allocates is written when it completes.
-template <int OFF>
+// Asynchronous global -> LDS copy (global_load_lds): lane l reads base + voff and its bytes
+// land at dst + l * size (dst is the same in every lane; the instruction takes it from M0).
+// Written as asm so that the compiler does not add a wait for all copies in flight before
+// every LDS read; the pipeline below waits for exactly the copies it needs.  The
+// instruction has no register result, so nothing the compiler allocates is written when
+// it completes.
 MOE_DEV void dma16(const uint8_t *base, uint32_t voff, const unsigned char *dst) {
     const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
-    asm volatile("global_load_lds_dwordx4 %0, %1 offset:%2" ::"v"(voff), "s"(base), "i"(OFF), "{m0}"(l) : "memory");
+    asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(base), "{m0}"(l) : "memory");
 }
 MOE_DEV void dma4(const uint8_t *base, uint32_t voff, const unsigned char *dst) {
     const uint32_t l = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst);
@@ -95,353 +99,367 @@ MOE_DEV const uint8_t *uniform_ptr(const void *q) {
     return (const uint8_t *)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 
-// Wait until at most N of this wave's memory operations are outstanding, finish its LDS
-// reads, then meet the other waves.  One asm block, so no memory access moves across it.
-template <int N>
-MOE_DEV void wait_vm_and_barrier() {
-    asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"i"(N) : "memory");
-}
+// All of this wave's copies have landed and its LDS reads are done; then the waves meet.
+// One asm block, so no memory access moves across it.
+MOE_DEV void wait_copies_and_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
-// K-step of MOE_GEMM_KSTEP values (256: each operand row contributes one whole 128-byte
-// line per step; 128: half a line, so that more steps fit in LDS at once).
-#ifndef MOE_GEMM_KSTEP
-#define MOE_GEMM_KSTEP 256
-#endif
-constexpr int kGStep = MOE_GEMM_KSTEP;
-constexpr int kRowB = kGStep / 2;              // code bytes per row per step
-constexpr int kCh = kRowB / 16;                // 16-byte chunks (K-blocks) per row per step
-constexpr int kRpc = 1024 / kRowB;             // rows moved by one 1-KB copy
-constexpr int kRowsPW = kGBM / kNW;            // rows of each operand a wave copies
-constexpr int kCpo = kRowsPW / kRpc;           // copies per operand per wave
-constexpr int kScB = 16;                       // LDS bytes per scale row per step (window)
-static_assert(kGStep == 256 || kGStep == 128, "K-step");
+// Position of 16-byte chunk c of LDS row r is c ^ qswz(r): a quarter's operand read (rows
+// r .. r+31 at one chunk) then spreads over all 16-byte bank groups whether the banks repeat
+// every 128 or every 256 bytes.
+MOE_DEV int qswz(int r) { return ((r >> 1) & 7) ^ ((r & 1) << 2); }
 
-// Chunk position of chunk c of row r in LDS: rows sharing a 256-byte bank period get
-// different chunk keys, so an operand read (16 rows at one chunk) hits 16 bank groups.
-MOE_DEV int chunk_swz(int r) { return (r / (256 / kRowB)) & (kCh - 1); }
+// One unit of work: rows [m0, m0 + live) of expert e (row0 = its first sorted row, M its
+// row count) against weight rows n0 .. n0+127 of gate and up (pair) or n0 .. n0+255 (down).
+struct QUnit {
+    int e, n0, m0, row0, M;
+};
 
-template <bool PAIR>
-constexpr int gemm_stages() { return kGStep == 256 ? (PAIR ? 2 : 3) : (PAIR ? 5 : 7); }   // steps resident in LDS
-
-template <bool PAIR, bool ROUTED>
-__global__ __launch_bounds__(kGThreads) void mxgemm_kernel(const GemmParams p) {
-    constexpr int NM = PAIR ? 2 : 1;
-    constexpr int kStages = gemm_stages<PAIR>();
-    constexpr int kA = kGBM * kRowB;                   // A codes of a step
-    constexpr int kB = NM * kGBN * kRowB;              // B codes of a step
-    constexpr int kSRows = kGBM + NM * kGBN;           // scale rows: A, then each matrix's
-    constexpr int kStage = kA + kB + kSRows * kScB;
-    constexpr int kCodeCopies = (kGBM + NM * kGBN) / kRpc / kNW;   // 1-KB copies per wave
-    constexpr int kScCopies = kSRows / 16 / kNW;       // scale copies (16 rows x 4 dwords) per wave
-    constexpr int kOps = kCodeCopies + kScCopies;      // memory operations per wave per stage
-    static_assert(kSRows % (16 * kNW) == 0 && kRowsPW % kRpc == 0, "copy split");
-    static_assert((kStages - 2) * kOps <= 63, "vmcnt limit");
-    __shared__ __align__(16) unsigned char smem[kStages * kStage];
-    __shared__ uint8_t s_off[kSRows];
-    __shared__ int s_tp[ROUTED ? MOE_MAX_EXPERTS : 1];
-    __shared__ int s_wave[kGThreads / 64];
-
-    const int NT = (p.N + kGBN - 1) / kGBN;
-    const int total_mt = ROUTED ? build_tile_prefix<kGThreads, kGBM>(p.offsets, p.E, p.R, s_tp, s_wave) : (p.T + kGBM - 1) / kGBM;
-    const int items = total_mt * NT;
-    // Items are ordered expert by expert, then by column tile, then by row tile, and each
-    // round of G workgroups hands XCD x (workgroups x, x+8, ...) a contiguous run of G/8
-    // items: the row tiles of one expert that share a column tile of weights run at the
-    // same time on the same XCD, so those weight bytes come from that XCD's L2.
-    const int G = gridDim.x;
-    const int slot = xcd_slot(blockIdx.x, G);
+template <bool PAIR, int TM>
+MOE_DEV void qgemm_unit(const GemmParams &p, const QUnit &u, unsigned char *smem, const int *s_arow) {
+    constexpr int NA = 2 * TM;                    // 1-KB A copies per wave (A holds 64*TM rows)
     const int lane = lane_id(), wave = wave_id();
-    const int wm = wave / kWN, wn = wave % kWN;        // output block of this wave
-    const int hr = lane & 31, hb = lane >> 5;          // MFMA operand row / K-block of this lane
+    const int wm = wave >> 1, wn = wave & 1;
+    const int hr = lane & 31, hb = lane >> 5;
     const int Kh = p.K / 2, Kb = p.K / 32;
-    const int S = (Kb + kCh - 1) / kCh;                // K-steps
+    const int S = (Kb + 7) / 8;                   // K-steps
+    const int nvalid = Kb - 8 * (S - 1);          // blocks of the last step (1..8)
+    const int eu = __builtin_amdgcn_readfirstlane(u.e);
 
-    for (int item = slot; item < items; item += G) {
-        int e = 0, tile = 0, nt = 0, row0 = 0, M = p.T;
-        if constexpr (ROUTED) {
-            e = tile_expert(s_tp, p.E, item / NT);
-            const int tpx = e > 0 ? s_tp[e - 1] : 0, te = s_tp[e] - tpx;
-            const int r = item - NT * tpx;
-            nt = r / te;
-            tile = r - nt * te;
-            row0 = p.offsets[e];
-            M = p.offsets[e + 1] - row0;
-        } else {
-            nt = item / total_mt;
-            tile = item - nt * total_mt;
+    // ---- copy sources.  A: rows wave*16*TM + 8t + lane/8 of the unit (LDS rows in that
+    // order), lane%8 = the LDS chunk position, fetching chunk (lane%8) ^ qswz(row).
+    const uint8_t *a_base = uniform_ptr(p.a);
+    const uint8_t *as_base = uniform_ptr((const uint8_t *)((uintptr_t)p.as & ~(uintptr_t)3));
+    const uint32_t as_mis = (uint32_t)((uintptr_t)p.as & 3u);
+    // B: wave w copies weight rows 64w .. 64w+63 of the item: gate (w < 2) or up (w >= 2) rows
+    // n0 + (64w mod 128) + .. for the pair, down rows n0 + 64w + .. otherwise.
+    const int bmat = PAIR ? (wave >> 1) : 0;
+    const int bl0 = PAIR ? 64 * (wave & 1) : 64 * wave;        // first matrix row (past n0) it copies
+    const uint8_t *b_base = uniform_ptr((PAIR && bmat ? p.w[1] : p.w[0]) + (size_t)eu * p.N * Kh);
+    const int cr = lane >> 3, cpos = lane & 7;
+    uint32_t aoff[NA], boff[8];
+    int achunk[NA], bchunk[8];
+#pragma unroll
+    for (int t = 0; t < NA; ++t) {
+        const int r = wave * 16 * TM + 8 * t + cr;
+        achunk[t] = cpos ^ qswz(r);
+        aoff[t] = (uint32_t)s_arow[r] * Kh + 16 * achunk[t];
+    }
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        const int r = 64 * wave + 8 * t + cr;                   // LDS B row
+        bchunk[t] = cpos ^ qswz(r);
+        boff[t] = (uint32_t)min(u.n0 + bl0 + 8 * t + cr, p.N - 1) * Kh + 16 * bchunk[t];
+    }
+    // Scale windows: LDS scale row q (A rows 0..255, then B rows 0..255) holds, from byte 0,
+    // the aligned dwords covering the step's bytes of that row; 4 lanes per row, dword d of
+    // the window.  A dword past the step's bytes fetches the window's first dword again, so
+    // every fetched dword lies inside the array.  Wave w copies scale rows 128w .. 128w+127.
+    const uint8_t *sc_base;
+    uint32_t sc_rel[8];                           // (scale row start - aligned base), per copy
+    {
+        const bool arows = wave < 2;
+        const uint8_t *bs = PAIR && wave == 3 ? p.ws[1] : p.ws[0];
+        const uintptr_t bsa = (uintptr_t)bs & ~(uintptr_t)3;
+        sc_base = uniform_ptr(arows ? (const uint8_t *)as_base : (const uint8_t *)(bsa + (size_t)eu * p.N * Kb));
+        const uint32_t bmis = (uint32_t)((uintptr_t)bs & 3u);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int q = 128 * wave + 16 * i + (lane >> 2);
+            if (arows) {
+                sc_rel[i] = as_mis + (uint32_t)s_arow[q] * Kb;
+            } else {
+                const int br = q - 256;                            // B row of the item
+                const int n = PAIR ? u.n0 + (br & 127) : u.n0 + br;
+                sc_rel[i] = bmis + (uint32_t)min(n, p.N - 1) * Kb;
+            }
         }
-        const int m0 = tile * kGBM;
-        const int n0 = nt * kGBN;
+    }
+    const int sd = lane & 3;
+    // window dword offset of this lane for a window of `len` bytes
+    auto sc_voff = [&](uint32_t rel, int len) {
+        const uint32_t o = rel & 3u;
+        const uint32_t need = (o + (uint32_t)len - 1u) >> 2;
+        return rel - o + ((uint32_t)sd <= need ? 4u * sd : 0u);
+    };
 
-        // Source row of A row r of the tile (rows past the expert's end repeat a valid row).
-        auto a_src_row = [&](int r) {
-            int src = row0 + min(m0 + r, M - 1);
-            if (p.gather) src = p.sorted_pairs[src] / p.k;
-            return min(max(src, 0), p.n_arows - 1);
+    // Issue the copies of step s into stage `st`.  In the last step, chunks past the end of
+    // a row are clamped to its last block (read, never used) and the scale windows shrink.
+    auto issue = [&](int s, int st) {
+        const bool last = s == S - 1;
+        const uint8_t *ab = a_base + 128 * s, *bb = b_base + 128 * s;
+        const uint32_t cmax = 16u * (uint32_t)(Kb - 1 - 8 * s);   // last valid chunk (bytes) in the step
+        unsigned char *adst = smem + kQOffA + st * kQA + wave * 16 * TM * kQRowB;
+        unsigned char *bdst = smem + kQOffB + st * kQB + 64 * wave * kQRowB;
+#pragma unroll
+        for (int t = 0; t < NA; ++t) {
+            uint32_t v = aoff[t];
+            if (last) v = v - 16 * achunk[t] + min(16u * achunk[t], cmax);
+            dma16(ab, v, adst + t * 1024);
+        }
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            uint32_t v = boff[t];
+            if (last) v = v - 16 * bchunk[t] + min(16u * bchunk[t], cmax);
+            dma16(bb, v, bdst + t * 1024);
+        }
+        const int len = last ? nvalid : 8;
+        const uint8_t *sb = sc_base + 8 * s;
+        unsigned char *sdst = smem + kQOffS + st * kQS + 128 * wave * kQSlot;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) dma4(sb, sc_voff(sc_rel[i], len), sdst + i * 256);
+    };
+
+    // ---- consumer side.  Row tiles of this wave: rows 32*TM*wm + 32i (i < TM) of the unit;
+    // weight tiles jb: the pair's gate columns 64wn + 32j (jb = j) and up columns (jb = 2 + j);
+    // down: columns 128wn + 32jb.  Operand address of tile x in quarter q: row base + chunk
+    // (4hb + q) ^ swz = (4hb ^ swz) ^ q.
+    int a_at[TM], b_at[4], sa_at[TM], sb_at[4];
+    uint32_t sa_o[TM], sb_o[4];
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+        const int r = 32 * TM * wm + 32 * i + hr;
+        a_at[i] = kQOffA + r * kQRowB + (((4 * hb) ^ qswz(r)) << 4);
+        sa_at[i] = kQOffS + r * kQSlot + 4 * hb;
+        sa_o[i] = (as_mis + (uint32_t)s_arow[r] * Kb) & 3u;
+    }
+#pragma unroll
+    for (int jb = 0; jb < 4; ++jb) {
+        const int br = PAIR ? 128 * (jb >> 1) + 64 * wn + 32 * (jb & 1) + hr : 128 * wn + 32 * jb + hr;
+        b_at[jb] = kQOffB + br * kQRowB + (((4 * hb) ^ qswz(br)) << 4);
+        sb_at[jb] = kQOffS + (kQBM + br) * kQSlot + 4 * hb;
+        const uint8_t *bs = PAIR && jb >= 2 ? p.ws[1] : p.ws[0];
+        const int n = PAIR ? u.n0 + (br & 127) : u.n0 + br;
+        sb_o[jb] = (uint32_t)(((uintptr_t)bs & 3u) + ((size_t)eu * p.N + min(n, p.N - 1)) * Kb) & 3u;
+    }
+
+    f32x16 acc[TM][4];
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) acc[i][jb][v] = 0.0f;
+
+    auto lds16 = [&](int addr) { return *(const u32x4 *)(smem + addr); };
+    auto scale4 = [&](int addr, uint32_t o) {     // 4 scale bytes from byte o of a two-dword window
+        const uint32_t d0 = *(const uint32_t *)(smem + addr), d1 = *(const uint32_t *)(smem + addr + 4);
+        return __builtin_amdgcn_alignbyte(d1, d0, o);
+    };
+
+    // One K-step from stage s % 2.  In the last step, blocks past K (4hb + q >= nvalid) get
+    // scale byte 0 on both operands: each of their products is at most 36 * 2^-254 in
+    // magnitude, far below float32's smallest subnormal (2^-149), so it adds an exact zero
+    // (their codes are real codes of a clamped block, never NaN or infinite: E2M1 has none).
+    auto step = [&](int s) {
+        const int so = s & 1;
+        uint32_t sa[TM], sb[4];
+#pragma unroll
+        for (int i = 0; i < TM; ++i) sa[i] = scale4(sa_at[i] + so * kQS, sa_o[i]);
+#pragma unroll
+        for (int jb = 0; jb < 4; ++jb) sb[jb] = scale4(sb_at[jb] + so * kQS, sb_o[jb]);
+        if (s == S - 1) {
+            uint32_t kmask = 0xffffffffu;          // bytes of this lane's valid quarters
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                if (4 * hb + q >= nvalid) kmask &= ~(0xffu << (8 * q));
+#pragma unroll
+            for (int i = 0; i < TM; ++i) sa[i] &= kmask;
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) sb[jb] &= kmask;
+        }
+        u32x4 fa[2][TM], fb[2][4];
+        auto rd = [&](int q, u32x4 (&a)[TM], u32x4 (&b)[4]) {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) a[i] = lds16((a_at[i] ^ (q << 4)) + so * kQA);
+#pragma unroll
+            for (int jb = 0; jb < 4; ++jb) b[jb] = lds16((b_at[jb] ^ (q << 4)) + so * kQB);
         };
-        auto b_src_row = [&](int n) { return min(n0 + n, p.N - 1); };
-
-        // ---- copies.  A step's codes sit row-major in LDS, kRowB bytes per row, with the
-        // 16-byte chunk c of row r stored at chunk position c ^ chunk_swz(r): one 1-KB copy
-        // moves kRpc rows, kCh lanes per row, and an MFMA operand read (rows r .. r+15 at one
-        // chunk, served 16 lanes per LDS cycle) hits 16 distinct 16-byte bank groups.  Wave w
-        // copies rows kRowsPW*w .. kRowsPW*(w+1)-1 of A and of each B matrix.
-        const int eu = __builtin_amdgcn_readfirstlane(e);
-        const uint8_t *a_base = uniform_ptr(p.a);
-        const uint8_t *b_base[NM], *bs_base[NM];
+        // quarter Q: the next quarter's operands are read while this one's products run
+        auto quarter = [&](auto q_c) {
+            constexpr int Q = decltype(q_c)::value;
+            if constexpr (Q < 3) rd(Q + 1, fa[(Q + 1) & 1], fb[(Q + 1) & 1]);
 #pragma unroll
-        for (int mi = 0; mi < NM; ++mi) {
-            b_base[mi] = uniform_ptr(p.w[mi] + (size_t)eu * p.N * Kh);
-            bs_base[mi] = uniform_ptr(p.ws[mi] + (size_t)eu * p.N * Kb);
-        }
-        const int cr = lane / kCh;                         // copy lane: row within the copy
-        uint32_t a_off[kCpo], b_off[kCpo];
+            for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int t = 0; t < kCpo; ++t) {
-            a_off[t] = (uint32_t)a_src_row(kRowsPW * wave + kRpc * t + cr) * Kh;
-            b_off[t] = (uint32_t)b_src_row(kRowsPW * wave + kRpc * t + cr) * Kh;
-        }
-        // Scale rows: 4 lanes per row, dword d of the row's window starting at the aligned
-        // dword that holds the step's first byte.  A dword is fetched only when it holds a
-        // byte of the step (otherwise the window's first dword is fetched again), so every
-        // fetched dword lies inside the array.
-        const int sd = lane & 3;
-        const uint8_t *sc_base[kScCopies];
-        uint32_t sc_off[kScCopies];
-#pragma unroll
-        for (int i = 0; i < kScCopies; ++i) {
-            const int q0 = __builtin_amdgcn_readfirstlane(16 * (kScCopies * wave + i));   // first row of the copy
-            const int q = q0 + (lane >> 2);
-            sc_base[i] = q0 < kGBM ? uniform_ptr(p.as) : bs_base[q0 < kGBM + kGBN ? 0 : NM - 1];
-            sc_off[i] = q < kGBM ? (uint32_t)a_src_row(q) * Kb : (uint32_t)b_src_row((q - kGBM) & (kGBN - 1)) * Kb;
-            if (sd == 0) s_off[q] = (uint8_t)((uintptr_t)(sc_base[i] + sc_off[i]) & 3u);
-        }
-        __syncthreads();
-        uint32_t sc_mis[kScCopies];
-#pragma unroll
-        for (int i = 0; i < kScCopies; ++i) sc_mis[i] = s_off[16 * (kScCopies * wave + i) + (lane >> 2)];
-        // Consumer side: LDS byte (step-relative) of block 0 of each scale row this lane feeds.
-        int sa_at[kTM], sb_at[NM][kTN];
-#pragma unroll
-        for (int i = 0; i < kTM; ++i) {
-            const int r = 32 * (kTM * wm + i) + hr;
-            sa_at[i] = kA + kB + r * kScB + s_off[r] + hb;
-        }
-#pragma unroll
-        for (int j = 0; j < kTN; ++j)
-#pragma unroll
-            for (int mi = 0; mi < NM; ++mi) {
-                const int q = kGBM + mi * kGBN + 32 * (kTN * wn + j) + hr;
-                sb_at[mi][j] = kA + kB + q * kScB + s_off[q] + hb;
-            }
-
-        // Issue the copies of step s into its stage buffer.  Steps past the end re-fetch the
-        // last step (never read); K-blocks past the end of a row are clamped to its last one.
-        auto issue = [&](int s) {
-            const int sc = min(s, S - 1);
-            unsigned char *st = smem + (s % kStages) * kStage;
-#pragma unroll
-            for (int t = 0; t < kCpo; ++t) {
-                const int cc = (lane % kCh) ^ chunk_swz(kRowsPW * wave + kRpc * t + cr);   // chunk this lane fetches
-                const uint32_t ko = (uint32_t)min(kCh * sc + cc, Kb - 1) * 16;
-                dma16<0>(a_base, a_off[t] + ko, st + (kRowsPW * wave + kRpc * t) * kRowB);
-#pragma unroll
-                for (int mi = 0; mi < NM; ++mi)
-                    dma16<0>(b_base[mi], b_off[t] + ko, st + kA + (mi * kGBN + kRowsPW * wave + kRpc * t) * kRowB);
-            }
-            const int last = min(kCh, Kb - kCh * sc) - 1;  // last block of the step in the row
-#pragma unroll
-            for (int i = 0; i < kScCopies; ++i) {
-                const uint32_t o = sc_mis[i];
-                const uint32_t need = (o + (uint32_t)last) >> 2;   // dwords 0..need hold bytes of the step
-                const uint32_t v = sc_off[i] + (uint32_t)kCh * sc - o + ((uint32_t)sd <= need ? 4u * sd : 0u);
-                dma4(sc_base[i], v, st + kA + kB + (16 * (kScCopies * wave + i)) * kScB);
-            }
-        };
-
-        // Operands of one 64-value K-quarter q of a step: chunk 2q + hb of each row.
-        struct Quarter {
-            u32x4 a[kTM], b[NM][kTN];
-            int sa[kTM], sb[NM][kTN];
-        };
-        auto read = [&](const unsigned char *st, int q, Quarter &f) {
-            const int c = 2 * q + hb;
-#pragma unroll
-            for (int i = 0; i < kTM; ++i) {
-                const int r = 32 * (kTM * wm + i) + hr;
-                f.a[i] = *(const u32x4 *)(st + r * kRowB + ((c ^ chunk_swz(r)) << 4));
-                f.sa[i] = st[sa_at[i] + 2 * q];
-            }
-#pragma unroll
-            for (int j = 0; j < kTN; ++j)
-#pragma unroll
-                for (int mi = 0; mi < NM; ++mi) {
-                    const int n = mi * kGBN + 32 * (kTN * wn + j) + hr;
-                    f.b[mi][j] = *(const u32x4 *)(st + kA + n * kRowB + ((c ^ chunk_swz(n)) << 4));
-                    f.sb[mi][j] = st[sb_at[mi][j] + 2 * q];
+                for (int jb = 0; jb < 4; ++jb) {
+                    const u32x4 av = fa[Q & 1][i], bv = fb[Q & 1][jb];
+                    acc[i][jb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        i32x8_t{(int)av[0], (int)av[1], (int)av[2], (int)av[3], 0, 0, 0, 0},
+                        i32x8_t{(int)bv[0], (int)bv[1], (int)bv[2], (int)bv[3], 0, 0, 0, 0}, acc[i][jb], 4, 4, Q,
+                        (int)sa[i], Q, (int)sb[jb]);
                 }
         };
-        // K-blocks past the end of K (last step only): zero A codes, unit scales.
-        auto kill = [&](int s, int q, Quarter &f) {
-            if (kCh * s + 2 * q + hb < Kb) return;
+        rd(0, fa[0], fb[0]);
+        quarter(std::integral_constant<int, 0>{});
+        quarter(std::integral_constant<int, 1>{});
+        quarter(std::integral_constant<int, 2>{});
+        quarter(std::integral_constant<int, 3>{});
+    };
+
+    // ---- pipeline: two stages.  At the top of step s its copies have landed and every wave
+    // is done with step s-1, whose stage then takes the copies of step s+1.
+    issue(0, 0);
+    for (int s = 0; s < S; ++s) {
+        wait_copies_and_barrier();
+        if (s + 1 < S) issue(s + 1, (s + 1) & 1);
+        step(s);
+    }
+    __syncthreads();                              // every wave is done with the stages
+
+    // ---- epilogue.  Lane l holds C[8(v/4) + 4(l/32) + v%4][l%32] of each 32x32 tile.
+    const int rbase = u.m0 + 32 * TM * wm;        // first row (within the expert) of this wave
+    if constexpr (!PAIR) {
 #pragma unroll
-            for (int i = 0; i < kTM; ++i) {
-                f.a[i] = u32x4{0, 0, 0, 0};
-                f.sa[i] = 127;
+        for (int i = 0; i < TM; ++i)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int r = rbase + 32 * i + 8 * (v >> 2) + 4 * hb + (v & 3);
+                if (r >= u.M) continue;
+                const size_t orow = (size_t)(u.row0 + r);
+#pragma unroll
+                for (int jb = 0; jb < 4; ++jb) {
+                    const int n = u.n0 + 128 * wn + 32 * jb + hr;
+                    if (n < p.N) p.out[orow * p.N + n] = acc[i][jb][v];
+                }
             }
+    } else {
+        // h = silu(g) * u of the wave's 32*TM rows x 64 columns into LDS (row stride kQLd,
+        // skewed against bank conflicts), then each lane quantises one row's 32-column block
+        // at a time: block maximum, 32 codes packed into 16 bytes, one scale byte.
+        float *hq_lds = (float *)smem + wave * (128 * kQLd);
 #pragma unroll
-            for (int j = 0; j < kTN; ++j)
+        for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int mi = 0; mi < NM; ++mi) f.sb[mi][j] = 127;
-        };
-
-        f32x16 acc[NM][kTM][kTN];
-#pragma unroll
-        for (int mi = 0; mi < NM; ++mi)
-#pragma unroll
-            for (int i = 0; i < kTM; ++i)
-#pragma unroll
-                for (int j = 0; j < kTN; ++j)
-#pragma unroll
-                    for (int v = 0; v < 16; ++v) acc[mi][i][j][v] = 0.0f;
-        // 32-row MFMA tiles of this wave that hold no row of the expert are skipped: their
-        // outputs are never stored.  An expert with at most 64 rows in a tile (most of them
-        // under skewed routing) then costs half the matrix work; the waves of rows 0-63 and
-        // 64-127 share each SIMD, so the remaining work stays spread over all four.
-        bool tlive[kTM];
-#pragma unroll
-        for (int i = 0; i < kTM; ++i)
-            tlive[i] = __builtin_amdgcn_readfirstlane(32 * (kTM * wm + i) < M - m0 ? 1 : 0) != 0;
-        auto mma = [&](const Quarter &f) {
-#pragma unroll
-            for (int mi = 0; mi < NM; ++mi)
-#pragma unroll
-                for (int j = 0; j < kTN; ++j)
-#pragma unroll
-                    for (int i = 0; i < kTM; ++i) {
-                        if (!tlive[i]) continue;
-                        const u32x4 av = f.a[i], bv = f.b[mi][j];
-                        acc[mi][i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                            i32x8_t{(int)av[0], (int)av[1], (int)av[2], (int)av[3], 0, 0, 0, 0},
-                            i32x8_t{(int)bv[0], (int)bv[1], (int)bv[2], (int)bv[3], 0, 0, 0, 0}, acc[mi][i][j], 4, 4,
-                            0, f.sa[i], 0, f.sb[mi][j]);
-                    }
-        };
-
-        // Pipeline: kStages steps in LDS.  At step s, stage s must have landed (the later
-        // kStages-2 may still be in flight); the barrier also tells every wave that step s-1's
-        // buffer has been read, so step s+kStages-1 can refill it.  Within a step the next
-        // quarter's operands load while the current quarter's MFMAs run.
-        auto step = [&](int s, auto last) {
-            wait_vm_and_barrier<(kStages - 2) * kOps>();
-            issue(s + kStages - 1);
-            const unsigned char *st = smem + (s % kStages) * kStage;
-            Quarter f0, f1;
-            read(st, 0, f0);
-#pragma unroll
-            for (int q = 0; q < kCh / 2; q += 2) {
-                read(st, q + 1, f1);
-                if constexpr (decltype(last)::value) kill(s, q, f0);
-                mma(f0);
-                if (q + 2 < kCh / 2) read(st, q + 2, f0);
-                if constexpr (decltype(last)::value) kill(s, q + 1, f1);
-                mma(f1);
-            }
-        };
-#pragma unroll
-        for (int s = 0; s < kStages - 1; ++s) issue(s);
-        for (int s = 0; s < S - 1; ++s) step(s, std::false_type{});
-        step(S - 1, std::true_type{});
-        wait_vm_and_barrier<0>();                          // no copy in flight past this point
-
-        // ---- epilogue.  Lane l holds C[8(v/4) + 4(l/32) + v%4][l%32] of each 32x32 tile.
-        if constexpr (!PAIR) {
-            // y rows: each (tile, v) is 32 consecutive float32 columns of one row per half-wave
-#pragma unroll
-            for (int i = 0; i < kTM; ++i)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
-                    const int r = m0 + 32 * (kTM * wm + i) + 8 * (v >> 2) + 4 * hb + (v & 3);
-                    if (r >= M) continue;
-                    const size_t orow = (size_t)(row0 + r);
-#pragma unroll
-                    for (int j = 0; j < kTN; ++j) {
-                        const int n = n0 + 32 * (kTN * wn + j) + hr;
-                        if (n < p.N) p.out[orow * p.N + n] = acc[0][i][j][v];
-                    }
+                    const int r = 32 * i + 8 * (v >> 2) + 4 * hb + (v & 3);
+                    hq_lds[r * kQLd + 32 * j + hr] = silu_fast(acc[i][j][v]) * acc[i][2 + j][v];
                 }
-        } else {
-            // h = silu(g) * u goes through LDS (the stage buffers are idle now): the wave writes
-            // its RW x 32*kTN block row-major (row stride skewed by 4 floats against bank
-            // conflicts), then each lane owns one 32-column block of one row at a time and
-            // OCP-MX quantises it alone: block maximum, 32 codes packed into 16 bytes, one
-            // scale byte.
-            constexpr int kLd = 32 * kTN + 4;                         // row stride (floats), skewed
-            constexpr int RW = 32 * kTM;                              // rows of the wave's block
-            static_assert(kNW * RW * kLd * 4 <= kStages * kStage, "epilogue staging fits the stage buffers");
-            float *hq_lds = (float *)smem + wave * (RW * kLd);
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");    // LDS is in order within a wave
+        const bool vec_ok = (((uintptr_t)p.oq) & 15u) == 0;
 #pragma unroll
-            for (int i = 0; i < kTM; ++i)
+        for (int it0 = 0; it0 < 64 * TM; it0 += 64) {
+            const int pi = it0 + lane;
+            const int rr = pi >> 1, jb = pi & 1;                  // row in the wave's block, column block
+            const int r = rbase + rr;
+            const int nb = u.n0 + 64 * wn + 32 * jb;               // first column of the block
+            f32x4 h[8];
 #pragma unroll
-                for (int j = 0; j < kTN; ++j)
+            for (int q = 0; q < 8; ++q) h[q] = *(const f32x4 *)(hq_lds + rr * kQLd + 32 * jb + 4 * q);
+            if (r >= u.M || nb >= p.N) continue;
+            const size_t orow = (size_t)(u.row0 + r);
+            if (p.out) {
 #pragma unroll
-                    for (int v = 0; v < 16; ++v) {
-                        const int r = 32 * i + 8 * (v >> 2) + 4 * hb + (v & 3);
-                        hq_lds[r * kLd + 32 * j + hr] = silu_fast(acc[0][i][j][v]) * acc[1][i][j][v];
-                    }
-            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");    // LDS is in order within a wave
-            const bool vec_ok = (((uintptr_t)p.oq) & 15u) == 0;
+                for (int q = 0; q < 8; ++q) *(f32x4 *)(p.out + orow * p.N + nb + 4 * q) = h[q];
+            }
+            uint32_t amax = 0;
 #pragma unroll
-            for (int it0 = 0; it0 < RW * kTN; it0 += 64) {
-                const int rr = (it0 + lane) % RW, jb = (it0 + lane) / RW;   // row in the block, column block
-                const int r = m0 + RW * wm + rr;                          // row within the expert
-                const bool row_ok = r < M;
-                const size_t orow = (size_t)(row0 + (row_ok ? r : 0));
-                const int nb = n0 + 32 * kTN * wn + 32 * jb;              // first column of the block
-                f32x4 h[8];
+            for (int q = 0; q < 8; ++q)
 #pragma unroll
-                for (int q = 0; q < 8; ++q) h[q] = *(const f32x4 *)(hq_lds + rr * kLd + 32 * jb + 4 * q);
-                if (!row_ok || nb >= p.N) continue;
-                if (p.out) {
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) *(f32x4 *)(p.out + orow * p.N + nb + 4 * q) = h[q];
-                }
-                uint32_t amax = 0;
+                for (int c = 0; c < 4; ++c) amax = max(amax, __float_as_uint(h[q][c]) & 0x7fffffffu);
+            uint32_t w[4] = {0, 0, 0, 0}, sbyte = 255;
+            if (amax < 0x7f800000u) {
+                const int ebits = (int)(amax >> 23);
+                int X = ebits == 0 ? -127 : ebits - 127 - 2;
+                X = X < -127 ? -127 : (X > 127 ? 127 : X);
+                const float inv = __uint_as_float((uint32_t)(127 - X) << 23);
 #pragma unroll
                 for (int q = 0; q < 8; ++q)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) amax = max(amax, __float_as_uint(h[q][c]) & 0x7fffffffu);
-                uint32_t w[4] = {0, 0, 0, 0}, sbyte = 255;
-                if (amax < 0x7f800000u) {
-                    const int ebits = (int)(amax >> 23);
-                    int X = ebits == 0 ? -127 : ebits - 127 - 2;
-                    X = X < -127 ? -127 : (X > 127 ? 127 : X);
-                    const float inv = __uint_as_float((uint32_t)(127 - X) << 23);
-#pragma unroll
-                    for (int q = 0; q < 8; ++q)
-#pragma unroll
-                        for (int c = 0; c < 4; ++c) {
-                            const float x = h[q][c];
-                            const uint32_t code = e2m1_code_of(fabsf(x) * inv) | ((__float_as_uint(x) >> 31) << 3);
-                            w[q >> 1] |= code << (4 * (4 * (q & 1) + c));
-                        }
-                    sbyte = (uint32_t)(X + 127);
-                }
-                uint8_t *dst = p.oq + orow * (size_t)(p.N / 2) + nb / 2;
-                if (vec_ok) {
-                    *(u32x4 *)dst = u32x4{w[0], w[1], w[2], w[3]};
-                } else {
-#pragma unroll
-                    for (int q = 0; q < 16; ++q) dst[q] = (uint8_t)(w[q >> 2] >> (8 * (q & 3)));
-                }
-                p.os[orow * (size_t)(p.N / 32) + nb / 32] = (uint8_t)sbyte;
+                    for (int c = 0; c < 4; ++c) {
+                        const float x = h[q][c];
+                        const uint32_t code = e2m1_code_of(fabsf(x) * inv) | ((__float_as_uint(x) >> 31) << 3);
+                        w[q >> 1] |= code << (4 * (4 * (q & 1) + c));
+                    }
+                sbyte = (uint32_t)(X + 127);
             }
+            uint8_t *dst = p.oq + orow * (size_t)(p.N / 2) + nb / 2;
+            if (vec_ok) {
+                *(u32x4 *)dst = u32x4{w[0], w[1], w[2], w[3]};
+            } else {
+#pragma unroll
+                for (int q = 0; q < 16; ++q) dst[q] = (uint8_t)(w[q >> 2] >> (8 * (q & 3)));
+            }
+            p.os[orow * (size_t)(p.N / 32) + nb / 32] = (uint8_t)sbyte;
         }
     }
 }
 
+// One workgroup per CU (its LDS takes 147 KB), so each wave may use a SIMD's whole register
+// file: the 16 accumulator tiles alone take 256 registers.
+template <bool PAIR, bool ROUTED>
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void mxgemm_kernel(
+    const GemmParams p) {
+    __shared__ __align__(16) unsigned char smem[kQLds];
+    __shared__ int s_tp[ROUTED ? MOE_MAX_EXPERTS : 1];
+    __shared__ int s_wave[kQThreads / 64];
+    __shared__ int s_arow[kQBM];
+
+    const int NB = PAIR ? kQBR / 2 : kQBR;                  // output columns per item
+    const int NT = (p.N + NB - 1) / NB;
+    const int total_mt = ROUTED ? build_tile_prefix<kQThreads, kQBM>(p.offsets, p.E, p.R, s_tp, s_wave)
+                                : (p.T + kQBM - 1) / kQBM;
+    const int items = total_mt * NT;
+    // Work units: whole items while they fill rounds of G workgroups; the items of a last,
+    // partial round are split by rows into f parts (f = 2 or 4, as many as the idle
+    // workgroups allow), so that round takes a fraction of an item's time.
+    const int G = gridDim.x;
+    const int full = items / G * G, tail = items - full;
+    const int f = tail > 0 && 4 * tail <= G ? 4 : (tail > 0 && 2 * tail <= G ? 2 : 1);
+    const int units = full + f * tail;
+    // Each round of G workgroups hands XCD x (workgroups x, x+8, ...) a contiguous run of G/8
+    // units: units are ordered expert by expert, then by column tile, then by row tile (and
+    // part), so the row tiles that share a column tile of weights run at the same time on the
+    // same XCD and take those weight bytes from its L2.
+    const int slot = xcd_slot(blockIdx.x, G);
+
+    for (int un = slot; un < units; un += G) {
+        int item = un, part = 0, nparts = 1;
+        if (un >= full) {
+            item = full + (un - full) / f;
+            part = (un - full) % f;
+            nparts = f;
+        }
+        QUnit u;
+        int tile = 0, nt = 0;
+        u.e = 0;
+        u.row0 = 0;
+        u.M = p.T;
+        if constexpr (ROUTED) {
+            u.e = tile_expert(s_tp, p.E, item / NT);
+            const int tpx = u.e > 0 ? s_tp[u.e - 1] : 0, te = s_tp[u.e] - tpx;
+            const int r = item - NT * tpx;
+            nt = r / te;
+            tile = r - nt * te;
+            u.row0 = p.offsets[u.e];
+            u.M = p.offsets[u.e + 1] - u.row0;
+        } else {
+            nt = item / total_mt;
+            tile = item - nt * total_mt;
+        }
+        const int plen = kQBM / nparts;
+        u.m0 = tile * kQBM + part * plen;
+        u.n0 = nt * NB;
+        const int live = min(u.M - u.m0, plen);
+        if (live <= 0) continue;                             // a part past the expert's last row
+        const int TM = __builtin_amdgcn_readfirstlane(live > 128 ? 4 : (live > 64 ? 2 : 1));
+        // source row of each A row of the unit (rows past the expert's end repeat its last row)
+        for (int r = threadIdx.x; r < kQBM; r += kQThreads) {
+            int src = u.row0 + min(u.m0 + r, u.M - 1);
+            if (p.gather) src = p.sorted_pairs[src] / p.k;
+            s_arow[r] = min(max(src, 0), p.n_arows - 1);
+        }
+        __syncthreads();
+        if (TM == 4) qgemm_unit<PAIR, 4>(p, u, smem, s_arow);
+        else if (TM == 2) qgemm_unit<PAIR, 2>(p, u, smem, s_arow);
+        else qgemm_unit<PAIR, 1>(p, u, smem, s_arow);
+        __syncthreads();                                     // the unit is done with s_arow and LDS
+    }
+}
+
 // The matrix-core GEMM serves MX-quantised activations when there are enough rows per
-// expert to fill 128-row tiles at least partly (prefill); decode sizes use the GEMV.
+// expert to fill its row tiles at least partly (prefill); decode sizes use the GEMV.
 bool mfma_path_wanted(const moe_expert_weights *w, int act, int T, int k, bool routed) {
     (void)k;
     (void)routed;
@@ -459,7 +477,7 @@ static int resident_workgroups() {
     if (cache[dev] == 0) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mxgemm_kernel<PAIR, ROUTED>, kGThreads, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mxgemm_kernel<PAIR, ROUTED>, kQThreads, 0) !=
                 hipSuccess ||
             per_cu <= 0)
             per_cu = 1;
@@ -468,21 +486,22 @@ static int resident_workgroups() {
     return cache[dev];
 }
 
-// Persistent launch: at most one wave of resident workgroups, each walking the (row tile,
-// column tile) items with a stride of the grid size.  `mt_bound` bounds the row tiles.
+// Persistent launch: at most one wave of resident workgroups, each walking the work units
+// with a stride of the grid size.  `mt_bound` bounds the row tiles (4 parts each at most).
 template <bool PAIR, bool ROUTED>
 static moe_status gemm_launch(const GemmParams &p, int mt_bound, hipStream_t stream, const char *what) {
-    const int64_t items = (int64_t)mt_bound * ((p.N + kGBN - 1) / kGBN);
-    const int64_t g = std::min<int64_t>(items, resident_workgroups<PAIR, ROUTED>());
+    const int NB = PAIR ? kQBR / 2 : kQBR;
+    const int64_t units = 4 * (int64_t)mt_bound * ((p.N + NB - 1) / NB);
+    const int64_t g = std::min<int64_t>(units, resident_workgroups<PAIR, ROUTED>());
     if (g <= 0) return MOE_OK;
-    hipLaunchKernelGGL((mxgemm_kernel<PAIR, ROUTED>), dim3((unsigned)g), dim3(kGThreads), 0, stream, p);
+    hipLaunchKernelGGL((mxgemm_kernel<PAIR, ROUTED>), dim3((unsigned)g), dim3(kQThreads), 0, stream, p);
     return launch_check(what);
 }
 
 static int tile_slots(const moe_expert_weights *w, int T, int R, bool routed) {
-    if (!routed) return (T + kGBM - 1) / kGBM;
+    if (!routed) return (T + kQBM - 1) / kQBM;
     const int ne = w->num_experts < R ? w->num_experts : R;
-    return ne + R / kGBM;            // >= sum over experts of ceil(M_e / 128)
+    return ne + R / kQBM;            // >= sum over experts of ceil(M_e / 256)
 }
 
 moe_status mfma_gateup_launch(const moe_expert_weights *w, int T, int k, const uint8_t *xq, const uint8_t *xs,
