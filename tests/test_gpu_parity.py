@@ -70,6 +70,26 @@ def test_dequant_mxfp4_every_code_and_scale_bitexact(dev, M):
     _bits_equal(to_np(g), OF.dequant_mxfp4(codes, scales))
 
 
+def test_dequant_bf16_product_decode_every_code_and_scale_bitexact(dev, M):
+    """The scaled FP4 -> bf16 conversion that every matrix-core kernel multiplies, over all 16
+    codes x 256 scale bytes, against the oracle's exact value rounded to bf16: E2M1(code) times a
+    power of two is a bf16 value unless it leaves bf16's range, which only scale byte 254 with
+    |value| >= 2 reaches (rounded to infinity); byte 255 is NaN."""
+    codes = np.tile(np.arange(256, dtype=np.uint8), (256, 1))
+    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], 16, axis=1)
+    g = M.moe_dequant_bf16(torch.from_numpy(codes).to(dev), torch.from_numpy(scales).to(dev))
+    ref64 = OF.dequant_mxfp4(codes, scales)
+    ref = torch.from_numpy(ref64).to(torch.bfloat16)
+    finite = np.isfinite(ref.float().numpy())
+    # the oracle values are bf16 values wherever bf16 holds them (no rounding happened)
+    np.testing.assert_array_equal(ref.double().numpy()[finite], ref64[finite])
+    gb, rb = g.cpu().view(torch.int16).numpy(), ref.view(torch.int16).numpy()
+    nan = np.isnan(ref64)
+    assert (np.isnan(g.cpu().float().numpy()) == nan).all()
+    bad = np.argwhere((gb != rb) & ~nan)
+    assert bad.size == 0, f"{len(bad)} values differ, first (scale byte, element): {bad[:8].tolist()}"
+
+
 def test_dequant_fp8_every_code_bitexact(dev, M):
     r = np.arange(256)
     codes = ((r[:, None] + r[None, :]) % 256).astype(np.uint8)
@@ -120,6 +140,8 @@ ROUTE_CASES = {
     "prefill_router_zipf": (synth.get("qwen38max_prefill"), 0),
     "fp8_router_sigmoid": (synth.get("glm52_fp8"), 0),
     "tiny_no_renorm": (tiny(renormalize=False, routed_scaling=2.5), 0),
+    "tiny_sigmoid_no_renorm": (tiny(score="sigmoid", select_bias_std=0.01, k=3, renormalize=False,
+                                    routed_scaling=2.5), 0),
     # tiled float64 router (T >= 32, H a multiple of 512): ragged token and row tiles
     "tiled_ragged_gated": (tiny(name="rt", T=300, H=1024, E=200, k=6, shared="gated"), 3),
     "tiled_min_tokens": (tiny(name="rt32", T=32, H=512, E=130, k=4), 4),
@@ -329,6 +351,9 @@ LAYER_CASES = {
                              I=256, T=9, k=3, shared="ungated", shared_K=256, shared_I=128),
     "tiny_latent": tiny(name="tl", wtag=86, latent=128, H=512, I=96, shared="ungated", shared_K=512,
                         shared_I=64),
+    # LatentMoE with a gated shared expert: the gate scales the shared output added after P_u
+    "tiny_latent_gated": tiny(name="tlg", wtag=89, latent=128, H=512, I=96, shared="gated", shared_K=512,
+                              shared_I=64),
     # decode fusion (T <= 4, shared d_ff == d_ff): fused gate/up + down-combine calls
     "tiny_fused_gated": tiny(name="tfg", wtag=87, T=3, k=3, shared="gated", shared_K=256, shared_I=128),
     "tiny_fused_fp8_ungated": tiny(name="tff", wtag=88, wfmt="fp8b128", score="sigmoid", select_bias_std=0.01,
@@ -441,9 +466,47 @@ def test_down_combine_drops_invalid_pairs(dev, M):
 
 # ------------------------------------------------------------------ MX activation mode, stage by stage
 
+E2M1_MIDPOINTS = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+FLIP_BOUND = 2.0 ** -16
+
+
+def _mx_flip_distances(h_ref, hq, hs):
+    """Where the GPU's MX codes of h (hq, hs) decode to another value than the oracle's own
+    quantisation of its float64 h_ref: the relative distance of the quantity that decided the
+    code from its rounding boundary.  A different scale byte is decided by the block maximum
+    against a power of two (the exponent is floor(log2 amax) - 2); a different element with the
+    same scale by |v| / 2^X against the nearest E2M1 rounding midpoint."""
+    rq, rs = OF.mx_quantize(h_ref)
+    diff = OF.mx_dequantize(hq, hs) != OF.mx_dequantize(rq, rs)
+    d = []
+    for r, c in zip(*np.nonzero(diff)):
+        b = c // 32
+        if hs[r, b] != rs[r, b]:
+            amax = np.abs(h_ref[r, 32 * b:32 * b + 32]).max()
+            p2 = 2.0 ** np.round(np.log2(amax))
+            d.append(abs(amax - p2) / p2)
+        else:
+            a = abs(h_ref[r, c]) / 2.0 ** (int(rs[r, b]) - 127)
+            m = E2M1_MIDPOINTS[np.argmin(np.abs(E2M1_MIDPOINTS - a))]
+            d.append(abs(a - m) / m)
+    return np.array(d)
+
+
+def _check_flips(h_ref, hq, hs, what):
+    d = _mx_flip_distances(h_ref, hq, hs)
+    say(f"  {what}: {len(d)} h values differ from the oracle's own quantisation, "
+        f"max distance from the rounding boundary {d.max() if len(d) else 0.0:.2e} (bound 2^-16)")
+    assert (d < FLIP_BOUND).all(), f"{what}: a code differs {d.max():.3e} away from its rounding boundary"
+    return len(d)
+
+
+
 def _stagewise_mx(M, cfg, dev, tokens=None):
     """Stage-wise parity of the MX-activation FFN (codes of x exact; g/u within tolerance; oracle's
-    quantiser on the GPU's h gives the GPU's h codes; down within tolerance on the GPU's h codes)."""
+    quantiser on the GPU's h gives the GPU's h codes; down within tolerance on the GPU's h codes;
+    every h code that differs from the oracle's own quantisation lies within 2^-16 of a rounding
+    boundary).  `tokens`: check the h and y rows of these tokens only (the codes of every row are
+    still checked against the oracle's quantiser)."""
     t, inp = build(cfg, dev)
     w = layer_weights(cfg, t)
     r = OL.route(inp.x, inp.w_router, cfg.k, cfg.score, cfg.renormalize, cfg.routed_scaling, inp.logit_bias)
@@ -479,10 +542,8 @@ def _stagewise_mx(M, cfg, dev, tokens=None):
         y_ref[sel] = hdeq[rows[sel]] @ D.T
     assert_close(h[rows], h_ref, f"{cfg.name} mx h")
     assert_close(y[rows], y_ref, f"{cfg.name} mx y_rows (on GPU h codes)")
-    # end to end against the oracle's own h codes: report code flips (near-ties only)
-    flips = int((OF.mx_quantize(h_ref)[0] != hq[rows]).sum())
-    say(f"  {cfg.name}: {flips} h code bytes differ from the oracle's own quantisation")
-    return flips
+    # end to end against the oracle's own h codes: a differing code is a near-tie
+    return _check_flips(h_ref, hq[rows], hs[rows], f"{cfg.name} h codes")
 
 
 def test_mx_activation_tiny_stagewise(dev, M):
@@ -503,28 +564,52 @@ def test_mx_gemm_stagewise(dev, M, name):
     _stagewise_mx(M, MX_GEMM_CASES[name], dev)
 
 
-def test_mx_gemm_layer_with_gated_shared_end_to_end(dev, M):
-    cfg = tiny(name="g4", wtag=94, act="mxfp4", T=96, H=256, I=128, E=8, k=2, shared="gated", shared_K=256,
-               shared_I=160)
+def _mx_layer_end_to_end(M, cfg, dev):
+    """A whole MX-activation layer step: ids exact; the output within tolerance of the oracle's
+    layer with the GPU's h codes (routed and shared) substituted for its own; every h code that
+    differs from the oracle's own quantisation a near-tie (within 2^-16 of its boundary)."""
     layer, out, inp = _run_layer(M, cfg, dev)
     ge, gs = host_expert_getter(cfg)
     ref = OL.layer(cfg, inp, ge, gs)
     np.testing.assert_array_equal(to_np(layer.ids), ref.routing.ids)
-    # end to end against the oracle's own h quantisation: a near-tie may flip a code, so
-    # the bound is the per-element one; the stage-wise tests pin each stage exactly
-    g, r = to_np(out).astype(np.float64), ref.out
-    rel = np.linalg.norm(g - r) / np.linalg.norm(r)
-    say(f"  mx layer end to end rel_l2={rel:.3e}")
-    assert rel < 1e-3
+    hq, hs = to_np(layer.hq), to_np(layer.hs)
+    perm, r = ref.perm, ref.routing
+    aq = OF.mx_dequantize(*OF.mx_quantize(OF.bf16_value(inp.x)))
+    hdeq = OF.mx_dequantize(hq, hs)
+    y_rows = np.zeros((len(perm.sorted_pairs), cfg.d_model))
+    h_ref = np.zeros((len(perm.sorted_pairs), cfg.I))
+    for e in range(cfg.E):
+        r0, r1 = int(perm.expert_offsets[e]), int(perm.expert_offsets[e + 1])
+        if r0 == r1:
+            continue
+        G, U, D = OL.dequant_expert(ge(e))
+        a = aq[perm.sorted_pairs[r0:r1] // cfg.k]
+        h_ref[r0:r1] = OL.silu(a @ G.T) * (a @ U.T)
+        y_rows[r0:r1] = hdeq[r0:r1] @ D.T
+    nflip = _check_flips(h_ref, hq, hs, f"{cfg.name} routed h")
+    y_s = None
+    if cfg.shared:
+        G, U, D = OL.dequant_expert(gs())
+        hsq, hss = (to_np(layer.hq_sh), to_np(layer.hs_sh)) if layer.hq_sh is not None else (None, None)
+        if hsq is None:                      # decode-sized steps run the shared expert in the fused call
+            y_s = ref.y_shared
+        else:
+            nflip += _check_flips(OL.silu(aq @ G.T) * (aq @ U.T), hsq, hss, f"{cfg.name} shared h")
+            y_s = OF.mx_dequantize(hsq, hss) @ D.T
+    want = OL.combine(y_rows, perm.pair_to_row, r.weights, cfg.k, y_s, r.shared_gate)
+    assert_close(to_np(out), want, f"{cfg.name} out (oracle on the GPU's h codes)")
+    if nflip == 0:
+        assert_close(to_np(out), ref.out, f"{cfg.name} out (oracle's own h codes)")
+
+
+def test_mx_gemm_layer_with_gated_shared_end_to_end(dev, M):
+    _mx_layer_end_to_end(M, tiny(name="g4", wtag=94, act="mxfp4", T=96, H=256, I=128, E=8, k=2, shared="gated",
+                                 shared_K=256, shared_I=160), dev)
 
 
 def test_mx_activation_layer_tiny_end_to_end(dev, M):
-    cfg = tiny(name="tmx2", wtag=88, act="mxfp4", shared="gated", shared_K=256, shared_I=128)
-    layer, out, inp = _run_layer(M, cfg, dev)
-    ge, gs = host_expert_getter(cfg)
-    ref = OL.layer(cfg, inp, ge, gs)
-    np.testing.assert_array_equal(to_np(layer.ids), ref.routing.ids)
-    assert_close(to_np(out), ref.out, "tiny mx layer out")
+    _mx_layer_end_to_end(M, tiny(name="tmx2", wtag=88, act="mxfp4", shared="gated", shared_K=256, shared_I=128),
+                         dev)
 
 
 # ------------------------------------------------------------------ full-size workloads
@@ -585,6 +670,16 @@ def test_prefill_mx_full_size_stagewise_sampled(dev, M):
     cfg = synth.get("qwen38max_prefill")
     say("prefill, MX activations, stage-wise on sampled tokens")
     _stagewise_mx(M, cfg, dev, tokens=[3, 300])
+
+
+def test_prefill_hot_mx_full_size_stagewise(dev, M):
+    """The compute-bound prefill slice at full size (512 tokens on the same 10 experts, 512 rows
+    each): the codes of every h row against the oracle's quantiser, and h and y of tokens
+    200 .. 327 -- 128 consecutive rows of every expert, across the boundary between its two
+    256-row tiles -- against the oracle."""
+    cfg = synth.get("qwen38max_prefill_hot")
+    say("hot prefill, MX activations, stage-wise on 128 rows of every expert")
+    _stagewise_mx(M, cfg, dev, tokens=list(range(200, 328)))
 
 
 @pytest.mark.parametrize("name,sample", [("qwen38max_prefill_hot_float", [0, 129, 511]),
