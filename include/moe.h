@@ -137,6 +137,23 @@ moe_status moe_route_permute(const moe_route_desc *desc, const void *x, const vo
                              int32_t *pair_to_row, void *ws, size_t ws_bytes, moe_stream stream);
 
 /*
+ * moe_route_permute_noalloc -- moe_route_permute without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Arguments, results and errors are those of
+ * moe_route_permute; the routing scratch (moe_route_workspace(desc) bytes) lives instead in
+ * a static device array of 8 MiB inside the library, one per GPU, held until the process
+ * ends.  A request needing more scratch than that returns MOE_ERR_UNSUPPORTED before
+ * anything is enqueued.  The call allocates nothing.  Every call on a GPU uses that GPU's
+ * one array: calls that overlap in time on the same GPU (different streams or threads)
+ * race and must be ordered by the caller.
+ */
+moe_status moe_route_permute_noalloc(const moe_route_desc *desc, const void *x, const void *w_router,
+                                     const float *logit_bias, const float *select_bias,
+                                     const void *w_shared_gate, int32_t *topk_ids, float *topk_w,
+                                     float *shared_gate, int32_t *expert_offsets, int32_t *sorted_pairs,
+                                     int32_t *pair_to_row, moe_stream stream);
+
+/*
  * Expert weights for E experts (or one shared expert), stacked along the expert axis.
  *   MOE_W_MXFP4:          gate, up: codes uint8 [E][d_ff][d_model/2], scales uint8 E8M0
  *                         [E][d_ff][d_model/32]; down: codes [E][d_model][d_ff/2], scales

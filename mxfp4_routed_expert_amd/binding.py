@@ -66,6 +66,7 @@ _sig("moe_route_workspace", _sz, ctypes.POINTER(RouteDesc))
 _sig("moe_permute", _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _sz, _p)
 _sig("moe_route_permute", _i32, ctypes.POINTER(RouteDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p)
 _sig("moe_permute_workspace", _sz, _i32, _i32, _i32)
+_sig("moe_route_permute_noalloc", _i32, ctypes.POINTER(RouteDesc), _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p)
 _sig("moe_expert_ffn", _i32, ctypes.POINTER(ExpertWeightsC), _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p, _sz, _p)
 _sig("moe_expert_ffn_workspace", _sz, ctypes.POINTER(ExpertWeightsC), _i32, _i32, _i32)
 _sig("moe_expert_gateup", _i32, ctypes.POINTER(ExpertWeightsC), _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p, _p,
@@ -83,6 +84,7 @@ _sig("moe_dequant", _i32, _i32, _i32, _i32, _p, _p, _p, _p)
 _sig("moe_mx_quantize", _i32, _i32, _i32, _p, _i32, _p, _p, _p)
 
 EXPORTS = ["moe_route", "moe_route_workspace", "moe_permute", "moe_permute_workspace", "moe_route_permute",
+           "moe_route_permute_noalloc",
            "moe_expert_ffn", "moe_expert_gateup_shared", "moe_expert_down_combine",
            "moe_expert_ffn_workspace", "moe_expert_gateup", "moe_expert_gateup_workspace", "moe_expert_down",
            "moe_combine", "moe_dense_bf16", "moe_dequant", "moe_dequant_bf16", "moe_mx_quantize", "moe_last_error",
@@ -199,6 +201,32 @@ def moe_route_permute(x, w_router, k, score="softmax", renormalize=True, routed_
     check(lib.moe_route_permute(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(logit_bias), _ptr(select_bias),
                                 _ptr(w_shared_gate), _ptr(ids), _ptr(w), _ptr(sg), _ptr(offs), _ptr(sp), _ptr(p2r),
                                 _ptr(ws), ws.numel(), _stream()))
+    return ids, w, sg, offs, sp, p2r
+
+
+def moe_route_permute_noalloc(x, w_router, k, score="softmax", renormalize=True, routed_scaling=1.0,
+                              logit_bias=None, select_bias=None, w_shared_gate=None, out=None, n_group=1,
+                              topk_group=1):
+    """moe_route_permute with the library's static scratch instead of a workspace.  `out` as for
+    moe_route_permute (allocated here, by torch, when None)."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    _need(x, torch.bfloat16, "x")
+    _need(w_router, torch.bfloat16, "w_router", (E, H))
+    _need(logit_bias, torch.float32, "logit_bias", (E,))
+    _need(select_bias, torch.float32, "select_bias", (E,))
+    _need(w_shared_gate, torch.bfloat16, "w_shared_gate", (H,))
+    d = RouteDesc(T, H, E, k, SCORE[score], 1 if renormalize else 0, routed_scaling, n_group, topk_group)
+    dev = x.device
+    if out is None:
+        out = (torch.empty((T, k), dtype=torch.int32, device=dev), torch.empty((T, k), dtype=torch.float32, device=dev),
+               torch.empty((T,), dtype=torch.float32, device=dev) if w_shared_gate is not None else None,
+               torch.empty((E + 1,), dtype=torch.int32, device=dev), torch.empty((T * k,), dtype=torch.int32, device=dev),
+               torch.empty((T * k,), dtype=torch.int32, device=dev))
+    ids, w, sg, offs, sp, p2r = out
+    check(lib.moe_route_permute_noalloc(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(logit_bias),
+                                        _ptr(select_bias), _ptr(w_shared_gate), _ptr(ids), _ptr(w), _ptr(sg),
+                                        _ptr(offs), _ptr(sp), _ptr(p2r), _stream()))
     return ids, w, sg, offs, sp, p2r
 
 

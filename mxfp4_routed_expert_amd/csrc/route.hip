@@ -10,6 +10,8 @@
 #include <limits.h>
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 
 namespace moe {
@@ -623,4 +625,59 @@ extern "C" moe_status moe_route_permute(const moe_route_desc *d, const void *x, 
     MOE_TRY(launch_topk(d, (const float *)ws, rows, logit_bias, select_bias, w_shared_gate != nullptr, topk_ids,
                         topk_w, shared_gate, nullptr, nullptr, nullptr, s));
     return moe_permute(d->T, d->k, d->E, topk_ids, expert_offsets, sorted_pairs, pair_to_row, nullptr, 0, stream);
+}
+
+// ------------------------------------------------------------------ no-allocation entry point
+// moe_route_permute_noalloc keeps the routing scratch (float32 logits, and for the tiled
+// router its float64 split-K partials) in this file-scope device array instead of a
+// caller-provided workspace.  Each GPU holds its own copy, at its own address, until the
+// process ends; host code uses that address (from hipGetSymbolAddress, once per device),
+// never the array's name.  Every call on a GPU shares the array: the kernels overwrite all
+// of it that they read, so nothing needs clearing, and calls that overlap on one GPU race.
+constexpr size_t kRouteScratchBytes = (size_t)8 << 20;
+static __device__ __align__(256) unsigned char scratch[kRouteScratchBytes];
+
+namespace {
+
+constexpr int kScratchMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kScratchMaxDevices] = {};
+
+// This device's address of `scratch`, looked up on its first use with the device current.
+moe_status route_scratch(void **out) {
+    int dev = -1;
+    MOE_TRY(hip_check(hipGetDevice(&dev), "moe_route_permute_noalloc: hipGetDevice"));
+    if (dev < 0 || dev >= kScratchMaxDevices) {
+        set_error("moe_route_permute_noalloc: device %d outside [0, %d)", dev, kScratchMaxDevices);
+        return MOE_ERR_UNSUPPORTED;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[dev]) {
+        void *p = nullptr;
+        MOE_TRY(hip_check(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)), "moe_route_permute_noalloc: hipGetSymbolAddress"));
+        g_scratch[dev] = p;
+    }
+    *out = g_scratch[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" moe_status moe_route_permute_noalloc(const moe_route_desc *d, const void *x, const void *w_router,
+                                                const float *logit_bias, const float *select_bias,
+                                                const void *w_shared_gate, int32_t *topk_ids, float *topk_w,
+                                                float *shared_gate, int32_t *expert_offsets, int32_t *sorted_pairs,
+                                                int32_t *pair_to_row, moe_stream stream) {
+    clear_error();
+    MOE_TRY(validate_route(d));
+    const size_t need = moe_route_workspace(d);
+    if (need > kRouteScratchBytes) {
+        set_error("moe_route_permute_noalloc: T = %d, E = %d need %zu bytes of scratch, more than the %zu it holds",
+                  d->T, d->E, need, kRouteScratchBytes);
+        return MOE_ERR_UNSUPPORTED;
+    }
+    void *ws = nullptr;
+    if (d->T > 0) MOE_TRY(route_scratch(&ws));
+    return moe_route_permute(d, x, w_router, logit_bias, select_bias, w_shared_gate, topk_ids, topk_w, shared_gate,
+                             expert_offsets, sorted_pairs, pair_to_row, ws, kRouteScratchBytes, stream);
 }

@@ -244,3 +244,13 @@ def test_layer_fusion_rule():
     assert not fuses(w(shared=NS(fmt="mxfp4", d_model=7168, d_ff=1024)), 1)
     assert not fuses(w(shared=NS(fmt="fp8b128", d_model=7168, d_ff=2368)), 1)
     assert not fuses(w(k=16, experts=NS(fmt="mxfp4", d_model=7168, d_ff=4096), shared=None), 1)  # LDS
+
+
+def test_route_permute_noalloc_refuses_more_than_its_scratch():
+    """A request whose routing scratch exceeds the static array is refused on the host, before
+    anything touches the GPU (here 5000 x 2049 float32 logits, about 41 MB)."""
+    d = _desc(T=5000, H=512, E=2048, k=8)
+    st = lib.moe_route_permute_noalloc(ctypes.byref(d), DUMMY, DUMMY, None, None, None, DUMMY, DUMMY, None, DUMMY,
+                                       DUMMY, DUMMY, None)
+    assert st == B.MOE_ERR_UNSUPPORTED
+    assert "scratch" in B.last_error()
