@@ -18,7 +18,9 @@
 // K advances in steps of 256 values: every operand row contributes one whole 128-byte
 // line per step.  A step's A rows (gathered token rows), B rows (weight rows) and scale
 // windows go from global memory straight into LDS (global_load_lds), two steps resident
-// (2 x 72 KB), the next one in flight while the matrix cores work on the current one.
+// (2 x 72 KB): the copies of the next step are issued a piece at a time between the
+// matrix instructions of the current one, rather than in one burst that would hold the
+// wave's instruction stream while the L1 accepts them.
 // Small row counts: an item whose live rows fit 128 (or 64) runs with 2 (or 1) row tiles
 // per wave, so all four waves share the smaller tile; and when the last round of items
 // would leave CUs idle, its items are split into halves or quarters by rows.
@@ -182,32 +184,34 @@ MOE_DEV void qgemm_unit(const GemmParams &p, const QUnit &u, unsigned char *smem
         return rel - o + ((uint32_t)sd <= need ? 4u * sd : 0u);
     };
 
-    // Issue the copies of step s into stage `st`.  In the last step, chunks past the end of
-    // a row are clamped to its last block (read, never used) and the scale windows shrink.
-    auto issue = [&](int s, int st) {
+    // Copies of step s into stage s % 2 (a step past the last copies the last step's bytes into
+    // the stage no step reads any more), as 24 pieces per wave: 0-7 A codes (pieces past the
+    // 2*TM this unit needs repeat its first one: same bytes to the same place, so every step
+    // issues the same number), 8-15 B codes, 16-23 scale windows.  In the last step, chunks
+    // past the end of a row are clamped to its last block (read, never used) and the scale
+    // windows shrink.
+    auto issue_piece = [&](int s_in, int pc) {
+        const int s = min(s_in, S - 1);           // past the last step: its bytes again (never read)
         const bool last = s == S - 1;
-        const uint8_t *ab = a_base + 128 * s, *bb = b_base + 128 * s;
+        const int st = s_in & 1;
         const uint32_t cmax = 16u * (uint32_t)(Kb - 1 - 8 * s);   // last valid chunk (bytes) in the step
-        unsigned char *adst = smem + kQOffA + st * kQA + wave * 16 * TM * kQRowB;
-        unsigned char *bdst = smem + kQOffB + st * kQB + 64 * wave * kQRowB;
-#pragma unroll
-        for (int t = 0; t < NA; ++t) {
+        if (pc < 8) {
+            const int t = pc < NA ? pc : 0;
             uint32_t v = aoff[t];
             if (last) v = v - 16 * achunk[t] + min(16u * achunk[t], cmax);
-            dma16(ab, v, adst + t * 1024);
-        }
-#pragma unroll
-        for (int t = 0; t < 8; ++t) {
+            dma16(a_base + 128 * s, v, smem + kQOffA + st * kQA + wave * 16 * TM * kQRowB + t * 1024);
+        } else if (pc < 16) {
+            const int t = pc - 8;
             uint32_t v = boff[t];
             if (last) v = v - 16 * bchunk[t] + min(16u * bchunk[t], cmax);
-            dma16(bb, v, bdst + t * 1024);
+            dma16(b_base + 128 * s, v, smem + kQOffB + st * kQB + 64 * wave * kQRowB + t * 1024);
+        } else {
+            const int i = pc - 16;
+            dma4(sc_base + 8 * s, sc_voff(sc_rel[i], last ? nvalid : 8),
+                 smem + kQOffS + st * kQS + 128 * wave * kQSlot + i * 256);
         }
-        const int len = last ? nvalid : 8;
-        const uint8_t *sb = sc_base + 8 * s;
-        unsigned char *sdst = smem + kQOffS + st * kQS + 128 * wave * kQSlot;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) dma4(sb, sc_voff(sc_rel[i], len), sdst + i * 256);
     };
+    constexpr int kPieces = 24;
 
     // ---- consumer side.  Row tiles of this wave: rows 32*TM*wm + 32i (i < TM) of the unit;
     // weight tiles jb: the pair's gate columns 64wn + 32j (jb = j) and up columns (jb = 2 + j);
@@ -250,8 +254,12 @@ MOE_DEV void qgemm_unit(const GemmParams &p, const QUnit &u, unsigned char *smem
     // scale byte 0 on both operands: each of their products is at most 36 * 2^-254 in
     // magnitude, far below float32's smallest subnormal (2^-149), so it adds an exact zero
     // (their codes are real codes of a clamped block, never NaN or infinite: E2M1 has none).
+    // The copies of step s+1 go out during the first half of step s's products, a piece after
+    // every few of them: issued in one burst they would hold back the wave's matrix
+    // instructions while the L1 takes them; spread over the step they land before its end.
     auto step = [&](int s) {
         const int so = s & 1;
+
         uint32_t sa[TM], sb[4];
 #pragma unroll
         for (int i = 0; i < TM; ++i) sa[i] = scale4(sa_at[i] + so * kQS, sa_o[i]);
@@ -278,6 +286,7 @@ MOE_DEV void qgemm_unit(const GemmParams &p, const QUnit &u, unsigned char *smem
         auto quarter = [&](auto q_c) {
             constexpr int Q = decltype(q_c)::value;
             if constexpr (Q < 3) rd(Q + 1, fa[(Q + 1) & 1], fb[(Q + 1) & 1]);
+            constexpr int NH = 8 * TM;             // products in the first half of the step
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -287,6 +296,12 @@ MOE_DEV void qgemm_unit(const GemmParams &p, const QUnit &u, unsigned char *smem
                         i32x8_t{(int)av[0], (int)av[1], (int)av[2], (int)av[3], 0, 0, 0, 0},
                         i32x8_t{(int)bv[0], (int)bv[1], (int)bv[2], (int)bv[3], 0, 0, 0, 0}, acc[i][jb], 4, 4, Q,
                         (int)sa[i], Q, (int)sb[jb]);
+                    if constexpr (Q < 2) {
+                        const int m = Q * 4 * TM + 4 * i + jb;
+#pragma unroll
+                        for (int pc = m * kPieces / NH; pc < (m + 1) * kPieces / NH; ++pc) issue_piece(s + 1, pc);
+                        __builtin_amdgcn_sched_barrier(0);
+                    }
                 }
         };
         rd(0, fa[0], fb[0]);
@@ -297,13 +312,14 @@ MOE_DEV void qgemm_unit(const GemmParams &p, const QUnit &u, unsigned char *smem
     };
 
     // ---- pipeline: two stages.  At the top of step s its copies have landed and every wave
-    // is done with step s-1, whose stage then takes the copies of step s+1.
-    issue(0, 0);
+    // is done with step s-1, whose stage takes the copies of step s+1 during step s.
+#pragma unroll
+    for (int pc = 0; pc < kPieces; ++pc) issue_piece(0, pc);
     for (int s = 0; s < S; ++s) {
         wait_copies_and_barrier();
-        if (s + 1 < S) issue(s + 1, (s + 1) & 1);
-        step(s);
+        step(s);                                  // issues the copies of step s + 1 as it goes
     }
+    wait_copies_and_barrier();                    // no copy in flight past this point
     __syncthreads();                              // every wave is done with the stages
 
     // ---- epilogue.  Lane l holds C[8(v/4) + 4(l/32) + v%4][l%32] of each 32x32 tile.

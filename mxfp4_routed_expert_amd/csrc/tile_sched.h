@@ -10,10 +10,11 @@
 namespace moe {
 
 // Inclusive prefix over experts of their BM-row tile counts: tp[e] = tiles of experts
-// 0..e.  Offsets outside [0, R] (or decreasing) give the expert no tiles.  Returns the
-// total; every thread of the THREADS-wide workgroup must call it (it synchronises).
-template <int THREADS, int BM>
-MOE_DEV int build_tile_prefix(const int32_t *offsets, int E, int R, int *tp, int *s_wave) {
+// 0..e (TP = int, or uint16_t where LDS is tight: R / BM + E < 65536).  Offsets outside
+// [0, R] (or decreasing) give the expert no tiles.  Returns the total; every thread of the
+// THREADS-wide workgroup must call it (it synchronises).
+template <int THREADS, int BM, typename TP>
+MOE_DEV int build_tile_prefix(const int32_t *offsets, int E, int R, TP *tp, int *s_wave) {
     constexpr int kPer = (MOE_MAX_EXPERTS + THREADS - 1) / THREADS;   // experts per thread
     const int tid = threadIdx.x, lane = lane_id(), wave = wave_id();
     int t[kPer], sum = 0;
@@ -44,20 +45,21 @@ MOE_DEV int build_tile_prefix(const int32_t *offsets, int E, int R, int *tp, int
     for (int u = 0; u < kPer; ++u) {
         run += t[u];
         const int e = tid * kPer + u;
-        if (e < E) tp[e] = run;
+        if (e < E) tp[e] = (TP)run;
     }
     __syncthreads();
     return total;
 }
 
 // Expert owning row tile mt: the first e with tp[e] > mt (E <= 64 * 32: two probes).
-MOE_DEV int tile_expert(const int *tp, int E, int mt) {
+template <typename TP>
+MOE_DEV int tile_expert(const TP *tp, int E, int mt) {
     const int lane = lane_id();
     const int probe = min(lane * 32 + 31, E - 1);
-    const uint64_t m1 = __ballot(lane * 32 < E && tp[probe] > mt);
+    const uint64_t m1 = __ballot(lane * 32 < E && (int)tp[probe] > mt);
     const int c = __ffsll((long long)m1) - 1;                  // chunk of 32 experts
     const int e2 = c * 32 + (lane & 31);
-    const uint64_t m2 = __ballot(lane < 32 && e2 < E && tp[min(e2, E - 1)] > mt);
+    const uint64_t m2 = __ballot(lane < 32 && e2 < E && (int)tp[min(e2, E - 1)] > mt);
     return c * 32 + __ffsll((long long)m2) - 1;
 }
 
