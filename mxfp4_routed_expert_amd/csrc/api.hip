@@ -25,6 +25,19 @@ moe_status hip_check(hipError_t e, const char *what) {
 
 moe_status launch_check(const char *what) { return hip_check(hipGetLastError(), what); }
 
+int device_cu_count() {
+    constexpr int kMaxDev = 64;
+    static int cache[kMaxDev] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return 256;
+    if (cache[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+        cache[dev] = cus;
+    }
+    return cache[dev];
+}
+
 }  // namespace moe
 
 extern "C" const char *moe_last_error(void) { return moe::g_err; }

@@ -7,6 +7,9 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 #include "moe.h"
 
 #define MOE_DEV __device__ __forceinline__
@@ -61,6 +64,27 @@ MOE_DEV bf16x8 fp4x8_scaled_bf16(uint32_t w, float sc) {
     return pack8(__builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 0), __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 1),
                  __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 2), __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, sc, 3));
 }
+// f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N - 1>{}): an unrolled
+// loop whose index is a constant expression, so per-iteration register arrays indexed by it
+// stay in registers.
+template <class F, int... Ds>
+MOE_DEV void static_for_impl(F &&f, std::integer_sequence<int, Ds...>) {
+    (f(std::integral_constant<int, Ds>{}), ...);
+}
+template <int N, class F>
+MOE_DEV void static_for(F &&f) {
+    static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+// Loads through the global address space.  A pointer that reaches a load through a struct
+// or a select may lose its address space; the compiler then emits flat loads, which count
+// against the LDS wait counter too, so every LDS access waits for every load in flight.
+#define MOE_GLOBAL __attribute__((address_space(1)))
+MOE_DEV u32x4 gload16_nt(const void *p) { return __builtin_nontemporal_load((const MOE_GLOBAL u32x4 *)p); }
+MOE_DEV uint32_t gload_u8(const void *p) { return *(const MOE_GLOBAL uint8_t *)p; }
+MOE_DEV uint32_t gload_u32(const void *p) { return *(const MOE_GLOBAL uint32_t *)p; }
+MOE_DEV int gload_i32(const void *p) { return *(const MOE_GLOBAL int *)p; }
+
 MOE_DEV u32x4 fp4x8_scaled_bf16_bits(uint32_t w, float sc) { return __builtin_bit_cast(u32x4, fp4x8_scaled_bf16(w, sc)); }
 
 // MFMA operand slices of one 32-code MXFP4 unit with its block scale: slice q = values 8q..8q+7.
@@ -217,6 +241,8 @@ moe_status hip_check(hipError_t e, const char *what);
 moe_status launch_check(const char *what);
 
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+// Compute units of the current device (queried once per device; 256 if the query fails).
+int device_cu_count();
 
 }  // namespace moe
 

@@ -63,6 +63,8 @@ size_t down_combine_lds(int k, bool shared, int I);
 // or bf16 hi + lo planes of dc_plane_ld(I) values.
 constexpr int kDcThreads = 512;
 constexpr int kDcMaxRows = 128;
+// The matrix-core (MXFP4) form keeps two partial sums per (slot, row): at most 64 rows.
+constexpr int kDmMaxRows = kDcMaxRows / 2;
 __host__ __device__ constexpr int dc_plane_ld(int I) { return (I + 255) / 256 * 256; }
 void down_combine_mfma_launch(const DownCombineParams &p, dim3 grid, size_t lds, hipStream_t stream);
 

@@ -18,6 +18,8 @@
 //   * a workgroup owns one expert and a range of rows; the expert is found from
 //     expert_offsets on the device (the slot-th expert that has rows), so no host
 //     synchronisation is needed and empty experts cost nothing.
+#include <algorithm>
+
 #include "gemv.h"
 
 namespace moe {
@@ -444,6 +446,354 @@ __global__ MOE_GEMV_ATTR void gemv_kernel(const GemvParams p0) {
     }
 }
 
+// ------------------------------------------------------------------ flat schedule
+// Decode-sized launches (at most kFlatMaxTok float or bf16 activation rows): one workgroup of
+// kFlatThreads threads per CU.  The launch's work is a list of passes -- rows_per_pass matrix
+// rows of one slot for up to MAXM of the slot's rows -- slot after slot, where a slot is a
+// routed expert that owns rows (in expert order) or the fused shared expert.  Workgroup b
+// takes the b-th of gridDim.x equal contiguous ranges of the list, and its waves take passes
+// from that range one at a time through an LDS counter.  (With several workgroups per CU the
+// oldest one's waves win the issue arbitration, and the youngest finishes last with a quarter
+// of the CU's loads in flight; one workgroup per CU keeps every wave streaming until the CU's
+// share is done.)  Every activation row is staged once per workgroup by direct global->LDS
+// copies, and the slot table -- expert, first row, rows, first pass -- is built once per
+// workgroup from expert_offsets while those copies are in flight.
+constexpr int kFlatThreads = 1024;
+constexpr int kFlatMaxTok = 8;            // activation rows staged: all of the launch's rows
+constexpr int kFlatMaxSlots = 256;        // routed rows (<= kFlatMaxSlots - 1) plus the shared slot
+constexpr size_t kFlatLdsBudget = 96 * 1024;
+
+template <int FMT, int ACT>
+MOE_DEV void stage_rows_dma(const GemvParams &p, unsigned char *smem, int rs) {
+    constexpr bool F32 = ACT == kActF32;
+    constexpr int P = act_slots<FMT, F32>();
+    const int act_vec = p.K * (F32 ? 4 : 2) / 16;
+    const int nblk = (act_vec + 63) / 64;
+    const int lane = lane_id();
+    for (int c = __builtin_amdgcn_readfirstlane(wave_id()); c < p.n_act_rows * nblk; c += kFlatThreads / 64) {
+        const int m = c / nblk, cb = c - m * nblk;
+        const int q = cb * 64 + lane;
+        const int b = q / P, sl = q - b * P;
+        const int v = q < act_vec ? b * P + (sl ^ act_swizzle<FMT, F32>(b)) : 0;
+        const u32x4 *row = (const u32x4 *)((const unsigned char *)p.act + (size_t)m * p.K * (F32 ? 4 : 2));
+        gemv_dma16(row + v, (uint32_t)(uintptr_t)(smem + (size_t)m * rs + (size_t)cb * 1024));
+    }
+}
+
+// A pass resolved to its slot: wave-uniform fields, plus this lane's matrix row n, the row's
+// index in the stacked matrix and its scale row.
+struct FlatPass {
+    int e, N, r0, m0, mc, n;
+    bool sh, live;
+    size_t ridx, srow;
+    const uint8_t *wb;
+    const void *sb;
+};
+
+// Pass P -> its slot and rows.  Scalars are passed one by one: with a struct of them the
+// compiler turns a select between two fields into a load from a selected field address,
+// and the struct then stays in scratch memory.
+template <int FMT, int MAXM>
+MOE_DEV FlatPass flat_resolve(int P, int end, int ns, int pN, int sN, int rpp, int grp, const uint8_t *w_r,
+                              const void *s_rt, const uint8_t *w_s, const void *s_s, int &cursor, const int *s_e,
+                              const int *s_r0, const int *s_m, const int *s_pass0) {
+    FlatPass f;
+    f.live = P < end;
+    if (!f.live) {                                         // no pass: loads read row 0, nothing is stored
+        f.e = f.r0 = f.m0 = f.mc = f.n = 0;
+        f.N = pN;
+        f.sh = false;
+        f.ridx = f.srow = 0;
+        f.wb = w_r;
+        f.sb = s_rt;
+        return f;
+    }
+    int cur = cursor;
+    while (cur + 1 < ns && s_pass0[cur + 1] <= P) ++cur;
+    const int sl = __builtin_amdgcn_readfirstlane(cur);
+    cursor = sl;
+    const int e = __builtin_amdgcn_readfirstlane(s_e[sl]);
+    f.sh = e < 0;
+    f.e = f.sh ? 0 : e;
+    f.N = f.sh ? sN : pN;
+    f.r0 = __builtin_amdgcn_readfirstlane(s_r0[sl]);
+    const int M = __builtin_amdgcn_readfirstlane(s_m[sl]);
+    const int rpc = max((f.N + rpp - 1) / rpp, 1);
+    const int local = P - __builtin_amdgcn_readfirstlane(s_pass0[sl]);
+    const int mch = local / rpc;
+    f.m0 = mch * MAXM;
+    f.mc = min(MAXM, M - f.m0);
+    f.n = (local - mch * rpc) * rpp + grp;
+    const int nc = min(f.n, f.N - 1);
+    f.ridx = (size_t)f.e * f.N + nc;
+    f.srow = FMT == kFmtFP8 ? (size_t)f.e * (f.N / 128) + nc / 128 : 0;
+    f.wb = f.sh ? w_s : w_r;
+    f.sb = f.sh ? s_s : s_rt;
+    return f;
+}
+
+template <int FMT, int ACT, int MAXM, bool PAIR>
+__global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParams p) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int s_e[kFlatMaxSlots], s_r0[kFlatMaxSlots], s_m[kFlatMaxSlots], s_pass0[kFlatMaxSlots + 1];
+    __shared__ int s_tok[kFlatMaxSlots];
+    __shared__ int s_ns, s_beg, s_end, s_next;
+    constexpr int NW = kFlatThreads / 64;
+    constexpr bool F32 = ACT == kActF32;
+    constexpr int ASZ = F32 ? 4 : 2;
+    constexpr int EPU = FMT == kFmtMXFP4 ? 32 : (FMT == kFmtFP8 ? 16 : 8);
+    // units per lane and batch (batches of 8 with two passes in flight measured slower)
+    constexpr int U = 4;
+    constexpr int SD = U / 4;                              // scale dwords per lane and batch (MXFP4)
+    constexpr int NSC = FMT == kFmtMXFP4 ? SD : U;         // scale registers per batch
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(wave_id());
+    // parameters in locals (a lambda that captures the parameter block by reference can make
+    // the compiler keep it in scratch memory and read its fields through pointers)
+    const int K = p.K, pN = p.N, sN = p.sN, E = p.E, R = p.R, T = p.T, kk = p.k, nl = p.nl, G = p.G;
+    const int n_act = p.n_act_rows;
+    const bool routed = p.offsets != nullptr, gather = p.gather != 0, has_sh = p.shared_slot >= 0;
+    const int32_t *offsets = p.offsets, *sorted = p.sorted_pairs;
+    float *out = p.out, *sout = p.sout;
+    const float *residual = p.residual;
+    const int rs = (K * ASZ + 1023) / 1024 * 1024;         // LDS bytes per staged row
+    const int rpp = PAIR ? 32 / G : 64 / G;
+    const int units = units_per_row<FMT>(K);
+    stage_rows_dma<FMT, ACT>(p, smem, rs);
+
+    if (wave == 0) {
+        // slots: the experts that own a valid range of rows, in expert order, then the shared
+        // expert (e = -1) over the identity rows
+        int ns = 0;
+        if (routed) {
+            int o[kMaxOffsetChunks];
+#pragma unroll
+            for (int c = 0; c < kMaxOffsetChunks; ++c) o[c] = gload_i32(offsets + min(c * 64 + lane, E));
+#pragma unroll
+            for (int c = 0; c < kMaxOffsetChunks; ++c) {
+                if (c * 64 >= E) break;
+                const int next = c + 1 < kMaxOffsetChunks ? __shfl(o[c + 1], 0, kWave) : 0;
+                int o1 = __shfl_down(o[c], 1, kWave);
+                if (lane == 63) o1 = next;
+                const int e = c * 64 + lane;
+                const bool ne = e < E && o1 > o[c] && o[c] >= 0 && o1 <= R;
+                const uint64_t mk = __ballot(ne);
+                const int at = ns + __popcll(mk & ((1ull << lane) - 1ull));
+                if (ne && at < kFlatMaxSlots - 1) {
+                    s_e[at] = e;
+                    s_r0[at] = o[c];
+                    s_m[at] = o1 - o[c];
+                }
+                ns += __popcll(mk);
+            }
+            ns = min(ns, kFlatMaxSlots - 1);
+        } else {
+            if (lane == 0) {
+                s_e[0] = 0;
+                s_r0[0] = 0;
+                s_m[0] = T;
+            }
+            ns = 1;
+        }
+        if (has_sh) {
+            if (lane == 0) {
+                s_e[ns] = -1;
+                s_r0[ns] = 0;
+                s_m[ns] = T;
+            }
+            ++ns;
+        }
+        // first pass of each slot: exclusive prefix of ceil(rows / MAXM) * ceil(N / rpp)
+        int base = 0;
+        for (int c = 0; c < ns; c += 64) {
+            const int sl = c + lane;
+            int cnt = 0;
+            if (sl < ns) {
+                const int N = s_e[sl] < 0 ? sN : pN;
+                cnt = (s_m[sl] + MAXM - 1) / MAXM * ((N + rpp - 1) / rpp);
+            }
+            int inc = cnt;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const int v = __shfl_up(inc, d, kWave);
+                if (lane >= d) inc += v;
+            }
+            if (sl < ns) s_pass0[sl] = base + inc - cnt;
+            base += __shfl(inc, 63, kWave);
+        }
+        if (lane == 0) {
+            s_pass0[ns] = base;
+            s_ns = ns;
+            const long long b = blockIdx.x, nb = gridDim.x;
+            const int beg = (int)(b * base / nb), end = (int)((b + 1) * base / nb);
+            s_beg = beg;
+            s_end = end;
+            s_next = beg + NW;
+        }
+    } else if (wave == 1) {
+        // activation row of each routed row (or identity row): -1 when out of range
+        const int Rr = routed ? R : T;
+        for (int r = lane; r < Rr && r < kFlatMaxSlots; r += 64) {
+            int a = r;
+            if (routed && gather) {
+                a = gload_i32(sorted + r);
+                a = a >= 0 ? a / kk : -1;
+            }
+            s_tok[r] = (a >= 0 && a < n_act) ? a : -1;
+        }
+    }
+    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+
+    const int ns = s_ns, beg = s_beg, end = s_end;
+    const int grp = PAIR ? (lane & 31) / G : lane / G;
+    const int j = lane & (G - 1);
+    const int mat = PAIR ? (lane >> 5) : 0;
+    const uint8_t *w_r = PAIR && mat ? p.w[1] : p.w[0];
+    const void *s_rt = PAIR && mat ? p.s[1] : p.s[0];
+    const uint8_t *w_s = has_sh ? (PAIR && mat ? p.sw[1] : p.sw[0]) : w_r;
+    const void *s_s = has_sh ? (PAIR && mat ? p.ss[1] : p.ss[0]) : s_rt;
+    const int nb = (nl + U - 1) / U;    // batches per pass
+
+    // pass P -> its slot; the passes a wave takes only increase, so the slot cursor moves forward
+    int cursor = 0;
+    auto resolve = [&](int P) __attribute__((always_inline)) {
+        return flat_resolve<FMT, MAXM>(P, end, ns, pN, sN, rpp, grp, w_r, s_rt, w_s, s_s, cursor, s_e, s_r0, s_m,
+                                       s_pass0);
+    };
+    // loads of batch ib of a pass (row ridx of the stack wb / sb), from clamped valid addresses
+    auto load = [&](const uint8_t *wb, const void *sb, size_t ridx, size_t srow, int ib, u32x4 (&w)[U],
+                    uint32_t (&sc)[NSC]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int b = min(j + (ib * U + u) * G, units - 1);
+            w[u] = gload16_nt(wb + (ridx * (size_t)units + b) * 16);
+            if constexpr (FMT == kFmtMXFP4) {
+                // SD dwords of scales per lane and batch: load k of lane j of the group holds the
+                // bytes of units 4(ib*SD*G + k*G + j) .. +3; compute() picks each unit's byte
+                if (u < SD) {
+                    const int dw = min(ib * SD * G + u * G + j, units / 4 - 1);
+                    sc[u] = gload_u32((const uint8_t *)sb + ridx * units + 4 * dw);
+                }
+            } else if constexpr (FMT == kFmtFP8) {
+                sc[u] = gload_u32((const float *)sb + srow * (K / 128) + (b * 16) / 128);
+            } else {
+                sc[u] = 0;
+            }
+        }
+    };
+    float acc[MAXM];
+#pragma unroll
+    for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
+    int tok[MAXM];
+    auto tokens = [&](const FlatPass &f) __attribute__((always_inline)) {
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) {
+            const int r = f.r0 + f.m0 + m;
+            const int tk = m < f.mc ? (f.sh ? (f.m0 + m < n_act ? f.m0 + m : -1) : s_tok[min(r, kFlatMaxSlots - 1)]) : -1;
+            tok[m] = __builtin_amdgcn_readfirstlane(tk);
+        }
+    };
+    // accumulate batch ib of pass f; after its last batch reduce over the lane group, apply
+    // SwiGLU for the pair, write the rows and clear acc
+    auto compute = [&](const FlatPass &f, int ib, const u32x4 (&w)[U],
+                       const uint32_t (&sc)[NSC]) __attribute__((always_inline)) {
+        const bool row_ok = f.n < f.N;
+        uint32_t scv[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            if constexpr (FMT == kFmtMXFP4) {
+                // unit j + G*(U ib + u): byte j%4 of scale dword u/4 of lane (j + G*(u%4))/4
+                const uint32_t d = __shfl(sc[u / 4], (lane - j) + ((j + G * (u % 4)) >> 2), kWave);
+                scv[u] = (d >> (8 * (j & 3))) & 0xffu;
+            } else {
+                scv[u] = sc[u];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int b = j + (ib * U + u) * G;
+            if (row_ok && (ib * U + u) < nl && b < units) {
+#pragma unroll
+                for (int m = 0; m < MAXM; ++m) {
+                    if (m < f.mc) {
+                        const void *a = smem + (size_t)max(tok[m], 0) * rs + (size_t)b * EPU * ASZ;
+                        acc[m] = fmaf(unit_dot<FMT, F32>(w[u], a, act_swizzle<FMT, F32>(b)),
+                                      unit_scale_value(FMT, scv[u]), acc[m]);
+                    }
+                }
+            }
+        }
+        if (ib != nb - 1) return;
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) acc[m] = group_sum(acc[m], G);
+        if constexpr (PAIR) {
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) {
+                const float up = __shfl_xor(acc[m], 32, kWave);
+                acc[m] = silu(acc[m]) * up;
+            }
+        }
+        if (row_ok && j == 0 && mat == 0) {
+#pragma unroll
+            for (int m = 0; m < MAXM; ++m) {
+                if (m < f.mc) {
+                    float v = tok[m] >= 0 ? acc[m] : 0.0f;
+                    if (f.sh) {
+                        sout[(size_t)(f.m0 + m) * f.N + f.n] = v;
+                    } else {
+                        const size_t o = (size_t)(f.r0 + f.m0 + m) * f.N + f.n;
+                        if (residual) v += residual[o];
+                        out[o] = v;
+                    }
+                }
+            }
+        }
+#pragma unroll
+        for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
+    };
+    auto grab = [&]() __attribute__((always_inline)) {
+        int g = 0;
+        if (lane == 0) g = atomicAdd(&s_next, 1);
+        return min(__builtin_amdgcn_readfirstlane(g), end);
+    };
+
+    int P = min(beg + wave, end);
+    FlatPass fc = resolve(P);
+    u32x4 wa[U], wb[U];
+    uint32_t sa[NSC], sb[NSC];
+    load(fc.wb, fc.sb, fc.ridx, fc.srow, 0, wa, sa);
+    int Pn = P < end ? grab() : end;
+    FlatPass fn = resolve(Pn);
+    tokens(fc);
+    int ib = 0;
+    // one batch: load the following one into `nx` (the next pass's first batch after the
+    // last one; every field selected, so the load is unconditional), consume `cu`
+    auto step = [&](u32x4 (&cu)[U], uint32_t (&cs)[NSC], u32x4 (&nx)[U],
+                    uint32_t (&nsc)[NSC]) __attribute__((always_inline)) {
+        const bool last = ib + 1 == nb;
+        load(last ? fn.wb : fc.wb, last ? fn.sb : fc.sb, last ? fn.ridx : fc.ridx, last ? fn.srow : fc.srow,
+             last ? 0 : ib + 1, nx, nsc);
+        compute(fc, ib, cu, cs);
+        if (last) {
+            P = Pn;
+            fc = fn;
+            Pn = P < end ? grab() : end;
+            fn = resolve(Pn);
+            tokens(fc);
+            ib = 0;
+        } else {
+            ++ib;
+        }
+        return P < end;
+    };
+    bool more = P < end;
+    while (more) {
+        more = step(wa, sa, wb, sb);
+        if (!more) break;
+        more = step(wb, sb, wa, sa);
+    }
+}
+
 static void pick_layout(int units, bool pair, int *G, int *nl);
 
 // ------------------------------------------------------------------ down + combine
@@ -461,9 +811,6 @@ static void pick_layout(int units, bool pair, int *G, int *nl);
 //     and keeps kDcDepth batches of loads in flight.  Each item's dot products go to an
 //     LDS table part[slot][row]; after a barrier every row's output is the slot-ordered
 //     sum of its table column.
-#ifndef MOE_DM_ROUND
-#define MOE_DM_ROUND 4           // MXFP4 (matrix-core) path: rows per workgroup rounded to this (tiles of 16 may end past them)
-#endif
 #ifndef MOE_DC_ROWS
 #define MOE_DC_ROWS 4            // weight rows per lane group
 #endif
@@ -726,7 +1073,7 @@ static int down_combine_batch(int nl) {
 moe_status down_combine_launch(int fmt, DownCombineParams p, hipStream_t stream) {
     const bool mfma = fmt == kFmtMXFP4;
     const int units = fmt == kFmtMXFP4 ? p.I / 32 : p.I / 16;
-    int U = 1, rpp = MOE_DM_ROUND;                         // MFMA path: 16-row tiles, the last one clamped
+    int U = 1, rpp = 4;                                    // MFMA path: 16-row tiles, the last one clamped
 
     if (!mfma) {
         // 16 lanes per row segment while a lane still gets >= 4 units; short rows use the
@@ -738,11 +1085,12 @@ moe_status down_combine_launch(int fmt, DownCombineParams p, hipStream_t stream)
         rpp = (64 / p.G) * kDcRows;
     }
     // about one workgroup per CU in total (LDS holds k+1 rows of h; an HBM-bound launch
-    // does not need every CU), whole passes, at most kDcMaxRows rows
+    // does not need every CU), whole passes, at most kDcMaxRows rows (kDmMaxRows on the
+    // matrix cores, which keep two partial sums per row)
     const long long rows_total = (long long)p.N * p.T;
     int rpw = (int)((rows_total + 255) / 256);
     rpw = (max(rpw, rpp) + rpp - 1) / rpp * rpp;
-    rpw = min(rpw, max(rpp, kDcMaxRows / rpp * rpp));
+    rpw = min(rpw, max(rpp, (mfma ? kDmMaxRows : kDcMaxRows) / rpp * rpp));
     p.rows_per_wg = rpw;
     const int nslot = p.k + (p.sw ? 1 : 0);
     p.h_lds_bytes = (int)align_up((size_t)nslot * 4 * dc_plane_ld(p.I), 1024);
@@ -816,12 +1164,54 @@ static GemvFn pick_kernel(int fmt, int act, bool pair, int maxm, bool routed) {
 #endif
 constexpr size_t kGemvLdsBudget = MOE_GEMV_LDS_BUDGET;
 
+template <int FMT, int ACT, bool PAIR>
+static GemvFn pick_flat_m(int maxm) {
+    switch (maxm) {
+        case 1: return gemv_flat_kernel<FMT, ACT, 1, PAIR>;
+        case 2: return gemv_flat_kernel<FMT, ACT, 2, PAIR>;
+        case 4: return gemv_flat_kernel<FMT, ACT, 4, PAIR>;
+        default: return gemv_flat_kernel<FMT, ACT, 8, PAIR>;
+    }
+}
+
+template <int FMT, bool PAIR>
+static GemvFn pick_flat_a(int act, int maxm) {
+    return act == kActF32 ? pick_flat_m<FMT, kActF32, PAIR>(maxm) : pick_flat_m<FMT, kActBF16, PAIR>(maxm);
+}
+
+static GemvFn pick_flat(int fmt, int act, bool pair, int maxm) {
+    if (fmt == kFmtMXFP4) return pair ? pick_flat_a<kFmtMXFP4, true>(act, maxm) : pick_flat_a<kFmtMXFP4, false>(act, maxm);
+    if (fmt == kFmtFP8) return pair ? pick_flat_a<kFmtFP8, true>(act, maxm) : pick_flat_a<kFmtFP8, false>(act, maxm);
+    return pick_flat_a<kFmtBF16, false>(act, maxm);
+}
+
 moe_status gemv_launch(int fmt, int act, bool pair, GemvParams p, int slots, int max_rows_per_expert,
                        hipStream_t stream, const char *what) {
     const bool act_f32 = act == kActF32;
     const int units = fmt == kFmtMXFP4 ? p.K / 32 : (fmt == kFmtFP8 ? p.K / 16 : p.K / 8);
     pick_layout(units, pair, &p.G, &p.nl);
     const size_t row_lds = (size_t)p.K * (act_f32 ? 4 : 2);
+
+    // Decode-sized launches (every activation row fits in LDS at once, float or bf16): the
+    // flat schedule, one workgroup per CU over an equal share of the passes.
+    const bool routed = p.offsets != nullptr;
+    const size_t rs = align_up(row_lds, 1024);
+    if (act != kActMX && p.n_act_rows >= 1 && p.n_act_rows <= kFlatMaxTok && (size_t)p.n_act_rows * rs <= kFlatLdsBudget &&
+        (fmt != kFmtMXFP4 || (units % 4 == 0 && p.G >= 4)) &&
+        (routed ? p.R : p.T) <= kFlatMaxSlots - 1 && (routed || p.T <= kFlatMaxTok)) {
+        int want = max_rows_per_expert < 1 ? 1 : (max_rows_per_expert > 8 ? 8 : max_rows_per_expert);
+        int maxm = 1;
+        while (maxm < want) maxm *= 2;
+        const int rpp = pair ? 32 / p.G : 64 / p.G;
+        const int routed_slots = routed ? slots - (p.shared_slot >= 0 ? 1 : 0) : 1;
+        long long passes = (long long)routed_slots * ((p.N + rpp - 1) / rpp);
+        if (p.shared_slot >= 0) passes += (p.sN + rpp - 1) / rpp;
+        const long long per_wg = kFlatThreads / 64;
+        const int nwg = (int)std::min<long long>(device_cu_count(), std::max<long long>(1, (passes + per_wg - 1) / per_wg));
+        hipLaunchKernelGGL(pick_flat(fmt, act, pair, maxm), dim3(nwg), dim3(kFlatThreads), (size_t)p.n_act_rows * rs,
+                           stream, p);
+        return launch_check(what);
+    }
     int fit = (int)(kGemvLdsBudget / row_lds);
     if (fit < 1) fit = (int)(64 * 1024 / row_lds);   // wide rows: one token per chunk
     if (fit < 1) {

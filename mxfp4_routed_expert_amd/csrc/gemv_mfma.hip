@@ -5,48 +5,48 @@ namespace moe {
 
 // ------------------------------------------------------------------ down + combine
 // The decode down product with the weighted combine (as down_combine_kernel in gemv.hip),
-// MXFP4 weights, multiply-adds on v_mfma_f32_16x16x32_bf16.  A wave's work item is a tile
-// of 16 weight rows of one slot.  A step covers one 128-byte line of each row (8 units,
-// 256 values) as two K-steps of 128: lane l loads units 8m + l/16 and 8m + 4 + l/16 of row
-// l%16 and converts each to its A slices for four MFMAs.  B holds the slot's h as two bf16
-// columns, hi = RN_bf16(h) and lo = RN_bf16(h - hi) (together within 2^-17 |h|), the other
-// 14 columns zero, so C[row][0] + C[row][1] is the row's dot product.  The vector ALU only
-// converts codes (one instruction per two weights) and advances pointers: the float32
-// multiply-adds of the vector kernel cost as much issue time as the HBM stream.  Each wave
-// keeps kDmDepth steps of loads in flight across item boundaries; results go through the
-// part[slot][row] LDS table and the slot-ordered final sum.
-#ifndef MOE_DM_DEPTH
-#define MOE_DM_DEPTH 4           // steps of loads in flight per wave
-#endif
-#ifndef MOE_DM_NT
-#define MOE_DM_NT 0              // non-temporal weight loads (off: the two half-lines of a row arrive in separate loads)
-#endif
-constexpr int kDmDepth = MOE_DM_DEPTH;
+// MXFP4 weights, multiply-adds on v_mfma_f32_16x16x32_bf16.  A step covers one 128-byte
+// line of each of 16 weight rows (8 units, 256 values) as two K-steps of 128: lane l loads
+// the adjacent units 8m + 2(l/16) and 8m + 2(l/16) + 1 of row l%16 (with an even number of
+// units per row, both scale bytes in one 16-bit load) and converts each to its A slices for
+// four MFMAs.  B holds the slot's h as two bf16 columns, hi = RN_bf16(h) and
+// lo = RN_bf16(h - hi) (together within 2^-17 |h|), the other 14 columns zero, so
+// C[row][0] + C[row][1] is the row's dot product.  The vector ALU only converts codes (one
+// instruction per two weights) and advances pointers: the float32 multiply-adds of the
+// vector kernel cost as much issue time as the HBM stream.
+//
+// Work items are (tile of 16 rows, slot j, K part kp): the item's rows of slot j over its
+// part of the steps (two parts when an item has at least 2 * kDmDepth steps, else one).
+// Waves take items from an LDS counter, so a wave that is served late takes fewer of them.
+// Item (tile, j, kp) writes its 16 partial dot products to part[kp][j][rows] of an LDS
+// table whatever wave ran it; after a barrier every row's output is the slot-ordered sum of
+// w_j * (part[0] + part[1]), so the result does not depend on which wave ran what.  Each
+// wave keeps kDmDepth steps of loads in flight across item boundaries; every slot of that
+// ring records the position its loads belong to.
+//
+// Prologue: the slots' float32 h rows are loaded into registers first (each workgroup
+// starts at a different place in them, so the CUs of an XCD do not all ask the L2 for the
+// same lines at once), then the weights of the wave's first two steps; the h values are
+// written to LDS as the bf16 hi and lo planes, the wave counts itself in an LDS counter,
+// issues its next two steps and waits only for that counter to reach the wave count.  (A
+// workgroup barrier there would also wait for the slowest wave to get its weight loads
+// issued -- at the start every CU asks for its share of the first steps at once -- and the
+// waves already past it would issue nothing meanwhile.)
+constexpr int kDmDepth = 4;              // steps of loads in flight per wave
+constexpr int kDmThreads = 1024;         // 16 waves, four per SIMD
+constexpr int kDmMaxGroups = 4800;       // 8-value groups of h: slots * dc_plane_ld(I) / 8 within 150 KiB
+static_assert(2 * kDmMaxRows <= kDcMaxRows, "two partial sums per row must fit the table");
 
-MOE_DEV void dm_dma16(const void *src, uint32_t lds_wave_base) {
-    const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_wave_base);
-    asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(src), "{m0}"(m0) : "memory");
-}
+__device__ __align__(16) uint8_t g_dm_zero[16];   // read-only zeros (loads of a wave with no item left)
 
-__device__ __align__(16) uint8_t g_dm_zero[16];   // read-only zeros (loads past a wave's work)
-
-// A wave's position: step m of item (tile, slot j), with the item's matrix bases
-// (wave-uniform) and this lane's row offsets.
-struct DmIt {
-    int q, j, m, tile;
-    const uint8_t *wb, *sb;
-    uint32_t wo, so;
-};
-
-#ifndef MOE_DM_THREADS
-#define MOE_DM_THREADS 1024      // threads of a matrix-core down-combine workgroup (4 waves per SIMD)
-#endif
-constexpr int kDmThreads = MOE_DM_THREADS;
-
+// PS: the scale bytes of a lane's two units are read as one 16-bit word (units per row even,
+// scale array 2-byte aligned); otherwise as two bytes.
+template <bool PS>
 __global__ __launch_bounds__(kDmThreads) void down_combine_mfma_kernel(const DownCombineParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_e[MOE_MAX_TOPK + 1], s_r[MOE_MAX_TOPK + 1];
     __shared__ float s_w[MOE_MAX_TOPK + 1];
+    __shared__ int s_item, s_ready;
     constexpr int NW = kDmThreads / 64;
     const int t = blockIdx.y;
     const int nslot = p.k + (p.sw ? 1 : 0);
@@ -69,180 +69,229 @@ __global__ __launch_bounds__(kDmThreads) void down_combine_mfma_kernel(const Dow
         s_r[tid] = r;
         s_w[tid] = wt;
     }
+    if (tid == 0) {
+        s_item = NW;
+        s_ready = 0;
+    }
     __syncthreads();
 
-    const int units = p.I / 32;
-    const int nm = (units + 7) / 8;                        // steps per item
+    // parameters in locals: a lambda that captures the parameter block by reference keeps it
+    // in scratch memory, and a select between two of its fields becomes a select of addresses
+    const int I = p.I, N = p.N, kk = p.k, rpw = p.rows_per_wg;
+    const uint8_t *w_r = p.w, *w_s = p.sw;
+    const uint8_t *s_rt = (const uint8_t *)p.s, *s_s = (const uint8_t *)p.ss;
+    const int units = I / 32;
+    const int nm = (units + 7) / 8;                        // steps per (tile, slot)
     const int ld = dc_plane_ld(p.I);                       // bf16 values per plane (>= 256 * nm)
     const int n_begin = blockIdx.x * p.rows_per_wg;
     const int n_end = min(p.N, n_begin + p.rows_per_wg);
     if (n_begin >= n_end) return;                          // the whole workgroup
     const int ntile = (n_end - n_begin + 15) / 16;
-    const int nitems = ntile * nslot;
-    const int my_items = wave < nitems ? (nitems - 1 - wave) / NW + 1 : 0;
-    const int nq = my_items * nm;
+    const int KS = nm >= 2 * kDmDepth ? 2 : 1;             // K parts per (tile, slot)
+    const int per_tile = nslot * KS;
+    const int nitems = ntile * per_tile;
     const int r16 = lane & 15, g = lane >> 4;
     uint16_t *planes = (uint16_t *)smem;                   // slot j: hi plane 2j, lo plane 2j+1
-    float *part = (float *)(smem + p.h_lds_bytes);          // [nslot][rows_per_wg]
-    const uint32_t row_bytes = (uint32_t)p.I / 2;
+    float *part = (float *)(smem + p.h_lds_bytes);          // [2][nslot][rows_per_wg]
+    const uint32_t row_bytes = (uint32_t)I / 2;
 
-    auto setup = [&](DmIt &c) {
-        const bool sh = c.j >= p.k;
-        const int e = sh ? 0 : max(__builtin_amdgcn_readfirstlane(s_e[c.j]), 0);
-        const size_t first_row = (size_t)e * p.N;
-        c.wb = (sh ? p.sw : p.w) + first_row * row_bytes;
-        c.sb = (const uint8_t *)(sh ? p.ss : p.s) + first_row * units;
-        const uint32_t n = (uint32_t)min(n_begin + c.tile * 16 + r16, n_end - 1);
-        c.wo = n * row_bytes;
-        c.so = n * (uint32_t)units;
+    // load cursor: item `it` (nitems: none left), step m of [m, m_end); matrix bases of the
+    // item (wave-uniform) and this lane's row offsets
+    int it = min(wave, nitems), m = 0, m_end = 0, cj = 0, ctile = 0, ckp = 0;
+    const uint8_t *cwb = g_dm_zero, *csb = g_dm_zero;
+    uint32_t cwo = 0, cso = 0;
+    auto setup = [&]() __attribute__((always_inline)) {     // (branch-free: a wave with no item left reads zeros)
+        const bool has = it < nitems;
+        const int itc = has ? it : 0;
+        ctile = itc / per_tile;
+        const int rem = itc - ctile * per_tile;
+        cj = rem / KS;
+        ckp = rem - cj * KS;
+        m = has ? ckp * nm / KS : 0;
+        m_end = has ? (ckp + 1) * nm / KS : 0;
+        const bool sh = cj >= kk;
+        const int e = max(__builtin_amdgcn_readfirstlane(s_e[cj]), 0);   // (the shared slot's entry is 0)
+        const size_t first_row = (size_t)e * N;
+        // (casts make both arms values: a conditional on two captured variables is an lvalue,
+        // compiled as a select of their addresses, which keeps them in scratch memory)
+        const uint8_t *wbase = sh ? (const uint8_t *)w_s : (const uint8_t *)w_r;
+        const uint8_t *sbase = sh ? (const uint8_t *)s_s : (const uint8_t *)s_rt;
+        cwb = has ? wbase + first_row * row_bytes : g_dm_zero;
+        csb = has ? sbase + first_row * units : g_dm_zero;
+        const uint32_t n = (uint32_t)min(n_begin + ctile * 16 + r16, n_end - 1);
+        cwo = has ? n * row_bytes : 0u;
+        cso = has ? n * (uint32_t)units : 0u;
     };
-    auto advance = [&](DmIt &c) {
-        ++c.q;
-        if (++c.m == nm) {
-            c.m = 0;
-            c.j += NW;
-            while (c.j >= nslot) {
-                c.j -= nslot;
-                ++c.tile;
-            }
-            setup(c);
-        }
+    auto grab = [&]() __attribute__((always_inline)) {
+        int v = 0;
+        if (lane == 0) v = atomicAdd(&s_item, 1);
+        return min(__builtin_amdgcn_readfirstlane(v), nitems);
     };
     // Loads are issued unconditionally (a load under a branch leaves the compiler unable
-    // to count the loads in flight, and it then waits for all of them); positions past the
-    // wave's last step read a 16-byte block of zeros that stays in cache.
-    auto load = [&](const DmIt &c, u32x4 (&w)[2], uint8_t (&sc)[2]) {
-        const bool live = c.q < nq;
-        const uint8_t *wb = live ? c.wb : g_dm_zero;
-        const uint8_t *sb = live ? c.sb : g_dm_zero;
+    // to count the loads in flight, and it then waits for all of them); a wave with no item
+    // left reads a 16-byte block of zeros that stays in cache.
+    auto load = [&](u32x4 (&w)[2], uint16_t &sc) __attribute__((always_inline)) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const uint32_t u = (uint32_t)min(8 * c.m + 4 * h + g, units - 1);
-            const u32x4 *src = (const u32x4 *)(wb + (live ? c.wo + u * 16 : 0u));
-            if constexpr (MOE_DM_NT) w[h] = __builtin_nontemporal_load(src);
-            else w[h] = *src;
-            sc[h] = sb[live ? c.so + u : 0u];
+            const uint32_t u = (uint32_t)min(8 * m + 2 * g + h, units - 1);
+            w[h] = *(const u32x4 *)(cwb + (it < nitems ? cwo + u * 16 : 0u));
+        }
+        if constexpr (PS) {
+            // bytes of units base, base + 1; base = 8m + 2g whenever that unit is in the row
+            const uint32_t base = (uint32_t)min(8 * m + 2 * g, units - 2);
+            sc = *(const uint16_t *)(csb + (it < nitems ? cso + base : 0u));
+        } else {
+            const uint32_t u0 = (uint32_t)min(8 * m + 2 * g, units - 1), u1 = (uint32_t)min(8 * m + 2 * g + 1, units - 1);
+            const bool lv = it < nitems;
+            sc = (uint16_t)(csb[lv ? cso + u0 : 0u] | (csb[lv ? cso + u1 : 0u] << 8));
         }
     };
+    // ring slot d: the position its loads belong to
+    int pj[kDmDepth], ptile[kDmDepth], pkp[kDmDepth], pm[kDmDepth];
+    bool plive[kDmDepth], plast[kDmDepth];
+    int live_slots = 0;
+    auto fill = [&](auto dc, u32x4 (&w)[2], uint16_t &sc) __attribute__((always_inline)) {
+        constexpr int d = decltype(dc)::value;
+        const bool lv = it < nitems;
+        pj[d] = cj;
+        ptile[d] = ctile;
+        pkp[d] = ckp;
+        pm[d] = m;
+        plive[d] = lv;
+        plast[d] = m + 1 == m_end;
+        load(w, sc);
+        live_slots += lv ? 1 : 0;
+        if (lv && ++m == m_end) {
+            it = grab();
+            setup();
+        }
+    };
+
     f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
     u32x4 bq[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};   // zero outside columns 0, 1
-    // Step at c into acc (units past the row get scale 0, so A is zero there, and B is zero
-    // past d_ff); the item's last step adds the hi and lo columns and stores the tile's 16
-    // dot products for slot j (0 for a dropped pair).
-    auto compute = [&](const DmIt &c, const u32x4 (&w)[2], const uint8_t (&sc)[2]) {
+    // Step of ring slot d into acc (units past the row get scale 0, so A is zero there, and B
+    // is zero past d_ff); the item's last step adds the hi and lo columns and stores the
+    // tile's 16 partial dot products (0 for a dropped pair).
+    auto compute = [&](auto dc, const u32x4 (&w)[2], const uint16_t sc) __attribute__((always_inline)) {
+        constexpr int d = decltype(dc)::value;
+        const int j = pj[d];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int u = 8 * c.m + 4 * h + g;
+            const int u = 8 * pm[d] + 2 * g + h;
             bf16x8 a[4];
-            unit_to_bf16x8(w[h], u < units ? e8m0_to_f32((uint32_t)sc[h]) : 0.0f, a);
-            const uint16_t *bp = planes + (size_t)(2 * c.j + (r16 & 1)) * ld + u * 32;
+            unit_to_bf16x8(w[h], u < units ? e8m0_to_f32(((uint32_t)sc >> (8 * h)) & 0xffu) : 0.0f, a);
+            const uint16_t *bp = planes + (size_t)(2 * j + (r16 & 1)) * ld + u * 32;
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
                 if (r16 < 2) bq[q] = *(const u32x4 *)(bp + 8 * q);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q], __builtin_bit_cast(bf16x8, bq[q]), acc, 0, 0, 0);
             }
         }
-        if (c.m != nm - 1) return;
-        const bool drop = __builtin_amdgcn_readfirstlane(s_e[c.j]) < 0;
+        if (!plast[d]) return;
+        const bool drop = __builtin_amdgcn_readfirstlane(s_e[j]) < 0;
+        float *pp = part + (size_t)(pkp[d] * nslot + j) * rpw;
         // lane (col r16, group g) holds C[4g+v][r16]; column 1 moves down one lane
-        const int l0 = c.tile * 16 + 4 * g;
+        const int l0 = ptile[d] * 16 + 4 * g;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             float o = acc[v] + __shfl_down(acc[v], 1, kWave);
             if (drop) o = 0.0f;
-            if (r16 == 0 && n_begin + l0 + v < n_end) part[c.j * p.rows_per_wg + l0 + v] = o;
+            if (r16 == 0 && n_begin + l0 + v < n_end) pp[l0 + v] = o;
             acc[v] = 0.0f;
         }
     };
 
-    // h rows -> LDS by direct copies: slot j's float32 row at byte 4*ld*j, in whole 1 KiB
-    // blocks (the tail of a row's last block re-reads its last vector into the row's
-    // padding; 4*ld is a multiple of 1 KiB).  The copies are waited for before any weight
-    // load is issued: behind a full pipeline of weight loads they would land several times
-    // later.  The first kDmDepth steps of weight loads are then in flight during the
-    // conversion, whose barriers wait for LDS accesses only (a __syncthreads would also wait
-    // for every load in flight).
-    {
-        const int act_vec = p.I / 4;
-        const int bpr = (act_vec + 63) / 64;                 // copy blocks per row
-        for (int blk = wave; blk < nslot * bpr; blk += NW) {
-            const int j = blk / bpr, b0 = (blk - j * bpr) * 64;
-            const int v = min(b0 + lane, act_vec - 1);
-            const float *row = j < p.k ? p.h + (size_t)max(s_r[j], 0) * p.I : p.hs + (size_t)t * p.I;
-            dm_dma16(row + (size_t)v * 4, (uint32_t)(uintptr_t)(smem + (size_t)j * 4 * ld + (size_t)b0 * 16));
-        }
+    // h rows -> registers: 8-value group i = (slot j, group v) of the planes' layout, taken
+    // from a workgroup-dependent starting point; groups past d_ff and dropped slots become
+    // zeros when written (their loads read a valid group).
+    constexpr int kGroups = (kDmMaxGroups + kDmThreads - 1) / kDmThreads;
+    const int per = ld / 8;
+    const int total = nslot * per;
+    const int rot = (int)(((long long)blockIdx.x * 977 + (long long)blockIdx.y * 331) % total);
+    auto group_of = [&](int i) __attribute__((always_inline)) {
+        const int r = i + rot;
+        return r >= total ? r - total : r;
+    };
+    f32x4 va[kGroups], vb[kGroups];
+#pragma unroll
+    for (int u = 0; u < kGroups; ++u) {
+        const int i = group_of(min(tid + u * kDmThreads, total - 1));
+        const int j = i / per, v = min(i - j * per, I / 8 - 1);
+        const float *row = j < kk ? p.h + (size_t)max(s_r[j], 0) * I : p.hs + (size_t)t * I;
+        const f32x4 *src = (const f32x4 *)(row + (size_t)v * 8);
+        va[u] = src[0];
+        vb[u] = src[1];
     }
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
     u32x4 wv[kDmDepth][2];
-    uint8_t sv[kDmDepth][2];  // (bytes: a widened copy would be masked at the loop latch, forcing a wait)
-    DmIt lp{0, wave % nslot, 0, wave / nslot, nullptr, nullptr, 0, 0};
-    setup(lp);
-    const DmIt first = lp;
+    uint16_t sv[kDmDepth];    // (16 bits: a widened copy would be masked at the loop latch, forcing a wait)
+    setup();
+    static_assert(kDmDepth == 4, "the prologue issues two steps before the planes and two after");
+    fill(std::integral_constant<int, 0>{}, wv[0], sv[0]);
+    fill(std::integral_constant<int, 1>{}, wv[1], sv[1]);
+    // float32 h -> bf16 hi/lo planes: hi = RN_bf16(h), lo = RN_bf16(h - hi) by the packed
+    // round-to-nearest-even conversion; plane hi of slot j at element 2j*ld, lo at (2j+1)*ld.
 #pragma unroll
-    for (int d = 0; d < kDmDepth; ++d) {
-        load(lp, wv[d], sv[d]);
-        advance(lp);
-    }
-    // float32 rows -> bf16 hi/lo planes in place (all reads before the barrier, all writes
-    // after): plane hi at element 0 of the row's region, lo at element ld; zeros past d_ff
-    // and for dropped pairs.  hi = RN_bf16(h), lo = RN_bf16(h - hi) by the packed
-    // round-to-nearest-even conversion.
-    {
-        // 8-value groups: S * ld / 8 in all, S * 4 * ld <= 150 KiB -> <= 4800
-        constexpr int kGroups = (4800 + kDmThreads - 1) / kDmThreads;
-        const int per = ld / 8;
-        const int total = nslot * per;
-        f32x4 va[kGroups], vb[kGroups];
+    for (int u = 0; u < kGroups; ++u) {
+        if (tid + u * kDmThreads >= total) break;
+        const int i = group_of(tid + u * kDmThreads);
+        const int j = i / per, v = i - j * per;
+        const bool ok = v * 8 < I && (j >= kk || s_r[j] >= 0);
+        const f32x4 x0 = ok ? va[u] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const f32x4 x1 = ok ? vb[u] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        const f32x2 f[4] = {{x0[0], x0[1]}, {x0[2], x0[3]}, {x1[0], x1[1]}, {x1[2], x1[3]}};
+        u32x4 hv, lv;
 #pragma unroll
-        for (int u = 0; u < kGroups; ++u) {
-            const int i = min(tid + u * kDmThreads, total - 1);
-            const int j = i / per, v = i - j * per;
-            const bool ok = v * 8 < p.I && (j >= p.k || s_r[j] >= 0);
-            const f32x4 *src = (const f32x4 *)(smem + (size_t)j * 4 * ld) + 2 * v;
-            va[u] = ok ? src[0] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            vb[u] = ok ? src[1] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        for (int q = 0; q < 4; ++q) {
+            const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(f[q], bf16x2));
+            const f32x2 r = {f[q].x - __uint_as_float(hb << 16), f[q].y - __uint_as_float(hb & 0xffff0000u)};
+            hv[q] = hb;
+            lv[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
         }
-        lds_barrier();
-#pragma unroll
-        for (int u = 0; u < kGroups; ++u) {
-            const int i = tid + u * kDmThreads;
-            if (i >= total) break;
-            const int j = i / per, v = i - j * per;
-            const f32x2 f[4] = {{va[u][0], va[u][1]}, {va[u][2], va[u][3]}, {vb[u][0], vb[u][1]}, {vb[u][2], vb[u][3]}};
-            u32x4 hv, lv;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(f[q], bf16x2));
-                const f32x2 r = {f[q].x - __uint_as_float(hb << 16), f[q].y - __uint_as_float(hb & 0xffff0000u)};
-                hv[q] = hb;
-                lv[q] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2));
-            }
-            *(u32x4 *)(planes + (size_t)(2 * j) * ld + v * 8) = hv;
-            *(u32x4 *)(planes + (size_t)(2 * j + 1) * ld + v * 8) = lv;
-        }
+        *(u32x4 *)(planes + (size_t)(2 * j) * ld + v * 8) = hv;
+        *(u32x4 *)(planes + (size_t)(2 * j + 1) * ld + v * 8) = lv;
     }
-    lds_barrier();
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");     // this wave's plane writes are in LDS
+    if (lane == 0) atomicAdd(&s_ready, 1);
+    fill(std::integral_constant<int, 2>{}, wv[2], sv[2]);
+    fill(std::integral_constant<int, 3>{}, wv[3], sv[3]);
+    // every wave counts itself once, right after its writes, so the wait ends; the bound only
+    // keeps a fault elsewhere from turning into a hang
+    // (read through an LDS pointer: a generic volatile read is a flat load, and its wait
+    // would also wait for every weight load in flight)
+    volatile __attribute__((address_space(3))) int *ready = (volatile __attribute__((address_space(3))) int *)&s_ready;
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+        if (__builtin_amdgcn_readfirstlane(*ready) >= NW) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");                         // no plane read moves above the wait
 
-    DmIt cp = first;
-    for (int q0 = 0; q0 < nq; q0 += kDmDepth) {
-#pragma unroll
-        for (int d = 0; d < kDmDepth; ++d) {
-            if (cp.q < nq) compute(cp, wv[d], sv[d]);
-            advance(cp);
-            load(lp, wv[d], sv[d]);
-            advance(lp);
-        }
+    while (live_slots > 0) {
+        static_for<kDmDepth>([&](auto dc) __attribute__((always_inline)) {
+            constexpr int d = decltype(dc)::value;
+            if (plive[d]) {
+                compute(dc, wv[d], sv[d]);
+                --live_slots;
+            }
+            fill(dc, wv[d], sv[d]);
+        });
     }
     __syncthreads();
+    const float *q0p = part, *q1p = part + (size_t)nslot * p.rows_per_wg;
     for (int lr = tid; lr < n_end - n_begin; lr += kDmThreads) {
         float o = 0.0f;
-        for (int j = 0; j < nslot; ++j) o = fmaf(s_w[j], part[j * p.rows_per_wg + lr], o);   // slot order
+        for (int j = 0; j < nslot; ++j) {                  // slot order
+            const float v = KS == 2 ? q0p[j * p.rows_per_wg + lr] + q1p[j * p.rows_per_wg + lr]
+                                    : q0p[j * p.rows_per_wg + lr];
+            o = fmaf(s_w[j], v, o);
+        }
         p.out[(size_t)t * p.N + n_begin + lr] = o;
     }
 }
 
 void down_combine_mfma_launch(const DownCombineParams &p, dim3 grid, size_t lds, hipStream_t stream) {
-    hipLaunchKernelGGL(down_combine_mfma_kernel, grid, dim3(kDmThreads), lds, stream, p);
+    const bool ps = (p.I / 32) % 2 == 0 && (((uintptr_t)p.s | (uintptr_t)p.ss) & 1) == 0;
+    if (ps) hipLaunchKernelGGL(down_combine_mfma_kernel<true>, grid, dim3(kDmThreads), lds, stream, p);
+    else hipLaunchKernelGGL(down_combine_mfma_kernel<false>, grid, dim3(kDmThreads), lds, stream, p);
 }
 
 }  // namespace moe

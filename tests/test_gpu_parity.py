@@ -295,6 +295,25 @@ def test_expert_ffn_float_matches_oracle(dev, M, name, xdt):
     assert_close(to_np(y), ref, f"{name}/{xdt} y_rows")
 
 
+@pytest.mark.parametrize("groups", [(8, 0, 0, 0), (5, 0, 3, 0)])
+def test_expert_ffn_rows_beyond_register_tile(dev, M, groups):
+    """A grouping in which an expert owns more rows than a decode launch's register tile of
+    token rows (2 tokens, 4 pairs each: the launches hold up to 2 rows of an expert at once,
+    so rows are taken in chunks).  Against the oracle on the same grouping."""
+    cfg = tiny(name="rbt", wtag=102, T=2, k=4, E=4, H=256, I=128)
+    t, inp = build(cfg, dev)
+    counts = np.array(groups)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    sorted_pairs = np.arange(cfg.T * cfg.k, dtype=np.int64)
+    perm = OL.Permutation(offsets, sorted_pairs, sorted_pairs.copy())
+    w = layer_weights(cfg, t)
+    y = M.moe_expert_ffn(w.experts, t["x"], "float", cfg.k, torch.from_numpy(offsets.astype(np.int32)).to(dev),
+                         torch.from_numpy(sorted_pairs.astype(np.int32)).to(dev))
+    ge, _ = host_expert_getter(cfg)
+    ref = OL.expert_rows(ge, OF.bf16_value(inp.x), perm, cfg.k)
+    assert_close(to_np(y), ref, f"groups {groups} y_rows")
+
+
 @pytest.mark.parametrize("xdt", ["bf16", "f32"])
 def test_expert_ffn_identity_form_prefill_float(dev, M, xdt):
     """The shared expert's form (NULL offsets, one expert) at a prefill size: the bf16
@@ -358,6 +377,9 @@ LAYER_CASES = {
     "tiny_fused_gated": tiny(name="tfg", wtag=87, T=3, k=3, shared="gated", shared_K=256, shared_I=128),
     "tiny_fused_fp8_ungated": tiny(name="tff", wtag=88, wfmt="fp8b128", score="sigmoid", select_bias_std=0.01,
                                    I=256, T=2, k=4, shared="ungated", shared_K=256, shared_I=256),
+    # an odd number of 32-value blocks per down row (the down-combine reads the two scale bytes
+    # of a lane one by one)
+    "tiny_fused_odd_blocks": tiny(name="tfo", wtag=101, T=2, k=2, I=96, shared="ungated", shared_K=256, shared_I=96),
     # prefill sizes on the bf16 matrix-core GEMM: the shared expert in the identity form, and
     # the latent form (float32 x_lat split into two bf16 terms)
     "prefill_gated_shared": tiny(name="pgs", wtag=97, T=160, H=512, I=160, E=8, k=2, shared="gated",
@@ -423,7 +445,7 @@ def test_layer_matches_oracle(dev, M, name):
     assert_close(to_np(out), ref.out, f"{name} out")
 
 
-FUSED_CASES = ["tiny", "tiny_fused_gated", "tiny_fused_fp8_ungated"]
+FUSED_CASES = ["tiny", "tiny_fused_gated", "tiny_fused_fp8_ungated", "tiny_fused_odd_blocks"]
 
 
 @pytest.mark.parametrize("name", FUSED_CASES)
