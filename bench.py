@@ -1,28 +1,37 @@
 #!/usr/bin/env python3
-"""Throughput of one routed MoE layer step on one MI355X, as one JSON line.
+"""Throughput of the routed MoE layer on one MI355X, as one JSON line.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME] [--no-prefill]
 
 A step is one pass of the whole layer (router, top-k, permutation, routed experts,
 shared expert, combine; LatentMoE projections where the workload has them) over one
 batch of seeded synthetic tokens, with all weights resident in HBM.  Steps rotate over
-several independently generated layer instances and token batches, so no step finds the
-previous step's weights in the 256 MB last-level cache.  Each step is captured once as a
-HIP graph; the timed region replays K graphs back to back between two events.
+four independently generated layer instances and sixteen token batches, so no step finds
+the previous step's weights in the 256 MB last-level cache.  Each step slot is captured
+once as a HIP graph; the timed region replays K graphs back to back between two events.
 
-Also reported:
-  roofline      the routed gate/up dequant-GEMV (the kernel that moves the most bytes):
-                algorithmic bytes per launch / its average duration, measured with events
-                on the launch stream in a second, instrumented pass of the same steps;
-  cpu_baseline  the float64 oracle on a bounded sample of the same workload, on the
-                host cores (a baseline only).
-  traffic       HBM bytes per launch of that kernel from the hardware counters (FETCH_SIZE,
-                WRITE_SIZE), each scaled by what the same counter reads for a 1 GiB copy, taken
-                from profiles/traffic_<workload>.json when its sources still match the library's;
-                otherwise null.  Collect with two counter passes over `--traffic-run`:
+The headline workload (`value`, `ms_per_step`) is the one-token decode layer.  By default
+the same run also times the two 512-token prefill workloads on the same expert instances
+(the weights are shared: no extra memory): the compute-bound slice in which every token
+goes to the same ten experts, and the Zipf-routed prefill.  They are reported under
+`prefill` with their own rooflines.
+
+Per kernel (`kernels`, and `roofline` for the decode gate/up, the kernel that moves the
+most bytes): algorithmic bytes or flops per launch / the kernel's mean duration.  The
+duration comes from HIP events recorded on the launch stream right before and after each
+launch, in an eager pass over the same step slots after the timed region, with the GPU
+kept busy so that the events bracket device time only.  rocprofv3 --kernel-trace --stats
+summaries of the same command are kept under profiles/.
+
+  traffic       HBM bytes per launch of the decode gate/up kernel from the hardware counters
+                (FETCH_SIZE, WRITE_SIZE), each scaled by what the same counter reads for a 1 GiB
+                copy, taken from profiles/traffic_<workload>.json when its sources still match the
+                library's; otherwise null.  Collect with two counter passes over `--traffic-run`:
                   rocprofv3 --pmc FETCH_SIZE -d D1 -o run --output-format csv -- python3 bench.py --traffic-run
                   rocprofv3 --pmc WRITE_SIZE -d D2 -o run --output-format csv -- python3 bench.py --traffic-run
                   python3 bench.py --traffic-parse D1 D2
+  cpu_baseline  the float64 oracle on a bounded sample of the decode workload on the host cores,
+                plus one-thread times of the small layer and of one decode step (a baseline only).
 """
 from __future__ import annotations
 
@@ -36,15 +45,20 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "mxfp4_routed_expert_amd", "csrc")
 PEAK_HBM_GBPS = 8000.0
 PEAK_TFLOPS = {"fp4": 10100.0, "fp8": 5000.0, "bf16": 2500.0}
+PREFILL_DEFAULT = ("qwen38max_prefill_hot", "qwen38max_prefill")
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _mx_bytes(values):
+    return values * 17 // 32
+
+
 def algorithmic(cfg, D, fused=False):
     """Algorithmic bytes and flops of one step at D distinct routed experts touched, for the
-    layer and for the routed gate/up kernel (weights of touched experts, router, shared
+    layer and for the routed gate/up launch (weights of touched experts, router, shared
     expert and projections once, activations in and out once).  `fused`: the gate/up launch
     also computes the shared expert's gate/up (its weights and h rows count there too)."""
     K, I, H, T, k = cfg.d_model, cfg.I, cfg.H, cfg.T, cfg.k
@@ -64,7 +78,7 @@ def algorithmic(cfg, D, fused=False):
     if cfg.latent:
         flops += 2 * T * 2 * cfg.latent * H
     if cfg.act == "mxfp4":
-        gu_in, gu_out = T * K * 17 // 32, P * I * 17 // 32
+        gu_in, gu_out = _mx_bytes(T * K), _mx_bytes(P * I)
     else:
         gu_in, gu_out = T * K * (4 if cfg.latent else 2), P * I * 4
     gu_bytes, gu_flops = D * gu_w + gu_in + gu_out, 2 * P * 2 * K * I
@@ -74,37 +88,26 @@ def algorithmic(cfg, D, fused=False):
     return dict(layer_bytes=layer_bytes, layer_flops=flops, gu_bytes=gu_bytes, gu_flops=gu_flops)
 
 
-def cpu_baseline(cfg, steps):
-    """The float64 oracle on `steps` layer steps (token batches 0..steps-1 of instance 0)."""
-    import synth
-    from oracle import layer as OL
-    try:
-        from threadpoolctl import threadpool_info, threadpool_limits
-    except ImportError:
-        threadpool_info = threadpool_limits = None
-    cores = len(os.sched_getaffinity(0))
-    limiter = threadpool_limits(cores) if threadpool_limits else None
-    total = 0.0
-    cache = {}
-    for b in range(steps):
-        inp = synth.layer_inputs_np(cfg, 0, 0, b)
-        r = OL.route(inp.x, inp.w_router, cfg.k, cfg.score, cfg.renormalize, cfg.routed_scaling, inp.logit_bias,
-                     inp.select_bias, inp.w_shared_gate if cfg.shared == "gated" else None)
-        for e in set(int(v) for v in r.ids.reshape(-1)):        # generation is not timed
-            if e not in cache:
-                cache[e] = synth.expert_np(cfg, e)
-        if cfg.shared and "s" not in cache:
-            cache["s"] = synth.expert_np(cfg, synth.SHARED)
-        t0 = time.perf_counter()
-        OL.layer(cfg, inp, lambda e: cache[e], lambda: cache["s"])
-        total += time.perf_counter() - t0
-    # threads the oracle could use: the BLAS pools (NumPy's elementwise work is single-threaded)
-    used = max((i.get("num_threads", 1) for i in threadpool_info()), default=1) if threadpool_info else 1
-    if limiter is not None:
-        limiter.restore_original_limits()
-    return dict(value=steps * cfg.T / total, unit="tokens/s", cores=used, kind="oracle",
-                sample=f"{steps} step(s) of {cfg.name} ({steps * cfg.T} tokens), float64 NumPy, "
-                       f"{total:.1f} s; expert bytes generated outside the timed region")
+def down_algorithmic(cfg, D, fused=False):
+    """Algorithmic bytes and flops of the routed down launch: the touched experts' down
+    weights, h in, the rows out.  `fused`: the decode down product with the combine, which
+    also covers the shared expert's down rows and writes one output row per token."""
+    K, I, T, k = cfg.d_model, cfg.I, cfg.T, cfg.k
+    P = T * k
+    w_down = K * I * 17 // 32 if cfg.wfmt == "mxfp4" else K * I + (K // 128) * (I // 128) * 4
+    flops = 2 * P * K * I
+    if cfg.act == "mxfp4":
+        h_in, out = _mx_bytes(P * I), P * K * 4
+    else:
+        h_in, out = P * I * 4, P * K * 4
+    nbytes = D * w_down + h_in + out
+    if fused:
+        out = T * K * 4
+        nbytes = D * w_down + h_in + out
+        if cfg.shared:
+            nbytes += cfg.expert_bytes(cfg.shared_K, cfg.shared_I) // 3 + T * cfg.shared_I * 4
+            flops += 2 * T * K * cfg.shared_I
+    return dict(bytes=nbytes, flops=flops)
 
 
 def dominant_kernel(cfg):
@@ -113,7 +116,20 @@ def dominant_kernel(cfg):
         return r"mxgemm_kernel<true, true>"
     if cfg.wfmt == "mxfp4" and cfg.T >= 64:
         return r"fgemm_pair_kernel<\w+, true>"
+    if cfg.T <= 8:
+        return r"gemv_flat_kernel<\d+, \d+, \d+, true>"
     return r"gemv_kernel<\d+, \d+, \d+, true, true>"
+
+
+def down_kernel(cfg, fused):
+    """Name pattern of the routed down kernel of a workload."""
+    if fused:
+        return r"down_combine_mfma_kernel" if cfg.wfmt == "mxfp4" else r"down_combine_kernel"
+    if cfg.act == "mxfp4" and cfg.T >= 64:
+        return r"mxgemm_kernel<false, true>"
+    if cfg.wfmt == "mxfp4" and cfg.T >= 64:
+        return r"fgemm_down_kernel"
+    return r"gemv_\w*kernel<\d+, \d+, \d+, false"
 
 
 def source_digest():
@@ -174,45 +190,75 @@ def parse_traffic(cfg, fetch_dir, write_dir):
     print(json.dumps(res))
 
 
-def main():
-    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="qwen38max_decode")
-    ap.add_argument("--instances", type=int, default=4, help="independent layer instances rotated over")
-    ap.add_argument("--batches", type=int, default=16, help="token batches rotated over")
-    ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps for the CPU baseline (0: skip)")
-    ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of graph replays")
-    ap.add_argument("--json-out", default=None)
-    ap.add_argument("--traffic-run", action="store_true",
-                    help="run a few steps and a 1 GiB calibration copy, untimed (for counter passes)")
-    ap.add_argument("--traffic-parse", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
-                    help="turn two counter passes into profiles/traffic_<workload>.json")
-    args = ap.parse_args()
-    if args.traffic_parse:
-        import synth
-        parse_traffic(synth.get(args.config), *args.traffic_parse)
-        return
+def roofline(nbytes, flops, us, peak_tflops):
+    """bound (the roof the kernel's intensity puts it under), achieved, peak, unit, frac."""
+    if flops / nbytes * PEAK_HBM_GBPS * 1e9 > peak_tflops * 1e12:
+        a = flops / (us * 1e-6) / 1e12
+        return dict(bound="mfma", achieved=round(a, 1), peak=peak_tflops, unit="TFLOP/s", frac=round(a / peak_tflops, 4))
+    a = nbytes / (us * 1e-6) / 1e9
+    return dict(bound="hbm", achieved=round(a, 1), peak=PEAK_HBM_GBPS, unit="GB/s", frac=round(a / PEAK_HBM_GBPS, 4))
 
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
-              file=sys.stderr)
-        sys.exit(2)
 
-    import torch
+def peak_for(cfg):
+    """Matrix peak of the arithmetic the routed products run in."""
+    if cfg.act == "mxfp4":
+        return PEAK_TFLOPS["fp4"]
+    return PEAK_TFLOPS["bf16"]
+
+
+# ------------------------------------------------------------------ CPU baseline
+
+def _oracle_step(cfg, b, cache):
     import synth
-    from synth import device as sdev
-    import mxfp4_routed_expert_amd as M
+    from oracle import layer as OL
+    inp = synth.layer_inputs_np(cfg, 0, 0, b)
+    r = OL.route(inp.x, inp.w_router, cfg.k, cfg.score, cfg.renormalize, cfg.routed_scaling, inp.logit_bias,
+                 inp.select_bias, inp.w_shared_gate if cfg.shared == "gated" else None)
+    for e in set(int(v) for v in r.ids.reshape(-1)):        # generation is not timed
+        if (cfg.name, e) not in cache:
+            cache[(cfg.name, e)] = synth.expert_np(cfg, e)
+    if cfg.shared and (cfg.name, "s") not in cache:
+        cache[(cfg.name, "s")] = synth.expert_np(cfg, synth.SHARED)
+    t0 = time.perf_counter()
+    OL.layer(cfg, inp, lambda e: cache[(cfg.name, e)], lambda: cache[(cfg.name, "s")])
+    return time.perf_counter() - t0
 
-    cfg = synth.get(args.config)
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    R, NB = max(1, args.instances), max(1, args.batches)
-    log(f"[bench] {cfg.name}: building {R} layer instance(s)")
+
+def cpu_baseline(cfg, steps):
+    """The float64 oracle on `steps` steps of `cfg` (token batches 0..steps-1 of instance 0)
+    with the host's BLAS threads, and one-thread times of one step of the small layer and
+    of `cfg`."""
+    import synth
+    try:
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except ImportError:
+        threadpool_info = threadpool_limits = None
+    affinity = len(os.sched_getaffinity(0))
+    cache = {}
+    limiter = threadpool_limits(affinity) if threadpool_limits else None
+    total = sum(_oracle_step(cfg, b, cache) for b in range(steps))
+    used = max((i.get("num_threads", 1) for i in threadpool_info()), default=1) if threadpool_info else 1
+    if limiter is not None:
+        limiter.restore_original_limits()
+    one = {}
+    if threadpool_limits:
+        small = synth.get("tiny")
+        with threadpool_limits(1):
+            one = {small.name: round(small.T / _oracle_step(small, 0, cache), 2),
+                   cfg.name: round(cfg.T / _oracle_step(cfg, 0, cache), 4)}
+    return dict(value=round(steps * cfg.T / total, 4), unit="tokens/s", cores=used, kind="oracle",
+                sample=f"{steps} step(s) of {cfg.name} ({steps * cfg.T} tokens), float64 NumPy, {total:.1f} s; "
+                       f"expert bytes generated outside the timed region",
+                affinity_cores=affinity, cpu_count=os.cpu_count(), one_thread_tokens_per_s=one)
+
+
+# ------------------------------------------------------------------ GPU runs
+
+def make_layers(M, sdev, cfg, insts, dev):
+    """One MoELayer per instance, on the instance's shared expert stacks."""
     layers = []
-    for r in range(R):
-        t, _ = sdev.layer_tensors(cfg, dev, 0, r)
+    for inst, (ex, sh) in enumerate(insts):
+        t, _ = sdev.layer_tensors(cfg, dev, 0, inst, experts=ex, shared=sh)
         w = M.LayerWeights(score=cfg.score, k=cfg.k, renormalize=cfg.renormalize, routed_scaling=cfg.routed_scaling,
                            act=cfg.act, w_router=t["w_router"], experts=M.ExpertWeights.from_arrays(t["experts"]),
                            logit_bias=t["logit_bias"], select_bias=t["select_bias"],
@@ -220,19 +266,23 @@ def main():
                            w_shared_gate=t["w_shared_gate"] if cfg.shared == "gated" else None,
                            p_down=t["p_down"], p_up=t["p_up"])
         layers.append(M.MoELayer(w, cfg.T, dev))
+    return layers
+
+
+def run_workload(torch, sdev, cfg, layers, NB, steps, warmup, use_graphs, dev, traffic_run=False):
+    """Time `steps` layer steps (graph replays over the step slots); then count the distinct
+    experts of every slot and time the routed gate/up and down launches with events."""
+    R = len(layers)
     xs = [sdev.token_batch(cfg, dev, 0, 0, b) for b in range(NB)]
     S = max(R, NB)
     slot = lambda j: (layers[j % R], xs[j % NB])
     torch.cuda.synchronize()
-
-    # eager warm-up of every slot (also what the graphs capture)
-    for j in range(S):
+    for j in range(S):                                   # eager warm-up of every slot
         L, x = slot(j)
         L.forward(x)
     torch.cuda.synchronize()
     graphs = None
-    if not args.no_graph:
-        log("[bench] capturing one graph per step slot")
+    if use_graphs:
         graphs = []
         stream = torch.cuda.Stream()
         stream.wait_stream(torch.cuda.current_stream())
@@ -253,25 +303,21 @@ def main():
             L, x = slot(s)
             L.forward(x)
 
-    for s in range(args.warmup):
+    for s in range(warmup):
         step(s)
     torch.cuda.synchronize()
-    if args.traffic_run:
-        for s in range(args.steps):
-            step(args.warmup + s)
-        a = torch.empty(1 << 27, dtype=torch.float64, device=dev).fill_(1.0)
-        torch.neg(a)
+    if traffic_run:
+        for s in range(steps):
+            step(warmup + s)
         torch.cuda.synchronize()
-        log("[bench] traffic run done")
-        return
+        return None
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
-    for s in range(args.steps):
-        step(args.warmup + s)
+    for s in range(steps):
+        step(warmup + s)
     ev1.record()
     torch.cuda.synchronize()
-    ms_per_step = ev0.elapsed_time(ev1) / args.steps
-    log(f"[bench] {args.steps} steps: {ms_per_step * 1e3:.2f} us/step")
+    ms_per_step = ev0.elapsed_time(ev1) / steps
 
     # distinct routed experts touched per slot (read back after a step of that slot)
     D_slot = []
@@ -281,66 +327,244 @@ def main():
         torch.cuda.synchronize()
         offs = L.offs.cpu()
         D_slot.append(int(((offs[1:] - offs[:-1]) > 0).sum()))
-    D_steps = [D_slot[(args.warmup + s) % S] for s in range(args.steps)]
-    D_mean = sum(D_steps) / len(D_steps)
+    D_steps = [D_slot[(warmup + s) % S] for s in range(steps)]
 
-    # instrumented pass: events around the routed gate/up kernel on its stream.  A block of
-    # matrix products is queued first so every step of the pass is enqueued before the GPU
-    # reaches it (no host gaps inside the measured intervals).
+    # per-kernel durations: events on the step's stream around the routed gate/up and down
+    # calls, over the same slots; a block of matrix products queued first keeps the GPU busy,
+    # so every launch of the pass is enqueued before the GPU reaches it
+    n = min(steps, 2 * S)
     a = torch.randn(8192, 8192, device=dev)
-    for _ in range(4):
+    for _ in range(4 if cfg.T < 64 else 8):
         a = a @ a * 1e-4
-    marks = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
-    for s in range(args.steps):
-        L, x = slot(args.warmup + s)
-        pair = marks[s]
-        L.forward(x, mark=lambda name, pair=pair: pair[0 if name == "gateup_begin" else 1].record())
+    ev = [{k: torch.cuda.Event(enable_timing=True) for k in ("gateup_begin", "gateup_end", "down_begin", "down_end")}
+          for _ in range(n)]
+    for s in range(n):
+        L, x = slot(warmup + s)
+        L.forward(x, mark=lambda name, e=ev[s]: e[name].record())
     torch.cuda.synchronize()
-    gu_ms = [b.elapsed_time(c) for b, c in marks]
-    gu_us = 1e3 * sum(gu_ms) / len(gu_ms)
     del a
+    gu_us = 1e3 * sum(e["gateup_begin"].elapsed_time(e["gateup_end"]) for e in ev) / n
+    dn_us = 1e3 * sum(e["down_begin"].elapsed_time(e["down_end"]) for e in ev) / n
+    D_ev = [D_slot[(warmup + s) % S] for s in range(n)]
+    # launches of each step kernel, in order: eager warm-up (one per slot), warm-up replays,
+    # timed replays, the per-slot expert count, the instrumented pass
+    phases = [["warm", S], ["warm_replay", warmup], ["timed", steps], ["count", S], ["events", n]]
+    return dict(ms_per_step=ms_per_step, D_steps=D_steps, D_ev=D_ev, gu_us=gu_us, dn_us=dn_us, launches=n,
+                graphs=graphs is not None, slots=S, phases=phases)
 
+
+def kernel_entries(cfg, fused, r):
+    """Roofline entries of the routed gate/up and down launches of one workload."""
+    peak = peak_for(cfg)
+    D_ev = r["D_ev"]
+    gu = [algorithmic(cfg, D, fused) for D in D_ev]
+    dn = [down_algorithmic(cfg, D, fused) for D in D_ev]
+    gu_b, gu_f = sum(x["gu_bytes"] for x in gu) / len(gu), sum(x["gu_flops"] for x in gu) / len(gu)
+    dn_b, dn_f = sum(x["bytes"] for x in dn) / len(dn), sum(x["flops"] for x in dn) / len(dn)
+    timing = ("HIP events on the launch stream around each launch, eager pass over the step slots "
+              "after the timed region, GPU kept busy; mean over launches")
+    out = []
+    for role, pat, b, f, us in (("routed gate/up" + (" + shared gate/up" if fused and cfg.shared else ""),
+                                 dominant_kernel(cfg), gu_b, gu_f, r["gu_us"]),
+                                ("routed down" + (" + shared down + combine" if fused else ""),
+                                 down_kernel(cfg, fused), dn_b, dn_f, r["dn_us"])):
+        e = dict(workload=cfg.name, role=role, kernel=pat)
+        e.update(roofline(b, f, us, peak))
+        e.update(bytes_per_launch=int(b), flops_per_launch=int(f), avg_launch_us=round(us, 2), launches=r["launches"],
+                 timing=timing, phases=r["phases"])
+        out.append(e)
+    return out
+
+
+def profile_file(cfg):
+    return os.path.join(HERE, "profiles", f"kernels_{cfg.name}.json")
+
+
+def attach_profile(cfg, kernels):
+    """Add the rocprofv3 mean duration of each kernel over the timed replays of the same
+    command (profiles/kernels_<workload>.json, written by --profile-parse) when that file's
+    sources match the library's; the fraction recomputed from it goes beside the events'."""
+    try:
+        with open(profile_file(cfg)) as f:
+            prof = json.load(f)
+    except (OSError, ValueError):
+        return
+    if prof.get("source_sha256") != source_digest():
+        return
+    by = {(k["workload"], k["kernel"]): k for k in prof["kernels"]}
+    for e in kernels:
+        k = by.get((e["workload"], e["kernel"]))
+        if k is None:
+            continue
+        us = k["timed_mean_us"]
+        a = e["flops_per_launch"] / (us * 1e-6) / 1e12 if e["bound"] == "mfma" else e["bytes_per_launch"] / (us * 1e-6) / 1e9
+        e["rocprof"] = dict(avg_launch_us=round(us, 2), achieved=round(a, 1), frac=round(a / e["peak"], 4),
+                            launches=k["timed_launches"], file=os.path.relpath(profile_file(cfg), HERE))
+
+
+def parse_profile(trace_dir, json_line_file, headline):
+    """rocprofv3 kernel trace of a bench run + that run's JSON line -> profiles/kernels_<workload>.json:
+    per kernel of the line, the mean duration of its launches in the timed replays (each workload's
+    launches of a kernel are taken in run order, sliced by the phases the line records)."""
+    import csv
+    import glob
+    import re
+    with open(json_line_file) as f:
+        res = json.loads([l for l in f.read().splitlines() if l.startswith("{")][-1])
+    rows = []
+    for fn in glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True):
+        rows += list(csv.DictReader(open(fn)))
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    used = {}
+    out = []
+    for e in res["kernels"]:
+        pat = re.compile(e["kernel"])
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows if pat.search(r["Kernel_Name"])]
+        start = used.get(e["kernel"], 0)
+        n_all = sum(c for _, c in e["phases"])
+        mine = durs[start:start + n_all]
+        used[e["kernel"]] = start + n_all
+        off = 0
+        timed = []
+        for name, c in e["phases"]:
+            if name == "timed":
+                timed = mine[off:off + c]
+            off += c
+        if not timed:
+            raise SystemExit(f"no timed launches of {e['kernel']} for {e['workload']} in {trace_dir}")
+        out.append(dict(workload=e["workload"], kernel=e["kernel"], role=e["role"], timed_launches=len(timed),
+                        timed_mean_us=sum(timed) / len(timed), timed_min_us=min(timed), timed_max_us=max(timed),
+                        all_launches=len(mine)))
+    cfg_name = res["config"]["workload"]
+    prof = {"workload": cfg_name, "source_sha256": source_digest(), "kernels": out,
+            "commands": [f"rocprofv3 --kernel-trace --stats -d P -o run --output-format csv -- python3 bench.py "
+                         f"--config {cfg_name} --cpu-steps 0 --json-out P/line.json",
+                         f"python3 bench.py --config {cfg_name} --profile-parse P P/line.json"]}
+    path = os.path.join(HERE, "profiles", f"kernels_{cfg_name}.json")
+    with open(path, "w") as f:
+        json.dump(prof, f, indent=1)
+    print(json.dumps(prof))
+
+
+def workload_summary(cfg, fused, r):
+    alg = [algorithmic(cfg, D, fused) for D in r["D_steps"]]
+    step_s = r["ms_per_step"] * 1e-3
+    lb = sum(x["layer_bytes"] for x in alg) / len(alg)
+    lf = sum(x["layer_flops"] for x in alg) / len(alg)
+    return dict(bytes_per_step=int(lb), flops_per_step=int(lf), **{"GB/s": round(lb / step_s / 1e9, 1)},
+                hbm_frac=round(lb / step_s / 1e9 / PEAK_HBM_GBPS, 4), **{"TFLOP/s": round(lf / step_s / 1e12, 2)},
+                distinct_experts_per_step=round(sum(r["D_steps"]) / len(r["D_steps"]), 2))
+
+
+def arith_of(cfg):
+    return {("mxfp4", "float"): "mxfp4 weights decoded exactly to bf16 x bf16 activations, fp32 accumulate",
+            ("mxfp4", "mxfp4"): "mxfp4 weights x OCP-MX fp4 activations on the scaled MFMA, fp32 accumulate",
+            ("fp8b128", "float"): "fp8 e4m3 weights decoded exactly to bf16 x bf16 activations, fp32 accumulate"
+            }[(cfg.wfmt, cfg.act)]
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="qwen38max_decode", help="headline workload")
+    ap.add_argument("--prefill", nargs="*", default=None,
+                    help="further workloads timed in the same run (default: the two 512-token prefills "
+                         "when the headline is the decode layer)")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--prefill-steps", type=int, default=20)
+    ap.add_argument("--instances", type=int, default=4, help="independent layer instances rotated over")
+    ap.add_argument("--batches", type=int, default=16, help="token batches rotated over")
+    ap.add_argument("--cpu-steps", type=int, default=3, help="oracle steps for the CPU baseline (0: skip)")
+    ap.add_argument("--no-graph", action="store_true", help="launch steps eagerly instead of graph replays")
+    ap.add_argument("--json-out", default=None)
+    ap.add_argument("--traffic-run", action="store_true",
+                    help="run a few steps and a 1 GiB calibration copy, untimed (for counter passes)")
+    ap.add_argument("--traffic-parse", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="turn two counter passes into profiles/traffic_<workload>.json")
+    ap.add_argument("--profile-parse", nargs=2, metavar=("TRACE_DIR", "JSON_LINE"),
+                    help="turn a rocprofv3 --kernel-trace run of this command into profiles/kernels_<workload>.json")
+    args = ap.parse_args()
+    if args.traffic_parse:
+        import synth
+        parse_traffic(synth.get(args.config), *args.traffic_parse)
+        return
+    if args.profile_parse:
+        parse_profile(*args.profile_parse, args.config)
+        return
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: the library has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import synth
+    from synth import device as sdev
+    import mxfp4_routed_expert_amd as M
+
+    cfg = synth.get(args.config)
+    if args.no_prefill or args.traffic_run:
+        extra = []
+    elif args.prefill is not None:
+        extra = [synth.get(n) for n in args.prefill]
+    else:
+        extra = [synth.get(n) for n in PREFILL_DEFAULT] if cfg.name == "qwen38max_decode" else []
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    R, NB = max(1, args.instances), max(1, args.batches)
+
+    # expert stacks per (weight stream, instance): workloads with the same stream share them
+    stacks = {}
+
+    def instances(c):
+        key = (c.wtag, c.wfmt, c.d_model, c.I, c.E, c.shared_K, c.shared_I)
+        if key not in stacks:
+            log(f"[bench] generating {R} expert instance(s) for {c.name}")
+            stacks[key] = [(synth.experts_torch(c, dev, 0, r),
+                            synth.experts_torch(c, dev, 0, r, shared=True) if c.shared else None) for r in range(R)]
+        return stacks[key]
+
+    log(f"[bench] {cfg.name}: {R} instance(s), {NB} token batches")
+    layers = make_layers(M, sdev, cfg, instances(cfg), dev)
     fused = layers[0].fused
-    alg = [algorithmic(cfg, D, fused) for D in D_steps]
-    gu_bytes = sum(x["gu_bytes"] for x in alg) / len(alg)
-    gu_flops = sum(x["gu_flops"] for x in alg) / len(alg)
-    layer_bytes = sum(x["layer_bytes"] for x in alg) / len(alg)
-    layer_flops = sum(x["layer_flops"] for x in alg) / len(alg)
-    step_s = ms_per_step * 1e-3
-    peak_flops = PEAK_TFLOPS["fp4"] if cfg.act == "mxfp4" else (PEAK_TFLOPS["fp8"] if cfg.wfmt != "mxfp4" else
-                                                                  PEAK_TFLOPS["bf16"])
-    intensity = gu_flops / gu_bytes
-    if intensity * PEAK_HBM_GBPS * 1e9 > peak_flops * 1e12:
-        achieved = gu_flops / (gu_us * 1e-6) / 1e12
-        roof = dict(bound="mfma", achieved=round(achieved, 2), peak=peak_flops, unit="TFLOP/s",
-                    frac=round(achieved / peak_flops, 4))
-    else:
-        achieved = gu_bytes / (gu_us * 1e-6) / 1e9
-        roof = dict(bound="hbm", achieved=round(achieved, 1), peak=PEAK_HBM_GBPS, unit="GB/s",
-                    frac=round(achieved / PEAK_HBM_GBPS, 4))
-    if cfg.act == "mxfp4" and cfg.T >= 64:
-        kname = "routed gate/up grouped GEMM (mxgemm_kernel, FP4 x FP4)"
-    elif cfg.wfmt == "mxfp4" and cfg.T >= 64:
-        kname = "routed gate/up grouped GEMM (fgemm_pair_kernel, MXFP4 weights decoded to bf16)"
-    else:
-        kname = "moe::gemv_kernel (routed gate/up" + (" + shared gate/up" if fused and cfg.shared else "") + \
-                ", fused SwiGLU)"
-    roof.update(traffic=load_traffic(cfg), kernel=kname,
-                bytes_per_launch=int(gu_bytes), flops_per_launch=int(gu_flops), avg_launch_us=round(gu_us, 2),
-                launches=len(gu_ms))
+    r = run_workload(torch, sdev, cfg, layers, NB, args.steps, args.warmup, not args.no_graph, dev,
+                     traffic_run=args.traffic_run)
+    if args.traffic_run:
+        a = torch.empty(1 << 27, dtype=torch.float64, device=dev).fill_(1.0)
+        torch.neg(a)
+        torch.cuda.synchronize()
+        log("[bench] traffic run done")
+        return
+    log(f"[bench] {cfg.name}: {args.steps} steps, {r['ms_per_step'] * 1e3:.2f} us/step")
+    kernels = kernel_entries(cfg, fused, r)
+    del layers
+
+    prefill = {}
+    for pc in extra:
+        pl = make_layers(M, sdev, pc, instances(pc), dev)
+        pf = pl[0].fused
+        pr = run_workload(torch, sdev, pc, pl, NB, args.prefill_steps, 2, not args.no_graph, dev)
+        log(f"[bench] {pc.name}: {args.prefill_steps} steps, {pr['ms_per_step'] * 1e3:.1f} us/step")
+        pk = kernel_entries(pc, pf, pr)
+        kernels += pk
+        prefill[pc.name] = dict(T=pc.T, steps=args.prefill_steps, warmup=2, ms_per_step=round(pr["ms_per_step"], 5),
+                                tokens_per_s=round(pc.T / (pr["ms_per_step"] * 1e-3), 1),
+                                dtype="fp4" if pc.act == "mxfp4" else "bf16", arith=arith_of(pc),
+                                routing=pc.notes, layer=workload_summary(pc, pf, pr), roofline=pk[0])  # (same dict)
+        del pl
+        torch.cuda.empty_cache()
 
     cpu = None
     if args.cpu_steps > 0:
-        log(f"[bench] CPU baseline: oracle on {args.cpu_steps} step(s)")
+        log(f"[bench] CPU baseline: oracle on {args.cpu_steps} step(s) of {cfg.name}")
         cpu = cpu_baseline(cfg, args.cpu_steps)
 
-    # arithmetic type of the dominant products: bf16 dot products on exactly decoded weights
-    # (FLOAT mode), or FP4 x FP4 on the block-scaled MFMA (MX mode); fp32 accumulation
-    dtype = "fp4" if cfg.act == "mxfp4" else "bf16"
-    arith = {("mxfp4", "float"): "mxfp4 weights decoded exactly to bf16 x bf16 activations, fp32 accumulate",
-             ("mxfp4", "mxfp4"): "mxfp4 weights x OCP-MX fp4 activations on the scaled MFMA, fp32 accumulate",
-             ("fp8b128", "float"): "fp8 e4m3 weights decoded exactly to bf16 x bf16 activations, fp32 accumulate"
-             }[(cfg.wfmt, cfg.act)]
+    attach_profile(cfg, kernels)
+    roof = dict(kernels[0])
+    roof["traffic"] = load_traffic(cfg)
+    step_s = r["ms_per_step"] * 1e-3
     res = {
         "metric": "MoE layer tokens/s; decode HBM GB/s and prefill TFLOP/s as % roofline",
         "value": round(cfg.T / step_s, 2),
@@ -348,21 +572,22 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(r["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": dtype,
+        # arithmetic type of the dominant products: bf16 dot products on exactly decoded
+        # weights (FLOAT mode) or FP4 x FP4 on the block-scaled MFMA (MX mode); fp32 accumulation
+        "dtype": "fp4" if cfg.act == "mxfp4" else "bf16",
         "data": "synthetic",
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "d_model": cfg.d_model, "I": cfg.I, "E": cfg.E,
                    "k": cfg.k, "score": cfg.score, "weights": cfg.wfmt, "activations": cfg.act,
-                   "shared": cfg.shared, "latent": cfg.latent, "arith": arith, "instances": R, "token_batches": NB,
-                   "graphs": graphs is not None, "distinct_experts_per_step": round(D_mean, 2)},
-        "layer": {"bytes_per_step": int(layer_bytes), "flops_per_step": int(layer_flops),
-                  "GB/s": round(layer_bytes / step_s / 1e9, 1),
-                  "hbm_frac": round(layer_bytes / step_s / 1e9 / PEAK_HBM_GBPS, 4),
-                  "TFLOP/s": round(layer_flops / step_s / 1e12, 3)},
+                   "shared": cfg.shared, "latent": cfg.latent, "arith": arith_of(cfg), "instances": R,
+                   "token_batches": NB, "graphs": r["graphs"]},
+        "layer": workload_summary(cfg, fused, r),
         "roofline": roof,
+        "kernels": kernels,
+        "prefill": prefill,
         "cpu_baseline": cpu,
     }
     line = json.dumps(res)

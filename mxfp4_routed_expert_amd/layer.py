@@ -113,8 +113,10 @@ class MoELayer:
     def forward(self, x, mark=None):
         """One layer step on tokens x (bf16 [T][H]); returns the float32 output buffer.
 
-        With `mark`, mark("gateup_begin") / mark("gateup_end") are called around the routed
-        gate/up call, so a caller can record events on the stream around that kernel."""
+        With `mark`, mark(name) is called on the step's stream before and after the routed
+        gate/up call ("gateup_begin", "gateup_end") and the down call ("down_begin",
+        "down_end"; the down product with the combine in the fused form), so a caller can
+        record events around those kernels."""
         w = self.w
         if self.fused:
             B.moe_route_permute(x, w.w_router, w.k, w.score, w.renormalize, w.routed_scaling, w.logit_bias,
@@ -126,8 +128,12 @@ class MoELayer:
             B.moe_expert_gateup_shared(w.experts, w.shared, x, w.k, self.offs, self.sp, out=(self.h, self.h_sh))
             if mark is not None:
                 mark("gateup_end")
+            if mark is not None:
+                mark("down_begin")
             B.moe_expert_down_combine(w.experts, w.shared, self.h, self.h_sh, self.ids, self.topk_w, self.p2r,
                                       self.sg, out=self.out)
+            if mark is not None:
+                mark("down_end")
             return self.out
         mx = w.act == "mxfp4"
         if w.shared is not None:
@@ -151,7 +157,11 @@ class MoELayer:
                             out=(None if mx else self.h, self.hq, self.hs), ws=self.ws_gu)
         if mark is not None:
             mark("gateup_end")
+        if mark is not None:
+            mark("down_begin")
         B.moe_expert_down(w.experts, self.T, w.act, w.k, self.offs, self.h, self.hq, self.hs, out=self.y_rows)
+        if mark is not None:
+            mark("down_end")
         if w.shared is not None:
             cur.wait_stream(self.side)
         if w.p_up is not None:

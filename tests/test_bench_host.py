@@ -34,9 +34,34 @@ def test_mx_prefill_gateup_bytes():
     assert a["gu_bytes"] == 10 * 2 * 2368 * 3808 + 512 * 7168 * 17 // 32 + 5120 * 2368 * 17 // 32
 
 
+def test_decode_down_combine_bytes_and_flops():
+    cfg = synth.get("qwen38max_decode")
+    a = bench.down_algorithmic(cfg, 10, fused=True)
+    row = 2368 * 17 // 32                             # one MXFP4 down row over d_ff = 2368: 1258 B
+    assert row == 1258
+    routed, shared = 10 * 7168 * row, 7168 * row      # ten experts' down matrices and the shared one
+    h_in, hs_in, out = 10 * 2368 * 4, 2368 * 4, 7168 * 4
+    assert a["bytes"] == routed + shared + h_in + hs_in + out == 99_323_648
+    assert a["flops"] == 2 * 11 * 7168 * 2368
+
+
+def test_mx_prefill_down_bytes_and_flops():
+    cfg = synth.get("qwen38max_prefill_hot")
+    a = bench.down_algorithmic(cfg, 10, fused=False)
+    assert a["bytes"] == 10 * 7168 * 1258 + 5120 * 2368 * 17 // 32 + 5120 * 7168 * 4
+    assert a["flops"] == 2 * 5120 * 7168 * 2368
+
+
+def test_roofline_picks_the_binding_roof():
+    hbm = bench.roofline(198_500_096, 746_848_256, 40.0, bench.PEAK_TFLOPS["bf16"])
+    assert hbm["bound"] == "hbm" and abs(hbm["achieved"] - 198_500_096 / 40e-6 / 1e9) < 0.1
+    mfma = bench.roofline(237_000_000, 347_623_915_520, 100.0, bench.PEAK_TFLOPS["fp4"])
+    assert mfma["bound"] == "mfma" and abs(mfma["frac"] - 347_623_915_520 / 100e-6 / 1e12 / 10100.0) < 1e-4
+
+
 def test_dominant_kernel_patterns_select_one_instantiation():
     names = {
-        "qwen38max_decode": ("void moe::gemv_kernel<0, 0, 1, true, true>(moe::GemvParams)",
+        "qwen38max_decode": ("void moe::gemv_flat_kernel<0, 0, 1, true>(moe::GemvParams)",
                              "void moe::gemv_kernel<0, 0, 1, true, false>(moe::GemvParams)"),
         "qwen38max_prefill_hot": ("void moe::mxgemm_kernel<true, true>(moe::GemmParams)",
                                   "void moe::mxgemm_kernel<true, false>(moe::GemmParams)"),
