@@ -48,8 +48,8 @@ def _compile(src: str, build_dir: str = BUILD, extra=()) -> str:
 
 
 def build(jobs: int = 8, verbose: bool = False, extra_flags=(), out: str = LIB, build_dir: str = BUILD) -> str:
-    """Compile every csrc/*.hip and link `out`.  extra_flags (e.g. -D tuning overrides) and
-    another out/build_dir produce a variant build next to the default one."""
+    """Compile every csrc/*.hip and link `out` (extra compiler flags and another out/build_dir
+    give a separate build next to the default one)."""
     os.makedirs(build_dir, exist_ok=True)
     srcs = sources()
     with cf.ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
@@ -68,11 +68,10 @@ def build(jobs: int = 8, verbose: bool = False, extra_flags=(), out: str = LIB, 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("-j", type=int, default=min(8, os.cpu_count() or 1))
-    ap.add_argument("-D", action="append", default=[], help="extra preprocessor definition (NAME=VALUE)")
     ap.add_argument("--out", default=LIB)
     ap.add_argument("--build-dir", default=BUILD)
     a = ap.parse_args()
-    build(a.j, verbose=True, extra_flags=[f"-D{d}" for d in a.D], out=os.path.abspath(a.out),
+    build(a.j, verbose=True, out=os.path.abspath(a.out),
           build_dir=os.path.abspath(a.build_dir))
 
 

@@ -36,18 +36,8 @@
 
 namespace moe {
 
-#ifndef MOE_USE_BF16_GEMM
-#define MOE_USE_BF16_GEMM 1                // 0: prefill with unquantised activations on the GEMV
-#endif
-#ifndef MOE_FGEMM_SKIP_DEAD
-#define MOE_FGEMM_SKIP_DEAD 1              // 0: compute 16-row tiles past an expert's last row too
-#endif
-#ifndef MOE_FGEMM_PAIR_PF
-#define MOE_FGEMM_PAIR_PF 2                // gate/up: steps whose loads are in flight
-#endif
-#ifndef MOE_FGEMM_DOWN_PF
-#define MOE_FGEMM_DOWN_PF 1                // down: steps whose loads are in flight
-#endif
+constexpr int kFPairPF = 2;               // gate/up: steps whose loads are in flight
+constexpr int kFDownPF = 1;               // down: steps whose loads are in flight
 
 constexpr int kFBM = 128;                  // rows (tokens) per tile
 constexpr int kFThreads = 512;             // 8 waves: 2 along the rows x 4 along the columns
@@ -136,7 +126,7 @@ struct PStep {                     // one thread's loads for one K-step
 
 template <bool SPLIT, bool ROUTED>
 __global__ __launch_bounds__(kFThreads) void fgemm_pair_kernel(const FGemmParams p) {
-    constexpr int PF = MOE_FGEMM_PAIR_PF;
+    constexpr int PF = kFPairPF;
     constexpr int NP = SPLIT ? 2 : 1;                  // activation planes: hi (and lo)
     constexpr int kCodes = 2 * kPBN * 32;              // codes of a step: 256 weight rows x 2 units
     constexpr int kScales = 2 * kPBN * 2 * 4;          // their scales, as float32
@@ -287,7 +277,7 @@ __global__ __launch_bounds__(kFThreads) void fgemm_pair_kernel(const FGemmParams
         };
         // one test per item: full tiles run the loop without per-tile tests (float32 x always:
         // a second copy of its loop does not fit in the registers)
-        if (SPLIT || !MOE_FGEMM_SKIP_DEAD || tlive[3]) run(std::true_type{});
+        if (SPLIT || tlive[3]) run(std::true_type{});
         else run(std::false_type{});
 
         // ---- epilogue: lane (lr, lg) of tile (i, j) holds columns 4 lg .. 4 lg + 3 of row lr
@@ -329,7 +319,7 @@ struct DWts {                      // one lane's weight units for one K-step
 
 template <bool ROUTED>
 __global__ __launch_bounds__(kFThreads) void fgemm_down_kernel(const FGemmParams p) {
-    constexpr int PF = MOE_FGEMM_DOWN_PF;
+    constexpr int PF = kFDownPF;
     constexpr int kAPlane = kFBM * kDRow;              // one activation plane's step
     constexpr int kStage = 2 * kAPlane;                // hi and lo planes
     static_assert(PF >= 1 && PF <= 4, "prefetch depth");
@@ -461,7 +451,7 @@ __global__ __launch_bounds__(kFThreads) void fgemm_down_kernel(const FGemmParams
                 if (Sf + j < S) step(WL[j], Sf + j, all);
         };
         // one test per item: full tiles run the loop without per-tile tests
-        if (!MOE_FGEMM_SKIP_DEAD || tlive[3]) run(std::true_type{});
+        if (tlive[3]) run(std::true_type{});
         else run(std::false_type{});
 
         // ---- epilogue: lane (lr, lg) of tile (i, j) holds columns 4 lg .. 4 lg + 3 of row lr
@@ -482,7 +472,7 @@ __global__ __launch_bounds__(kFThreads) void fgemm_down_kernel(const FGemmParams
 // The bf16 matrix-core GEMM serves unquantised activations over MXFP4 weights when there
 // are enough tokens to fill 128-row tiles at least partly (prefill); decode sizes use the GEMV.
 bool fgemm_wanted(const moe_expert_weights *w, int act, int T) {
-    return MOE_USE_BF16_GEMM && act == MOE_ACT_FLOAT && w->format == MOE_W_MXFP4 && T >= 64 && w->d_ff % 32 == 0 &&
+    return act == MOE_ACT_FLOAT && w->format == MOE_W_MXFP4 && T >= 64 && w->d_ff % 32 == 0 &&
            w->d_model % 32 == 0;
 }
 

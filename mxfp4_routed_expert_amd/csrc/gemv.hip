@@ -24,29 +24,9 @@
 
 namespace moe {
 
-// Tuning constants (compile-time; -D overrides build variants for sweeps).
-#ifndef MOE_GEMV_UNROLL
-#define MOE_GEMV_UNROLL 4        // 16-byte weight loads issued per lane per batch
-#endif
-#ifndef MOE_GEMV_TARGET_WAVES
-#define MOE_GEMV_TARGET_WAVES 4096  // waves a launch aims for (all resident at once)
-#endif
-#ifndef MOE_GEMV_THREADS
-#define MOE_GEMV_THREADS 256        // threads per workgroup
-#endif
-#ifndef MOE_GEMV_NT
-#define MOE_GEMV_NT 1            // non-temporal weight loads
-#endif
-#ifndef MOE_GEMV_WAVES_PER_EU
-#define MOE_GEMV_WAVES_PER_EU 0  // occupancy hint (0: compiler's choice)
-#endif
-constexpr int kGemvThreads = MOE_GEMV_THREADS;
-constexpr int kGemvUnroll = MOE_GEMV_UNROLL;
-#if MOE_GEMV_WAVES_PER_EU > 0
-#define MOE_GEMV_ATTR __launch_bounds__(kGemvThreads) __attribute__((amdgpu_waves_per_eu(MOE_GEMV_WAVES_PER_EU)))
-#else
-#define MOE_GEMV_ATTR __launch_bounds__(kGemvThreads)
-#endif
+constexpr int kGemvThreads = 256;          // threads per workgroup (per-expert GEMV)
+constexpr int kGemvUnroll = 4;             // 16-byte weight loads issued per lane per batch
+constexpr int kGemvTargetWaves = 4096;     // waves a launch aims for (all resident at once)
 
 template <int FMT>
 MOE_DEV int units_per_row(int K) {
@@ -266,11 +246,7 @@ MOE_DEV void load_batch(const GemvParams &p, int n_row, int n_end, int ib, int e
     for (int u = 0; u < kGemvUnroll; ++u) {
         const int b = live ? min(j + (i0 + u) * p.G, units - 1) : 0;
         const size_t wo = (ridx * (size_t)units + b) * 16;
-#if MOE_GEMV_NT
         w[u] = __builtin_nontemporal_load((const u32x4 *)(wbase + wo));
-#else
-        w[u] = *(const u32x4 *)(wbase + wo);
-#endif
         if constexpr (FMT == kFmtMXFP4) {
             sc[u] = ((const uint8_t *)sbase)[ridx * units + b];
         } else if constexpr (FMT == kFmtFP8) {
@@ -338,7 +314,7 @@ MOE_DEV void compute_batch(const GemvParams &p, int n, int n_end, int ib, int nb
 }
 
 template <int FMT, int ACT, int MAXM, bool PAIR, bool ROUTED>
-__global__ MOE_GEMV_ATTR void gemv_kernel(const GemvParams p0) {
+__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvParams p0) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int NW = kGemvThreads / 64;
 
@@ -811,14 +787,8 @@ static void pick_layout(int units, bool pair, int *G, int *nl);
 //     and keeps kDcDepth batches of loads in flight.  Each item's dot products go to an
 //     LDS table part[slot][row]; after a barrier every row's output is the slot-ordered
 //     sum of its table column.
-#ifndef MOE_DC_ROWS
-#define MOE_DC_ROWS 4            // weight rows per lane group
-#endif
-#ifndef MOE_DC_DEPTH
-#define MOE_DC_DEPTH 2           // batches in flight per wave
-#endif
-constexpr int kDcRows = MOE_DC_ROWS;
-constexpr int kDcDepth = MOE_DC_DEPTH;
+constexpr int kDcRows = 4;                 // weight rows per lane group
+constexpr int kDcDepth = 2;                // batches in flight per wave
 static_assert((64 / 4) * kDcRows <= kDcMaxRows, "a pass of the narrowest lane groups must fit the table");
 
 MOE_DEV void dc_dma16(const void *src, uint32_t lds_wave_base) {
@@ -1159,10 +1129,7 @@ static GemvFn pick_kernel(int fmt, int act, bool pair, int maxm, bool routed) {
 // LDS for staged activations per workgroup.  Small enough that several workgroups share a
 // CU (occupancy matters more than the token tile: decode experts mostly own one row);
 // experts with more rows than fit loop over token chunks.
-#ifndef MOE_GEMV_LDS_BUDGET
-#define MOE_GEMV_LDS_BUDGET (32 * 1024)
-#endif
-constexpr size_t kGemvLdsBudget = MOE_GEMV_LDS_BUDGET;
+constexpr size_t kGemvLdsBudget = 32 * 1024;
 
 template <int FMT, int ACT, bool PAIR>
 static GemvFn pick_flat_m(int maxm) {
@@ -1225,12 +1192,12 @@ moe_status gemv_launch(int fmt, int act, bool pair, GemvParams p, int slots, int
     while (maxm < want) maxm *= 2;
     p.chunk = want;
     const int rows_per_pass = pair ? 32 / p.G : 64 / p.G;
-    // aim for at most MOE_GEMV_TARGET_WAVES waves over the whole launch (rounding the rows
+    // aim for at most kGemvTargetWaves waves over the whole launch (rounding the rows
     // per workgroup up: a workgroup more than the target puts a fifth one on some CUs, whose
     // workgroups then finish last), at least one pass per wave
     const int n_grid = p.shared_slot >= 0 ? max(p.N, p.sN) : p.N;
     const long long rows_total = (long long)n_grid * slots;
-    const int target_wgs = MOE_GEMV_TARGET_WAVES / (kGemvThreads / 64);
+    const int target_wgs = kGemvTargetWaves / (kGemvThreads / 64);
     int rpw = (int)((rows_total + target_wgs - 1) / target_wgs);
     const int min_rpw = rows_per_pass * (kGemvThreads / 64);
     if (rpw < min_rpw) rpw = min_rpw;

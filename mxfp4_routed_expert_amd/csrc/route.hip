@@ -263,10 +263,7 @@ MOE_DEV int wave_best_lane(uint64_t hk, int hi) {
     return __ffsll((long long)cand) - 1;
 }
 
-#ifndef MOE_TOPK_SORT_NK
-#define MOE_TOPK_SORT_NK 8       // most keys per lane that are sorted (more: per-round rescans)
-#endif
-constexpr int kSortNK = MOE_TOPK_SORT_NK;
+constexpr int kSortNK = 8;                 // most keys per lane that are sorted (more: per-round rescans)
 
 // In-register bitonic sort of a lane's N (power of two) entries into descending order of
 // (key, then lower index first); base values move with their keys.
