@@ -117,7 +117,7 @@ def dominant_kernel(cfg):
     if cfg.wfmt == "mxfp4" and cfg.T >= 64:
         return r"fgemm_pair_kernel<\w+, true>"
     if cfg.T <= 8:
-        return r"gemv_flat_kernel<\d+, \d+, \d+, true>"
+        return r"gemv_flat_kernel<\d+, \d+, \d+, true(?:, (?:true|false))?>"
     return r"gemv_kernel<\d+, \d+, \d+, true, true>"
 
 

@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
     MOE_OK = 0,
@@ -245,6 +245,34 @@ moe_status moe_expert_gateup_shared(const moe_expert_weights *w, const moe_exper
                                     int32_t T, int32_t k, const void *x, int32_t x_dtype,
                                     const int32_t *expert_offsets, const int32_t *sorted_pairs,
                                     float *h, float *h_shared, moe_stream stream);
+/*
+ * moe_router_logits -- the first half of moe_route: the float32 router logits
+ *   logits[t][e] = x[t] . w_router[e] (e < E), then logits[t][E] = x[t] . w_shared_gate when
+ *   w_shared_gate is given (the shared gate before its sigmoid); [T][E (+1)], row-major.
+ *   Same rounding as moe_route (exact bf16 products summed in float64, rounded once).
+ *   ws: moe_route_workspace(desc) bytes.  Errors: those of moe_route.
+ * moe_topk_gateup_shared -- the rest of moe_route_permute on those logits, then
+ *   moe_expert_gateup_shared on its results, as ONE launch: every workgroup of the gate/up
+ *   kernel selects the experts from the logits itself (moe_route's selection) before
+ *   streaming their weights, so a decode step is moe_router_logits, this call and
+ *   moe_expert_down_combine -- three kernels.  (A step's routed experts in one launch, the
+ *   host not waiting on the routing: Rulith Inference README, engine section.)
+ *   Arguments: desc, logit_bias, select_bias, topk_ids, topk_w, shared_gate, expert_offsets,
+ *   sorted_pairs, pair_to_row as for moe_route_permute (has_shared_gate: logits hold the
+ *   shared-gate column E, shared_gate is written); w, shared, x (bf16 [T][H]), h, h_shared as
+ *   for moe_expert_gateup_shared; desc->E and desc->H must be w's expert count and d_model.
+ *   Results: exactly those of moe_route_permute followed by moe_expert_gateup_shared, bit for
+ *   bit.  With T <= 4, T*k <= 64, E <= 512 and activation rows that fit in LDS the selection
+ *   runs in the gate/up launch; otherwise the route kernel's selection runs first (same
+ *   results, one launch more).  No workspace.  Errors: those of the two calls.
+ */
+moe_status moe_router_logits(const moe_route_desc *desc, const void *x, const void *w_router,
+                             const void *w_shared_gate, float *logits, void *ws, size_t ws_bytes, moe_stream stream);
+moe_status moe_topk_gateup_shared(const moe_route_desc *desc, const float *logits, const float *logit_bias,
+                                  const float *select_bias, int32_t has_shared_gate, const moe_expert_weights *w,
+                                  const moe_expert_weights *shared, const void *x, int32_t *topk_ids, float *topk_w,
+                                  float *shared_gate, int32_t *expert_offsets, int32_t *sorted_pairs,
+                                  int32_t *pair_to_row, float *h, float *h_shared, moe_stream stream);
 moe_status moe_expert_down_combine(const moe_expert_weights *w, const moe_expert_weights *shared,
                                    int32_t T, int32_t k, const float *h, const float *h_shared,
                                    const int32_t *topk_ids, const float *topk_w,

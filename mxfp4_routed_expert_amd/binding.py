@@ -74,6 +74,9 @@ _sig("moe_expert_gateup_workspace", _sz, ctypes.POINTER(ExpertWeightsC), _i32, _
 _sig("moe_expert_down", _i32, ctypes.POINTER(ExpertWeightsC), _i32, _i32, _i32, _p, _p, _p, _p, _p, _p)
 _sig("moe_expert_gateup_shared", _i32, ctypes.POINTER(ExpertWeightsC), ctypes.POINTER(ExpertWeightsC), _i32, _i32, _p,
      _i32, _p, _p, _p, _p, _p)
+_sig("moe_router_logits", _i32, ctypes.POINTER(RouteDesc), _p, _p, _p, _p, _p, _sz, _p)
+_sig("moe_topk_gateup_shared", _i32, ctypes.POINTER(RouteDesc), _p, _p, _p, _i32, ctypes.POINTER(ExpertWeightsC),
+     ctypes.POINTER(ExpertWeightsC), _p, _p, _p, _p, _p, _p, _p, _p, _p, _p)
 _sig("moe_expert_down_combine", _i32, ctypes.POINTER(ExpertWeightsC), ctypes.POINTER(ExpertWeightsC), _i32, _i32, _p,
      _p, _p, _p, _p, _p, _p, _p)
 _sig("moe_combine", _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p)
@@ -84,7 +87,8 @@ _sig("moe_mx_quantize", _i32, _i32, _i32, _p, _i32, _p, _p, _p)
 
 EXPORTS = ["moe_route", "moe_route_workspace", "moe_permute", "moe_permute_workspace", "moe_route_permute",
            "moe_route_permute_noalloc",
-           "moe_expert_ffn", "moe_expert_gateup_shared", "moe_expert_down_combine",
+           "moe_expert_ffn", "moe_expert_gateup_shared", "moe_router_logits", "moe_topk_gateup_shared",
+           "moe_expert_down_combine",
            "moe_expert_ffn_workspace", "moe_expert_gateup", "moe_expert_gateup_workspace", "moe_expert_down",
            "moe_combine", "moe_dense_bf16", "moe_dequant", "moe_dequant_bf16", "moe_mx_quantize", "moe_last_error",
            "moe_abi_version"]
@@ -352,6 +356,59 @@ def moe_expert_gateup_shared(w: ExpertWeights, shared, x, k, expert_offsets, sor
                                        DT[x.dtype], _ptr(expert_offsets), _ptr(sorted_pairs), _ptr(h), _ptr(hsh),
                                        _stream()))
     return h, hsh
+
+
+def moe_router_logits(x, w_router, k, score="softmax", w_shared_gate=None, out=None, ws=None, n_group=1,
+                      topk_group=1):
+    """float32 router logits [T][E (+1 with the shared gate)]."""
+    T, H = x.shape
+    E = w_router.shape[0]
+    _need(x, torch.bfloat16, "x")
+    _need(w_router, torch.bfloat16, "w_router", (E, H))
+    _need(w_shared_gate, torch.bfloat16, "w_shared_gate", (H,))
+    d = RouteDesc(T, H, E, k, SCORE[score], 1, 1.0, n_group, topk_group)
+    rows = E + (1 if w_shared_gate is not None else 0)
+    lg = out if out is not None else torch.empty((T, rows), dtype=torch.float32, device=x.device)
+    _need(lg, torch.float32, "logits", (T, rows))
+    if ws is None:
+        ws = _workspace(lib.moe_route_workspace(ctypes.byref(d)), x.device)
+    check(lib.moe_router_logits(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(w_shared_gate), _ptr(lg), _ptr(ws),
+                                ws.numel(), _stream()))
+    return lg
+
+
+def moe_topk_gateup_shared(logits, x, k, w: ExpertWeights, shared=None, score="softmax", renormalize=True,
+                           routed_scaling=1.0, logit_bias=None, select_bias=None, has_shared_gate=False, out=None,
+                           n_group=1, topk_group=1):
+    """Routing of `logits` (moe_route_permute's selection) and the routed + shared gate/up on it,
+    in one launch.  Returns (topk_ids, topk_w, shared_gate or None, expert_offsets, sorted_pairs,
+    pair_to_row, h [T*k][d_ff], h_shared [T][d_ff_s] or None)."""
+    T, H = x.shape
+    E = w.num_experts
+    _need(x, torch.bfloat16, "x")
+    _need(logits, torch.float32, "logits", (T, E + (1 if has_shared_gate else 0)))
+    _need(logit_bias, torch.float32, "logit_bias", (E,))
+    _need(select_bias, torch.float32, "select_bias", (E,))
+    d = RouteDesc(T, H, E, k, SCORE[score], 1 if renormalize else 0, routed_scaling, n_group, topk_group)
+    dev = x.device
+    if out is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+        sg = torch.empty((T,), dtype=torch.float32, device=dev) if has_shared_gate else None
+        offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+        sp = torch.empty((T * k,), dtype=torch.int32, device=dev)
+        p2r = torch.empty((T * k,), dtype=torch.int32, device=dev)
+        h = torch.empty((T * k, w.d_ff), dtype=torch.float32, device=dev)
+        hsh = torch.empty((T, shared.d_ff), dtype=torch.float32, device=dev) if shared is not None else None
+    else:
+        ids, tw, sg, offs, sp, p2r, h, hsh = out
+    c = w.c_struct()
+    cs = shared.c_struct() if shared is not None else None
+    check(lib.moe_topk_gateup_shared(ctypes.byref(d), _ptr(logits), _ptr(logit_bias), _ptr(select_bias),
+                                     1 if has_shared_gate else 0, ctypes.byref(c),
+                                     ctypes.byref(cs) if cs is not None else None, _ptr(x), _ptr(ids), _ptr(tw),
+                                     _ptr(sg), _ptr(offs), _ptr(sp), _ptr(p2r), _ptr(h), _ptr(hsh), _stream()))
+    return ids, tw, sg, offs, sp, p2r, h, hsh
 
 
 def moe_expert_down_combine(w: ExpertWeights, shared, h, h_shared, topk_ids, topk_w, pair_to_row, shared_gate=None,

@@ -319,6 +319,81 @@ extern "C" moe_status moe_expert_gateup_shared(const moe_expert_weights *w, cons
                        (hipStream_t)stream, "moe_expert_gateup_shared");
 }
 
+extern "C" moe_status moe_topk_gateup_shared(const moe_route_desc *d, const float *logits, const float *logit_bias,
+                                             const float *select_bias, int32_t has_shared_gate,
+                                             const moe_expert_weights *w, const moe_expert_weights *shared,
+                                             const void *x, int32_t *topk_ids, float *topk_w, float *shared_gate,
+                                             int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_to_row,
+                                             float *h, float *h_shared, moe_stream stream) {
+    clear_error();
+    const char *fn = "moe_topk_gateup_shared";
+    MOE_TRY(check_route_desc(d));
+    MOE_TRY(validate_weights(w, MOE_ACT_FLOAT, fn));
+    MOE_TRY(validate_shared(w, shared, fn));
+    MOE_REQUIRE(d->E == w->num_experts && d->H == w->d_model,
+                "%s: the router's E = %d and H = %d must be the experts' count (%d) and d_model (%d)", fn, d->E, d->H,
+                w->num_experts, w->d_model);
+    MOE_REQUIRE(!(select_bias && d->score != MOE_SCORE_SIGMOID), "%s: select_bias is only defined for MOE_SCORE_SIGMOID",
+                fn);
+    MOE_REQUIRE(expert_offsets && sorted_pairs && pair_to_row, "%s: NULL expert_offsets, sorted_pairs or pair_to_row",
+                fn);
+    MOE_REQUIRE((int64_t)d->T * d->k < INT32_MAX && (int64_t)d->T * w->d_ff < INT32_MAX, "%s: sizes overflow int32", fn);
+    if (d->T == 0) return moe_permute(0, d->k, d->E, topk_ids, expert_offsets, sorted_pairs, pair_to_row, nullptr, 0,
+                                      stream);
+    MOE_REQUIRE(logits && x && topk_ids && topk_w && h, "%s: NULL logits, x, topk_ids, topk_w or h", fn);
+    MOE_REQUIRE(!has_shared_gate || shared_gate, "%s: NULL shared_gate with has_shared_gate", fn);
+    MOE_REQUIRE(!shared || h_shared, "%s: NULL h_shared with a shared expert", fn);
+    hipStream_t s = (hipStream_t)stream;
+    const int T = d->T, k = d->k, R = T * k;
+    const int fmt = w->format == MOE_W_MXFP4 ? kFmtMXFP4 : kFmtFP8;
+    const int slots = w->num_experts < R ? w->num_experts : R;
+    GemvParams p = base_params(w, T, k, nullptr, nullptr, R);
+    p.w[0] = w->gate;
+    p.w[1] = w->up;
+    p.s[0] = w->gate_s;
+    p.s[1] = w->up_s;
+    p.N = w->d_ff;
+    p.K = w->d_model;
+    p.gather = 1;
+    p.n_act_rows = T;
+    p.act = x;
+    p.out = h;
+    if (shared) {
+        p.shared_slot = slots;
+        p.sw[0] = shared->gate;
+        p.sw[1] = shared->up;
+        p.ss[0] = shared->gate_s;
+        p.ss[1] = shared->up_s;
+        p.sN = shared->d_ff;
+        p.sout = h_shared;
+    }
+    RouteArgs &ra = p.route;
+    ra.logits = logits;
+    ra.rows = d->E + (has_shared_gate ? 1 : 0);
+    ra.score = d->score;
+    ra.renorm = d->renormalize;
+    ra.scaling = d->routed_scaling;
+    ra.lbias = logit_bias;
+    ra.sbias = select_bias;
+    ra.has_sg = has_shared_gate ? 1 : 0;
+    ra.n_group = d->n_group > 1 ? d->n_group : 1;
+    ra.topk_group = d->n_group > 1 ? d->topk_group : 1;
+    ra.ids = topk_ids;
+    ra.tw = topk_w;
+    ra.sg = shared_gate;
+    ra.offsets = expert_offsets;
+    ra.sorted = sorted_pairs;
+    ra.p2r = pair_to_row;
+    moe_status st = MOE_OK;
+    if (gemv_route_launch(fmt, kActBF16, p, slots + (shared ? 1 : 0), s, &st)) return st;
+    // shapes the routing-in-the-prologue form does not take: the route kernel's selection,
+    // then the gate/up launch on its permutation
+    MOE_TRY(route_select_step(d, logits, logit_bias, select_bias, has_shared_gate != 0, topk_ids, topk_w, shared_gate,
+                              expert_offsets, sorted_pairs, pair_to_row, s));
+    return moe_expert_gateup_shared(w, shared, T, k, x, MOE_DT_BF16, expert_offsets, sorted_pairs, h, h_shared,
+                                    stream);
+}
+
 extern "C" moe_status moe_expert_down_combine(const moe_expert_weights *w, const moe_expert_weights *shared,
                                               int32_t T, int32_t k, const float *h, const float *h_shared,
                                               const int32_t *topk_ids, const float *topk_w,

@@ -8,6 +8,19 @@ namespace moe {
 enum WFmt { kFmtMXFP4 = 0, kFmtFP8 = 1, kFmtBF16 = 2 };
 enum ActKind { kActBF16 = 0, kActF32 = 1, kActMX = 2 };
 
+// Routing done by the decode gate/up kernel itself (moe_route_gateup_shared): the router's
+// logits in, the routing results out (written by workgroup 0; every workgroup selects the
+// same experts from the same logits).
+struct RouteArgs {
+    const float *logits = nullptr;  // [T][rows]: E expert logits, then the shared-gate logit
+    int rows = 0, score = 0, renorm = 0, has_sg = 0, n_group = 1, topk_group = 1;
+    float scaling = 1.0f;
+    const float *lbias = nullptr, *sbias = nullptr;
+    int32_t *ids = nullptr;
+    float *tw = nullptr, *sg = nullptr;
+    int32_t *offsets = nullptr, *sorted = nullptr, *p2r = nullptr;
+};
+
 struct GemvParams {
     const uint8_t *w[2];       // codes of the matrix (gate, up for the pair)
     const void *s[2];          // scales (MXFP4: u8 [E][N][K/32]; FP8: f32 [E][N/128][K/128])
@@ -34,6 +47,7 @@ struct GemvParams {
     const void *ss[2] = {nullptr, nullptr};
     int sN = 0;
     float *sout = nullptr;     // [T][sN]
+    RouteArgs route;           // the routing-in-the-prologue form only
 };
 
 // Down product and weighted combine of decode-sized batches in one launch (gemv.hip):
@@ -73,7 +87,20 @@ void down_combine_mfma_launch(const DownCombineParams &p, dim3 grid, size_t lds,
 // picks the register tile of tokens.
 moe_status gemv_launch(int fmt, int act, bool pair, GemvParams p, int slots, int max_rows_per_expert,
                        hipStream_t stream, const char *what);
+// The decode gate/up (+ shared) launch that also routes (top-k and permutation of p.route's
+// logits in every workgroup), bf16 activations: false when the shapes do not allow it
+// (T > 4, T*k > 64, E > 512, or activation rows too wide), else the launch status in *st.
+bool gemv_route_launch(int fmt, int act, GemvParams p, int slots, hipStream_t stream, moe_status *st);
 
+
+// route.hip: the routing arguments' checks of moe_route, and the selection (top-k, weights,
+// permutation) of moe_route_permute from logits
+// already computed (the first T*(E + has_sg) floats of `ws`).
+moe_status check_route_desc(const moe_route_desc *d);
+moe_status route_select_step(const moe_route_desc *d, const void *ws, const float *logit_bias,
+                             const float *select_bias, bool has_sg, int32_t *topk_ids, float *topk_w,
+                             float *shared_gate, int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_to_row,
+                             hipStream_t s);
 
 moe_status mx_quantize_launch(int rows, int cols, const void *x, bool f32, uint8_t *codes, uint8_t *scales,
                               hipStream_t stream);

@@ -21,6 +21,7 @@
 #include <algorithm>
 
 #include "gemv.h"
+#include "topk.h"
 
 namespace moe {
 
@@ -508,9 +509,16 @@ MOE_DEV FlatPass flat_resolve(int P, int end, int ns, int pN, int sN, int rpp, i
     return f;
 }
 
-template <int FMT, int ACT, int MAXM, bool PAIR>
+constexpr int kFlatTopkNK = 8;             // routing in the prologue: E <= 64 * kFlatTopkNK
+
+// ROUTE: the routing-in-the-prologue form (p.route): wave t < T selects token t's experts
+// (topk_select, the route kernel's selection), and wave 0 builds the slot table and the rows'
+// tokens from the selections in the permutation's order (expert, then pair); workgroup 0 also
+// writes the routing results and the permutation.
+template <int FMT, int ACT, int MAXM, bool PAIR, bool ROUTE = false>
 __global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
+    __shared__ int s_sid[ROUTE ? 64 : 1];
     __shared__ int s_e[kFlatMaxSlots], s_r0[kFlatMaxSlots], s_m[kFlatMaxSlots], s_pass0[kFlatMaxSlots + 1];
     __shared__ int s_tok[kFlatMaxSlots];
     __shared__ int s_ns, s_beg, s_end, s_next;
@@ -536,12 +544,54 @@ __global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParam
     const int rpp = PAIR ? 32 / G : 64 / G;
     const int units = units_per_row<FMT>(K);
     stage_rows_dma<FMT, ACT>(p, smem, rs);
+    const RouteArgs ra = p.route;
+    if constexpr (ROUTE) {
+        if (wave < T) {
+            double *gk = (double *)(smem + (size_t)n_act * rs) + (size_t)wave * E;   // group-limited keys
+            const TopkLane r = topk_select<kFlatTopkNK>(ra.logits + (size_t)wave * ra.rows, E, kk, ra.score, ra.renorm,
+                                                        ra.scaling, ra.lbias, ra.sbias, ra.has_sg, gk, ra.n_group,
+                                                        ra.topk_group);
+            if (lane < kk) {
+                s_sid[wave * kk + lane] = r.e;            // -1 when fewer than k keys compare
+                if (blockIdx.x == 0) {
+                    ra.ids[wave * kk + lane] = r.e;
+                    ra.tw[wave * kk + lane] = r.w;
+                }
+            }
+            if (blockIdx.x == 0 && ra.has_sg && lane == 0) ra.sg[wave] = r.sg;
+        }
+        lds_barrier();                                   // (the row copies may still be in flight)
+    }
 
     if (wave == 0) {
         // slots: the experts that own a valid range of rows, in expert order, then the shared
         // expert (e = -1) over the identity rows
         int ns = 0;
-        if (routed) {
+        if constexpr (ROUTE) {
+            // pair q = (token q / k, slot q % k) -> row = pairs of lower experts + earlier pairs
+            // of its expert; the first pair of an expert opens its slot
+            const int P = T * kk;
+            const int e = lane < P ? s_sid[lane] : -1;
+            int row = 0, cnt = 0;
+            bool first = e >= 0;
+            for (int q = 0; q < P; ++q) {
+                const int eq = s_sid[q];
+                row += (eq >= 0 && (eq < e || (eq == e && q < lane))) ? 1 : 0;
+                cnt += eq == e ? 1 : 0;
+                first = first && !(eq == e && q < lane);
+            }
+            const uint64_t fm = __ballot(first);
+            int slot = 0;
+            for (int q = 0; q < P; ++q) slot += (((fm >> q) & 1ull) && s_sid[q] < e) ? 1 : 0;
+            if (e >= 0) s_tok[row] = lane / kk;
+            if (first) {
+                s_e[slot] = e;
+                s_r0[slot] = row;
+                s_m[slot] = cnt;
+            }
+            ns = __popcll(fm);
+            if (blockIdx.x == 0) small_permutation(s_sid, P, E, ra.offsets, ra.sorted, ra.p2r, lane, 64);
+        } else if (routed) {
             int o[kMaxOffsetChunks];
 #pragma unroll
             for (int c = 0; c < kMaxOffsetChunks; ++c) o[c] = gload_i32(offsets + min(c * 64 + lane, E));
@@ -606,7 +656,7 @@ __global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParam
             s_end = end;
             s_next = beg + NW;
         }
-    } else if (wave == 1) {
+    } else if (!ROUTE && wave == 1) {
         // activation row of each routed row (or identity row): -1 when out of range
         const int Rr = routed ? R : T;
         for (int r = lane; r < Rr && r < kFlatMaxSlots; r += 64) {
@@ -1150,6 +1200,38 @@ static GemvFn pick_flat(int fmt, int act, bool pair, int maxm) {
     if (fmt == kFmtMXFP4) return pair ? pick_flat_a<kFmtMXFP4, true>(act, maxm) : pick_flat_a<kFmtMXFP4, false>(act, maxm);
     if (fmt == kFmtFP8) return pair ? pick_flat_a<kFmtFP8, true>(act, maxm) : pick_flat_a<kFmtFP8, false>(act, maxm);
     return pick_flat_a<kFmtBF16, false>(act, maxm);
+}
+
+template <int FMT, int ACT>
+static GemvFn pick_flat_route_m(int maxm) {
+    switch (maxm) {
+        case 1: return gemv_flat_kernel<FMT, ACT, 1, true, true>;
+        case 2: return gemv_flat_kernel<FMT, ACT, 2, true, true>;
+        default: return gemv_flat_kernel<FMT, ACT, 4, true, true>;
+    }
+}
+
+bool gemv_route_launch(int fmt, int act, GemvParams p, int slots, hipStream_t stream, moe_status *st) {
+    if ((fmt != kFmtMXFP4 && fmt != kFmtFP8) || act != kActBF16) return false;
+    const int units = fmt == kFmtMXFP4 ? p.K / 32 : p.K / 16;
+    pick_layout(units, true, &p.G, &p.nl);
+    const size_t rs = align_up((size_t)p.K * 2, 1024);
+    const int ng = p.route.n_group > 1 ? p.route.n_group : 1;
+    const size_t lds = (size_t)p.T * rs + (ng > 1 ? (size_t)p.T * p.E * sizeof(double) : 0);
+    if (p.T < 1 || p.T > 4 || p.T * p.k > 64 || p.E > 64 * kFlatTopkNK || p.n_act_rows != p.T ||
+        lds > kFlatLdsBudget || (fmt == kFmtMXFP4 && units % 4 != 0) || p.G < 4)
+        return false;
+    int maxm = 1;
+    while (maxm < p.T) maxm *= 2;
+    const int rpp = 32 / p.G;
+    long long passes = (long long)(slots - (p.shared_slot >= 0 ? 1 : 0)) * ((p.N + rpp - 1) / rpp);
+    if (p.shared_slot >= 0) passes += (p.sN + rpp - 1) / rpp;
+    const long long per_wg = kFlatThreads / 64;
+    const int nwg = (int)std::min<long long>(device_cu_count(), std::max<long long>(1, (passes + per_wg - 1) / per_wg));
+    GemvFn fn = fmt == kFmtMXFP4 ? pick_flat_route_m<kFmtMXFP4, kActBF16>(maxm) : pick_flat_route_m<kFmtFP8, kActBF16>(maxm);
+    hipLaunchKernelGGL(fn, dim3(nwg), dim3(kFlatThreads), lds, stream, p);
+    *st = launch_check("moe_route_gateup_shared: gemv_flat_kernel");
+    return true;
 }
 
 moe_status gemv_launch(int fmt, int act, bool pair, GemvParams p, int slots, int max_rows_per_expert,

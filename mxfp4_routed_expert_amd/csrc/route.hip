@@ -13,6 +13,7 @@
 #include <mutex>
 
 #include "common.h"
+#include "topk.h"
 
 namespace moe {
 namespace {
@@ -214,90 +215,7 @@ __global__ __launch_bounds__(256) void router_reduce_kernel(const double *__rest
 
 bool router_tiled(const moe_route_desc *d) { return d->T >= 32 && d->H % (32 * kRouterKS) == 0; }
 
-MOE_DEV double sigmoid_f64(double v) { return 1.0 / (1.0 + exp(-v)); }
-
-MOE_DEV double readlane_f64(double v, int l) {
-    const uint64_t b = (uint64_t)__double_as_longlong(v);
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
-    return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
-
-// Selection order: larger key first, equal keys (-0 == +0) -> lower expert index.  A key
-// is mapped to an unsigned 64-bit integer with the same order (NaN -> 0, below every
-// number), so the wave-wide maximum runs on 32-bit integer halves.
-MOE_DEV uint64_t order_key(double k) {
-    if (k != k) return 0;
-    const uint64_t b = (uint64_t)__double_as_longlong(k + 0.0);          // -0 -> +0
-    return b ^ ((b >> 63) ? ~0ull : 0x8000000000000000ull);
-}
-
-// Maximum of v over the wave, in every lane: a DPP butterfly inside each 16-lane row
-// (quad xor 1, quad xor 2, half-row mirror, row mirror), then the four rows via readlane.
-MOE_DEV uint32_t wave_max_u32(uint32_t v) {
-    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));
-    v = max(v, (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));
-    const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
-    const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-    return max(max(r0, r1), max(r2, r3));
-}
-
-// Lane of the wave-wide best (key, index) among the lanes' current heads: the largest high
-// key half, then (only on a tie) the largest low half, then the lowest index.
-MOE_DEV int wave_best_lane(uint64_t hk, int hi) {
-    const uint32_t kh = (uint32_t)(hk >> 32), kl = (uint32_t)hk;
-    const uint32_t mh = wave_max_u32(kh);
-    uint64_t cand = __ballot(kh == mh);
-    if (__popcll(cand) > 1) {
-        const bool c1 = kh == mh;
-        const uint32_t ml = wave_max_u32(c1 ? kl : 0u);
-        cand = __ballot(c1 && kl == ml);
-        if (__popcll(cand) > 1) {
-            const bool c2 = c1 && kl == ml;
-            const uint32_t mi = ~wave_max_u32(c2 ? ~(uint32_t)hi : 0u);   // lowest index
-            cand = __ballot(c2 && (uint32_t)hi == mi);
-        }
-    }
-    return __ffsll((long long)cand) - 1;
-}
-
-constexpr int kSortNK = 8;                 // most keys per lane that are sorted (more: per-round rescans)
-
-// In-register bitonic sort of a lane's N (power of two) entries into descending order of
-// (key, then lower index first); base values move with their keys.
-template <int N>
-MOE_DEV void sort_desc(uint64_t (&key)[N], int (&idx)[N], double (&base)[N]) {
-#pragma unroll
-    for (int size = 2; size <= N; size <<= 1) {
-#pragma unroll
-        for (int stride = size / 2; stride > 0; stride >>= 1) {
-#pragma unroll
-            for (int i = 0; i < N; ++i) {
-                const int p = i ^ stride;
-                if (p <= i) continue;
-                // entries i < p: descending run when (i & size) == 0, ascending otherwise
-                const bool first_better = key[i] > key[p] || (key[i] == key[p] && idx[i] < idx[p]);
-                const bool swap = ((i & size) == 0) ? !first_better : first_better;
-                const uint64_t ka = key[i], kb = key[p];
-                const int ia = idx[i], ib = idx[p];
-                const double ba = base[i], bb = base[p];
-                key[i] = swap ? kb : ka;
-                key[p] = swap ? ka : kb;
-                idx[i] = swap ? ib : ia;
-                idx[p] = swap ? ia : ib;
-                base[i] = swap ? bb : ba;
-                base[p] = swap ? ba : bb;
-            }
-        }
-    }
-}
-
-// One wave per token.  Lane l holds the selection keys of experts l, l+64, ... in
-// registers; each of the k rounds takes the wave-wide best of the lanes' best untaken keys
-// (see the selection below).  NaN keys are never selected (ids -1 are emitted if fewer
-// than k keys compare).
+// One wave per token (topk_select).
 // PERM: one workgroup holds every token (T <= 4, T*k <= 64) and also writes the token ->
 // expert permutation of the selected ids, as moe_permute would.
 template <int NK, bool PERM>
@@ -315,166 +233,14 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     if (!PERM && t >= T) return;
     const int lane = lane_id();
     if (t < T) {
-    const float *lt = logits + (size_t)t * rows;
-
-    // All loads are issued before any is used (an absent bias array is read from the logits
-    // and the value dropped), so the keys cost one memory round trip.  base[i] is what a
-    // selected expert's weight is computed from -- its logit (softmax) or sigmoid (sigmoid)
-    // -- so nothing is read again after the selection.
-    const float *lbp = lbias ? lbias : lt, *sbp = sbias ? sbias : lt;
-    float lv[NK], lbv[NK], sbv[NK];
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-        const int e = min(lane + 64 * i, E - 1);
-        lv[i] = lt[e];
-        lbv[i] = lbp[e];
-        sbv[i] = sbp[e];
-    }
-    const float sg_logit = lt[has_sg ? E : 0];
-#pragma unroll
-    for (int i = 0; i < NK; ++i) asm volatile("" : "+v"(lv[i]), "+v"(lbv[i]), "+v"(sbv[i]));   // loads stay here
-    uint64_t key[NK];
-    double base[NK];
-#pragma unroll
-    for (int i = 0; i < NK; ++i) {
-        double l = (double)lv[i] + (lbias ? (double)lbv[i] : 0.0);
-        double kv = l;
-        if (score == MOE_SCORE_SIGMOID) {
-            l = sigmoid_f64(l);
-            kv = l + (sbias ? (double)sbv[i] : 0.0);
+        const TopkLane r = topk_select<NK>(logits + (size_t)t * rows, E, k, score, renorm, scaling, lbias, sbias,
+                                           has_sg, s_gkey + wave_id() * E, n_group, topk_group);
+        if (lane < k) {
+            ids[(size_t)t * k + lane] = r.e;
+            w[(size_t)t * k + lane] = r.w;
+            if constexpr (PERM) sid[t * k + lane] = r.e;        // -1 when fewer than k keys compare
         }
-        base[i] = l;
-        key[i] = lane + 64 * i < E ? order_key(kv) : 0;
-        if (n_group > 1 && lane + 64 * i < E) s_gkey[wave_id() * E + lane + 64 * i] = kv;
-    }
-    if (n_group > 1) {
-        // group-limited selection: lane g < n_group scores group g from the keys in LDS (a
-        // wave's LDS accesses complete in order), the topk_group best groups are taken by
-        // wave arg-max rounds, and keys outside them can no longer be selected
-        const int gs = E / n_group;
-        const double *kw = s_gkey + wave_id() * E;
-        double b1 = -INFINITY, b2 = -INFINITY;
-        if (lane < n_group) {
-            for (int q = 0; q < gs; ++q) {
-                double v = kw[lane * gs + q];
-                if (v != v) v = -INFINITY;
-                if (v > b1) {
-                    b2 = b1;
-                    b1 = v;
-                } else if (v > b2) {
-                    b2 = v;
-                }
-            }
-        }
-        uint64_t gk = lane < n_group ? order_key(score == MOE_SCORE_SIGMOID ? b1 + b2 : b1) : 0;
-        uint64_t keep = 0;
-        for (int r = 0; r < topk_group; ++r) {
-            const int L = wave_best_lane(gk, lane);
-            keep |= 1ull << L;
-            if (lane == L) gk = 0;
-        }
-#pragma unroll
-        for (int i = 0; i < NK; ++i) {
-            const int e = lane + 64 * i;
-            if (e < E && !((keep >> (e / gs)) & 1ull)) key[i] = 0;
-        }
-    }
-    // Up to kSortNK keys per lane: the lane's keys are sorted once, best first (larger key,
-    // then lower expert); each round takes the wave-wide best of the lanes' first entries
-    // and the winner shifts its list.  More keys per lane: each lane tracks its best
-    // untaken key (its head) and only the round's winner rescans -- the sorting network
-    // grows as n log^2 n while the rescans grow as k n.  Both select the same experts in
-    // the same order.  Key 0 (NaN, masked or past E) is never selected.
-    double braw[NK];             // unsorted, for the full softmax denominator
-#pragma unroll
-    for (int i = 0; i < NK; ++i) braw[i] = base[i];
-    int my_e = -1;
-    double l = 0.0;              // lane j < k: base value of the j-th selected expert
-    if constexpr (NK <= kSortNK) {
-        int idx[NK];
-#pragma unroll
-        for (int i = 0; i < NK; ++i) idx[i] = lane + 64 * i;
-        sort_desc<NK>(key, idx, base);
-        for (int j = 0; j < k; ++j) {
-            const int L = wave_best_lane(key[0], key[0] ? idx[0] : INT_MAX);
-            const int wi = key[0] ? idx[0] : INT_MAX;
-            const int win = __builtin_amdgcn_readlane(wi, L);
-            const double wl = readlane_f64(base[0], L);
-            if (lane == j && win != INT_MAX) {
-                my_e = win;
-                l = wl;
-            }
-            if (lane == L) {     // the winner drops its first entry
-#pragma unroll
-                for (int i = 0; i + 1 < NK; ++i) {
-                    key[i] = key[i + 1];
-                    idx[i] = idx[i + 1];
-                    base[i] = base[i + 1];
-                }
-                key[NK - 1] = 0;
-            }
-        }
-    } else {
-        uint32_t taken = 0;
-        uint64_t hk;
-        int hi;
-        double hv;
-        auto head = [&]() {      // best untaken key of this lane (equal keys: lower i = lower expert)
-            hk = 0;
-            hi = INT_MAX;
-            hv = 0.0;
-#pragma unroll
-            for (int i = 0; i < NK; ++i) {
-                if (!((taken >> i) & 1u) && key[i] > hk) {
-                    hk = key[i];
-                    hi = lane + 64 * i;
-                    hv = base[i];
-                }
-            }
-        };
-        head();
-        for (int j = 0; j < k; ++j) {
-            const int L = wave_best_lane(hk, hi);
-            const int win = __builtin_amdgcn_readlane(hi, L);
-            const double wl = readlane_f64(hv, L);
-            if (lane == j && win != INT_MAX) {
-                my_e = win;
-                l = wl;
-            }
-            if (lane == L && win != INT_MAX) {   // the winner drops its key
-                taken |= 1u << (win >> 6);
-                head();
-            }
-        }
-    }
-
-    const bool mine = lane < k && my_e >= 0;
-    double wv;
-    if (score == MOE_SCORE_SOFTMAX) {
-        const double lmax = __shfl(l, 0, kWave);   // first selected = largest logit
-        double p = mine ? exp(l - lmax) : 0.0;
-        double denom;
-        if (renorm) {
-            denom = group_sum_f64(p, kWave);
-        } else {
-            double s = 0.0;
-#pragma unroll
-            for (int i = 0; i < NK; ++i)
-                if (lane + 64 * i < E) s += exp(braw[i] - lmax);
-            denom = group_sum_f64(s, kWave);
-        }
-        wv = p / denom;
-    } else {
-        const double sv = mine ? l : 0.0;
-        wv = renorm ? sv / group_sum_f64(sv, kWave) : sv;
-    }
-    wv *= (double)scaling;
-    if (lane < k) {
-        ids[(size_t)t * k + lane] = my_e;
-        w[(size_t)t * k + lane] = mine ? (float)wv : NAN;
-        if constexpr (PERM) sid[t * k + lane] = my_e;        // -1 when fewer than k keys compare
-    }
-    if (has_sg && lane == 0) sg[t] = (float)sigmoid_f64((double)sg_logit);
+        if (has_sg && lane == 0) sg[t] = r.sg;
     }
     if constexpr (PERM) {
         lds_barrier();           // sid is in LDS; the id and weight stores need not land first
@@ -549,6 +315,31 @@ namespace {
 
 // Checks the routing arguments and enqueues the logits (router_logits_kernel, or the tiled
 // product and its reduction) into the workspace.
+// Enqueues the float32 logits [T][E (+1 for the shared-gate row)] (router_logits_kernel, or
+// the tiled product into `partial` and its reduction).
+moe_status enqueue_logits(const moe_route_desc *d, const void *x, const void *w_router, const void *w_shared_gate,
+                          float *logits, double *partial, hipStream_t s) {
+    const int rows = d->E + (w_shared_gate ? 1 : 0);
+    if (router_tiled(d)) {
+        dim3 gt((rows + kRtRow - 1) / kRtRow, (d->T + kRtTok - 1) / kRtTok, kRouterKS);
+        hipLaunchKernelGGL(router_tiled_kernel, gt, dim3(256), 0, s, (const uint16_t *)x, (const uint16_t *)w_router,
+                           (const uint16_t *)w_shared_gate, d->T, d->H, d->E, rows, partial);
+        MOE_TRY(launch_check("moe_route: router_tiled_kernel"));
+        const int n = d->T * rows;
+        hipLaunchKernelGGL(router_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, partial, n, logits);
+        return launch_check("moe_route: router_reduce_kernel");
+    }
+    dim3 g1(rows, (d->T + kRouterTB - 1) / kRouterTB);
+    hipLaunchKernelGGL(router_logits_kernel, g1, dim3(64 * kRouterWaves), 0, s, (const uint16_t *)x,
+                       (const uint16_t *)w_router, (const uint16_t *)w_shared_gate, d->T, d->H, d->E, rows, logits);
+    return launch_check("moe_route: router_logits_kernel");
+}
+
+double *partial_of(const moe_route_desc *d, void *ws) {
+    return (double *)((unsigned char *)ws + align_up((size_t)d->T * (d->E + 1) * sizeof(float), 256));
+}
+
+// Checks the routing arguments and enqueues the logits into the workspace.
 moe_status route_logits(const moe_route_desc *d, const void *x, const void *w_router, const float *logit_bias,
                         const float *select_bias, const void *w_shared_gate, int32_t *topk_ids, float *topk_w,
                         float *shared_gate, void *ws, size_t ws_bytes, hipStream_t s) {
@@ -562,28 +353,48 @@ moe_status route_logits(const moe_route_desc *d, const void *x, const void *w_ro
         set_error("moe_route: workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
         return MOE_ERR_WORKSPACE;
     }
-    const int rows = d->E + (w_shared_gate ? 1 : 0);
-    float *logits = (float *)ws;
-    if (router_tiled(d)) {
-        double *partial = (double *)((unsigned char *)ws + align_up((size_t)d->T * (d->E + 1) * sizeof(float), 256));
-        dim3 gt((rows + kRtRow - 1) / kRtRow, (d->T + kRtTok - 1) / kRtTok, kRouterKS);
-        hipLaunchKernelGGL(router_tiled_kernel, gt, dim3(256), 0, s, (const uint16_t *)x, (const uint16_t *)w_router,
-                           (const uint16_t *)w_shared_gate, d->T, d->H, d->E, rows, partial);
-        MOE_TRY(launch_check("moe_route: router_tiled_kernel"));
-        const int n = d->T * rows;
-        hipLaunchKernelGGL(router_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, partial, n, logits);
-        MOE_TRY(launch_check("moe_route: router_reduce_kernel"));
-    } else {
-        dim3 g1(rows, (d->T + kRouterTB - 1) / kRouterTB);
-        hipLaunchKernelGGL(router_logits_kernel, g1, dim3(64 * kRouterWaves), 0, s, (const uint16_t *)x,
-                           (const uint16_t *)w_router, (const uint16_t *)w_shared_gate, d->T, d->H, d->E,
-                           rows, logits);
-        MOE_TRY(launch_check("moe_route: router_logits_kernel"));
-    }
-    return MOE_OK;
+    return enqueue_logits(d, x, w_router, w_shared_gate, (float *)ws, partial_of(d, ws), s);
 }
 
 }  // namespace
+
+namespace moe {
+
+moe_status check_route_desc(const moe_route_desc *d) { return validate_route(d); }
+
+// The selection half of moe_route_permute (top-k, weights, permutation) from logits already
+// computed, for callers inside the library.
+moe_status route_select_step(const moe_route_desc *d, const void *ws, const float *logit_bias,
+                             const float *select_bias, bool has_sg, int32_t *topk_ids, float *topk_w,
+                             float *shared_gate, int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_to_row,
+                             hipStream_t s) {
+    if (d->T == 0) return MOE_OK;
+    const int rows = d->E + (has_sg ? 1 : 0);
+    if (d->T <= 4 && d->T * d->k <= 64)
+        return launch_topk(d, (const float *)ws, rows, logit_bias, select_bias, has_sg, topk_ids, topk_w, shared_gate,
+                           expert_offsets, sorted_pairs, pair_to_row, s);
+    MOE_TRY(launch_topk(d, (const float *)ws, rows, logit_bias, select_bias, has_sg, topk_ids, topk_w, shared_gate,
+                        nullptr, nullptr, nullptr, s));
+    return moe_permute(d->T, d->k, d->E, topk_ids, expert_offsets, sorted_pairs, pair_to_row, nullptr, 0,
+                       (moe_stream)s);
+}
+
+}  // namespace moe
+
+extern "C" moe_status moe_router_logits(const moe_route_desc *d, const void *x, const void *w_router,
+                                        const void *w_shared_gate, float *logits, void *ws, size_t ws_bytes,
+                                        moe_stream stream) {
+    clear_error();
+    MOE_TRY(validate_route(d));
+    if (d->T == 0) return MOE_OK;
+    MOE_REQUIRE(x && w_router && logits, "moe_router_logits: NULL x, w_router or logits");
+    const size_t need = moe_route_workspace(d);
+    if (!ws || ws_bytes < need) {
+        set_error("moe_router_logits: workspace of %zu bytes needed, %zu given", need, ws ? ws_bytes : (size_t)0);
+        return MOE_ERR_WORKSPACE;
+    }
+    return enqueue_logits(d, x, w_router, w_shared_gate, logits, partial_of(d, ws), (hipStream_t)stream);
+}
 
 extern "C" moe_status moe_route(const moe_route_desc *d, const void *x, const void *w_router,
                                 const float *logit_bias, const float *select_bias,

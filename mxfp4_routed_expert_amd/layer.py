@@ -3,11 +3,12 @@
 route -> permute -> routed experts (moe_expert_ffn) -> shared expert (moe_expert_ffn,
 identity form) -> combine; LatentMoE layers add moe_dense_bf16 before the routed experts
 and after the combine (Kimi K3 article, architecture section); a gated shared expert's
-output is scaled by its gate before it is added after the up projection.  Decode-sized batches use
-the fused calls instead: route+permute, routed and shared gate/up in one launch, down and
-combine in one launch.  Every step runs in the
-HIP library; this module only wires buffers.  All buffers for a token count are
-allocated once, so a step enqueues kernels and allocates nothing.
+output is scaled by its gate before it is added after the up projection.  Decode-sized
+batches use the fused calls instead, three kernels a step: the router's logits; the
+selection with the routed and shared gate/up in one launch (moe_topk_gateup_shared); down
+and combine in one launch.  Every step runs in the HIP library; this module only wires
+buffers.  All buffers for a token count are allocated once, so a step enqueues kernels and
+allocates nothing.
 """
 from __future__ import annotations
 
@@ -93,6 +94,7 @@ class MoELayer:
         self.no_w = e(T, 0)
         self.out = e(T, H)
         self.ws_route = B._workspace(B.moe_route_workspace(T, H, E, k, w.score), device)
+        self.logits = e(T, E + (1 if w.w_shared_gate is not None else 0)) if self.fused else None
         # h rows: the staged form runs gate/up and down as separate calls on these buffers
         # (float32 h in FLOAT mode, MX codes and scales in MXFP4 mode), as does the fused form
         mx = w.act == "mxfp4"
@@ -119,13 +121,17 @@ class MoELayer:
         record events around those kernels."""
         w = self.w
         if self.fused:
-            B.moe_route_permute(x, w.w_router, w.k, w.score, w.renormalize, w.routed_scaling, w.logit_bias,
-                                w.select_bias, w.w_shared_gate,
-                                out=(self.ids, self.topk_w, self.sg, self.offs, self.sp, self.p2r), ws=self.ws_route,
+            # three kernels: the router's logits, one gate/up launch that routes in its
+            # prologue (the routing results land in the same buffers as moe_route_permute's),
+            # and the down product with the combine
+            B.moe_router_logits(x, w.w_router, w.k, w.score, w.w_shared_gate, out=self.logits, ws=self.ws_route,
                                 n_group=w.n_group, topk_group=w.topk_group)
             if mark is not None:
                 mark("gateup_begin")
-            B.moe_expert_gateup_shared(w.experts, w.shared, x, w.k, self.offs, self.sp, out=(self.h, self.h_sh))
+            B.moe_topk_gateup_shared(self.logits, x, w.k, w.experts, w.shared, w.score, w.renormalize,
+                                     w.routed_scaling, w.logit_bias, w.select_bias, w.w_shared_gate is not None,
+                                     out=(self.ids, self.topk_w, self.sg, self.offs, self.sp, self.p2r, self.h,
+                                          self.h_sh), n_group=w.n_group, topk_group=w.topk_group)
             if mark is not None:
                 mark("gateup_end")
             if mark is not None:

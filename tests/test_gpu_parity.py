@@ -469,6 +469,50 @@ def test_fused_decode_calls_match_unfused(dev, M, name):
     assert_close(to_np(out), to_np(ref), f"{name} out")
 
 
+# routing in the gate/up launch (moe_router_logits + moe_topk_gateup_shared) against
+# moe_route_permute + moe_expert_gateup_shared: (config, n_group, topk_group)
+TOPK_GATEUP_CASES = {
+    "tiny": (tiny(), 1, 1),
+    "tiny_fused_gated": (LAYER_CASES["tiny_fused_gated"], 1, 1),
+    "tiny_sigmoid_fp8": (LAYER_CASES["tiny_fused_fp8_ungated"], 1, 1),
+    "tiny_groups": (tiny(name="tgk", wtag=103, score="sigmoid", select_bias_std=0.01, k=4, T=3, E=16,
+                         shared="gated", shared_K=256, shared_I=128), 4, 2),
+    "decode_full": (synth.get("qwen38max_decode"), 1, 1),
+    # more experts than the in-launch selection holds: the route kernel selects first
+    "tiny_many_experts": (tiny(name="tme", wtag=104, E=640, k=3, T=2, shared="gated", shared_K=256, shared_I=128),
+                          1, 1),
+}
+
+
+@pytest.mark.parametrize("name", list(TOPK_GATEUP_CASES))
+def test_topk_gateup_equals_route_then_gateup(dev, M, name):
+    """The three-kernel decode step's first two calls give the routing, the permutation, h and
+    h_shared of moe_route_permute followed by moe_expert_gateup_shared, bit for bit."""
+    cfg, ng, tg = TOPK_GATEUP_CASES[name]
+    t, inp = build(cfg, dev)
+    w = layer_weights(cfg, t)
+    x = t["x"]
+    wsg = t["w_shared_gate"] if cfg.shared == "gated" else None
+    ref = M.moe_route_permute(x, t["w_router"], cfg.k, cfg.score, cfg.renormalize, cfg.routed_scaling,
+                              t["logit_bias"], t["select_bias"], wsg, n_group=ng, topk_group=tg)
+    ids, tw, sg, offs, sp, p2r = ref
+    h_ref, hs_ref = M.moe_expert_gateup_shared(w.experts, w.shared, x, cfg.k, offs, sp)
+    lg = M.moe_router_logits(x, t["w_router"], cfg.k, cfg.score, wsg, n_group=ng, topk_group=tg)
+    got = M.moe_topk_gateup_shared(lg, x, cfg.k, w.experts, w.shared, cfg.score, cfg.renormalize, cfg.routed_scaling,
+                                   t["logit_bias"], t["select_bias"], wsg is not None, n_group=ng, topk_group=tg)
+    torch.cuda.synchronize()
+    names = ["topk_ids", "topk_w", "shared_gate", "expert_offsets", "sorted_pairs", "pair_to_row"]
+    for nm, a, b in zip(names, got[:6], ref):
+        if b is None:
+            assert a is None, nm
+            continue
+        np.testing.assert_array_equal(to_np(a), to_np(b), err_msg=f"{name} {nm}")
+    np.testing.assert_array_equal(to_np(got[6]), to_np(h_ref), err_msg=f"{name} h")
+    if hs_ref is not None:
+        np.testing.assert_array_equal(to_np(got[7]), to_np(hs_ref), err_msg=f"{name} h_shared")
+    say(f"  {name}: routing, permutation, h equal")
+
+
 def test_down_combine_drops_invalid_pairs(dev, M):
     """A pair with id -1 or row -1 adds nothing; the rest is the weighted sum."""
     cfg = LAYER_CASES["tiny_fused_gated"]
