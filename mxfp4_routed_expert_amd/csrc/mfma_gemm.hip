@@ -11,18 +11,18 @@
 //
 // Item: 256 rows of one expert (tokens routed to it, in sorted order) by 256 weight rows
 // (128 columns of gate AND of up for the SwiGLU pair; 256 output columns for down).  One
-// workgroup of 4 waves per CU, one wave per SIMD; wave (wm, wn) owns 128 rows x 4 weight
-// tiles of 32, i.e. 16 accumulator tiles (256 registers), so each quarter it reads 8 KB
-// of operands from LDS for 16 matrix instructions -- half of what a 64 x 64 wave tile
-// reads -- which keeps LDS under its bandwidth at the matrix cores' rate.
+// workgroup of 8 waves per CU, two waves per SIMD; wave (wm, wn) owns 128 rows x 2 weight
+// tiles of 32 (a gate and an up tile of the same 32 columns for the pair, 64 output
+// columns for down), i.e. 8 accumulator tiles (128 registers).
 // K advances in steps of 256 values: every operand row contributes one whole 128-byte
 // line per step.  A step's A rows (gathered token rows), B rows (weight rows) and scale
 // windows go from global memory straight into LDS (global_load_lds), two steps resident
-// (2 x 72 KB): the copies of the next step are issued a piece at a time between the
-// matrix instructions of the current one, rather than in one burst that would hold the
-// wave's instruction stream while the L1 accepts them.
+// (2 x 72 KB); every wave issues an eighth of the next step's copies between its matrix
+// instructions of the current step.  A wave stalls while the L1 accepts its copies (the
+// copy rate grows with the number of waves issuing), so the second wave on each SIMD keeps
+// the matrix core busy meanwhile.
 // Small row counts: an item whose live rows fit 128 (or 64) runs with 2 (or 1) row tiles
-// per wave, so all four waves share the smaller tile; and when the last round of items
+// per wave, so all eight waves share the smaller tile; and when the last round of items
 // would leave CUs idle, its items are split into halves or quarters by rows.
 // Epilogue, gate/up: h = silu(g) * u, staged through LDS so that each lane owns a row's
 // 32-column block and OCP-MX quantises it alone (block maximum, 16 packed code bytes, one
@@ -41,7 +41,7 @@ typedef int32_t i32x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kQBM = 256;              // rows per item
 constexpr int kQBR = 256;              // weight rows per item
-constexpr int kQThreads = 256;         // 4 waves, 2 along the rows x 2 along the weight rows
+constexpr int kQThreads = 512;         // 8 waves, 2 along the rows x 4 along the weight rows
 constexpr int kQRowB = 128;            // code bytes per row per K-step (256 values)
 constexpr int kQSlot = 16;             // LDS bytes per scale row per step
 // LDS: A codes of both stages, then B codes of both stages, then scale windows of both.
@@ -50,8 +50,8 @@ constexpr int kQB = kQBR * kQRowB;                   // 32 KB per stage
 constexpr int kQS = (kQBM + kQBR) * kQSlot;          // 8 KB per stage
 constexpr int kQOffA = 0, kQOffB = 2 * kQA, kQOffS = 2 * kQA + 2 * kQB;
 constexpr int kQLds = kQOffS + 2 * kQS;              // 144 KB
-constexpr int kQLd = 64 + 4;                         // epilogue staging row stride (floats)
-static_assert(4 * 128 * kQLd * 4 <= kQLds, "epilogue staging fits the stage buffers");
+constexpr int kQLd = 32 + 4;                         // epilogue staging row stride (floats)
+static_assert(8 * 128 * kQLd * 4 <= kQLds, "epilogue staging fits the stage buffers");
 
 struct GemmParams {
     const uint8_t *a;              // A codes: token rows [n_arows][K/2] (gather) or rows [R][K/2]
@@ -105,6 +105,14 @@ MOE_DEV const uint8_t *uniform_ptr(const void *q) {
 // One asm block, so no memory access moves across it.
 MOE_DEV void wait_copies_and_barrier() { asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
+// The lane id, read so that the compiler neither hoists it nor keeps values derived from it
+// alive across a loop.
+MOE_DEV int lane_fresh() {
+    int l;
+    asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+    return l;
+}
+
 // Position of 16-byte chunk c of LDS row r is c ^ qswz(r): a quarter's operand read (rows
 // r .. r+31 at one chunk) then spreads over all 16-byte bank groups whether the banks repeat
 // every 128 or every 256 bytes.
@@ -116,57 +124,60 @@ struct QUnit {
     int e, n0, m0, row0, M;
 };
 
-template <bool PAIR, int TM>
+template <bool PAIR, int TM, bool AS>
 MOE_DEV void qgemm_unit(const GemmParams &p, const QUnit &u, unsigned char *smem, const int *s_arow) {
-    constexpr int NA = 2 * TM;                    // 1-KB A copies per wave (A holds 64*TM rows)
     const int lane = lane_id(), wave = wave_id();
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int hr = lane & 31, hb = lane >> 5;
     const int Kh = p.K / 2, Kb = p.K / 32;
     const int S = (Kb + 7) / 8;                   // K-steps
     const int nvalid = Kb - 8 * (S - 1);          // blocks of the last step (1..8)
     const int eu = __builtin_amdgcn_readfirstlane(u.e);
 
-    // ---- copy sources.  A: rows wave*16*TM + 8t + lane/8 of the unit (LDS rows in that
-    // order), lane%8 = the LDS chunk position, fetching chunk (lane%8) ^ qswz(row).
+    // ---- copy sources.  A: the unit's 64*TM rows, 8*TM per wave: rows wave*8*TM + 8t + lane/8
+    // (t < TM; LDS rows in that order), lane%8 = the LDS chunk position, fetching chunk
+    // (lane%8) ^ qswz(row).
     const uint8_t *a_base = uniform_ptr(p.a);
     const uint8_t *as_base = uniform_ptr((const uint8_t *)((uintptr_t)p.as & ~(uintptr_t)3));
     const uint32_t as_mis = (uint32_t)((uintptr_t)p.as & 3u);
-    // B: wave w copies weight rows 64w .. 64w+63 of the item: gate (w < 2) or up (w >= 2) rows
-    // n0 + (64w mod 128) + .. for the pair, down rows n0 + 64w + .. otherwise.
-    const int bmat = PAIR ? (wave >> 1) : 0;
-    const int bl0 = PAIR ? 64 * (wave & 1) : 64 * wave;        // first matrix row (past n0) it copies
+    // B: wave w copies LDS B rows 32w .. 32w+31: for the pair, gate rows n0 + 32w + .. (w < 4)
+    // or up rows n0 + 32(w-4) + .. (w >= 4); for down, rows n0 + 32w + ...
+    const int bmat = PAIR ? (wave >> 2) : 0;
+    const int bl0 = PAIR ? 32 * (wave & 3) : 32 * wave;        // first matrix row (past n0) it copies
     const uint8_t *b_base = uniform_ptr((PAIR && bmat ? p.w[1] : p.w[0]) + (size_t)eu * p.N * Kh);
     const int cr = lane >> 3, cpos = lane & 7;
-    uint32_t aoff[NA], boff[8];
-    int achunk[NA], bchunk[8];
+    uint32_t aoff[TM];
 #pragma unroll
-    for (int t = 0; t < NA; ++t) {
-        const int r = wave * 16 * TM + 8 * t + cr;
-        achunk[t] = cpos ^ qswz(r);
-        aoff[t] = (uint32_t)s_arow[r] * Kh + 16 * achunk[t];
+    for (int t = 0; t < TM; ++t) {
+        const int r = wave * 8 * TM + 8 * t + cr;
+        aoff[t] = (uint32_t)s_arow[r] * Kh + 16 * (cpos ^ qswz(r));
     }
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-        const int r = 64 * wave + 8 * t + cr;                   // LDS B row
-        bchunk[t] = cpos ^ qswz(r);
-        boff[t] = (uint32_t)min(u.n0 + bl0 + 8 * t + cr, p.N - 1) * Kh + 16 * bchunk[t];
-    }
-    // Scale windows: LDS scale row q (A rows 0..255, then B rows 0..255) holds, from byte 0,
-    // the aligned dwords covering the step's bytes of that row; 4 lanes per row, dword d of
-    // the window.  A dword past the step's bytes fetches the window's first dword again, so
-    // every fetched dword lies inside the array.  Wave w copies scale rows 128w .. 128w+127.
+    // B source of piece t, computed when it is issued: matrix row min(brow0 + 8t, N-1), chunk
+    // (lane%8) ^ qswz(LDS row)
+    const int brow0 = u.n0 + bl0 + cr;
+    auto boff = [&](int t) {
+        return (uint32_t)min(brow0 + 8 * t, p.N - 1) * Kh + 16 * (cpos ^ qswz(32 * wave + 8 * t + cr));
+    };
+    // Scale windows.  LDS scale row q (A rows 0..255, then B rows 0..255) has a 16-byte slot
+    // per stage; wave w copies scale rows 64w .. 64w+63.
+    //  * AS (every scale row starts on a dword: K % 128 == 0, aligned bases, K >= 512): one
+    //    lane per row copies a two-step window, the row's bytes min(16j, Kb-16) .. +15 for
+    //    steps 2j and 2j+1, into the slots of stage j % 2 -- one copy per wave every other step.
+    //  * otherwise: every step, the aligned dwords covering the step's 8 bytes of the row, from
+    //    byte 0 of the slot; 4 lanes per row, dword d of the window.  A dword past the step's
+    //    bytes fetches the window's first dword again, so every fetched dword lies inside the
+    //    array.
     const uint8_t *sc_base;
-    uint32_t sc_rel[8];                           // (scale row start - aligned base), per copy
+    uint32_t sc_rel[AS ? 1 : 4];                  // scale row start (- aligned base), per copy
     {
-        const bool arows = wave < 2;
-        const uint8_t *bs = PAIR && wave == 3 ? p.ws[1] : p.ws[0];
+        const bool arows = wave < 4;
+        const uint8_t *bs = PAIR && wave >= 6 ? p.ws[1] : p.ws[0];
         const uintptr_t bsa = (uintptr_t)bs & ~(uintptr_t)3;
         sc_base = uniform_ptr(arows ? (const uint8_t *)as_base : (const uint8_t *)(bsa + (size_t)eu * p.N * Kb));
         const uint32_t bmis = (uint32_t)((uintptr_t)bs & 3u);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int q = 128 * wave + 16 * i + (lane >> 2);
+        for (int i = 0; i < (AS ? 1 : 4); ++i) {
+            const int q = AS ? 64 * wave + lane : 64 * wave + 16 * i + (lane >> 2);
             if (arows) {
                 sc_rel[i] = as_mis + (uint32_t)s_arow[q] * Kb;
             } else {
@@ -183,11 +194,12 @@ MOE_DEV void qgemm_unit(const GemmParams &p, const QUnit &u, unsigned char *smem
         const uint32_t need = (o + (uint32_t)len - 1u) >> 2;
         return rel - o + ((uint32_t)sd <= need ? 4u * sd : 0u);
     };
+    auto win_start = [&](int j) { return min(16 * j, Kb - 16); };   // AS: first byte of window j
 
     // Copies of step s into stage s % 2 (a step past the last copies the last step's bytes into
-    // the stage no step reads any more), as 24 pieces per wave: 0-7 A codes (pieces past the
-    // 2*TM this unit needs repeat its first one: same bytes to the same place, so every step
-    // issues the same number), 8-15 B codes, 16-23 scale windows.  In the last step, chunks
+    // the stage no step reads any more), as 12 pieces per wave: 0-3 A codes (pieces past the
+    // TM this unit needs repeat its first one: same bytes to the same place, so every step
+    // issues the same number), 4-7 B codes, 8-11 scale windows.  In the last step, chunks
     // past the end of a row are clamped to its last block (read, never used) and the scale
     // windows shrink.
     auto issue_piece = [&](int s_in, int pc) {
@@ -195,52 +207,72 @@ MOE_DEV void qgemm_unit(const GemmParams &p, const QUnit &u, unsigned char *smem
         const bool last = s == S - 1;
         const int st = s_in & 1;
         const uint32_t cmax = 16u * (uint32_t)(Kb - 1 - 8 * s);   // last valid chunk (bytes) in the step
-        if (pc < 8) {
-            const int t = pc < NA ? pc : 0;
+        if (pc < 4) {
+            const int t = pc < TM ? pc : 0;
             uint32_t v = aoff[t];
-            if (last) v = v - 16 * achunk[t] + min(16u * achunk[t], cmax);
-            dma16(a_base + 128 * s, v, smem + kQOffA + st * kQA + wave * 16 * TM * kQRowB + t * 1024);
-        } else if (pc < 16) {
-            const int t = pc - 8;
-            uint32_t v = boff[t];
-            if (last) v = v - 16 * bchunk[t] + min(16u * bchunk[t], cmax);
-            dma16(b_base + 128 * s, v, smem + kQOffB + st * kQB + 64 * wave * kQRowB + t * 1024);
+            if (last) {                           // the chunk's byte offset within the row's step line
+                const uint32_t c = 16u * (uint32_t)(cpos ^ qswz(wave * 8 * TM + 8 * t + cr));
+                v = v - c + min(c, cmax);
+            }
+            dma16(a_base + 128 * s, v, smem + kQOffA + st * kQA + wave * 8 * TM * kQRowB + t * 1024);
+        } else if (pc < 8) {
+            const int t = pc - 4;
+            uint32_t v = boff(t);
+            if (last) {
+                const uint32_t c = 16u * (uint32_t)(cpos ^ qswz(32 * wave + 8 * t + cr));
+                v = v - c + min(c, cmax);
+            }
+            dma16(b_base + 128 * s, v, smem + kQOffB + st * kQB + 32 * wave * kQRowB + t * 1024);
+        } else if constexpr (AS) {
+            if ((s_in & 1) || s_in >= S) return;  // a window serves steps s_in and s_in + 1
+            const int j = s_in >> 1;
+            dma16(sc_base + win_start(j), sc_rel[0], smem + kQOffS + (j & 1) * kQS + 64 * wave * kQSlot);
         } else {
-            const int i = pc - 16;
+            const int i = pc - 8;
             dma4(sc_base + 8 * s, sc_voff(sc_rel[i], last ? nvalid : 8),
-                 smem + kQOffS + st * kQS + 128 * wave * kQSlot + i * 256);
+                 smem + kQOffS + st * kQS + 64 * wave * kQSlot + i * 256);
         }
     };
-    constexpr int kPieces = 24;
+    constexpr int kPieces = AS ? 9 : 12;
 
     // ---- consumer side.  Row tiles of this wave: rows 32*TM*wm + 32i (i < TM) of the unit;
-    // weight tiles jb: the pair's gate columns 64wn + 32j (jb = j) and up columns (jb = 2 + j);
-    // down: columns 128wn + 32jb.  Operand address of tile x in quarter q: row base + chunk
+    // weight tiles jb < 2: the pair's gate columns 32wn (jb = 0) and up columns 32wn (jb = 1);
+    // down: columns 64wn + 32jb.  Operand address of tile x in quarter q: row base + chunk
     // (4hb + q) ^ swz = (4hb ^ swz) ^ q.
-    int a_at[TM], b_at[4], sa_at[TM], sb_at[4];
-    uint32_t sa_o[TM], sb_o[4];
+    // Tile i's rows are 32i past tile 0's, with the same low bits (so the same swizzle): its
+    // operand and scale addresses are tile 0's plus a constant.  The scale bytes' offset within
+    // their dword (the window starts at an aligned dword) is kept per tile in 4 bits: A tile i at
+    // bit 4i, B tile jb at bit 16 + 4jb.
+    // The four base addresses are recomputed at every step from a lane id the compiler cannot
+    // hoist (the step loop has no registers to spare for them).
+    const int ra = 32 * TM * wm + hr;
+    constexpr int kBTile = PAIR ? 128 : 32;        // LDS B rows between the wave's two weight tiles
+    const int rb = PAIR ? 32 * wn + hr : 64 * wn + hr;
+    struct Bases {
+        int a, b, sa, sb;
+    };
+    auto bases = [&]() {
+        const int ln = lane_fresh(), hr_ = ln & 31, hb_ = ln >> 5;
+        const int ra_ = 32 * TM * wm + hr_, rb_ = (PAIR ? 32 : 64) * wn + hr_;
+        return Bases{kQOffA + ra_ * kQRowB + (((4 * hb_) ^ qswz(ra_)) << 4),
+                     kQOffB + rb_ * kQRowB + (((4 * hb_) ^ qswz(rb_)) << 4), kQOffS + ra_ * kQSlot + 4 * hb_,
+                     kQOffS + (kQBM + rb_) * kQSlot + 4 * hb_};
+    };
+    uint32_t so_pack = 0;
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-        const int r = 32 * TM * wm + 32 * i + hr;
-        a_at[i] = kQOffA + r * kQRowB + (((4 * hb) ^ qswz(r)) << 4);
-        sa_at[i] = kQOffS + r * kQSlot + 4 * hb;
-        sa_o[i] = (as_mis + (uint32_t)s_arow[r] * Kb) & 3u;
-    }
+    for (int i = 0; i < TM; ++i) so_pack |= ((as_mis + (uint32_t)s_arow[ra + 32 * i] * Kb) & 3u) << (4 * i);
 #pragma unroll
-    for (int jb = 0; jb < 4; ++jb) {
-        const int br = PAIR ? 128 * (jb >> 1) + 64 * wn + 32 * (jb & 1) + hr : 128 * wn + 32 * jb + hr;
-        b_at[jb] = kQOffB + br * kQRowB + (((4 * hb) ^ qswz(br)) << 4);
-        sb_at[jb] = kQOffS + (kQBM + br) * kQSlot + 4 * hb;
-        const uint8_t *bs = PAIR && jb >= 2 ? p.ws[1] : p.ws[0];
-        const int n = PAIR ? u.n0 + (br & 127) : u.n0 + br;
-        sb_o[jb] = (uint32_t)(((uintptr_t)bs & 3u) + ((size_t)eu * p.N + min(n, p.N - 1)) * Kb) & 3u;
+    for (int jb = 0; jb < 2; ++jb) {
+        const uint8_t *bs = PAIR && jb == 1 ? p.ws[1] : p.ws[0];
+        const int n = PAIR ? u.n0 + 32 * wn + hr : u.n0 + 64 * wn + 32 * jb + hr;
+        so_pack |= ((uint32_t)(((uintptr_t)bs & 3u) + ((size_t)eu * p.N + min(n, p.N - 1)) * Kb) & 3u) << (16 + 4 * jb);
     }
 
-    f32x16 acc[TM][4];
+    f32x16 acc[TM][2];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb)
+        for (int jb = 0; jb < 2; ++jb)
 #pragma unroll
             for (int v = 0; v < 16; ++v) acc[i][jb][v] = 0.0f;
 
@@ -255,16 +287,30 @@ MOE_DEV void qgemm_unit(const GemmParams &p, const QUnit &u, unsigned char *smem
     // magnitude, far below float32's smallest subnormal (2^-149), so it adds an exact zero
     // (their codes are real codes of a clamped block, never NaN or infinite: E2M1 has none).
     // The copies of step s+1 go out during the first half of step s's products, a piece after
-    // every few of them: issued in one burst they would hold back the wave's matrix
-    // instructions while the L1 takes them; spread over the step they land before its end.
+    // every product or so.
     auto step = [&](int s) {
         const int so = s & 1;
+        const Bases bs = bases();
+        const int a_at = bs.a, b_at = bs.b, sa_at = bs.sa, sb_at = bs.sb;
 
-        uint32_t sa[TM], sb[4];
+        uint32_t sa[TM], sb[2];
+        if constexpr (AS) {
+            // the step's bytes sit at 8s - win_start(s/2) in the window; a dword wholly past K
+            // (offset 16) is never needed (its blocks get scale 0 below), so it reads byte 12
+            const int j = s >> 1;
+            const int o = min(8 * s - win_start(j) + 4 * hb, 12) - 4 * hb;
+            const int sw = (j & 1) * kQS + o;
 #pragma unroll
-        for (int i = 0; i < TM; ++i) sa[i] = scale4(sa_at[i] + so * kQS, sa_o[i]);
+            for (int i = 0; i < TM; ++i) sa[i] = *(const uint32_t *)(smem + sa_at + 32 * i * kQSlot + sw);
 #pragma unroll
-        for (int jb = 0; jb < 4; ++jb) sb[jb] = scale4(sb_at[jb] + so * kQS, sb_o[jb]);
+            for (int jb = 0; jb < 2; ++jb) sb[jb] = *(const uint32_t *)(smem + sb_at + kBTile * jb * kQSlot + sw);
+        } else {
+#pragma unroll
+            for (int i = 0; i < TM; ++i) sa[i] = scale4(sa_at + 32 * i * kQSlot + so * kQS, (so_pack >> (4 * i)) & 3u);
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb)
+                sb[jb] = scale4(sb_at + kBTile * jb * kQSlot + so * kQS, (so_pack >> (16 + 4 * jb)) & 3u);
+        }
         if (s == S - 1) {
             uint32_t kmask = 0xffffffffu;          // bytes of this lane's valid quarters
 #pragma unroll
@@ -273,31 +319,31 @@ MOE_DEV void qgemm_unit(const GemmParams &p, const QUnit &u, unsigned char *smem
 #pragma unroll
             for (int i = 0; i < TM; ++i) sa[i] &= kmask;
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) sb[jb] &= kmask;
+            for (int jb = 0; jb < 2; ++jb) sb[jb] &= kmask;
         }
-        u32x4 fa[2][TM], fb[2][4];
-        auto rd = [&](int q, u32x4 (&a)[TM], u32x4 (&b)[4]) {
+        u32x4 fa[2][TM], fb[2][2];
+        auto rd = [&](int q, u32x4 (&a)[TM], u32x4 (&b)[2]) {
 #pragma unroll
-            for (int i = 0; i < TM; ++i) a[i] = lds16((a_at[i] ^ (q << 4)) + so * kQA);
+            for (int i = 0; i < TM; ++i) a[i] = lds16((a_at ^ (q << 4)) + 32 * i * kQRowB + so * kQA);
 #pragma unroll
-            for (int jb = 0; jb < 4; ++jb) b[jb] = lds16((b_at[jb] ^ (q << 4)) + so * kQB);
+            for (int jb = 0; jb < 2; ++jb) b[jb] = lds16((b_at ^ (q << 4)) + kBTile * jb * kQRowB + so * kQB);
         };
         // quarter Q: the next quarter's operands are read while this one's products run
         auto quarter = [&](auto q_c) {
             constexpr int Q = decltype(q_c)::value;
             if constexpr (Q < 3) rd(Q + 1, fa[(Q + 1) & 1], fb[(Q + 1) & 1]);
-            constexpr int NH = 8 * TM;             // products in the first half of the step
+            constexpr int NH = 4 * TM;             // products in the first half of the step
 #pragma unroll
             for (int i = 0; i < TM; ++i)
 #pragma unroll
-                for (int jb = 0; jb < 4; ++jb) {
+                for (int jb = 0; jb < 2; ++jb) {
                     const u32x4 av = fa[Q & 1][i], bv = fb[Q & 1][jb];
                     acc[i][jb] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
                         i32x8_t{(int)av[0], (int)av[1], (int)av[2], (int)av[3], 0, 0, 0, 0},
                         i32x8_t{(int)bv[0], (int)bv[1], (int)bv[2], (int)bv[3], 0, 0, 0, 0}, acc[i][jb], 4, 4, Q,
                         (int)sa[i], Q, (int)sb[jb]);
                     if constexpr (Q < 2) {
-                        const int m = Q * 4 * TM + 4 * i + jb;
+                        const int m = Q * 2 * TM + 2 * i + jb;
 #pragma unroll
                         for (int pc = m * kPieces / NH; pc < (m + 1) * kPieces / NH; ++pc) issue_piece(s + 1, pc);
                         __builtin_amdgcn_sched_barrier(0);
@@ -333,36 +379,34 @@ MOE_DEV void qgemm_unit(const GemmParams &p, const QUnit &u, unsigned char *smem
                 if (r >= u.M) continue;
                 const size_t orow = (size_t)(u.row0 + r);
 #pragma unroll
-                for (int jb = 0; jb < 4; ++jb) {
-                    const int n = u.n0 + 128 * wn + 32 * jb + hr;
+                for (int jb = 0; jb < 2; ++jb) {
+                    const int n = u.n0 + 64 * wn + 32 * jb + hr;
                     if (n < p.N) p.out[orow * p.N + n] = acc[i][jb][v];
                 }
             }
     } else {
-        // h = silu(g) * u of the wave's 32*TM rows x 64 columns into LDS (row stride kQLd,
-        // skewed against bank conflicts), then each lane quantises one row's 32-column block
-        // at a time: block maximum, 32 codes packed into 16 bytes, one scale byte.
+        // h = silu(g) * u of the wave's 32*TM rows x 32 columns into LDS (row stride kQLd,
+        // skewed against bank conflicts), then each lane quantises one row's 32-column block:
+        // block maximum, 32 codes packed into 16 bytes, one scale byte.
         float *hq_lds = (float *)smem + wave * (128 * kQLd);
 #pragma unroll
         for (int i = 0; i < TM; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) {
-                    const int r = 32 * i + 8 * (v >> 2) + 4 * hb + (v & 3);
-                    hq_lds[r * kQLd + 32 * j + hr] = silu_fast(acc[i][j][v]) * acc[i][2 + j][v];
-                }
+            for (int v = 0; v < 16; ++v) {
+                const int r = 32 * i + 8 * (v >> 2) + 4 * hb + (v & 3);
+                hq_lds[r * kQLd + hr] = silu_fast(acc[i][0][v]) * acc[i][1][v];
+            }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");    // LDS is in order within a wave
         const bool vec_ok = (((uintptr_t)p.oq) & 15u) == 0;
+        const int nb = u.n0 + 32 * wn;                         // first column of the wave's block
 #pragma unroll
-        for (int it0 = 0; it0 < 64 * TM; it0 += 64) {
-            const int pi = it0 + lane;
-            const int rr = pi >> 1, jb = pi & 1;                  // row in the wave's block, column block
-            const int r = rbase + rr;
-            const int nb = u.n0 + 64 * wn + 32 * jb;               // first column of the block
+        for (int it0 = 0; it0 < 32 * TM; it0 += 64) {
+            const int rr = it0 + lane;                         // row in the wave's block
+            if (rr >= 32 * TM) continue;
             f32x4 h[8];
 #pragma unroll
-            for (int q = 0; q < 8; ++q) h[q] = *(const f32x4 *)(hq_lds + rr * kQLd + 32 * jb + 4 * q);
+            for (int q = 0; q < 8; ++q) h[q] = *(const f32x4 *)(hq_lds + rr * kQLd + 4 * q);
+            const int r = rbase + rr;
             if (r >= u.M || nb >= p.N) continue;
             const size_t orow = (size_t)(u.row0 + r);
             if (p.out) {
@@ -402,10 +446,10 @@ MOE_DEV void qgemm_unit(const GemmParams &p, const QUnit &u, unsigned char *smem
     }
 }
 
-// One workgroup per CU (its LDS takes 147 KB), so each wave may use a SIMD's whole register
-// file: the 16 accumulator tiles alone take 256 registers.
-template <bool PAIR, bool ROUTED>
-__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void mxgemm_kernel(
+// One workgroup per CU (its LDS takes 147 KB) of 8 waves, two per SIMD: each wave may use
+// half a SIMD's register file, 256 registers, of which the 8 accumulator tiles take 128.
+template <bool PAIR, bool ROUTED, bool AS>
+__global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void mxgemm_kernel(
     const GemmParams p) {
     __shared__ __align__(16) unsigned char smem[kQLds];
     __shared__ int s_tp[ROUTED ? MOE_MAX_EXPERTS : 1];
@@ -467,9 +511,9 @@ __global__ __launch_bounds__(kQThreads) __attribute__((amdgpu_waves_per_eu(1, 1)
             s_arow[r] = min(max(src, 0), p.n_arows - 1);
         }
         __syncthreads();
-        if (TM == 4) qgemm_unit<PAIR, 4>(p, u, smem, s_arow);
-        else if (TM == 2) qgemm_unit<PAIR, 2>(p, u, smem, s_arow);
-        else qgemm_unit<PAIR, 1>(p, u, smem, s_arow);
+        if (TM == 4) qgemm_unit<PAIR, 4, AS>(p, u, smem, s_arow);
+        else if (TM == 2) qgemm_unit<PAIR, 2, AS>(p, u, smem, s_arow);
+        else qgemm_unit<PAIR, 1, AS>(p, u, smem, s_arow);
         __syncthreads();                                     // the unit is done with s_arow and LDS
     }
 }
@@ -484,7 +528,7 @@ bool mfma_path_wanted(const moe_expert_weights *w, int act, int T, int k, bool r
 }
 
 // Workgroups resident at once for a kernel on the current device (queried once per device).
-template <bool PAIR, bool ROUTED>
+template <bool PAIR, bool ROUTED, bool AS>
 static int resident_workgroups() {
     constexpr int kMaxDev = 64;
     static int cache[kMaxDev] = {};
@@ -493,7 +537,7 @@ static int resident_workgroups() {
     if (cache[dev] == 0) {
         int cus = 0, per_cu = 0;
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
-        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mxgemm_kernel<PAIR, ROUTED>, kQThreads, 0) !=
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, mxgemm_kernel<PAIR, ROUTED, AS>, kQThreads, 0) !=
                 hipSuccess ||
             per_cu <= 0)
             per_cu = 1;
@@ -504,13 +548,21 @@ static int resident_workgroups() {
 
 // Persistent launch: at most one wave of resident workgroups, each walking the work units
 // with a stride of the grid size.  `mt_bound` bounds the row tiles (4 parts each at most).
+// The two-step scale windows need every scale row on a dword (K % 128 == 0, dword-aligned
+// scale arrays) and at least two K-steps of scales per row (K >= 512).
 template <bool PAIR, bool ROUTED>
 static moe_status gemm_launch(const GemmParams &p, int mt_bound, hipStream_t stream, const char *what) {
     const int NB = PAIR ? kQBR / 2 : kQBR;
+    const bool as = p.K % 128 == 0 && p.K >= 512 && ((uintptr_t)p.as & 3u) == 0 && ((uintptr_t)p.ws[0] & 3u) == 0 &&
+                    (!PAIR || ((uintptr_t)p.ws[1] & 3u) == 0);
     const int64_t units = 4 * (int64_t)mt_bound * ((p.N + NB - 1) / NB);
-    const int64_t g = std::min<int64_t>(units, resident_workgroups<PAIR, ROUTED>());
+    const int64_t g = std::min<int64_t>(units, as ? resident_workgroups<PAIR, ROUTED, true>()
+                                                   : resident_workgroups<PAIR, ROUTED, false>());
     if (g <= 0) return MOE_OK;
-    hipLaunchKernelGGL((mxgemm_kernel<PAIR, ROUTED>), dim3((unsigned)g), dim3(kQThreads), 0, stream, p);
+    if (as)
+        hipLaunchKernelGGL((mxgemm_kernel<PAIR, ROUTED, true>), dim3((unsigned)g), dim3(kQThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL((mxgemm_kernel<PAIR, ROUTED, false>), dim3((unsigned)g), dim3(kQThreads), 0, stream, p);
     return launch_check(what);
 }
 

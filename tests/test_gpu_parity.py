@@ -622,6 +622,9 @@ MX_GEMM_CASES = {
     "ragged_k_and_n": tiny(name="g1", wtag=91, act="mxfp4", T=160, H=544, I=320, E=4, k=2),
     "multi_tile_rows": tiny(name="g2", wtag=92, act="mxfp4", T=300, H=256, I=128, E=2, k=1),
     "many_experts": tiny(name="g3", wtag=93, act="mxfp4", T=128, H=512, I=256, E=64, k=6),
+    # K = 640 (gate/up) and 768 (down): dword-aligned scale rows, an odd number of K-steps, so the
+    # last two-step scale window is moved back to end at the row's last byte
+    "odd_steps_aligned_scales": tiny(name="g4", wtag=94, act="mxfp4", T=200, H=640, I=768, E=8, k=2),
 }
 
 
