@@ -113,7 +113,7 @@ def down_algorithmic(cfg, D, fused=False):
 def dominant_kernel(cfg):
     """Name pattern (as rocprofv3 reports it) of the routed gate/up kernel of a workload."""
     if cfg.act == "mxfp4" and cfg.T >= 64:
-        return r"mxgemm_kernel<true, true>"
+        return r"mxgemm_kernel<true, true, (?:true|false)>"
     if cfg.wfmt == "mxfp4" and cfg.T >= 64:
         return r"fgemm_pair_kernel<\w+, true>"
     if cfg.T <= 8:
@@ -126,7 +126,7 @@ def down_kernel(cfg, fused):
     if fused:
         return r"down_combine_mfma_kernel" if cfg.wfmt == "mxfp4" else r"down_combine_kernel"
     if cfg.act == "mxfp4" and cfg.T >= 64:
-        return r"mxgemm_kernel<false, true>"
+        return r"mxgemm_kernel<false, true, (?:true|false)>"
     if cfg.wfmt == "mxfp4" and cfg.T >= 64:
         return r"fgemm_down_kernel"
     return r"gemv_\w*kernel<\d+, \d+, \d+, false"

@@ -63,8 +63,8 @@ def test_dominant_kernel_patterns_select_one_instantiation():
     names = {
         "qwen38max_decode": ("void moe::gemv_flat_kernel<0, 0, 1, true, true>(moe::GemvParams)",
                              "void moe::gemv_kernel<0, 0, 1, true, false>(moe::GemvParams)"),
-        "qwen38max_prefill_hot": ("void moe::mxgemm_kernel<true, true>(moe::GemmParams)",
-                                  "void moe::mxgemm_kernel<true, false>(moe::GemmParams)"),
+        "qwen38max_prefill_hot": ("void moe::mxgemm_kernel<true, true, true>(moe::GemmParams)",
+                                  "void moe::mxgemm_kernel<true, false, true>(moe::GemmParams)"),
         "qwen38max_prefill_hot_float": ("void moe::fgemm_pair_kernel<false, true>(moe::FGemmParams)",
                                         "void moe::fgemm_pair_kernel<false, false>(moe::FGemmParams)"),
     }
