@@ -593,7 +593,8 @@ def main():
     line = json.dumps(res)
     print(line, flush=True)
     if args.json_out:
-        with open(args.json_out, "w") as f:
+        os.makedirs(os.path.dirname(os.path.abspath(args.json_out)), exist_ok=True)
+    with open(args.json_out, "w") as f:
             f.write(line + "\n")
 
 
