@@ -88,10 +88,11 @@ def algorithmic(cfg, D, fused=False):
     return dict(layer_bytes=layer_bytes, layer_flops=flops, gu_bytes=gu_bytes, gu_flops=gu_flops)
 
 
-def down_algorithmic(cfg, D, fused=False):
+def down_algorithmic(cfg, D, fused=False, combined=None):
     """Algorithmic bytes and flops of the routed down launch: the touched experts' down
-    weights, h in, the rows out.  `fused`: the decode down product with the combine, which
-    also covers the shared expert's down rows and writes one output row per token."""
+    weights, h in, the rows out.  `combined` (default: `fused`): the down product with the
+    combine, which writes one output row per token; `fused`: that launch also covers the
+    shared expert's down rows."""
     K, I, T, k = cfg.d_model, cfg.I, cfg.T, cfg.k
     P = T * k
     w_down = K * I * 17 // 32 if cfg.wfmt == "mxfp4" else K * I + (K // 128) * (I // 128) * 4
@@ -101,10 +102,10 @@ def down_algorithmic(cfg, D, fused=False):
     else:
         h_in, out = P * I * 4, P * K * 4
     nbytes = D * w_down + h_in + out
-    if fused:
+    if fused if combined is None else combined:
         out = T * K * 4
         nbytes = D * w_down + h_in + out
-        if cfg.shared:
+        if fused and cfg.shared:
             nbytes += cfg.expert_bytes(cfg.shared_K, cfg.shared_I) // 3 + T * cfg.shared_I * 4
             flops += 2 * T * K * cfg.shared_I
     return dict(bytes=nbytes, flops=flops)
@@ -121,9 +122,9 @@ def dominant_kernel(cfg):
     return r"gemv_kernel<\d+, \d+, \d+, true, true>"
 
 
-def down_kernel(cfg, fused):
+def down_kernel(cfg, fused, combined=None):
     """Name pattern of the routed down kernel of a workload."""
-    if fused:
+    if fused if combined is None else combined:
         return r"down_combine_mfma_kernel" if cfg.wfmt == "mxfp4" else r"down_combine_kernel"
     if cfg.act == "mxfp4" and cfg.T >= 64:
         return r"mxgemm_kernel<false, true, (?:true|false)>"
@@ -353,12 +354,13 @@ def run_workload(torch, sdev, cfg, layers, NB, steps, warmup, use_graphs, dev, t
                 graphs=graphs is not None, slots=S, phases=phases)
 
 
-def kernel_entries(cfg, fused, r):
+def kernel_entries(cfg, fused, r, combined=None):
     """Roofline entries of the routed gate/up and down launches of one workload."""
+    combined = fused if combined is None else combined
     peak = peak_for(cfg)
     D_ev = r["D_ev"]
     gu = [algorithmic(cfg, D, fused) for D in D_ev]
-    dn = [down_algorithmic(cfg, D, fused) for D in D_ev]
+    dn = [down_algorithmic(cfg, D, fused, combined) for D in D_ev]
     gu_b, gu_f = sum(x["gu_bytes"] for x in gu) / len(gu), sum(x["gu_flops"] for x in gu) / len(gu)
     dn_b, dn_f = sum(x["bytes"] for x in dn) / len(dn), sum(x["flops"] for x in dn) / len(dn)
     timing = ("HIP events on the launch stream around each launch, eager pass over the step slots "
@@ -366,8 +368,9 @@ def kernel_entries(cfg, fused, r):
     out = []
     for role, pat, b, f, us in (("routed gate/up" + (" + shared gate/up" if fused and cfg.shared else ""),
                                  dominant_kernel(cfg), gu_b, gu_f, r["gu_us"]),
-                                ("routed down" + (" + shared down + combine" if fused else ""),
-                                 down_kernel(cfg, fused), dn_b, dn_f, r["dn_us"])):
+                                ("routed down" + (" + shared down + combine" if fused else
+                                                  (" + combine" if combined else "")),
+                                 down_kernel(cfg, fused, combined), dn_b, dn_f, r["dn_us"])):
         e = dict(workload=cfg.name, role=role, kernel=pat)
         e.update(roofline(b, f, us, peak))
         e.update(bytes_per_launch=int(b), flops_per_launch=int(f), avg_launch_us=round(us, 2), launches=r["launches"],
@@ -538,7 +541,7 @@ def main():
         log("[bench] traffic run done")
         return
     log(f"[bench] {cfg.name}: {args.steps} steps, {r['ms_per_step'] * 1e3:.2f} us/step")
-    kernels = kernel_entries(cfg, fused, r)
+    kernels = kernel_entries(cfg, fused, r, layers[0].down_combined)
     del layers
 
     prefill = {}
@@ -547,7 +550,7 @@ def main():
         pf = pl[0].fused
         pr = run_workload(torch, sdev, pc, pl, NB, args.prefill_steps, 2, not args.no_graph, dev)
         log(f"[bench] {pc.name}: {args.prefill_steps} steps, {pr['ms_per_step'] * 1e3:.1f} us/step")
-        pk = kernel_entries(pc, pf, pr)
+        pk = kernel_entries(pc, pf, pr, pl[0].down_combined)
         kernels += pk
         prefill[pc.name] = dict(T=pc.T, steps=args.prefill_steps, warmup=2, ms_per_step=round(pr["ms_per_step"], 5),
                                 tokens_per_s=round(pc.T / (pr["ms_per_step"] * 1e-3), 1),
@@ -594,7 +597,7 @@ def main():
     print(line, flush=True)
     if args.json_out:
         os.makedirs(os.path.dirname(os.path.abspath(args.json_out)), exist_ok=True)
-    with open(args.json_out, "w") as f:
+        with open(args.json_out, "w") as f:
             f.write(line + "\n")
 
 

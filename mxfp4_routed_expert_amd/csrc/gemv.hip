@@ -1211,6 +1211,13 @@ static GemvFn pick_flat_route_m(int maxm) {
     }
 }
 
+// Workgroups of a flat launch: one per CU, or one per pass when there are fewer passes than
+// CUs.  A launch of few passes (a small projection, a lone shared expert) spreads them over
+// every CU: the bytes in flight scale with the CUs streaming, not with the waves of one CU.
+static int flat_grid(long long passes) {
+    return (int)std::min<long long>(device_cu_count(), std::max<long long>(1, passes));
+}
+
 bool gemv_route_launch(int fmt, int act, GemvParams p, int slots, hipStream_t stream, moe_status *st) {
     if ((fmt != kFmtMXFP4 && fmt != kFmtFP8) || act != kActBF16) return false;
     const int units = fmt == kFmtMXFP4 ? p.K / 32 : p.K / 16;
@@ -1226,8 +1233,7 @@ bool gemv_route_launch(int fmt, int act, GemvParams p, int slots, hipStream_t st
     const int rpp = 32 / p.G;
     long long passes = (long long)(slots - (p.shared_slot >= 0 ? 1 : 0)) * ((p.N + rpp - 1) / rpp);
     if (p.shared_slot >= 0) passes += (p.sN + rpp - 1) / rpp;
-    const long long per_wg = kFlatThreads / 64;
-    const int nwg = (int)std::min<long long>(device_cu_count(), std::max<long long>(1, (passes + per_wg - 1) / per_wg));
+    const int nwg = flat_grid(passes);
     GemvFn fn = fmt == kFmtMXFP4 ? pick_flat_route_m<kFmtMXFP4, kActBF16>(maxm) : pick_flat_route_m<kFmtFP8, kActBF16>(maxm);
     hipLaunchKernelGGL(fn, dim3(nwg), dim3(kFlatThreads), lds, stream, p);
     *st = launch_check("moe_route_gateup_shared: gemv_flat_kernel");
@@ -1255,8 +1261,7 @@ moe_status gemv_launch(int fmt, int act, bool pair, GemvParams p, int slots, int
         const int routed_slots = routed ? slots - (p.shared_slot >= 0 ? 1 : 0) : 1;
         long long passes = (long long)routed_slots * ((p.N + rpp - 1) / rpp);
         if (p.shared_slot >= 0) passes += (p.sN + rpp - 1) / rpp;
-        const long long per_wg = kFlatThreads / 64;
-        const int nwg = (int)std::min<long long>(device_cu_count(), std::max<long long>(1, (passes + per_wg - 1) / per_wg));
+        const int nwg = flat_grid(passes);
         hipLaunchKernelGGL(pick_flat(fmt, act, pair, maxm), dim3(nwg), dim3(kFlatThreads), (size_t)p.n_act_rows * rs,
                            stream, p);
         return launch_check(what);

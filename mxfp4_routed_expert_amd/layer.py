@@ -4,6 +4,8 @@ route -> permute -> routed experts (moe_expert_ffn) -> shared expert (moe_expert
 identity form) -> combine; LatentMoE layers add moe_dense_bf16 before the routed experts
 and after the combine (Kimi K3 article, architecture section); a gated shared expert's
 output is scaled by its gate before it is added after the up projection.  Decode-sized
+LatentMoE steps run the routed down product and the combine into z as one down-combine
+launch.  Decode-sized
 batches use the fused calls instead, three kernels a step: the router's logits; the
 selection with the routed and shared gate/up in one launch (moe_topk_gateup_shared); down
 and combine in one launch.  Every step runs in the HIP library; this module only wires
@@ -78,12 +80,18 @@ class MoELayer:
         # down product writes the combined output directly (moe_expert_gateup_shared,
         # moe_expert_down_combine), so y_rows and y_shared never exist.
         self.fused = fuses(w, T)
+        # decode-sized LatentMoE steps: the routed down product and the combine into z run as
+        # one down-combine launch with no shared slot (the shared expert's output is added after
+        # the up projection), so y_rows never exists
+        self.latent_down_combine = (w.act == "float" and w.p_up is not None and 1 <= T <= 8
+                                    and down_combine_lds(w.k, False, w.experts.d_ff) <= FUSED_LDS_LIMIT)
+        self.down_combined = self.fused or self.latent_down_combine
         sh = w.shared
         self.ids, self.topk_w = e(T, k, dt=i32), e(T, k)
         self.sg = e(T) if w.w_shared_gate is not None else None
         self.offs, self.sp, self.p2r = e(E + 1, dt=i32), e(T * k, dt=i32), e(T * k, dt=i32)
         self.x_lat = e(T, L) if w.p_down is not None else None
-        self.y_rows = None if self.fused else e(T * k, L)
+        self.y_rows = None if self.down_combined else e(T * k, L)
         self.y_s = e(T, H) if (sh is not None and not self.fused) else None
         self.z = e(T, L) if w.p_up is not None else None
         # LatentMoE with a gated shared expert: g * y_s is formed by moe_combine with no
@@ -165,13 +173,17 @@ class MoELayer:
             mark("gateup_end")
         if mark is not None:
             mark("down_begin")
-        B.moe_expert_down(w.experts, self.T, w.act, w.k, self.offs, self.h, self.hq, self.hs, out=self.y_rows)
+        if self.latent_down_combine:
+            B.moe_expert_down_combine(w.experts, None, self.h, None, self.ids, self.topk_w, self.p2r, out=self.z)
+        else:
+            B.moe_expert_down(w.experts, self.T, w.act, w.k, self.offs, self.h, self.hq, self.hs, out=self.y_rows)
         if mark is not None:
             mark("down_end")
         if w.shared is not None:
             cur.wait_stream(self.side)
         if w.p_up is not None:
-            B.moe_combine(self.y_rows, self.p2r, self.topk_w, out=self.z)
+            if not self.latent_down_combine:
+                B.moe_combine(self.y_rows, self.p2r, self.topk_w, out=self.z)
             res = self.y_s
             if self.latent_gate:
                 res = B.moe_combine(None, self.no_rows, self.no_w, self.y_s, self.sg, out=self.y_sg)

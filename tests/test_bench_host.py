@@ -83,3 +83,11 @@ def test_more_than_one_gpu_is_refused_before_any_device_work():
                        text=True, timeout=300, cwd=here)
     assert r.returncode != 0
     assert "one GPU only" in (r.stdout + r.stderr)
+
+
+def test_latent_down_combine_bytes():
+    cfg = synth.get("kimik3_latent_decode")          # T=4, k=8, latent 2048 (d_model of the experts), I=2048
+    a = bench.down_algorithmic(cfg, 31, fused=False, combined=True)
+    row = 2048 * 17 // 32                             # one MXFP4 down row over I = 2048: 1088 B
+    assert a["bytes"] == 31 * 2048 * row + 32 * 2048 * 4 + 4 * 2048 * 4   # no shared rows: it is added after P_u
+    assert bench.down_kernel(cfg, False, True) == r"down_combine_mfma_kernel"

@@ -440,7 +440,7 @@ def test_layer_matches_oracle(dev, M, name):
     ref = OL.layer(cfg, inp, ge, gs)
     np.testing.assert_array_equal(to_np(layer.ids), ref.routing.ids)
     np.testing.assert_array_equal(to_np(layer.sp), ref.perm.sorted_pairs)
-    if not layer.fused:          # the fused calls never write y_rows
+    if layer.y_rows is not None:          # the down-combine calls never write y_rows
         assert_close(to_np(layer.y_rows), ref.y_rows, f"{name} y_rows")
     assert_close(to_np(out), ref.out, f"{name} out")
 
@@ -710,7 +710,10 @@ def test_latent_layer_full_size(dev, M):
     ref = OL.layer(cfg, inp, ge, gs)
     np.testing.assert_array_equal(to_np(layer.ids), ref.routing.ids)
     assert_close(to_np(layer.x_lat), ref.x_expert, "latent x_lat")
-    assert_close(to_np(layer.y_rows), ref.y_rows, "latent y_rows")
+    if layer.y_rows is not None:
+        assert_close(to_np(layer.y_rows), ref.y_rows, "latent y_rows")
+    assert_close(to_np(layer.z), ref.z, "latent z (routed sum at the latent width)")
+    assert_close(to_np(layer.y_s), ref.y_shared, "latent shared")
     assert_close(to_np(out), ref.out, "latent out")
 
 
