@@ -10,7 +10,6 @@
 #include <limits.h>
 #include <math.h>
 
-#include <algorithm>
 #include <mutex>
 
 #include "common.h"
@@ -19,94 +18,74 @@
 namespace moe {
 namespace {
 
-constexpr int kRouterTB = 4;      // tokens per workgroup
-constexpr int kRouterUnroll = 4;  // 16-byte loads in flight per lane per row and pass
-constexpr int kRouterRows = 4;    // weight rows per workgroup (at most)
+constexpr int kRouterTB = 8;      // tokens per wave
+constexpr int kRouterUnroll = 4;  // 16-byte loads in flight per lane per pass
 
-// A workgroup computes the dot products of up to kRouterRows consecutive weight rows (expert
-// rows e < E, then the shared-gate row e == E) with up to kRouterTB tokens; wave w covers the
-// w-th quarter of H, so a row is read with four waves' worth of loads in flight.  Lanes stride
-// over the quarter in 8-element (16-byte) vectors.  Per pass a lane loads its token vectors
-// once and the vectors of every row of the group, all before any is used, so x is read once
-// per workgroup instead of once per row; loads are issued unconditionally from clamped
-// indices (a load under a branch would be waited for at the join) and out-of-range vectors
-// are skipped when consumed.  Float64 partial sums are reduced over the wave in a fixed
-// butterfly order, then over the four waves in order: every (row, token) sum is taken in the
-// same order whatever the grouping.
+// A workgroup computes the dot products of one weight row (expert e < E, or the shared
+// gate row e == E) with up to kRouterTB tokens; wave w covers the w-th quarter of H, so a
+// row is read with four waves' worth of loads in flight.  Lanes stride over the quarter in
+// 8-element (16-byte) vectors; loads are issued unconditionally from clamped indices (a
+// load under a branch would be waited for at the join) and out-of-range vectors are
+// skipped when consumed.  Float64 partial sums are reduced over the wave in a fixed
+// butterfly order, then over the four waves in order.
 constexpr int kRouterWaves = 4;
 
 __global__ __launch_bounds__(64 * kRouterWaves) void router_logits_kernel(const uint16_t *__restrict__ x,
                                                                          const uint16_t *__restrict__ wr,
                                                                          const uint16_t *__restrict__ wsg,
-                                                                         int T, int H, int E, int rows, int rpw,
+                                                                         int T, int H, int E, int rows,
                                                                          float *__restrict__ logits) {
-    __shared__ double part[kRouterWaves][kRouterRows][kRouterTB];
-    const int r0 = blockIdx.x * rpw;
-    const int nr = min(rpw, rows - r0);
+    __shared__ double part[kRouterWaves][kRouterTB];
+    const int row = blockIdx.x;
+    const uint16_t *w = row < E ? wr + (size_t)row * H : wsg;
     const int t0 = blockIdx.y * kRouterTB;
     const int nt = min(kRouterTB, T - t0);
     const int lane = lane_id(), wave = wave_id();
-    double acc[kRouterRows][kRouterTB];
+    double acc[kRouterTB];
 #pragma unroll
-    for (int r = 0; r < kRouterRows; ++r)
-#pragma unroll
-        for (int t = 0; t < kRouterTB; ++t) acc[r][t] = 0.0;
+    for (int t = 0; t < kRouterTB; ++t) acc[t] = 0.0;
 
     const int nvec = H >> 3;                                   // H % 32 == 0: quarters are whole
     const int q0 = wave * (nvec / kRouterWaves), q1 = q0 + nvec / kRouterWaves;
     for (int v0 = q0 + lane; v0 < q1 + lane; v0 += kWave * kRouterUnroll) {
-        u32x4 xv[kRouterTB][kRouterUnroll], wv[kRouterRows][kRouterUnroll];
+        u32x4 wv[kRouterUnroll];
+#pragma unroll
+        for (int u = 0; u < kRouterUnroll; ++u)
+            wv[u] = __builtin_nontemporal_load((const u32x4 *)(w) + min(v0 + u * kWave, q1 - 1));
 #pragma unroll
         for (int t = 0; t < kRouterTB; ++t) {
-            const u32x4 *xr = (const u32x4 *)(x + (size_t)(t0 + min(t, nt - 1)) * H);
+            if (t >= nt) break;                      // uniform across the wave
+            const u32x4 *xr = (const u32x4 *)(x + (size_t)(t0 + t) * H);
+            u32x4 xv[kRouterUnroll];
 #pragma unroll
-            for (int u = 0; u < kRouterUnroll; ++u) xv[t][u] = xr[min(v0 + u * kWave, q1 - 1)];
-        }
+            for (int u = 0; u < kRouterUnroll; ++u) xv[u] = xr[min(v0 + u * kWave, q1 - 1)];
+            double s = acc[t];
 #pragma unroll
-        for (int r = 0; r < kRouterRows; ++r) {
-            const int row = r0 + min(r, nr - 1);
-            const uint16_t *w = row < E ? wr + (size_t)row * H : wsg;
+            for (int u = 0; u < kRouterUnroll; ++u) {
+                if (v0 + u * kWave < q1) {
 #pragma unroll
-            for (int u = 0; u < kRouterUnroll; ++u)
-                wv[r][u] = __builtin_nontemporal_load((const u32x4 *)(w) + min(v0 + u * kWave, q1 - 1));
-        }
-#pragma unroll
-        for (int r = 0; r < kRouterRows; ++r) {
-            if (r >= nr) break;                      // uniform across the workgroup
-#pragma unroll
-            for (int t = 0; t < kRouterTB; ++t) {
-                if (t >= nt) break;
-                double s = acc[r][t];
-#pragma unroll
-                for (int u = 0; u < kRouterUnroll; ++u) {
-                    if (v0 + u * kWave < q1) {
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const f32x2 fw = bf16x2_to_f32x2(wv[r][u][q]);
-                            const f32x2 fx = bf16x2_to_f32x2(xv[t][u][q]);
-                            s = fma((double)fw.x, (double)fx.x, s);
-                            s = fma((double)fw.y, (double)fx.y, s);
-                        }
+                    for (int q = 0; q < 4; ++q) {
+                        const f32x2 fw = bf16x2_to_f32x2(wv[u][q]);
+                        const f32x2 fx = bf16x2_to_f32x2(xv[u][q]);
+                        s = fma((double)fw.x, (double)fx.x, s);
+                        s = fma((double)fw.y, (double)fx.y, s);
                     }
                 }
-                acc[r][t] = s;
             }
+            acc[t] = s;
         }
     }
 #pragma unroll
-    for (int r = 0; r < kRouterRows; ++r)
-#pragma unroll
-        for (int t = 0; t < kRouterTB; ++t) {
-            const double s = group_sum_f64(acc[r][t], kWave);
-            if (lane == 0) part[wave][r][t] = s;
-        }
+    for (int t = 0; t < kRouterTB; ++t) {
+        const double s = group_sum_f64(acc[t], kWave);
+        if (lane == 0) part[wave][t] = s;
+    }
     __syncthreads();
-    if (threadIdx.x < nr * nt) {
-        const int r = threadIdx.x / nt, t = threadIdx.x - r * nt;
+    if (threadIdx.x < nt) {
         double s = 0.0;
 #pragma unroll
-        for (int w4 = 0; w4 < kRouterWaves; ++w4) s += part[w4][r][t];
-        logits[(size_t)(t0 + t) * rows + r0 + r] = (float)s;
+        for (int w4 = 0; w4 < kRouterWaves; ++w4) s += part[w4][threadIdx.x];
+        logits[(size_t)(t0 + threadIdx.x) * rows + row] = (float)s;
     }
 }
 
@@ -350,12 +329,9 @@ moe_status enqueue_logits(const moe_route_desc *d, const void *x, const void *w_
         hipLaunchKernelGGL(router_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, partial, n, logits);
         return launch_check("moe_route: router_reduce_kernel");
     }
-    // rows per workgroup: about a workgroup per CU's worth of rows, at most kRouterRows
-    const int rpw = std::max(1, std::min(kRouterRows, rows / 256));
-    dim3 g1((rows + rpw - 1) / rpw, (d->T + kRouterTB - 1) / kRouterTB);
+    dim3 g1(rows, (d->T + kRouterTB - 1) / kRouterTB);
     hipLaunchKernelGGL(router_logits_kernel, g1, dim3(64 * kRouterWaves), 0, s, (const uint16_t *)x,
-                       (const uint16_t *)w_router, (const uint16_t *)w_shared_gate, d->T, d->H, d->E, rows, rpw,
-                       logits);
+                       (const uint16_t *)w_router, (const uint16_t *)w_shared_gate, d->T, d->H, d->E, rows, logits);
     return launch_check("moe_route: router_logits_kernel");
 }
 
