@@ -26,6 +26,10 @@
 namespace moe {
 
 constexpr int kGemvThreads = 256;          // threads per workgroup (per-expert GEMV)
+// ... with wide activation rows (see gemv_launch): 16 waves for bf16 activations, 8 for
+// float32 ones, whose dot products read twice the LDS bytes and hold more registers
+template <int ACT>
+constexpr int gemv_wide_threads() { return ACT == kActF32 ? 512 : 1024; }
 constexpr int kGemvUnroll = 4;             // 16-byte weight loads issued per lane per batch
 constexpr int kGemvTargetWaves = 4096;     // waves a launch aims for (all resident at once)
 
@@ -125,7 +129,7 @@ MOE_DEV float unit_dot(const u32x4 wv, const void *a_unit, int z) {
 // trips rather than one per element.
 constexpr int kStageU = 4;
 
-template <int FMT, int ACT>
+template <int FMT, int ACT, int THREADS>
 MOE_DEV void stage_activations(const GemvParams &p, unsigned char *smem, int row0, int c0, int mc) {
     constexpr int ASZ = ACT == kActF32 ? 4 : 2;
     const int K = p.K;
@@ -145,13 +149,13 @@ MOE_DEV void stage_activations(const GemvParams &p, unsigned char *smem, int row
     if constexpr (ACT == kActMX) {
         const int nb = K / 32;
         const int total = mc * nb;
-        for (int i0 = threadIdx.x; i0 < total; i0 += kGemvThreads * kStageU) {
+        for (int i0 = threadIdx.x; i0 < total; i0 += THREADS * kStageU) {
             u32x4 cv[kStageU];
             uint32_t sb[kStageU];
             int src[kStageU];
 #pragma unroll
             for (int u = 0; u < kStageU; ++u) {
-                const int i = min(i0 + u * kGemvThreads, total - 1);
+                const int i = min(i0 + u * THREADS, total - 1);
                 const int m = i / nb, blk = i - m * nb;
                 src[u] = row_of(m);
                 const int a = max(src[u], 0);
@@ -160,7 +164,7 @@ MOE_DEV void stage_activations(const GemvParams &p, unsigned char *smem, int row
             }
 #pragma unroll
             for (int u = 0; u < kStageU; ++u) {
-                const int i = i0 + u * kGemvThreads;
+                const int i = i0 + u * THREADS;
                 if (i >= total) break;
                 const int m = i / nb, blk = i - m * nb;
                 u32x4 *dst = (u32x4 *)(smem + ((size_t)m * K + (size_t)blk * 32) * 2);
@@ -175,19 +179,19 @@ MOE_DEV void stage_activations(const GemvParams &p, unsigned char *smem, int row
         const int act_vec = K * ASZ / 16;      // 16-byte vectors per activation row
         const int total = mc * act_vec;
         constexpr int P = act_slots<FMT, ACT == kActF32>();
-        for (int i0 = threadIdx.x; i0 < total; i0 += kGemvThreads * kStageU) {
+        for (int i0 = threadIdx.x; i0 < total; i0 += THREADS * kStageU) {
             u32x4 val[kStageU];
             int src[kStageU];
 #pragma unroll
             for (int u = 0; u < kStageU; ++u) {
-                const int i = min(i0 + u * kGemvThreads, total - 1);
+                const int i = min(i0 + u * THREADS, total - 1);
                 const int m = i / act_vec, v = i - m * act_vec;
                 src[u] = row_of(m);
                 val[u] = ((const u32x4 *)((const unsigned char *)p.act + (size_t)max(src[u], 0) * K * ASZ))[v];
             }
 #pragma unroll
             for (int u = 0; u < kStageU; ++u) {
-                const int i = i0 + u * kGemvThreads;
+                const int i = i0 + u * THREADS;
                 if (i >= total) break;
                 const int m = i / act_vec, v = i - m * act_vec;
                 const int b = v / P, sl = v - b * P;
@@ -210,14 +214,14 @@ MOE_DEV void wait_vm_all() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // reads source vector b*P + (q%P ^ z(b)).  Lanes past the row read vector 0 into the padding
 // of the last 1 KiB block (the launch rounds the LDS size up to 1 KiB).  Issued before the
 // expert lookup, so the two memory round trips overlap; wait_vm_all() before LDS is read.
-template <int FMT, int ACT>
+template <int FMT, int ACT, int THREADS>
 MOE_DEV void stage_row_dma(const GemvParams &p, unsigned char *smem) {
     constexpr bool F32 = ACT == kActF32;
     constexpr int P = act_slots<FMT, F32>();
     const int act_vec = p.K * (F32 ? 4 : 2) / 16;
     const int nblk = (act_vec + 63) / 64;
     const int lane = lane_id();
-    for (int c = __builtin_amdgcn_readfirstlane(wave_id()); c < nblk; c += kGemvThreads / 64) {
+    for (int c = __builtin_amdgcn_readfirstlane(wave_id()); c < nblk; c += THREADS / 64) {
         const int q = c * 64 + lane;
         const int b = q / P, sl = q - b * P;
         const int v = q < act_vec ? b * P + (sl ^ act_swizzle<FMT, F32>(b)) : 0;
@@ -314,10 +318,10 @@ MOE_DEV void compute_batch(const GemvParams &p, int n, int n_end, int ib, int nb
     for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
 }
 
-template <int FMT, int ACT, int MAXM, bool PAIR, bool ROUTED>
-__global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvParams p0) {
+template <int FMT, int ACT, int MAXM, bool PAIR, bool ROUTED, int THREADS>
+__global__ __launch_bounds__(THREADS) void gemv_kernel(const GemvParams p0) {
     extern __shared__ __align__(16) unsigned char smem[];
-    constexpr int NW = kGemvThreads / 64;
+    constexpr int NW = THREADS / 64;
 
     // the shared-expert slot reads its own weight set over the identity rows
     const bool shared = ROUTED && p0.shared_slot >= 0 && (int)blockIdx.y == p0.shared_slot;
@@ -334,7 +338,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvParams p0)
         p.residual = nullptr;
     }
     const bool pre = ACT != kActMX && p.n_act_rows == 1;
-    if (pre) stage_row_dma<FMT, ACT>(p, smem);
+    if (pre) stage_row_dma<FMT, ACT, THREADS>(p, smem);
     int e = 0, row0 = 0, M = p.T;
     if (ROUTED && !shared) {
         e = wave_nth_nonempty(p.offsets, p.E, blockIdx.y, &row0, &M);
@@ -392,7 +396,7 @@ __global__ __launch_bounds__(kGemvThreads) void gemv_kernel(const GemvParams p0)
         // the first weight batch is in flight while the activations are staged
         load_batch<FMT>(p, row_of(P), n_end, 0, e, wbase, sbase, j, units, P < passes, wa, sa);
         if (pre && c0 == 0) wait_vm_all();     // the row copied at entry (and the first batch)
-        if (!(pre && mc == 1)) stage_activations<FMT, ACT>(p, smem, row0, c0, mc);
+        if (!(pre && mc == 1)) stage_activations<FMT, ACT, THREADS>(p, smem, row0, c0, mc);
         lds_barrier();
         int Pn = grab(P);                      // the wave's next pass
         int Pnn = passes;
@@ -1143,43 +1147,51 @@ static void pick_layout(int units, bool pair, int *G, int *nl) {
 
 using GemvFn = void (*)(const GemvParams);
 
-template <int FMT, int ACT, bool PAIR>
-static GemvFn pick_kernel_m(int maxm, bool routed) {
-    if (routed) {
+template <int FMT, int ACT, bool PAIR, bool ROUTED>
+static GemvFn pick_kernel_t(int maxm, bool wide) {
+    if (wide) {
         switch (maxm) {
-            case 1: return gemv_kernel<FMT, ACT, 1, PAIR, true>;
-            case 2: return gemv_kernel<FMT, ACT, 2, PAIR, true>;
-            case 4: return gemv_kernel<FMT, ACT, 4, PAIR, true>;
-            default: return gemv_kernel<FMT, ACT, 8, PAIR, true>;
+            case 1:
+            case 2: return gemv_kernel<FMT, ACT, 2, PAIR, ROUTED, gemv_wide_threads<ACT>()>;
+            case 4: return gemv_kernel<FMT, ACT, 4, PAIR, ROUTED, gemv_wide_threads<ACT>()>;
+            default: return gemv_kernel<FMT, ACT, 8, PAIR, ROUTED, gemv_wide_threads<ACT>()>;
         }
     }
     switch (maxm) {
-        case 1: return gemv_kernel<FMT, ACT, 1, PAIR, false>;
-        case 2: return gemv_kernel<FMT, ACT, 2, PAIR, false>;
-        case 4: return gemv_kernel<FMT, ACT, 4, PAIR, false>;
-        default: return gemv_kernel<FMT, ACT, 8, PAIR, false>;
+        case 1: return gemv_kernel<FMT, ACT, 1, PAIR, ROUTED, kGemvThreads>;
+        case 2: return gemv_kernel<FMT, ACT, 2, PAIR, ROUTED, kGemvThreads>;
+        case 4: return gemv_kernel<FMT, ACT, 4, PAIR, ROUTED, kGemvThreads>;
+        default: return gemv_kernel<FMT, ACT, 8, PAIR, ROUTED, kGemvThreads>;
     }
 }
 
-template <int FMT, bool PAIR>
-static GemvFn pick_kernel_a(int act, int maxm, bool routed) {
-    if (act == kActF32) return pick_kernel_m<FMT, kActF32, PAIR>(maxm, routed);
-    if (act == kActMX && FMT == kFmtMXFP4) return pick_kernel_m<kFmtMXFP4, kActMX, PAIR>(maxm, routed);
-    return pick_kernel_m<FMT, kActBF16, PAIR>(maxm, routed);
+template <int FMT, int ACT, bool PAIR>
+static GemvFn pick_kernel_m(int maxm, bool routed, bool wide) {
+    return routed ? pick_kernel_t<FMT, ACT, PAIR, true>(maxm, wide) : pick_kernel_t<FMT, ACT, PAIR, false>(maxm, wide);
 }
 
-static GemvFn pick_kernel(int fmt, int act, bool pair, int maxm, bool routed) {
+template <int FMT, bool PAIR>
+static GemvFn pick_kernel_a(int act, int maxm, bool routed, bool wide) {
+    if (act == kActF32) return pick_kernel_m<FMT, kActF32, PAIR>(maxm, routed, wide);
+    if (act == kActMX && FMT == kFmtMXFP4) return pick_kernel_m<kFmtMXFP4, kActMX, PAIR>(maxm, routed, wide);
+    return pick_kernel_m<FMT, kActBF16, PAIR>(maxm, routed, wide);
+}
+
+static GemvFn pick_kernel(int fmt, int act, bool pair, int maxm, bool routed, bool wide) {
     if (fmt == kFmtMXFP4)
-        return pair ? pick_kernel_a<kFmtMXFP4, true>(act, maxm, routed) : pick_kernel_a<kFmtMXFP4, false>(act, maxm, routed);
+        return pair ? pick_kernel_a<kFmtMXFP4, true>(act, maxm, routed, wide)
+                    : pick_kernel_a<kFmtMXFP4, false>(act, maxm, routed, wide);
     if (fmt == kFmtFP8)
-        return pair ? pick_kernel_a<kFmtFP8, true>(act, maxm, routed) : pick_kernel_a<kFmtFP8, false>(act, maxm, routed);
-    return pick_kernel_a<kFmtBF16, false>(act, maxm, false);
+        return pair ? pick_kernel_a<kFmtFP8, true>(act, maxm, routed, wide)
+                    : pick_kernel_a<kFmtFP8, false>(act, maxm, routed, wide);
+    return pick_kernel_a<kFmtBF16, false>(act, maxm, false, wide);
 }
 
 // LDS for staged activations per workgroup.  Small enough that several workgroups share a
 // CU (occupancy matters more than the token tile: decode experts mostly own one row);
 // experts with more rows than fit loop over token chunks.
 constexpr size_t kGemvLdsBudget = 32 * 1024;
+constexpr size_t kGemvWideLdsBudget = 96 * 1024;
 
 template <int FMT, int ACT, bool PAIR>
 static GemvFn pick_flat_m(int maxm) {
@@ -1272,8 +1284,17 @@ moe_status gemv_launch(int fmt, int act, bool pair, GemvParams p, int slots, int
         set_error("%s: an activation row of %zu bytes does not fit in LDS", what, row_lds);
         return MOE_ERR_UNSUPPORTED;
     }
-    // token chunk: rows per expert that fit, at most the widest register tile (8)
-    int want = max_rows_per_expert < fit ? max_rows_per_expert : fit;
+    // token chunk: rows per expert that fit, at most the widest register tile (8).  When an
+    // expert's rows need more than one chunk of the small budget (wide rows: two bf16 rows of
+    // K = 6144 fill 24 of its 32 KiB), every further chunk streams the expert's weights
+    // again; the wide form then holds up to 8 rows in 96 KiB with one workgroup (of 16 waves,
+    // 8 with float32 rows) per CU, so each expert of up to 8 rows streams once.
+    const int rows_needed = max_rows_per_expert < 1 ? 1 : (max_rows_per_expert > 8 ? 8 : max_rows_per_expert);
+    const int fit_wide = (int)(kGemvWideLdsBudget / row_lds);
+    const bool wide = rows_needed > fit && fit_wide > fit;
+    const int threads = !wide ? kGemvThreads
+                              : (act_f32 ? gemv_wide_threads<kActF32>() : gemv_wide_threads<kActBF16>());
+    int want = rows_needed < (wide ? fit_wide : fit) ? rows_needed : (wide ? fit_wide : fit);
     want = want < 1 ? 1 : (want > 8 ? 8 : want);
     int maxm = 1;
     while (maxm < want) maxm *= 2;
@@ -1281,19 +1302,20 @@ moe_status gemv_launch(int fmt, int act, bool pair, GemvParams p, int slots, int
     const int rows_per_pass = pair ? 32 / p.G : 64 / p.G;
     // aim for at most kGemvTargetWaves waves over the whole launch (rounding the rows
     // per workgroup up: a workgroup more than the target puts a fifth one on some CUs, whose
-    // workgroups then finish last), at least one pass per wave
+    // workgroups then finish last), at least one pass per wave; the wide form (one workgroup
+    // per CU at a time) aims for 8 workgroups per CU over the launch, so the rounds balance
     const int n_grid = p.shared_slot >= 0 ? max(p.N, p.sN) : p.N;
     const long long rows_total = (long long)n_grid * slots;
-    const int target_wgs = kGemvTargetWaves / (kGemvThreads / 64);
+    const int target_wgs = wide ? 8 * device_cu_count() : kGemvTargetWaves / (kGemvThreads / 64);
     int rpw = (int)((rows_total + target_wgs - 1) / target_wgs);
-    const int min_rpw = rows_per_pass * (kGemvThreads / 64);
+    const int min_rpw = rows_per_pass * (threads / 64);
     if (rpw < min_rpw) rpw = min_rpw;
     rpw = (rpw + rows_per_pass - 1) / rows_per_pass * rows_per_pass;
     p.rows_per_wg = rpw;
     dim3 grid((n_grid + rpw - 1) / rpw, slots);
     const size_t lds = align_up((size_t)p.chunk * row_lds, 1024);   // whole 1 KiB blocks: stage_row_dma
-    GemvFn fn = pick_kernel(fmt, act, pair, maxm, p.offsets != nullptr);
-    hipLaunchKernelGGL(fn, grid, dim3(kGemvThreads), lds, stream, p);
+    GemvFn fn = pick_kernel(fmt, act, pair, maxm, p.offsets != nullptr, wide);
+    hipLaunchKernelGGL(fn, grid, dim3(threads), lds, stream, p);
     return launch_check(what);
 }
 

@@ -380,6 +380,10 @@ LAYER_CASES = {
     # an odd number of 32-value blocks per down row (the down-combine reads the two scale bytes
     # of a lane one by one)
     "tiny_fused_odd_blocks": tiny(name="tfo", wtag=101, T=2, k=2, I=96, shared="ungated", shared_K=256, shared_I=96),
+    # FP8 with 40 tokens and 6 KB activation rows: the per-slot GEMV's wide form (8 rows of a
+    # chunk in LDS, 512-thread workgroups), two chunks per routed expert, five for the shared
+    "fp8_wide_chunks": tiny(name="fw", wtag=102, wfmt="fp8b128", score="sigmoid", select_bias_std=0.01, T=40,
+                            H=3072, I=512, E=16, k=4, shared="ungated", shared_K=3072, shared_I=256),
     # prefill sizes on the bf16 matrix-core GEMM: the shared expert in the identity form, and
     # the latent form (float32 x_lat split into two bf16 terms)
     "prefill_gated_shared": tiny(name="pgs", wtag=97, T=160, H=512, I=160, E=8, k=2, shared="gated",
