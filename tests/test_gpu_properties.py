@@ -11,8 +11,8 @@
   * an expert that no token selects changes nothing: overwriting its weights leaves the
     output bit for bit the same, while overwriting a selected expert changes it.
 
-The cases cover the fused decode calls, the decode GEMV over FP8 weights, the bf16
-matrix-core prefill and the FP4 matrix-core prefill.
+The cases cover the fused decode calls, the decode GEMV over FP8 weights, the per-slot
+GEMV in its wide form, the bf16 matrix-core prefill and the FP4 matrix-core prefill.
 """
 from __future__ import annotations
 
@@ -54,6 +54,10 @@ CASES = {
     # decode GEMV over FP8 weights with sigmoid scoring, staged calls
     "decode_fp8": (tiny(name="pf", wtag=111, wfmt="fp8b128", score="sigmoid", select_bias_std=0.01, I=256, T=7, k=3,
                         E=24, shared="ungated", shared_K=256, shared_I=128), 1),
+    # per-slot GEMV over FP8 weights in its wide form (8 token rows of 6 KB per chunk, two
+    # chunks for experts with more rows), staged calls
+    "mid_fp8_wide": (tiny(name="pw", wtag=114, wfmt="fp8b128", score="sigmoid", select_bias_std=0.01, T=40, H=3072,
+                          I=512, E=64, k=4, shared="ungated", shared_K=3072, shared_I=256), 20),
     # bf16 matrix-core grouped GEMM (float activations)
     "prefill_float": (tiny(name="pp", wtag=112, T=192, H=512, I=160, E=256, k=2, shared="gated", shared_K=512,
                            shared_I=192), 64),
