@@ -238,7 +238,7 @@ moe_status moe_expert_down(const moe_expert_weights *w, int32_t act, int32_t T, 
  * shared: one-expert set of the same format and d_model (and, for the down product, d_ff)
  * or NULL.  h and h_shared 16-byte aligned.  A workgroup holds the slots' h rows and a
  * table of 128 partial sums per slot in LDS: with S = k (+1 with a shared expert),
- * S * (4 * roundup(d_ff, 256) + 512) bytes must be <= 150 KiB, else
+ * S * (4 * roundup(d_ff, 512) + 512) bytes must be <= 150 KiB, else
  * MOE_ERR_UNSUPPORTED.  No workspace.
  */
 moe_status moe_expert_gateup_shared(const moe_expert_weights *w, const moe_expert_weights *shared,

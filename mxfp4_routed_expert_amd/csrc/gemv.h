@@ -73,13 +73,13 @@ struct DownCombineParams {
 moe_status down_combine_launch(int fmt, DownCombineParams p, hipStream_t stream);
 size_t down_combine_lds(int k, bool shared, int I);
 // Down-combine launch shape: 512 threads; at most kDcMaxRows output rows per workgroup.
-// A slot's h occupies 4 * dc_plane_ld(I) bytes of LDS (a multiple of 1 KiB): the float32 row,
-// or bf16 hi + lo planes of dc_plane_ld(I) values.
+// A slot's h occupies 4 * dc_plane_ld(I) bytes of LDS (a multiple of 2 KiB): the float32 row,
+// or bf16 hi + lo planes of dc_plane_ld(I) values (whole steps of 512 of the matrix-core form).
 constexpr int kDcThreads = 512;
 constexpr int kDcMaxRows = 128;
 // The matrix-core (MXFP4) form keeps two partial sums per (slot, row): at most 64 rows.
 constexpr int kDmMaxRows = kDcMaxRows / 2;
-__host__ __device__ constexpr int dc_plane_ld(int I) { return (I + 255) / 256 * 256; }
+__host__ __device__ constexpr int dc_plane_ld(int I) { return (I + 511) / 512 * 512; }
 void down_combine_mfma_launch(const DownCombineParams &p, dim3 grid, size_t lds, hipStream_t stream);
 
 // Enqueue one GEMV launch.  `slots` is the number of expert slots in the grid (experts

@@ -1097,7 +1097,7 @@ static int down_combine_batch(int nl) {
 moe_status down_combine_launch(int fmt, DownCombineParams p, hipStream_t stream) {
     const bool mfma = fmt == kFmtMXFP4;
     const int units = fmt == kFmtMXFP4 ? p.I / 32 : p.I / 16;
-    int U = 1, rpp = 4;                                    // MFMA path: 16-row tiles, the last one clamped
+    int U = 1, rpp = 4;                                    // MFMA path: 8-row tiles, the last one clamped
 
     if (!mfma) {
         // 16 lanes per row segment while a lane still gets >= 4 units; short rows use the

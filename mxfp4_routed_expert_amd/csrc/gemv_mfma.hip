@@ -5,21 +5,27 @@ namespace moe {
 
 // ------------------------------------------------------------------ down + combine
 // The decode down product with the weighted combine (as down_combine_kernel in gemv.hip),
-// MXFP4 weights, multiply-adds on v_mfma_f32_16x16x32_bf16.  A step covers one 128-byte
-// line of each of 16 weight rows (8 units, 256 values) as two K-steps of 128: lane l loads
-// the adjacent units 8m + 2(l/16) and 8m + 2(l/16) + 1 of row l%16 (with an even number of
-// units per row, both scale bytes in one 16-bit load) and converts each to its A slices for
-// four MFMAs.  B holds the slot's h as two bf16 columns, hi = RN_bf16(h) and
-// lo = RN_bf16(h - hi) (together within 2^-17 |h|), the other 14 columns zero, so
-// C[row][0] + C[row][1] is the row's dot product.  The vector ALU only converts codes (one
-// instruction per two weights) and advances pointers: the float32 multiply-adds of the
-// vector kernel cost as much issue time as the HBM stream.
+// MXFP4 weights, multiply-adds on v_mfma_f32_16x16x32_bf16.
 //
-// Work items are (tile of 16 rows, slot j, K part kp): the item's rows of slot j over its
+// The instruction's A operand puts row i of the tile in lanes i, 16 + i, 32 + i, 48 + i, so
+// four neighbouring lanes hold four different rows; loaded in that layout, every group of
+// four lanes reads from four weight rows, and the L1 handles each lane's 16 bytes as an
+// access of its own.  Here four neighbouring lanes read four consecutive 16-byte units of
+// one row instead: A row i = 4a + b is weight row a over part b, where part b of a step is
+// the units 16m + 4g + b read by lane group g (g = 0..3).  B holds the slot's h in eight
+// columns, column 2b + p being plane p (hi = RN_bf16(h), lo = RN_bf16(h - hi), together
+// within 2^-17 |h|) at the units of part b; the other eight columns are zero.  Then
+// C[4a + b][2b + p] is row a's dot product over part b with plane p, and the row's dot
+// product is the sum of those eight entries.  A step covers 16 units (512 values) of 8 rows
+// as two such tiles of 4 rows on one B: each load instruction reads 256 contiguous bytes of
+// each of 4 rows, and each group of four lanes 64 of them.  The vector ALU only converts
+// codes (one instruction per two weights) and advances pointers.
+//
+// Work items are (tile of 8 rows, slot j, K part kp): the item's rows of slot j over its
 // part of the steps (two parts when an item has at least 2 * kDmDepth steps, else one).
 // Waves take items from an LDS counter, so a wave that is served late takes fewer of them.
-// Item (tile, j, kp) writes its 16 partial dot products to part[kp][j][rows] of an LDS
-// table whatever wave ran it; after a barrier every row's output is the slot-ordered sum of
+// Item (tile, j, kp) writes its 8 dot products to part[kp][j][rows] of an LDS table
+// whatever wave ran it; after a barrier every row's output is the slot-ordered sum of
 // w_j * (part[0] + part[1]), so the result does not depend on which wave ran what.  Each
 // wave keeps kDmDepth steps of loads in flight across item boundaries; every slot of that
 // ring records the position its loads belong to.
@@ -34,14 +40,13 @@ namespace moe {
 // waves already past it would issue nothing meanwhile.)
 constexpr int kDmDepth = 4;              // steps of loads in flight per wave
 constexpr int kDmThreads = 1024;         // 16 waves, four per SIMD
+constexpr int kDmTile = 8;               // weight rows per item (two A tiles of 4 rows)
 constexpr int kDmMaxGroups = 4800;       // 8-value groups of h: slots * dc_plane_ld(I) / 8 within 150 KiB
 static_assert(2 * kDmMaxRows <= kDcMaxRows, "two partial sums per row must fit the table");
+static_assert(dc_plane_ld(1) % 512 == 0, "a plane must hold whole steps of 16 units");
 
 __device__ __align__(16) uint8_t g_dm_zero[16];   // read-only zeros (loads of a wave with no item left)
 
-// PS: the scale bytes of a lane's two units are read as one 16-bit word (units per row even,
-// scale array 2-byte aligned); otherwise as two bytes.
-template <bool PS>
 __global__ __launch_bounds__(kDmThreads) void down_combine_mfma_kernel(const DownCombineParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_e[MOE_MAX_TOPK + 1], s_r[MOE_MAX_TOPK + 1];
@@ -81,25 +86,26 @@ __global__ __launch_bounds__(kDmThreads) void down_combine_mfma_kernel(const Dow
     const uint8_t *w_r = p.w, *w_s = p.sw;
     const uint8_t *s_rt = (const uint8_t *)p.s, *s_s = (const uint8_t *)p.ss;
     const int units = I / 32;
-    const int nm = (units + 7) / 8;                        // steps per (tile, slot)
-    const int ld = dc_plane_ld(p.I);                       // bf16 values per plane (>= 256 * nm)
+    const int nm = (units + 15) / 16;                      // steps per (tile, slot)
+    const int ld = dc_plane_ld(p.I);                       // bf16 values per plane (>= 512 * nm)
     const int n_begin = blockIdx.x * p.rows_per_wg;
     const int n_end = min(p.N, n_begin + p.rows_per_wg);
     if (n_begin >= n_end) return;                          // the whole workgroup
-    const int ntile = (n_end - n_begin + 15) / 16;
+    const int ntile = (n_end - n_begin + kDmTile - 1) / kDmTile;
     const int KS = nm >= 2 * kDmDepth ? 2 : 1;             // K parts per (tile, slot)
     const int per_tile = nslot * KS;
     const int nitems = ntile * per_tile;
-    const int r16 = lane & 15, g = lane >> 4;
+    const int i16 = lane & 15, g = lane >> 4;
+    const int ra = i16 >> 2, pb = i16 & 3;                 // A: row ra (+ 4) of the tile, part pb
     uint16_t *planes = (uint16_t *)smem;                   // slot j: hi plane 2j, lo plane 2j+1
     float *part = (float *)(smem + p.h_lds_bytes);          // [2][nslot][rows_per_wg]
     const uint32_t row_bytes = (uint32_t)I / 2;
 
     // load cursor: item `it` (nitems: none left), step m of [m, m_end); matrix bases of the
-    // item (wave-uniform) and this lane's row offsets
+    // item (wave-uniform) and this lane's offsets of its two rows
     int it = min(wave, nitems), m = 0, m_end = 0, cj = 0, ctile = 0, ckp = 0;
     const uint8_t *cwb = g_dm_zero, *csb = g_dm_zero;
-    uint32_t cwo = 0, cso = 0;
+    uint32_t cwo0 = 0, cwo1 = 0, cso0 = 0, cso1 = 0;
     auto setup = [&]() __attribute__((always_inline)) {     // (branch-free: a wave with no item left reads zeros)
         const bool has = it < nitems;
         const int itc = has ? it : 0;
@@ -118,9 +124,13 @@ __global__ __launch_bounds__(kDmThreads) void down_combine_mfma_kernel(const Dow
         const uint8_t *sbase = sh ? (const uint8_t *)s_s : (const uint8_t *)s_rt;
         cwb = has ? wbase + first_row * row_bytes : g_dm_zero;
         csb = has ? sbase + first_row * units : g_dm_zero;
-        const uint32_t n = (uint32_t)min(n_begin + ctile * 16 + r16, n_end - 1);
-        cwo = has ? n * row_bytes : 0u;
-        cso = has ? n * (uint32_t)units : 0u;
+        // rows past the range repeat its last row (their results are not stored)
+        const uint32_t n0 = (uint32_t)min(n_begin + ctile * kDmTile + ra, n_end - 1);
+        const uint32_t n1 = (uint32_t)min(n_begin + ctile * kDmTile + 4 + ra, n_end - 1);
+        cwo0 = has ? n0 * row_bytes : 0u;
+        cwo1 = has ? n1 * row_bytes : 0u;
+        cso0 = has ? n0 * (uint32_t)units : 0u;
+        cso1 = has ? n1 * (uint32_t)units : 0u;
     };
     auto grab = [&]() __attribute__((always_inline)) {
         int v = 0;
@@ -129,28 +139,21 @@ __global__ __launch_bounds__(kDmThreads) void down_combine_mfma_kernel(const Dow
     };
     // Loads are issued unconditionally (a load under a branch leaves the compiler unable
     // to count the loads in flight, and it then waits for all of them); a wave with no item
-    // left reads a 16-byte block of zeros that stays in cache.
-    auto load = [&](u32x4 (&w)[2], uint16_t &sc) __attribute__((always_inline)) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint32_t u = (uint32_t)min(8 * m + 2 * g + h, units - 1);
-            w[h] = *(const u32x4 *)(cwb + (it < nitems ? cwo + u * 16 : 0u));
-        }
-        if constexpr (PS) {
-            // bytes of units base, base + 1; base = 8m + 2g whenever that unit is in the row
-            const uint32_t base = (uint32_t)min(8 * m + 2 * g, units - 2);
-            sc = *(const uint16_t *)(csb + (it < nitems ? cso + base : 0u));
-        } else {
-            const uint32_t u0 = (uint32_t)min(8 * m + 2 * g, units - 1), u1 = (uint32_t)min(8 * m + 2 * g + 1, units - 1);
-            const bool lv = it < nitems;
-            sc = (uint16_t)(csb[lv ? cso + u0 : 0u] | (csb[lv ? cso + u1 : 0u] << 8));
-        }
+    // left reads a 16-byte block of zeros that stays in cache.  Units past the row repeat
+    // its last unit (their scale is taken as 0 when converted).
+    auto load = [&](u32x4 (&w)[2], uint8_t (&sc)[2]) __attribute__((always_inline)) {
+        const bool lv = it < nitems;
+        const uint32_t u = (uint32_t)min(16 * m + 4 * g + pb, units - 1);
+        w[0] = *(const u32x4 *)(cwb + (lv ? cwo0 + u * 16 : 0u));
+        w[1] = *(const u32x4 *)(cwb + (lv ? cwo1 + u * 16 : 0u));
+        sc[0] = csb[lv ? cso0 + u : 0u];
+        sc[1] = csb[lv ? cso1 + u : 0u];
     };
     // ring slot d: the position its loads belong to
     int pj[kDmDepth], ptile[kDmDepth], pkp[kDmDepth], pm[kDmDepth];
     bool plive[kDmDepth], plast[kDmDepth];
     int live_slots = 0;
-    auto fill = [&](auto dc, u32x4 (&w)[2], uint16_t &sc) __attribute__((always_inline)) {
+    auto fill = [&](auto dc, u32x4 (&w)[2], uint8_t (&sc)[2]) __attribute__((always_inline)) {
         constexpr int d = decltype(dc)::value;
         const bool lv = it < nitems;
         pj[d] = cj;
@@ -167,37 +170,45 @@ __global__ __launch_bounds__(kDmThreads) void down_combine_mfma_kernel(const Dow
         }
     };
 
-    f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-    u32x4 bq[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};   // zero outside columns 0, 1
-    // Step of ring slot d into acc (units past the row get scale 0, so A is zero there, and B
-    // is zero past d_ff); the item's last step adds the hi and lo columns and stores the
-    // tile's 16 partial dot products (0 for a dropped pair).
-    auto compute = [&](auto dc, const u32x4 (&w)[2], const uint16_t sc) __attribute__((always_inline)) {
+    f32x4 acc[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
+    u32x4 bq[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};   // zero outside columns 0..7
+    // Step of ring slot d into acc (units past the row get scale 0, so A is zero there, and
+    // the planes are zero past d_ff); the item's last step sums each row's eight entries and
+    // stores the tile's 8 dot products (0 for a dropped pair).
+    auto compute = [&](auto dc, const u32x4 (&w)[2], const uint8_t (&sc)[2]) __attribute__((always_inline)) {
         constexpr int d = decltype(dc)::value;
         const int j = pj[d];
+        // B lane (column i16 < 8, group g): plane i16 & 1 of slot j at unit 16m + 4g + i16 / 2
+        const uint16_t *bp = planes + (size_t)(2 * j + (i16 & 1)) * ld + (16 * pm[d] + 4 * g + (i16 >> 1)) * 32;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            if (i16 < 8) bq[q] = *(const u32x4 *)(bp + 8 * q);
+        const bool uin = 16 * pm[d] + 4 * g + pb < units;
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            const int u = 8 * pm[d] + 2 * g + h;
             bf16x8 a[4];
-            unit_to_bf16x8(w[h], u < units ? e8m0_to_f32(((uint32_t)sc >> (8 * h)) & 0xffu) : 0.0f, a);
-            const uint16_t *bp = planes + (size_t)(2 * j + (r16 & 1)) * ld + u * 32;
+            unit_to_bf16x8(w[h], uin ? e8m0_to_f32(sc[h]) : 0.0f, a);
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (r16 < 2) bq[q] = *(const u32x4 *)(bp + 8 * q);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q], __builtin_bit_cast(bf16x8, bq[q]), acc, 0, 0, 0);
-            }
+            for (int q = 0; q < 4; ++q)
+                acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[q], __builtin_bit_cast(bf16x8, bq[q]), acc[h], 0, 0, 0);
         }
         if (!plast[d]) return;
         const bool drop = __builtin_amdgcn_readfirstlane(s_e[j]) < 0;
         float *pp = part + (size_t)(pkp[d] * nslot + j) * rpw;
-        // lane (col r16, group g) holds C[4g+v][r16]; column 1 moves down one lane
-        const int l0 = ptile[d] * 16 + 4 * g;
+        // lane (column c = i16, group G = g) holds C[4G + v][c]: row G of the A tile over part
+        // v; the entries of row G are those with c < 8, v = c / 2
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            float o = acc[v] + __shfl_down(acc[v], 1, kWave);
-            if (drop) o = 0.0f;
-            if (r16 == 0 && n_begin + l0 + v < n_end) pp[l0 + v] = o;
-            acc[v] = 0.0f;
+        for (int h = 0; h < 2; ++h) {
+            const int v = i16 >> 1;
+            float x = v == 0 ? acc[h][0] : v == 1 ? acc[h][1] : v == 2 ? acc[h][2] : acc[h][3];
+            x = i16 < 8 ? x : 0.0f;
+            x += __shfl_xor(x, 1, kWave);
+            x += __shfl_xor(x, 2, kWave);
+            x += __shfl_xor(x, 4, kWave);
+            if (drop) x = 0.0f;
+            const int lr = ptile[d] * kDmTile + 4 * h + g;
+            if (i16 == 0 && n_begin + lr < n_end) pp[lr] = x;
+            acc[h] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
         }
     };
 
@@ -223,7 +234,7 @@ __global__ __launch_bounds__(kDmThreads) void down_combine_mfma_kernel(const Dow
         vb[u] = src[1];
     }
     u32x4 wv[kDmDepth][2];
-    uint16_t sv[kDmDepth];    // (16 bits: a widened copy would be masked at the loop latch, forcing a wait)
+    uint8_t sv[kDmDepth][2];  // (the loaded bytes as they are: a value combined from two loads waits for both)
     setup();
     static_assert(kDmDepth == 4, "the prologue issues two steps before the planes and two after");
     fill(std::integral_constant<int, 0>{}, wv[0], sv[0]);
@@ -289,9 +300,7 @@ __global__ __launch_bounds__(kDmThreads) void down_combine_mfma_kernel(const Dow
 }
 
 void down_combine_mfma_launch(const DownCombineParams &p, dim3 grid, size_t lds, hipStream_t stream) {
-    const bool ps = (p.I / 32) % 2 == 0 && (((uintptr_t)p.s | (uintptr_t)p.ss) & 1) == 0;
-    if (ps) hipLaunchKernelGGL(down_combine_mfma_kernel<true>, grid, dim3(kDmThreads), lds, stream, p);
-    else hipLaunchKernelGGL(down_combine_mfma_kernel<false>, grid, dim3(kDmThreads), lds, stream, p);
+    hipLaunchKernelGGL(down_combine_mfma_kernel, grid, dim3(kDmThreads), lds, stream, p);
 }
 
 }  // namespace moe

@@ -50,13 +50,13 @@ class LayerWeights:
 
 
 # LDS a down-combine workgroup may hold: per slot (k, +1 with a shared expert) the h row
-# in 4 * roundup(d_ff, 256) bytes and a table of 128 floats (the library's own rule)
+# in 4 * roundup(d_ff, 512) bytes and a table of 128 floats (the library's own rule)
 FUSED_LDS_LIMIT = 150 * 1024
 
 
 def down_combine_lds(k: int, shared: bool, d_ff: int) -> int:
     s = k + (1 if shared else 0)
-    return s * 4 * ((d_ff + 255) // 256 * 256) + s * 128 * 4
+    return s * 4 * ((d_ff + 511) // 512 * 512) + s * 128 * 4
 
 
 def fuses(w: LayerWeights, T: int) -> bool:
