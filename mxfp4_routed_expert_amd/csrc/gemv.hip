@@ -444,14 +444,16 @@ constexpr int kFlatMaxTok = 8;            // activation rows staged: all of the 
 constexpr int kFlatMaxSlots = 256;        // routed rows (<= kFlatMaxSlots - 1) plus the shared slot
 constexpr size_t kFlatLdsBudget = 96 * 1024;
 
+// (by waves first_wave .. the last; the caller's wave is one of them)
 template <int FMT, int ACT>
-MOE_DEV void stage_rows_dma(const GemvParams &p, unsigned char *smem, int rs) {
+MOE_DEV void stage_rows_dma(const GemvParams &p, unsigned char *smem, int rs, int first_wave) {
     constexpr bool F32 = ACT == kActF32;
     constexpr int P = act_slots<FMT, F32>();
     const int act_vec = p.K * (F32 ? 4 : 2) / 16;
     const int nblk = (act_vec + 63) / 64;
     const int lane = lane_id();
-    for (int c = __builtin_amdgcn_readfirstlane(wave_id()); c < p.n_act_rows * nblk; c += kFlatThreads / 64) {
+    for (int c = __builtin_amdgcn_readfirstlane(wave_id()) - first_wave; c < p.n_act_rows * nblk;
+         c += kFlatThreads / 64 - first_wave) {
         const int m = c / nblk, cb = c - m * nblk;
         const int q = cb * 64 + lane;
         const int b = q / P, sl = q - b * P;
@@ -515,17 +517,37 @@ MOE_DEV FlatPass flat_resolve(int P, int end, int ns, int pN, int sN, int rpp, i
 
 constexpr int kFlatTopkNK = 8;             // routing in the prologue: E <= 64 * kFlatTopkNK
 
+// Wait (bounded, sleeping) until an LDS counter reaches v.  Read through an LDS pointer: a
+// generic volatile read is a flat load, and its wait would also wait for every global load
+// in flight.  The bound only keeps a fault elsewhere from turning into a hang.
+MOE_DEV void lds_wait_at_least(int *ctr, int v) {
+    volatile __attribute__((address_space(3))) int *c = (volatile __attribute__((address_space(3))) int *)ctr;
+    for (int spin = 0; spin < (1 << 22); ++spin) {
+        if (__builtin_amdgcn_readfirstlane(*c) >= v) break;
+        __builtin_amdgcn_s_sleep(1);
+    }
+    asm volatile("" ::: "memory");                         // no LDS read moves above the wait
+}
+
 // ROUTE: the routing-in-the-prologue form (p.route): wave t < T selects token t's experts
-// (topk_select, the route kernel's selection), and wave 0 builds the slot table and the rows'
-// tokens from the selections in the permutation's order (expert, then pair); workgroup 0 also
-// writes the routing results and the permutation.
+// (topk_select, the route kernel's selection), and wave 0 builds the slot table of the routed
+// experts and the rows' tokens from the selections in the permutation's order (expert, then
+// pair); workgroup 0 also writes the routing results and the permutation.  The shared expert
+// does not depend on the routing: the other waves copy the activation rows and take the
+// workgroup's share of the shared expert's passes (an equal contiguous range of them) while
+// the routing runs, and every wave takes routed passes once wave 0 has published the table.
+// Waves hand over through LDS counters, not workgroup barriers, so none holds the others
+// back.
 template <int FMT, int ACT, int MAXM, bool PAIR, bool ROUTE = false>
 __global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParams p) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_sid[ROUTE ? 64 : 1];
     __shared__ int s_e[kFlatMaxSlots], s_r0[kFlatMaxSlots], s_m[kFlatMaxSlots], s_pass0[kFlatMaxSlots + 1];
     __shared__ int s_tok[kFlatMaxSlots];
-    __shared__ int s_ns, s_beg, s_end, s_next;
+    __shared__ int s_ns, s_beg, s_end, s_next, s_perm;
+    // ROUTE: the shared slot as a one-entry table, its pass counter and the hand-off counters
+    __shared__ int s_she[1], s_shr0[1], s_shm[1], s_shpass0[2];
+    __shared__ int s_shnext, s_dma, s_topk, s_tab;
     constexpr int NW = kFlatThreads / 64;
     constexpr bool F32 = ACT == kActF32;
     constexpr int ASZ = F32 ? 4 : 2;
@@ -547,9 +569,31 @@ __global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParam
     const int rs = (K * ASZ + 1023) / 1024 * 1024;         // LDS bytes per staged row
     const int rpp = PAIR ? 32 / G : 64 / G;
     const int units = units_per_row<FMT>(K);
-    stage_rows_dma<FMT, ACT>(p, smem, rs);
     const RouteArgs ra = p.route;
+    const int T0 = ROUTE ? T : 0;                          // waves that route (and copy no rows)
+    int sh_end = 0;
     if constexpr (ROUTE) {
+        // the shared slot's passes (rows 0 .. T-1) and this workgroup's equal share of them
+        const long long S = has_sh ? (long long)((T + MAXM - 1) / MAXM) * ((sN + rpp - 1) / rpp) : 0;
+        const long long b = blockIdx.x, nb = gridDim.x;
+        sh_end = (int)((b + 1) * S / nb);
+        if (threadIdx.x == 0) {
+            s_she[0] = -1;
+            s_shr0[0] = 0;
+            s_shm[0] = T;
+            s_shpass0[0] = 0;
+            s_shpass0[1] = (int)S;
+            s_shnext = (int)(b * S / nb);
+            s_dma = s_topk = s_tab = s_perm = 0;
+        }
+        __syncthreads();
+    }
+    if (wave >= T0) stage_rows_dma<FMT, ACT>(p, smem, rs, T0);
+    if constexpr (ROUTE) {
+        if (wave >= T) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's row copies are in LDS
+            if (lane == 0) atomicAdd(&s_dma, 1);
+        }
         if (wave < T) {
             double *gk = (double *)(smem + (size_t)n_act * rs) + (size_t)wave * E;   // group-limited keys
             const TopkLane r = topk_select<kFlatTopkNK>(ra.logits + (size_t)wave * ra.rows, E, kk, ra.score, ra.renorm,
@@ -563,8 +607,9 @@ __global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParam
                 }
             }
             if (blockIdx.x == 0 && ra.has_sg && lane == 0) ra.sg[wave] = r.sg;
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // s_sid holds this token's experts
+            if (lane == 0) atomicAdd(&s_topk, 1);
         }
-        lds_barrier();                                   // (the row copies may still be in flight)
     }
 
     if (wave == 0) {
@@ -572,21 +617,24 @@ __global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParam
         // expert (e = -1) over the identity rows
         int ns = 0;
         if constexpr (ROUTE) {
+            lds_wait_at_least(&s_topk, T);
             // pair q = (token q / k, slot q % k) -> row = pairs of lower experts + earlier pairs
             // of its expert; the first pair of an expert opens its slot
+            // (pair q's expert read from lane q's register: a loop of LDS reads waits out each
+            // read's latency in turn)
             const int P = T * kk;
             const int e = lane < P ? s_sid[lane] : -1;
             int row = 0, cnt = 0;
             bool first = e >= 0;
             for (int q = 0; q < P; ++q) {
-                const int eq = s_sid[q];
+                const int eq = __builtin_amdgcn_readlane(e, q);
                 row += (eq >= 0 && (eq < e || (eq == e && q < lane))) ? 1 : 0;
                 cnt += eq == e ? 1 : 0;
                 first = first && !(eq == e && q < lane);
             }
             const uint64_t fm = __ballot(first);
             int slot = 0;
-            for (int q = 0; q < P; ++q) slot += (((fm >> q) & 1ull) && s_sid[q] < e) ? 1 : 0;
+            for (int q = 0; q < P; ++q) slot += (((fm >> q) & 1ull) && __builtin_amdgcn_readlane(e, q) < e) ? 1 : 0;
             if (e >= 0) s_tok[row] = lane / kk;
             if (first) {
                 s_e[slot] = e;
@@ -594,7 +642,6 @@ __global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParam
                 s_m[slot] = cnt;
             }
             ns = __popcll(fm);
-            if (blockIdx.x == 0) small_permutation(s_sid, P, E, ra.offsets, ra.sorted, ra.p2r, lane, 64);
         } else if (routed) {
             int o[kMaxOffsetChunks];
 #pragma unroll
@@ -625,7 +672,7 @@ __global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParam
             }
             ns = 1;
         }
-        if (has_sh) {
+        if (!ROUTE && has_sh) {
             if (lane == 0) {
                 s_e[ns] = -1;
                 s_r0[ns] = 0;
@@ -658,7 +705,11 @@ __global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParam
             const int beg = (int)(b * base / nb), end = (int)((b + 1) * base / nb);
             s_beg = beg;
             s_end = end;
-            s_next = beg + NW;
+            s_next = ROUTE ? beg : beg + NW;
+        }
+        if constexpr (ROUTE) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the table is in LDS
+            if (lane == 0) atomicAdd(&s_tab, 1);
         }
     } else if (!ROUTE && wave == 1) {
         // activation row of each routed row (or identity row): -1 when out of range
@@ -672,9 +723,8 @@ __global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParam
             s_tok[r] = (a >= 0 && a < n_act) ? a : -1;
         }
     }
-    asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if constexpr (!ROUTE) asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
 
-    const int ns = s_ns, beg = s_beg, end = s_end;
     const int grp = PAIR ? (lane & 31) / G : lane / G;
     const int j = lane & (G - 1);
     const int mat = PAIR ? (lane >> 5) : 0;
@@ -684,12 +734,6 @@ __global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParam
     const void *s_s = has_sh ? (PAIR && mat ? p.ss[1] : p.ss[0]) : s_rt;
     const int nb = (nl + U - 1) / U;    // batches per pass
 
-    // pass P -> its slot; the passes a wave takes only increase, so the slot cursor moves forward
-    int cursor = 0;
-    auto resolve = [&](int P) __attribute__((always_inline)) {
-        return flat_resolve<FMT, MAXM>(P, end, ns, pN, sN, rpp, grp, w_r, s_rt, w_s, s_s, cursor, s_e, s_r0, s_m,
-                                       s_pass0);
-    };
     // loads of batch ib of a pass (row ridx of the stack wb / sb), from clamped valid addresses
     auto load = [&](const uint8_t *wb, const void *sb, size_t ridx, size_t srow, int ib, u32x4 (&w)[U],
                     uint32_t (&sc)[NSC]) __attribute__((always_inline)) {
@@ -781,46 +825,82 @@ __global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParam
 #pragma unroll
         for (int m = 0; m < MAXM; ++m) acc[m] = 0.0f;
     };
-    auto grab = [&]() __attribute__((always_inline)) {
-        int g = 0;
-        if (lane == 0) g = atomicAdd(&s_next, 1);
-        return min(__builtin_amdgcn_readfirstlane(g), end);
-    };
+    // One phase: passes [.., end) of the routed table (SH false) or of the shared slot's
+    // one-entry table (SH true), handed out by that phase's LDS counter; the wave starts at
+    // pass P0 (< 0: the counter's next).
+    auto run = [&](auto shc, int P0, int end, int ns) __attribute__((always_inline)) {
+        constexpr bool SH = decltype(shc)::value;
+        // pass P -> its slot; the passes a wave takes only increase, so the slot cursor moves
+        // forward
+        int cursor = 0;
+        auto resolve = [&](int Q) __attribute__((always_inline)) {
+            if constexpr (SH)
+                return flat_resolve<FMT, MAXM>(Q, end, 1, pN, sN, rpp, grp, w_r, s_rt, w_s, s_s, cursor, s_she, s_shr0,
+                                               s_shm, s_shpass0);
+            else
+                return flat_resolve<FMT, MAXM>(Q, end, ns, pN, sN, rpp, grp, w_r, s_rt, w_s, s_s, cursor, s_e, s_r0,
+                                               s_m, s_pass0);
+        };
+        auto grab = [&]() __attribute__((always_inline)) {
+            int g = 0;
+            if (lane == 0) g = atomicAdd(SH ? &s_shnext : &s_next, 1);
+            return min(__builtin_amdgcn_readfirstlane(g), end);
+        };
 
-    int P = min(beg + wave, end);
-    FlatPass fc = resolve(P);
-    u32x4 wa[U], wb[U];
-    uint32_t sa[NSC], sb[NSC];
-    load(fc.wb, fc.sb, fc.ridx, fc.srow, 0, wa, sa);
-    int Pn = P < end ? grab() : end;
-    FlatPass fn = resolve(Pn);
-    tokens(fc);
-    int ib = 0;
-    // one batch: load the following one into `nx` (the next pass's first batch after the
-    // last one; every field selected, so the load is unconditional), consume `cu`
-    auto step = [&](u32x4 (&cu)[U], uint32_t (&cs)[NSC], u32x4 (&nx)[U],
-                    uint32_t (&nsc)[NSC]) __attribute__((always_inline)) {
-        const bool last = ib + 1 == nb;
-        load(last ? fn.wb : fc.wb, last ? fn.sb : fc.sb, last ? fn.ridx : fc.ridx, last ? fn.srow : fc.srow,
-             last ? 0 : ib + 1, nx, nsc);
-        compute(fc, ib, cu, cs);
-        if (last) {
-            P = Pn;
-            fc = fn;
-            Pn = P < end ? grab() : end;
-            fn = resolve(Pn);
-            tokens(fc);
-            ib = 0;
-        } else {
-            ++ib;
+        int P = P0 < 0 ? grab() : min(P0, end);
+        FlatPass fc = resolve(P);
+        u32x4 wa[U], wb[U];
+        uint32_t sa[NSC], sb[NSC];
+        load(fc.wb, fc.sb, fc.ridx, fc.srow, 0, wa, sa);
+        int Pn = P < end ? grab() : end;
+        FlatPass fn = resolve(Pn);
+        tokens(fc);
+        int ib = 0;
+        // one batch: load the following one into `nx` (the next pass's first batch after the
+        // last one; every field selected, so the load is unconditional), consume `cu`
+        auto step = [&](u32x4 (&cu)[U], uint32_t (&cs)[NSC], u32x4 (&nx)[U],
+                        uint32_t (&nsc)[NSC]) __attribute__((always_inline)) {
+            const bool last = ib + 1 == nb;
+            load(last ? fn.wb : fc.wb, last ? fn.sb : fc.sb, last ? fn.ridx : fc.ridx, last ? fn.srow : fc.srow,
+                 last ? 0 : ib + 1, nx, nsc);
+            compute(fc, ib, cu, cs);
+            if (last) {
+                P = Pn;
+                fc = fn;
+                Pn = P < end ? grab() : end;
+                fn = resolve(Pn);
+                tokens(fc);
+                ib = 0;
+            } else {
+                ++ib;
+            }
+            return P < end;
+        };
+        bool more = P < end;
+        while (more) {
+            more = step(wa, sa, wb, sb);
+            if (!more) break;
+            more = step(wb, sb, wa, sa);
         }
-        return P < end;
     };
-    bool more = P < end;
-    while (more) {
-        more = step(wa, sa, wb, sb);
-        if (!more) break;
-        more = step(wb, sb, wa, sa);
+    if constexpr (ROUTE) {
+        lds_wait_at_least(&s_dma, NW - T0);                // every activation row is in LDS
+        run(std::true_type{}, -1, sh_end, 1);
+        lds_wait_at_least(&s_tab, 1);
+        run(std::false_type{}, -1, s_end, s_ns);
+    } else {
+        const int end = s_end;
+        run(std::false_type{}, s_beg + wave, end, s_ns);
+    }
+    if constexpr (ROUTE) {
+        // workgroup 0 writes the permutation, by the first of its waves to run out of passes
+        // (written at the start, it held back every wave of workgroup 0 by that long)
+        if (blockIdx.x == 0) {
+            int v = 1;
+            if (lane == 0) v = atomicAdd(&s_perm, 1);
+            if (__builtin_amdgcn_readfirstlane(v) == 0)
+                small_permutation(s_sid, T * kk, E, ra.offsets, ra.sorted, ra.p2r, lane, 64);
+        }
     }
 }
 
