@@ -77,6 +77,7 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_logits_kernel(const 
     }
 #pragma unroll
     for (int t = 0; t < kRouterTB; ++t) {
+        if (t >= nt) break;                          // (each reduction is a chain of shuffles)
         const double s = group_sum_f64(acc[t], kWave);
         if (lane == 0) part[wave][t] = s;
     }
