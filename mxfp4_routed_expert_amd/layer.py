@@ -117,8 +117,11 @@ class MoELayer:
         self.hs_sh = e(T, Is // 32, dt=torch.uint8) if (staged_sh and mx) else None
         self.ws_gu_sh = B._workspace(B.moe_expert_gateup_workspace(sh, w.act, T, 1), device) if staged_sh else None
         # otherwise the shared expert does not depend on routing: it runs on a second stream,
-        # joined before the combine, so it overlaps router, permutation and routed experts
-        self.side = torch.cuda.Stream(device=device) if (w.shared is not None and not self.fused) else None
+        # joined before the combine, so it overlaps router, permutation and routed experts;
+        # so does the latent down-projection, which the routed gate/up waits for
+        side = w.shared is not None or w.p_down is not None
+        self.side = torch.cuda.Stream(device=device) if (side and not self.fused) else None
+        self.lat_ready = torch.cuda.Event() if (w.p_down is not None and not self.fused) else None
 
     def forward(self, x, mark=None):
         """One layer step on tokens x (bf16 [T][H]); returns the float32 output buffer.
@@ -150,21 +153,25 @@ class MoELayer:
                 mark("down_end")
             return self.out
         mx = w.act == "mxfp4"
-        if w.shared is not None:
-            cur = torch.cuda.current_stream()
+        cur = torch.cuda.current_stream()
+        xe = x
+        if self.side is not None:
             self.side.wait_stream(cur)
             with torch.cuda.stream(self.side):
-                B.moe_expert_gateup(w.shared, x, w.act, 1, None, None,
-                                    out=(None if mx else self.h_sh, self.hq_sh, self.hs_sh), ws=self.ws_gu_sh)
-                B.moe_expert_down(w.shared, self.T, w.act, 1, None, self.h_sh, self.hq_sh, self.hs_sh,
-                                  out=self.y_s)
+                if w.p_down is not None:
+                    xe = B.moe_dense_bf16(x, w.p_down, out=self.x_lat)
+                    self.lat_ready.record(self.side)
+                if w.shared is not None:
+                    B.moe_expert_gateup(w.shared, x, w.act, 1, None, None,
+                                        out=(None if mx else self.h_sh, self.hq_sh, self.hs_sh), ws=self.ws_gu_sh)
+                    B.moe_expert_down(w.shared, self.T, w.act, 1, None, self.h_sh, self.hq_sh, self.hs_sh,
+                                      out=self.y_s)
         B.moe_route_permute(x, w.w_router, w.k, w.score, w.renormalize, w.routed_scaling, w.logit_bias,
                             w.select_bias, w.w_shared_gate,
                             out=(self.ids, self.topk_w, self.sg, self.offs, self.sp, self.p2r), ws=self.ws_route,
                             n_group=w.n_group, topk_group=w.topk_group)
-        xe = x
         if w.p_down is not None:
-            xe = B.moe_dense_bf16(x, w.p_down, out=self.x_lat)
+            cur.wait_event(self.lat_ready)
         if mark is not None:
             mark("gateup_begin")
         B.moe_expert_gateup(w.experts, xe, w.act, w.k, self.offs, self.sp,
@@ -179,7 +186,7 @@ class MoELayer:
             B.moe_expert_down(w.experts, self.T, w.act, w.k, self.offs, self.h, self.hq, self.hs, out=self.y_rows)
         if mark is not None:
             mark("down_end")
-        if w.shared is not None:
+        if self.side is not None:
             cur.wait_stream(self.side)
         if w.p_up is not None:
             if not self.latent_down_combine:
