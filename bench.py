@@ -111,8 +111,14 @@ def down_algorithmic(cfg, D, fused=False, combined=None):
     return dict(bytes=nbytes, flops=flops)
 
 
-def dominant_kernel(cfg):
-    """Name pattern (as rocprofv3 reports it) of the routed gate/up kernel of a workload."""
+STEP_KERNEL = r"decode_step_kernel<\d+>"
+
+
+def dominant_kernel(cfg, single=False):
+    """Name pattern (as rocprofv3 reports it) of the routed gate/up kernel of a workload, or
+    of the single-launch decode step that holds it."""
+    if single:
+        return STEP_KERNEL
     if cfg.act == "mxfp4" and cfg.T >= 64:
         return r"mxgemm_kernel<true, true, (?:true|false)>"
     if cfg.wfmt == "mxfp4" and cfg.T >= 64:
@@ -120,6 +126,12 @@ def dominant_kernel(cfg):
     if cfg.T <= 8:
         return r"gemv_flat_kernel<\d+, \d+, \d+, true(?:, (?:true|false))?>"
     return r"gemv_kernel<\d+, \d+, \d+, true, true>"
+
+
+def single_launch(cfg):
+    """Whether the layer runs a step of this workload as one moe_decode_step launch (the
+    decode-sized fused form over MXFP4 weights with bf16 activations and no latent width)."""
+    return cfg.T <= 4 and cfg.act == "float" and cfg.wfmt == "mxfp4" and not cfg.latent and cfg.E <= 512
 
 
 def down_kernel(cfg, fused, combined=None):
@@ -162,12 +174,13 @@ def parse_traffic(cfg, fetch_dir, write_dir):
     import csv
     import glob
     import re
+    single = single_launch(cfg)
 
     def per_dispatch(d, counter):
         rows = []
         for f in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
             rows += list(csv.DictReader(open(f)))
-        pat = re.compile(dominant_kernel(cfg))
+        pat = re.compile(dominant_kernel(cfg, single))
         kern = [float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == counter and pat.search(r["Kernel_Name"])]
         cal = [float(r["Counter_Value"]) for r in rows if r["Counter_Name"] == counter and "neg_kernel" in r["Kernel_Name"]]
         if not kern or not cal:
@@ -177,7 +190,7 @@ def parse_traffic(cfg, fetch_dir, write_dir):
     w_k, nw, w_c = per_dispatch(write_dir, "WRITE_SIZE")
     gib = float(1 << 30)
     ff, fw = gib / (f_c * 1024.0), gib / (w_c * 1024.0)
-    res = {"workload": cfg.name, "kernel": dominant_kernel(cfg), "source_sha256": source_digest(),
+    res = {"workload": cfg.name, "kernel": dominant_kernel(cfg, single), "source_sha256": source_digest(),
            "fetch_kib_per_dispatch": f_k, "write_kib_per_dispatch": w_k, "dispatches": [nf, nw],
            "calibration": "torch.neg of a 1 GiB float64 tensor (1 GiB read, 1 GiB written)",
            "calib_fetch_kib": f_c, "calib_write_kib": w_c, "fetch_factor": ff, "write_factor": fw,
@@ -337,21 +350,25 @@ def run_workload(torch, sdev, cfg, layers, NB, steps, warmup, use_graphs, dev, t
     a = torch.randn(8192, 8192, device=dev)
     for _ in range(4 if cfg.T < 64 else 8):
         a = a @ a * 1e-4
-    ev = [{k: torch.cuda.Event(enable_timing=True) for k in ("gateup_begin", "gateup_end", "down_begin", "down_end")}
-          for _ in range(n)]
+    single = bool(getattr(layers[0], "single", False))
+    keys = ("step_begin", "step_end") if single else ("gateup_begin", "gateup_end", "down_begin", "down_end")
+    ev = [{k: torch.cuda.Event(enable_timing=True) for k in keys} for _ in range(n)]
     for s in range(n):
         L, x = slot(warmup + s)
         L.forward(x, mark=lambda name, e=ev[s]: e[name].record())
     torch.cuda.synchronize()
     del a
-    gu_us = 1e3 * sum(e["gateup_begin"].elapsed_time(e["gateup_end"]) for e in ev) / n
-    dn_us = 1e3 * sum(e["down_begin"].elapsed_time(e["down_end"]) for e in ev) / n
+    mean_us = lambda b, e_: 1e3 * sum(e[b].elapsed_time(e[e_]) for e in ev) / n
+    if single:
+        gu_us, dn_us, st_us = None, None, mean_us("step_begin", "step_end")
+    else:
+        gu_us, dn_us, st_us = mean_us("gateup_begin", "gateup_end"), mean_us("down_begin", "down_end"), None
     D_ev = [D_slot[(warmup + s) % S] for s in range(n)]
     # launches of each step kernel, in order: eager warm-up (one per slot), warm-up replays,
     # timed replays, the per-slot expert count, the instrumented pass
     phases = [["warm", S], ["warm_replay", warmup], ["timed", steps], ["count", S], ["events", n]]
-    return dict(ms_per_step=ms_per_step, D_steps=D_steps, D_ev=D_ev, gu_us=gu_us, dn_us=dn_us, launches=n,
-                graphs=graphs is not None, slots=S, phases=phases)
+    return dict(ms_per_step=ms_per_step, D_steps=D_steps, D_ev=D_ev, gu_us=gu_us, dn_us=dn_us, st_us=st_us,
+                single=single, launches=n, graphs=graphs is not None, slots=S, phases=phases)
 
 
 def kernel_entries(cfg, fused, r, combined=None):
@@ -366,6 +383,17 @@ def kernel_entries(cfg, fused, r, combined=None):
     timing = ("HIP events on the launch stream around each launch, eager pass over the step slots "
               "after the timed region, GPU kept busy; mean over launches")
     out = []
+    if r.get("single"):
+        # one launch holds the whole step: its bytes and flops are the layer's
+        st = [algorithmic(cfg, D, fused) for D in D_ev]
+        b = sum(x["layer_bytes"] for x in st) / len(st)
+        f = sum(x["layer_flops"] for x in st) / len(st)
+        e = dict(workload=cfg.name, role="whole decode step: router, top-k, routed + shared gate/up, down, combine",
+                 kernel=STEP_KERNEL)
+        e.update(roofline(b, f, r["st_us"], peak))
+        e.update(bytes_per_launch=int(b), flops_per_launch=int(f), avg_launch_us=round(r["st_us"], 2),
+                 launches=r["launches"], timing=timing, phases=r["phases"])
+        return [e]
     for role, pat, b, f, us in (("routed gate/up" + (" + shared gate/up" if fused and cfg.shared else ""),
                                  dominant_kernel(cfg), gu_b, gu_f, r["gu_us"]),
                                 ("routed down" + (" + shared down + combine" if fused else

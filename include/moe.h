@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum {
     MOE_OK = 0,
@@ -278,6 +278,42 @@ moe_status moe_expert_down_combine(const moe_expert_weights *w, const moe_expert
                                    const int32_t *topk_ids, const float *topk_w,
                                    const int32_t *pair_to_row, const float *shared_gate, float *out,
                                    moe_stream stream);
+
+/*
+ * moe_decode_step -- a whole decode layer step: moe_router_logits, moe_topk_gateup_shared
+ * and moe_expert_down_combine as ONE launch ("the routed experts of a step run as one
+ * launch" and the host does not wait between its parts: Rulith Inference README, engine
+ * section).  The launch runs one workgroup per compute unit, every one resident at once,
+ * in three phases that hand over through `sync`: the router logits (rows spread over the
+ * workgroups), then the top-k selection in every workgroup with the routed and shared
+ * gate/up (the shared expert's weights stream while the logits are awaited), then the
+ * down product with the weighted combine (the first down weights are read while the h
+ * rows are awaited).
+ *   Arguments: desc, x, w_router, w_shared_gate, logit_bias, select_bias as for moe_route
+ *   (desc->E and desc->H must be w's expert count and d_model); w, shared as for
+ *   moe_expert_gateup_shared / moe_expert_down_combine; the results logits [T][E (+1)],
+ *   topk_ids, topk_w, shared_gate (written when w_shared_gate is given), expert_offsets,
+ *   sorted_pairs, pair_to_row, h [T*k][d_ff], h_shared [T][d_ff] and out [T][d_model] are
+ *   those of the three calls, bit for bit (shared_gate scales the shared term when given).
+ *   sync: caller-owned device memory of moe_decode_step_sync_bytes() bytes, zero-filled
+ *   once before its first use and then left to the library: word 0 counts the launches
+ *   that used it, word 1 is an error word (nonzero after a launch whose hand-off waited
+ *   past its bound, tens of milliseconds; that launch's results are undefined), the rest are
+ *   per-workgroup flags.  A sync buffer serves one stream: launches that use the same
+ *   buffer must not overlap, and a launch needs every compute unit for a workgroup, so it
+ *   should not share the GPU with another such launch.
+ *   The single launch takes MXFP4 weights, 1 <= T <= 4, T*k <= 64, E <= 512, bf16 x rows
+ *   that fit in LDS and k (+1) h rows within the down-combine's LDS limit; other shapes
+ *   (up to T = 8) run as the three calls, with the same results.  Errors: those of the
+ *   three calls, MOE_ERR_INVALID_ARG for T > 8 or a NULL sync.
+ */
+size_t moe_decode_step_sync_bytes(void);
+moe_status moe_decode_step(const moe_route_desc *desc, const void *x, const void *w_router,
+                           const void *w_shared_gate, const float *logit_bias, const float *select_bias,
+                           const moe_expert_weights *w, const moe_expert_weights *shared, float *logits,
+                           int32_t *topk_ids, float *topk_w, float *shared_gate, int32_t *expert_offsets,
+                           int32_t *sorted_pairs, int32_t *pair_to_row, float *h, float *h_shared, float *out,
+                           uint32_t *sync, moe_stream stream);
 
 /*
  * moe_combine -- atomic-free weighted sum (rabbit README, design section: routed expert

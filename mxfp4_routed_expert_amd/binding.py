@@ -79,6 +79,9 @@ _sig("moe_topk_gateup_shared", _i32, ctypes.POINTER(RouteDesc), _p, _p, _p, _i32
      ctypes.POINTER(ExpertWeightsC), _p, _p, _p, _p, _p, _p, _p, _p, _p, _p)
 _sig("moe_expert_down_combine", _i32, ctypes.POINTER(ExpertWeightsC), ctypes.POINTER(ExpertWeightsC), _i32, _i32, _p,
      _p, _p, _p, _p, _p, _p, _p)
+_sig("moe_decode_step_sync_bytes", _sz)
+_sig("moe_decode_step", _i32, ctypes.POINTER(RouteDesc), _p, _p, _p, _p, _p, ctypes.POINTER(ExpertWeightsC),
+     ctypes.POINTER(ExpertWeightsC), _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p, _p)
 _sig("moe_combine", _i32, _i32, _i32, _i32, _p, _p, _p, _p, _p, _p, _p)
 _sig("moe_dense_bf16", _i32, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _p)
 _sig("moe_dequant_bf16", _i32, _i32, _i32, _p, _p, _p, _p)
@@ -88,7 +91,7 @@ _sig("moe_mx_quantize", _i32, _i32, _i32, _p, _i32, _p, _p, _p)
 EXPORTS = ["moe_route", "moe_route_workspace", "moe_permute", "moe_permute_workspace", "moe_route_permute",
            "moe_route_permute_noalloc",
            "moe_expert_ffn", "moe_expert_gateup_shared", "moe_router_logits", "moe_topk_gateup_shared",
-           "moe_expert_down_combine",
+           "moe_expert_down_combine", "moe_decode_step", "moe_decode_step_sync_bytes",
            "moe_expert_ffn_workspace", "moe_expert_gateup", "moe_expert_gateup_workspace", "moe_expert_down",
            "moe_combine", "moe_dense_bf16", "moe_dequant", "moe_dequant_bf16", "moe_mx_quantize", "moe_last_error",
            "moe_abi_version"]
@@ -424,6 +427,53 @@ def moe_expert_down_combine(w: ExpertWeights, shared, h, h_shared, topk_ids, top
                                       _ptr(h_shared), _ptr(topk_ids), _ptr(topk_w), _ptr(pair_to_row),
                                       _ptr(shared_gate), _ptr(o), _stream()))
     return o
+
+
+def decode_step_sync(device):
+    """A zero-filled sync buffer for moe_decode_step (one per stream that runs steps)."""
+    return torch.zeros((lib.moe_decode_step_sync_bytes() // 4,), dtype=torch.int32, device=device)
+
+
+def moe_decode_step(x, w_router, k, w: ExpertWeights, shared=None, score="softmax", renormalize=True,
+                    routed_scaling=1.0, logit_bias=None, select_bias=None, w_shared_gate=None, sync=None, out=None,
+                    n_group=1, topk_group=1):
+    """A whole decode layer step (router logits, top-k with the routed and shared gate/up, down
+    with the weighted combine) in one launch when the shapes allow it.  `sync`: a buffer from
+    decode_step_sync(), kept across calls.  Returns (logits, topk_ids, topk_w, shared_gate or
+    None, expert_offsets, sorted_pairs, pair_to_row, h, h_shared or None, out [T][d_model])."""
+    T, H = x.shape
+    E = w.num_experts
+    _need(x, torch.bfloat16, "x")
+    _need(w_router, torch.bfloat16, "w_router", (E, H))
+    _need(w_shared_gate, torch.bfloat16, "w_shared_gate", (H,))
+    _need(logit_bias, torch.float32, "logit_bias", (E,))
+    _need(select_bias, torch.float32, "select_bias", (E,))
+    if sync is None:
+        raise MoeError(1, "moe_decode_step: a sync buffer (decode_step_sync) is required")
+    _need(sync, torch.int32, "sync", (lib.moe_decode_step_sync_bytes() // 4,))
+    d = RouteDesc(T, H, E, k, SCORE[score], 1 if renormalize else 0, routed_scaling, n_group, topk_group)
+    dev = x.device
+    has_sg = w_shared_gate is not None
+    if out is None:
+        lg = torch.empty((T, E + (1 if has_sg else 0)), dtype=torch.float32, device=dev)
+        ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+        sg = torch.empty((T,), dtype=torch.float32, device=dev) if has_sg else None
+        offs = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+        sp = torch.empty((T * k,), dtype=torch.int32, device=dev)
+        p2r = torch.empty((T * k,), dtype=torch.int32, device=dev)
+        h = torch.empty((T * k, w.d_ff), dtype=torch.float32, device=dev)
+        hsh = torch.empty((T, shared.d_ff), dtype=torch.float32, device=dev) if shared is not None else None
+        o = torch.empty((T, w.d_model), dtype=torch.float32, device=dev)
+    else:
+        lg, ids, tw, sg, offs, sp, p2r, h, hsh, o = out
+    c = w.c_struct()
+    cs = shared.c_struct() if shared is not None else None
+    check(lib.moe_decode_step(ctypes.byref(d), _ptr(x), _ptr(w_router), _ptr(w_shared_gate), _ptr(logit_bias),
+                              _ptr(select_bias), ctypes.byref(c), ctypes.byref(cs) if cs is not None else None,
+                              _ptr(lg), _ptr(ids), _ptr(tw), _ptr(sg), _ptr(offs), _ptr(sp), _ptr(p2r), _ptr(h),
+                              _ptr(hsh), _ptr(o), _ptr(sync), _stream()))
+    return lg, ids, tw, sg, offs, sp, p2r, h, hsh, o
 
 
 # ------------------------------------------------------------------ combine, dense, formats

@@ -7,6 +7,11 @@
 // on the block-scaled FP4 matrix-core grouped GEMM, and unquantised activations over MXFP4
 // weights on the bf16 matrix-core grouped GEMM.
 #include "gemv.h"
+#include "step_sync.h"
+
+namespace {
+constexpr int kRouterDecodeMaxT = 8;   // tokens of a moe_decode_step call
+}
 
 namespace moe {
 
@@ -319,33 +324,13 @@ extern "C" moe_status moe_expert_gateup_shared(const moe_expert_weights *w, cons
                        (hipStream_t)stream, "moe_expert_gateup_shared");
 }
 
-extern "C" moe_status moe_topk_gateup_shared(const moe_route_desc *d, const float *logits, const float *logit_bias,
-                                             const float *select_bias, int32_t has_shared_gate,
-                                             const moe_expert_weights *w, const moe_expert_weights *shared,
-                                             const void *x, int32_t *topk_ids, float *topk_w, float *shared_gate,
-                                             int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_to_row,
-                                             float *h, float *h_shared, moe_stream stream) {
-    clear_error();
-    const char *fn = "moe_topk_gateup_shared";
-    MOE_TRY(check_route_desc(d));
-    MOE_TRY(validate_weights(w, MOE_ACT_FLOAT, fn));
-    MOE_TRY(validate_shared(w, shared, fn));
-    MOE_REQUIRE(d->E == w->num_experts && d->H == w->d_model,
-                "%s: the router's E = %d and H = %d must be the experts' count (%d) and d_model (%d)", fn, d->E, d->H,
-                w->num_experts, w->d_model);
-    MOE_REQUIRE(!(select_bias && d->score != MOE_SCORE_SIGMOID), "%s: select_bias is only defined for MOE_SCORE_SIGMOID",
-                fn);
-    MOE_REQUIRE(expert_offsets && sorted_pairs && pair_to_row, "%s: NULL expert_offsets, sorted_pairs or pair_to_row",
-                fn);
-    MOE_REQUIRE((int64_t)d->T * d->k < INT32_MAX && (int64_t)d->T * w->d_ff < INT32_MAX, "%s: sizes overflow int32", fn);
-    if (d->T == 0) return moe_permute(0, d->k, d->E, topk_ids, expert_offsets, sorted_pairs, pair_to_row, nullptr, 0,
-                                      stream);
-    MOE_REQUIRE(logits && x && topk_ids && topk_w && h, "%s: NULL logits, x, topk_ids, topk_w or h", fn);
-    MOE_REQUIRE(!has_shared_gate || shared_gate, "%s: NULL shared_gate with has_shared_gate", fn);
-    MOE_REQUIRE(!shared || h_shared, "%s: NULL h_shared with a shared expert", fn);
-    hipStream_t s = (hipStream_t)stream;
+// Parameters of the gate/up launch that routes in its prologue (moe_topk_gateup_shared).
+static GemvParams topk_gateup_params(const moe_route_desc *d, const float *logits, const float *logit_bias,
+                                     const float *select_bias, int32_t has_shared_gate, const moe_expert_weights *w,
+                                     const moe_expert_weights *shared, const void *x, int32_t *topk_ids,
+                                     float *topk_w, float *shared_gate, int32_t *expert_offsets,
+                                     int32_t *sorted_pairs, int32_t *pair_to_row, float *h, float *h_shared) {
     const int T = d->T, k = d->k, R = T * k;
-    const int fmt = w->format == MOE_W_MXFP4 ? kFmtMXFP4 : kFmtFP8;
     const int slots = w->num_experts < R ? w->num_experts : R;
     GemvParams p = base_params(w, T, k, nullptr, nullptr, R);
     p.w[0] = w->gate;
@@ -384,6 +369,40 @@ extern "C" moe_status moe_topk_gateup_shared(const moe_route_desc *d, const floa
     ra.offsets = expert_offsets;
     ra.sorted = sorted_pairs;
     ra.p2r = pair_to_row;
+    return p;
+}
+
+extern "C" moe_status moe_topk_gateup_shared(const moe_route_desc *d, const float *logits, const float *logit_bias,
+                                             const float *select_bias, int32_t has_shared_gate,
+                                             const moe_expert_weights *w, const moe_expert_weights *shared,
+                                             const void *x, int32_t *topk_ids, float *topk_w, float *shared_gate,
+                                             int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_to_row,
+                                             float *h, float *h_shared, moe_stream stream) {
+    clear_error();
+    const char *fn = "moe_topk_gateup_shared";
+    MOE_TRY(check_route_desc(d));
+    MOE_TRY(validate_weights(w, MOE_ACT_FLOAT, fn));
+    MOE_TRY(validate_shared(w, shared, fn));
+    MOE_REQUIRE(d->E == w->num_experts && d->H == w->d_model,
+                "%s: the router's E = %d and H = %d must be the experts' count (%d) and d_model (%d)", fn, d->E, d->H,
+                w->num_experts, w->d_model);
+    MOE_REQUIRE(!(select_bias && d->score != MOE_SCORE_SIGMOID), "%s: select_bias is only defined for MOE_SCORE_SIGMOID",
+                fn);
+    MOE_REQUIRE(expert_offsets && sorted_pairs && pair_to_row, "%s: NULL expert_offsets, sorted_pairs or pair_to_row",
+                fn);
+    MOE_REQUIRE((int64_t)d->T * d->k < INT32_MAX && (int64_t)d->T * w->d_ff < INT32_MAX, "%s: sizes overflow int32", fn);
+    if (d->T == 0) return moe_permute(0, d->k, d->E, topk_ids, expert_offsets, sorted_pairs, pair_to_row, nullptr, 0,
+                                      stream);
+    MOE_REQUIRE(logits && x && topk_ids && topk_w && h, "%s: NULL logits, x, topk_ids, topk_w or h", fn);
+    MOE_REQUIRE(!has_shared_gate || shared_gate, "%s: NULL shared_gate with has_shared_gate", fn);
+    MOE_REQUIRE(!shared || h_shared, "%s: NULL h_shared with a shared expert", fn);
+    hipStream_t s = (hipStream_t)stream;
+    const int T = d->T, k = d->k, R = T * k;
+    const int fmt = w->format == MOE_W_MXFP4 ? kFmtMXFP4 : kFmtFP8;
+    const int slots = w->num_experts < R ? w->num_experts : R;
+    const GemvParams p = topk_gateup_params(d, logits, logit_bias, select_bias, has_shared_gate, w, shared, x, topk_ids,
+                                            topk_w, shared_gate, expert_offsets, sorted_pairs, pair_to_row, h,
+                                            h_shared);
     moe_status st = MOE_OK;
     if (gemv_route_launch(fmt, kActBF16, p, slots + (shared ? 1 : 0), s, &st)) return st;
     // shapes the routing-in-the-prologue form does not take: the route kernel's selection,
@@ -392,6 +411,32 @@ extern "C" moe_status moe_topk_gateup_shared(const moe_route_desc *d, const floa
                               expert_offsets, sorted_pairs, pair_to_row, s));
     return moe_expert_gateup_shared(w, shared, T, k, x, MOE_DT_BF16, expert_offsets, sorted_pairs, h, h_shared,
                                     stream);
+}
+
+// Parameters of the down-combine launch (moe_expert_down_combine).
+static DownCombineParams down_combine_params(const moe_expert_weights *w, const moe_expert_weights *shared, int32_t T,
+                                             int32_t k, const float *h, const float *h_shared,
+                                             const int32_t *topk_ids, const float *topk_w,
+                                             const int32_t *pair_to_row, const float *shared_gate, float *out) {
+    DownCombineParams p = {};
+    p.w = w->down;
+    p.s = w->down_s;
+    p.sw = shared ? shared->down : nullptr;
+    p.ss = shared ? shared->down_s : nullptr;
+    p.E = w->num_experts;
+    p.N = w->d_model;
+    p.I = w->d_ff;
+    p.h = h;
+    p.hs = h_shared;
+    p.ids = topk_ids;
+    p.tw = topk_w;
+    p.p2r = pair_to_row;
+    p.sg = shared ? shared_gate : nullptr;
+    p.T = T;
+    p.k = k;
+    p.R = T * k;
+    p.out = out;
+    return p;
 }
 
 extern "C" moe_status moe_expert_down_combine(const moe_expert_weights *w, const moe_expert_weights *shared,
@@ -420,23 +465,70 @@ extern "C" moe_status moe_expert_down_combine(const moe_expert_weights *w, const
     MOE_REQUIRE(!shared || h_shared, "moe_expert_down_combine: NULL h_shared with a shared expert");
     MOE_REQUIRE((((uintptr_t)h | (uintptr_t)h_shared) & 15) == 0, "moe_expert_down_combine: h and h_shared must be "
                 "16-byte aligned");
-    DownCombineParams p = {};
-    p.w = w->down;
-    p.s = w->down_s;
-    p.sw = shared ? shared->down : nullptr;
-    p.ss = shared ? shared->down_s : nullptr;
-    p.E = w->num_experts;
-    p.N = w->d_model;
-    p.I = w->d_ff;
-    p.h = h;
-    p.hs = h_shared;
-    p.ids = topk_ids;
-    p.tw = topk_w;
-    p.p2r = pair_to_row;
-    p.sg = shared ? shared_gate : nullptr;
-    p.T = T;
-    p.k = k;
-    p.R = T * k;
-    p.out = out;
+    const DownCombineParams p = down_combine_params(w, shared, T, k, h, h_shared, topk_ids, topk_w, pair_to_row,
+                                                    shared_gate, out);
     return down_combine_launch(w->format == MOE_W_MXFP4 ? kFmtMXFP4 : kFmtFP8, p, (hipStream_t)stream);
+}
+
+extern "C" size_t moe_decode_step_sync_bytes(void) { return (size_t)kSyncWords * sizeof(uint32_t); }
+
+extern "C" moe_status moe_decode_step(const moe_route_desc *d, const void *x, const void *w_router,
+                                      const void *w_shared_gate, const float *logit_bias, const float *select_bias,
+                                      const moe_expert_weights *w, const moe_expert_weights *shared, float *logits,
+                                      int32_t *topk_ids, float *topk_w, float *shared_gate, int32_t *expert_offsets,
+                                      int32_t *sorted_pairs, int32_t *pair_to_row, float *h, float *h_shared,
+                                      float *out, uint32_t *sync, moe_stream stream) {
+    clear_error();
+    const char *fn = "moe_decode_step";
+    MOE_TRY(check_route_desc(d));
+    MOE_TRY(validate_weights(w, MOE_ACT_FLOAT, fn));
+    MOE_TRY(validate_shared(w, shared, fn));
+    MOE_REQUIRE(d->E == w->num_experts && d->H == w->d_model,
+                "%s: the router's E = %d and H = %d must be the experts' count (%d) and d_model (%d)", fn, d->E, d->H,
+                w->num_experts, w->d_model);
+    MOE_REQUIRE(d->T <= kRouterDecodeMaxT, "%s: T = %d above %d (a decode step)", fn, d->T, kRouterDecodeMaxT);
+    MOE_REQUIRE(!(select_bias && d->score != MOE_SCORE_SIGMOID), "%s: select_bias is only defined for MOE_SCORE_SIGMOID",
+                fn);
+    MOE_REQUIRE(expert_offsets && sorted_pairs && pair_to_row, "%s: NULL expert_offsets, sorted_pairs or pair_to_row",
+                fn);
+    if (shared)
+        MOE_REQUIRE(shared->d_ff == w->d_ff, "%s: the shared expert's d_ff (%d) must equal d_ff (%d)", fn,
+                    shared->d_ff, w->d_ff);
+    if (down_combine_lds(d->k, shared != nullptr, w->d_ff) > 150 * 1024) {
+        set_error("%s: %d rows of d_ff = %d and the output table do not fit in LDS", fn, d->k + (shared ? 1 : 0),
+                  w->d_ff);
+        return MOE_ERR_UNSUPPORTED;
+    }
+    if (d->T == 0) return moe_permute(0, d->k, d->E, topk_ids, expert_offsets, sorted_pairs, pair_to_row, nullptr, 0,
+                                      stream);
+    MOE_REQUIRE(x && w_router && logits && topk_ids && topk_w && h && out && sync,
+                "%s: NULL x, w_router, logits, topk_ids, topk_w, h, out or sync", fn);
+    MOE_REQUIRE(!w_shared_gate || shared_gate, "%s: NULL shared_gate with w_shared_gate", fn);
+    MOE_REQUIRE(!shared || h_shared, "%s: NULL h_shared with a shared expert", fn);
+    MOE_REQUIRE((((uintptr_t)h | (uintptr_t)h_shared) & 15) == 0, "%s: h and h_shared must be 16-byte aligned", fn);
+    MOE_REQUIRE(((uintptr_t)sync & 3) == 0, "%s: sync must be 4-byte aligned", fn);
+    hipStream_t s = (hipStream_t)stream;
+    const int has_sg = w_shared_gate ? 1 : 0;
+    StepParams sp = {};
+    sp.gu = topk_gateup_params(d, logits, logit_bias, select_bias, has_sg, w, shared, x, topk_ids, topk_w, shared_gate,
+                               expert_offsets, sorted_pairs, pair_to_row, h, h_shared);
+    sp.dc = down_combine_params(w, shared, d->T, d->k, h, h_shared, topk_ids, topk_w, pair_to_row,
+                                has_sg ? shared_gate : nullptr, out);
+    sp.x = (const uint16_t *)x;
+    sp.wr = (const uint16_t *)w_router;
+    sp.wsg = (const uint16_t *)w_shared_gate;
+    sp.T = d->T;
+    sp.H = d->H;
+    sp.E = d->E;
+    sp.rows = d->E + has_sg;
+    sp.logits = logits;
+    sp.sync = sync;
+    moe_status st = MOE_OK;
+    if (w->format == MOE_W_MXFP4 && decode_step_launch(sp, s, &st)) return st;
+    // shapes the single launch does not take: the three-call form, same results
+    MOE_TRY(router_logits_small(d, x, w_router, w_shared_gate, logits, s));
+    MOE_TRY(moe_topk_gateup_shared(d, logits, logit_bias, select_bias, has_sg, w, shared, x, topk_ids, topk_w,
+                                   shared_gate, expert_offsets, sorted_pairs, pair_to_row, h, h_shared, stream));
+    return moe_expert_down_combine(w, shared, d->T, d->k, h, h_shared, topk_ids, topk_w, pair_to_row,
+                                   has_sg ? shared_gate : nullptr, out, stream);
 }

@@ -93,6 +93,25 @@ moe_status gemv_launch(int fmt, int act, bool pair, GemvParams p, int slots, int
 bool gemv_route_launch(int fmt, int act, GemvParams p, int slots, hipStream_t stream, moe_status *st);
 
 
+// The single-launch decode step (decode_step_kernel, gemv.hip): router logits, top-k with
+// the routed and shared gate/up, down with the weighted combine, one persistent launch of
+// one workgroup per compute unit whose phases hand over through the caller's sync buffer.
+struct StepParams {
+    GemvParams gu;             // the routing-in-the-prologue gate/up launch's parameters
+    DownCombineParams dc;      // the down-combine's
+    const uint16_t *x;         // bf16 [T][H]
+    const uint16_t *wr;        // router rows bf16 [E][H]
+    const uint16_t *wsg;       // shared-gate row bf16 [H] or NULL
+    int T, H, E, rows;         // rows = E + (wsg != NULL): logit rows per token
+    float *logits;             // [T][rows]
+    uint32_t *sync;            // the caller's sync buffer
+    int nx;                    // down-combine row ranges per token
+};
+// Enqueues the step as one launch: false when the shapes do not allow it (the gate/up or
+// down-combine forms do not take them, or one workgroup per CU does not fit), else the
+// launch status in *st.
+bool decode_step_launch(StepParams sp, hipStream_t stream, moe_status *st);
+
 // route.hip: the routing arguments' checks of moe_route, and the selection (top-k, weights,
 // permutation) of moe_route_permute from logits
 // already computed (the first T*(E + has_sg) floats of `ws`).
@@ -101,6 +120,10 @@ moe_status route_select_step(const moe_route_desc *d, const void *ws, const floa
                              const float *select_bias, bool has_sg, int32_t *topk_ids, float *topk_w,
                              float *shared_gate, int32_t *expert_offsets, int32_t *sorted_pairs, int32_t *pair_to_row,
                              hipStream_t s);
+
+// The router logits of T < 32 tokens with no workspace (route.hip).
+moe_status router_logits_small(const moe_route_desc *d, const void *x, const void *w_router, const void *w_shared_gate,
+                               float *logits, hipStream_t s);
 
 moe_status mx_quantize_launch(int rows, int cols, const void *x, bool f32, uint8_t *codes, uint8_t *scales,
                               hipStream_t stream);

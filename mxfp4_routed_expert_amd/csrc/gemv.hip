@@ -20,7 +20,10 @@
 //     synchronisation is needed and empty experts cost nothing.
 #include <algorithm>
 
+#include "dm_body.h"
 #include "gemv.h"
+#include "router_row.h"
+#include "step_sync.h"
 #include "topk.h"
 
 namespace moe {
@@ -538,8 +541,13 @@ MOE_DEV void lds_wait_at_least(int *ctr, int v) {
 // the routing runs, and every wave takes routed passes once wave 0 has published the table.
 // Waves hand over through LDS counters, not workgroup barriers, so none holds the others
 // back.
-template <int FMT, int ACT, int MAXM, bool PAIR, bool ROUTE = false>
-__global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParams p) {
+//
+// STEP (with ROUTE): the gate/up phase of the single-launch decode step (decode_step_kernel):
+// the routing waves first wait for every workgroup's logits (step_wait), the workgroup's
+// routing is also kept in sc->lds for the down phase, and every wave waits for its h stores
+// before it returns.
+template <int FMT, int ACT, int MAXM, bool PAIR, bool ROUTE, bool STEP>
+MOE_DEV void flat_body(const GemvParams &p, const StepCtx *sc) {
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_sid[ROUTE ? 64 : 1];
     __shared__ int s_e[kFlatMaxSlots], s_r0[kFlatMaxSlots], s_m[kFlatMaxSlots], s_pass0[kFlatMaxSlots + 1];
@@ -595,6 +603,7 @@ __global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParam
             if (lane == 0) atomicAdd(&s_dma, 1);
         }
         if (wave < T) {
+            if constexpr (STEP) step_wait(sc->sync, sc->nwg, sc->target_logits);
             double *gk = (double *)(smem + (size_t)n_act * rs) + (size_t)wave * E;   // group-limited keys
             const TopkLane r = topk_select<kFlatTopkNK>(ra.logits + (size_t)wave * ra.rows, E, kk, ra.score, ra.renorm,
                                                         ra.scaling, ra.lbias, ra.sbias, ra.has_sg, gk, ra.n_group,
@@ -607,6 +616,13 @@ __global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParam
                 }
             }
             if (blockIdx.x == 0 && ra.has_sg && lane == 0) ra.sg[wave] = r.sg;
+            if constexpr (STEP) {
+                if (lane < kk) {
+                    sc->lds->ids[wave * kk + lane] = r.e;
+                    sc->lds->tw[wave * kk + lane] = r.w;
+                }
+                if (lane == 0) sc->lds->sg[wave] = r.sg;
+            }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // s_sid holds this token's experts
             if (lane == 0) atomicAdd(&s_topk, 1);
         }
@@ -636,6 +652,9 @@ __global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParam
             int slot = 0;
             for (int q = 0; q < P; ++q) slot += (((fm >> q) & 1ull) && __builtin_amdgcn_readlane(e, q) < e) ? 1 : 0;
             if (e >= 0) s_tok[row] = lane / kk;
+            if constexpr (STEP) {
+                if (lane < P) sc->lds->p2r[lane] = e >= 0 ? row : -1;
+            }
             if (first) {
                 s_e[slot] = e;
                 s_r0[slot] = row;
@@ -902,6 +921,12 @@ __global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParam
                 small_permutation(s_sid, T * kk, E, ra.offsets, ra.sorted, ra.p2r, lane, 64);
         }
     }
+    if constexpr (STEP) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this wave's h rows are stored
+}
+
+template <int FMT, int ACT, int MAXM, bool PAIR, bool ROUTE = false>
+__global__ __launch_bounds__(kFlatThreads) void gemv_flat_kernel(const GemvParams p) {
+    flat_body<FMT, ACT, MAXM, PAIR, ROUTE, false>(p, nullptr);
 }
 
 static void pick_layout(int units, bool pair, int *G, int *nl);
@@ -1174,7 +1199,9 @@ static int down_combine_batch(int nl) {
     return best;
 }
 
-moe_status down_combine_launch(int fmt, DownCombineParams p, hipStream_t stream) {
+// Launch shape of the down-combine: fills p.G, p.nl, p.rows_per_wg and p.h_lds_bytes;
+// returns the grid (row ranges, tokens), the LDS bytes and the FP8 form's batch U.
+static dim3 down_combine_shape(int fmt, DownCombineParams &p, size_t *lds, int *U_out) {
     const bool mfma = fmt == kFmtMXFP4;
     const int units = fmt == kFmtMXFP4 ? p.I / 32 : p.I / 16;
     int U = 1, rpp = 4;                                    // MFMA path: 8-row tiles, the last one clamped
@@ -1198,8 +1225,16 @@ moe_status down_combine_launch(int fmt, DownCombineParams p, hipStream_t stream)
     p.rows_per_wg = rpw;
     const int nslot = p.k + (p.sw ? 1 : 0);
     p.h_lds_bytes = (int)align_up((size_t)nslot * 4 * dc_plane_ld(p.I), 1024);
-    const size_t lds = down_combine_lds(p.k, p.sw != nullptr, p.I);
-    dim3 grid((p.N + rpw - 1) / rpw, p.T);
+    *lds = down_combine_lds(p.k, p.sw != nullptr, p.I);
+    *U_out = U;
+    return dim3((p.N + rpw - 1) / rpw, p.T);
+}
+
+moe_status down_combine_launch(int fmt, DownCombineParams p, hipStream_t stream) {
+    const bool mfma = fmt == kFmtMXFP4;
+    size_t lds = 0;
+    int U = 1;
+    const dim3 grid = down_combine_shape(fmt, p, &lds, &U);
     if (mfma) {
         down_combine_mfma_launch(p, grid, lds, stream);
     } else {
@@ -1310,7 +1345,9 @@ static int flat_grid(long long passes) {
     return (int)std::min<long long>(device_cu_count(), std::max<long long>(1, passes));
 }
 
-bool gemv_route_launch(int fmt, int act, GemvParams p, int slots, hipStream_t stream, moe_status *st) {
+// Shape of the routing-in-the-prologue gate/up launch: fills p.G and p.nl, the LDS bytes and
+// the token tile; false when the shapes do not allow the form.
+static bool gemv_route_shape(int fmt, int act, GemvParams &p, size_t *lds_out, int *maxm_out) {
     if ((fmt != kFmtMXFP4 && fmt != kFmtFP8) || act != kActBF16) return false;
     const int units = fmt == kFmtMXFP4 ? p.K / 32 : p.K / 16;
     pick_layout(units, true, &p.G, &p.nl);
@@ -1322,6 +1359,15 @@ bool gemv_route_launch(int fmt, int act, GemvParams p, int slots, hipStream_t st
         return false;
     int maxm = 1;
     while (maxm < p.T) maxm *= 2;
+    *lds_out = lds;
+    *maxm_out = maxm;
+    return true;
+}
+
+bool gemv_route_launch(int fmt, int act, GemvParams p, int slots, hipStream_t stream, moe_status *st) {
+    size_t lds = 0;
+    int maxm = 1;
+    if (!gemv_route_shape(fmt, act, p, &lds, &maxm)) return false;
     const int rpp = 32 / p.G;
     long long passes = (long long)(slots - (p.shared_slot >= 0 ? 1 : 0)) * ((p.N + rpp - 1) / rpp);
     if (p.shared_slot >= 0) passes += (p.sN + rpp - 1) / rpp;
@@ -1397,6 +1443,99 @@ moe_status gemv_launch(int fmt, int act, bool pair, GemvParams p, int slots, int
     GemvFn fn = pick_kernel(fmt, act, pair, maxm, p.offsets != nullptr, wide);
     hipLaunchKernelGGL(fn, grid, dim3(threads), lds, stream, p);
     return launch_check(what);
+}
+
+// ------------------------------------------------------------------ single-launch decode step
+// The whole decode layer step in one launch of one workgroup per compute unit (Rulith
+// Inference README, engine section: a step's routed experts in one launch, with no host
+// round trip between its parts).  Three phases, separated by the flag hand-offs of
+// step_sync.h:
+//   1. router logits: rows b, b + nwg, ... of the router (and the shared-gate row) by
+//      groups of four waves, each wave a quarter of H (router_quarter: the same sums as
+//      router_logits_kernel);
+//   2. top-k and gate/up (flat_body<..., ROUTE, STEP>): the shared expert's gate/up passes
+//      do not depend on the routing and run while the routing waves wait for every
+//      workgroup's logits; then the routed passes;
+//   3. down and combine (dm_body<true>): each workgroup issues its first weight loads, then
+//      waits for every workgroup's h rows, over the down-combine's (row range, token) items
+//      b, b + nwg, ....
+// Every workgroup selects the same experts from the same logits, so each keeps its own
+// routing in LDS for phase 3; workgroup 0 writes the routing results and the permutation.
+template <int MAXM>
+__global__ __launch_bounds__(kFlatThreads) void decode_step_kernel(const StepParams sp) {
+    __shared__ StepRouting s_route;
+    constexpr int NG = kFlatThreads / 64 / kRouterWaves;   // router row groups per workgroup
+    __shared__ double s_rpart[NG][kRouterWaves][kRouterTB];
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(wave_id());
+    const int nwg = gridDim.x;
+    const uint32_t c = __builtin_amdgcn_readfirstlane(step_launch_count(sp.sync));
+    StepCtx sc;
+    sc.sync = sp.sync;
+    sc.target_logits = 2u * c + 1u;
+    sc.target_h = 2u * c + 2u;
+    sc.nwg = nwg;
+    sc.lds = &s_route;
+
+    // 1. router logits
+    const int grp = wave / kRouterWaves, quarter = wave % kRouterWaves;
+    const int nround = (sp.rows + nwg * NG - 1) / (nwg * NG);
+    for (int rd = 0; rd < nround; ++rd) {
+        const int row = (int)blockIdx.x + nwg * (rd * NG + grp);
+        if (row < sp.rows) {
+            const uint16_t *w = row < sp.E ? sp.wr + (size_t)row * sp.H : sp.wsg;
+            double s[kRouterTB];
+            router_quarter(sp.x, w, 0, sp.T, sp.H, quarter, s);
+#pragma unroll
+            for (int t = 0; t < kRouterTB; ++t) {
+                if (t >= sp.T) break;
+                if (lane == 0) s_rpart[grp][quarter][t] = s[t];
+            }
+        }
+        __syncthreads();
+        if (quarter == 0 && row < sp.rows && lane < sp.T)
+            sp.logits[(size_t)lane * sp.rows + row] = router_finish(s_rpart[grp], lane);
+        __syncthreads();
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this wave's logits are stored
+    __syncthreads();
+    if (threadIdx.x == 0) step_arrive(sp.sync, sc.target_logits);
+
+    // 2. top-k, routed and shared gate/up (every wave returns with its h rows stored)
+    flat_body<kFmtMXFP4, kActBF16, MAXM, true, true, true>(sp.gu, &sc);
+    __syncthreads();
+    if (threadIdx.x == 0) step_arrive(sp.sync, sc.target_h);
+
+    // 3. down and combine
+    const int nitems = sp.nx * sp.T;
+    for (int v = (int)blockIdx.x; v < nitems; v += nwg) dm_body<true>(sp.dc, v % sp.nx, v / sp.nx, &sc, v == (int)blockIdx.x);
+    // every workgroup has arrived at the end of phase 2 (workgroup 0 has waited for it in its
+    // first item), so every one has read the launch count
+    if (blockIdx.x == 0 && threadIdx.x == 0)
+        __hip_atomic_store(sp.sync, c + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+bool decode_step_launch(StepParams sp, hipStream_t stream, moe_status *st) {
+    size_t lds_gu = 0, lds_dc = 0;
+    int maxm = 1, U = 1;
+    if (!gemv_route_shape(kFmtMXFP4, kActBF16, sp.gu, &lds_gu, &maxm)) return false;
+    const dim3 dgrid = down_combine_shape(kFmtMXFP4, sp.dc, &lds_dc, &U);
+    sp.nx = (int)dgrid.x;
+    const int nwg = device_cu_count();
+    if (nwg > kSyncMaxWG || sp.T > kRouterTB || sp.H % 32 != 0 || sp.T * sp.gu.k > 64 || sp.T > 4) return false;
+    const size_t lds = std::max(lds_gu, lds_dc);
+    using StepFn = void (*)(const StepParams);
+    StepFn fn = maxm == 1 ? decode_step_kernel<1> : (maxm == 2 ? decode_step_kernel<2> : decode_step_kernel<4>);
+    // every workgroup must be resident at once: one per CU
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)fn, kFlatThreads, lds) != hipSuccess ||
+        per_cu < 1) {
+        (void)hipGetLastError();
+        return false;
+    }
+    hipLaunchKernelGGL(fn, dim3(nwg), dim3(kFlatThreads), lds, stream, sp);
+    *st = launch_check("moe_decode_step: decode_step_kernel");
+    return true;
 }
 
 }  // namespace moe

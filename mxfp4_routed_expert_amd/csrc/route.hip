@@ -13,23 +13,16 @@
 #include <mutex>
 
 #include "common.h"
+#include "router_row.h"
 #include "topk.h"
 
 namespace moe {
 namespace {
 
-constexpr int kRouterTB = 8;      // tokens per wave
-constexpr int kRouterUnroll = 4;  // 16-byte loads in flight per lane per pass
-
 // A workgroup computes the dot products of one weight row (expert e < E, or the shared
-// gate row e == E) with up to kRouterTB tokens; wave w covers the w-th quarter of H, so a
-// row is read with four waves' worth of loads in flight.  Lanes stride over the quarter in
-// 8-element (16-byte) vectors; loads are issued unconditionally from clamped indices (a
-// load under a branch would be waited for at the join) and out-of-range vectors are
-// skipped when consumed.  Float64 partial sums are reduced over the wave in a fixed
-// butterfly order, then over the four waves in order.
-constexpr int kRouterWaves = 4;
-
+// gate row e == E) with up to kRouterTB tokens; wave w covers the w-th quarter of H
+// (router_quarter), so a row is read with four waves' worth of loads in flight, and the
+// quarters are added in order.
 __global__ __launch_bounds__(64 * kRouterWaves) void router_logits_kernel(const uint16_t *__restrict__ x,
                                                                          const uint16_t *__restrict__ wr,
                                                                          const uint16_t *__restrict__ wsg,
@@ -41,53 +34,15 @@ __global__ __launch_bounds__(64 * kRouterWaves) void router_logits_kernel(const 
     const int t0 = blockIdx.y * kRouterTB;
     const int nt = min(kRouterTB, T - t0);
     const int lane = lane_id(), wave = wave_id();
-    double acc[kRouterTB];
-#pragma unroll
-    for (int t = 0; t < kRouterTB; ++t) acc[t] = 0.0;
-
-    const int nvec = H >> 3;                                   // H % 32 == 0: quarters are whole
-    const int q0 = wave * (nvec / kRouterWaves), q1 = q0 + nvec / kRouterWaves;
-    for (int v0 = q0 + lane; v0 < q1 + lane; v0 += kWave * kRouterUnroll) {
-        u32x4 wv[kRouterUnroll];
-#pragma unroll
-        for (int u = 0; u < kRouterUnroll; ++u)
-            wv[u] = __builtin_nontemporal_load((const u32x4 *)(w) + min(v0 + u * kWave, q1 - 1));
-#pragma unroll
-        for (int t = 0; t < kRouterTB; ++t) {
-            if (t >= nt) break;                      // uniform across the wave
-            const u32x4 *xr = (const u32x4 *)(x + (size_t)(t0 + t) * H);
-            u32x4 xv[kRouterUnroll];
-#pragma unroll
-            for (int u = 0; u < kRouterUnroll; ++u) xv[u] = xr[min(v0 + u * kWave, q1 - 1)];
-            double s = acc[t];
-#pragma unroll
-            for (int u = 0; u < kRouterUnroll; ++u) {
-                if (v0 + u * kWave < q1) {
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const f32x2 fw = bf16x2_to_f32x2(wv[u][q]);
-                        const f32x2 fx = bf16x2_to_f32x2(xv[u][q]);
-                        s = fma((double)fw.x, (double)fx.x, s);
-                        s = fma((double)fw.y, (double)fx.y, s);
-                    }
-                }
-            }
-            acc[t] = s;
-        }
-    }
+    double s[kRouterTB];
+    router_quarter(x, w, t0, nt, H, wave, s);
 #pragma unroll
     for (int t = 0; t < kRouterTB; ++t) {
-        if (t >= nt) break;                          // (each reduction is a chain of shuffles)
-        const double s = group_sum_f64(acc[t], kWave);
-        if (lane == 0) part[wave][t] = s;
+        if (t >= nt) break;
+        if (lane == 0) part[wave][t] = s[t];
     }
     __syncthreads();
-    if (threadIdx.x < nt) {
-        double s = 0.0;
-#pragma unroll
-        for (int w4 = 0; w4 < kRouterWaves; ++w4) s += part[w4][threadIdx.x];
-        logits[(size_t)(t0 + threadIdx.x) * rows + row] = (float)s;
-    }
+    if (threadIdx.x < nt) logits[(size_t)(t0 + threadIdx.x) * rows + row] = router_finish(part, threadIdx.x);
 }
 
 // Many tokens: a tiled float64 product on the matrix cores.  A workgroup owns 128 tokens x
@@ -335,6 +290,24 @@ moe_status enqueue_logits(const moe_route_desc *d, const void *x, const void *w_
                        (const uint16_t *)w_router, (const uint16_t *)w_shared_gate, d->T, d->H, d->E, rows, logits);
     return launch_check("moe_route: router_logits_kernel");
 }
+
+}  // namespace
+
+namespace moe {
+
+// The logits of a few tokens (T < 32: the one-row-per-workgroup router, no workspace).
+moe_status router_logits_small(const moe_route_desc *d, const void *x, const void *w_router, const void *w_shared_gate,
+                               float *logits, hipStream_t s) {
+    if (router_tiled(d)) {
+        set_error("router_logits_small: %d tokens take the tiled router", d->T);
+        return MOE_ERR_UNSUPPORTED;
+    }
+    return enqueue_logits(d, x, w_router, w_shared_gate, logits, nullptr, s);
+}
+
+}  // namespace moe
+
+namespace {
 
 double *partial_of(const moe_route_desc *d, void *ws) {
     return (double *)((unsigned char *)ws + align_up((size_t)d->T * (d->E + 1) * sizeof(float), 256));

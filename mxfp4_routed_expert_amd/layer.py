@@ -6,10 +6,10 @@ and after the combine (Kimi K3 article, architecture section); a gated shared ex
 output is scaled by its gate before it is added after the up projection.  Decode-sized
 LatentMoE steps run the routed down product and the combine into z as one down-combine
 launch.  Decode-sized
-batches use the fused calls instead, three kernels a step: the router's logits; the
-selection with the routed and shared gate/up in one launch (moe_topk_gateup_shared); down
-and combine in one launch.  Every step runs in the HIP library; this module only wires
-buffers.  All buffers for a token count are allocated once, so a step enqueues kernels and
+batches use the fused calls instead: by default the whole step as one launch
+(moe_decode_step), or its three calls -- the router's logits; the selection with the routed
+and shared gate/up in one launch (moe_topk_gateup_shared); down and combine in one launch.
+Every step runs in the HIP library; this module only wires buffers.  All buffers for a token count are allocated once, so a step enqueues kernels and
 allocates nothing.
 """
 from __future__ import annotations
@@ -70,7 +70,9 @@ def fuses(w: LayerWeights, T: int) -> bool:
 
 
 class MoELayer:
-    def __init__(self, w: LayerWeights, T: int, device):
+    def __init__(self, w: LayerWeights, T: int, device, single_launch: bool = True):
+        """single_launch: fused decode steps run as one moe_decode_step launch (False: its three
+        calls, moe_router_logits, moe_topk_gateup_shared and moe_expert_down_combine)."""
         self.w, self.T, self.dev = w, T, device
         E, H, k = w.E, w.H, w.k
         L, I = w.experts.d_model, w.experts.d_ff
@@ -103,6 +105,8 @@ class MoELayer:
         self.out = e(T, H)
         self.ws_route = B._workspace(B.moe_route_workspace(T, H, E, k, w.score), device)
         self.logits = e(T, E + (1 if w.w_shared_gate is not None else 0)) if self.fused else None
+        self.single = self.fused and single_launch
+        self.sync = B.decode_step_sync(device) if self.single else None
         # h rows: the staged form runs gate/up and down as separate calls on these buffers
         # (float32 h in FLOAT mode, MX codes and scales in MXFP4 mode), as does the fused form
         mx = w.act == "mxfp4"
@@ -128,9 +132,21 @@ class MoELayer:
 
         With `mark`, mark(name) is called on the step's stream before and after the routed
         gate/up call ("gateup_begin", "gateup_end") and the down call ("down_begin",
-        "down_end"; the down product with the combine in the fused form), so a caller can
-        record events around those kernels."""
+        "down_end"; the down product with the combine in the fused form), or around the
+        single-launch step ("step_begin", "step_end"), so a caller can record events around
+        those kernels."""
         w = self.w
+        if self.single:
+            # the whole step in one launch (the three calls below, same results)
+            if mark is not None:
+                mark("step_begin")
+            B.moe_decode_step(x, w.w_router, w.k, w.experts, w.shared, w.score, w.renormalize, w.routed_scaling,
+                              w.logit_bias, w.select_bias, w.w_shared_gate, sync=self.sync,
+                              out=(self.logits, self.ids, self.topk_w, self.sg, self.offs, self.sp, self.p2r, self.h,
+                                   self.h_sh, self.out), n_group=w.n_group, topk_group=w.topk_group)
+            if mark is not None:
+                mark("step_end")
+            return self.out
         if self.fused:
             # three kernels: the router's logits, one gate/up launch that routes in its
             # prologue (the routing results land in the same buffers as moe_route_permute's),

@@ -254,3 +254,28 @@ def test_route_permute_noalloc_refuses_more_than_its_scratch():
                                        DUMMY, DUMMY, None)
     assert st == B.MOE_ERR_UNSUPPORTED
     assert "scratch" in B.last_error()
+
+
+def _decode_step(d, w, sync=DUMMY, shared=None, wsg=None, sg=None):
+    return lib.moe_decode_step(ctypes.byref(d), DUMMY, DUMMY, wsg, None, None, ctypes.byref(w),
+                               ctypes.byref(shared) if shared is not None else None, DUMMY, DUMMY, DUMMY, sg,
+                               DUMMY, DUMMY, DUMMY, DUMMY, DUMMY if shared is not None else None, DUMMY, sync, None)
+
+
+def test_decode_step_checks():
+    assert lib.moe_decode_step_sync_bytes() == 4 * (64 + 1024)
+    w = _weights()
+    # a sync buffer is required
+    assert _decode_step(_desc(), w, sync=None) == B.MOE_ERR_INVALID_ARG and "sync" in B.last_error()
+    # more than 8 tokens is not a decode step
+    assert _decode_step(_desc(T=9), w) == B.MOE_ERR_INVALID_ARG and "T = 9" in B.last_error()
+    # the router's E and H must be the experts'
+    assert _decode_step(_desc(E=16), w) == B.MOE_ERR_INVALID_ARG
+    assert _decode_step(_desc(H=512), w) == B.MOE_ERR_INVALID_ARG
+    # a shared gate needs its output
+    assert _decode_step(_desc(), w, wsg=DUMMY, sg=None) == B.MOE_ERR_INVALID_ARG
+    # k + 1 rows of a wide d_ff do not fit the down-combine's LDS
+    wide = _weights(E=16, K=256, I=8192)
+    assert _decode_step(_desc(E=16, k=8), wide, shared=_weights(E=1, K=256, I=8192)) == B.MOE_ERR_UNSUPPORTED
+    # a bad descriptor is refused first; zero tokens with NULL outputs is a no-op
+    assert _decode_step(_desc(k=0), w) == B.MOE_ERR_INVALID_ARG

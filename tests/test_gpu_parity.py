@@ -517,6 +517,85 @@ def test_topk_gateup_equals_route_then_gateup(dev, M, name):
     say(f"  {name}: routing, permutation, h equal")
 
 
+# the single-launch decode step (moe_decode_step) against its three calls:
+# (config, n_group, topk_group, whether the shapes take the single launch)
+DECODE_STEP_CASES = {
+    "tiny": (tiny(), 1, 1, True),
+    "tiny_fused_gated": (LAYER_CASES["tiny_fused_gated"], 1, 1, True),
+    "tiny_fused_odd_blocks": (LAYER_CASES["tiny_fused_odd_blocks"], 1, 1, True),
+    "tiny_groups": (TOPK_GATEUP_CASES["tiny_groups"][0], 4, 2, True),
+    "tiny_4tok_sigmoid": (tiny(name="t4s", wtag=105, score="sigmoid", select_bias_std=0.01, k=6, T=4, E=32,
+                               shared="gated", shared_K=256, shared_I=128), 1, 1, True),
+    "decode_full": (synth.get("qwen38max_decode"), 1, 1, True),
+    # shapes the single launch does not take run as the three calls
+    "tiny_sigmoid_fp8": (LAYER_CASES["tiny_fused_fp8_ungated"], 1, 1, False),
+    "tiny_many_experts": (TOPK_GATEUP_CASES["tiny_many_experts"][0], 1, 1, False),
+    "tiny_6tok": (tiny(name="t6", wtag=106, T=6, shared="gated", shared_K=256, shared_I=128), 1, 1, False),
+}
+
+
+@pytest.mark.parametrize("name", list(DECODE_STEP_CASES))
+def test_decode_step_equals_three_calls(dev, M, name):
+    """moe_decode_step gives the logits, routing, permutation, h rows and output of
+    moe_router_logits + moe_topk_gateup_shared + moe_expert_down_combine bit for bit, on three
+    inputs in a row with one sync buffer; the buffer counts the single launches and its error
+    word stays 0."""
+    cfg, ng, tg, single = DECODE_STEP_CASES[name]
+    t, inp = build(cfg, dev)
+    w = layer_weights(cfg, t)
+    wsg = t["w_shared_gate"] if cfg.shared == "gated" else None
+    sync = M.decode_step_sync(dev)
+    x0 = t["x"]
+    xs = [x0, (x0.float() * 0.5).to(torch.bfloat16), x0.roll(1, dims=1).contiguous()]
+    names = ["logits", "topk_ids", "topk_w", "shared_gate", "expert_offsets", "sorted_pairs", "pair_to_row", "h",
+             "h_shared", "out"]
+    for i, x in enumerate(xs):
+        lg = M.moe_router_logits(x, t["w_router"], cfg.k, cfg.score, wsg, n_group=ng, topk_group=tg)
+        r = M.moe_topk_gateup_shared(lg, x, cfg.k, w.experts, w.shared, cfg.score, cfg.renormalize,
+                                     cfg.routed_scaling, t["logit_bias"], t["select_bias"], wsg is not None,
+                                     n_group=ng, topk_group=tg)
+        ids, tw, sg, offs, sp, p2r, h, hs = r
+        o = M.moe_expert_down_combine(w.experts, w.shared, h, hs, ids, tw, p2r, sg)
+        ref = (lg, ids, tw, sg, offs, sp, p2r, h, hs, o)
+        got = M.moe_decode_step(x, t["w_router"], cfg.k, w.experts, w.shared, cfg.score, cfg.renormalize,
+                                cfg.routed_scaling, t["logit_bias"], t["select_bias"], wsg, sync=sync, n_group=ng,
+                                topk_group=tg)
+        torch.cuda.synchronize()
+        for nm, a, b in zip(names, got, ref):
+            if b is None:
+                assert a is None, nm
+                continue
+            np.testing.assert_array_equal(to_np(a), to_np(b), err_msg=f"{name} input {i} {nm}")
+    sv = to_np(sync)
+    assert sv[1] == 0, f"{name}: a hand-off wait gave up"
+    assert sv[0] == (len(xs) if single else 0), (name, sv[0])
+    say(f"  {name}: {'single launch' if single else 'three calls'}, every output equal")
+
+
+def test_decode_step_layer_matches_oracle_after_other_steps(dev, M):
+    """A decode layer whose sync buffer has served other layers' steps (the launch count is
+    well past zero, with a different grid of experts in between) still matches the oracle."""
+    cfg = LAYER_CASES["tiny_fused_gated"]
+    other = DECODE_STEP_CASES["tiny_4tok_sigmoid"][0]
+    t, inp = build(cfg, dev)
+    t2, _ = build(other, dev)
+    layer = M.MoELayer(layer_weights(cfg, t), cfg.T, dev)
+    layer2 = M.MoELayer(layer_weights(other, t2), other.T, dev)
+    assert layer.single and layer2.single
+    layer2.sync = layer.sync                              # one stream, one sync buffer
+    for _ in range(5):
+        layer2.forward(t2["x"])
+        layer.forward(t["x"])
+    out = layer.forward(t["x"])
+    torch.cuda.synchronize()
+    ge, gs = host_expert_getter(cfg)
+    ref = OL.layer(cfg, inp, ge, gs)
+    np.testing.assert_array_equal(to_np(layer.ids), ref.routing.ids)
+    assert_close(to_np(out), ref.out, "decode step after other steps")
+    sv = to_np(layer.sync)
+    assert sv[0] == 11 and sv[1] == 0, sv[:2]
+
+
 def test_down_combine_drops_invalid_pairs(dev, M):
     """A pair with id -1 or row -1 adds nothing; the rest is the weighted sum."""
     cfg = LAYER_CASES["tiny_fused_gated"]
@@ -704,6 +783,11 @@ def test_decode_layer_full_size(dev, M):
     first = to_np(out).copy()
     out2 = to_np(layer.forward(bf16_tensor(inp.x, dev)))
     np.testing.assert_array_equal(out2, first)
+    # the single launch and the three calls give the same bits
+    assert layer.single
+    three = M.MoELayer(layer.w, cfg.T, dev, single_launch=False)
+    out3 = to_np(three.forward(bf16_tensor(inp.x, dev)))
+    np.testing.assert_array_equal(out3, first)
 
 
 def test_latent_layer_full_size(dev, M):
