@@ -7,8 +7,12 @@ A step is one pass of the whole layer (router, top-k, permutation, routed expert
 shared expert, combine; LatentMoE projections where the workload has them) over one
 batch of seeded synthetic tokens, with all weights resident in HBM.  Steps rotate over
 four independently generated layer instances and sixteen token batches, so no step finds
-the previous step's weights in the 256 MB last-level cache.  Each step slot is captured
-once as a HIP graph; the timed region replays K graphs back to back between two events.
+the previous step's weights in the 256 MB last-level cache.  The sixteen step slots are
+captured in order as one HIP graph (a model's forward pass holds its layers in one graph),
+and each slot also as a graph of its own; the timed region replays K steps back to back
+between two events -- whole sixteen-step graphs, then single-step graphs for the rest.
+The same K steps with one graph launch per step are reported beside it
+(`ms_per_step_one_graph_per_step`).
 
 The headline workload (`value`, `ms_per_step`) is the one-token decode layer.  By default
 the same run also times the two 512-token prefill workloads on the same expert instances
@@ -128,12 +132,6 @@ def dominant_kernel(cfg, single=False):
     return r"gemv_kernel<\d+, \d+, \d+, true, true>"
 
 
-def single_launch(cfg):
-    """Whether the layer runs a step of this workload as one moe_decode_step launch (the
-    decode-sized fused form over MXFP4 weights with bf16 activations and no latent width)."""
-    return cfg.T <= 4 and cfg.act == "float" and cfg.wfmt == "mxfp4" and not cfg.latent and cfg.E <= 512
-
-
 def down_kernel(cfg, fused, combined=None):
     """Name pattern of the routed down kernel of a workload."""
     if fused if combined is None else combined:
@@ -174,7 +172,7 @@ def parse_traffic(cfg, fetch_dir, write_dir):
     import csv
     import glob
     import re
-    single = single_launch(cfg)
+    single = False
 
     def per_dispatch(d, counter):
         rows = []
@@ -268,7 +266,7 @@ def cpu_baseline(cfg, steps):
 
 # ------------------------------------------------------------------ GPU runs
 
-def make_layers(M, sdev, cfg, insts, dev):
+def make_layers(M, sdev, cfg, insts, dev, single_launch=False):
     """One MoELayer per instance, on the instance's shared expert stacks."""
     layers = []
     for inst, (ex, sh) in enumerate(insts):
@@ -279,7 +277,7 @@ def make_layers(M, sdev, cfg, insts, dev):
                            shared=M.ExpertWeights.from_arrays(t["shared"]) if t["shared"] is not None else None,
                            w_shared_gate=t["w_shared_gate"] if cfg.shared == "gated" else None,
                            p_down=t["p_down"], p_up=t["p_up"])
-        layers.append(M.MoELayer(w, cfg.T, dev))
+        layers.append(M.MoELayer(w, cfg.T, dev, single_launch=single_launch))
     return layers
 
 
@@ -295,8 +293,10 @@ def run_workload(torch, sdev, cfg, layers, NB, steps, warmup, use_graphs, dev, t
         L, x = slot(j)
         L.forward(x)
     torch.cuda.synchronize()
-    graphs = None
+    graphs = seq = None
     if use_graphs:
+        # one graph per step slot, and one graph of all S slots in order (a model's forward
+        # pass holds its layers' steps in one graph, so a step does not pay a graph launch)
         graphs = []
         stream = torch.cuda.Stream()
         stream.wait_stream(torch.cuda.current_stream())
@@ -307,6 +307,11 @@ def run_workload(torch, sdev, cfg, layers, NB, steps, warmup, use_graphs, dev, t
                 with torch.cuda.graph(g, stream=stream):
                     L.forward(x)
                 graphs.append(g)
+            seq = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(seq, stream=stream):
+                for j in range(S):
+                    L, x = slot(j)
+                    L.forward(x)
         torch.cuda.current_stream().wait_stream(stream)
         torch.cuda.synchronize()
 
@@ -316,6 +321,17 @@ def run_workload(torch, sdev, cfg, layers, NB, steps, warmup, use_graphs, dev, t
         else:
             L, x = slot(s)
             L.forward(x)
+
+    def run_steps(n):
+        """n steps from slot 0: whole S-step graphs, then single-step graphs for the rest."""
+        if seq is None:
+            for s in range(n):
+                step(s)
+            return
+        for _ in range(n // S):
+            seq.replay()
+        for s in range(n % S):
+            graphs[s].replay()
 
     for s in range(warmup):
         step(s)
@@ -327,11 +343,19 @@ def run_workload(torch, sdev, cfg, layers, NB, steps, warmup, use_graphs, dev, t
         return None
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
-    for s in range(steps):
-        step(warmup + s)
+    run_steps(steps)
     ev1.record()
     torch.cuda.synchronize()
     ms_per_step = ev0.elapsed_time(ev1) / steps
+    ms_one_graph = None
+    if graphs is not None:
+        # the same steps, one graph launch per step
+        ev0.record()
+        for s in range(steps):
+            step(s)
+        ev1.record()
+        torch.cuda.synchronize()
+        ms_one_graph = ev0.elapsed_time(ev1) / steps
 
     # distinct routed experts touched per slot (read back after a step of that slot)
     D_slot = []
@@ -341,7 +365,7 @@ def run_workload(torch, sdev, cfg, layers, NB, steps, warmup, use_graphs, dev, t
         torch.cuda.synchronize()
         offs = L.offs.cpu()
         D_slot.append(int(((offs[1:] - offs[:-1]) > 0).sum()))
-    D_steps = [D_slot[(warmup + s) % S] for s in range(steps)]
+    D_steps = [D_slot[s % S] for s in range(steps)]
 
     # per-kernel durations: events on the step's stream around the routed gate/up and down
     # calls, over the same slots; a block of matrix products queued first keeps the GPU busy,
@@ -366,8 +390,11 @@ def run_workload(torch, sdev, cfg, layers, NB, steps, warmup, use_graphs, dev, t
     D_ev = [D_slot[(warmup + s) % S] for s in range(n)]
     # launches of each step kernel, in order: eager warm-up (one per slot), warm-up replays,
     # timed replays, the per-slot expert count, the instrumented pass
-    phases = [["warm", S], ["warm_replay", warmup], ["timed", steps], ["count", S], ["events", n]]
-    return dict(ms_per_step=ms_per_step, D_steps=D_steps, D_ev=D_ev, gu_us=gu_us, dn_us=dn_us, st_us=st_us,
+    phases = [["warm", S], ["warm_replay", warmup], ["timed", steps]]
+    if graphs is not None:
+        phases.append(["one_graph_per_step", steps])
+    phases += [["count", S], ["events", n]]
+    return dict(ms_per_step=ms_per_step, ms_one_graph=ms_one_graph, D_steps=D_steps, D_ev=D_ev, gu_us=gu_us, dn_us=dn_us, st_us=st_us,
                 single=single, launches=n, graphs=graphs is not None, slots=S, phases=phases)
 
 
@@ -570,7 +597,21 @@ def main():
         return
     log(f"[bench] {cfg.name}: {args.steps} steps, {r['ms_per_step'] * 1e3:.2f} us/step")
     kernels = kernel_entries(cfg, fused, r, layers[0].down_combined)
-    del layers
+    alt = None
+    if fused and not args.traffic_run:
+        # the decode step's other form (one launch, or its three calls) on the same steps
+        single = not layers[0].single
+        del layers
+        la = make_layers(M, sdev, cfg, instances(cfg), dev, single_launch=single)
+        ra = run_workload(torch, sdev, cfg, la, NB, args.steps, args.warmup, not args.no_graph, dev)
+        alt = dict(form="single launch (moe_decode_step)" if single else "three calls",
+                   ms_per_step=round(ra["ms_per_step"], 5),
+                   ms_per_step_one_graph_per_step=round(ra["ms_one_graph"], 5) if ra["ms_one_graph"] else None,
+                   kernels=kernel_entries(cfg, fused, ra, True))
+        log(f"[bench] {cfg.name}, {alt['form']}: {ra['ms_per_step'] * 1e3:.2f} us/step")
+        del la
+    else:
+        del layers
 
     prefill = {}
     for pc in extra:
@@ -604,6 +645,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(r["ms_per_step"], 5),
+        "ms_per_step_one_graph_per_step": round(r["ms_one_graph"], 5) if r["ms_one_graph"] else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -614,8 +656,11 @@ def main():
         "config": {"workload": cfg.name, "T": cfg.T, "H": cfg.H, "d_model": cfg.d_model, "I": cfg.I, "E": cfg.E,
                    "k": cfg.k, "score": cfg.score, "weights": cfg.wfmt, "activations": cfg.act,
                    "shared": cfg.shared, "latent": cfg.latent, "arith": arith_of(cfg), "instances": R,
-                   "token_batches": NB, "graphs": r["graphs"]},
+                   "token_batches": NB, "graphs": r["graphs"],
+                   "steps_per_graph": r["slots"] if r["graphs"] else None},
         "layer": workload_summary(cfg, fused, r),
+        "decode_form": "single launch (moe_decode_step)" if r.get("single") else "three calls",
+        "other_decode_form": alt,
         "roofline": roof,
         "kernels": kernels,
         "prefill": prefill,

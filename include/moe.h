@@ -298,8 +298,8 @@ moe_status moe_expert_down_combine(const moe_expert_weights *w, const moe_expert
  *   sync: caller-owned device memory of moe_decode_step_sync_bytes() bytes, zero-filled
  *   once before its first use and then left to the library: word 0 counts the launches
  *   that used it, word 1 is an error word (nonzero after a launch whose hand-off waited
- *   past its bound, tens of milliseconds; that launch's results are undefined), the rest are
- *   per-workgroup flags.  A sync buffer serves one stream: launches that use the same
+ *   past its bound, tens of milliseconds; that launch's results are undefined), the rest
+ *   holds per-workgroup flags and the launch's logits tagged with its count.  A sync buffer serves one stream: launches that use the same
  *   buffer must not overlap, and a launch needs every compute unit for a workgroup, so it
  *   should not share the GPU with another such launch.
  *   The single launch takes MXFP4 weights, 1 <= T <= 4, T*k <= 64, E <= 512, bf16 x rows

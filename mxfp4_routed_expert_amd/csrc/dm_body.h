@@ -54,8 +54,9 @@ static __device__ __align__(16) uint8_t g_dm_zero[16];   // read-only zeros (loa
 
 // STEP: the down phase of the single-launch decode step (decode_step_kernel): the slots'
 // experts, rows and weights come from the workgroup's own routing in LDS, the weight loads
-// of the first two steps are issued before the h rows are read, and with `wait_h` wave 0
-// first waits for every workgroup's h rows (step_wait) while those loads are in flight.
+// of the ring's four steps are issued before the h rows are read (at device scope,
+// step_get4), and with `wait_h` wave 0 first waits for every workgroup's h rows
+// (step_wait) while those loads are in flight.
 template <bool STEP>
 MOE_DEV void dm_body(const DownCombineParams &p, int bx, int t, const StepCtx *sc, bool wait_h) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -240,21 +241,28 @@ MOE_DEV void dm_body(const DownCombineParams &p, int bx, int t, const StepCtx *s
             const int i = group_of(min(tid + u * kDmThreads, total - 1));
             const int j = i / per, v = min(i - j * per, I / 8 - 1);
             const float *row = j < kk ? p.h + (size_t)max(s_r[j], 0) * I : p.hs + (size_t)t * I;
-            const f32x4 *src = (const f32x4 *)(row + (size_t)v * 8);
-            va[u] = src[0];
-            vb[u] = src[1];
+            if constexpr (STEP) {
+                va[u] = step_get4(row + (size_t)v * 8);
+                vb[u] = step_get4(row + (size_t)v * 8 + 4);
+            } else {
+                const f32x4 *src = (const f32x4 *)(row + (size_t)v * 8);
+                va[u] = src[0];
+                vb[u] = src[1];
+            }
         }
     };
     u32x4 wv[kDmDepth][2];
     uint8_t sv[kDmDepth][2];  // (the loaded bytes as they are: a value combined from two loads waits for both)
     static_assert(kDmDepth == 4, "the prologue issues two steps before the planes and two after");
     if constexpr (STEP) {
-        // the weights do not depend on h: their first loads go out before the wait
+        // the weights do not depend on h: the ring's loads go out before the wait
         setup();
         fill(std::integral_constant<int, 0>{}, wv[0], sv[0]);
         fill(std::integral_constant<int, 1>{}, wv[1], sv[1]);
+        fill(std::integral_constant<int, 2>{}, wv[2], sv[2]);
+        fill(std::integral_constant<int, 3>{}, wv[3], sv[3]);
         if (wait_h) {
-            if (wave == 0) step_wait(sc->sync, sc->nwg, sc->target_h);
+            if (wave == 0) step_wait(sc->sync, sc->nwg, sc->tag);
             asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
         }
         load_h();
@@ -288,8 +296,10 @@ MOE_DEV void dm_body(const DownCombineParams &p, int bx, int t, const StepCtx *s
     }
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");     // this wave's plane writes are in LDS
     if (lane == 0) atomicAdd(&s_ready, 1);
-    fill(std::integral_constant<int, 2>{}, wv[2], sv[2]);
-    fill(std::integral_constant<int, 3>{}, wv[3], sv[3]);
+    if constexpr (!STEP) {
+        fill(std::integral_constant<int, 2>{}, wv[2], sv[2]);
+        fill(std::integral_constant<int, 3>{}, wv[3], sv[3]);
+    }
     // every wave counts itself once, right after its writes, so the wait ends; the bound only
     // keeps a fault elsewhere from turning into a hang
     // (read through an LDS pointer: a generic volatile read is a flat load, and its wait

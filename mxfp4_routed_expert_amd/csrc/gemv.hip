@@ -543,9 +543,9 @@ MOE_DEV void lds_wait_at_least(int *ctr, int v) {
 // back.
 //
 // STEP (with ROUTE): the gate/up phase of the single-launch decode step (decode_step_kernel):
-// the routing waves first wait for every workgroup's logits (step_wait), the workgroup's
-// routing is also kept in sc->lds for the down phase, and every wave waits for its h stores
-// before it returns.
+// the routing waves first collect every workgroup's logits (step_get_logits), the
+// workgroup's routing is also kept in sc->lds for the down phase, h is stored at device
+// scope (step_put) and every wave waits for its h stores before it returns.
 template <int FMT, int ACT, int MAXM, bool PAIR, bool ROUTE, bool STEP>
 MOE_DEV void flat_body(const GemvParams &p, const StepCtx *sc) {
     extern __shared__ __align__(16) unsigned char smem[];
@@ -603,9 +603,16 @@ MOE_DEV void flat_body(const GemvParams &p, const StepCtx *sc) {
             if (lane == 0) atomicAdd(&s_dma, 1);
         }
         if (wave < T) {
-            if constexpr (STEP) step_wait(sc->sync, sc->nwg, sc->target_logits);
+            // the selection is on every workgroup's critical path: it goes first at issue
+            __builtin_amdgcn_s_setprio(3);
+            const float *lt = ra.logits + (size_t)wave * ra.rows;
+            if constexpr (STEP) {
+                step_get_logits(sc->sync, sc->tag, wave, ra.rows, sc->lds->lt[wave]);
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                lt = sc->lds->lt[wave];
+            }
             double *gk = (double *)(smem + (size_t)n_act * rs) + (size_t)wave * E;   // group-limited keys
-            const TopkLane r = topk_select<kFlatTopkNK>(ra.logits + (size_t)wave * ra.rows, E, kk, ra.score, ra.renorm,
+            const TopkLane r = topk_select<kFlatTopkNK>(lt, E, kk, ra.score, ra.renorm,
                                                         ra.scaling, ra.lbias, ra.sbias, ra.has_sg, gk, ra.n_group,
                                                         ra.topk_group);
             if (lane < kk) {
@@ -625,6 +632,7 @@ MOE_DEV void flat_body(const GemvParams &p, const StepCtx *sc) {
             }
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // s_sid holds this token's experts
             if (lane == 0) atomicAdd(&s_topk, 1);
+            if (wave != 0) __builtin_amdgcn_s_setprio(0);        // (wave 0 builds the table next)
         }
     }
 
@@ -729,6 +737,7 @@ MOE_DEV void flat_body(const GemvParams &p, const StepCtx *sc) {
         if constexpr (ROUTE) {
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // the table is in LDS
             if (lane == 0) atomicAdd(&s_tab, 1);
+            __builtin_amdgcn_s_setprio(0);
         }
     } else if (!ROUTE && wave == 1) {
         // activation row of each routed row (or identity row): -1 when out of range
@@ -832,11 +841,14 @@ MOE_DEV void flat_body(const GemvParams &p, const StepCtx *sc) {
                 if (m < f.mc) {
                     float v = tok[m] >= 0 ? acc[m] : 0.0f;
                     if (f.sh) {
-                        sout[(size_t)(f.m0 + m) * f.N + f.n] = v;
+                        float *dst = sout + (size_t)(f.m0 + m) * f.N + f.n;
+                        if constexpr (STEP) step_put(dst, v);
+                        else *dst = v;
                     } else {
                         const size_t o = (size_t)(f.r0 + f.m0 + m) * f.N + f.n;
                         if (residual) v += residual[o];
-                        out[o] = v;
+                        if constexpr (STEP) step_put(out + o, v);
+                        else out[o] = v;
                     }
                 }
             }
@@ -1452,9 +1464,9 @@ moe_status gemv_launch(int fmt, int act, bool pair, GemvParams p, int slots, int
 // step_sync.h:
 //   1. router logits: rows b, b + nwg, ... of the router (and the shared-gate row) by
 //      groups of four waves, each wave a quarter of H (router_quarter: the same sums as
-//      router_logits_kernel);
+//      router_logits_kernel), stored as tagged words;
 //   2. top-k and gate/up (flat_body<..., ROUTE, STEP>): the shared expert's gate/up passes
-//      do not depend on the routing and run while the routing waves wait for every
+//      do not depend on the routing and run while the routing waves collect every
 //      workgroup's logits; then the routed passes;
 //   3. down and combine (dm_body<true>): each workgroup issues its first weight loads, then
 //      waits for every workgroup's h rows, over the down-combine's (row range, token) items
@@ -1472,8 +1484,7 @@ __global__ __launch_bounds__(kFlatThreads) void decode_step_kernel(const StepPar
     const uint32_t c = __builtin_amdgcn_readfirstlane(step_launch_count(sp.sync));
     StepCtx sc;
     sc.sync = sp.sync;
-    sc.target_logits = 2u * c + 1u;
-    sc.target_h = 2u * c + 2u;
+    sc.tag = c + 1u;
     sc.nwg = nwg;
     sc.lds = &s_route;
 
@@ -1493,18 +1504,18 @@ __global__ __launch_bounds__(kFlatThreads) void decode_step_kernel(const StepPar
             }
         }
         __syncthreads();
-        if (quarter == 0 && row < sp.rows && lane < sp.T)
-            sp.logits[(size_t)lane * sp.rows + row] = router_finish(s_rpart[grp], lane);
+        if (quarter == 0 && row < sp.rows && lane < sp.T) {
+            const float v = router_finish(s_rpart[grp], lane);
+            sp.logits[(size_t)lane * sp.rows + row] = v;
+            step_put_logit(sp.sync, sc.tag, lane, row, v);
+        }
         __syncthreads();
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");      // this wave's logits are stored
-    __syncthreads();
-    if (threadIdx.x == 0) step_arrive(sp.sync, sc.target_logits);
 
     // 2. top-k, routed and shared gate/up (every wave returns with its h rows stored)
     flat_body<kFmtMXFP4, kActBF16, MAXM, true, true, true>(sp.gu, &sc);
     __syncthreads();
-    if (threadIdx.x == 0) step_arrive(sp.sync, sc.target_h);
+    if (threadIdx.x == 0) step_flag(sp.sync, sc.tag);
 
     // 3. down and combine
     const int nitems = sp.nx * sp.T;
@@ -1522,7 +1533,8 @@ bool decode_step_launch(StepParams sp, hipStream_t stream, moe_status *st) {
     const dim3 dgrid = down_combine_shape(kFmtMXFP4, sp.dc, &lds_dc, &U);
     sp.nx = (int)dgrid.x;
     const int nwg = device_cu_count();
-    if (nwg > kSyncMaxWG || sp.T > kRouterTB || sp.H % 32 != 0 || sp.T * sp.gu.k > 64 || sp.T > 4) return false;
+    if (nwg > kSyncMaxWG || sp.T > kSyncMaxT || sp.rows > kSyncRowStride || sp.H % 32 != 0 || sp.T * sp.gu.k > 64)
+        return false;
     const size_t lds = std::max(lds_gu, lds_dc);
     using StepFn = void (*)(const StepParams);
     StepFn fn = maxm == 1 ? decode_step_kernel<1> : (maxm == 2 ? decode_step_kernel<2> : decode_step_kernel<4>);

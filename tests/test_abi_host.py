@@ -263,7 +263,8 @@ def _decode_step(d, w, sync=DUMMY, shared=None, wsg=None, sg=None):
 
 
 def test_decode_step_checks():
-    assert lib.moe_decode_step_sync_bytes() == 4 * (64 + 1024)
+    # counters, 1024 workgroup flags, tagged logits of 4 tokens x 520 rows (64-bit words)
+    assert lib.moe_decode_step_sync_bytes() == 4 * (64 + 1024 + 2 * 4 * 520)
     w = _weights()
     # a sync buffer is required
     assert _decode_step(_desc(), w, sync=None) == B.MOE_ERR_INVALID_ARG and "sync" in B.last_error()

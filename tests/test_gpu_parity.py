@@ -393,17 +393,21 @@ LAYER_CASES = {
 }
 
 
-GRAPH_CASES = ["tiny_gated_shared", "tiny_fused_gated", "tiny_latent", "tiny_sigmoid_fp8", "prefill_gated_shared"]
+GRAPH_CASES = ["tiny_gated_shared", "tiny_fused_gated", "tiny_fused_gated/single", "tiny_latent",
+               "tiny_sigmoid_fp8", "prefill_gated_shared"]
 
 
 @pytest.mark.parametrize("name", GRAPH_CASES)
 def test_graph_replays_match_eager(dev, M, name):
     """One layer step captured as a HIP graph (with the shared expert's second stream where the
-    layer uses one) and replayed three times over three inputs, with eager copies and
-    synchronisations between the replays: every replay gives the eager output bit for bit."""
-    cfg = LAYER_CASES[name]
+    layer uses one; "/single": the single-launch decode step) and replayed three times over
+    three inputs, with eager copies and synchronisations between the replays: every replay
+    gives the eager output bit for bit."""
+    cfg = LAYER_CASES[name.split("/")[0]]
     t, _ = build(cfg, dev)
-    layer = M.MoELayer(layer_weights(cfg, t), cfg.T, dev)
+    layer = M.MoELayer(layer_weights(cfg, t), cfg.T, dev, single_launch=name.endswith("/single"))
+    if name.endswith("/single"):
+        assert layer.single
     x0 = t["x"]
     xs = [x0, (x0.float() * 0.5).to(torch.bfloat16), x0.roll(1, dims=1).contiguous()]
     eager = [layer.forward(x).clone() for x in xs]
@@ -579,8 +583,8 @@ def test_decode_step_layer_matches_oracle_after_other_steps(dev, M):
     other = DECODE_STEP_CASES["tiny_4tok_sigmoid"][0]
     t, inp = build(cfg, dev)
     t2, _ = build(other, dev)
-    layer = M.MoELayer(layer_weights(cfg, t), cfg.T, dev)
-    layer2 = M.MoELayer(layer_weights(other, t2), other.T, dev)
+    layer = M.MoELayer(layer_weights(cfg, t), cfg.T, dev, single_launch=True)
+    layer2 = M.MoELayer(layer_weights(other, t2), other.T, dev, single_launch=True)
     assert layer.single and layer2.single
     layer2.sync = layer.sync                              # one stream, one sync buffer
     for _ in range(5):
@@ -784,10 +788,11 @@ def test_decode_layer_full_size(dev, M):
     out2 = to_np(layer.forward(bf16_tensor(inp.x, dev)))
     np.testing.assert_array_equal(out2, first)
     # the single launch and the three calls give the same bits
-    assert layer.single
-    three = M.MoELayer(layer.w, cfg.T, dev, single_launch=False)
-    out3 = to_np(three.forward(bf16_tensor(inp.x, dev)))
-    np.testing.assert_array_equal(out3, first)
+    assert layer.fused and not layer.single
+    one = M.MoELayer(layer.w, cfg.T, dev, single_launch=True)
+    assert one.single
+    out1 = to_np(one.forward(bf16_tensor(inp.x, dev)))
+    np.testing.assert_array_equal(out1, first)
 
 
 def test_latent_layer_full_size(dev, M):

@@ -11,8 +11,9 @@
   * an expert that no token selects changes nothing: overwriting its weights leaves the
     output bit for bit the same, while overwriting a selected expert changes it.
 
-The cases cover the fused decode calls, the decode GEMV over FP8 weights, the per-slot
-GEMV in its wide form, the bf16 matrix-core prefill and the FP4 matrix-core prefill.
+The cases cover the fused decode calls (three calls and the single launch), the decode GEMV
+over FP8 weights, the per-slot GEMV in its wide form, the bf16 matrix-core prefill and the
+FP4 matrix-core prefill.
 """
 from __future__ import annotations
 
@@ -51,6 +52,8 @@ def tiny(**kw):
 CASES = {
     # fused decode: router logits, gate/up with routing in its prologue, down-combine
     "decode_fused": (tiny(name="pd", wtag=110, T=4, k=3, E=16, shared="gated", shared_K=256, shared_I=128), 1),
+    # the same decode step as one launch (moe_decode_step)
+    "decode_single": (tiny(name="pd", wtag=110, T=4, k=3, E=16, shared="gated", shared_K=256, shared_I=128), 1),
     # decode GEMV over FP8 weights with sigmoid scoring, staged calls
     "decode_fp8": (tiny(name="pf", wtag=111, wfmt="fp8b128", score="sigmoid", select_bias_std=0.01, I=256, T=7, k=3,
                         E=24, shared="ungated", shared_K=256, shared_I=128), 1),
@@ -67,8 +70,17 @@ CASES = {
 }
 
 
-def _step(M, cfg, t, x):
-    layer = M.MoELayer(layer_weights(cfg, t), x.shape[0], x.device)
+SINGLE = {"decode_single"}                 # cases that run the single-launch decode step
+
+
+def _layer(M, cfg, t, T, dev, name):
+    layer = M.MoELayer(layer_weights(cfg, t), T, dev, single_launch=name in SINGLE)
+    assert layer.single == (name in SINGLE and layer.fused)
+    return layer
+
+
+def _step(M, cfg, t, x, name):
+    layer = _layer(M, cfg, t, x.shape[0], x.device, name)
     out = layer.forward(x).clone()
     torch.cuda.synchronize()
     return out, to_np(layer.ids), to_np(layer.topk_w)
@@ -78,7 +90,7 @@ def _step(M, cfg, t, x):
 def test_two_runs_give_the_same_bits(dev, M, name):
     cfg, _ = CASES[name]
     t, _ = build(cfg, dev)
-    layer = M.MoELayer(layer_weights(cfg, t), cfg.T, dev)
+    layer = _layer(M, cfg, t, cfg.T, dev, name)
     a = layer.forward(t["x"]).clone()
     b = layer.forward(t["x"]).clone()
     torch.cuda.synchronize()
@@ -91,8 +103,8 @@ def test_token_permutation_permutes_outputs(dev, M, name):
     t, _ = build(cfg, dev)
     perm = np.random.default_rng(7).permutation(cfg.T)
     pt = torch.from_numpy(perm).to(dev)
-    out, ids, tw = _step(M, cfg, t, t["x"])
-    out_p, ids_p, tw_p = _step(M, cfg, t, t["x"][pt].contiguous())
+    out, ids, tw = _step(M, cfg, t, t["x"], name)
+    out_p, ids_p, tw_p = _step(M, cfg, t, t["x"][pt].contiguous(), name)
     np.testing.assert_array_equal(ids_p, ids[perm])
     np.testing.assert_array_equal(tw_p, tw[perm])
     assert torch.equal(out_p, out[pt]), name
@@ -102,11 +114,11 @@ def test_token_permutation_permutes_outputs(dev, M, name):
 def test_batch_equals_its_parts(dev, M, name):
     cfg, part = CASES[name]
     t, _ = build(cfg, dev)
-    out, ids, tw = _step(M, cfg, t, t["x"])
+    out, ids, tw = _step(M, cfg, t, t["x"], name)
     outs, idss, tws = [], [], []
     for s in range(0, cfg.T, part):
         cs = dataclasses.replace(cfg, T=min(part, cfg.T - s))
-        o, i, w = _step(M, cs, t, t["x"][s:s + part].contiguous())
+        o, i, w = _step(M, cs, t, t["x"][s:s + part].contiguous(), name)
         outs.append(to_np(o))
         idss.append(i)
         tws.append(w)
@@ -136,15 +148,15 @@ def _with_expert_overwritten(ex, e):
 def test_unrouted_expert_changes_nothing(dev, M, name):
     cfg, _ = CASES[name]
     t, _ = build(cfg, dev)
-    out, ids, _ = _step(M, cfg, t, t["x"])
+    out, ids, _ = _step(M, cfg, t, t["x"], name)
     used = set(ids.reshape(-1).tolist())
     idle = [e for e in range(cfg.E) if e not in used]
     assert idle, f"{name}: every expert is selected; the case needs more experts"
     t_idle = dict(t, experts=_with_expert_overwritten(t["experts"], idle[0]))
-    out_idle, ids_idle, _ = _step(M, cfg, t_idle, t["x"])
+    out_idle, ids_idle, _ = _step(M, cfg, t_idle, t["x"], name)
     np.testing.assert_array_equal(ids_idle, ids)
     assert torch.equal(out_idle, out), name
     # control: the same overwrite of a selected expert does change the output
     t_used = dict(t, experts=_with_expert_overwritten(t["experts"], int(ids[0, 0])))
-    out_used, _, _ = _step(M, cfg, t_used, t["x"])
+    out_used, _, _ = _step(M, cfg, t_used, t["x"], name)
     assert not torch.equal(out_used, out), name
