@@ -94,6 +94,39 @@ MOE_DEV void sort_desc(uint64_t (&key)[N], int (&idx)[N], double (&base)[N]) {
     }
 }
 
+// Softmax scores without a logit bias select on float32 logits, whose order a 32-bit key
+// carries exactly (NaN -> 0, below every number; -0 == +0).  Packed with the bitwise NOT of
+// the expert index in the low half, one 64-bit word orders (larger logit, then lower expert)
+// and holds both, so the sort and the k rounds move one value per entry instead of a key, an
+// index and a float64 base value.  A word with a zero high half is never selected.
+MOE_DEV uint32_t order_key32(float v) {
+    if (v != v) return 0u;
+    const uint32_t b = __float_as_uint(v + 0.0f);                         // -0 -> +0
+    return b ^ ((b >> 31) ? 0xffffffffu : 0x80000000u);
+}
+MOE_DEV float key32_value(uint32_t k) {
+    return __uint_as_float((k >> 31) ? (k ^ 0x80000000u) : ~k);
+}
+
+template <int N>
+MOE_DEV void sort_desc_packed(uint64_t (&key)[N]) {
+#pragma unroll
+    for (int size = 2; size <= N; size <<= 1) {
+#pragma unroll
+        for (int stride = size / 2; stride > 0; stride >>= 1) {
+#pragma unroll
+            for (int i = 0; i < N; ++i) {
+                const int p = i ^ stride;
+                if (p <= i) continue;
+                const bool swap = ((i & size) == 0) ? key[i] < key[p] : key[i] > key[p];
+                const uint64_t ka = key[i], kb = key[p];
+                key[i] = swap ? kb : ka;
+                key[p] = swap ? ka : kb;
+            }
+        }
+    }
+}
+
 // One token's selection in one wave.  Lane l holds the selection keys of experts l, l+64,
 // ... (NK per lane, E <= 64 * NK) in registers; each of the k rounds takes the wave-wide best
 // of the lanes' best untaken keys.  NaN keys are never selected.  lt: the token's logits
@@ -185,7 +218,33 @@ MOE_DEV TopkLane topk_select(const float *lt, int E, int k, int score, int renor
     for (int i = 0; i < NK; ++i) braw[i] = base[i];
     int my_e = -1;
     double l = 0.0;              // lane j < k: base value of the j-th selected expert
-    if constexpr (NK <= kSortNK) {
+    const bool packed = score == MOE_SCORE_SOFTMAX && !lbias && n_group <= 1;
+    if (NK <= kSortNK && packed) {
+        // keys from the loaded float logits (the same order as order_key of their float64 values)
+        uint64_t pk[NK];
+#pragma unroll
+        for (int i = 0; i < NK; ++i) {
+            const int e = lane + 64 * i;
+            const uint32_t k32 = e < E ? order_key32(lv[i]) : 0u;
+            pk[i] = k32 ? ((uint64_t)k32 << 32) | (uint32_t)~e : 0ull;
+        }
+        sort_desc_packed<NK>(pk);
+        for (int j = 0; j < k; ++j) {
+            // (low halves are distinct, so the wave-wide maximum is one lane's word)
+            const int L = wave_best_lane(pk[0], 0);
+            const uint32_t wh = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(pk[0] >> 32), L);
+            const uint32_t wl = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)pk[0], L);
+            if (lane == j && wh != 0u) {
+                my_e = (int)~wl;
+                l = (double)key32_value(wh);
+            }
+            if (lane == L) {     // the winner drops its first entry
+#pragma unroll
+                for (int i = 0; i + 1 < NK; ++i) pk[i] = pk[i + 1];
+                pk[NK - 1] = 0ull;
+            }
+        }
+    } else if constexpr (NK <= kSortNK) {
         int idx[NK];
 #pragma unroll
         for (int i = 0; i < NK; ++i) idx[i] = lane + 64 * i;

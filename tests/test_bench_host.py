@@ -91,3 +91,16 @@ def test_latent_down_combine_bytes():
     row = 2048 * 17 // 32                             # one MXFP4 down row over I = 2048: 1088 B
     assert a["bytes"] == 31 * 2048 * row + 32 * 2048 * 4 + 4 * 2048 * 4   # no shared rows: it is added after P_u
     assert bench.down_kernel(cfg, False, True) == r"down_combine_mfma_kernel"
+
+
+def test_single_launch_step_entry_uses_the_layer_bytes():
+    """The single-launch decode step's roofline divides the whole layer's algorithmic bytes
+    (router, ten experts, the shared expert, x in and out once) by the launch time."""
+    cfg = synth.get("qwen38max_decode")
+    r = dict(single=True, D_ev=[10, 10], st_us=76.2, launches=2, phases=[["timed", 2]])
+    (e,) = bench.kernel_entries(cfg, True, r)
+    layer = 11 * 27_052_032 + 512 * 7168 * 2 + 7168 * 2 + 7168 * 2 + 7168 * 4
+    assert layer == 304_969_728
+    assert e["bytes_per_launch"] == layer and e["bound"] == "hbm"
+    assert abs(e["achieved"] - layer / 76.2e-6 / 1e9) < 0.1
+    assert re.search(e["kernel"], "void moe::decode_step_kernel<1>(moe::StepParams)")

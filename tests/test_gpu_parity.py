@@ -167,6 +167,40 @@ def test_route_matches_oracle(dev, M, name):
         assert_close(to_np(sg), r.shared_gate, f"{name} shared_gate")
 
 
+def test_route_ties_and_zero_logits(dev, M):
+    """Exact ties (identical router rows) and a zero row, through the route kernel and the
+    gate/up prologue: ids as the oracle's (larger key first, a tie to the lower expert),
+    softmax and sigmoid with a selection bias."""
+    for score in ("softmax", "sigmoid"):
+        cfg = tiny(name="tie", wtag=107, E=16, k=6, T=4, score=score, shared="gated", shared_K=256, shared_I=128,
+                   select_bias_std=0.01 if score == "sigmoid" else 0.0)
+        inp = synth.layer_inputs_np(cfg, 0)
+        W = inp.w_router.copy()             # bf16 bits
+        for r in (5, 9, 12):
+            W[r] = W[2]                     # four experts with the same logit for every token
+        W[7] = W[3]
+        W[14] = 0                           # zero logits
+        wsg = inp.w_shared_gate
+        sbias = inp.select_bias if score == "sigmoid" else None
+        x = bf16_tensor(inp.x, dev)
+        wr = bf16_tensor(W, dev)
+        sb = f32_tensor(sbias, dev) if sbias is not None else None
+        ids, w, sg = M.moe_route(x, wr, cfg.k, score, True, 1.0, None, sb, bf16_tensor(wsg, dev))
+        r = OL.route(inp.x, W, cfg.k, score, True, 1.0, None, sbias, wsg)
+        np.testing.assert_array_equal(to_np(ids), r.ids, err_msg=score)
+        assert_close(to_np(w), r.weights, f"ties {score} topk_w")
+        if score == "softmax":
+            tied = sum(len(set(row) & {2, 5, 9, 12}) >= 2 for row in r.ids.tolist())
+            assert tied > 0, "the case must select tied experts"
+        # the gate/up prologue's selection on the same logits
+        t, _ = build(cfg, dev)
+        lw = layer_weights(cfg, t)
+        lg = M.moe_router_logits(x, wr, cfg.k, score, bf16_tensor(wsg, dev))
+        got = M.moe_topk_gateup_shared(lg, x, cfg.k, lw.experts, lw.shared, score, True, 1.0, None, sb, True)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(to_np(got[0]), r.ids, err_msg=f"{score} prologue")
+
+
 GROUP_CASES = {
     # noaux_tc-like: sigmoid + selection bias, 256 experts in 8 groups, 4 kept, top-8
     "glm_groups_decode": (dataclasses.replace(synth.get("glm52_fp8"), T=3), 8, 4),
