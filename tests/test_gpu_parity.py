@@ -565,6 +565,10 @@ DECODE_STEP_CASES = {
     "tiny_4tok_sigmoid": (tiny(name="t4s", wtag=105, score="sigmoid", select_bias_std=0.01, k=6, T=4, E=32,
                                shared="gated", shared_K=256, shared_I=128), 1, 1, True),
     "decode_full": (synth.get("qwen38max_decode"), 1, 1, True),
+    # one expert per token; a layer of a single routed expert (every token selects it)
+    "tiny_k1": (tiny(name="tk1", wtag=108, k=1, T=3, shared="ungated", shared_K=256, shared_I=128), 1, 1, True),
+    "tiny_one_expert": (tiny(name="t1e", wtag=109, E=1, k=1, T=2, shared="gated", shared_K=256, shared_I=128),
+                        1, 1, True),
     # shapes the single launch does not take run as the three calls
     "tiny_sigmoid_fp8": (LAYER_CASES["tiny_fused_fp8_ungated"], 1, 1, False),
     "tiny_many_experts": (TOPK_GATEUP_CASES["tiny_many_experts"][0], 1, 1, False),
