@@ -466,6 +466,15 @@ MOE_DEV void stage_rows_dma(const GemvParams &p, unsigned char *smem, int rs, in
     }
 }
 
+// b * total / nb: the start of workgroup b's equal share of `total` items.  In 32-bit unsigned
+// arithmetic when the product fits (a 64-bit division is a long software routine, and this
+// one sits on the routing's critical path).
+MOE_DEV int share_begin(int b, int total, int nb) {
+    const uint64_t prod = (uint64_t)(uint32_t)b * (uint32_t)total;
+    if (prod <= 0xffffffffull) return (int)((uint32_t)prod / (uint32_t)nb);
+    return (int)(prod / (uint32_t)nb);
+}
+
 // A pass resolved to its slot: wave-uniform fields, plus this lane's matrix row n, the row's
 // index in the stacked matrix and its scale row.
 struct FlatPass {
@@ -582,16 +591,16 @@ MOE_DEV void flat_body(const GemvParams &p, const StepCtx *sc) {
     int sh_end = 0;
     if constexpr (ROUTE) {
         // the shared slot's passes (rows 0 .. T-1) and this workgroup's equal share of them
-        const long long S = has_sh ? (long long)((T + MAXM - 1) / MAXM) * ((sN + rpp - 1) / rpp) : 0;
-        const long long b = blockIdx.x, nb = gridDim.x;
-        sh_end = (int)((b + 1) * S / nb);
+        const int S = has_sh ? ((T + MAXM - 1) / MAXM) * ((sN + rpp - 1) / rpp) : 0;
+        const int b = blockIdx.x, nb = gridDim.x;
+        sh_end = share_begin(b + 1, S, nb);
         if (threadIdx.x == 0) {
             s_she[0] = -1;
             s_shr0[0] = 0;
             s_shm[0] = T;
             s_shpass0[0] = 0;
-            s_shpass0[1] = (int)S;
-            s_shnext = (int)(b * S / nb);
+            s_shpass0[1] = S;
+            s_shnext = share_begin(b, S, nb);
             s_dma = s_topk = s_tab = s_perm = 0;
         }
         __syncthreads();
@@ -728,8 +737,8 @@ MOE_DEV void flat_body(const GemvParams &p, const StepCtx *sc) {
         if (lane == 0) {
             s_pass0[ns] = base;
             s_ns = ns;
-            const long long b = blockIdx.x, nb = gridDim.x;
-            const int beg = (int)(b * base / nb), end = (int)((b + 1) * base / nb);
+            const int b = blockIdx.x, nb = gridDim.x;
+            const int beg = share_begin(b, base, nb), end = share_begin(b + 1, base, nb);
             s_beg = beg;
             s_end = end;
             s_next = ROUTE ? beg : beg + NW;

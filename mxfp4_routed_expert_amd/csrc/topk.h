@@ -161,10 +161,16 @@ MOE_DEV TopkLane topk_select(const float *lt, int E, int k, int score, int renor
     const float sg_logit = lt[has_sg ? E : 0];
 #pragma unroll
     for (int i = 0; i < NK; ++i) asm volatile("" : "+v"(lv[i]), "+v"(lbv[i]), "+v"(sbv[i]));   // loads stay here
+    const bool packed = NK <= kSortNK && score == MOE_SCORE_SOFTMAX && !lbias && n_group <= 1;
     uint64_t key[NK];
     double base[NK];
 #pragma unroll
     for (int i = 0; i < NK; ++i) {
+        if (packed) {                // (the packed words below carry the keys; base: the full softmax sum)
+            base[i] = (double)lv[i] + 0.0;
+            key[i] = 0;
+            continue;
+        }
         double l = (double)lv[i] + (lbias ? (double)lbv[i] : 0.0);
         double kv = l;
         if (score == MOE_SCORE_SIGMOID) {
@@ -218,8 +224,7 @@ MOE_DEV TopkLane topk_select(const float *lt, int E, int k, int score, int renor
     for (int i = 0; i < NK; ++i) braw[i] = base[i];
     int my_e = -1;
     double l = 0.0;              // lane j < k: base value of the j-th selected expert
-    const bool packed = score == MOE_SCORE_SOFTMAX && !lbias && n_group <= 1;
-    if (NK <= kSortNK && packed) {
+    if (packed) {
         // keys from the loaded float logits (the same order as order_key of their float64 values)
         uint64_t pk[NK];
 #pragma unroll
