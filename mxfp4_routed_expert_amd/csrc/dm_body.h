@@ -35,18 +35,20 @@ namespace moe {
 // wave keeps kDmDepth steps of loads in flight across item boundaries; every slot of that
 // ring records the position its loads belong to.
 //
-// Prologue: the slots' float32 h rows are loaded into registers first (each workgroup
-// starts at a different place in them, so the CUs of an XCD do not all ask the L2 for the
-// same lines at once), then the weights of the wave's first two steps; the h values are
-// written to LDS as the bf16 hi and lo planes, the wave counts itself in an LDS counter,
-// issues its next two steps and waits only for that counter to reach the wave count.  (A
-// workgroup barrier there would also wait for the slowest wave to get its weight loads
-// issued -- at the start every CU asks for its share of the first steps at once -- and the
-// waves already past it would issue nothing meanwhile.)
+// Prologue: the slots' float32 h rows are loaded into registers first, then the weights of
+// the wave's first two steps; the h values are written to LDS as the bf16 hi and lo planes
+// slot by slot (each workgroup takes the slots in its own rotated order, so the CUs of a die
+// do not all ask the L2 for the same lines at once, and its items follow the same order),
+// and after each of its iterations a wave counts itself in that iteration's LDS counter.  An
+// item waits only for the counter of the last iteration holding its slot's h, so the first
+// slots' items start while the later slots' h is still arriving.  (A workgroup barrier
+// there would also wait for the slowest wave to get its weight loads issued, and the waves
+// already past it would issue nothing meanwhile.)
 constexpr int kDmDepth = 4;              // steps of loads in flight per wave
 constexpr int kDmThreads = 1024;         // 16 waves, four per SIMD
 constexpr int kDmTile = 8;               // weight rows per item (two A tiles of 4 rows)
 constexpr int kDmMaxGroups = 4800;       // 8-value groups of h: slots * dc_plane_ld(I) / 8 within 150 KiB
+constexpr int kDmIters = (kDmMaxGroups + kDmThreads - 1) / kDmThreads;   // h groups per thread
 static_assert(2 * kDmMaxRows <= kDcMaxRows, "two partial sums per row must fit the table");
 static_assert(dc_plane_ld(1) % 512 == 0, "a plane must hold whole steps of 16 units");
 
@@ -62,7 +64,7 @@ MOE_DEV void dm_body(const DownCombineParams &p, int bx, int t, const StepCtx *s
     extern __shared__ __align__(16) unsigned char smem[];
     __shared__ int s_e[MOE_MAX_TOPK + 1], s_r[MOE_MAX_TOPK + 1];
     __shared__ float s_w[MOE_MAX_TOPK + 1];
-    __shared__ int s_item, s_ready;
+    __shared__ int s_item, s_ready[kDmIters];
     constexpr int NW = kDmThreads / 64;
     const int nslot = p.k + (p.sw ? 1 : 0);
     const int tid = threadIdx.x, lane = lane_id();
@@ -87,7 +89,8 @@ MOE_DEV void dm_body(const DownCombineParams &p, int bx, int t, const StepCtx *s
     }
     if (tid == 0) {
         s_item = NW;
-        s_ready = 0;
+#pragma unroll
+        for (int u = 0; u < kDmIters; ++u) s_ready[u] = 0;
     }
     __syncthreads();
 
@@ -104,8 +107,12 @@ MOE_DEV void dm_body(const DownCombineParams &p, int bx, int t, const StepCtx *s
     if (n_begin >= n_end) return;                          // the whole workgroup (uniform)
     const int ntile = (n_end - n_begin + kDmTile - 1) / kDmTile;
     const int KS = nm >= 2 * kDmDepth ? 2 : 1;             // K parts per (tile, slot)
-    const int per_tile = nslot * KS;
-    const int nitems = ntile * per_tile;
+    const int per_pos = ntile * KS;                        // items per slot position
+    const int nitems = nslot * per_pos;
+    // slot order of this workgroup: position q is slot (q + srot) mod nslot, for the items and
+    // for the h rows alike, so that the CUs of a die do not all read the same h lines first
+    const int srot = (int)(((long long)bx * 5 + (long long)t * 3) % nslot);
+    const int per = ld / 8;                                // 8-value groups of h per slot
     const int i16 = lane & 15, g = lane >> 4;
     const int ra = i16 >> 2, pb = i16 & 3;                 // A: row ra (+ 4) of the tile, part pb
     uint16_t *planes = (uint16_t *)smem;                   // slot j: hi plane 2j, lo plane 2j+1
@@ -114,16 +121,17 @@ MOE_DEV void dm_body(const DownCombineParams &p, int bx, int t, const StepCtx *s
 
     // load cursor: item `it` (nitems: none left), step m of [m, m_end); matrix bases of the
     // item (wave-uniform) and this lane's offsets of its two rows
-    int it = min(wave, nitems), m = 0, m_end = 0, cj = 0, ctile = 0, ckp = 0;
+    int it = min(wave, nitems), m = 0, m_end = 0, cj = 0, ctile = 0, ckp = 0, cpos = 0;
     const uint8_t *cwb = g_dm_zero, *csb = g_dm_zero;
     uint32_t cwo0 = 0, cwo1 = 0, cso0 = 0, cso1 = 0;
     auto setup = [&]() __attribute__((always_inline)) {     // (branch-free: a wave with no item left reads zeros)
         const bool has = it < nitems;
         const int itc = has ? it : 0;
-        ctile = itc / per_tile;
-        const int rem = itc - ctile * per_tile;
-        cj = rem / KS;
-        ckp = rem - cj * KS;
+        cpos = itc / per_pos;                              // items are slot-position major
+        const int rem = itc - cpos * per_pos;
+        ctile = rem / KS;
+        ckp = rem - ctile * KS;
+        cj = cpos + srot >= nslot ? cpos + srot - nslot : cpos + srot;
         m = has ? ckp * nm / KS : 0;
         m_end = has ? (ckp + 1) * nm / KS : 0;
         const bool sh = cj >= kk;
@@ -161,13 +169,14 @@ MOE_DEV void dm_body(const DownCombineParams &p, int bx, int t, const StepCtx *s
         sc[1] = csb[lv ? cso1 + u : 0u];
     };
     // ring slot d: the position its loads belong to
-    int pj[kDmDepth], ptile[kDmDepth], pkp[kDmDepth], pm[kDmDepth];
+    int pj[kDmDepth], ptile[kDmDepth], pkp[kDmDepth], pm[kDmDepth], ppos[kDmDepth];
     bool plive[kDmDepth], plast[kDmDepth];
     int live_slots = 0;
     auto fill = [&](auto dc, u32x4 (&w)[2], uint8_t (&sc)[2]) __attribute__((always_inline)) {
         constexpr int d = decltype(dc)::value;
         const bool lv = it < nitems;
         pj[d] = cj;
+        ppos[d] = cpos;
         ptile[d] = ctile;
         pkp[d] = ckp;
         pm[d] = m;
@@ -226,12 +235,10 @@ MOE_DEV void dm_body(const DownCombineParams &p, int bx, int t, const StepCtx *s
     // h rows -> registers: 8-value group i = (slot j, group v) of the planes' layout, taken
     // from a workgroup-dependent starting point; groups past d_ff and dropped slots become
     // zeros when written (their loads read a valid group).
-    constexpr int kGroups = (kDmMaxGroups + kDmThreads - 1) / kDmThreads;
-    const int per = ld / 8;
+    constexpr int kGroups = kDmIters;
     const int total = nslot * per;
-    const int rot = (int)(((long long)bx * 977 + (long long)t * 331) % total);
-    auto group_of = [&](int i) __attribute__((always_inline)) {
-        const int r = i + rot;
+    auto group_of = [&](int i) __attribute__((always_inline)) {   // linear index -> group (slot order)
+        const int r = i + srot * per;
         return r >= total ? r - total : r;
     };
     f32x4 va[kGroups], vb[kGroups];
@@ -274,9 +281,12 @@ MOE_DEV void dm_body(const DownCombineParams &p, int bx, int t, const StepCtx *s
     }
     // float32 h -> bf16 hi/lo planes: hi = RN_bf16(h), lo = RN_bf16(h - hi) by the packed
     // round-to-nearest-even conversion; plane hi of slot j at element 2j*ld, lo at (2j+1)*ld.
+    // Iteration u covers linear indices [1024u, 1024(u+1)), i.e. slot positions in order; each
+    // wave counts itself in s_ready[u] after its writes of iteration u, so the items of a slot
+    // position can start once every wave is past the last iteration holding its groups.
 #pragma unroll
     for (int u = 0; u < kGroups; ++u) {
-        if (tid + u * kDmThreads >= total) break;
+        if (tid + u * kDmThreads < total) {
         const int i = group_of(tid + u * kDmThreads);
         const int j = i / per, v = i - j * per;
         const bool ok = v * 8 < I && (j >= kk || s_r[j] >= 0);
@@ -293,28 +303,38 @@ MOE_DEV void dm_body(const DownCombineParams &p, int bx, int t, const StepCtx *s
         }
         *(u32x4 *)(planes + (size_t)(2 * j) * ld + v * 8) = hv;
         *(u32x4 *)(planes + (size_t)(2 * j + 1) * ld + v * 8) = lv;
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");   // this wave's writes of iteration u are in LDS
+        if (lane == 0) atomicAdd(&s_ready[u], 1);
     }
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");     // this wave's plane writes are in LDS
-    if (lane == 0) atomicAdd(&s_ready, 1);
     if constexpr (!STEP) {
         fill(std::integral_constant<int, 2>{}, wv[2], sv[2]);
         fill(std::integral_constant<int, 3>{}, wv[3], sv[3]);
     }
-    // every wave counts itself once, right after its writes, so the wait ends; the bound only
-    // keeps a fault elsewhere from turning into a hang
-    // (read through an LDS pointer: a generic volatile read is a flat load, and its wait
-    // would also wait for every weight load in flight)
-    volatile __attribute__((address_space(3))) int *ready = (volatile __attribute__((address_space(3))) int *)&s_ready;
-    for (int spin = 0; spin < (1 << 22); ++spin) {
-        if (__builtin_amdgcn_readfirstlane(*ready) >= NW) break;
-        __builtin_amdgcn_s_sleep(1);
-    }
-    asm volatile("" ::: "memory");                         // no plane read moves above the wait
+    // Before an item's steps: wait until every wave has written the planes of its slot
+    // position (a wave's positions only increase).  Every wave counts itself in each counter,
+    // right after its writes, so the wait ends; the bound only keeps a fault elsewhere from
+    // turning into a hang.  (Read through an LDS pointer: a generic volatile read is a flat
+    // load, and its wait would also wait for every weight load in flight.)
+    int ready_known = -1;
+    auto wait_planes = [&](int pos) __attribute__((always_inline)) {
+        const int need = ((pos + 1) * per - 1) / kDmThreads;
+        if (need <= ready_known) return;
+        volatile __attribute__((address_space(3))) int *ready =
+            (volatile __attribute__((address_space(3))) int *)&s_ready[need];
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+            if (__builtin_amdgcn_readfirstlane(*ready) >= NW) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
+        asm volatile("" ::: "memory");                     // no plane read moves above the wait
+        ready_known = need;
+    };
 
     while (live_slots > 0) {
         static_for<kDmDepth>([&](auto dc) __attribute__((always_inline)) {
             constexpr int d = decltype(dc)::value;
             if (plive[d]) {
+                wait_planes(ppos[d]);
                 compute(dc, wv[d], sv[d]);
                 --live_slots;
             }
