@@ -19,6 +19,7 @@
 //     expert_offsets on the device (the slot-th expert that has rows), so no host
 //     synchronisation is needed and empty experts cost nothing.
 #include <algorithm>
+#include <mutex>
 
 #include "dm_body.h"
 #include "gemv.h"
@@ -649,35 +650,61 @@ MOE_DEV void flat_body(const GemvParams &p, const StepCtx *sc) {
         // slots: the experts that own a valid range of rows, in expert order, then the shared
         // expert (e = -1) over the identity rows
         int ns = 0;
+        int fast_base = -1;                                // the one-token table's pass count
         if constexpr (ROUTE) {
             lds_wait_at_least(&s_topk, T);
-            // pair q = (token q / k, slot q % k) -> row = pairs of lower experts + earlier pairs
-            // of its expert; the first pair of an expert opens its slot
-            // (pair q's expert read from lane q's register: a loop of LDS reads waits out each
-            // read's latency in turn)
-            const int P = T * kk;
-            const int e = lane < P ? s_sid[lane] : -1;
-            int row = 0, cnt = 0;
-            bool first = e >= 0;
-            for (int q = 0; q < P; ++q) {
-                const int eq = __builtin_amdgcn_readlane(e, q);
-                row += (eq >= 0 && (eq < e || (eq == e && q < lane))) ? 1 : 0;
-                cnt += eq == e ? 1 : 0;
-                first = first && !(eq == e && q < lane);
+            if (T == 1) {
+                // one token: its k experts are distinct, each a slot of one row whose index is the
+                // expert's rank among them; pass offsets are multiples of the passes per slot (the
+                // table the general form below builds, without its scans)
+                const int e = lane < kk ? s_sid[lane] : -1;
+                int row = 0;
+                for (int q = 0; q < kk; ++q) {
+                    const int eq = __builtin_amdgcn_readlane(e, q);
+                    row += (eq >= 0 && eq < e) ? 1 : 0;
+                }
+                if (e >= 0) {
+                    s_tok[row] = 0;
+                    s_e[row] = e;
+                    s_r0[row] = row;
+                    s_m[row] = 1;
+                }
+                if constexpr (STEP) {
+                    if (lane < kk) sc->lds->p2r[lane] = e >= 0 ? row : -1;
+                }
+                ns = __popcll(__ballot(e >= 0));
+                const int pps = (pN + rpp - 1) / rpp;
+                if (lane < ns) s_pass0[lane] = lane * pps;
+                fast_base = ns * pps;
+            } else {
+                // pair q = (token q / k, slot q % k) -> row = pairs of lower experts + earlier pairs
+                // of its expert; the first pair of an expert opens its slot
+                // (pair q's expert read from lane q's register: a loop of LDS reads waits out each
+                // read's latency in turn)
+                const int P = T * kk;
+                const int e = lane < P ? s_sid[lane] : -1;
+                int row = 0, cnt = 0;
+                bool first = e >= 0;
+                for (int q = 0; q < P; ++q) {
+                    const int eq = __builtin_amdgcn_readlane(e, q);
+                    row += (eq >= 0 && (eq < e || (eq == e && q < lane))) ? 1 : 0;
+                    cnt += eq == e ? 1 : 0;
+                    first = first && !(eq == e && q < lane);
+                }
+                const uint64_t fm = __ballot(first);
+                int slot = 0;
+                for (int q = 0; q < P; ++q) slot += (((fm >> q) & 1ull) && __builtin_amdgcn_readlane(e, q) < e) ? 1 : 0;
+                if (e >= 0) s_tok[row] = lane / kk;
+                if constexpr (STEP) {
+                    if (lane < P) sc->lds->p2r[lane] = e >= 0 ? row : -1;
+                }
+                if (first) {
+                    s_e[slot] = e;
+                    s_r0[slot] = row;
+                    s_m[slot] = cnt;
+                }
+                ns = __popcll(fm);
             }
-            const uint64_t fm = __ballot(first);
-            int slot = 0;
-            for (int q = 0; q < P; ++q) slot += (((fm >> q) & 1ull) && __builtin_amdgcn_readlane(e, q) < e) ? 1 : 0;
-            if (e >= 0) s_tok[row] = lane / kk;
-            if constexpr (STEP) {
-                if (lane < P) sc->lds->p2r[lane] = e >= 0 ? row : -1;
-            }
-            if (first) {
-                s_e[slot] = e;
-                s_r0[slot] = row;
-                s_m[slot] = cnt;
-            }
-            ns = __popcll(fm);
         } else if (routed) {
             int o[kMaxOffsetChunks];
 #pragma unroll
@@ -717,8 +744,8 @@ MOE_DEV void flat_body(const GemvParams &p, const StepCtx *sc) {
             ++ns;
         }
         // first pass of each slot: exclusive prefix of ceil(rows / MAXM) * ceil(N / rpp)
-        int base = 0;
-        for (int c = 0; c < ns; c += 64) {
+        int base = fast_base >= 0 ? fast_base : 0;
+        for (int c = 0; fast_base < 0 && c < ns; c += 64) {
             const int sl = c + lane;
             int cnt = 0;
             if (sl < ns) {
@@ -1535,6 +1562,25 @@ __global__ __launch_bounds__(kFlatThreads) void decode_step_kernel(const StepPar
         __hip_atomic_store(sp.sync, c + 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+static bool step_fits(void (*fn)(const StepParams), int maxm, size_t lds) {
+    constexpr int kMaxDev = 64, kSlots = 8;
+    struct Entry { int maxm; size_t lds; bool fits; };
+    static std::mutex mu;
+    static Entry cache[kMaxDev][kSlots];
+    static int used[kMaxDev];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDev) return false;
+    std::lock_guard<std::mutex> lock(mu);
+    for (int i = 0; i < used[dev]; ++i)
+        if (cache[dev][i].maxm == maxm && cache[dev][i].lds == lds) return cache[dev][i].fits;
+    int per_cu = 0;
+    const hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)fn, kFlatThreads, lds);
+    if (e != hipSuccess) (void)hipGetLastError();          // (a failed query only means: take the three calls)
+    const bool fits = e == hipSuccess && per_cu >= 1;
+    if (used[dev] < kSlots) cache[dev][used[dev]++] = Entry{maxm, lds, fits};
+    return fits;
+}
+
 bool decode_step_launch(StepParams sp, hipStream_t stream, moe_status *st) {
     size_t lds_gu = 0, lds_dc = 0;
     int maxm = 1, U = 1;
@@ -1547,13 +1593,9 @@ bool decode_step_launch(StepParams sp, hipStream_t stream, moe_status *st) {
     const size_t lds = std::max(lds_gu, lds_dc);
     using StepFn = void (*)(const StepParams);
     StepFn fn = maxm == 1 ? decode_step_kernel<1> : (maxm == 2 ? decode_step_kernel<2> : decode_step_kernel<4>);
-    // every workgroup must be resident at once: one per CU
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, (const void *)fn, kFlatThreads, lds) != hipSuccess ||
-        per_cu < 1) {
-        (void)hipGetLastError();
-        return false;
-    }
+    // every workgroup must be resident at once: one per CU (the occupancy query is cached per
+    // device, token tile and LDS size)
+    if (!step_fits(fn, maxm, lds)) return false;
     hipLaunchKernelGGL(fn, dim3(nwg), dim3(kFlatThreads), lds, stream, sp);
     *st = launch_check("moe_decode_step: decode_step_kernel");
     return true;
