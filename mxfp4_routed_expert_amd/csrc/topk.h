@@ -64,6 +64,7 @@ MOE_DEV int wave_best_lane(uint64_t hk, int hi) {
 }
 
 constexpr int kSortNK = 8;                 // most keys per lane that are sorted (more: per-round rescans)
+constexpr int kSortPackedNK = 16;          // ... for packed words, which sort with one compare per exchange
 
 // In-register bitonic sort of a lane's N (power of two) entries into descending order of
 // (key, then lower index first); base values move with their keys.
@@ -161,7 +162,7 @@ MOE_DEV TopkLane topk_select(const float *lt, int E, int k, int score, int renor
     const float sg_logit = lt[has_sg ? E : 0];
 #pragma unroll
     for (int i = 0; i < NK; ++i) asm volatile("" : "+v"(lv[i]), "+v"(lbv[i]), "+v"(sbv[i]));   // loads stay here
-    const bool packed = NK <= kSortNK && score == MOE_SCORE_SOFTMAX && !lbias && n_group <= 1;
+    const bool packed = NK <= kSortPackedNK && score == MOE_SCORE_SOFTMAX && !lbias && n_group <= 1;
     uint64_t key[NK];
     double base[NK];
 #pragma unroll
@@ -213,7 +214,8 @@ MOE_DEV TopkLane topk_select(const float *lt, int E, int k, int score, int renor
             if (e < E && !((keep >> (e / gs)) & 1ull)) key[i] = 0;
         }
     }
-    // Up to kSortNK keys per lane: the lane's keys are sorted once, best first (larger key,
+    // Up to kSortNK keys per lane (kSortPackedNK packed words): the lane's keys are sorted
+    // once, best first (larger key,
     // then lower expert); each round takes the wave-wide best of the lanes' first entries
     // and the winner shifts its list.  More keys per lane: each lane tracks its best
     // untaken key (its head) and only the round's winner rescans -- the sorting network
