@@ -12,7 +12,7 @@ captured in order as one HIP graph (a model's forward pass holds its layers in o
 and each slot also as a graph of its own; the timed region replays K steps back to back
 between two events -- whole sixteen-step graphs, then single-step graphs for the rest.
 The same K steps with one graph launch per step are reported beside it
-(`ms_per_step_one_graph_per_step`).
+(`ms_per_step_one_graph_per_step`, with the median, p10 and p90 of the per-step times).
 
 The headline workload (`value`, `ms_per_step`) is the one-token decode layer.  By default
 the same run also times the two 512-token prefill workloads on the same expert instances
@@ -348,14 +348,20 @@ def run_workload(torch, sdev, cfg, layers, NB, steps, warmup, use_graphs, dev, t
     torch.cuda.synchronize()
     ms_per_step = ev0.elapsed_time(ev1) / steps
     ms_one_graph = None
+    step_pct = None
     if graphs is not None:
-        # the same steps, one graph launch per step
-        ev0.record()
+        # the same steps, one graph launch per step, with an event after each: per-step times
+        # (median, p10, p90) beside the mean
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record()
         for s in range(steps):
             step(s)
-        ev1.record()
+            evs[s + 1].record()
         torch.cuda.synchronize()
-        ms_one_graph = ev0.elapsed_time(ev1) / steps
+        ms_one_graph = evs[0].elapsed_time(evs[-1]) / steps
+        per = sorted(evs[s].elapsed_time(evs[s + 1]) for s in range(steps))
+        pick = lambda q: per[min(steps - 1, int(round(q * (steps - 1))))]
+        step_pct = dict(p10=round(pick(0.1), 5), median=round(pick(0.5), 5), p90=round(pick(0.9), 5))
 
     # distinct routed experts touched per slot (read back after a step of that slot)
     D_slot = []
@@ -394,7 +400,7 @@ def run_workload(torch, sdev, cfg, layers, NB, steps, warmup, use_graphs, dev, t
     if graphs is not None:
         phases.append(["one_graph_per_step", steps])
     phases += [["count", S], ["events", n]]
-    return dict(ms_per_step=ms_per_step, ms_one_graph=ms_one_graph, D_steps=D_steps, D_ev=D_ev, gu_us=gu_us, dn_us=dn_us, st_us=st_us,
+    return dict(ms_per_step=ms_per_step, ms_one_graph=ms_one_graph, step_pct=step_pct, D_steps=D_steps, D_ev=D_ev, gu_us=gu_us, dn_us=dn_us, st_us=st_us,
                 single=single, launches=n, graphs=graphs is not None, slots=S, phases=phases)
 
 
@@ -646,6 +652,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(r["ms_per_step"], 5),
         "ms_per_step_one_graph_per_step": round(r["ms_one_graph"], 5) if r["ms_one_graph"] else None,
+        "ms_per_step_one_graph_per_step_pct": r["step_pct"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
